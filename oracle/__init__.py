@@ -1,0 +1,227 @@
+"""CPU oracle for the block-paged KV layout: numpy front end to liboracle.so.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. It shares no code
+with the GPU library (``block_table_gather_amd``) and neither imports the
+other. Nothing here may serve as a fallback for the GPU path.
+
+Every function takes numpy arrays, widens index arrays to uint64 (lossless)
+and calls the plain C element loops of ``oracle.c``, which cite the pages:
+
+* [Hurray] "Block-Paged Layout -- Hurray Format Specification"
+* [Rust20] "Keep token order across cache pages"
+* [Day51]  "Visualize PagedAttention block layout"
+
+Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
+``tests/test_oracle_pins.py`` and ``tests/test_oracle_cross.py``.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+# Oracle check outcomes (oracle.h, enum oracle_check), by name.
+CHECKS = {
+    0: "valid",
+    1: "rank",
+    2: "paged_axis",
+    3: "seq_ptr_first",
+    4: "seq_ptr_last",
+    5: "seq_ptr_order",
+    6: "page_range",
+    7: "seq_len",
+    8: "total_tokens",
+}
+
+_lib = None
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+_vp = ctypes.c_void_p
+_u64 = ctypes.c_uint64
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.oracle_element_index.restype = _u64
+    lib.oracle_element_index.argtypes = [_vp, _vp] + [_u64] * 9
+    lib.oracle_validate.restype = ctypes.c_int
+    lib.oracle_validate.argtypes = [ctypes.c_uint32, ctypes.c_uint32, _u64, _u64, _vp,
+                                    _u64, _vp, _u64, _vp, _vp, _u64, _vp]
+    lib.oracle_gather.restype = None
+    lib.oracle_gather.argtypes = [_vp, _u64, _u64, _u64, _u64, _vp, _vp, _vp, _u64,
+                                  _vp, _vp]
+    lib.oracle_gather_rows.restype = _u64
+    lib.oracle_gather_rows.argtypes = [_vp, _u64, _u64, _u64, _u64, _vp, _vp, _vp,
+                                       _u64, _vp, _u64, _vp]
+    lib.oracle_scatter.restype = None
+    lib.oracle_scatter.argtypes = [_vp, _u64, _u64, _u64, _u64, _vp, _vp, _vp, _vp,
+                                   _u64, _vp, ctypes.c_int]
+    lib.oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.oracle_bf16_rne.argtypes = [ctypes.c_float]
+    lib.oracle_bf16_rne_array.restype = None
+    lib.oracle_bf16_rne_array.argtypes = [_vp, _u64, _vp]
+    lib.oracle_gather_dequant.restype = None
+    lib.oracle_gather_dequant.argtypes = [_vp, _vp, _u64, _u64, _u64, _vp, _vp, _vp,
+                                          _u64, _vp]
+    lib.oracle_gather_dequant_rows.restype = _u64
+    lib.oracle_gather_dequant_rows.argtypes = [_vp, _vp, _u64, _u64, _u64, _vp, _vp,
+                                               _vp, _u64, _vp, _u64, _vp]
+    lib.oracle_payload.restype = ctypes.c_int
+    lib.oracle_payload.argtypes = [_u64] * 7 + [_vp]
+    _lib = lib
+    return lib
+
+
+def _idx(a):
+    """Index array as contiguous uint64 (kept alive by the caller)."""
+    return np.ascontiguousarray(np.asarray(a, dtype=np.uint64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def element_index(block_table, seq_ptr, s, t, h, d, page_size, strides):
+    """[Hurray] Element Lookup with explicit (page, slot, head, dim) strides."""
+    lib = _load()
+    bt, sp = _idx(block_table), _idx(seq_ptr)
+    return int(lib.oracle_element_index(_ptr(bt), _ptr(sp), s, t, h, d, page_size,
+                                        *strides))
+
+
+def validate(*, rank, paged_axis, num_pages, page_size, block_table, seq_ptr,
+             seq_lens, total_tokens, seq_start=None):
+    """First failing storage check, as (name, index); ("valid", 0) if none."""
+    lib = _load()
+    bt, sp, sl = _idx(block_table), _idx(seq_ptr), _idx(seq_lens)
+    ss = None if seq_start is None else _idx(seq_start)
+    num_seqs = len(sp) - 1
+    assert len(sl) == num_seqs and (ss is None or len(ss) == num_seqs)
+    index = np.zeros(1, dtype=np.uint64)
+    code = lib.oracle_validate(rank, paged_axis, num_pages, page_size,
+                               _ptr(bt) if len(bt) else None, len(bt), _ptr(sp),
+                               num_seqs, _ptr(sl), _ptr(ss), total_tokens,
+                               _ptr(index))
+    return CHECKS[code], int(index[0])
+
+
+def _pool_geometry(pool, page_size, num_heads, head_dim):
+    pool = np.ascontiguousarray(pool)
+    assert pool.size % (page_size * num_heads * head_dim) == 0
+    return pool, pool.dtype.itemsize
+
+
+def gather(pool, *, page_size, num_heads, head_dim, block_table, seq_ptr, seq_lens,
+           mark_reads=False):
+    """Logical [T, H, D] tensor in the pool's dtype (bit copy).
+
+    With mark_reads, also returns a uint8 array over the pool's slots that is 1
+    where the gather read a slot."""
+    lib = _load()
+    pool, eb = _pool_geometry(pool, page_size, num_heads, head_dim)
+    bt, sp, sl = _idx(block_table), _idx(seq_ptr), _idx(seq_lens)
+    total = int(sl.sum()) if len(sl) else 0
+    out = np.empty((total, num_heads, head_dim), dtype=pool.dtype)
+    mark = np.zeros(pool.size // (num_heads * head_dim), dtype=np.uint8) \
+        if mark_reads else None
+    lib.oracle_gather(_ptr(pool), eb, page_size, num_heads, head_dim,
+                      _ptr(bt) if len(bt) else None, _ptr(sp), _ptr(sl) if len(sl) else None,
+                      len(sl), _ptr(out) if out.size else None, _ptr(mark))
+    return (out, mark) if mark_reads else out
+
+
+def gather_rows(pool, rows, *, page_size, num_heads, head_dim, block_table, seq_ptr,
+                seq_lens):
+    """Rows `rows` of the logical tensor, computed one by one."""
+    lib = _load()
+    pool, eb = _pool_geometry(pool, page_size, num_heads, head_dim)
+    bt, sp, sl, rw = _idx(block_table), _idx(seq_ptr), _idx(seq_lens), _idx(rows)
+    out = np.zeros((len(rw), num_heads, head_dim), dtype=pool.dtype)
+    missing = lib.oracle_gather_rows(_ptr(pool), eb, page_size, num_heads, head_dim,
+                                     _ptr(bt), _ptr(sp), _ptr(sl), len(sl), _ptr(rw),
+                                     len(rw), _ptr(out))
+    assert missing == 0, f"{missing} rows past the logical total"
+    return out
+
+
+def scatter(pool, src, *, page_size, num_heads, head_dim, block_table, seq_ptr,
+            seq_lens, seq_start=None, zero_tail=False):
+    """Returns a copy of `pool` with the rows of `src` written into their slots."""
+    lib = _load()
+    pool, eb = _pool_geometry(pool, page_size, num_heads, head_dim)
+    result = pool.copy()
+    src = np.ascontiguousarray(src)
+    assert src.dtype.itemsize == eb
+    bt, sp, sl = _idx(block_table), _idx(seq_ptr), _idx(seq_lens)
+    ss = None if seq_start is None else _idx(seq_start)
+    lib.oracle_scatter(_ptr(result), eb, page_size, num_heads, head_dim,
+                       _ptr(bt) if len(bt) else None, _ptr(sp),
+                       _ptr(sl) if len(sl) else None, _ptr(ss) if ss is not None and len(ss) else None,
+                       len(sl), _ptr(src) if src.size else None, int(bool(zero_tail)))
+    return result
+
+
+def bf16_rne(x):
+    """float32 array -> uint16 bf16 bit patterns, round to nearest even."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    if x.size:
+        lib.oracle_bf16_rne_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def gather_dequant(pool, scales, *, page_size, num_heads, head_dim, block_table,
+                   seq_ptr, seq_lens):
+    """int8 pool + per-slot fp32 scales -> bf16 bit patterns [T, H, D] (uint16)."""
+    lib = _load()
+    pool = np.ascontiguousarray(pool, dtype=np.int8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    bt, sp, sl = _idx(block_table), _idx(seq_ptr), _idx(seq_lens)
+    total = int(sl.sum()) if len(sl) else 0
+    out = np.empty((total, num_heads, head_dim), dtype=np.uint16)
+    lib.oracle_gather_dequant(_ptr(pool), _ptr(scales), page_size, num_heads, head_dim,
+                              _ptr(bt) if len(bt) else None, _ptr(sp),
+                              _ptr(sl) if len(sl) else None, len(sl),
+                              _ptr(out) if out.size else None)
+    return out
+
+
+def gather_dequant_rows(pool, scales, rows, *, page_size, num_heads, head_dim,
+                        block_table, seq_ptr, seq_lens):
+    lib = _load()
+    pool = np.ascontiguousarray(pool, dtype=np.int8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    bt, sp, sl, rw = _idx(block_table), _idx(seq_ptr), _idx(seq_lens), _idx(rows)
+    out = np.zeros((len(rw), num_heads, head_dim), dtype=np.uint16)
+    missing = lib.oracle_gather_dequant_rows(_ptr(pool), _ptr(scales), page_size,
+                                             num_heads, head_dim, _ptr(bt), _ptr(sp),
+                                             _ptr(sl), len(sl), _ptr(rw), len(rw),
+                                             _ptr(out))
+    assert missing == 0
+    return out
+
+
+PAYLOAD_FIELDS = ("reserved_pages", "active_pages", "allocated_slots", "live_slots",
+                  "unused_slots", "tail_slots", "inactive_slots", "allocated_bytes",
+                  "live_bytes", "unused_bytes", "tail_bytes", "inactive_bytes",
+                  "contiguous_slots")
+
+
+def payload(*, capacity, page_tokens, length, batch, kv_heads, width, elem_bytes=8):
+    """[Rust20] payload accounting of one layer's K and V arrays, as a dict."""
+    lib = _load()
+    out = np.zeros(13, dtype=np.uint64)
+    rc = lib.oracle_payload(capacity, page_tokens, length, batch, kv_heads, width,
+                            elem_bytes, _ptr(out))
+    if rc != 0:
+        raise ValueError("invalid payload query")
+    return {k: int(v) for k, v in zip(PAYLOAD_FIELDS, out)}

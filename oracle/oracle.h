@@ -1,0 +1,134 @@
+/*
+ * oracle.h -- plain CPU oracle for the block-paged KV layout.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the package's smoke check and the
+ * benchmark's CPU-baseline leg may load or call this library. It shares no
+ * code, header, table or constant with the GPU library and must never be used
+ * as a fallback for it.
+ *
+ * Pages cited (by title and section):
+ *   [Hurray] "Block-Paged Layout -- Hurray Format Specification"
+ *   [Rust20] "Keep token order across cache pages" (practical LLM in Rust, ch. 20)
+ *   [Day51]  "Visualize PagedAttention block layout"
+ *
+ * Every index array (block_table, seq_ptr, seq_lens, seq_start) is passed as
+ * uint64 here; narrowing a uint32 table to this type is lossless, so the index
+ * type of a descriptor does not change what the oracle computes.
+ *
+ * All functions are single-threaded element loops. None allocates memory that
+ * outlives the call.
+ */
+#ifndef BTG_ORACLE_H
+#define BTG_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Outcome of oracle_validate, in the order the checks are taken. The numbers
+ * are the oracle's own; the test suite maps them to the GPU library's codes. */
+enum oracle_check {
+    ORACLE_VALID = 0,
+    ORACLE_BAD_RANK = 1,        /* [Hurray] Description: rank must be 3 */
+    ORACLE_BAD_PAGED_AXIS = 2,  /* [Hurray] Storage Invariants (6) */
+    ORACLE_SEQ_PTR_FIRST = 3,   /* (1) seq_ptr[0] = 0 */
+    ORACLE_SEQ_PTR_LAST = 4,    /* (1) seq_ptr[num_seqs] = total_logical_pages */
+    ORACLE_SEQ_PTR_ORDER = 5,   /* (2) non-decreasing */
+    ORACLE_PAGE_RANGE = 6,      /* (3) 0 <= block_table[k] < num_pages */
+    ORACLE_SEQ_LEN = 7,         /* token count fits the slice (Partial trailing page) */
+    ORACLE_TOTAL_TOKENS = 8     /* total_tokens = sum of counts (Logical Shape) */
+};
+
+/* [Hurray] Element Lookup, with the four axis strides of the physical array
+ * made explicit so that the same function also evaluates [Rust20]'s
+ * [N,B,H_kv,P,d] tutorial layout. Returns the flat element index. */
+uint64_t oracle_element_index(const uint64_t *block_table, const uint64_t *seq_ptr,
+                              uint64_t s, uint64_t t, uint64_t h, uint64_t d,
+                              uint64_t page_size, uint64_t stride_page,
+                              uint64_t stride_slot, uint64_t stride_head,
+                              uint64_t stride_dim);
+
+/* [Hurray] Storage Invariants (1)-(3), (6), Description (rank 3), plus the two
+ * checks the Partial-trailing-page and Logical-Shape paragraphs imply. Returns
+ * the first failing check (enum oracle_check) and writes its smallest failing
+ * index to *index_out. seq_start may be NULL (every sequence starts at 0). */
+int oracle_validate(uint32_t rank, uint32_t paged_axis, uint64_t num_pages,
+                    uint64_t page_size, const uint64_t *block_table,
+                    uint64_t num_block_entries, const uint64_t *seq_ptr,
+                    uint64_t num_seqs, const uint64_t *seq_lens,
+                    const uint64_t *seq_start, uint64_t total_tokens,
+                    uint64_t *index_out);
+
+/* Gather: the logical [total_tokens, H, D] tensor, sequences concatenated in
+ * index order, token t of sequence s at row (sum of earlier counts) + t.
+ * A bit copy of elem_bytes per element. If slot_read_mark is not NULL it has
+ * num_pages*page_size bytes and each pool slot the gather reads is set to 1. */
+void oracle_gather(const void *page_pool, uint64_t elem_bytes, uint64_t page_size,
+                   uint64_t num_heads, uint64_t head_dim,
+                   const uint64_t *block_table, const uint64_t *seq_ptr,
+                   const uint64_t *seq_lens, uint64_t num_seqs, void *out,
+                   uint8_t *slot_read_mark);
+
+/* Gather of selected logical rows only: rows[i] is a row of the logical
+ * tensor; out receives rows_count rows of H*D elements. Rows past the total
+ * are left untouched and counted in the return value. */
+uint64_t oracle_gather_rows(const void *page_pool, uint64_t elem_bytes,
+                            uint64_t page_size, uint64_t num_heads, uint64_t head_dim,
+                            const uint64_t *block_table, const uint64_t *seq_ptr,
+                            const uint64_t *seq_lens, uint64_t num_seqs,
+                            const uint64_t *rows, uint64_t rows_count, void *out);
+
+/* Scatter: for each sequence s the new tokens occupy logical positions
+ * [start_s, start_s + L_s) (start_s = 0 when seq_start is NULL); row i of src
+ * belonging to s is written to the pool slot of position start_s + i.
+ * With zero_tail != 0, every element of the slots after the last written
+ * position, up to the end of that page, is set to zero bytes. */
+void oracle_scatter(void *page_pool, uint64_t elem_bytes, uint64_t page_size,
+                    uint64_t num_heads, uint64_t head_dim,
+                    const uint64_t *block_table, const uint64_t *seq_ptr,
+                    const uint64_t *seq_lens, const uint64_t *seq_start,
+                    uint64_t num_seqs, const void *src, int zero_tail);
+
+/* fp32 -> bf16, round to nearest, ties to even, on the binary32 bit pattern
+ * (IEEE 754 roundTiesToEven). NaN stays NaN (quieted). */
+uint16_t oracle_bf16_rne(float x);
+
+/* oracle_bf16_rne applied to n values, one by one. */
+void oracle_bf16_rne_array(const float *x, uint64_t n, uint16_t *out);
+
+/* Dequant-gather: out = bf16(fp32(q * scale)) with q the int8 pool element
+ * and scale = scales[phys_page * page_size + offset_in_page]
+ * ([Hurray] Element Lookup, Per-page-slot parameters). */
+void oracle_gather_dequant(const int8_t *page_pool, const float *scales,
+                           uint64_t page_size, uint64_t num_heads, uint64_t head_dim,
+                           const uint64_t *block_table, const uint64_t *seq_ptr,
+                           const uint64_t *seq_lens, uint64_t num_seqs,
+                           uint16_t *out);
+
+/* Same arithmetic as oracle_gather_dequant for selected logical rows. */
+uint64_t oracle_gather_dequant_rows(const int8_t *page_pool, const float *scales,
+                                    uint64_t page_size, uint64_t num_heads,
+                                    uint64_t head_dim, const uint64_t *block_table,
+                                    const uint64_t *seq_ptr, const uint64_t *seq_lens,
+                                    uint64_t num_seqs, const uint64_t *rows,
+                                    uint64_t rows_count, uint16_t *out);
+
+/* [Rust20] "Count live rows and two kinds of unused payload": buffer-length
+ * payload of one layer's K and V arrays. out[] receives, in order:
+ *  0 reserved pages      1 active pages
+ *  2 allocated slots     3 live slots      4 unused slots
+ *  5 tail slots          6 inactive-page slots
+ *  7..11 the same five slot counts times elem_bytes
+ *  12 contiguous slots for the same capacity (U * capacity)
+ * Returns 0, or -1 if length > capacity or a zero size is given. */
+int oracle_payload(uint64_t capacity, uint64_t page_tokens, uint64_t length,
+                   uint64_t batch, uint64_t kv_heads, uint64_t width,
+                   uint64_t elem_bytes, uint64_t out[13]);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
