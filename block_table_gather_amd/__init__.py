@@ -1,0 +1,244 @@
+"""Block-paged KV gather / scatter / dequant-gather / validate on MI355X.
+
+Thin ctypes binding over ``libhp.so`` (the C ABI declared in
+``include/hp.h``). This module only marshals arguments: it reads pointers,
+sizes and the current HIP stream from torch tensors and calls the library;
+every step of the path runs in the library's HIP kernels. PyTorch is used for
+device memory and streams only.
+
+The layout is the one of "Block-Paged Layout -- Hurray Format Specification":
+page pool [num_pages, page_size, num_heads, head_dim], a block table of
+physical page IDs (uint32 or uint64), CSR offsets ``seq_ptr`` and one token
+count per sequence. Importing this package fails if the library was not built
+(``python -m block_table_gather_amd.build``); there is no fallback.
+"""
+import ctypes
+import os
+
+__all__ = ["Descriptor", "HpError", "gather", "scatter", "gather_dequant", "validate",
+           "workspace_bytes", "status_str", "lib", "LIB_PATH", "STATUS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhp.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m block_table_gather_amd.build` "
+        "(hipcc, gfx950). There is no fallback implementation.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# Status codes (include/hp.h, enum hp_status).
+STATUS = {
+    0: "HP_OK", 1: "HP_ERR_NULL", 2: "HP_ERR_ARG", 3: "HP_ERR_RANK", 4: "HP_ERR_PAGED_AXIS",
+    5: "HP_ERR_INDEX_TYPE", 6: "HP_ERR_DTYPE", 7: "HP_ERR_ALIGN", 8: "HP_ERR_WORKSPACE",
+    9: "HP_ERR_SHARDED", 16: "HP_ERR_SEQPTR_FIRST", 17: "HP_ERR_SEQPTR_LAST",
+    18: "HP_ERR_SEQPTR_ORDER", 19: "HP_ERR_PAGE_RANGE", 20: "HP_ERR_SEQ_LEN",
+    21: "HP_ERR_TOTAL_TOKENS", 32: "HP_ERR_HIP",
+}
+CODE = {v: k for k, v in STATUS.items()}
+HP_INDEX_U32, HP_INDEX_U64 = 0x00, 0x01
+DTYPE = {"i8": 1, "u8": 2, "f16": 3, "bf16": 4, "f32": 5, "f64": 6}
+HP_FLAG_CHECKED, HP_FLAG_ZERO_TAIL = 1, 2
+
+
+class HpDesc(ctypes.Structure):
+    """Mirror of ``hp_desc`` (include/hp.h)."""
+    _fields_ = [
+        ("rank", ctypes.c_uint32), ("paged_axis", ctypes.c_uint32),
+        ("index_type", ctypes.c_uint32), ("dtype", ctypes.c_uint32),
+        ("page_size", ctypes.c_uint32), ("num_heads", ctypes.c_uint32),
+        ("head_dim", ctypes.c_uint32), ("has_shard", ctypes.c_uint32),
+        ("kv_role", ctypes.c_uint32), ("layer_index", ctypes.c_uint32),
+        ("byte_offset", ctypes.c_uint64), ("num_pages", ctypes.c_uint64),
+        ("num_seqs", ctypes.c_uint64), ("num_block_entries", ctypes.c_uint64),
+        ("total_tokens", ctypes.c_uint64),
+        ("page_pool", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+        ("seq_ptr", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+    ]
+
+
+class HpValidateResult(ctypes.Structure):
+    _fields_ = [("code", ctypes.c_int32), ("reserved", ctypes.c_uint32),
+                ("index", ctypes.c_uint64)]
+
+
+_P = ctypes.POINTER(HpDesc)
+_vp, _sz, _u32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32
+_lib.hp_workspace_bytes.restype = _sz
+_lib.hp_workspace_bytes.argtypes = [_P]
+_lib.hp_validate.restype = ctypes.c_int
+_lib.hp_validate.argtypes = [_P, _vp, _vp, _sz, ctypes.POINTER(HpValidateResult), _vp]
+_lib.hp_gather.restype = ctypes.c_int
+_lib.hp_gather.argtypes = [_P, _vp, _vp, _sz, _u32, _vp]
+_lib.hp_scatter.restype = ctypes.c_int
+_lib.hp_scatter.argtypes = [_P, _vp, _vp, _vp, _sz, _u32, _vp]
+_lib.hp_gather_dequant.restype = ctypes.c_int
+_lib.hp_gather_dequant.argtypes = [_P, _vp, _u32, _vp, _sz, _u32, _vp]
+_lib.hp_status_str.restype = ctypes.c_char_p
+_lib.hp_status_str.argtypes = [ctypes.c_int]
+
+
+def lib():
+    """The loaded ctypes library (raw C ABI)."""
+    return _lib
+
+
+def status_str(code):
+    return _lib.hp_status_str(int(code)).decode()
+
+
+class HpError(RuntimeError):
+    def __init__(self, code, where=""):
+        self.code = int(code)
+        self.name = STATUS.get(self.code, str(code))
+        super().__init__(f"{where}: {status_str(code)}" if where else status_str(code))
+
+
+def _check(code, where):
+    if code != 0:
+        raise HpError(code, where)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    table = {torch.int8: "i8", torch.uint8: "u8", torch.float16: "f16",
+             torch.bfloat16: "bf16", torch.float32: "f32", torch.float64: "f64"}
+    if t.dtype not in table:
+        raise TypeError(f"unsupported page_pool dtype {t.dtype}")
+    return DTYPE[table[t.dtype]]
+
+
+def _index_code(t):
+    torch = _torch()
+    if t.element_size() == 4 and t.dtype in (torch.int32, getattr(torch, "uint32", None)):
+        return HP_INDEX_U32
+    if t.element_size() == 8 and t.dtype in (torch.int64, getattr(torch, "uint64", None)):
+        return HP_INDEX_U64
+    raise TypeError(f"index tensors must be 32- or 64-bit integers, got {t.dtype}")
+
+
+class Descriptor:
+    """A block-paged descriptor over device tensors (kept alive here).
+
+    page_pool: [num_pages, page_size, num_heads, head_dim] tensor (or any
+    contiguous tensor of that many elements; then pass the geometry).
+    block_table / seq_ptr / seq_lens: int32 (uint32 semantics) or int64
+    tensors, all of the same width. scales: float32 [num_pages*page_size] or
+    None. The fields rank / paged_axis / byte_offset / has_shard default to
+    the only values the layout admits and exist so that a foreign descriptor
+    can be passed through unchanged and rejected by the library.
+    """
+
+    def __init__(self, page_pool, block_table, seq_ptr, seq_lens, *, page_size=None,
+                 num_heads=None, head_dim=None, num_pages=None, scales=None, rank=3,
+                 paged_axis=0, byte_offset=0, has_shard=0, kv_role=0, layer_index=0,
+                 index_type=None, dtype=None, num_block_entries=None):
+        if page_pool.dim() == 4:
+            n, p, h, d = page_pool.shape
+        else:
+            n = p = h = d = None
+        self.page_pool, self.block_table, self.seq_ptr = page_pool, block_table, seq_ptr
+        self.seq_lens, self.scales = seq_lens, scales
+        self.c = HpDesc()
+        c = self.c
+        c.rank, c.paged_axis = rank, paged_axis
+        c.index_type = _index_code(seq_ptr) if index_type is None else index_type
+        c.dtype = _dtype_code(page_pool) if dtype is None else dtype
+        c.page_size = page_size if page_size is not None else p
+        c.num_heads = num_heads if num_heads is not None else h
+        c.head_dim = head_dim if head_dim is not None else d
+        c.has_shard, c.kv_role, c.layer_index = has_shard, kv_role, layer_index
+        c.byte_offset = byte_offset
+        c.num_pages = num_pages if num_pages is not None else n
+        c.num_seqs = seq_ptr.numel() - 1
+        c.num_block_entries = (block_table.numel() if block_table is not None else 0) \
+            if num_block_entries is None else num_block_entries
+        c.total_tokens = 0
+        c.page_pool = _ptr(page_pool)
+        c.block_table = _ptr(block_table) if block_table is not None and block_table.numel() else None
+        c.seq_ptr = _ptr(seq_ptr)
+        c.seq_lens = _ptr(seq_lens) if seq_lens is not None and seq_lens.numel() else None
+        c.scales = _ptr(scales)
+
+    @property
+    def device(self):
+        return self.seq_ptr.device
+
+    def with_tokens(self, total_tokens):
+        self.c.total_tokens = int(total_tokens)
+        return ctypes.byref(self.c)
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def workspace_bytes(desc, total_tokens=0):
+    return int(_lib.hp_workspace_bytes(desc.with_tokens(total_tokens)))
+
+
+def _workspace(desc, total_tokens, workspace):
+    if workspace is not None:
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    n = workspace_bytes(desc, total_tokens)
+    if n == 0:
+        return None, 0
+    torch = _torch()
+    ws = torch.empty(n, dtype=torch.uint8, device=desc.device)
+    desc._ws = ws  # keep alive until the next call on this descriptor
+    return ws.data_ptr(), n
+
+
+def validate(desc, total_tokens, seq_start=None, *, workspace=None, stream=None):
+    """Runs hp_validate; returns (status name, index). Synchronous."""
+    res = HpValidateResult()
+    p = desc.with_tokens(total_tokens)
+    ws, n = _workspace(desc, total_tokens, workspace)
+    code = _lib.hp_validate(p, _ptr(seq_start), ws, n, ctypes.byref(res),
+                            _stream(stream, desc.device))
+    return STATUS.get(code, str(code)), int(res.index)
+
+
+def gather(desc, out, *, checked=False, workspace=None, stream=None):
+    """out[T, H, D] <- the logical tensor (T = out.shape[0])."""
+    T = out.shape[0]
+    p = desc.with_tokens(T)
+    ws, n = _workspace(desc, T, workspace)
+    _check(_lib.hp_gather(p, _ptr(out), ws, n, HP_FLAG_CHECKED if checked else 0,
+                          _stream(stream, desc.device)), "hp_gather")
+    return out
+
+
+def scatter(desc, src, seq_start=None, *, zero_tail=False, checked=False, workspace=None,
+            stream=None):
+    """Writes src[T, H, D] (T = src.shape[0]) into the pool."""
+    T = src.shape[0]
+    p = desc.with_tokens(T)
+    ws, n = _workspace(desc, T, workspace)
+    flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_ZERO_TAIL if zero_tail else 0)
+    _check(_lib.hp_scatter(p, _ptr(src), _ptr(seq_start), ws, n, flags,
+                           _stream(stream, desc.device)), "hp_scatter")
+
+
+def gather_dequant(desc, out, *, checked=False, workspace=None, stream=None):
+    """out[T, H, D] (bfloat16) <- dequantised logical tensor of an int8 pool."""
+    T = out.shape[0]
+    p = desc.with_tokens(T)
+    ws, n = _workspace(desc, T, workspace)
+    _check(_lib.hp_gather_dequant(p, _ptr(out), DTYPE["bf16"], ws, n,
+                                  HP_FLAG_CHECKED if checked else 0,
+                                  _stream(stream, desc.device)), "hp_gather_dequant")
+    return out

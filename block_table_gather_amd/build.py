@@ -1,0 +1,57 @@
+"""Build libhp.so (the C-ABI library of include/hp.h) for gfx950, in place.
+
+    python -m block_table_gather_amd.build [-v] [-DNAME=VALUE ...] [-o OUT]
+
+Extra -D definitions (HP_UNIT_BYTES, HP_UNITS_PER_GROUP) override the build
+time tuning knobs; -o writes the library elsewhere (used for tuning sweeps).
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+SOURCES = [os.path.join(CSRC, "hp_api.cpp"), os.path.join(CSRC, "hp_kernels.hip")]
+LIB = os.path.join(HERE, "libhp.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    # packed fp32 instructions stay off: the code relies on ordinary fp32 ops
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+    "-I", CSRC,
+]
+
+
+def build(verbose=False, defines=(), out=None):
+    out = out or LIB
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *defines, "-o", tmp]
+    for src in SOURCES:
+        if src.endswith(".hip"):
+            cmd += ["-x", "hip", src]
+        else:
+            cmd += ["-x", "hip", src]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    args = sys.argv[1:]
+    out = None
+    if "-o" in args:
+        i = args.index("-o")
+        out = args[i + 1]
+        del args[i: i + 2]
+    defs = [a for a in args if a.startswith("-D")]
+    print(build(verbose="-v" in args, defines=defs, out=out))

@@ -1,0 +1,369 @@
+// hp_api.cpp -- the C ABI of include/hp.h: host-side argument checks, launch
+// planning and the synchronous validator. Everything that touches data runs
+// in the kernels of hp_kernels.hip.
+#include "hp.h"
+#include "hp_internal.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// Tuning knobs, fixed at build time.
+#ifndef HP_UNIT_BYTES
+#define HP_UNIT_BYTES hp::kDefaultUnitBytes
+#endif
+#ifndef HP_UNITS_PER_GROUP
+#define HP_UNITS_PER_GROUP hp::kDefaultUnitsPerGroup
+#endif
+
+namespace {
+
+constexpr uint64_t kValidateBytes = 256;  // workspace head: validator key + sum
+constexpr uint64_t kMaxIndex = (1ull << hp::kKeyShift) - 1;
+
+uint32_t elem_bytes_of(uint32_t dtype) {
+    switch (dtype) {
+    case HP_DTYPE_I8:
+    case HP_DTYPE_U8: return 1;
+    case HP_DTYPE_F16:
+    case HP_DTYPE_BF16: return 2;
+    case HP_DTYPE_F32: return 4;
+    case HP_DTYPE_F64: return 8;
+    default: return 0;
+    }
+}
+
+bool aligned(const void *p, uint64_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool mul(uint64_t a, uint64_t b, uint64_t *r) { return !__builtin_mul_overflow(a, b, r); }
+
+struct Geometry {
+    uint32_t elem_bytes, idx_bytes;
+    uint64_t row_bytes, pool_bytes;
+};
+
+// Checks shared by every call ([Hurray] Description: rank 3; Logical Shape /
+// invariant 6: paged_axis 0; Sharding: no shard descriptor; byte_offset: 0;
+// Additional Descriptor Fields: uint32 tables address at most 2^32 pages;
+// Alignment: descriptor buffers at least 64-byte aligned).
+hp_status check_desc(const hp_desc *d, Geometry *g) {
+    if (!d)
+        return HP_ERR_NULL;
+    if (d->rank != 3)
+        return HP_ERR_RANK;
+    if (d->paged_axis != 0)
+        return HP_ERR_PAGED_AXIS;
+    if (d->has_shard)
+        return HP_ERR_SHARDED;
+    if (d->index_type != HP_INDEX_U32 && d->index_type != HP_INDEX_U64)
+        return HP_ERR_INDEX_TYPE;
+    g->elem_bytes = elem_bytes_of(d->dtype);
+    if (!g->elem_bytes)
+        return HP_ERR_DTYPE;
+    g->idx_bytes = d->index_type == HP_INDEX_U32 ? 4 : 8;
+    if (d->byte_offset != 0)
+        return HP_ERR_ARG;
+    if (!d->page_size || !d->num_heads || !d->head_dim)
+        return HP_ERR_ARG;
+    uint64_t hd, tmp;
+    if (!mul(d->num_heads, d->head_dim, &hd) || !mul(hd, g->elem_bytes, &g->row_bytes))
+        return HP_ERR_ARG;
+    // Inner offsets of one work unit are 32-bit; a row must leave room for
+    // the dequant output (2 bytes per element) below 2^31.
+    if (hd * 2 >= (1ull << 31) || g->row_bytes >= (1ull << 31))
+        return HP_ERR_ARG;
+    if (!mul(d->num_pages, d->page_size, &tmp) || !mul(tmp, g->row_bytes, &g->pool_bytes))
+        return HP_ERR_ARG;
+    if (!mul(d->num_block_entries, d->page_size, &tmp))
+        return HP_ERR_ARG;
+    if (!mul(d->total_tokens, hd * 2 > g->row_bytes ? hd * 2 : g->row_bytes, &tmp))
+        return HP_ERR_ARG;
+    if (d->num_seqs >= kMaxIndex || d->num_block_entries >= kMaxIndex)
+        return HP_ERR_ARG;
+    if (d->num_seqs >= (1ull << 32))
+        return HP_ERR_ARG;
+    if (d->index_type == HP_INDEX_U32 &&
+        (d->num_pages > (1ull << 32) || d->num_block_entries > 0xffffffffull))
+        return HP_ERR_INDEX_TYPE;
+    if (!d->seq_ptr)
+        return HP_ERR_NULL;
+    if (d->num_block_entries && !d->block_table)
+        return HP_ERR_NULL;
+    if (d->num_seqs && !d->seq_lens)
+        return HP_ERR_NULL;
+    if (d->num_pages && !d->page_pool)
+        return HP_ERR_NULL;
+    if (!aligned(d->page_pool, 64) || !aligned(d->block_table, 64) ||
+        !aligned(d->seq_ptr, 64) || !aligned(d->scales, 64) ||
+        !aligned(d->seq_lens, g->idx_bytes))
+        return HP_ERR_ALIGN;
+    return HP_OK;
+}
+
+bool overlaps(const void *a, uint64_t an, const void *b, uint64_t bn) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return an && bn && x < y + bn && y < x + an;
+}
+
+hp_status check_workspace(const void *ws, size_t have, uint64_t need) {
+    if (!need)
+        return HP_OK;
+    if (!ws || have < need)
+        return HP_ERR_WORKSPACE;
+    if (!aligned(ws, 8))
+        return HP_ERR_ALIGN;
+    return HP_OK;
+}
+
+uint64_t plan_bytes(const hp_desc *d) {
+    return d->num_seqs > hp::kFusedMaxSeqs ? hp::plan_workspace_bytes(d->num_seqs) : 0;
+}
+
+hp_status run_validate(const hp_desc *d, const void *seq_start, void *ws,
+                       hp_validate_result *res, hipStream_t stream) {
+    hp::ValidateJob j;
+    j.idx64 = d->index_type == HP_INDEX_U64;
+    j.num_pages = d->num_pages;
+    j.page_size = d->page_size;
+    j.num_seqs = d->num_seqs;
+    j.num_block_entries = d->num_block_entries;
+    j.block_table = d->block_table;
+    j.seq_ptr = d->seq_ptr;
+    j.seq_lens = d->seq_lens;
+    j.seq_start = seq_start;
+    j.workspace = ws;
+    if (hp::launch_validate(j, stream) != hipSuccess)
+        return HP_ERR_HIP;
+    uint64_t host[2] = {0, 0};
+    if (hipMemcpyAsync(host, ws, sizeof host, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return HP_ERR_HIP;
+    res->code = HP_OK;
+    res->index = 0;
+    if (host[0] != ~0ull) {
+        static const hp_status by_rank[] = {HP_OK, HP_ERR_SEQPTR_FIRST, HP_ERR_SEQPTR_LAST,
+                                            HP_ERR_SEQPTR_ORDER, HP_ERR_PAGE_RANGE,
+                                            HP_ERR_SEQ_LEN};
+        const uint64_t rank = host[0] >> hp::kKeyShift;
+        res->code = rank >= 1 && rank <= 5 ? by_rank[rank] : HP_ERR_HIP;
+        res->index = host[0] & kMaxIndex;
+    } else if (host[1] != d->total_tokens) {
+        res->code = HP_ERR_TOTAL_TOKENS;
+    }
+    return (hp_status)res->code;
+}
+
+// Largest divisor of P whose run of rows fits the target unit size (at least
+// 1, at most `cap`).
+uint32_t rows_per_unit(uint32_t P, uint64_t row_bytes, uint32_t cap) {
+    uint64_t want = HP_UNIT_BYTES / (row_bytes ? row_bytes : 1);
+    if (want < 1)
+        want = 1;
+    if (want > cap)
+        want = cap;
+    if (want > P)
+        want = P;
+    for (uint32_t r = (uint32_t)want; r > 1; --r)
+        if (P % r == 0)
+            return r;
+    return 1;
+}
+
+uint32_t widest_vec(uint64_t row_bytes, const void *a, const void *b, uint32_t maxv) {
+    for (uint32_t v = maxv; v > 1; v >>= 1)
+        if (row_bytes % v == 0 && aligned(a, v) && aligned(b, v))
+            return v;
+    return 1;
+}
+
+hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const void *src, void *out,
+                 const void *seq_start, bool zero_tail, void *ws, hipStream_t stream) {
+    hp::CopyJob j = {};
+    j.op = op;
+    j.idx64 = d->index_type == HP_INDEX_U64;
+    j.zero_tail = zero_tail;
+    j.elem_bytes = g.elem_bytes;
+    j.page_size = d->page_size;
+    j.num_seqs = d->num_seqs;
+    j.total_tokens = d->total_tokens;
+    j.row_bytes = g.row_bytes;
+    j.out_row_bytes = op == hp::Op::Dequant ? g.row_bytes * 2 : g.row_bytes;
+    const uint64_t rmax = j.out_row_bytes > j.row_bytes ? j.out_row_bytes : j.row_bytes;
+    j.rows_per_unit = rows_per_unit(d->page_size, rmax, op == hp::Op::Dequant ? 64 : 0xffffffffu);
+    j.units_per_group = HP_UNITS_PER_GROUP;
+    const uint64_t rpc = j.rows_per_unit;
+    const uint64_t upp = d->page_size / rpc;
+    // Upper bound on the number of units, from host-known T and S only.
+    if (op == hp::Op::Scatter)
+        j.unit_bound = d->total_tokens / rpc + d->num_seqs * (2 + (zero_tail ? upp : 0));
+    else
+        j.unit_bound = d->total_tokens / rpc + d->num_seqs;
+    if (j.unit_bound >= (1ull << 32) - HP_UNITS_PER_GROUP)
+        return HP_ERR_ARG;
+    j.pool = d->page_pool;
+    j.pool_w = d->page_pool;
+    j.block_table = d->block_table;
+    j.seq_ptr = d->seq_ptr;
+    j.seq_lens = d->seq_lens;
+    j.seq_start = seq_start;
+    j.scales = d->scales;
+    j.src = src;
+    j.out = out;
+    j.workspace = ws ? static_cast<unsigned char *>(ws) + kValidateBytes : nullptr;
+    if (op == hp::Op::Dequant)
+        j.vec_bytes = widest_vec(g.row_bytes, d->page_pool, d->page_pool, 8);
+    else
+        j.vec_bytes = widest_vec(g.row_bytes, d->page_pool, op == hp::Op::Scatter ? src : out, 16);
+    if (op == hp::Op::Dequant && !aligned(out, 2 * (uint64_t)j.vec_bytes))
+        j.vec_bytes = 1;  // out is 2-byte aligned; 1-byte input vectors write 2 bytes
+    return hp::launch_copy(j, stream) == hipSuccess ? HP_OK : HP_ERR_HIP;
+}
+
+// Common front half of gather / scatter / dequant, after the descriptor and
+// the call's own buffers were checked: flags, workspace, optional
+// validation. *done is set when nothing is left to do.
+hp_status prologue(const hp_desc *d, const Geometry &g, uint32_t flags, uint32_t allowed,
+                   const void *seq_start, void *ws, size_t ws_bytes, hipStream_t stream,
+                   bool *done) {
+    *done = false;
+    if (flags & ~allowed)
+        return HP_ERR_ARG;
+    if (!aligned(seq_start, g.idx_bytes))
+        return HP_ERR_ALIGN;
+    const bool checked = flags & HP_FLAG_CHECKED;
+    const bool fused = d->num_seqs <= hp::kFusedMaxSeqs;
+    const uint64_t need = (checked || !fused) ? kValidateBytes + plan_bytes(d) : 0;
+    hp_status st = check_workspace(ws, ws_bytes, need);
+    if (st != HP_OK)
+        return st;
+    if (checked) {
+        hp_validate_result r;
+        st = run_validate(d, seq_start, ws, &r, stream);
+        if (st != HP_OK)
+            return st;
+    }
+    *done = d->num_seqs == 0 || d->total_tokens == 0;
+    return HP_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+size_t hp_workspace_bytes(const hp_desc *desc) {
+    Geometry g;
+    if (check_desc(desc, &g) != HP_OK)
+        return 0;
+    return (size_t)(kValidateBytes + plan_bytes(desc));
+}
+
+hp_status hp_validate(const hp_desc *desc, const void *seq_start, void *workspace,
+                      size_t workspace_bytes, hp_validate_result *result, void *stream) {
+    hp_validate_result local;
+    hp_validate_result *res = result ? result : &local;
+    res->code = HP_OK;
+    res->reserved = 0;
+    res->index = 0;
+    Geometry g;
+    hp_status st = check_desc(desc, &g);
+    if (st == HP_OK && !aligned(seq_start, g.idx_bytes))
+        st = HP_ERR_ALIGN;
+    if (st == HP_OK)
+        st = check_workspace(workspace, workspace_bytes, kValidateBytes);
+    if (st != HP_OK) {
+        res->code = st;
+        return st;
+    }
+    return run_validate(desc, seq_start, workspace, res, (hipStream_t)stream);
+}
+
+hp_status hp_gather(const hp_desc *desc, void *out, void *workspace, size_t workspace_bytes,
+                    uint32_t flags, void *stream) {
+    Geometry g;
+    bool done;
+    hp_status st = check_desc(desc, &g);
+    if (st != HP_OK)
+        return st;
+    if (desc->total_tokens && !out)
+        return HP_ERR_NULL;
+    if (!aligned(out, g.elem_bytes))
+        return HP_ERR_ALIGN;
+    if (overlaps(out, desc->total_tokens * g.row_bytes, desc->page_pool, g.pool_bytes))
+        return HP_ERR_ARG;
+    st = prologue(desc, g, flags, HP_FLAG_CHECKED, nullptr, workspace, workspace_bytes,
+                  (hipStream_t)stream, &done);
+    if (st != HP_OK || done)
+        return st;
+    return launch(desc, g, hp::Op::Gather, nullptr, out, nullptr, false, workspace,
+                  (hipStream_t)stream);
+}
+
+hp_status hp_scatter(const hp_desc *desc, const void *src, const void *seq_start,
+                     void *workspace, size_t workspace_bytes, uint32_t flags, void *stream) {
+    Geometry g;
+    bool done;
+    hp_status st = check_desc(desc, &g);
+    if (st != HP_OK)
+        return st;
+    if (desc->total_tokens && !src)
+        return HP_ERR_NULL;
+    if (!aligned(src, g.elem_bytes))
+        return HP_ERR_ALIGN;
+    if (overlaps(src, desc->total_tokens * g.row_bytes, desc->page_pool, g.pool_bytes))
+        return HP_ERR_ARG;
+    st = prologue(desc, g, flags, HP_FLAG_CHECKED | HP_FLAG_ZERO_TAIL, seq_start, workspace,
+                  workspace_bytes, (hipStream_t)stream, &done);
+    if (st != HP_OK || done)
+        return st;
+    return launch(desc, g, hp::Op::Scatter, src, nullptr, seq_start,
+                  (flags & HP_FLAG_ZERO_TAIL) != 0, workspace, (hipStream_t)stream);
+}
+
+hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype, void *workspace,
+                            size_t workspace_bytes, uint32_t flags, void *stream) {
+    Geometry g;
+    bool done;
+    hp_status st = check_desc(desc, &g);
+    if (st != HP_OK)
+        return st;
+    if (desc->dtype != HP_DTYPE_I8 || out_dtype != HP_DTYPE_BF16)
+        return HP_ERR_DTYPE;
+    if (!desc->scales || (desc->total_tokens && !out))
+        return HP_ERR_NULL;
+    if (!aligned(out, 2))
+        return HP_ERR_ALIGN;
+    const uint64_t out_bytes = desc->total_tokens * g.row_bytes * 2;
+    if (overlaps(out, out_bytes, desc->page_pool, g.pool_bytes) ||
+        overlaps(out, out_bytes, desc->scales, desc->num_pages * desc->page_size * 4))
+        return HP_ERR_ARG;
+    st = prologue(desc, g, flags, HP_FLAG_CHECKED, nullptr, workspace, workspace_bytes,
+                  (hipStream_t)stream, &done);
+    if (st != HP_OK || done)
+        return st;
+    return launch(desc, g, hp::Op::Dequant, nullptr, out, nullptr, false, workspace,
+                  (hipStream_t)stream);
+}
+
+const char *hp_status_str(int status) {
+    switch (status) {
+    case HP_OK: return "HP_OK";
+    case HP_ERR_NULL: return "HP_ERR_NULL: a required pointer is NULL";
+    case HP_ERR_ARG: return "HP_ERR_ARG: invalid size, field or flag";
+    case HP_ERR_RANK: return "HP_ERR_RANK: block-paged requires rank 3";
+    case HP_ERR_PAGED_AXIS: return "HP_ERR_PAGED_AXIS: paged_axis must be 0";
+    case HP_ERR_INDEX_TYPE: return "HP_ERR_INDEX_TYPE: unknown or too narrow index type";
+    case HP_ERR_DTYPE: return "HP_ERR_DTYPE: unsupported element type";
+    case HP_ERR_ALIGN: return "HP_ERR_ALIGN: buffer misaligned";
+    case HP_ERR_WORKSPACE: return "HP_ERR_WORKSPACE: workspace missing or too small";
+    case HP_ERR_SHARDED: return "HP_ERR_SHARDED: block-paged tensors cannot be sharded";
+    case HP_ERR_SEQPTR_FIRST: return "HP_ERR_SEQPTR_FIRST: seq_ptr[0] != 0";
+    case HP_ERR_SEQPTR_LAST: return "HP_ERR_SEQPTR_LAST: seq_ptr[num_seqs] != block_table length";
+    case HP_ERR_SEQPTR_ORDER: return "HP_ERR_SEQPTR_ORDER: seq_ptr decreases";
+    case HP_ERR_PAGE_RANGE: return "HP_ERR_PAGE_RANGE: page ID out of range";
+    case HP_ERR_SEQ_LEN: return "HP_ERR_SEQ_LEN: token count exceeds the sequence's pages";
+    case HP_ERR_TOTAL_TOKENS: return "HP_ERR_TOTAL_TOKENS: seq_lens do not sum to total_tokens";
+    case HP_ERR_HIP: return "HP_ERR_HIP: HIP runtime or launch failure";
+    default: return "unknown hp_status";
+    }
+}
+
+} // extern "C"

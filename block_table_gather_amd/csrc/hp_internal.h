@@ -1,0 +1,72 @@
+// hp_internal.h -- what the C-ABI layer (hp_api.cpp) hands to the kernel
+// launchers (hp_kernels.hip). Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hp {
+
+// Sequences whose per-sequence offsets fit in LDS: up to this many, every
+// workgroup rebuilds the offsets itself (one fused launch); beyond it a plan
+// pass writes them to the workspace first.
+constexpr uint64_t kFusedMaxSeqs = 4096;
+constexpr uint32_t kThreads = 256;            // threads per copy workgroup
+constexpr uint32_t kPlanChunk = kThreads * 8; // sequences per plan workgroup
+constexpr uint32_t kDefaultUnitBytes = 32768; // target bytes moved per work unit
+constexpr uint32_t kDefaultUnitsPerGroup = 4; // work units per workgroup
+
+enum class Op : int { Gather = 0, Scatter = 1, Dequant = 2 };
+
+// Everything a copy launch needs; filled and checked on the host.
+struct CopyJob {
+    Op op;
+    bool idx64;             // index type is uint64
+    bool zero_tail;         // scatter only
+    uint32_t elem_bytes;    // pool element width
+    uint32_t page_size;     // P
+    uint32_t rows_per_unit; // divides P
+    uint32_t units_per_group;
+    uint64_t num_seqs;      // S
+    uint64_t total_tokens;  // T
+    uint64_t row_bytes;     // H*D*elem_bytes (pool side)
+    uint64_t out_row_bytes; // logical-tensor side (dequant: H*D*2)
+    uint64_t unit_bound;    // host upper bound on the number of work units
+    const void *pool;       // gather/dequant: read; scatter: written
+    void *pool_w;
+    const void *block_table;
+    const void *seq_ptr;
+    const void *seq_lens;
+    const void *seq_start;  // scatter, may be null
+    const float *scales;    // dequant
+    const void *src;        // scatter rows
+    void *out;              // gather/dequant rows
+    void *workspace;        // plan arrays when num_seqs > kFusedMaxSeqs
+    uint32_t vec_bytes;     // widest vector width every span allows
+};
+
+struct ValidateJob {
+    bool idx64;
+    uint64_t num_pages, page_size, num_seqs, num_block_entries;
+    const void *block_table, *seq_ptr, *seq_lens, *seq_start;
+    void *workspace; // >= 16 bytes: [0] min key, [1] token sum
+};
+
+// Workspace layout for the plan arrays (num_seqs > kFusedMaxSeqs).
+uint64_t plan_workspace_bytes(uint64_t num_seqs);
+
+hipError_t launch_copy(const CopyJob &job, hipStream_t stream);
+hipError_t launch_validate(const ValidateJob &job, hipStream_t stream);
+
+// Key layout of the validator's atomicMin: check rank in the top byte,
+// failing index below it.
+constexpr int kKeyShift = 56;
+enum CheckRank : uint64_t {
+    kRankSeqPtrFirst = 1,
+    kRankSeqPtrLast = 2,
+    kRankSeqPtrOrder = 3,
+    kRankPageRange = 4,
+    kRankSeqLen = 5,
+};
+
+} // namespace hp

@@ -1,0 +1,655 @@
+// hp_kernels.hip -- gfx950 kernels for the block-paged KV layout.
+//
+// Source of the arithmetic: "Block-Paged Layout -- Hurray Format
+// Specification", sections Element Lookup (address of token t of sequence s),
+// Logical Shape (the ragged tensor is the sequences' tokens concatenated in
+// order), Partial trailing page (nothing past a sequence's count is read; a
+// writer should zero the unused slots), Per-page-slot parameters (one scale
+// per physical page slot) and Storage Invariants (what a reader validates).
+//
+// Design (one GPU, HBM-bound, nothing is a contraction so no MFMA):
+//  * A page of the interchange layout [N, P, H, D] is one contiguous span of
+//    P*R bytes (R = H*D*elem bytes), and so is a run of consecutive tokens of
+//    one sequence inside one page, on both sides of the move. The work unit
+//    is such a run: `rows_per_unit` consecutive tokens (a divisor of P, so a
+//    unit never crosses a page), i.e. one block-table entry and one
+//    contiguous span of up to ~32 KB.
+//  * Work units are numbered sequence by sequence. Each workgroup owns
+//    `units_per_group` consecutive units. To map a unit to its sequence it
+//    needs, per sequence, the running unit count and the running token count
+//    (the row where the sequence starts in the logical tensor). Up to
+//    kFusedMaxSeqs sequences every workgroup rebuilds both prefix sums in LDS
+//    from the token counts (a 64-lane shuffle scan per wave, wave totals
+//    combined through LDS), so one launch does everything; above it, a plan
+//    pass writes them to the workspace and the copy kernel reads them there.
+//  * The block-table entry of a unit is read once per unit into a scalar
+//    register; the sequence's scalars are reloaded only when the walk moves
+//    to the next sequence.
+//  * Copies are 16-byte vector loads and non-temporal 16-byte vector stores,
+//    unrolled so each lane keeps several loads in flight; narrower vectors
+//    are used only when a row size or pointer forbids 16 bytes.
+//  * Dequant reads 8 int8 values per lane and writes 8 bf16 values (16 B) per
+//    lane, so both sides stay fully coalesced; the unit's per-slot scales sit
+//    one per lane and are fetched with a cross-lane shuffle.
+#include "hp_internal.h"
+
+#include <stdint.h>
+
+namespace hp {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int B> struct Vec;
+template <> struct Vec<16> { using T = u32x4; };
+template <> struct Vec<8> { using T = u32x2; };
+template <> struct Vec<4> { using T = uint32_t; };
+template <> struct Vec<2> { using T = uint16_t; };
+template <> struct Vec<1> { using T = uint8_t; };
+
+constexpr int kCopyUnroll = 8;
+constexpr int kDequantUnroll = 8;
+
+// Device-side view of a launch. Offsets inside one unit are 32-bit (the host
+// guarantees rows_per_unit * row bytes < 2^31); page and row bases are 64-bit.
+struct Args {
+    const unsigned char *pool_r;
+    unsigned char *pool_w;
+    const void *block_table;
+    const void *seq_ptr;
+    const void *seq_lens;
+    const void *seq_start;
+    const float *scales;
+    const unsigned char *src;
+    unsigned char *out;
+    const uint32_t *g_unit_end;  // plan arrays (non-fused launches)
+    const uint64_t *g_tok_begin;
+    uint64_t *partials;
+    uint32_t num_seqs;
+    uint32_t page_size;
+    uint32_t rows_per_unit;
+    uint32_t units_per_page;  // page_size / rows_per_unit
+    uint32_t units_per_group;
+    uint32_t row_bytes;       // pool row
+    uint32_t out_row_bytes;   // logical-tensor row
+    uint32_t zero_tail;
+    uint32_t vecs_per_row;    // dequant: input vectors per row
+    uint32_t vpr_mul, vpr_shift;  // x / vecs_per_row = (umulhi(x, mul) + x) >> shift
+};
+
+__device__ __forceinline__ uint64_t min64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint32_t min32(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ uint32_t uni(uint32_t x) {
+    return __builtin_amdgcn_readfirstlane(x);
+}
+__device__ __forceinline__ uint64_t uni64(uint64_t x) {
+    uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <typename IdxT>
+__device__ __forceinline__ uint64_t ld_idx(const void *p, uint64_t i) {
+    return (uint64_t)static_cast<const IdxT *>(p)[i];
+}
+
+// Units (token runs) of sequence s. Gather/dequant: ceil(L / rpc) runs
+// starting at token 0. Scatter: the rpc-aligned windows of positions
+// [start, start + L), extended to the end of the last page when the tail is
+// zeroed.
+template <Op OP>
+__device__ __forceinline__ uint64_t units_of(const Args &a, uint64_t len, uint64_t start) {
+    const uint64_t rpc = a.rows_per_unit;
+    if (OP != Op::Scatter)
+        return (len + rpc - 1) / rpc;
+    if (len == 0)
+        return 0;
+    const uint64_t end = start + len;
+    const uint64_t w0 = start / rpc;
+    const uint64_t w1 = a.zero_tail
+        ? (end + a.page_size - 1) / a.page_size * a.units_per_page
+        : (end + rpc - 1) / rpc;
+    return w1 - w0;
+}
+
+// Exclusive scan of (units, tokens) over the workgroup's threads. Returns the
+// thread's exclusive prefix; `total_*` receives the workgroup totals.
+__device__ __forceinline__ void group_exclusive_scan(uint64_t &u, uint64_t &t,
+                                                     uint64_t &total_u, uint64_t &total_t) {
+    __shared__ uint64_t wave_u[kThreads / 64], wave_t[kThreads / 64];
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t ui = u, ti = t;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        uint64_t un = __shfl_up(ui, d, 64);
+        uint64_t tn = __shfl_up(ti, d, 64);
+        if (lane >= (uint32_t)d) {
+            ui += un;
+            ti += tn;
+        }
+    }
+    if (lane == 63) {
+        wave_u[wave] = ui;
+        wave_t[wave] = ti;
+    }
+    __syncthreads();
+    uint64_t bu = 0, bt = 0;
+    total_u = 0;
+    total_t = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < kThreads / 64; ++w) {
+        if (w < wave) {
+            bu += wave_u[w];
+            bt += wave_t[w];
+        }
+        total_u += wave_u[w];
+        total_t += wave_t[w];
+    }
+    u = bu + ui - u;
+    t = bt + ti - t;
+    __syncthreads();  // wave_u / wave_t may be reused by the next scan
+}
+
+// Writes unit_end[s] (inclusive running unit count) and tok_begin[s]
+// (exclusive running token count) for s in [s0, s1), starting from the given
+// bases. Each thread takes a contiguous run of ceil((s1-s0)/kThreads)
+// sequences. Ends with a barrier.
+template <typename IdxT, Op OP, typename UE, typename TB>
+__device__ __forceinline__ void scan_range(const Args &a, uint32_t s0, uint32_t s1,
+                                           uint64_t ubase, uint64_t tbase, UE *unit_end,
+                                           TB *tok_begin) {
+    const uint32_t n = s1 - s0;
+    const uint32_t per = (n + kThreads - 1) / kThreads;
+    const uint32_t i0 = s0 + min32(n, threadIdx.x * per);
+    const uint32_t i1 = s0 + min32(n, (threadIdx.x + 1) * per);
+    uint64_t u = 0, t = 0;
+    for (uint32_t i = i0; i < i1; ++i) {
+        const uint64_t len = ld_idx<IdxT>(a.seq_lens, i);
+        const uint64_t st = (OP == Op::Scatter && a.seq_start) ? ld_idx<IdxT>(a.seq_start, i) : 0;
+        u += units_of<OP>(a, len, st);
+        t += len;
+    }
+    uint64_t tu, tt;
+    group_exclusive_scan(u, t, tu, tt);
+    u += ubase;
+    t += tbase;
+    for (uint32_t i = i0; i < i1; ++i) {
+        const uint64_t len = ld_idx<IdxT>(a.seq_lens, i);
+        const uint64_t st = (OP == Op::Scatter && a.seq_start) ? ld_idx<IdxT>(a.seq_start, i) : 0;
+        u += units_of<OP>(a, len, st);
+        unit_end[i] = (UE)u;
+        tok_begin[i] = (TB)t;
+        t += len;
+    }
+    __syncthreads();
+}
+
+// ---- span movers -------------------------------------------------------------
+
+template <int VEC>
+__device__ __forceinline__ void copy_span(const unsigned char *__restrict__ src,
+                                          unsigned char *__restrict__ dst, uint32_t nbytes) {
+    using V = typename Vec<VEC>::T;
+    const V *s = reinterpret_cast<const V *>(src);
+    V *d = reinterpret_cast<V *>(dst);
+    const uint32_t n = nbytes / VEC;
+    for (uint32_t base = threadIdx.x; base < n; base += kThreads * kCopyUnroll) {
+        V tmp[kCopyUnroll];
+#pragma unroll
+        for (int j = 0; j < kCopyUnroll; ++j) {
+            const uint32_t i = base + j * kThreads;
+            if (i < n)
+                tmp[j] = s[i];
+        }
+#pragma unroll
+        for (int j = 0; j < kCopyUnroll; ++j) {
+            const uint32_t i = base + j * kThreads;
+            if (i < n)
+                __builtin_nontemporal_store(tmp[j], d + i);
+        }
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void zero_span(unsigned char *__restrict__ dst, uint32_t nbytes) {
+    using V = typename Vec<VEC>::T;
+    V *d = reinterpret_cast<V *>(dst);
+    const uint32_t n = nbytes / VEC;
+    const V z = V(0);
+    for (uint32_t i = threadIdx.x; i < n; i += kThreads)
+        __builtin_nontemporal_store(z, d + i);
+}
+
+// fp32 -> bf16 bits, round to nearest even (gfx950 has a hardware
+// conversion with IEEE rounding for this type).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+    __bf16 a = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, a);
+}
+__device__ __forceinline__ float sbyte(uint32_t w, int k) {
+    return (float)(int8_t)(w >> (8 * k));
+}
+
+// Dequantises `rows` rows of R_in int8 values into bf16. `scale_row` points at
+// the scale of the unit's first slot; rows <= 64, so lane r holds row r's
+// scale and every lane fetches its row's scale from that lane.
+template <int VIN>
+__device__ __forceinline__ void dequant_span(const Args &a, const unsigned char *__restrict__ src,
+                                             const float *__restrict__ scale_row,
+                                             unsigned char *__restrict__ dst, uint32_t rows) {
+    using VI = typename Vec<VIN>::T;
+    const uint32_t lane = threadIdx.x & 63;
+    const float my_scale = lane < rows ? scale_row[lane] : 0.0f;
+    const uint32_t n = rows * a.vecs_per_row;
+    const VI *s = reinterpret_cast<const VI *>(src);
+    // The trip count is the same for every lane: the shuffle below reads the
+    // scale from another lane, which must still be active.
+    for (uint32_t b0 = 0; b0 < n; b0 += kThreads * kDequantUnroll) {
+        const uint32_t base = b0 + threadIdx.x;
+        VI q[kDequantUnroll];
+#pragma unroll
+        for (int j = 0; j < kDequantUnroll; ++j) {
+            const uint32_t i = base + j * kThreads;
+            if (i < n)
+                q[j] = s[i];
+        }
+#pragma unroll
+        for (int j = 0; j < kDequantUnroll; ++j) {
+            const uint32_t i = base + j * kThreads;
+            const uint32_t row = (__umulhi(i, a.vpr_mul) + i) >> a.vpr_shift;
+            const float sc = __shfl(my_scale, (int)row, 64);
+            if (i < n) {
+                if constexpr (VIN == 8) {
+                    const u32x2 w = q[j];
+                    u32x4 o;
+                    o.x = pack_bf16x2(sbyte(w.x, 0) * sc, sbyte(w.x, 1) * sc);
+                    o.y = pack_bf16x2(sbyte(w.x, 2) * sc, sbyte(w.x, 3) * sc);
+                    o.z = pack_bf16x2(sbyte(w.y, 0) * sc, sbyte(w.y, 1) * sc);
+                    o.w = pack_bf16x2(sbyte(w.y, 2) * sc, sbyte(w.y, 3) * sc);
+                    __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(dst) + i);
+                } else if constexpr (VIN == 4) {
+                    const uint32_t w = q[j];
+                    u32x2 o;
+                    o.x = pack_bf16x2(sbyte(w, 0) * sc, sbyte(w, 1) * sc);
+                    o.y = pack_bf16x2(sbyte(w, 2) * sc, sbyte(w, 3) * sc);
+                    __builtin_nontemporal_store(o, reinterpret_cast<u32x2 *>(dst) + i);
+                } else if constexpr (VIN == 2) {
+                    const uint32_t w = q[j];
+                    const uint32_t o = pack_bf16x2(sbyte(w, 0) * sc, sbyte(w, 1) * sc);
+                    __builtin_nontemporal_store(o, reinterpret_cast<uint32_t *>(dst) + i);
+                } else {
+                    const uint16_t o = to_bf16(sbyte(q[j], 0) * sc);
+                    __builtin_nontemporal_store(o, reinterpret_cast<uint16_t *>(dst) + i);
+                }
+            }
+        }
+    }
+}
+
+// ---- the copy kernel -----------------------------------------------------------
+
+// One kernel for all three moves. FUSED: per-sequence offsets rebuilt in LDS
+// (dynamic LDS = 8*S + 4*S bytes); otherwise read from the plan arrays.
+template <typename IdxT, Op OP, int VEC, bool FUSED>
+__global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const uint32_t S = a.num_seqs;
+    const uint32_t *unit_end;
+    const uint64_t *tok_begin;
+    if constexpr (FUSED) {
+        uint64_t *tb = reinterpret_cast<uint64_t *>(lds);
+        uint32_t *ue = reinterpret_cast<uint32_t *>(lds + 8 * (size_t)S);
+        scan_range<IdxT, OP>(a, 0, S, 0, 0, ue, tb);
+        unit_end = ue;
+        tok_begin = tb;
+    } else {
+        unit_end = a.g_unit_end;
+        tok_begin = a.g_tok_begin;
+    }
+    const uint32_t total = uni(unit_end[S - 1]);
+    const uint32_t g0 = blockIdx.x * a.units_per_group;
+    if (g0 >= total)
+        return;
+    const uint32_t g1 = min32(g0 + a.units_per_group, total);
+
+    // First sequence whose units reach past g0.
+    uint32_t lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (unit_end[mid] > g0)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    uint32_t s = uni(lo);
+
+    const uint32_t P = a.page_size, rpc = a.rows_per_unit;
+    uint32_t ubeg = 0, uend = 0;
+    uint64_t len = 0, sp = 0, start = 0, tb = 0;
+    auto load_seq = [&](uint32_t q) {
+        ubeg = q ? uni(unit_end[q - 1]) : 0;
+        uend = uni(unit_end[q]);
+        tb = uni64(tok_begin[q]);
+        len = uni64(ld_idx<IdxT>(a.seq_lens, q));
+        sp = uni64(ld_idx<IdxT>(a.seq_ptr, q));
+        start = (OP == Op::Scatter && a.seq_start) ? uni64(ld_idx<IdxT>(a.seq_start, q)) : 0;
+    };
+    load_seq(s);
+
+    for (uint32_t g = g0; g < g1; ++g) {
+        while (g >= uend) {
+            ++s;
+            load_seq(s);
+        }
+        const uint32_t u = g - ubeg;
+        if constexpr (OP == Op::Scatter) {
+            // Window w of absolute positions [w*rpc, (w+1)*rpc) of sequence s.
+            const uint64_t w = start / rpc + u;
+            const uint64_t pos0 = w * rpc;
+            const uint64_t q = w / a.units_per_page;
+            const uint32_t slot0 = (uint32_t)(pos0 - q * P);
+            const uint64_t phys = uni64(ld_idx<IdxT>(a.block_table, sp + q));
+            const uint64_t end = start + len;
+            unsigned char *page = a.pool_w + phys * P * a.row_bytes;
+            const uint64_t wa = pos0 > start ? pos0 : start;
+            const uint64_t wb = pos0 + rpc < end ? pos0 + rpc : end;
+            if (wa < wb) {
+                const unsigned char *from = a.src + (tb + (wa - start)) * a.row_bytes;
+                copy_span<VEC>(from, page + (slot0 + (uint32_t)(wa - pos0)) * a.row_bytes,
+                               (uint32_t)(wb - wa) * a.row_bytes);
+            }
+            if (a.zero_tail) {
+                const uint64_t zend = (end + P - 1) / P * P;
+                const uint64_t za = pos0 > end ? pos0 : end;
+                const uint64_t zb = pos0 + rpc < zend ? pos0 + rpc : zend;
+                if (za < zb)
+                    zero_span<VEC>(page + (slot0 + (uint32_t)(za - pos0)) * a.row_bytes,
+                                   (uint32_t)(zb - za) * a.row_bytes);
+            }
+        } else {
+            const uint64_t t0 = (uint64_t)u * rpc;
+            const uint32_t rows = (uint32_t)min64(rpc, len - t0);
+            const uint32_t q = u / a.units_per_page;
+            const uint32_t slot0 = (u - q * a.units_per_page) * rpc;
+            const uint64_t phys = uni64(ld_idx<IdxT>(a.block_table, sp + q));
+            const unsigned char *from = a.pool_r + (phys * P + slot0) * a.row_bytes;
+            unsigned char *to = a.out + (tb + t0) * a.out_row_bytes;
+            if constexpr (OP == Op::Gather) {
+                copy_span<VEC>(from, to, rows * a.row_bytes);
+            } else {
+                dequant_span<VEC>(a, from, a.scales + phys * P + slot0, to, rows);
+            }
+        }
+    }
+}
+
+// ---- plan pass (more sequences than fit in LDS) ----------------------------------
+
+template <typename IdxT, Op OP>
+__global__ __launch_bounds__(kThreads) void plan_sum_kernel(Args a) {
+    const uint32_t s0 = blockIdx.x * kPlanChunk;
+    const uint32_t s1 = min32(s0 + kPlanChunk, a.num_seqs);
+    const uint32_t per = kPlanChunk / kThreads;
+    const uint32_t i0 = min32(s1, s0 + threadIdx.x * per);
+    const uint32_t i1 = min32(s1, i0 + per);
+    uint64_t u = 0, t = 0;
+    for (uint32_t i = i0; i < i1; ++i) {
+        const uint64_t len = ld_idx<IdxT>(a.seq_lens, i);
+        const uint64_t st = (OP == Op::Scatter && a.seq_start) ? ld_idx<IdxT>(a.seq_start, i) : 0;
+        u += units_of<OP>(a, len, st);
+        t += len;
+    }
+    uint64_t tu, tt;
+    group_exclusive_scan(u, t, tu, tt);
+    if (threadIdx.x == 0) {
+        a.partials[2 * blockIdx.x] = tu;
+        a.partials[2 * blockIdx.x + 1] = tt;
+    }
+}
+
+// One workgroup: exclusive scan of the per-chunk totals, in place.
+__global__ __launch_bounds__(kThreads) void plan_scan_kernel(uint64_t *partials, uint32_t chunks) {
+    uint64_t cu = 0, ct = 0;
+    for (uint32_t b = 0; b < chunks; b += kThreads) {
+        const uint32_t i = b + threadIdx.x;
+        uint64_t u = i < chunks ? partials[2 * i] : 0;
+        uint64_t t = i < chunks ? partials[2 * i + 1] : 0;
+        uint64_t tu, tt;
+        group_exclusive_scan(u, t, tu, tt);
+        if (i < chunks) {
+            partials[2 * i] = cu + u;
+            partials[2 * i + 1] = ct + t;
+        }
+        cu += tu;
+        ct += tt;
+    }
+}
+
+template <typename IdxT, Op OP>
+__global__ __launch_bounds__(kThreads) void plan_write_kernel(Args a, uint32_t *unit_end,
+                                                              uint64_t *tok_begin) {
+    const uint32_t s0 = blockIdx.x * kPlanChunk;
+    const uint32_t s1 = min32(s0 + kPlanChunk, a.num_seqs);
+    scan_range<IdxT, OP>(a, s0, s1, a.partials[2 * blockIdx.x], a.partials[2 * blockIdx.x + 1],
+                         unit_end, tok_begin);
+}
+
+// ---- validator -----------------------------------------------------------------------
+
+struct VArgs {
+    const void *block_table, *seq_ptr, *seq_lens, *seq_start;
+    unsigned long long *ws;  // [0] min key, [1] token sum
+    uint64_t num_pages, page_size, num_seqs, num_block_entries;
+};
+
+__global__ void validate_init_kernel(unsigned long long *ws) {
+    if (threadIdx.x == 0) {
+        ws[0] = ~0ull;
+        ws[1] = 0ull;
+    }
+}
+
+__device__ __forceinline__ unsigned long long vkey(uint64_t rank, uint64_t index) {
+    return (rank << kKeyShift) | index;
+}
+
+// One pass over max(K, S+1) items. Each item evaluates the checks that name
+// its index; the smallest (check, index) key wins through atomicMin, which
+// makes the report independent of scheduling.
+template <typename IdxT>
+__global__ __launch_bounds__(256) void validate_kernel(VArgs a) {
+    const uint64_t S = a.num_seqs, K = a.num_block_entries;
+    const uint64_t n = K > S + 1 ? K : S + 1;
+    unsigned long long key = ~0ull, sum = 0;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        if (i == 0) {
+            if (ld_idx<IdxT>(a.seq_ptr, 0) != 0)
+                key = min64(key, vkey(kRankSeqPtrFirst, 0));
+            if (ld_idx<IdxT>(a.seq_ptr, S) != K)
+                key = min64(key, vkey(kRankSeqPtrLast, S));
+        }
+        if (i < S) {
+            const uint64_t p0 = ld_idx<IdxT>(a.seq_ptr, i), p1 = ld_idx<IdxT>(a.seq_ptr, i + 1);
+            if (p0 > p1)
+                key = min64(key, vkey(kRankSeqPtrOrder, i));
+            const uint64_t len = ld_idx<IdxT>(a.seq_lens, i);
+            const uint64_t st = a.seq_start ? ld_idx<IdxT>(a.seq_start, i) : 0;
+            if (p0 <= p1) {
+                const uint64_t slice = p1 - p0;
+                const uint64_t cap = __umul64hi(slice, a.page_size) ? ~0ull : slice * a.page_size;
+                if (st > cap || len > cap - st)
+                    key = min64(key, vkey(kRankSeqLen, i));
+            }
+            sum += len;
+        }
+        if (i < K && ld_idx<IdxT>(a.block_table, i) >= a.num_pages)
+            key = min64(key, vkey(kRankPageRange, i));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        key = min64(key, (unsigned long long)__shfl_xor(key, off, 64));
+        sum += (unsigned long long)__shfl_xor(sum, off, 64);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        if (key != ~0ull)
+            atomicMin(&a.ws[0], key);
+        if (sum)
+            atomicAdd(&a.ws[1], sum);
+    }
+}
+
+// ---- host-side dispatch ----------------------------------------------------------------
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+template <typename IdxT, Op OP, int VEC>
+hipError_t launch_vec(const Args &a, bool fused, uint32_t grid, uint32_t plan_chunks,
+                      uint32_t *unit_end, uint64_t *tok_begin, hipStream_t stream) {
+    if (fused) {
+        const size_t lds = 12 * (size_t)a.num_seqs;
+        hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, true>), dim3(grid), dim3(kThreads), lds,
+                           stream, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((plan_sum_kernel<IdxT, OP>), dim3(plan_chunks), dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kThreads), 0, stream, a.partials, plan_chunks);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((plan_write_kernel<IdxT, OP>), dim3(plan_chunks), dim3(kThreads), 0, stream,
+                       a, unit_end, tok_begin);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename IdxT, Op OP>
+hipError_t launch_op(const Args &a, uint32_t vec, bool fused, uint32_t grid, uint32_t chunks,
+                     uint32_t *ue, uint64_t *tb, hipStream_t st) {
+    if constexpr (OP == Op::Dequant) {
+        switch (vec) {
+        case 8: return launch_vec<IdxT, OP, 8>(a, fused, grid, chunks, ue, tb, st);
+        case 4: return launch_vec<IdxT, OP, 4>(a, fused, grid, chunks, ue, tb, st);
+        case 2: return launch_vec<IdxT, OP, 2>(a, fused, grid, chunks, ue, tb, st);
+        default: return launch_vec<IdxT, OP, 1>(a, fused, grid, chunks, ue, tb, st);
+        }
+    } else {
+        switch (vec) {
+        case 16: return launch_vec<IdxT, OP, 16>(a, fused, grid, chunks, ue, tb, st);
+        case 8: return launch_vec<IdxT, OP, 8>(a, fused, grid, chunks, ue, tb, st);
+        case 4: return launch_vec<IdxT, OP, 4>(a, fused, grid, chunks, ue, tb, st);
+        case 2: return launch_vec<IdxT, OP, 2>(a, fused, grid, chunks, ue, tb, st);
+        default: return launch_vec<IdxT, OP, 1>(a, fused, grid, chunks, ue, tb, st);
+        }
+    }
+}
+
+template <typename IdxT>
+hipError_t launch_idx(const Args &a, Op op, uint32_t vec, bool fused, uint32_t grid,
+                      uint32_t chunks, uint32_t *ue, uint64_t *tb, hipStream_t st) {
+    switch (op) {
+    case Op::Gather: return launch_op<IdxT, Op::Gather>(a, vec, fused, grid, chunks, ue, tb, st);
+    case Op::Scatter: return launch_op<IdxT, Op::Scatter>(a, vec, fused, grid, chunks, ue, tb, st);
+    default: return launch_op<IdxT, Op::Dequant>(a, vec, fused, grid, chunks, ue, tb, st);
+    }
+}
+
+} // namespace
+
+uint64_t plan_workspace_bytes(uint64_t num_seqs) {
+    const uint64_t chunks = (num_seqs + kPlanChunk - 1) / kPlanChunk;
+    return align256(8 * num_seqs) + align256(4 * num_seqs) + align256(16 * chunks);
+}
+
+hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
+    Args a = {};
+    a.pool_r = static_cast<const unsigned char *>(job.pool);
+    a.pool_w = static_cast<unsigned char *>(job.pool_w);
+    a.block_table = job.block_table;
+    a.seq_ptr = job.seq_ptr;
+    a.seq_lens = job.seq_lens;
+    a.seq_start = job.seq_start;
+    a.scales = job.scales;
+    a.src = static_cast<const unsigned char *>(job.src);
+    a.out = static_cast<unsigned char *>(job.out);
+    a.num_seqs = (uint32_t)job.num_seqs;
+    a.page_size = job.page_size;
+    a.rows_per_unit = job.rows_per_unit;
+    a.units_per_page = job.page_size / job.rows_per_unit;
+    a.units_per_group = job.units_per_group;
+    a.row_bytes = (uint32_t)job.row_bytes;
+    a.out_row_bytes = (uint32_t)job.out_row_bytes;
+    a.zero_tail = job.zero_tail ? 1u : 0u;
+    if (job.op == Op::Dequant) {
+        // Divisor for the row of an input vector: x / v = (umulhi(x, m) + x) >> l
+        // with l = ceil(log2 v), m = floor(2^32 (2^l - v) / v) + 1, exact for
+        // x < 2^31 (division by invariant integers using multiplication,
+        // Granlund and Montgomery, 1994).
+        const uint32_t v = (uint32_t)(job.row_bytes / job.vec_bytes);
+        uint32_t l = 0;
+        while ((1ull << l) < v)
+            ++l;
+        a.vecs_per_row = v;
+        a.vpr_mul = (uint32_t)(((1ull << 32) * ((1ull << l) - v)) / v + 1);
+        a.vpr_shift = l;
+    }
+    const bool fused = job.num_seqs <= kFusedMaxSeqs;
+    const uint64_t grid64 = (job.unit_bound + job.units_per_group - 1) / job.units_per_group;
+    const uint32_t grid = (uint32_t)grid64;
+    uint32_t chunks = 0;
+    uint32_t *ue = nullptr;
+    uint64_t *tb = nullptr;
+    if (!fused) {
+        unsigned char *ws = static_cast<unsigned char *>(job.workspace);
+        const uint64_t S = job.num_seqs;
+        chunks = (uint32_t)((S + kPlanChunk - 1) / kPlanChunk);
+        tb = reinterpret_cast<uint64_t *>(ws);
+        ue = reinterpret_cast<uint32_t *>(ws + align256(8 * S));
+        a.partials = reinterpret_cast<uint64_t *>(ws + align256(8 * S) + align256(4 * S));
+        a.g_unit_end = ue;
+        a.g_tok_begin = tb;
+    }
+    if (job.idx64)
+        return launch_idx<uint64_t>(a, job.op, job.vec_bytes, fused, grid, chunks, ue, tb, stream);
+    return launch_idx<uint32_t>(a, job.op, job.vec_bytes, fused, grid, chunks, ue, tb, stream);
+}
+
+hipError_t launch_validate(const ValidateJob &job, hipStream_t stream) {
+    VArgs a;
+    a.block_table = job.block_table;
+    a.seq_ptr = job.seq_ptr;
+    a.seq_lens = job.seq_lens;
+    a.seq_start = job.seq_start;
+    a.ws = static_cast<unsigned long long *>(job.workspace);
+    a.num_pages = job.num_pages;
+    a.page_size = job.page_size;
+    a.num_seqs = job.num_seqs;
+    a.num_block_entries = job.num_block_entries;
+    hipLaunchKernelGGL(validate_init_kernel, dim3(1), dim3(64), 0, stream, a.ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const uint64_t n = job.num_block_entries > job.num_seqs + 1 ? job.num_block_entries
+                                                                 : job.num_seqs + 1;
+    uint64_t blocks = (n + 255) / 256;
+    if (blocks > 4096)
+        blocks = 4096;
+    if (job.idx64)
+        hipLaunchKernelGGL(validate_kernel<uint64_t>, dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(validate_kernel<uint32_t>, dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+} // namespace hp

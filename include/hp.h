@@ -1,0 +1,191 @@
+/*
+ * hp.h -- block-paged KV layout on MI355X (gfx950): gather, scatter,
+ * dequant-gather and storage-invariant validation through a block table.
+ *
+ * The layout is the one defined by "Block-Paged Layout -- Hurray Format
+ * Specification" (cited below as [Hurray]): a shared page pool
+ * [num_pages, page_size, num_heads, head_dim], a block table of physical page
+ * IDs, and a CSR offset array seq_ptr delimiting each sequence's slice of the
+ * block table. The logical tensor is the ragged [total_tokens, num_heads,
+ * head_dim] tensor whose rows are the sequences' tokens, sequence after
+ * sequence, each in token order ([Hurray] Logical Shape).
+ *
+ * Element lookup ([Hurray] Element Lookup), for token t of sequence s:
+ *   phys_page = block_table[seq_ptr[s] + t / page_size]
+ *   flat      = ((phys_page*page_size + t % page_size)*num_heads + h)*head_dim + d
+ *
+ * Conventions shared by every call:
+ *   - Every buffer pointer is a DEVICE pointer unless stated otherwise, owned
+ *     by the caller. The library allocates nothing, frees nothing, keeps no
+ *     pointer after a call returns and holds no global mutable state; calls
+ *     are thread-safe.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on
+ *     it; buffers are read and written when the stream reaches that work.
+ *   - Argument errors are detected on the host before anything is enqueued:
+ *     on any non-HP_OK return nothing has been written.
+ *   - gather / scatter / gather_dequant are permissive readers ([Hurray]
+ *     Storage Invariants permits a permissive mode): they trust the data
+ *     invariants unless HP_FLAG_CHECKED is given, in which case hp_validate
+ *     runs first (synchronously) and its code is returned without writing.
+ *     Unchecked calls on a descriptor that violates (1)-(3) or the
+ *     token-count bound have undefined results.
+ *   - An empty batch (num_seqs = 0, seq_ptr = [0], block_table may be NULL;
+ *     [Hurray] Buffer Table note) is valid; calls on it enqueue nothing.
+ */
+#ifndef HP_H
+#define HP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. No call throws; every call returns one of these. */
+typedef enum hp_status {
+    HP_OK = 0,
+    HP_ERR_NULL = 1,          /* a required pointer is NULL */
+    HP_ERR_ARG = 2,           /* zero page_size/num_heads/head_dim, size overflow,
+                                 byte_offset != 0, reserved field != 0, bad flag */
+    HP_ERR_RANK = 3,          /* rank != 3 ([Hurray] Description) */
+    HP_ERR_PAGED_AXIS = 4,    /* paged_axis != 0 ([Hurray] Logical Shape, invariant 6) */
+    HP_ERR_INDEX_TYPE = 5,    /* unknown index type, or uint32 too narrow
+                                 ([Hurray] Additional Descriptor Fields note) */
+    HP_ERR_DTYPE = 6,         /* unknown or unsupported element type */
+    HP_ERR_ALIGN = 7,         /* descriptor buffer not 64-byte aligned ([Hurray]
+                                 Alignment) or other buffer not element aligned */
+    HP_ERR_WORKSPACE = 8,     /* workspace NULL or smaller than hp_workspace_bytes */
+    HP_ERR_SHARDED = 9,       /* a shard descriptor is attached ([Hurray] Sharding) */
+    HP_ERR_SEQPTR_FIRST = 16, /* seq_ptr[0] != 0                     (invariant 1) */
+    HP_ERR_SEQPTR_LAST = 17,  /* seq_ptr[num_seqs] != num_block_entries (invariant 1) */
+    HP_ERR_SEQPTR_ORDER = 18, /* seq_ptr[s] > seq_ptr[s+1]           (invariant 2) */
+    HP_ERR_PAGE_RANGE = 19,   /* block_table[k] >= num_pages         (invariant 3) */
+    HP_ERR_SEQ_LEN = 20,      /* seq_start[s] + seq_lens[s] > slice pages * page_size
+                                 ([Hurray] Partial trailing page: reads and writes
+                                 are bounded by the slice and the token count) */
+    HP_ERR_TOTAL_TOKENS = 21, /* sum of seq_lens != total_tokens ([Hurray] Logical Shape) */
+    HP_ERR_HIP = 32           /* a HIP runtime call or kernel launch failed */
+} hp_status;
+
+/* block_table_index_type ([Hurray] Additional Descriptor Fields, Example):
+ * element type of block_table, seq_ptr, seq_lens and seq_start. */
+enum { HP_INDEX_U32 = 0x00, HP_INDEX_U64 = 0x01 };
+
+/* Element types of page_pool / the logical tensor. Gather and scatter are bit
+ * copies, so only the width matters to them. */
+enum {
+    HP_DTYPE_I8 = 1, HP_DTYPE_U8 = 2, HP_DTYPE_F16 = 3, HP_DTYPE_BF16 = 4,
+    HP_DTYPE_F32 = 5, HP_DTYPE_F64 = 6
+};
+
+/* Flags. */
+enum {
+    HP_FLAG_CHECKED = 1u << 0,   /* validate first; on a violation write nothing */
+    HP_FLAG_ZERO_TAIL = 1u << 1  /* scatter: zero the slots of each sequence's last
+                                    written page past its last new token ([Hurray]
+                                    Partial trailing page: a writer should zero them) */
+};
+
+/* A block-paged descriptor for one {kv_role, layer_index} pair ([Hurray]
+ * Description, Buffer Table, Additional Descriptor Fields, Example).
+ * Host memory; read during the call only. */
+typedef struct hp_desc {
+    uint32_t rank;              /* must be 3 */
+    uint32_t paged_axis;        /* must be 0 */
+    uint32_t index_type;        /* HP_INDEX_U32 or HP_INDEX_U64 */
+    uint32_t dtype;             /* HP_DTYPE_* of page_pool elements */
+    uint32_t page_size;         /* P > 0 (tokens per page) */
+    uint32_t num_heads;         /* H > 0 */
+    uint32_t head_dim;          /* D > 0 */
+    uint32_t has_shard;         /* must be 0: block-paged may not be sharded */
+    uint32_t kv_role;           /* informational (0 key, 1 value); not read */
+    uint32_t layer_index;       /* informational; not read */
+    uint64_t byte_offset;       /* must be 0 ([Hurray] byte_offset) */
+    uint64_t num_pages;         /* N: pages in page_pool */
+    uint64_t num_seqs;          /* S */
+    uint64_t num_block_entries; /* K: entries in block_table (total_logical_pages) */
+    uint64_t total_tokens;      /* T: rows of the logical tensor = sum of seq_lens */
+    void *page_pool;            /* buffer 0: N*P*H*D elements, 64-byte aligned;
+                                   written only by hp_scatter */
+    const void *block_table;    /* buffer 1: K page IDs (index_type), 64-byte
+                                   aligned; may be NULL when K == 0 */
+    const void *seq_ptr;        /* buffer 2: S+1 offsets (index_type), 64-byte aligned */
+    const void *seq_lens;       /* S token counts (index_type); NULL allowed if S == 0 */
+    const float *scales;        /* buffer 3 (quantized pools only): N*P fp32, one per
+                                   page slot ([Hurray] Per-page-slot parameters),
+                                   64-byte aligned; NULL otherwise */
+} hp_desc;
+
+/* Result of hp_validate, written to HOST memory. */
+typedef struct hp_validate_result {
+    int32_t code;      /* HP_OK or the first failing HP_ERR_* */
+    uint32_t reserved;
+    uint64_t index;    /* smallest failing s or k for that check; num_seqs for
+                          HP_ERR_SEQPTR_LAST; 0 otherwise */
+} hp_validate_result;
+
+/* Bytes of device workspace (any alignment >= 256 is fine) that any call on
+ * `desc` needs; 0 if none. Returns 0 for an invalid descriptor too (the call
+ * itself reports the error). */
+size_t hp_workspace_bytes(const hp_desc *desc);
+
+/* Storage-invariant validator ([Hurray] Storage Invariants: a reader should
+ * validate (1)-(3) and (6) and must reject violations).
+ * Host-side: rank, paged_axis, shard, sizes. Device-side, one parallel pass:
+ * (1) seq_ptr[0] = 0 and seq_ptr[S] = K; (2) seq_ptr non-decreasing;
+ * (3) block_table[k] < N; then the token-count bound
+ *     seq_start[s] + seq_lens[s] <= (seq_ptr[s+1] - seq_ptr[s]) * P
+ * (seq_start NULL means all starts are 0; pass the scatter's seq_start to
+ * check a scatter's windows); then sum(seq_lens) = T.
+ * The first failing check in that order is reported, with its smallest
+ * failing index, so the result is deterministic. Aliased page IDs are
+ * allowed ([Hurray] Prefix Sharing) and not checked.
+ * Synchronous: enqueues on `stream`, copies 16 bytes back and waits for the
+ * stream. `result` is a host pointer and may be NULL. Returns result->code. */
+hp_status hp_validate(const hp_desc *desc, const void *seq_start, void *workspace,
+                      size_t workspace_bytes, hp_validate_result *result,
+                      void *stream);
+
+/* Gather ([Hurray] Element Lookup, Logical Shape): writes the logical tensor
+ *   out[(sum_{s'<s} seq_lens[s']) + t][h][d] = page_pool[flat(s, t, h, d)]
+ * for every s < S, t < seq_lens[s], as a bit copy. `out` is a device buffer
+ * of T*H*D elements of desc->dtype, element aligned, not overlapping
+ * page_pool. No slot at or past a sequence's token count is read ([Hurray]
+ * Partial trailing page). Slices may alias pages. Asynchronous.
+ * Flags: HP_FLAG_CHECKED. */
+hp_status hp_gather(const hp_desc *desc, void *out, void *workspace,
+                    size_t workspace_bytes, uint32_t flags, void *stream);
+
+/* Scatter: the inverse move. `src` holds T = sum(seq_lens) new rows
+ * [T, H, D] of desc->dtype in logical order; the i-th new row of sequence s
+ * is token seq_start[s] + i of that sequence and is written to
+ *   page_pool[flat(s, seq_start[s] + i, h, d)]
+ * (seq_start: S device entries of index_type, or NULL for all zeros).
+ * With HP_FLAG_ZERO_TAIL and seq_lens[s] > 0, the slots of the page holding
+ * the last new token that come after it are set to zero bytes ([Hurray]
+ * Partial trailing page). Destinations of different rows must be distinct
+ * slots (aliased pages must be copied before they are written); otherwise
+ * the result is undefined. Asynchronous.
+ * Flags: HP_FLAG_CHECKED (validates with seq_start), HP_FLAG_ZERO_TAIL. */
+hp_status hp_scatter(const hp_desc *desc, const void *src, const void *seq_start,
+                     void *workspace, size_t workspace_bytes, uint32_t flags,
+                     void *stream);
+
+/* Dequant-gather ([Hurray] Element Lookup, Per-page-slot parameters): for an
+ * int8 pool (desc->dtype = HP_DTYPE_I8) with per-slot scales (desc->scales),
+ *   out[row][h][d] = bf16_rne( fp32(q) * scales[phys_page*P + t % P] )
+ * one IEEE binary32 multiply, then round to nearest even into bfloat16; rows
+ * as in hp_gather. out_dtype must be HP_DTYPE_BF16; `out` holds T*H*D bf16
+ * values, 2-byte aligned. Asynchronous. Flags: HP_FLAG_CHECKED. */
+hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype,
+                            void *workspace, size_t workspace_bytes, uint32_t flags,
+                            void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *hp_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HP_H */

@@ -153,11 +153,16 @@ def gather_rows(pool, rows, *, page_size, num_heads, head_dim, block_table, seq_
 
 
 def scatter(pool, src, *, page_size, num_heads, head_dim, block_table, seq_ptr,
-            seq_lens, seq_start=None, zero_tail=False):
-    """Returns a copy of `pool` with the rows of `src` written into their slots."""
+            seq_lens, seq_start=None, zero_tail=False, in_place=False):
+    """Returns a copy of `pool` with the rows of `src` written into their slots
+    (with in_place, writes into `pool` itself, which must be contiguous)."""
     lib = _load()
-    pool, eb = _pool_geometry(pool, page_size, num_heads, head_dim)
-    result = pool.copy()
+    if in_place:
+        assert pool.flags["C_CONTIGUOUS"]
+        result, eb = pool, pool.dtype.itemsize
+    else:
+        pool, eb = _pool_geometry(pool, page_size, num_heads, head_dim)
+        result = pool.copy()
     src = np.ascontiguousarray(src)
     assert src.dtype.itemsize == eb
     bt, sp, sl = _idx(block_table), _idx(seq_ptr), _idx(seq_lens)

@@ -1,0 +1,152 @@
+"""The C-ABI library loads, exports every symbol include/hp.h declares, and
+rejects bad arguments on the host before any HIP call (no GPU needed: every
+call here returns before the library touches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_table_gather_amd as hp
+from conftest import ROOT
+
+HDR = os.path.join(ROOT, "include", "hp.h")
+L = hp.lib()
+S = hp.CODE
+ALIGNED = 0x7F0000000000  # a fake, 256-byte aligned device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HDR).read()
+    return re.findall(r"^(?:hp_status|size_t|const char \*)\s*(hp_\w+)\(", text, re.M)
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == {"hp_workspace_bytes", "hp_validate", "hp_gather", "hp_scatter",
+                          "hp_gather_dequant", "hp_status_str"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code, name in hp.STATUS.items():
+        assert hp.status_str(code).startswith(name)
+    assert hp.status_str(999) == "unknown hp_status"
+
+
+def desc(**kw):
+    d = hp.HpDesc()
+    d.rank, d.paged_axis, d.index_type, d.dtype = 3, 0, hp.HP_INDEX_U32, hp.DTYPE["f16"]
+    d.page_size, d.num_heads, d.head_dim = 16, 4, 8
+    d.num_pages, d.num_seqs, d.num_block_entries, d.total_tokens = 20, 3, 10, 114
+    d.page_pool = ALIGNED
+    d.block_table = ALIGNED + 0x100000
+    d.seq_ptr = ALIGNED + 0x200000
+    d.seq_lens = ALIGNED + 0x300000
+    d.scales = None
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+OUT = ALIGNED + 0x100000000
+
+
+def gather(d, out=OUT, ws=None, n=0, flags=0):
+    return L.hp_gather(ctypes.byref(d) if d is not None else None, out, ws, n, flags, None)
+
+
+@pytest.mark.parametrize("fields,code", [
+    (dict(rank=2), "HP_ERR_RANK"),
+    (dict(rank=4), "HP_ERR_RANK"),
+    (dict(paged_axis=1), "HP_ERR_PAGED_AXIS"),
+    (dict(has_shard=1), "HP_ERR_SHARDED"),
+    (dict(index_type=2), "HP_ERR_INDEX_TYPE"),
+    (dict(dtype=0), "HP_ERR_DTYPE"),
+    (dict(dtype=99), "HP_ERR_DTYPE"),
+    (dict(byte_offset=64), "HP_ERR_ARG"),
+    (dict(page_size=0), "HP_ERR_ARG"),
+    (dict(num_heads=0), "HP_ERR_ARG"),
+    (dict(head_dim=0), "HP_ERR_ARG"),
+    (dict(num_pages=1 << 62), "HP_ERR_ARG"),                       # pool bytes overflow
+    (dict(num_heads=1 << 20, head_dim=1 << 12), "HP_ERR_ARG"),     # row too large
+    (dict(num_pages=(1 << 32) + 1), "HP_ERR_INDEX_TYPE"),          # uint32 too narrow
+    (dict(seq_ptr=None), "HP_ERR_NULL"),
+    (dict(block_table=None), "HP_ERR_NULL"),
+    (dict(seq_lens=None), "HP_ERR_NULL"),
+    (dict(page_pool=None), "HP_ERR_NULL"),
+    (dict(page_pool=ALIGNED + 32), "HP_ERR_ALIGN"),                # descriptor buffers: 64 B
+    (dict(block_table=ALIGNED + 4), "HP_ERR_ALIGN"),
+    (dict(seq_ptr=ALIGNED + 8), "HP_ERR_ALIGN"),
+    (dict(seq_lens=ALIGNED + 2), "HP_ERR_ALIGN"),
+])
+def test_descriptor_rejections(fields, code):
+    d = desc(**fields)
+    assert gather(d) == S[code]
+    assert L.hp_scatter(ctypes.byref(d), OUT, None, None, 0, 0, None) == S[code]
+    res = hp.HpValidateResult()
+    assert L.hp_validate(ctypes.byref(d), None, OUT, 4096, ctypes.byref(res), None) == S[code]
+    assert res.code == S[code]
+    assert L.hp_workspace_bytes(ctypes.byref(d)) == 0
+
+
+def test_null_descriptor():
+    assert gather(None) == S["HP_ERR_NULL"]
+    assert L.hp_scatter(None, OUT, None, None, 0, 0, None) == S["HP_ERR_NULL"]
+    assert L.hp_gather_dequant(None, OUT, hp.DTYPE["bf16"], None, 0, 0, None) == S["HP_ERR_NULL"]
+    assert L.hp_validate(None, None, None, 0, None, None) == S["HP_ERR_NULL"]
+    assert L.hp_workspace_bytes(None) == 0
+
+
+def test_call_buffer_rejections():
+    d = desc()
+    assert gather(d, out=None) == S["HP_ERR_NULL"]
+    assert gather(d, out=OUT + 1) == S["HP_ERR_ALIGN"]
+    assert gather(d, out=ALIGNED + 64) == S["HP_ERR_ARG"]            # overlaps the pool
+    assert gather(d, flags=4) == S["HP_ERR_ARG"]                     # unknown flag
+    assert gather(d, flags=hp.HP_FLAG_ZERO_TAIL) == S["HP_ERR_ARG"]  # scatter-only flag
+    assert gather(d, flags=hp.HP_FLAG_CHECKED) == S["HP_ERR_WORKSPACE"]
+    assert gather(d, ws=OUT + 0x100000, n=255, flags=hp.HP_FLAG_CHECKED) == S["HP_ERR_WORKSPACE"]
+    assert gather(d, ws=OUT + 0x100004, n=4096, flags=hp.HP_FLAG_CHECKED) == S["HP_ERR_ALIGN"]
+    sc = ctypes.byref(d)
+    assert L.hp_scatter(sc, None, None, None, 0, 0, None) == S["HP_ERR_NULL"]
+    assert L.hp_scatter(sc, OUT, ALIGNED + 0x400002, None, 0, 0, None) == S["HP_ERR_ALIGN"]
+    assert L.hp_scatter(sc, OUT, None, None, 0, 8, None) == S["HP_ERR_ARG"]
+    res = hp.HpValidateResult()
+    assert L.hp_validate(sc, None, None, 0, ctypes.byref(res), None) == S["HP_ERR_WORKSPACE"]
+    assert L.hp_validate(sc, None, OUT, 16, ctypes.byref(res), None) == S["HP_ERR_WORKSPACE"]
+
+
+def test_dequant_rejections():
+    q = desc(dtype=hp.DTYPE["i8"], scales=ALIGNED + 0x500000)
+    bf16 = hp.DTYPE["bf16"]
+    call = lambda d, out=OUT, od=bf16: L.hp_gather_dequant(ctypes.byref(d), out, od, None, 0, 0, None)  # noqa: E731
+    assert call(desc(scales=ALIGNED + 0x500000)) == S["HP_ERR_DTYPE"]   # f16 pool
+    assert call(q, od=hp.DTYPE["f16"]) == S["HP_ERR_DTYPE"]
+    assert call(desc(dtype=hp.DTYPE["i8"])) == S["HP_ERR_NULL"]        # no scales
+    assert call(desc(dtype=hp.DTYPE["i8"], scales=ALIGNED + 0x500004)) == S["HP_ERR_ALIGN"]
+    assert call(q, out=None) == S["HP_ERR_NULL"]
+    assert call(q, out=OUT + 1) == S["HP_ERR_ALIGN"]
+    assert call(q, out=ALIGNED + 0x500000) == S["HP_ERR_ARG"]          # overlaps scales
+
+
+def test_workspace_bytes():
+    d = desc()
+    assert L.hp_workspace_bytes(ctypes.byref(d)) == 256
+    big = desc(num_seqs=5000, num_block_entries=20000, num_pages=20000)
+    n = L.hp_workspace_bytes(ctypes.byref(big))
+    # validator head + per-sequence offsets (8 + 4 bytes) + chunk totals
+    assert n >= 256 + 12 * 5000
+    # more sequences than fit in LDS: an unchecked call needs the plan arrays
+    assert gather(big) == S["HP_ERR_WORKSPACE"]
+
+
+def test_empty_batch_and_zero_tokens_enqueue_nothing():
+    """[Hurray] Buffer Table note: num_seqs = 0, seq_ptr = [0], block_table
+    may be NULL. No work is enqueued, so this runs without a GPU."""
+    d = desc(num_seqs=0, num_block_entries=0, block_table=None, seq_lens=None, total_tokens=0)
+    assert gather(d, out=None) == S["HP_OK"]
+    assert L.hp_scatter(ctypes.byref(d), None, None, None, 0, hp.HP_FLAG_ZERO_TAIL, None) == 0
+    z = desc(total_tokens=0)
+    assert gather(z, out=None) == S["HP_OK"]

@@ -92,7 +92,10 @@ class Workload:
         return self.num_heads * self.head_dim * self.elem_bytes
 
     def referenced_pages(self):
-        return np.unique(self.block_table.astype(np.int64))
+        """Page IDs the block table names that exist in the pool (IDs out of
+        range, as in deliberately invalid descriptors, are skipped)."""
+        ids = np.unique(self.block_table.astype(np.int64))
+        return ids[(ids >= 0) & (ids < self.num_pages)]
 
     # ---- element values (seeded, on any torch device) -------------------
     def _generator(self, device, salt):
