@@ -15,17 +15,39 @@ count per sequence. Importing this package fails if the library was not built
 import ctypes
 import os
 
+# PyTorch ships its own HIP runtime under the same soname (libamdhip64.so.7)
+# as the system ROCm one that libhp.so is linked against. Loading torch first
+# makes the dynamic linker bind libhp.so to torch's copy, so that one HIP
+# runtime serves both (two runtimes in one process cannot share a device).
+import torch  # noqa: F401,E402
+
 __all__ = ["Descriptor", "HpError", "gather", "scatter", "gather_dequant", "validate",
-           "workspace_bytes", "status_str", "lib", "LIB_PATH", "STATUS"]
+           "workspace_bytes", "status_str", "last_hip_error", "lib", "LIB_PATH", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhp.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m block_table_gather_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python block_table_gather_amd/build.py` "
         "(hipcc, gfx950). There is no fallback implementation.")
 
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes():
+    """Distinct libamdhip64 files mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return set()
+    return {os.path.realpath(p) for p in paths}
+
+
+if len(_hip_runtimes()) > 1:
+    raise ImportError(
+        "two HIP runtimes are loaded in this process (" + ", ".join(sorted(_hip_runtimes()))
+        + "); libhp.so must share torch's: import torch before loading libhp.so")
 
 # Status codes (include/hp.h, enum hp_status).
 STATUS = {
@@ -38,7 +60,7 @@ STATUS = {
 CODE = {v: k for k, v in STATUS.items()}
 HP_INDEX_U32, HP_INDEX_U64 = 0x00, 0x01
 DTYPE = {"i8": 1, "u8": 2, "f16": 3, "bf16": 4, "f32": 5, "f64": 6}
-HP_FLAG_CHECKED, HP_FLAG_ZERO_TAIL = 1, 2
+HP_FLAG_CHECKED, HP_FLAG_ZERO_TAIL, HP_FLAG_STREAM = 1, 2, 4
 
 
 class HpDesc(ctypes.Structure):
@@ -77,6 +99,8 @@ _lib.hp_gather_dequant.restype = ctypes.c_int
 _lib.hp_gather_dequant.argtypes = [_P, _vp, _u32, _vp, _sz, _u32, _vp]
 _lib.hp_status_str.restype = ctypes.c_char_p
 _lib.hp_status_str.argtypes = [ctypes.c_int]
+_lib.hp_last_hip_error.restype = ctypes.c_char_p
+_lib.hp_last_hip_error.argtypes = []
 
 
 def lib():
@@ -88,11 +112,19 @@ def status_str(code):
     return _lib.hp_status_str(int(code)).decode()
 
 
+def last_hip_error():
+    """HIP error name behind this thread's last HP_ERR_HIP."""
+    return _lib.hp_last_hip_error().decode()
+
+
 class HpError(RuntimeError):
     def __init__(self, code, where=""):
         self.code = int(code)
         self.name = STATUS.get(self.code, str(code))
-        super().__init__(f"{where}: {status_str(code)}" if where else status_str(code))
+        msg = status_str(code)
+        if self.name == "HP_ERR_HIP":
+            msg += f" ({last_hip_error()})"
+        super().__init__(f"{where}: {msg}" if where else msg)
 
 
 def _check(code, where):
@@ -105,7 +137,6 @@ def _ptr(t):
 
 
 def _torch():
-    import torch
     return torch
 
 
@@ -209,16 +240,23 @@ def validate(desc, total_tokens, seq_start=None, *, workspace=None, stream=None)
     ws, n = _workspace(desc, total_tokens, workspace)
     code = _lib.hp_validate(p, _ptr(seq_start), ws, n, ctypes.byref(res),
                             _stream(stream, desc.device))
-    return STATUS.get(code, str(code)), int(res.index)
+    name = STATUS.get(code, str(code))
+    if name == "HP_ERR_HIP":
+        raise HpError(code, "hp_validate")
+    return name, int(res.index)
 
 
-def gather(desc, out, *, checked=False, workspace=None, stream=None):
-    """out[T, H, D] <- the logical tensor (T = out.shape[0])."""
+def gather(desc, out, *, checked=False, streaming=False, workspace=None, stream=None):
+    """out[T, H, D] <- the logical tensor (T = out.shape[0]).
+
+    streaming: hint that no pool page is read twice (slices do not alias), so
+    the pool is read with non-temporal loads; the result is the same."""
     T = out.shape[0]
     p = desc.with_tokens(T)
     ws, n = _workspace(desc, T, workspace)
-    _check(_lib.hp_gather(p, _ptr(out), ws, n, HP_FLAG_CHECKED if checked else 0,
-                          _stream(stream, desc.device)), "hp_gather")
+    flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_STREAM if streaming else 0)
+    _check(_lib.hp_gather(p, _ptr(out), ws, n, flags, _stream(stream, desc.device)),
+           "hp_gather")
     return out
 
 

@@ -1,8 +1,11 @@
 """Build libhp.so (the C-ABI library of include/hp.h) for gfx950, in place.
 
-    python -m block_table_gather_amd.build [-v] [-DNAME=VALUE ...] [-o OUT]
+    python block_table_gather_amd/build.py [-v] [-DNAME=VALUE ...] [-o OUT]
 
-Extra -D definitions (HP_UNIT_BYTES, HP_UNITS_PER_GROUP) override the build
+Run it as a script (or load it by path): importing the package would load the
+library this builds.
+
+Extra -D definitions (HP_GATHER_UNIT_BYTES, HP_THREADS, ...) override the build
 time tuning knobs; -o writes the library elsewhere (used for tuning sweeps).
 """
 import os
@@ -35,10 +38,7 @@ def build(verbose=False, defines=(), out=None):
     tmp = out + ".tmp"
     cmd = [HIPCC, *FLAGS, *defines, "-o", tmp]
     for src in SOURCES:
-        if src.endswith(".hip"):
-            cmd += ["-x", "hip", src]
-        else:
-            cmd += ["-x", "hip", src]
+        cmd += ["-x", "hip", src]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -7,17 +7,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-// Tuning knobs, fixed at build time.
-#ifndef HP_UNIT_BYTES
-#define HP_UNIT_BYTES hp::kDefaultUnitBytes
-#endif
-#ifndef HP_UNITS_PER_GROUP
-#define HP_UNITS_PER_GROUP hp::kDefaultUnitsPerGroup
-#endif
-
 namespace {
 
 constexpr uint64_t kValidateBytes = 256;  // workspace head: validator key + sum
+
+// The HIP error behind the calling thread's last HP_ERR_HIP (per thread, so
+// concurrent callers do not see each other's errors).
+thread_local hipError_t t_last_hip_error = hipSuccess;
+
+hp_status hip_failed(hipError_t e) {
+    t_last_hip_error = e;
+    return HP_ERR_HIP;
+}
 constexpr uint64_t kMaxIndex = (1ull << hp::kKeyShift) - 1;
 
 uint32_t elem_bytes_of(uint32_t dtype) {
@@ -131,12 +132,14 @@ hp_status run_validate(const hp_desc *d, const void *seq_start, void *ws,
     j.seq_lens = d->seq_lens;
     j.seq_start = seq_start;
     j.workspace = ws;
-    if (hp::launch_validate(j, stream) != hipSuccess)
-        return HP_ERR_HIP;
+    hipError_t e = hp::launch_validate(j, stream);
+    if (e != hipSuccess)
+        return hip_failed(e);
     uint64_t host[2] = {0, 0};
-    if (hipMemcpyAsync(host, ws, sizeof host, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-        hipStreamSynchronize(stream) != hipSuccess)
-        return HP_ERR_HIP;
+    if ((e = hipMemcpyAsync(host, ws, sizeof host, hipMemcpyDeviceToHost, stream)) != hipSuccess)
+        return hip_failed(e);
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess)
+        return hip_failed(e);
     res->code = HP_OK;
     res->index = 0;
     if (host[0] != ~0ull) {
@@ -154,8 +157,8 @@ hp_status run_validate(const hp_desc *d, const void *seq_start, void *ws,
 
 // Largest divisor of P whose run of rows fits the target unit size (at least
 // 1, at most `cap`).
-uint32_t rows_per_unit(uint32_t P, uint64_t row_bytes, uint32_t cap) {
-    uint64_t want = HP_UNIT_BYTES / (row_bytes ? row_bytes : 1);
+uint32_t rows_per_unit(uint32_t P, uint64_t row_bytes, uint64_t unit_bytes, uint32_t cap) {
+    uint64_t want = unit_bytes / (row_bytes ? row_bytes : 1);
     if (want < 1)
         want = 1;
     if (want > cap)
@@ -176,7 +179,8 @@ uint32_t widest_vec(uint64_t row_bytes, const void *a, const void *b, uint32_t m
 }
 
 hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const void *src, void *out,
-                 const void *seq_start, bool zero_tail, void *ws, hipStream_t stream) {
+                 const void *seq_start, uint32_t flags, void *ws, hipStream_t stream) {
+    const bool zero_tail = (flags & HP_FLAG_ZERO_TAIL) != 0;
     hp::CopyJob j = {};
     j.op = op;
     j.idx64 = d->index_type == HP_INDEX_U64;
@@ -188,8 +192,28 @@ hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const void *src
     j.row_bytes = g.row_bytes;
     j.out_row_bytes = op == hp::Op::Dequant ? g.row_bytes * 2 : g.row_bytes;
     const uint64_t rmax = j.out_row_bytes > j.row_bytes ? j.out_row_bytes : j.row_bytes;
-    j.rows_per_unit = rows_per_unit(d->page_size, rmax, op == hp::Op::Dequant ? 64 : 0xffffffffu);
-    j.units_per_group = HP_UNITS_PER_GROUP;
+    // Per-move launch shape (measured on MI355X): target unit size, units per
+    // workgroup, and whether the source is streamed with non-temporal loads.
+    uint64_t unit_bytes;
+    switch (op) {
+    case hp::Op::Gather:
+        unit_bytes = HP_GATHER_UNIT_BYTES;
+        j.units_per_group = HP_GATHER_UNITS_PER_GROUP;
+        j.load_nt = (flags & HP_FLAG_STREAM) != 0;
+        break;
+    case hp::Op::Scatter:
+        unit_bytes = HP_SCATTER_UNIT_BYTES;
+        j.units_per_group = HP_SCATTER_UNITS_PER_GROUP;
+        j.load_nt = false;
+        break;
+    default:
+        unit_bytes = HP_DEQUANT_UNIT_BYTES;
+        j.units_per_group = HP_DEQUANT_UNITS_PER_GROUP;
+        j.load_nt = false;
+        break;
+    }
+    j.rows_per_unit =
+        rows_per_unit(d->page_size, rmax, unit_bytes, op == hp::Op::Dequant ? 64 : 0xffffffffu);
     const uint64_t rpc = j.rows_per_unit;
     const uint64_t upp = d->page_size / rpc;
     // Upper bound on the number of units, from host-known T and S only.
@@ -197,7 +221,7 @@ hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const void *src
         j.unit_bound = d->total_tokens / rpc + d->num_seqs * (2 + (zero_tail ? upp : 0));
     else
         j.unit_bound = d->total_tokens / rpc + d->num_seqs;
-    if (j.unit_bound >= (1ull << 32) - HP_UNITS_PER_GROUP)
+    if (j.unit_bound >= (1ull << 32) - hp::kMaxUnitsPerGroup)
         return HP_ERR_ARG;
     j.pool = d->page_pool;
     j.pool_w = d->page_pool;
@@ -215,7 +239,8 @@ hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const void *src
         j.vec_bytes = widest_vec(g.row_bytes, d->page_pool, op == hp::Op::Scatter ? src : out, 16);
     if (op == hp::Op::Dequant && !aligned(out, 2 * (uint64_t)j.vec_bytes))
         j.vec_bytes = 1;  // out is 2-byte aligned; 1-byte input vectors write 2 bytes
-    return hp::launch_copy(j, stream) == hipSuccess ? HP_OK : HP_ERR_HIP;
+    const hipError_t e = hp::launch_copy(j, stream);
+    return e == hipSuccess ? HP_OK : hip_failed(e);
 }
 
 // Common front half of gather / scatter / dequant, after the descriptor and
@@ -289,11 +314,11 @@ hp_status hp_gather(const hp_desc *desc, void *out, void *workspace, size_t work
         return HP_ERR_ALIGN;
     if (overlaps(out, desc->total_tokens * g.row_bytes, desc->page_pool, g.pool_bytes))
         return HP_ERR_ARG;
-    st = prologue(desc, g, flags, HP_FLAG_CHECKED, nullptr, workspace, workspace_bytes,
-                  (hipStream_t)stream, &done);
+    st = prologue(desc, g, flags, HP_FLAG_CHECKED | HP_FLAG_STREAM, nullptr, workspace,
+                  workspace_bytes, (hipStream_t)stream, &done);
     if (st != HP_OK || done)
         return st;
-    return launch(desc, g, hp::Op::Gather, nullptr, out, nullptr, false, workspace,
+    return launch(desc, g, hp::Op::Gather, nullptr, out, nullptr, flags, workspace,
                   (hipStream_t)stream);
 }
 
@@ -314,8 +339,8 @@ hp_status hp_scatter(const hp_desc *desc, const void *src, const void *seq_start
                   workspace_bytes, (hipStream_t)stream, &done);
     if (st != HP_OK || done)
         return st;
-    return launch(desc, g, hp::Op::Scatter, src, nullptr, seq_start,
-                  (flags & HP_FLAG_ZERO_TAIL) != 0, workspace, (hipStream_t)stream);
+    return launch(desc, g, hp::Op::Scatter, src, nullptr, seq_start, flags, workspace,
+                  (hipStream_t)stream);
 }
 
 hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype, void *workspace,
@@ -339,9 +364,11 @@ hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype, 
                   (hipStream_t)stream, &done);
     if (st != HP_OK || done)
         return st;
-    return launch(desc, g, hp::Op::Dequant, nullptr, out, nullptr, false, workspace,
+    return launch(desc, g, hp::Op::Dequant, nullptr, out, nullptr, flags, workspace,
                   (hipStream_t)stream);
 }
+
+const char *hp_last_hip_error(void) { return hipGetErrorName(t_last_hip_error); }
 
 const char *hp_status_str(int status) {
     switch (status) {

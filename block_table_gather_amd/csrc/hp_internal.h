@@ -7,14 +7,40 @@
 
 namespace hp {
 
+// Tuning constants; each can be overridden at build time (-DHP_...). Unit
+// bytes are the target size of one work unit on its larger side; measured on
+// MI355X (16 KB gather spans stream best; dequant and scatter prefer 32 KB).
+#ifndef HP_THREADS
+#define HP_THREADS 256
+#endif
+#ifndef HP_GATHER_UNIT_BYTES
+#define HP_GATHER_UNIT_BYTES 16384
+#endif
+#ifndef HP_SCATTER_UNIT_BYTES
+#define HP_SCATTER_UNIT_BYTES 32768
+#endif
+#ifndef HP_DEQUANT_UNIT_BYTES
+#define HP_DEQUANT_UNIT_BYTES 32768
+#endif
+#ifndef HP_GATHER_UNITS_PER_GROUP
+#define HP_GATHER_UNITS_PER_GROUP 1
+#endif
+#ifndef HP_SCATTER_UNITS_PER_GROUP
+#define HP_SCATTER_UNITS_PER_GROUP 2
+#endif
+#ifndef HP_DEQUANT_UNITS_PER_GROUP
+#define HP_DEQUANT_UNITS_PER_GROUP 1
+#endif
 // Sequences whose per-sequence offsets fit in LDS: up to this many, every
 // workgroup rebuilds the offsets itself (one fused launch); beyond it a plan
 // pass writes them to the workspace first.
-constexpr uint64_t kFusedMaxSeqs = 4096;
-constexpr uint32_t kThreads = 256;            // threads per copy workgroup
-constexpr uint32_t kPlanChunk = kThreads * 8; // sequences per plan workgroup
-constexpr uint32_t kDefaultUnitBytes = 32768; // target bytes moved per work unit
-constexpr uint32_t kDefaultUnitsPerGroup = 4; // work units per workgroup
+#ifndef HP_FUSED_MAX_SEQS
+#define HP_FUSED_MAX_SEQS 4096
+#endif
+constexpr uint64_t kFusedMaxSeqs = HP_FUSED_MAX_SEQS;
+constexpr uint32_t kThreads = HP_THREADS;     // threads per copy workgroup
+constexpr uint32_t kPlanChunk = 2048;         // sequences per plan workgroup
+constexpr uint32_t kMaxUnitsPerGroup = 16;
 
 enum class Op : int { Gather = 0, Scatter = 1, Dequant = 2 };
 
@@ -27,6 +53,7 @@ struct CopyJob {
     uint32_t page_size;     // P
     uint32_t rows_per_unit; // divides P
     uint32_t units_per_group;
+    bool load_nt;           // stream the source with non-temporal loads
     uint64_t num_seqs;      // S
     uint64_t total_tokens;  // T
     uint64_t row_bytes;     // H*D*elem_bytes (pool side)

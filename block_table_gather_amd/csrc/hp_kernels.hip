@@ -48,8 +48,44 @@ template <> struct Vec<4> { using T = uint32_t; };
 template <> struct Vec<2> { using T = uint16_t; };
 template <> struct Vec<1> { using T = uint8_t; };
 
-constexpr int kCopyUnroll = 8;
+#ifndef HP_COPY_UNROLL
+#define HP_COPY_UNROLL 8
+#endif
+#ifndef HP_STORE_NT
+#define HP_STORE_NT 1
+#endif
+constexpr int kCopyUnroll = HP_COPY_UNROLL;
 constexpr int kDequantUnroll = 8;
+
+// Loads of the moved data: non-temporal when every source byte is read once
+// (a streamed pool or a scatter's source rows), cached otherwise (aliased
+// pages are then fetched from HBM once and served from L2 after that).
+template <bool NT, typename V>
+__device__ __forceinline__ V ld_stream(const V *p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+// Stores of the moved data: non-temporal by default (nothing here re-reads
+// them).
+template <typename V>
+__device__ __forceinline__ void st_stream(V v, V *p) {
+#if HP_STORE_NT
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+// Division by a launch-invariant 32-bit divisor d as a multiply and a shift:
+// q = (umulhi(n, mul) + n) >> shift with shift = ceil(log2 d) and
+// mul = floor(2^32 (2^shift - d) / d) + 1, exact for every 32-bit n
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994).
+struct Div {
+    uint32_t d, mul, shift;
+};
 
 // Device-side view of a launch. Offsets inside one unit are 32-bit (the host
 // guarantees rows_per_unit * row bytes < 2^31); page and row bases are 64-bit.
@@ -75,7 +111,8 @@ struct Args {
     uint32_t out_row_bytes;   // logical-tensor row
     uint32_t zero_tail;
     uint32_t vecs_per_row;    // dequant: input vectors per row
-    uint32_t vpr_mul, vpr_shift;  // x / vecs_per_row = (umulhi(x, mul) + x) >> shift
+    Div div_vpr, div_rpc, div_page, div_upp;  // by vecs_per_row, rows_per_unit,
+                                              // page_size, units_per_page
 };
 
 __device__ __forceinline__ uint64_t min64(uint64_t a, uint64_t b) { return a < b ? a : b; }
@@ -88,6 +125,15 @@ __device__ __forceinline__ uint64_t uni64(uint64_t x) {
     uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
     uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
     return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t udiv32(uint32_t n, Div f) {
+    return (uint32_t)(((uint64_t)__umulhi(n, f.mul) + n) >> f.shift);
+}
+__device__ __forceinline__ uint64_t udiv(uint64_t n, Div f) {
+    if ((n >> 32) == 0)
+        return udiv32((uint32_t)n, f);
+    return n / f.d;
 }
 
 template <typename IdxT>
@@ -103,14 +149,14 @@ template <Op OP>
 __device__ __forceinline__ uint64_t units_of(const Args &a, uint64_t len, uint64_t start) {
     const uint64_t rpc = a.rows_per_unit;
     if (OP != Op::Scatter)
-        return (len + rpc - 1) / rpc;
+        return udiv(len + rpc - 1, a.div_rpc);
     if (len == 0)
         return 0;
     const uint64_t end = start + len;
-    const uint64_t w0 = start / rpc;
+    const uint64_t w0 = udiv(start, a.div_rpc);
     const uint64_t w1 = a.zero_tail
-        ? (end + a.page_size - 1) / a.page_size * a.units_per_page
-        : (end + rpc - 1) / rpc;
+        ? udiv(end + a.page_size - 1, a.div_page) * a.units_per_page
+        : udiv(end + rpc - 1, a.div_rpc);
     return w1 - w0;
 }
 
@@ -188,7 +234,7 @@ __device__ __forceinline__ void scan_range(const Args &a, uint32_t s0, uint32_t 
 
 // ---- span movers -------------------------------------------------------------
 
-template <int VEC>
+template <int VEC, bool NTL>
 __device__ __forceinline__ void copy_span(const unsigned char *__restrict__ src,
                                           unsigned char *__restrict__ dst, uint32_t nbytes) {
     using V = typename Vec<VEC>::T;
@@ -201,13 +247,13 @@ __device__ __forceinline__ void copy_span(const unsigned char *__restrict__ src,
         for (int j = 0; j < kCopyUnroll; ++j) {
             const uint32_t i = base + j * kThreads;
             if (i < n)
-                tmp[j] = s[i];
+                tmp[j] = ld_stream<NTL>(s + i);
         }
 #pragma unroll
         for (int j = 0; j < kCopyUnroll; ++j) {
             const uint32_t i = base + j * kThreads;
             if (i < n)
-                __builtin_nontemporal_store(tmp[j], d + i);
+                st_stream(tmp[j], d + i);
         }
     }
 }
@@ -219,7 +265,7 @@ __device__ __forceinline__ void zero_span(unsigned char *__restrict__ dst, uint3
     const uint32_t n = nbytes / VEC;
     const V z = V(0);
     for (uint32_t i = threadIdx.x; i < n; i += kThreads)
-        __builtin_nontemporal_store(z, d + i);
+        st_stream(z, d + i);
 }
 
 // fp32 -> bf16 bits, round to nearest even (gfx950 has a hardware
@@ -258,12 +304,12 @@ __device__ __forceinline__ void dequant_span(const Args &a, const unsigned char 
         for (int j = 0; j < kDequantUnroll; ++j) {
             const uint32_t i = base + j * kThreads;
             if (i < n)
-                q[j] = s[i];
+                q[j] = ld_stream<false>(s + i);
         }
 #pragma unroll
         for (int j = 0; j < kDequantUnroll; ++j) {
             const uint32_t i = base + j * kThreads;
-            const uint32_t row = (__umulhi(i, a.vpr_mul) + i) >> a.vpr_shift;
+            const uint32_t row = udiv32(i, a.div_vpr);
             const float sc = __shfl(my_scale, (int)row, 64);
             if (i < n) {
                 if constexpr (VIN == 8) {
@@ -273,20 +319,20 @@ __device__ __forceinline__ void dequant_span(const Args &a, const unsigned char 
                     o.y = pack_bf16x2(sbyte(w.x, 2) * sc, sbyte(w.x, 3) * sc);
                     o.z = pack_bf16x2(sbyte(w.y, 0) * sc, sbyte(w.y, 1) * sc);
                     o.w = pack_bf16x2(sbyte(w.y, 2) * sc, sbyte(w.y, 3) * sc);
-                    __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(dst) + i);
+                    st_stream(o, reinterpret_cast<u32x4 *>(dst) + i);
                 } else if constexpr (VIN == 4) {
                     const uint32_t w = q[j];
                     u32x2 o;
                     o.x = pack_bf16x2(sbyte(w, 0) * sc, sbyte(w, 1) * sc);
                     o.y = pack_bf16x2(sbyte(w, 2) * sc, sbyte(w, 3) * sc);
-                    __builtin_nontemporal_store(o, reinterpret_cast<u32x2 *>(dst) + i);
+                    st_stream(o, reinterpret_cast<u32x2 *>(dst) + i);
                 } else if constexpr (VIN == 2) {
                     const uint32_t w = q[j];
                     const uint32_t o = pack_bf16x2(sbyte(w, 0) * sc, sbyte(w, 1) * sc);
-                    __builtin_nontemporal_store(o, reinterpret_cast<uint32_t *>(dst) + i);
+                    st_stream(o, reinterpret_cast<uint32_t *>(dst) + i);
                 } else {
                     const uint16_t o = to_bf16(sbyte(q[j], 0) * sc);
-                    __builtin_nontemporal_store(o, reinterpret_cast<uint16_t *>(dst) + i);
+                    st_stream(o, reinterpret_cast<uint16_t *>(dst) + i);
                 }
             }
         }
@@ -297,7 +343,7 @@ __device__ __forceinline__ void dequant_span(const Args &a, const unsigned char 
 
 // One kernel for all three moves. FUSED: per-sequence offsets rebuilt in LDS
 // (dynamic LDS = 8*S + 4*S bytes); otherwise read from the plan arrays.
-template <typename IdxT, Op OP, int VEC, bool FUSED>
+template <typename IdxT, Op OP, int VEC, bool FUSED, bool NTL>
 __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const uint32_t S = a.num_seqs;
@@ -351,9 +397,9 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
         const uint32_t u = g - ubeg;
         if constexpr (OP == Op::Scatter) {
             // Window w of absolute positions [w*rpc, (w+1)*rpc) of sequence s.
-            const uint64_t w = start / rpc + u;
+            const uint64_t w = udiv(start, a.div_rpc) + u;
             const uint64_t pos0 = w * rpc;
-            const uint64_t q = w / a.units_per_page;
+            const uint64_t q = udiv(w, a.div_upp);
             const uint32_t slot0 = (uint32_t)(pos0 - q * P);
             const uint64_t phys = uni64(ld_idx<IdxT>(a.block_table, sp + q));
             const uint64_t end = start + len;
@@ -362,11 +408,11 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
             const uint64_t wb = pos0 + rpc < end ? pos0 + rpc : end;
             if (wa < wb) {
                 const unsigned char *from = a.src + (tb + (wa - start)) * a.row_bytes;
-                copy_span<VEC>(from, page + (slot0 + (uint32_t)(wa - pos0)) * a.row_bytes,
+                copy_span<VEC, NTL>(from, page + (slot0 + (uint32_t)(wa - pos0)) * a.row_bytes,
                                (uint32_t)(wb - wa) * a.row_bytes);
             }
             if (a.zero_tail) {
-                const uint64_t zend = (end + P - 1) / P * P;
+                const uint64_t zend = udiv(end + P - 1, a.div_page) * P;
                 const uint64_t za = pos0 > end ? pos0 : end;
                 const uint64_t zb = pos0 + rpc < zend ? pos0 + rpc : zend;
                 if (za < zb)
@@ -376,13 +422,13 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
         } else {
             const uint64_t t0 = (uint64_t)u * rpc;
             const uint32_t rows = (uint32_t)min64(rpc, len - t0);
-            const uint32_t q = u / a.units_per_page;
+            const uint32_t q = udiv32(u, a.div_upp);
             const uint32_t slot0 = (u - q * a.units_per_page) * rpc;
             const uint64_t phys = uni64(ld_idx<IdxT>(a.block_table, sp + q));
             const unsigned char *from = a.pool_r + (phys * P + slot0) * a.row_bytes;
             unsigned char *to = a.out + (tb + t0) * a.out_row_bytes;
             if constexpr (OP == Op::Gather) {
-                copy_span<VEC>(from, to, rows * a.row_bytes);
+                copy_span<VEC, NTL>(from, to, rows * a.row_bytes);
             } else {
                 dequant_span<VEC>(a, from, a.scales + phys * P + slot0, to, rows);
             }
@@ -510,12 +556,12 @@ __global__ __launch_bounds__(256) void validate_kernel(VArgs a) {
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-template <typename IdxT, Op OP, int VEC>
+template <typename IdxT, Op OP, int VEC, bool NTL>
 hipError_t launch_vec(const Args &a, bool fused, uint32_t grid, uint32_t plan_chunks,
                       uint32_t *unit_end, uint64_t *tok_begin, hipStream_t stream) {
     if (fused) {
         const size_t lds = 12 * (size_t)a.num_seqs;
-        hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, true>), dim3(grid), dim3(kThreads), lds,
+        hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, true, NTL>), dim3(grid), dim3(kThreads), lds,
                            stream, a);
         return hipGetLastError();
     }
@@ -530,39 +576,71 @@ hipError_t launch_vec(const Args &a, bool fused, uint32_t grid, uint32_t plan_ch
                        a, unit_end, tok_begin);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, false, NTL>), dim3(grid), dim3(kThreads), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
+// Load policy per move: a gather streams the pool only when the caller says no
+// page is read twice; scatter and dequant read through the cache (measured on
+// MI355X: non-temporal source loads gain nothing for the decode-batch scatter
+// and slow the small append scatter; dequant's 1:2 read:write mix prefers
+// cached loads too).
+template <typename IdxT, Op OP, int VEC>
+hipError_t launch_policy(const Args &a, bool ntl, bool fused, uint32_t grid, uint32_t chunks,
+                         uint32_t *ue, uint64_t *tb, hipStream_t st) {
+    if constexpr (OP == Op::Gather) {
+        if (ntl)
+            return launch_vec<IdxT, OP, VEC, true>(a, fused, grid, chunks, ue, tb, st);
+        return launch_vec<IdxT, OP, VEC, false>(a, fused, grid, chunks, ue, tb, st);
+    } else {
+        return launch_vec<IdxT, OP, VEC, false>(a, fused, grid, chunks, ue, tb, st);
+    }
+}
+
 template <typename IdxT, Op OP>
-hipError_t launch_op(const Args &a, uint32_t vec, bool fused, uint32_t grid, uint32_t chunks,
-                     uint32_t *ue, uint64_t *tb, hipStream_t st) {
+hipError_t launch_op(const Args &a, uint32_t vec, bool ntl, bool fused, uint32_t grid,
+                     uint32_t chunks, uint32_t *ue, uint64_t *tb, hipStream_t st) {
     if constexpr (OP == Op::Dequant) {
         switch (vec) {
-        case 8: return launch_vec<IdxT, OP, 8>(a, fused, grid, chunks, ue, tb, st);
-        case 4: return launch_vec<IdxT, OP, 4>(a, fused, grid, chunks, ue, tb, st);
-        case 2: return launch_vec<IdxT, OP, 2>(a, fused, grid, chunks, ue, tb, st);
-        default: return launch_vec<IdxT, OP, 1>(a, fused, grid, chunks, ue, tb, st);
+        case 8: return launch_policy<IdxT, OP, 8>(a, ntl, fused, grid, chunks, ue, tb, st);
+        case 4: return launch_policy<IdxT, OP, 4>(a, ntl, fused, grid, chunks, ue, tb, st);
+        case 2: return launch_policy<IdxT, OP, 2>(a, ntl, fused, grid, chunks, ue, tb, st);
+        default: return launch_policy<IdxT, OP, 1>(a, ntl, fused, grid, chunks, ue, tb, st);
         }
     } else {
         switch (vec) {
-        case 16: return launch_vec<IdxT, OP, 16>(a, fused, grid, chunks, ue, tb, st);
-        case 8: return launch_vec<IdxT, OP, 8>(a, fused, grid, chunks, ue, tb, st);
-        case 4: return launch_vec<IdxT, OP, 4>(a, fused, grid, chunks, ue, tb, st);
-        case 2: return launch_vec<IdxT, OP, 2>(a, fused, grid, chunks, ue, tb, st);
-        default: return launch_vec<IdxT, OP, 1>(a, fused, grid, chunks, ue, tb, st);
+        case 16: return launch_policy<IdxT, OP, 16>(a, ntl, fused, grid, chunks, ue, tb, st);
+        case 8: return launch_policy<IdxT, OP, 8>(a, ntl, fused, grid, chunks, ue, tb, st);
+        case 4: return launch_policy<IdxT, OP, 4>(a, ntl, fused, grid, chunks, ue, tb, st);
+        case 2: return launch_policy<IdxT, OP, 2>(a, ntl, fused, grid, chunks, ue, tb, st);
+        default: return launch_policy<IdxT, OP, 1>(a, ntl, fused, grid, chunks, ue, tb, st);
         }
     }
 }
 
 template <typename IdxT>
-hipError_t launch_idx(const Args &a, Op op, uint32_t vec, bool fused, uint32_t grid,
+hipError_t launch_idx(const Args &a, Op op, uint32_t vec, bool ntl, bool fused, uint32_t grid,
                       uint32_t chunks, uint32_t *ue, uint64_t *tb, hipStream_t st) {
     switch (op) {
-    case Op::Gather: return launch_op<IdxT, Op::Gather>(a, vec, fused, grid, chunks, ue, tb, st);
-    case Op::Scatter: return launch_op<IdxT, Op::Scatter>(a, vec, fused, grid, chunks, ue, tb, st);
-    default: return launch_op<IdxT, Op::Dequant>(a, vec, fused, grid, chunks, ue, tb, st);
+    case Op::Gather:
+        return launch_op<IdxT, Op::Gather>(a, vec, ntl, fused, grid, chunks, ue, tb, st);
+    case Op::Scatter:
+        return launch_op<IdxT, Op::Scatter>(a, vec, ntl, fused, grid, chunks, ue, tb, st);
+    default:
+        return launch_op<IdxT, Op::Dequant>(a, vec, ntl, fused, grid, chunks, ue, tb, st);
     }
+}
+
+Div make_div(uint32_t d) {
+    Div f;
+    f.d = d;
+    f.shift = 0;
+    while ((1ull << f.shift) < d)
+        ++f.shift;
+    const unsigned __int128 num = ((unsigned __int128)1 << 32) * (((uint64_t)1 << f.shift) - d);
+    f.mul = (uint32_t)(num / d + 1);
+    return f;
 }
 
 } // namespace
@@ -573,6 +651,10 @@ uint64_t plan_workspace_bytes(uint64_t num_seqs) {
 }
 
 hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
+    // hipGetLastError reports the thread's last error from any HIP call; clear
+    // what earlier calls (not ours) left so that the checks after each launch
+    // see only that launch.
+    (void)hipGetLastError();
     Args a = {};
     a.pool_r = static_cast<const unsigned char *>(job.pool);
     a.pool_w = static_cast<unsigned char *>(job.pool_w);
@@ -591,19 +673,12 @@ hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
     a.row_bytes = (uint32_t)job.row_bytes;
     a.out_row_bytes = (uint32_t)job.out_row_bytes;
     a.zero_tail = job.zero_tail ? 1u : 0u;
-    if (job.op == Op::Dequant) {
-        // Divisor for the row of an input vector: x / v = (umulhi(x, m) + x) >> l
-        // with l = ceil(log2 v), m = floor(2^32 (2^l - v) / v) + 1, exact for
-        // x < 2^31 (division by invariant integers using multiplication,
-        // Granlund and Montgomery, 1994).
-        const uint32_t v = (uint32_t)(job.row_bytes / job.vec_bytes);
-        uint32_t l = 0;
-        while ((1ull << l) < v)
-            ++l;
-        a.vecs_per_row = v;
-        a.vpr_mul = (uint32_t)(((1ull << 32) * ((1ull << l) - v)) / v + 1);
-        a.vpr_shift = l;
-    }
+    if (job.op == Op::Dequant)
+        a.vecs_per_row = (uint32_t)(job.row_bytes / job.vec_bytes);
+    a.div_vpr = make_div(a.vecs_per_row ? a.vecs_per_row : 1);
+    a.div_rpc = make_div(job.rows_per_unit);
+    a.div_page = make_div(job.page_size);
+    a.div_upp = make_div(a.units_per_page);
     const bool fused = job.num_seqs <= kFusedMaxSeqs;
     const uint64_t grid64 = (job.unit_bound + job.units_per_group - 1) / job.units_per_group;
     const uint32_t grid = (uint32_t)grid64;
@@ -621,8 +696,10 @@ hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
         a.g_tok_begin = tb;
     }
     if (job.idx64)
-        return launch_idx<uint64_t>(a, job.op, job.vec_bytes, fused, grid, chunks, ue, tb, stream);
-    return launch_idx<uint32_t>(a, job.op, job.vec_bytes, fused, grid, chunks, ue, tb, stream);
+        return launch_idx<uint64_t>(a, job.op, job.vec_bytes, job.load_nt, fused, grid, chunks, ue,
+                                    tb, stream);
+    return launch_idx<uint32_t>(a, job.op, job.vec_bytes, job.load_nt, fused, grid, chunks, ue, tb,
+                                stream);
 }
 
 hipError_t launch_validate(const ValidateJob &job, hipStream_t stream) {
@@ -636,6 +713,7 @@ hipError_t launch_validate(const ValidateJob &job, hipStream_t stream) {
     a.page_size = job.page_size;
     a.num_seqs = job.num_seqs;
     a.num_block_entries = job.num_block_entries;
+    (void)hipGetLastError();  // see launch_copy
     hipLaunchKernelGGL(validate_init_kernel, dim3(1), dim3(64), 0, stream, a.ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

@@ -82,9 +82,14 @@ enum {
 /* Flags. */
 enum {
     HP_FLAG_CHECKED = 1u << 0,   /* validate first; on a violation write nothing */
-    HP_FLAG_ZERO_TAIL = 1u << 1  /* scatter: zero the slots of each sequence's last
+    HP_FLAG_ZERO_TAIL = 1u << 1, /* scatter: zero the slots of each sequence's last
                                     written page past its last new token ([Hurray]
                                     Partial trailing page: a writer should zero them) */
+    HP_FLAG_STREAM = 1u << 2     /* gather: performance hint that no pool page is read
+                                    twice by this call (the slices do not alias, [Hurray]
+                                    Prefix Sharing); the pool is then read with
+                                    non-temporal loads. Results are identical with or
+                                    without it; with aliased pages it is only slower. */
 };
 
 /* A block-paged descriptor for one {kv_role, layer_index} pair ([Hurray]
@@ -153,7 +158,7 @@ hp_status hp_validate(const hp_desc *desc, const void *seq_start, void *workspac
  * of T*H*D elements of desc->dtype, element aligned, not overlapping
  * page_pool. No slot at or past a sequence's token count is read ([Hurray]
  * Partial trailing page). Slices may alias pages. Asynchronous.
- * Flags: HP_FLAG_CHECKED. */
+ * Flags: HP_FLAG_CHECKED, HP_FLAG_STREAM. */
 hp_status hp_gather(const hp_desc *desc, void *out, void *workspace,
                     size_t workspace_bytes, uint32_t flags, void *stream);
 
@@ -184,6 +189,11 @@ hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype,
 
 /* Static, human-readable name of a status code. */
 const char *hp_status_str(int status);
+
+/* Name of the HIP error (e.g. "hipErrorInvalidValue") behind the calling
+ * thread's most recent HP_ERR_HIP, or "hipSuccess" if it has had none. The
+ * value is kept per thread. Static string; never NULL. */
+const char *hp_last_hip_error(void);
 
 #ifdef __cplusplus
 }

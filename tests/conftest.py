@@ -36,8 +36,12 @@ def pytest_sessionstart(session):
     if not os.path.exists(lib):
         import torch
         if not torch.cuda.is_available():
-            from block_table_gather_amd import build as hbuild
-            hbuild.build()
+            import importlib.util
+            spec = importlib.util.spec_from_file_location(
+                "_hp_build", os.path.join(ROOT, "block_table_gather_amd", "build.py"))
+            mod = importlib.util.module_from_spec(spec)
+            spec.loader.exec_module(mod)
+            mod.build()
 
 
 def pytest_collection_modifyitems(config, items):

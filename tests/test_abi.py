@@ -24,7 +24,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"hp_workspace_bytes", "hp_validate", "hp_gather", "hp_scatter",
-                          "hp_gather_dequant", "hp_status_str"}
+                          "hp_gather_dequant", "hp_status_str", "hp_last_hip_error"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -33,6 +33,7 @@ def test_status_strings():
     for code, name in hp.STATUS.items():
         assert hp.status_str(code).startswith(name)
     assert hp.status_str(999) == "unknown hp_status"
+    assert hp.last_hip_error() == "hipSuccess"
 
 
 def desc(**kw):
@@ -104,7 +105,9 @@ def test_call_buffer_rejections():
     assert gather(d, out=None) == S["HP_ERR_NULL"]
     assert gather(d, out=OUT + 1) == S["HP_ERR_ALIGN"]
     assert gather(d, out=ALIGNED + 64) == S["HP_ERR_ARG"]            # overlaps the pool
-    assert gather(d, flags=4) == S["HP_ERR_ARG"]                     # unknown flag
+    assert gather(d, flags=8) == S["HP_ERR_ARG"]                     # unknown flag
+    assert L.hp_scatter(ctypes.byref(d), OUT, None, None, 0, hp.HP_FLAG_STREAM, None) == \
+        S["HP_ERR_ARG"]                                              # gather-only hint
     assert gather(d, flags=hp.HP_FLAG_ZERO_TAIL) == S["HP_ERR_ARG"]  # scatter-only flag
     assert gather(d, flags=hp.HP_FLAG_CHECKED) == S["HP_ERR_WORKSPACE"]
     assert gather(d, ws=OUT + 0x100000, n=255, flags=hp.HP_FLAG_CHECKED) == S["HP_ERR_WORKSPACE"]

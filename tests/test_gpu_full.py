@@ -33,7 +33,7 @@ def test_decode_gather_and_round_trip(hp):
     d = OnDevice(w)
     assert hp.validate(d.desc, w.total_tokens) == ("HP_OK", 0)
     out = d.empty_out()
-    hp.gather(d.desc, out)
+    hp.gather(d.desc, out, streaming=True)  # unique pages: the benchmark's launch
     torch.cuda.synchronize()
     pool_host = host_bits(d.pool)
     want = oracle.gather(pool_host, **d.oracle_kw())
@@ -144,7 +144,7 @@ def test_pool_beyond_4gib_uses_64bit_offsets(hp):
     say("pool > 4 GiB", w.describe())
     d = OnDevice(w)
     out = d.empty_out()
-    hp.gather(d.desc, out)
+    hp.gather(d.desc, out, streaming=True)  # unique pages: the benchmark's launch
     torch.cuda.synchronize()
     pool_host = host_bits(d.pool).view(np.int8)
     assert_bits_equal(host_bits(out).view(np.int8),

@@ -43,13 +43,14 @@ def test_gather_small(hp, seed):
     assert_bits_equal(host_bits(out), oracle_gather(d), f"seed {seed}")
 
 
+@pytest.mark.parametrize("streaming", [False, True])
 @pytest.mark.parametrize("seed", range(24))
-def test_gather_medium(hp, seed):
+def test_gather_medium(hp, seed, streaming):
     w = medium(100 + seed)
-    say("gather medium", seed, w.describe())
+    say("gather medium", seed, streaming, w.describe())
     d = OnDevice(w)
     out = d.empty_out()
-    hp.gather(d.desc, out)
+    hp.gather(d.desc, out, streaming=streaming)
     torch.cuda.synchronize()
     assert_bits_equal(host_bits(out), oracle_gather(d), f"seed {seed}")
 
