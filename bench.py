@@ -3,24 +3,34 @@
 
 One step is one pass of every stage of the path over one batch of the decode
 workload (64 sequences, lengths uniform in 1..2048, page_size 16, 32 heads x
-128 fp16, 12,000-page pool, uint32 block table):
+128 fp16, 12,000-page pool, uint32 block table of unique pages):
 
   1. hp_validate        storage invariants of the descriptor (synchronous);
-  2. hp_gather          pool -> logical [T, 32, 128] fp16 tensor;
+  2. hp_gather          pool -> logical [T, 32, 128] fp16 tensor (streaming hint:
+                        the table names each page once);
   3. hp_scatter         that tensor back into its slots (the write direction);
   4. hp_gather_dequant  the same table over an int8 copy of the pool with one
                         fp32 scale per slot -> bf16 [T, 32, 128].
 
 Inputs are resident in HBM before timing starts. `value` is the step's
-algorithmic bytes (each live row read once and written once per move, scales,
-metadata read by the validator) over the measured step time, in GB/s
-(1 GB = 1e9 B). Per-stage kernel times come from HIP events recorded on the
-launch stream around each call. The CPU oracle is timed on the host on a
+algorithmic bytes (each live row read once and written once per move, one
+scale per row, the validator's metadata reads) over the wall-clock step time
+(K steps bracketed by device synchronisation), in GB/s (1 GB = 1e9 B).
+
+Per-kernel launch durations come from HIP events on the launch stream around
+back-to-back launches of each kernel (the GPU stays busy, so the interval is
+kernel time); `roofline` uses the gather kernel's. The per-stage times inside
+the step (`ops[*].in_step_ms`) also include the host's launch latency after
+the validator's synchronisation. The CPU oracle is timed on the host on a
 bounded prefix of the same batch (single-threaded, as it stands).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR
+      (writes the rocprofv3 summaries under profiles/)
 """
 import argparse
+import ctypes
 import dataclasses
 import hashlib
 import json
@@ -33,13 +43,31 @@ sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s (and % of peak) for paged gather/scatter, tokens/s"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "block_table_gather_amd", "csrc", "hp_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gather_copy_kernel_decode_traffic.json")
+CSRC = os.path.join(ROOT, "block_table_gather_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("hp_kernels.hip", "hp_api.cpp", "hp_internal.h")]
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "gather_copy_kernel_decode_traffic.json")
+GATHER_KERNEL = "copy_kernel<unsigned int, (hp::Op)0, 16, true, true>"
+KERNEL_LABELS = {
+    "copy_kernel<unsigned int, (hp::Op)0, 16, true, true>": "gather (u32, 16 B vectors, fused, streaming loads)",
+    "copy_kernel<unsigned int, (hp::Op)1, 16, true, false>": "scatter (u32, 16 B vectors, fused)",
+    "copy_kernel<unsigned int, (hp::Op)2, 8, true, false>": "dequant-gather (u32, 8 B int8 vectors, fused)",
+    "validate_kernel<unsigned int>": "validator (u32)",
+    "validate_init_kernel": "validator init",
+}
+CALIBRATION_BYTES = 1 << 30
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o trace -- "
+             "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline")
+PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/prof_{d} -o {d} -- "
+           "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration")
 
 
 def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def step_bytes(T, S, K, H, D, idx_bytes=4):
@@ -52,9 +80,9 @@ def step_bytes(T, S, K, H, D, idx_bytes=4):
     return {"validate": validate, "gather": gather, "scatter": scatter, "dequant": dequant}
 
 
-def traffic_for(launch_count_bytes):
+def traffic_for():
     """HBM bytes per gather launch from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
+    was taken on the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -62,7 +90,7 @@ def traffic_for(launch_count_bytes):
         return None
     if t.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return t.get("bytes_per_launch")
+    return t.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(w, pool_h, qpool_h, scales_h, seconds):
@@ -71,7 +99,6 @@ def cpu_baseline(w, pool_h, qpool_h, scales_h, seconds):
     import numpy as np
     import oracle
     lens = w.seq_lens.astype(np.int64)
-    # estimate from the first sequence, then take a prefix of ~`seconds`
     kw = dict(page_size=w.page_size, num_heads=w.num_heads, head_dim=w.head_dim)
 
     def run(n):
@@ -104,6 +131,118 @@ def cpu_baseline(w, pool_h, qpool_h, scales_h, seconds):
                       "one step: validate + gather + scatter + dequant-gather, single thread"}
 
 
+# ---- rocprofv3 summaries --------------------------------------------------------
+
+def _short(name):
+    name = name.replace("hp::(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    return name.rsplit("(", 1)[0]  # drop the parameter list
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir):
+    """Writes the kernel-trace and counter summaries (markdown) and the gather
+    kernel's calibrated traffic (json) under profiles/."""
+    import csv
+    import glob
+
+    def one(d, pattern):
+        files = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+        if len(files) != 1:
+            raise SystemExit(f"expected one {pattern} under {d}, found {files}")
+        with open(files[0]) as f:
+            return list(csv.DictReader(f))
+
+    stats = one(trace_dir, "*kernel_stats.csv")
+    lines = ["# Kernel durations: decode-batch bench step (rocprofv3 kernel trace)", "",
+             "Command (from the repository root, on one MI355X):", "",
+             f"    {TRACE_CMD}", "",
+             "All launches of the run (50 timed + 5 warm-up steps, plus the back-to-back",
+             "kernel-timing launches of each move). Durations in microseconds.", "",
+             "| kernel | what | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    gather_avg = None
+    for r in stats:
+        short = _short(r["Name"])
+        if short not in KERNEL_LABELS:
+            continue
+        avg = float(r["AverageNs"]) / 1e3
+        if short == GATHER_KERNEL:
+            gather_avg = avg
+        lines.append(f"| `{short}` | {KERNEL_LABELS[short]} | {r['Calls']} | {avg:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    lines += ["", "Other kernels in the trace are PyTorch's input generation (random values,",
+              "fills, index_put) and the runtime's copies; they are outside the timed step."]
+    with open(os.path.join(PROFILES, "decode_step_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def per_kernel(rows, counter):
+        agg = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            agg.setdefault(r["Kernel_Name"], []).append((int(r["Grid_Size"]),
+                                                         float(r["Counter_Value"])))
+        return agg
+
+    fetch = per_kernel(one(fetch_dir, "*counter_collection.csv"), "FETCH_SIZE")
+    write = per_kernel(one(write_dir, "*counter_collection.csv"), "WRITE_SIZE")
+
+    def calib(agg):
+        # the 1 GiB calibration copies are the runtime copy kernel's largest grids
+        rows = agg.get("__amd_rocclr_copyBuffer", [])
+        g = max(x[0] for x in rows)
+        vals = [x[1] for x in rows if x[0] == g]
+        return sum(vals) / len(vals), len(vals)
+
+    f_kib, nf = calib(fetch)
+    w_kib, nw = calib(write)
+    f_factor = CALIBRATION_BYTES / (f_kib * 1024)
+    w_factor = CALIBRATION_BYTES / (w_kib * 1024)
+    out = ["# HBM traffic per launch: decode-batch kernels (rocprofv3 counters)", "",
+           "Two counter passes, each in its own run (commands from the repository root):", "",
+           f"    {PMC_CMD.format(c='FETCH_SIZE', d='fetch')}",
+           f"    {PMC_CMD.format(c='WRITE_SIZE', d='write')}", "",
+           "Calibration: `--copy-calibration` runs three plain 1 GiB device-to-device copies",
+           "(the runtime's copy kernel) that read and write exactly 1,073,741,824 bytes.",
+           f"They read FETCH_SIZE = {f_kib:.1f} KiB ({nf} dispatches) and WRITE_SIZE = "
+           f"{w_kib:.1f} KiB ({nw}),",
+           f"so bytes = FETCH_SIZE x 1024 x {f_factor:.4f} and WRITE_SIZE x 1024 x {w_factor:.4f}.", "",
+           "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read GB | HBM write GB | total GB |",
+           "|---|---|---|---|---|---|"]
+    traffic = None
+    for name in sorted(fetch):
+        short = _short(name)
+        if short not in KERNEL_LABELS or name not in write:
+            continue
+        fk = sum(v for _, v in fetch[name]) / len(fetch[name])
+        wk = sum(v for _, v in write[name]) / len(write[name])
+        rb, wb = fk * 1024 * f_factor, wk * 1024 * w_factor
+        out.append(f"| `{short}` | {fk:.1f} | {wk:.1f} | {rb / 1e9:.4f} | {wb / 1e9:.4f} | "
+                   f"{(rb + wb) / 1e9:.4f} |")
+        if short == GATHER_KERNEL:
+            traffic = {"kernel": short, "fetch_kib": fk, "write_kib": wk,
+                       "hbm_read_bytes": round(rb), "hbm_write_bytes": round(wb),
+                       "hbm_bytes_per_launch": round(rb + wb)}
+    out += ["", "Per launch, averaged over the run's launches of each kernel. The gather's",
+            "algorithmic bytes per launch are 1,041,039,360 (63,540 rows of 8 KiB read once",
+            "and written once)."]
+    with open(os.path.join(PROFILES, "decode_step_hbm_traffic.md"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    if traffic is None:
+        raise SystemExit("gather kernel not found in the counter runs")
+    traffic.update({"kernel_source_sha256_16": kernel_source_hash(),
+                    "fetch_factor": f_factor, "write_factor": w_factor,
+                    "calibration_bytes": CALIBRATION_BYTES,
+                    "rocprof_avg_launch_us": gather_avg,
+                    "commands": [PMC_CMD.format(c="FETCH_SIZE", d="fetch"),
+                                 PMC_CMD.format(c="WRITE_SIZE", d="write")]})
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(traffic, f, indent=1)
+    print(json.dumps(traffic))
+
+
+# ---- the benchmark -------------------------------------------------------------
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,9 +250,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernel-reps", type=int, default=20,
+                    help="back-to-back launches per kernel for the launch durations")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (counter calibration runs)")
+                    help="also run plain 1 GiB device copies (counter calibration runs)")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"))
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: --gpus {args.gpus} (WORLD_SIZE {world}) requested, but this build "
@@ -147,29 +292,45 @@ def main():
     qout = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(max(hp.workspace_bytes(desc, T), 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-
     if hp.validate(desc, T, workspace=ws) != ("HP_OK", 0):
         raise SystemExit("bench descriptor failed validation")
 
-    names = ("validate", "gather", "scatter", "dequant")
+    # Arguments marshalled once; each call below is one C-ABI call.
+    L = hp.lib()
+    sh = stream.cuda_stream
+    pd, pq = desc.with_tokens(T), qdesc.with_tokens(T)
+    wsp, wsn = ws.data_ptr(), ws.numel()
+    res = hp.HpValidateResult()
+    pres = ctypes.byref(res)
+    o_p, q_p = out.data_ptr(), qout.data_ptr()
+    bf16 = hp.DTYPE["bf16"]
+
+    def do_validate():
+        if L.hp_validate(pd, None, wsp, wsn, pres, sh) != 0:
+            raise SystemExit(f"hp_validate: {hp.status_str(res.code)}")
+
+    def do_gather():
+        if L.hp_gather(pd, o_p, wsp, wsn, hp.HP_FLAG_STREAM, sh) != 0:
+            raise SystemExit("hp_gather failed")
+
+    def do_scatter():
+        if L.hp_scatter(pd, o_p, None, wsp, wsn, 0, sh) != 0:
+            raise SystemExit("hp_scatter failed")
+
+    def do_dequant():
+        if L.hp_gather_dequant(pq, q_p, bf16, wsp, wsn, 0, sh) != 0:
+            raise SystemExit("hp_gather_dequant failed")
+
+    stages = [("validate", do_validate), ("gather", do_gather), ("scatter", do_scatter),
+              ("dequant", do_dequant)]
     events = []
 
     def step(record):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
-        if record:
-            ev[0].record(stream)
-        code = hp.validate(desc, T, workspace=ws, stream=stream)
-        if code[0] != "HP_OK":
-            raise SystemExit(f"validation failed: {code}")
-        if record:
-            ev[1].record(stream)
-        hp.gather(desc, out, streaming=True, workspace=ws, stream=stream)
-        if record:
-            ev[2].record(stream)
-        hp.scatter(desc, out, workspace=ws, stream=stream)
-        if record:
-            ev[3].record(stream)
-        hp.gather_dequant(qdesc, qout, workspace=ws, stream=stream)
+        for i, (_, fn) in enumerate(stages):
+            if record:
+                ev[i].record(stream)
+            fn()
         if record:
             ev[4].record(stream)
             events.append(ev)
@@ -191,18 +352,33 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    in_step_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events]))
+                  for i, (n, _) in enumerate(stages)}
 
-    per_op_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events]))
-                 for i, n in enumerate(names)}
+    # Launch durations: back-to-back launches of each kernel between two events.
+    launch_ms = {}
+    for n, fn in stages[1:]:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        a.record(stream)
+        for _ in range(args.kernel_reps):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        launch_ms[n] = a.elapsed_time(b) / args.kernel_reps
+
     nbytes = step_bytes(T, S, K, H, D)
     total_bytes = sum(nbytes.values())
     value = total_bytes / (ms_per_step / 1e3) / 1e9
-    ops = {n: {"ms": round(per_op_ms[n], 4),
-               "gb_per_s": round(nbytes[n] / (per_op_ms[n] / 1e3) / 1e9, 1),
-               "frac_of_hbm_peak": round(nbytes[n] / (per_op_ms[n] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-               "algorithmic_bytes": nbytes[n]} for n in names}
-    g_achieved = nbytes["gather"] / (per_op_ms["gather"] / 1e3) / 1e9
-    traffic = traffic_for(nbytes["gather"])
+    ops = {}
+    for n, _ in stages:
+        ms = launch_ms.get(n)
+        ops[n] = {"in_step_ms": round(in_step_ms[n], 4), "algorithmic_bytes": nbytes[n]}
+        if ms is not None:
+            gbs = nbytes[n] / (ms / 1e3) / 1e9
+            ops[n].update({"launch_ms": round(ms, 4), "gb_per_s": round(gbs, 1),
+                           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+    g_achieved = nbytes["gather"] / (launch_ms["gather"] / 1e3) / 1e9
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -226,13 +402,12 @@ def main():
         "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "ops": ops,
-        "roofline": {"bound": "hbm",
-                     "kernel": "copy_kernel (gather, fused, 16-byte vectors, streaming loads)",
+        "roofline": {"bound": "hbm", "kernel": GATHER_KERNEL + " (gather)",
                      "achieved": round(g_achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(g_achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
+                     "traffic": traffic_for(),
                      "algorithmic_bytes_per_launch": nbytes["gather"],
-                     "avg_launch_ms": round(per_op_ms["gather"], 4)},
+                     "avg_launch_ms": round(launch_ms["gather"], 4)},
     }
     if not args.no_cpu_baseline:
         pool_h = pool.view(torch.int16).cpu().numpy().view(np.uint16)
