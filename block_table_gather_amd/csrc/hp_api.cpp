@@ -202,9 +202,15 @@ hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const void *src
         j.load_nt = (flags & HP_FLAG_STREAM) != 0;
         break;
     case hp::Op::Scatter:
-        unit_bytes = HP_SCATTER_UNIT_BYTES;
-        j.units_per_group = HP_SCATTER_UNITS_PER_GROUP;
-        j.load_nt = false;
+        if (d->total_tokens * g.row_bytes >= HP_SCATTER_STREAM_BYTES / 2) {  // bytes moved
+            unit_bytes = HP_SCATTER_STREAM_UNIT_BYTES;
+            j.units_per_group = 1;
+            j.load_nt = true;
+        } else {
+            unit_bytes = HP_SCATTER_UNIT_BYTES;
+            j.units_per_group = HP_SCATTER_UNITS_PER_GROUP;
+            j.load_nt = false;
+        }
         break;
     default:
         unit_bytes = HP_DEQUANT_UNIT_BYTES;

@@ -28,6 +28,16 @@ namespace hp {
 #ifndef HP_SCATTER_UNITS_PER_GROUP
 #define HP_SCATTER_UNITS_PER_GROUP 2
 #endif
+// A scatter that moves at least this many bytes cannot stay resident in the
+// 256 MB Infinity Cache (MALL): it streams its source with non-temporal loads
+// in small units; smaller scatters (appends) read through the cache in larger
+// units, which measured faster when their source is cache-resident.
+#ifndef HP_SCATTER_STREAM_BYTES
+#define HP_SCATTER_STREAM_BYTES (256ull << 20)
+#endif
+#ifndef HP_SCATTER_STREAM_UNIT_BYTES
+#define HP_SCATTER_STREAM_UNIT_BYTES 8192
+#endif
 #ifndef HP_DEQUANT_UNITS_PER_GROUP
 #define HP_DEQUANT_UNITS_PER_GROUP 1
 #endif

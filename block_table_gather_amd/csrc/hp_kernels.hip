@@ -581,19 +581,22 @@ hipError_t launch_vec(const Args &a, bool fused, uint32_t grid, uint32_t plan_ch
     return hipGetLastError();
 }
 
-// Load policy per move: a gather streams the pool only when the caller says no
-// page is read twice; scatter and dequant read through the cache (measured on
-// MI355X: non-temporal source loads gain nothing for the decode-batch scatter
-// and slow the small append scatter; dequant's 1:2 read:write mix prefers
-// cached loads too).
+// Load policy per move (chosen on the host, measured on MI355X): a gather
+// streams the pool only when the caller says no page is read twice; a scatter
+// streams its source only when the move is larger than the Infinity Cache;
+// dequant's 1:2 read:write mix reads through the cache.
 template <typename IdxT, Op OP, int VEC>
 hipError_t launch_policy(const Args &a, bool ntl, bool fused, uint32_t grid, uint32_t chunks,
                          uint32_t *ue, uint64_t *tb, hipStream_t st) {
     if constexpr (OP == Op::Gather) {
         if (ntl)
             return launch_vec<IdxT, OP, VEC, true>(a, fused, grid, chunks, ue, tb, st);
+        if (OP == Op::Scatter && ntl)
+            return launch_vec<IdxT, OP, VEC, true>(a, fused, grid, chunks, ue, tb, st);
         return launch_vec<IdxT, OP, VEC, false>(a, fused, grid, chunks, ue, tb, st);
     } else {
+        if (OP == Op::Scatter && ntl)
+            return launch_vec<IdxT, OP, VEC, true>(a, fused, grid, chunks, ue, tb, st);
         return launch_vec<IdxT, OP, VEC, false>(a, fused, grid, chunks, ue, tb, st);
     }
 }

@@ -157,3 +157,25 @@ def test_pool_beyond_4gib_uses_64bit_offsets(hp):
                     "dequant > 4 GiB")
     del d, out, outq
     _free()
+
+
+@pytest.mark.parametrize("zero_tail", [False, True])
+def test_large_ragged_scatter_streams(hp, zero_tail):
+    """A scatter moving more than the Infinity Cache holds (streamed source,
+    8 KB units) with ragged lengths, start offsets and tail zeroing: the
+    whole pool against the oracle."""
+    w = workloads.random_small(515 + int(zero_tail), max_seqs=96, max_len=2000,
+                               page_sizes=(16,), heads=(32,), dims=(128,), dtypes=("f16",),
+                               alias=False, with_start=True)
+    if 2 * w.total_tokens * w.row_bytes < (256 << 20):
+        pytest.skip("draw too small for the streaming path")
+    say("large scatter", zero_tail, w.describe())
+    d = OnDevice(w)
+    src = w.make_src(DEV)
+    want = oracle.scatter(host_bits(d.pool), host_bits(src), zero_tail=zero_tail,
+                          **d.oracle_kw(with_start=True))
+    hp.scatter(d.desc, src, d.ss, zero_tail=zero_tail)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_bits(d.pool), want, "large scatter")
+    del d, src, want
+    _free()
