@@ -300,7 +300,9 @@ def main():
     sh = stream.cuda_stream
     pd, pq = desc.with_tokens(T), qdesc.with_tokens(T)
     wsp, wsn = ws.data_ptr(), ws.numel()
-    res = hp.HpValidateResult()
+    res_mem = torch.zeros(ctypes.sizeof(hp.HpValidateResult), dtype=torch.uint8,
+                          pin_memory=True)  # pinned: the 16-byte result is a direct DMA
+    res = hp.HpValidateResult.from_address(res_mem.data_ptr())
     pres = ctypes.byref(res)
     o_p, q_p = out.data_ptr(), qout.data_ptr()
     bf16 = hp.DTYPE["bf16"]

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
 
 namespace {
 
@@ -135,12 +136,19 @@ hp_status run_validate(const hp_desc *d, const void *seq_start, void *ws,
     hipError_t e = hp::launch_validate(j, stream);
     if (e != hipSuccess)
         return hip_failed(e);
-    uint64_t host[2] = {0, 0};
-    if ((e = hipMemcpyAsync(host, ws, sizeof host, hipMemcpyDeviceToHost, stream)) != hipSuccess)
+    // The two result words are copied straight into the caller's result
+    // struct (16 bytes, like them), so that a result in pinned host memory
+    // takes a direct DMA; they are decoded in place after the wait.
+    static_assert(sizeof(hp_validate_result) == 2 * sizeof(uint64_t), "result layout");
+    if ((e = hipMemcpyAsync(res, ws, sizeof(hp_validate_result), hipMemcpyDeviceToHost,
+                            stream)) != hipSuccess)
         return hip_failed(e);
     if ((e = hipStreamSynchronize(stream)) != hipSuccess)
         return hip_failed(e);
+    uint64_t host[2];
+    memcpy(host, res, sizeof host);
     res->code = HP_OK;
+    res->reserved = 0;
     res->index = 0;
     if (host[0] != ~0ull) {
         static const hp_status by_rank[] = {HP_OK, HP_ERR_SEQPTR_FIRST, HP_ERR_SEQPTR_LAST,

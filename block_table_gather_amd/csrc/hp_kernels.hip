@@ -339,6 +339,27 @@ __device__ __forceinline__ void dequant_span(const Args &a, const unsigned char 
     }
 }
 
+#ifndef HP_XCD_REMAP
+#define HP_XCD_REMAP 0
+#endif
+constexpr uint32_t kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
+
+// Order in which workgroups take work. The dispatcher hands consecutive
+// workgroup IDs to the 8 XCDs in turn; with the remap, the workgroups that
+// land on one XCD take one contiguous range of work units (a bijection on
+// [0, groups)), so neighbouring units of one page share that XCD's L2.
+__device__ __forceinline__ uint32_t group_order(uint32_t b, uint32_t groups) {
+#if HP_XCD_REMAP
+    const uint32_t per = (groups + kXcds - 1) / kXcds;  // groups on the fullest XCDs
+    const uint32_t full = groups - (per - 1) * kXcds;   // XCDs that get `per` groups
+    const uint32_t xcd = b % kXcds, local = b / kXcds;
+    return xcd < full ? xcd * per + local : full * per + (xcd - full) * (per - 1) + local;
+#else
+    (void)groups;
+    return b;
+#endif
+}
+
 // ---- the copy kernel -----------------------------------------------------------
 
 // One kernel for all three moves. FUSED: per-sequence offsets rebuilt in LDS
@@ -360,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
         tok_begin = a.g_tok_begin;
     }
     const uint32_t total = uni(unit_end[S - 1]);
-    const uint32_t g0 = blockIdx.x * a.units_per_group;
+    const uint32_t g0 = group_order(blockIdx.x, gridDim.x) * a.units_per_group;
     if (g0 >= total)
         return;
     const uint32_t g1 = min32(g0 + a.units_per_group, total);
