@@ -369,6 +369,35 @@ def main():
         b.synchronize()
         launch_ms[n] = a.elapsed_time(b) / args.kernel_reps
 
+    # Reference copies of the gather's bytes: the same gather kernel on an
+    # identity table (one sequence over pages 0..K-1: a contiguous copy) and
+    # the runtime's plain device-to-device copy.
+    ident = hp.Descriptor(pool, idx(np.arange(K)), idx(np.array([0, K])), idx(np.array([K * 16])))
+    ident_out = torch.empty((K * 16, H, D), dtype=torch.float16, device=dev)
+    pi, io_p = ident.with_tokens(K * 16), ident_out.data_ptr()
+
+    def ident_gather():
+        if L.hp_gather(pi, io_p, wsp, wsn, hp.HP_FLAG_STREAM, sh) != 0:
+            raise SystemExit("hp_gather (identity table) failed")
+
+    def back_to_back(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        a.record(stream)
+        for _ in range(args.kernel_reps):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / args.kernel_reps
+
+    ident_bytes = 2 * K * 16 * H * D * 2
+    copy_src = pool.view(-1)[: K * 16 * H * D]
+    copy_dst = ident_out.view(-1)
+    refs = {"identity_table_gather": round(ident_bytes / (back_to_back(ident_gather) / 1e3) / 1e9, 1),
+            "runtime_device_copy": round(ident_bytes / (back_to_back(lambda: copy_dst.copy_(copy_src)) / 1e3) / 1e9, 1),
+            "unit": "GB/s", "bytes": ident_bytes}
+    del ident_out
+
     nbytes = step_bytes(T, S, K, H, D)
     total_bytes = sum(nbytes.values())
     value = total_bytes / (ms_per_step / 1e3) / 1e9
@@ -404,6 +433,7 @@ def main():
         "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "ops": ops,
+        "reference_copies": refs,
         "roofline": {"bound": "hbm", "kernel": GATHER_KERNEL + " (gather)",
                      "achieved": round(g_achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(g_achieved / HBM_PEAK_GBS, 4),
