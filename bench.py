@@ -50,6 +50,7 @@ TRAFFIC_FILE = os.path.join(PROFILES, "gather_copy_kernel_decode_traffic.json")
 GATHER_KERNEL = "copy_kernel<unsigned int, (hp::Op)0, 16, true, true>"
 KERNEL_LABELS = {
     "copy_kernel<unsigned int, (hp::Op)0, 16, true, true>": "gather (u32, 16 B vectors, fused, streaming loads)",
+    "copy_kernel<unsigned int, (hp::Op)1, 16, true, true>": "scatter (u32, 16 B vectors, fused, streamed source)",
     "copy_kernel<unsigned int, (hp::Op)1, 16, true, false>": "scatter (u32, 16 B vectors, fused)",
     "copy_kernel<unsigned int, (hp::Op)2, 8, true, false>": "dequant-gather (u32, 8 B int8 vectors, fused)",
     "validate_kernel<unsigned int>": "validator (u32)",
@@ -57,9 +58,10 @@ KERNEL_LABELS = {
 }
 CALIBRATION_BYTES = 1 << 30
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o trace -- "
-             "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline")
+             "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-reference-copies")
 PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/prof_{d} -o {d} -- "
-           "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration")
+           "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-reference-copies "
+           "--copy-calibration")
 
 
 def kernel_source_hash():
@@ -182,6 +184,12 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir):
                 continue
             agg.setdefault(r["Kernel_Name"], []).append((int(r["Grid_Size"]),
                                                          float(r["Counter_Value"])))
+        for name, vals in agg.items():
+            # one launch shape per kernel of the step; several would mean the
+            # run mixed other work into the same kernel's average
+            if "hp::" in name and len({g for g, _ in vals}) != 1:
+                raise SystemExit(f"{name}: several grid sizes in one run; profile with "
+                                 "--no-reference-copies")
         return agg
 
     fetch = per_kernel(one(fetch_dir, "*counter_collection.csv"), "FETCH_SIZE")
@@ -189,9 +197,12 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir):
 
     def calib(agg):
         # the 1 GiB calibration copies are the runtime copy kernel's largest grids
+        # (the profiled runs make no other large copy)
         rows = agg.get("__amd_rocclr_copyBuffer", [])
         g = max(x[0] for x in rows)
         vals = [x[1] for x in rows if x[0] == g]
+        if len(vals) != 3:
+            raise SystemExit(f"expected the 3 calibration copies, found {len(vals)}")
         return sum(vals) / len(vals), len(vals)
 
     f_kib, nf = calib(fetch)
@@ -254,6 +265,8 @@ def main():
                     help="back-to-back launches per kernel for the launch durations")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB device copies (counter calibration runs)")
+    ap.add_argument("--no-reference-copies", action="store_true",
+                    help="skip the identity-table gather and runtime copy (profiling runs)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"))
     args = ap.parse_args()
     if args.summarize_profiles:
@@ -390,12 +403,16 @@ def main():
         b.synchronize()
         return a.elapsed_time(b) / args.kernel_reps
 
-    ident_bytes = 2 * K * 16 * H * D * 2
-    copy_src = pool.view(-1)[: K * 16 * H * D]
-    copy_dst = ident_out.view(-1)
-    refs = {"identity_table_gather": round(ident_bytes / (back_to_back(ident_gather) / 1e3) / 1e9, 1),
-            "runtime_device_copy": round(ident_bytes / (back_to_back(lambda: copy_dst.copy_(copy_src)) / 1e3) / 1e9, 1),
-            "unit": "GB/s", "bytes": ident_bytes}
+    refs = None
+    if not args.no_reference_copies:
+        ident_bytes = 2 * K * 16 * H * D * 2
+        copy_src = pool.view(-1)[: K * 16 * H * D]
+        copy_dst = ident_out.view(-1)
+        t_ident = back_to_back(ident_gather)
+        t_copy = back_to_back(lambda: copy_dst.copy_(copy_src))
+        refs = {"identity_table_gather": round(ident_bytes / (t_ident / 1e3) / 1e9, 1),
+                "runtime_device_copy": round(ident_bytes / (t_copy / 1e3) / 1e9, 1),
+                "unit": "GB/s", "bytes": ident_bytes}
     del ident_out
 
     nbytes = step_bytes(T, S, K, H, D)
