@@ -252,6 +252,76 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir):
     print(json.dumps(traffic))
 
 
+# ---- batched moves (optional) ----------------------------------------------------
+
+def batched_append(hp, torch, np, dev, stream, reps):
+    """One decode step's KV append for a 32-layer model: each of the decode
+    batch's 64 sequences writes one new token (8 KV heads x 128 bf16) at its
+    current length, into each of 64 pools (32 layers x {K, V}) that share one
+    block table. 64 single hp_scatter calls against one hp_scatter_batch."""
+    import workloads
+    dec = workloads.decode()
+    prior = dec.seq_lens.astype(np.int64)
+    pages = (prior + 1 + 15) // 16
+    rng = np.random.default_rng(5)
+    n_pages = int(pages.sum()) + 64
+    bt = rng.permutation(n_pages)[: int(pages.sum())].astype(np.uint32)
+    sp = np.concatenate([[0], np.cumsum(pages)]).astype(np.uint32)
+
+    def idx(a):
+        return torch.from_numpy(np.asarray(a, dtype=np.uint32).view(np.int32).copy()).to(dev)
+
+    S, H, D, layers = 64, 8, 128, 32
+    tbt, tsp, tsl, tss = idx(bt), idx(sp), idx(np.ones(S)), idx(prior)
+    pools = [torch.empty((n_pages, 16, H, D), dtype=torch.bfloat16, device=dev)
+             for _ in range(2 * layers)]
+    srcs = [torch.randn((S, H, D), device=dev).to(torch.bfloat16) for _ in pools]
+    descs = [hp.Descriptor(p, tbt, tsp, tsl) for p in pools]
+    if hp.validate(descs[0], S, tss) != ("HP_OK", 0):
+        raise SystemExit("batched append descriptor failed validation")
+    L = hp.lib()
+    sh = stream.cuda_stream
+    pds = [d.with_tokens(S) for d in descs]
+    parr = (ctypes.c_void_p * len(pools))(*[p.data_ptr() for p in pools])
+    sarr = (ctypes.c_void_p * len(srcs))(*[x.data_ptr() for x in srcs])
+    src_p = [x.data_ptr() for x in srcs]
+    ss_p = tss.data_ptr()
+    flags = hp.HP_FLAG_ZERO_TAIL
+
+    def singles():
+        for pd, sp_ in zip(pds, src_p):
+            if L.hp_scatter(pd, sp_, ss_p, None, 0, flags, sh) != 0:
+                raise SystemExit("hp_scatter failed")
+
+    def batched():
+        if L.hp_scatter_batch(pds[0], len(pools), parr, sarr, ss_p, None, 0, flags, sh) != 0:
+            raise SystemExit("hp_scatter_batch failed")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_single, t_batch = timed(singles), timed(batched)
+    end = prior + 1
+    tail_rows = int(((-end) % 16).sum())
+    moved = len(pools) * (2 * S * H * D * 2 + tail_rows * H * D * 2)
+    return {"workload": "decode-step KV append: 64 sequences x 1 token, 8 KV heads x 128 "
+                        "bf16, 32 layers x {K, V} = 64 pools sharing one block table, "
+                        "tails zeroed",
+            "pools": len(pools), "algorithmic_bytes": moved,
+            "single_calls_us": round(t_single * 1e3, 1),
+            "batched_call_us": round(t_batch * 1e3, 1),
+            "speedup": round(t_single / t_batch, 2),
+            "batched_gb_per_s": round(moved / (t_batch / 1e3) / 1e9, 1)}
+
+
 # ---- the benchmark -------------------------------------------------------------
 
 def main():
@@ -265,6 +335,8 @@ def main():
                     help="back-to-back launches per kernel for the launch durations")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB device copies (counter calibration runs)")
+    ap.add_argument("--extras", action="store_true",
+                    help="also measure the batched calls (decode-step KV append over 64 pools)")
     ap.add_argument("--no-reference-copies", action="store_true",
                     help="skip the identity-table gather and runtime copy (profiling runs)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"))
@@ -458,6 +530,9 @@ def main():
                      "algorithmic_bytes_per_launch": nbytes["gather"],
                      "avg_launch_ms": round(launch_ms["gather"], 4)},
     }
+    if args.extras:
+        result["extras"] = {"batched_append": batched_append(hp, torch, np, dev, stream,
+                                                             args.kernel_reps)}
     if not args.no_cpu_baseline:
         pool_h = pool.view(torch.int16).cpu().numpy().view(np.uint16)
         qpool_h = qpool.cpu().numpy()

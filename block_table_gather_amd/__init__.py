@@ -22,7 +22,8 @@ import os
 import torch  # noqa: F401,E402
 
 __all__ = ["Descriptor", "HpError", "gather", "scatter", "gather_dequant", "validate",
-           "workspace_bytes", "status_str", "last_hip_error", "lib", "LIB_PATH", "STATUS"]
+           "gather_batch", "scatter_batch", "gather_dequant_batch", "workspace_bytes",
+           "status_str", "last_hip_error", "lib", "LIB_PATH", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhp.so")
 
@@ -101,6 +102,12 @@ _lib.hp_status_str.restype = ctypes.c_char_p
 _lib.hp_status_str.argtypes = [ctypes.c_int]
 _lib.hp_last_hip_error.restype = ctypes.c_char_p
 _lib.hp_last_hip_error.argtypes = []
+_lib.hp_gather_batch.restype = ctypes.c_int
+_lib.hp_gather_batch.argtypes = [_P, _u32, _vp, _vp, _vp, _sz, _u32, _vp]
+_lib.hp_scatter_batch.restype = ctypes.c_int
+_lib.hp_scatter_batch.argtypes = [_P, _u32, _vp, _vp, _vp, _vp, _sz, _u32, _vp]
+_lib.hp_gather_dequant_batch.restype = ctypes.c_int
+_lib.hp_gather_dequant_batch.argtypes = [_P, _u32, _vp, _vp, _vp, _u32, _vp, _sz, _u32, _vp]
 
 
 def lib():
@@ -280,3 +287,50 @@ def gather_dequant(desc, out, *, checked=False, workspace=None, stream=None):
                                   HP_FLAG_CHECKED if checked else 0,
                                   _stream(stream, desc.device)), "hp_gather_dequant")
     return out
+
+
+# ---- batched calls: several pools through the table of one descriptor -------
+
+def _ptr_array(tensors):
+    arr = (ctypes.c_void_p * len(tensors))(*[_ptr(t) for t in tensors])
+    return arr
+
+
+def gather_batch(desc, pools, outs, *, checked=False, streaming=False, workspace=None,
+                 stream=None):
+    """outs[i][T, H, D] <- gather of pools[i] through desc's table (desc's own
+    page_pool is ignored). T = outs[0].shape[0]."""
+    T = outs[0].shape[0] if len(outs) else 0
+    p = desc.with_tokens(T)
+    ws, n = _workspace(desc, T, workspace)
+    pa, oa = _ptr_array(pools), _ptr_array(outs)
+    flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_STREAM if streaming else 0)
+    _check(_lib.hp_gather_batch(p, len(pools), pa, oa, ws, n, flags,
+                                _stream(stream, desc.device)), "hp_gather_batch")
+    return outs
+
+
+def scatter_batch(desc, pools, srcs, seq_start=None, *, zero_tail=False, checked=False,
+                  workspace=None, stream=None):
+    """Writes srcs[i][T, H, D] into pools[i] through desc's table."""
+    T = srcs[0].shape[0] if len(srcs) else 0
+    p = desc.with_tokens(T)
+    ws, n = _workspace(desc, T, workspace)
+    pa, sa = _ptr_array(pools), _ptr_array(srcs)
+    flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_ZERO_TAIL if zero_tail else 0)
+    _check(_lib.hp_scatter_batch(p, len(pools), pa, sa, _ptr(seq_start), ws, n, flags,
+                                 _stream(stream, desc.device)), "hp_scatter_batch")
+
+
+def gather_dequant_batch(desc, pools, scales, outs, *, checked=False, workspace=None,
+                         stream=None):
+    """outs[i] (bf16) <- dequantised gather of int8 pools[i] with scales[i]."""
+    T = outs[0].shape[0] if len(outs) else 0
+    p = desc.with_tokens(T)
+    ws, n = _workspace(desc, T, workspace)
+    pa, sa, oa = _ptr_array(pools), _ptr_array(scales), _ptr_array(outs)
+    _check(_lib.hp_gather_dequant_batch(p, len(pools), pa, sa, oa, DTYPE["bf16"], ws, n,
+                                        HP_FLAG_CHECKED if checked else 0,
+                                        _stream(stream, desc.device)),
+           "hp_gather_dequant_batch")
+    return outs

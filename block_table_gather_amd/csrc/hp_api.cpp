@@ -179,14 +179,30 @@ uint32_t rows_per_unit(uint32_t P, uint64_t row_bytes, uint64_t unit_bytes, uint
     return 1;
 }
 
-uint32_t widest_vec(uint64_t row_bytes, const void *a, const void *b, uint32_t maxv) {
-    for (uint32_t v = maxv; v > 1; v >>= 1)
-        if (row_bytes % v == 0 && aligned(a, v) && aligned(b, v))
+// The pools and logical tensors one call moves: `count` of each (a single
+// call passes one), plus the per-slot scales of a dequant.
+struct Members {
+    uint32_t count;
+    void *const *pools;
+    void *const *rows;
+    const float *const *scales;
+};
+
+// Widest vector (in source bytes) that divides a row and keeps every pool
+// access, and every logical-tensor access (out_scale bytes per source byte),
+// aligned.
+uint32_t widest_vec(uint64_t row_bytes, const Members &m, uint32_t maxv, uint32_t out_scale) {
+    for (uint32_t v = maxv; v > 1; v >>= 1) {
+        bool ok = row_bytes % v == 0;
+        for (uint32_t i = 0; ok && i < m.count; ++i)
+            ok = aligned(m.pools[i], v) && aligned(m.rows[i], (uint64_t)v * out_scale);
+        if (ok)
             return v;
+    }
     return 1;
 }
 
-hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const void *src, void *out,
+hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const Members &m,
                  const void *seq_start, uint32_t flags, void *ws, hipStream_t stream) {
     const bool zero_tail = (flags & HP_FLAG_ZERO_TAIL) != 0;
     hp::CopyJob j = {};
@@ -210,7 +226,8 @@ hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const void *src
         j.load_nt = (flags & HP_FLAG_STREAM) != 0;
         break;
     case hp::Op::Scatter:
-        if (d->total_tokens * g.row_bytes >= HP_SCATTER_STREAM_BYTES / 2) {  // bytes moved
+        // bytes moved by the whole call: count * T * R read and written
+        if ((uint64_t)m.count * d->total_tokens * g.row_bytes >= HP_SCATTER_STREAM_BYTES / 2) {
             unit_bytes = HP_SCATTER_STREAM_UNIT_BYTES;
             j.units_per_group = 1;
             j.load_nt = true;
@@ -237,22 +254,17 @@ hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const void *src
         j.unit_bound = d->total_tokens / rpc + d->num_seqs;
     if (j.unit_bound >= (1ull << 32) - hp::kMaxUnitsPerGroup)
         return HP_ERR_ARG;
-    j.pool = d->page_pool;
-    j.pool_w = d->page_pool;
     j.block_table = d->block_table;
     j.seq_ptr = d->seq_ptr;
     j.seq_lens = d->seq_lens;
     j.seq_start = seq_start;
-    j.scales = d->scales;
-    j.src = src;
-    j.out = out;
+    j.count = m.count;
+    j.pools = m.pools;
+    j.rows = m.rows;
+    j.scales = m.scales;
     j.workspace = ws ? static_cast<unsigned char *>(ws) + kValidateBytes : nullptr;
-    if (op == hp::Op::Dequant)
-        j.vec_bytes = widest_vec(g.row_bytes, d->page_pool, d->page_pool, 8);
-    else
-        j.vec_bytes = widest_vec(g.row_bytes, d->page_pool, op == hp::Op::Scatter ? src : out, 16);
-    if (op == hp::Op::Dequant && !aligned(out, 2 * (uint64_t)j.vec_bytes))
-        j.vec_bytes = 1;  // out is 2-byte aligned; 1-byte input vectors write 2 bytes
+    j.vec_bytes = op == hp::Op::Dequant ? widest_vec(g.row_bytes, m, 8, 2)
+                                        : widest_vec(g.row_bytes, m, 16, 1);
     const hipError_t e = hp::launch_copy(j, stream);
     return e == hipSuccess ? HP_OK : hip_failed(e);
 }
@@ -281,6 +293,48 @@ hp_status prologue(const hp_desc *d, const Geometry &g, uint32_t flags, uint32_t
             return st;
     }
     *done = d->num_seqs == 0 || d->total_tokens == 0;
+    return HP_OK;
+}
+
+// Checks shared by the batched calls: the descriptor (with pools[0] standing
+// in for its page_pool and scales[0] for its scales), every member pointer,
+// and that no written buffer overlaps another buffer of the call.
+hp_status check_batch(const hp_desc *desc, uint32_t count, void *const *pools,
+                      void *const *rows, const float *const *scales, bool rows_written,
+                      bool need_scales, hp_desc *local, Geometry *g) {
+    if (!desc || !pools || !rows || (need_scales && !scales))
+        return HP_ERR_NULL;
+    *local = *desc;
+    local->page_pool = pools[0];
+    local->scales = need_scales ? scales[0] : nullptr;
+    hp_status st = check_desc(local, g);
+    if (st != HP_OK)
+        return st;
+    const uint64_t rows_bytes =
+        local->total_tokens * g->row_bytes * (need_scales ? 2 : 1);  // dequant writes bf16
+    const uint32_t row_align = need_scales ? 2 : g->elem_bytes;
+    const uint64_t scale_bytes = local->num_pages * local->page_size * 4;
+    for (uint32_t i = 0; i < count; ++i) {
+        if ((local->num_pages && !pools[i]) || (local->total_tokens && !rows[i]) ||
+            (need_scales && !scales[i]))
+            return HP_ERR_NULL;
+        if (!aligned(pools[i], 64) || !aligned(rows[i], row_align) ||
+            (need_scales && !aligned(scales[i], 64)))
+            return HP_ERR_ALIGN;
+    }
+    for (uint32_t i = 0; i < count; ++i) {
+        for (uint32_t k = 0; k < count; ++k) {
+            // a logical tensor never overlaps a pool or scales; written buffers
+            // of different members never overlap each other
+            if (overlaps(rows[i], rows_bytes, pools[k], g->pool_bytes) ||
+                (need_scales && overlaps(rows[i], rows_bytes, scales[k], scale_bytes)))
+                return HP_ERR_ARG;
+            if (i != k && rows_written && overlaps(rows[i], rows_bytes, rows[k], rows_bytes))
+                return HP_ERR_ARG;
+            if (i != k && !rows_written && overlaps(pools[i], g->pool_bytes, pools[k], g->pool_bytes))
+                return HP_ERR_ARG;
+        }
+    }
     return HP_OK;
 }
 
@@ -332,8 +386,9 @@ hp_status hp_gather(const hp_desc *desc, void *out, void *workspace, size_t work
                   workspace_bytes, (hipStream_t)stream, &done);
     if (st != HP_OK || done)
         return st;
-    return launch(desc, g, hp::Op::Gather, nullptr, out, nullptr, flags, workspace,
-                  (hipStream_t)stream);
+    void *pool = desc->page_pool;
+    const Members m = {1, &pool, &out, nullptr};
+    return launch(desc, g, hp::Op::Gather, m, nullptr, flags, workspace, (hipStream_t)stream);
 }
 
 hp_status hp_scatter(const hp_desc *desc, const void *src, const void *seq_start,
@@ -353,8 +408,10 @@ hp_status hp_scatter(const hp_desc *desc, const void *src, const void *seq_start
                   workspace_bytes, (hipStream_t)stream, &done);
     if (st != HP_OK || done)
         return st;
-    return launch(desc, g, hp::Op::Scatter, src, nullptr, seq_start, flags, workspace,
-                  (hipStream_t)stream);
+    void *pool = desc->page_pool;
+    void *rows = const_cast<void *>(src);  // read, never written
+    const Members m = {1, &pool, &rows, nullptr};
+    return launch(desc, g, hp::Op::Scatter, m, seq_start, flags, workspace, (hipStream_t)stream);
 }
 
 hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype, void *workspace,
@@ -378,8 +435,79 @@ hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype, 
                   (hipStream_t)stream, &done);
     if (st != HP_OK || done)
         return st;
-    return launch(desc, g, hp::Op::Dequant, nullptr, out, nullptr, flags, workspace,
-                  (hipStream_t)stream);
+    void *pool = desc->page_pool;
+    const float *scales = desc->scales;
+    const Members m = {1, &pool, &out, &scales};
+    return launch(desc, g, hp::Op::Dequant, m, nullptr, flags, workspace, (hipStream_t)stream);
+}
+
+// ---- batched calls: several pools through one shared table --------------------
+
+hp_status hp_gather_batch(const hp_desc *desc, uint32_t count, void *const *pools,
+                          void *const *outs, void *workspace, size_t workspace_bytes,
+                          uint32_t flags, void *stream) {
+    if (!desc)
+        return HP_ERR_NULL;
+    if (count == 0)
+        return HP_OK;
+    hp_desc d;
+    Geometry g;
+    bool done;
+    hp_status st = check_batch(desc, count, pools, outs, nullptr, true, false, &d, &g);
+    if (st != HP_OK)
+        return st;
+    st = prologue(&d, g, flags, HP_FLAG_CHECKED | HP_FLAG_STREAM, nullptr, workspace,
+                  workspace_bytes, (hipStream_t)stream, &done);
+    if (st != HP_OK || done)
+        return st;
+    const Members m = {count, pools, outs, nullptr};
+    return launch(&d, g, hp::Op::Gather, m, nullptr, flags, workspace, (hipStream_t)stream);
+}
+
+hp_status hp_scatter_batch(const hp_desc *desc, uint32_t count, void *const *pools,
+                           const void *const *srcs, const void *seq_start, void *workspace,
+                           size_t workspace_bytes, uint32_t flags, void *stream) {
+    if (!desc)
+        return HP_ERR_NULL;
+    if (count == 0)
+        return HP_OK;
+    hp_desc d;
+    Geometry g;
+    bool done;
+    void *const *rows = const_cast<void *const *>(srcs);  // read, never written
+    hp_status st = check_batch(desc, count, pools, rows, nullptr, false, false, &d, &g);
+    if (st != HP_OK)
+        return st;
+    st = prologue(&d, g, flags, HP_FLAG_CHECKED | HP_FLAG_ZERO_TAIL, seq_start, workspace,
+                  workspace_bytes, (hipStream_t)stream, &done);
+    if (st != HP_OK || done)
+        return st;
+    const Members m = {count, pools, rows, nullptr};
+    return launch(&d, g, hp::Op::Scatter, m, seq_start, flags, workspace, (hipStream_t)stream);
+}
+
+hp_status hp_gather_dequant_batch(const hp_desc *desc, uint32_t count, void *const *pools,
+                                  const float *const *scales, void *const *outs,
+                                  uint32_t out_dtype, void *workspace, size_t workspace_bytes,
+                                  uint32_t flags, void *stream) {
+    if (!desc)
+        return HP_ERR_NULL;
+    if (count == 0)
+        return HP_OK;
+    hp_desc d;
+    Geometry g;
+    bool done;
+    hp_status st = check_batch(desc, count, pools, outs, scales, true, true, &d, &g);
+    if (st != HP_OK)
+        return st;
+    if (d.dtype != HP_DTYPE_I8 || out_dtype != HP_DTYPE_BF16)
+        return HP_ERR_DTYPE;
+    st = prologue(&d, g, flags, HP_FLAG_CHECKED, nullptr, workspace, workspace_bytes,
+                  (hipStream_t)stream, &done);
+    if (st != HP_OK || done)
+        return st;
+    const Members m = {count, pools, outs, scales};
+    return launch(&d, g, hp::Op::Dequant, m, nullptr, flags, workspace, (hipStream_t)stream);
 }
 
 const char *hp_last_hip_error(void) { return hipGetErrorName(t_last_hip_error); }

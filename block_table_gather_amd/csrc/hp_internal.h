@@ -51,6 +51,9 @@ constexpr uint64_t kFusedMaxSeqs = HP_FUSED_MAX_SEQS;
 constexpr uint32_t kThreads = HP_THREADS;     // threads per copy workgroup
 constexpr uint32_t kPlanChunk = 2048;         // sequences per plan workgroup
 constexpr uint32_t kMaxUnitsPerGroup = 16;
+// Pools moved by one launch of a batched call (one grid row each); the
+// pointers travel in the kernel arguments. Larger batches take more launches.
+constexpr uint32_t kMaxBatch = 32;
 
 enum class Op : int { Gather = 0, Scatter = 1, Dequant = 2 };
 
@@ -69,15 +72,14 @@ struct CopyJob {
     uint64_t row_bytes;     // H*D*elem_bytes (pool side)
     uint64_t out_row_bytes; // logical-tensor side (dequant: H*D*2)
     uint64_t unit_bound;    // host upper bound on the number of work units
-    const void *pool;       // gather/dequant: read; scatter: written
-    void *pool_w;
     const void *block_table;
     const void *seq_ptr;
     const void *seq_lens;
     const void *seq_start;  // scatter, may be null
-    const float *scales;    // dequant
-    const void *src;        // scatter rows
-    void *out;              // gather/dequant rows
+    uint32_t count;         // pools moved (each with its own rows and scales)
+    void *const *pools;     // [count] pools: gather/dequant read them, scatter writes
+    void *const *rows;      // [count] logical tensors: gather/dequant write, scatter reads
+    const float *const *scales;  // [count] per-slot scales (dequant), else null
     void *workspace;        // plan arrays when num_seqs > kFusedMaxSeqs
     uint32_t vec_bytes;     // widest vector width every span allows
 };

@@ -90,15 +90,10 @@ struct Div {
 // Device-side view of a launch. Offsets inside one unit are 32-bit (the host
 // guarantees rows_per_unit * row bytes < 2^31); page and row bases are 64-bit.
 struct Args {
-    const unsigned char *pool_r;
-    unsigned char *pool_w;
     const void *block_table;
     const void *seq_ptr;
     const void *seq_lens;
     const void *seq_start;
-    const float *scales;
-    const unsigned char *src;
-    unsigned char *out;
     const uint32_t *g_unit_end;  // plan arrays (non-fused launches)
     const uint64_t *g_tok_begin;
     uint64_t *partials;
@@ -113,6 +108,10 @@ struct Args {
     uint32_t vecs_per_row;    // dequant: input vectors per row
     Div div_vpr, div_rpc, div_page, div_upp;  // by vecs_per_row, rows_per_unit,
                                               // page_size, units_per_page
+    // Pool m of the launch is moved by grid row m (blockIdx.y).
+    unsigned char *pool[kMaxBatch];   // scatter writes it, gather/dequant read it
+    unsigned char *rows[kMaxBatch];   // the logical tensor of pool m
+    const float *scales[kMaxBatch];   // dequant: per-slot scales of pool m
 };
 
 __device__ __forceinline__ uint64_t min64(uint64_t a, uint64_t b) { return a < b ? a : b; }
@@ -342,7 +341,6 @@ __device__ __forceinline__ void dequant_span(const Args &a, const unsigned char 
 #ifndef HP_XCD_REMAP
 #define HP_XCD_REMAP 0
 #endif
-constexpr uint32_t kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 
 // Order in which workgroups take work. The dispatcher hands consecutive
 // workgroup IDs to the 8 XCDs in turn; with the remap, the workgroups that
@@ -350,6 +348,7 @@ constexpr uint32_t kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs eac
 // [0, groups)), so neighbouring units of one page share that XCD's L2.
 __device__ __forceinline__ uint32_t group_order(uint32_t b, uint32_t groups) {
 #if HP_XCD_REMAP
+    constexpr uint32_t kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
     const uint32_t per = (groups + kXcds - 1) / kXcds;  // groups on the fullest XCDs
     const uint32_t full = groups - (per - 1) * kXcds;   // XCDs that get `per` groups
     const uint32_t xcd = b % kXcds, local = b / kXcds;
@@ -398,6 +397,8 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
     uint32_t s = uni(lo);
 
     const uint32_t P = a.page_size, rpc = a.rows_per_unit;
+    unsigned char *const pool = a.pool[blockIdx.y];
+    unsigned char *const rowsp = a.rows[blockIdx.y];
     uint32_t ubeg = 0, uend = 0;
     uint64_t len = 0, sp = 0, start = 0, tb = 0;
     auto load_seq = [&](uint32_t q) {
@@ -424,11 +425,11 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
             const uint32_t slot0 = (uint32_t)(pos0 - q * P);
             const uint64_t phys = uni64(ld_idx<IdxT>(a.block_table, sp + q));
             const uint64_t end = start + len;
-            unsigned char *page = a.pool_w + phys * P * a.row_bytes;
+            unsigned char *page = pool + phys * P * a.row_bytes;
             const uint64_t wa = pos0 > start ? pos0 : start;
             const uint64_t wb = pos0 + rpc < end ? pos0 + rpc : end;
             if (wa < wb) {
-                const unsigned char *from = a.src + (tb + (wa - start)) * a.row_bytes;
+                const unsigned char *from = rowsp + (tb + (wa - start)) * a.row_bytes;
                 copy_span<VEC, NTL>(from, page + (slot0 + (uint32_t)(wa - pos0)) * a.row_bytes,
                                (uint32_t)(wb - wa) * a.row_bytes);
             }
@@ -446,12 +447,12 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
             const uint32_t q = udiv32(u, a.div_upp);
             const uint32_t slot0 = (u - q * a.units_per_page) * rpc;
             const uint64_t phys = uni64(ld_idx<IdxT>(a.block_table, sp + q));
-            const unsigned char *from = a.pool_r + (phys * P + slot0) * a.row_bytes;
-            unsigned char *to = a.out + (tb + t0) * a.out_row_bytes;
+            const unsigned char *from = pool + (phys * P + slot0) * a.row_bytes;
+            unsigned char *to = rowsp + (tb + t0) * a.out_row_bytes;
             if constexpr (OP == Op::Gather) {
                 copy_span<VEC, NTL>(from, to, rows * a.row_bytes);
             } else {
-                dequant_span<VEC>(a, from, a.scales + phys * P + slot0, to, rows);
+                dequant_span<VEC>(a, from, a.scales[blockIdx.y] + phys * P + slot0, to, rows);
             }
         }
     }
@@ -578,27 +579,30 @@ __global__ __launch_bounds__(256) void validate_kernel(VArgs a) {
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 template <typename IdxT, Op OP, int VEC, bool NTL>
-hipError_t launch_vec(const Args &a, bool fused, uint32_t grid, uint32_t plan_chunks,
+hipError_t launch_vec(const Args &a, bool fused, dim3 grid, uint32_t plan_chunks,
                       uint32_t *unit_end, uint64_t *tok_begin, hipStream_t stream) {
     if (fused) {
         const size_t lds = 12 * (size_t)a.num_seqs;
-        hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, true, NTL>), dim3(grid), dim3(kThreads), lds,
+        hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, true, NTL>), grid, dim3(kThreads), lds,
                            stream, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((plan_sum_kernel<IdxT, OP>), dim3(plan_chunks), dim3(kThreads), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kThreads), 0, stream, a.partials, plan_chunks);
-    if ((e = hipGetLastError()) != hipSuccess)
-        return e;
-    hipLaunchKernelGGL((plan_write_kernel<IdxT, OP>), dim3(plan_chunks), dim3(kThreads), 0, stream,
-                       a, unit_end, tok_begin);
-    if ((e = hipGetLastError()) != hipSuccess)
-        return e;
-    hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, false, NTL>), dim3(grid), dim3(kThreads), 0,
-                       stream, a);
+    if (plan_chunks) {  // 0: the plan arrays are already in the workspace
+        hipLaunchKernelGGL((plan_sum_kernel<IdxT, OP>), dim3(plan_chunks), dim3(kThreads), 0, stream,
+                           a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kThreads), 0, stream, a.partials,
+                           plan_chunks);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL((plan_write_kernel<IdxT, OP>), dim3(plan_chunks), dim3(kThreads), 0,
+                           stream, a, unit_end, tok_begin);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, false, NTL>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -607,7 +611,7 @@ hipError_t launch_vec(const Args &a, bool fused, uint32_t grid, uint32_t plan_ch
 // streams its source only when the move is larger than the Infinity Cache;
 // dequant's 1:2 read:write mix reads through the cache.
 template <typename IdxT, Op OP, int VEC>
-hipError_t launch_policy(const Args &a, bool ntl, bool fused, uint32_t grid, uint32_t chunks,
+hipError_t launch_policy(const Args &a, bool ntl, bool fused, dim3 grid, uint32_t chunks,
                          uint32_t *ue, uint64_t *tb, hipStream_t st) {
     if constexpr (OP == Op::Gather) {
         if (ntl)
@@ -623,7 +627,7 @@ hipError_t launch_policy(const Args &a, bool ntl, bool fused, uint32_t grid, uin
 }
 
 template <typename IdxT, Op OP>
-hipError_t launch_op(const Args &a, uint32_t vec, bool ntl, bool fused, uint32_t grid,
+hipError_t launch_op(const Args &a, uint32_t vec, bool ntl, bool fused, dim3 grid,
                      uint32_t chunks, uint32_t *ue, uint64_t *tb, hipStream_t st) {
     if constexpr (OP == Op::Dequant) {
         switch (vec) {
@@ -644,7 +648,7 @@ hipError_t launch_op(const Args &a, uint32_t vec, bool ntl, bool fused, uint32_t
 }
 
 template <typename IdxT>
-hipError_t launch_idx(const Args &a, Op op, uint32_t vec, bool ntl, bool fused, uint32_t grid,
+hipError_t launch_idx(const Args &a, Op op, uint32_t vec, bool ntl, bool fused, dim3 grid,
                       uint32_t chunks, uint32_t *ue, uint64_t *tb, hipStream_t st) {
     switch (op) {
     case Op::Gather:
@@ -680,15 +684,10 @@ hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
     // see only that launch.
     (void)hipGetLastError();
     Args a = {};
-    a.pool_r = static_cast<const unsigned char *>(job.pool);
-    a.pool_w = static_cast<unsigned char *>(job.pool_w);
     a.block_table = job.block_table;
     a.seq_ptr = job.seq_ptr;
     a.seq_lens = job.seq_lens;
     a.seq_start = job.seq_start;
-    a.scales = job.scales;
-    a.src = static_cast<const unsigned char *>(job.src);
-    a.out = static_cast<unsigned char *>(job.out);
     a.num_seqs = (uint32_t)job.num_seqs;
     a.page_size = job.page_size;
     a.rows_per_unit = job.rows_per_unit;
@@ -719,11 +718,25 @@ hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
         a.g_unit_end = ue;
         a.g_tok_begin = tb;
     }
-    if (job.idx64)
-        return launch_idx<uint64_t>(a, job.op, job.vec_bytes, job.load_nt, fused, grid, chunks, ue,
-                                    tb, stream);
-    return launch_idx<uint32_t>(a, job.op, job.vec_bytes, job.load_nt, fused, grid, chunks, ue, tb,
-                                stream);
+    // The plan arrays depend only on the shared table: the plan kernels run
+    // with the first launch only, later launches of a large batch reuse them.
+    for (uint32_t first = 0; first < job.count; first += kMaxBatch, chunks = 0) {
+        const uint32_t n = job.count - first < kMaxBatch ? job.count - first : kMaxBatch;
+        for (uint32_t m = 0; m < n; ++m) {
+            a.pool[m] = static_cast<unsigned char *>(job.pools[first + m]);
+            a.rows[m] = static_cast<unsigned char *>(job.rows[first + m]);
+            a.scales[m] = job.scales ? job.scales[first + m] : nullptr;
+        }
+        const dim3 g(grid, n);
+        const hipError_t e =
+            job.idx64 ? launch_idx<uint64_t>(a, job.op, job.vec_bytes, job.load_nt, fused, g, chunks,
+                                             ue, tb, stream)
+                      : launch_idx<uint32_t>(a, job.op, job.vec_bytes, job.load_nt, fused, g, chunks,
+                                             ue, tb, stream);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_validate(const ValidateJob &job, hipStream_t stream) {

@@ -189,6 +189,35 @@ hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype,
                             void *workspace, size_t workspace_bytes, uint32_t flags,
                             void *stream);
 
+/* ---- Batched moves over pools that share one block table ------------------
+ *
+ * [Hurray] Description: a whole KV cache ([layers, 2, ...]) travels as a
+ * stream of descriptors, one per {kv_role, layer_index}; in a paged cache all
+ * of them use the same block table, seq_ptr and token counts and differ only
+ * in their page pool (and scales). A batched call moves `count` such pools in
+ * one pass over the table: member i uses pools[i] (and scales[i]) with the
+ * geometry and index buffers of `desc`, whose own page_pool and scales fields
+ * are ignored. The result for member i is exactly that of the single call on
+ * the descriptor with page_pool = pools[i] (scales = scales[i]).
+ *
+ * pools, outs, srcs and scales are HOST arrays of `count` DEVICE pointers.
+ * Every pool is 64-byte aligned; outputs are element aligned (bf16 for
+ * dequant). No output overlaps any pool, scale buffer or another output; for
+ * scatter the pools do not overlap each other. count == 0 enqueues nothing.
+ * Flags, workspace and errors are those of the single calls. */
+hp_status hp_gather_batch(const hp_desc *desc, uint32_t count, void *const *pools,
+                          void *const *outs, void *workspace, size_t workspace_bytes,
+                          uint32_t flags, void *stream);
+
+hp_status hp_scatter_batch(const hp_desc *desc, uint32_t count, void *const *pools,
+                           const void *const *srcs, const void *seq_start, void *workspace,
+                           size_t workspace_bytes, uint32_t flags, void *stream);
+
+hp_status hp_gather_dequant_batch(const hp_desc *desc, uint32_t count, void *const *pools,
+                                  const float *const *scales, void *const *outs,
+                                  uint32_t out_dtype, void *workspace, size_t workspace_bytes,
+                                  uint32_t flags, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *hp_status_str(int status);
 

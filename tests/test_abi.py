@@ -24,7 +24,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"hp_workspace_bytes", "hp_validate", "hp_gather", "hp_scatter",
-                          "hp_gather_dequant", "hp_status_str", "hp_last_hip_error"}
+                          "hp_gather_dequant", "hp_status_str", "hp_last_hip_error",
+                          "hp_gather_batch", "hp_scatter_batch", "hp_gather_dequant_batch"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -153,3 +154,48 @@ def test_empty_batch_and_zero_tokens_enqueue_nothing():
     assert L.hp_scatter(ctypes.byref(d), None, None, None, 0, hp.HP_FLAG_ZERO_TAIL, None) == 0
     z = desc(total_tokens=0)
     assert gather(z, out=None) == S["HP_OK"]
+
+
+def _arr(*ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def test_batch_rejections():
+    """Batched calls check every member before enqueuing anything."""
+    d = desc()
+    P1, P2 = ALIGNED, ALIGNED + 0x10000000          # two distinct 64-byte aligned pools
+    O1, O2 = OUT, OUT + 0x10000000
+    g = lambda n, pools, outs, flags=0: L.hp_gather_batch(  # noqa: E731
+        ctypes.byref(d), n, pools, outs, None, 0, flags, None)
+    assert L.hp_gather_batch(None, 2, _arr(P1, P2), _arr(O1, O2), None, 0, 0, None) == S["HP_ERR_NULL"]
+    assert g(0, None, None) == S["HP_OK"]                      # nothing to do
+    assert g(2, None, _arr(O1, O2)) == S["HP_ERR_NULL"]
+    assert g(2, _arr(P1, None), _arr(O1, O2)) == S["HP_ERR_NULL"]
+    assert g(2, _arr(P1, P2 + 32), _arr(O1, O2)) == S["HP_ERR_ALIGN"]
+    assert g(2, _arr(P1, P2), _arr(O1, O2 + 1)) == S["HP_ERR_ALIGN"]
+    assert g(2, _arr(P1, P2), _arr(O1, O1 + 64)) == S["HP_ERR_ARG"]     # outputs overlap
+    assert g(2, _arr(P1, P2), _arr(O1, P2 + 256)) == S["HP_ERR_ARG"]    # output inside a pool
+    assert g(2, _arr(P1, P2), _arr(O1, O2), flags=8) == S["HP_ERR_ARG"]
+    assert g(2, _arr(P1, P2), _arr(O1, O2), flags=hp.HP_FLAG_CHECKED) == S["HP_ERR_WORKSPACE"]
+    bad = desc(rank=2)
+    assert L.hp_gather_batch(ctypes.byref(bad), 2, _arr(P1, P2), _arr(O1, O2), None, 0, 0,
+                             None) == S["HP_ERR_RANK"]
+    sc = lambda pools, srcs, flags=0: L.hp_scatter_batch(  # noqa: E731
+        ctypes.byref(d), 2, pools, srcs, None, None, 0, flags, None)
+    assert sc(_arr(P1, P1 + 64), _arr(O1, O2)) == S["HP_ERR_ARG"]      # written pools overlap
+    assert sc(_arr(P1, P2), _arr(O1, O2), hp.HP_FLAG_STREAM) == S["HP_ERR_ARG"]
+    q = desc(dtype=hp.DTYPE["i8"])
+    S1, S2 = ALIGNED + 0x20000000, ALIGNED + 0x30000000
+    dq = lambda scales, od=hp.DTYPE["bf16"], dd=q: L.hp_gather_dequant_batch(  # noqa: E731
+        ctypes.byref(dd), 2, _arr(P1, P2), scales, _arr(O1, O2), od, None, 0, 0, None)
+    assert dq(None) == S["HP_ERR_NULL"]
+    assert dq(_arr(S1, None)) == S["HP_ERR_NULL"]
+    assert dq(_arr(S1, S2 + 4)) == S["HP_ERR_ALIGN"]
+    assert dq(_arr(S1, S2), od=hp.DTYPE["f16"]) == S["HP_ERR_DTYPE"]
+    assert dq(_arr(S1, S2), dd=d) == S["HP_ERR_DTYPE"]
+
+
+def test_batch_empty_batch_enqueues_nothing():
+    d = desc(num_seqs=0, num_block_entries=0, block_table=None, seq_lens=None, total_tokens=0)
+    assert L.hp_gather_batch(ctypes.byref(d), 2, _arr(ALIGNED, ALIGNED + 0x10000000),
+                             _arr(None, None), None, 0, 0, None) == S["HP_OK"]
