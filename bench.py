@@ -531,8 +531,21 @@ def main():
                      "avg_launch_ms": round(launch_ms["gather"], 4)},
     }
     if args.extras:
-        result["extras"] = {"batched_append": batched_append(hp, torch, np, dev, stream,
-                                                             args.kernel_reps)}
+        # copy-on-write page copy: 1,024 referenced pages of the decode pool
+        # (128 KiB each) into pages no sequence references
+        free = np.setdiff1d(np.arange(w.num_pages), w.block_table.astype(np.int64))
+        rng = np.random.default_rng(6)
+        n_copy = 1024
+        src_p = idx(rng.choice(w.block_table.astype(np.int64), n_copy, replace=False))
+        dst_p = idx(rng.choice(free, n_copy, replace=False))
+        t_copy = back_to_back(lambda: hp.copy_pages(desc, src_p, dst_p, stream=stream))
+        copy_bytes = 2 * n_copy * 16 * H * D * 2
+        result["extras"] = {
+            "batched_append": batched_append(hp, torch, np, dev, stream, args.kernel_reps),
+            "copy_pages": {"workload": "1,024 pages of the decode pool (16 x 32 x 128 fp16 = "
+                                       "128 KiB each) copied to unreferenced pages",
+                           "algorithmic_bytes": copy_bytes, "launch_us": round(t_copy * 1e3, 1),
+                           "gb_per_s": round(copy_bytes / (t_copy / 1e3) / 1e9, 1)}}
     if not args.no_cpu_baseline:
         pool_h = pool.view(torch.int16).cpu().numpy().view(np.uint16)
         qpool_h = qpool.cpu().numpy()

@@ -22,7 +22,8 @@ import os
 import torch  # noqa: F401,E402
 
 __all__ = ["Descriptor", "HpError", "gather", "scatter", "gather_dequant", "validate",
-           "gather_batch", "scatter_batch", "gather_dequant_batch", "workspace_bytes",
+           "gather_batch", "scatter_batch", "gather_dequant_batch", "copy_pages",
+           "copy_pages_batch", "workspace_bytes",
            "status_str", "last_hip_error", "lib", "LIB_PATH", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhp.so")
@@ -106,6 +107,11 @@ _lib.hp_gather_batch.restype = ctypes.c_int
 _lib.hp_gather_batch.argtypes = [_P, _u32, _vp, _vp, _vp, _sz, _u32, _vp]
 _lib.hp_scatter_batch.restype = ctypes.c_int
 _lib.hp_scatter_batch.argtypes = [_P, _u32, _vp, _vp, _vp, _vp, _sz, _u32, _vp]
+_lib.hp_copy_pages.restype = ctypes.c_int
+_lib.hp_copy_pages.argtypes = [_P, _vp, _vp, ctypes.c_uint64, _vp, _sz, _u32, _vp]
+_lib.hp_copy_pages_batch.restype = ctypes.c_int
+_lib.hp_copy_pages_batch.argtypes = [_P, _u32, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp, _sz,
+                                     _u32, _vp]
 _lib.hp_gather_dequant_batch.restype = ctypes.c_int
 _lib.hp_gather_dequant_batch.argtypes = [_P, _u32, _vp, _vp, _vp, _u32, _vp, _sz, _u32, _vp]
 
@@ -334,3 +340,32 @@ def gather_dequant_batch(desc, pools, scales, outs, *, checked=False, workspace=
                                         _stream(stream, desc.device)),
            "hp_gather_dequant_batch")
     return outs
+
+
+# ---- copy-on-write page copy ----------------------------------------------------
+
+def copy_pages(desc, src_pages, dst_pages, *, checked=False, workspace=None, stream=None):
+    """Page dst_pages[i] of desc's pool (and its slot scales) <- page src_pages[i]."""
+    n = src_pages.numel()
+    if dst_pages.numel() != n:
+        raise ValueError("src_pages and dst_pages differ in length")
+    p = desc.with_tokens(0)
+    ws, wn = _workspace(desc, 0, workspace)
+    _check(_lib.hp_copy_pages(p, _ptr(src_pages), _ptr(dst_pages), n, ws, wn,
+                              HP_FLAG_CHECKED if checked else 0, _stream(stream, desc.device)),
+           "hp_copy_pages")
+
+
+def copy_pages_batch(desc, pools, scales, src_pages, dst_pages, *, checked=False,
+                     workspace=None, stream=None):
+    """The same page copies in every pool of `pools` (scales: list or None)."""
+    n = src_pages.numel()
+    if dst_pages.numel() != n:
+        raise ValueError("src_pages and dst_pages differ in length")
+    p = desc.with_tokens(0)
+    ws, wn = _workspace(desc, 0, workspace)
+    pa = _ptr_array(pools)
+    sa = _ptr_array(scales) if scales is not None else None
+    _check(_lib.hp_copy_pages_batch(p, len(pools), pa, sa, _ptr(src_pages), _ptr(dst_pages), n,
+                                    ws, wn, HP_FLAG_CHECKED if checked else 0,
+                                    _stream(stream, desc.device)), "hp_copy_pages_batch")

@@ -338,6 +338,84 @@ hp_status check_batch(const hp_desc *desc, uint32_t count, void *const *pools,
     return HP_OK;
 }
 
+// Shared by hp_copy_pages and hp_copy_pages_batch: every pool of the call
+// gets the same page copies.
+hp_status copy_pages_common(const hp_desc *desc, uint32_t num_pools, void *const *pools,
+                            float *const *scales, const void *src_pages, const void *dst_pages,
+                            uint64_t copies, void *ws, size_t ws_bytes, uint32_t flags,
+                            hipStream_t stream) {
+    if (!desc || !pools)
+        return HP_ERR_NULL;
+    if (num_pools == 0)
+        return HP_OK;
+    hp_desc d = *desc;
+    d.page_pool = pools[0];
+    d.scales = scales ? scales[0] : nullptr;
+    Geometry g;
+    hp_status st = check_desc(&d, &g);
+    if (st != HP_OK)
+        return st;
+    if (flags & ~(uint32_t)HP_FLAG_CHECKED)
+        return HP_ERR_ARG;
+    const uint64_t page_bytes = (uint64_t)d.page_size * g.row_bytes;
+    if (page_bytes >= (1ull << 32))
+        return HP_ERR_ARG;
+    for (uint32_t i = 0; i < num_pools; ++i) {
+        if (d.num_pages && !pools[i])
+            return HP_ERR_NULL;
+        if (!aligned(pools[i], 64) || (scales && !aligned(scales[i], 64)))
+            return HP_ERR_ALIGN;
+        for (uint32_t k = 0; k < i; ++k)
+            if (overlaps(pools[i], g.pool_bytes, pools[k], g.pool_bytes))
+                return HP_ERR_ARG;
+    }
+    if (copies == 0)
+        return HP_OK;
+    if (!src_pages || !dst_pages)
+        return HP_ERR_NULL;
+    if (!aligned(src_pages, g.idx_bytes) || !aligned(dst_pages, g.idx_bytes))
+        return HP_ERR_ALIGN;
+    const uint64_t chunks = (page_bytes + 16383) / 16384;
+    if (copies >= kMaxIndex || copies * chunks >= (1ull << 31))
+        return HP_ERR_ARG;
+    if (flags & HP_FLAG_CHECKED) {
+        if ((st = check_workspace(ws, ws_bytes, kValidateBytes)) != HP_OK)
+            return st;
+        hp::PageCheckJob c;
+        c.idx64 = d.index_type == HP_INDEX_U64;
+        c.copies = copies;
+        c.num_pages = d.num_pages;
+        c.src_pages = src_pages;
+        c.dst_pages = dst_pages;
+        c.workspace = ws;
+        hipError_t e = hp::launch_check_pages(c, stream);
+        uint64_t key = 0;
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(&key, ws, sizeof key, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess)
+            e = hipStreamSynchronize(stream);
+        if (e != hipSuccess)
+            return hip_failed(e);
+        if (key != ~0ull)
+            return HP_ERR_PAGE_RANGE;
+    }
+    hp::PageCopyJob j;
+    j.idx64 = d.index_type == HP_INDEX_U64;
+    j.vec_bytes = 16;
+    while (j.vec_bytes > 1 && page_bytes % j.vec_bytes)
+        j.vec_bytes >>= 1;
+    j.page_size = d.page_size;
+    j.page_bytes = page_bytes;
+    j.copies = copies;
+    j.src_pages = src_pages;
+    j.dst_pages = dst_pages;
+    j.count = num_pools;
+    j.pools = pools;
+    j.scales = scales;
+    const hipError_t e = hp::launch_copy_pages(j, stream);
+    return e == hipSuccess ? HP_OK : hip_failed(e);
+}
+
 } // namespace
 
 extern "C" {
@@ -508,6 +586,26 @@ hp_status hp_gather_dequant_batch(const hp_desc *desc, uint32_t count, void *con
         return st;
     const Members m = {count, pools, outs, scales};
     return launch(&d, g, hp::Op::Dequant, m, nullptr, flags, workspace, (hipStream_t)stream);
+}
+
+hp_status hp_copy_pages(const hp_desc *desc, const void *src_pages, const void *dst_pages,
+                        uint64_t count, void *workspace, size_t workspace_bytes, uint32_t flags,
+                        void *stream) {
+    if (!desc)
+        return HP_ERR_NULL;
+    void *pool = desc->page_pool;
+    float *scales = const_cast<float *>(desc->scales);  // written by this call
+    return copy_pages_common(desc, 1, &pool, desc->scales ? &scales : nullptr, src_pages,
+                             dst_pages, count, workspace, workspace_bytes, flags,
+                             (hipStream_t)stream);
+}
+
+hp_status hp_copy_pages_batch(const hp_desc *desc, uint32_t num_pools, void *const *pools,
+                              float *const *scales, const void *src_pages, const void *dst_pages,
+                              uint64_t count, void *workspace, size_t workspace_bytes,
+                              uint32_t flags, void *stream) {
+    return copy_pages_common(desc, num_pools, pools, scales, src_pages, dst_pages, count,
+                             workspace, workspace_bytes, flags, (hipStream_t)stream);
 }
 
 const char *hp_last_hip_error(void) { return hipGetErrorName(t_last_hip_error); }

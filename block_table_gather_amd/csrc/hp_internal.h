@@ -84,6 +84,28 @@ struct CopyJob {
     uint32_t vec_bytes;     // widest vector width every span allows
 };
 
+// Copy-on-write page copy over `count` pools that share the page IDs.
+struct PageCopyJob {
+    bool idx64;
+    uint32_t vec_bytes;
+    uint32_t page_size;
+    uint64_t page_bytes;      // P * R
+    uint64_t copies;          // entries of src_pages / dst_pages
+    const void *src_pages, *dst_pages;
+    uint32_t count;
+    void *const *pools;
+    float *const *scales;     // per pool, may be null (or hold nulls)
+};
+
+// Page-range check of a copy's page IDs (checked mode): first failing copy
+// index in the workspace head, like the validator.
+struct PageCheckJob {
+    bool idx64;
+    uint64_t copies, num_pages;
+    const void *src_pages, *dst_pages;
+    void *workspace;
+};
+
 struct ValidateJob {
     bool idx64;
     uint64_t num_pages, page_size, num_seqs, num_block_entries;
@@ -96,6 +118,8 @@ uint64_t plan_workspace_bytes(uint64_t num_seqs);
 
 hipError_t launch_copy(const CopyJob &job, hipStream_t stream);
 hipError_t launch_validate(const ValidateJob &job, hipStream_t stream);
+hipError_t launch_copy_pages(const PageCopyJob &job, hipStream_t stream);
+hipError_t launch_check_pages(const PageCheckJob &job, hipStream_t stream);
 
 // Key layout of the validator's atomicMin: check rank in the top byte,
 // failing index below it.

@@ -574,6 +574,59 @@ __global__ __launch_bounds__(256) void validate_kernel(VArgs a) {
     }
 }
 
+// ---- copy-on-write page copy ---------------------------------------------------------
+
+constexpr uint32_t kPageChunkBytes = 16384;  // bytes of one page a workgroup copies
+
+struct PArgs {
+    const void *src_pages, *dst_pages;
+    uint64_t page_bytes;
+    uint32_t page_size, chunks_per_page;
+    unsigned char *pool[kMaxBatch];
+    float *scales[kMaxBatch];
+};
+
+// Workgroup (x, m) copies chunk x % chunks_per_page of copy x / chunks_per_page
+// in pool m; the chunk-0 workgroup also copies the page's slot scales. Every
+// copy reads a page and writes another one exactly once: non-temporal both
+// ways.
+template <typename IdxT, int VEC>
+__global__ __launch_bounds__(kThreads) void copy_pages_kernel(PArgs a) {
+    const uint64_t x = blockIdx.x;
+    const uint64_t i = x / a.chunks_per_page;
+    const uint32_t c = (uint32_t)(x - i * a.chunks_per_page);
+    const uint64_t src = uni64(ld_idx<IdxT>(a.src_pages, i));
+    const uint64_t dst = uni64(ld_idx<IdxT>(a.dst_pages, i));
+    unsigned char *pool = a.pool[blockIdx.y];
+    const uint64_t off = (uint64_t)c * kPageChunkBytes;
+    const uint64_t left = a.page_bytes - off;
+    const uint32_t n = (uint32_t)(left < kPageChunkBytes ? left : kPageChunkBytes);
+    copy_span<VEC, true>(pool + src * a.page_bytes + off, pool + dst * a.page_bytes + off, n);
+    float *scales = a.scales[blockIdx.y];
+    if (scales && c == 0) {
+        for (uint32_t t = threadIdx.x; t < a.page_size; t += kThreads)
+            scales[dst * a.page_size + t] = scales[src * a.page_size + t];
+    }
+}
+
+template <typename IdxT>
+__global__ __launch_bounds__(256) void check_pages_kernel(const void *src_pages,
+                                                          const void *dst_pages, uint64_t copies,
+                                                          uint64_t num_pages,
+                                                          unsigned long long *ws) {
+    unsigned long long key = ~0ull;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < copies;
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        if (ld_idx<IdxT>(src_pages, i) >= num_pages || ld_idx<IdxT>(dst_pages, i) >= num_pages)
+            key = min64(key, vkey(kRankPageRange, i));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        key = min64(key, (unsigned long long)__shfl_xor(key, off, 64));
+    if ((threadIdx.x & 63) == 0 && key != ~0ull)
+        atomicMin(&ws[0], key);
+}
+
 // ---- host-side dispatch ----------------------------------------------------------------
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -737,6 +790,66 @@ hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
             return e;
     }
     return hipSuccess;
+}
+
+template <typename IdxT, int VEC>
+hipError_t launch_pages(PArgs &a, const PageCopyJob &job, hipStream_t stream) {
+    const uint64_t units = job.copies * a.chunks_per_page;
+    for (uint32_t first = 0; first < job.count; first += kMaxBatch) {
+        const uint32_t n = job.count - first < kMaxBatch ? job.count - first : kMaxBatch;
+        for (uint32_t m = 0; m < n; ++m) {
+            a.pool[m] = static_cast<unsigned char *>(job.pools[first + m]);
+            a.scales[m] = job.scales ? job.scales[first + m] : nullptr;
+        }
+        hipLaunchKernelGGL((copy_pages_kernel<IdxT, VEC>), dim3((uint32_t)units, n),
+                           dim3(kThreads), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+template <typename IdxT>
+hipError_t launch_pages_idx(PArgs &a, const PageCopyJob &job, hipStream_t st) {
+    switch (job.vec_bytes) {
+    case 16: return launch_pages<IdxT, 16>(a, job, st);
+    case 8: return launch_pages<IdxT, 8>(a, job, st);
+    case 4: return launch_pages<IdxT, 4>(a, job, st);
+    case 2: return launch_pages<IdxT, 2>(a, job, st);
+    default: return launch_pages<IdxT, 1>(a, job, st);
+    }
+}
+
+hipError_t launch_copy_pages(const PageCopyJob &job, hipStream_t stream) {
+    (void)hipGetLastError();  // see launch_copy
+    PArgs a = {};
+    a.src_pages = job.src_pages;
+    a.dst_pages = job.dst_pages;
+    a.page_bytes = job.page_bytes;
+    a.page_size = job.page_size;
+    a.chunks_per_page = (uint32_t)((job.page_bytes + kPageChunkBytes - 1) / kPageChunkBytes);
+    return job.idx64 ? launch_pages_idx<uint64_t>(a, job, stream)
+                     : launch_pages_idx<uint32_t>(a, job, stream);
+}
+
+hipError_t launch_check_pages(const PageCheckJob &job, hipStream_t stream) {
+    (void)hipGetLastError();  // see launch_copy
+    unsigned long long *ws = static_cast<unsigned long long *>(job.workspace);
+    hipLaunchKernelGGL(validate_init_kernel, dim3(1), dim3(64), 0, stream, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    uint64_t blocks = (job.copies + 255) / 256;
+    if (blocks > 4096)
+        blocks = 4096;
+    if (job.idx64)
+        hipLaunchKernelGGL(check_pages_kernel<uint64_t>, dim3((uint32_t)blocks), dim3(256), 0,
+                           stream, job.src_pages, job.dst_pages, job.copies, job.num_pages, ws);
+    else
+        hipLaunchKernelGGL(check_pages_kernel<uint32_t>, dim3((uint32_t)blocks), dim3(256), 0,
+                           stream, job.src_pages, job.dst_pages, job.copies, job.num_pages, ws);
+    return hipGetLastError();
 }
 
 hipError_t launch_validate(const ValidateJob &job, hipStream_t stream) {

@@ -218,6 +218,34 @@ hp_status hp_gather_dequant_batch(const hp_desc *desc, uint32_t count, void *con
                                   uint32_t out_dtype, void *workspace, size_t workspace_bytes,
                                   uint32_t flags, void *stream);
 
+/* ---- Copy-on-write page copy -----------------------------------------------
+ *
+ * [Day51] "Copy-on-write for beam search and prefix sharing": pages shared by
+ * several sequences ([Hurray] Prefix Sharing) are copied before one of them
+ * writes into it; [Hurray] Per-page-slot parameters: a page carries its own
+ * slot scales. For i < count, page dst_pages[i] of the pool becomes a copy of
+ * page src_pages[i] (all page_size * num_heads * head_dim elements), and, when
+ * the pool has scales, scales[dst*P .. dst*P+P) become those of src.
+ *
+ * src_pages / dst_pages: `count` DEVICE page IDs of desc->index_type. The
+ * destinations must be distinct and must not be sources of the same call
+ * (otherwise the result depends on scheduling). Only the pool (and its
+ * scales) is read and written; block_table / seq_ptr / seq_lens are not used.
+ * Asynchronous. Flags: HP_FLAG_CHECKED checks that every page ID is below
+ * num_pages (HP_ERR_PAGE_RANGE otherwise; workspace >= 256 bytes needed). */
+hp_status hp_copy_pages(const hp_desc *desc, const void *src_pages, const void *dst_pages,
+                        uint64_t count, void *workspace, size_t workspace_bytes, uint32_t flags,
+                        void *stream);
+
+/* The same copies in `num_pools` pools at once (every layer and role of a KV
+ * cache names a page by the same ID): pools and scales are HOST arrays of
+ * `num_pools` DEVICE pointers (scales may be NULL, or hold NULLs); the pools
+ * must not overlap. desc's own page_pool and scales are ignored. */
+hp_status hp_copy_pages_batch(const hp_desc *desc, uint32_t num_pools, void *const *pools,
+                              float *const *scales, const void *src_pages, const void *dst_pages,
+                              uint64_t count, void *workspace, size_t workspace_bytes,
+                              uint32_t flags, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *hp_status_str(int status);
 

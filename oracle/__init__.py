@@ -74,6 +74,8 @@ def _load():
     lib.oracle_gather_dequant_rows.restype = _u64
     lib.oracle_gather_dequant_rows.argtypes = [_vp, _vp, _u64, _u64, _u64, _vp, _vp,
                                                _vp, _u64, _vp, _u64, _vp]
+    lib.oracle_copy_pages.restype = None
+    lib.oracle_copy_pages.argtypes = [_vp, _u64, _u64, _u64, _u64, _vp, _vp, _vp, _u64]
     lib.oracle_payload.restype = ctypes.c_int
     lib.oracle_payload.argtypes = [_u64] * 7 + [_vp]
     _lib = lib
@@ -213,6 +215,20 @@ def gather_dequant_rows(pool, scales, rows, *, page_size, num_heads, head_dim,
                                              _ptr(out))
     assert missing == 0
     return out
+
+
+def copy_pages(pool, src_pages, dst_pages, *, page_size, num_heads, head_dim, scales=None):
+    """Copy-on-write page copy; returns (new pool, new scales or None)."""
+    lib = _load()
+    pool, eb = _pool_geometry(pool, page_size, num_heads, head_dim)
+    result = pool.copy()
+    sc = None if scales is None else np.array(scales, dtype=np.float32, copy=True)
+    src, dst = _idx(src_pages), _idx(dst_pages)
+    assert len(src) == len(dst)
+    lib.oracle_copy_pages(_ptr(result), eb, page_size, num_heads, head_dim, _ptr(sc),
+                          _ptr(src) if len(src) else None, _ptr(dst) if len(dst) else None,
+                          len(src))
+    return result, sc
 
 
 PAYLOAD_FIELDS = ("reserved_pages", "active_pages", "allocated_slots", "live_slots",

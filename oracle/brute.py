@@ -73,3 +73,16 @@ def validate(rank, paged_axis, num_pages, page_size, block_table, seq_ptr, seq_l
     if sum(seq_lens) != total_tokens:
         fails.append(("total_tokens", 0))
     return fails
+
+
+def copy_pages(pool4, scales, src_pages, dst_pages):
+    """Deep copy of pool4 (and of the flat scales list) with page dst_pages[i]
+    replaced by page src_pages[i], applied in order."""
+    page_size = len(pool4[0])
+    pool = [[[list(head) for head in slot] for slot in page] for page in pool4]
+    sc = None if scales is None else list(scales)
+    for src, dst in zip(src_pages, dst_pages):
+        pool[dst] = [[list(head) for head in slot] for slot in pool[src]]
+        if sc is not None:
+            sc[dst * page_size:(dst + 1) * page_size] = sc[src * page_size:(src + 1) * page_size]
+    return pool, sc

@@ -333,6 +333,34 @@ uint64_t oracle_gather_dequant_rows(const int8_t *page_pool, const float *scales
     return missing;
 }
 
+/* Copy-on-write page copy: page by page, slot by slot, element by element,
+ * in the order the copies are listed. */
+void oracle_copy_pages(void *page_pool, uint64_t elem_bytes, uint64_t page_size,
+                       uint64_t num_heads, uint64_t head_dim, float *scales,
+                       const uint64_t *src_pages, const uint64_t *dst_pages,
+                       uint64_t count)
+{
+    unsigned char *pool = (unsigned char *)page_pool;
+    uint64_t i, slot, h, d;
+
+    for (i = 0; i < count; i++) {
+        for (slot = 0; slot < page_size; slot++) {
+            for (h = 0; h < num_heads; h++) {
+                for (d = 0; d < head_dim; d++) {
+                    uint64_t from = ((src_pages[i] * page_size + slot) * num_heads + h) *
+                                    head_dim + d;
+                    uint64_t to = ((dst_pages[i] * page_size + slot) * num_heads + h) *
+                                  head_dim + d;
+                    memcpy(pool + to * elem_bytes, pool + from * elem_bytes, elem_bytes);
+                }
+            }
+            if (scales)
+                scales[dst_pages[i] * page_size + slot] =
+                    scales[src_pages[i] * page_size + slot];
+        }
+    }
+}
+
 /* [Rust20] "Count live rows and two kinds of unused payload": with
  * U = 2*B*H_kv*d slots per token position (K and V), A = ceil(n/P) active
  * pages and ceil(C/P)*P reserved positions,

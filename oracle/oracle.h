@@ -116,6 +116,17 @@ uint64_t oracle_gather_dequant_rows(const int8_t *page_pool, const float *scales
                                     uint64_t num_seqs, const uint64_t *rows,
                                     uint64_t rows_count, uint16_t *out);
 
+/* Copy-on-write page copy ([Day51] "Copy-on-write for beam search and prefix
+ * sharing": a shared block is copied before one request modifies it;
+ * [Hurray] Per-page-slot parameters: a page carries its own scales). For
+ * i = 0 .. count-1 in order, every element of page src_pages[i] is copied to
+ * page dst_pages[i], and, when scales is not NULL, so are that page's
+ * page_size slot scales. */
+void oracle_copy_pages(void *page_pool, uint64_t elem_bytes, uint64_t page_size,
+                       uint64_t num_heads, uint64_t head_dim, float *scales,
+                       const uint64_t *src_pages, const uint64_t *dst_pages,
+                       uint64_t count);
+
 /* [Rust20] "Count live rows and two kinds of unused payload": buffer-length
  * payload of one layer's K and V arrays. out[] receives, in order:
  *  0 reserved pages      1 active pages

@@ -25,7 +25,8 @@ def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"hp_workspace_bytes", "hp_validate", "hp_gather", "hp_scatter",
                           "hp_gather_dequant", "hp_status_str", "hp_last_hip_error",
-                          "hp_gather_batch", "hp_scatter_batch", "hp_gather_dequant_batch"}
+                          "hp_gather_batch", "hp_scatter_batch", "hp_gather_dequant_batch",
+                          "hp_copy_pages", "hp_copy_pages_batch"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -199,3 +200,26 @@ def test_batch_empty_batch_enqueues_nothing():
     d = desc(num_seqs=0, num_block_entries=0, block_table=None, seq_lens=None, total_tokens=0)
     assert L.hp_gather_batch(ctypes.byref(d), 2, _arr(ALIGNED, ALIGNED + 0x10000000),
                              _arr(None, None), None, 0, 0, None) == S["HP_OK"]
+
+
+def test_copy_pages_rejections():
+    d = desc()
+    src, dst = ALIGNED + 0x40000000, ALIGNED + 0x40001000
+    cp = lambda dd, s_, d_, n, flags=0, ws=None, wn=0: L.hp_copy_pages(  # noqa: E731
+        ctypes.byref(dd) if dd is not None else None, s_, d_, n, ws, wn, flags, None)
+    assert cp(None, src, dst, 4) == S["HP_ERR_NULL"]
+    assert cp(desc(rank=2), src, dst, 4) == S["HP_ERR_RANK"]
+    assert cp(d, src, dst, 0) == S["HP_OK"]                       # nothing to copy
+    assert cp(d, None, dst, 4) == S["HP_ERR_NULL"]
+    assert cp(d, src + 2, dst, 4) == S["HP_ERR_ALIGN"]            # u32 page IDs
+    assert cp(d, src, dst, 4, flags=2) == S["HP_ERR_ARG"]         # scatter-only flag
+    assert cp(d, src, dst, 4, flags=hp.HP_FLAG_CHECKED) == S["HP_ERR_WORKSPACE"]
+    assert cp(desc(page_pool=ALIGNED + 16), src, dst, 4) == S["HP_ERR_ALIGN"]
+    P1, P2 = ALIGNED, ALIGNED + 0x10000000
+    cb = lambda pools, n=2: L.hp_copy_pages_batch(  # noqa: E731
+        ctypes.byref(d), n, pools, None, src, dst, 4, None, 0, 0, None)
+    assert cb(None) == S["HP_ERR_NULL"]
+    assert cb(_arr(P1, P1 + 64)) == S["HP_ERR_ARG"]               # written pools overlap
+    assert cb(_arr(P1, None)) == S["HP_ERR_NULL"]
+    assert cb(_arr(P1, P2 + 8)) == S["HP_ERR_ALIGN"]
+    assert cb(_arr(P1, P2), n=0) == S["HP_OK"]

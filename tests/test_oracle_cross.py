@@ -168,3 +168,23 @@ def test_planted_index_mistakes_fail_the_pins():
     assert [good(p) for p in range(7)] == expect
     for m in mutants:
         assert [m(p) for p in range(7)] != expect
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_copy_pages_brute(seed):
+    rng = np.random.default_rng(5000 + seed)
+    w = workloads.random_small(5000 + seed, dtypes=("f16", "i8", "f64"))
+    pool = _np_pool(w)
+    N = w.num_pages
+    n = int(rng.integers(0, max(1, N // 2) + 1))
+    perm = rng.permutation(N)
+    dst = perm[:n]                                   # distinct destinations
+    src = rng.permutation(perm[n:])[:n] if N - n >= n else perm[n:n + n]
+    src = np.resize(src, n) if n else src
+    scales = rng.random(N * w.page_size).astype(np.float32)
+    got, got_sc = oracle.copy_pages(pool, src, dst, page_size=w.page_size,
+                                    num_heads=w.num_heads, head_dim=w.head_dim, scales=scales)
+    ref, ref_sc = brute.copy_pages(pool.tolist(), scales.tolist(), [int(x) for x in src],
+                                   [int(x) for x in dst])
+    assert got.tolist() == ref
+    assert got_sc.tolist() == ref_sc

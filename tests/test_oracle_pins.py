@@ -317,3 +317,33 @@ def test_dequant_matches_library_arithmetic():
            * torch.from_numpy(sc)[:, None]).to(torch.bfloat16)
     ref = ref.view(torch.int16).numpy().view(np.uint16).reshape(got.shape)
     assert np.array_equal(got, ref)
+
+
+def test_day51_copy_on_write_keeps_the_other_request_intact():
+    """[Day51] Copy-on-write: requests D and E share a 24-token system prompt
+    (blocks 0 and 1; block 1 half full) and each has a private block. Before
+    E writes its next token into the shared half-full block, that block is
+    copied to a fresh one and E's table points there ([Hurray] Prefix
+    Sharing: aliasing is static structure; the copy is the writer's job).
+    D's gathered rows are unchanged, E's prefix rows equal D's, E's new token
+    is in place, and the shared page itself is untouched."""
+    P, H, D, N = 16, 2, 4, 8
+    pool = _labelled_pool(N, P, H, D)
+    shared = [0, 1]
+    bt_d, bt_e = shared + [2], shared + [3]
+    sp = [0, 3, 6]
+    lens = [24, 24]                                  # both hold only the prompt
+    kw = dict(page_size=P, num_heads=H, head_dim=D)
+    before = oracle.gather(pool, block_table=bt_d + bt_e, seq_ptr=sp, seq_lens=lens, **kw)
+    # copy-on-write: block 1 -> fresh block 4 for E, then E appends at position 24
+    pool2, _ = oracle.copy_pages(pool, [1], [4], **kw)
+    bt_e2 = [0, 4, 3]
+    new_row = np.full((1, H, D), 0x7777, dtype=pool.dtype)
+    pool3 = oracle.scatter(pool2, new_row, block_table=bt_e2, seq_ptr=[0, 3], seq_lens=[1],
+                           seq_start=[24], **kw)
+    after = oracle.gather(pool3, block_table=bt_d + bt_e2, seq_ptr=sp, seq_lens=[24, 25], **kw)
+    assert np.array_equal(after[:24], before[:24])           # D unchanged
+    assert np.array_equal(after[24:48], before[:24])         # E's prefix == D's
+    assert np.all(after[48] == 0x7777)                       # E's new token
+    assert np.array_equal(pool3[1], pool[1])                 # the shared page untouched
+    assert np.array_equal(pool3[4, 8], new_row[0])           # slot 24 mod 16 of the copy
