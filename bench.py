@@ -540,7 +540,26 @@ def main():
         dst_p = idx(rng.choice(free, n_copy, replace=False))
         t_copy = back_to_back(lambda: hp.copy_pages(desc, src_p, dst_p, stream=stream))
         copy_bytes = 2 * n_copy * 16 * H * D * 2
+        # dequant-gather of the step's int8 pool under each quantization
+        # scheme, with zero points (the general kernel); per-slot is the step's
+        qout = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+        zrng = np.random.default_rng(8)
+        schemes = {}
+        for name, scheme, axis, n_par, per_tok in (
+                ("per_tensor_zp", "per_tensor", 0, 1, 0),
+                ("per_channel_head_zp", "per_channel", 1, H, 0),
+                ("per_channel_head_dim_zp", "per_channel", 2, D, 0),
+                ("per_block_affine_zp", "per_block_affine", 0, wq.num_pages * 16, 5)):
+            sc = torch.from_numpy(zrng.uniform(1e-3, 1e-1, n_par).astype(np.float32)).to(dev)
+            zp = torch.from_numpy(zrng.integers(-128, 128, n_par).astype(np.int8)).to(dev)
+            t_q = back_to_back(lambda: hp.gather_dequant_q(qdesc, qout, scheme, sc, axis=axis,
+                                                           zero_points=zp, stream=stream))
+            qb = T * H * D * 3 + per_tok * T
+            schemes[name] = {"algorithmic_bytes": qb, "launch_us": round(t_q * 1e3, 1),
+                             "gb_per_s": round(qb / (t_q / 1e3) / 1e9, 1)}
+        del qout
         result["extras"] = {
+            "dequant_schemes": schemes,
             "batched_append": batched_append(hp, torch, np, dev, stream, args.kernel_reps),
             "copy_pages": {"workload": "1,024 pages of the decode pool (16 x 32 x 128 fp16 = "
                                        "128 KiB each) copied to unreferenced pages",

@@ -22,6 +22,7 @@ import os
 import torch  # noqa: F401,E402
 
 __all__ = ["Descriptor", "HpError", "gather", "scatter", "gather_dequant", "validate",
+           "gather_dequant_q", "QUANT_SCHEME",
            "gather_batch", "scatter_batch", "gather_dequant_batch", "copy_pages",
            "copy_pages_batch", "workspace_bytes",
            "status_str", "last_hip_error", "lib", "LIB_PATH", "STATUS"]
@@ -55,7 +56,7 @@ if len(_hip_runtimes()) > 1:
 STATUS = {
     0: "HP_OK", 1: "HP_ERR_NULL", 2: "HP_ERR_ARG", 3: "HP_ERR_RANK", 4: "HP_ERR_PAGED_AXIS",
     5: "HP_ERR_INDEX_TYPE", 6: "HP_ERR_DTYPE", 7: "HP_ERR_ALIGN", 8: "HP_ERR_WORKSPACE",
-    9: "HP_ERR_SHARDED", 16: "HP_ERR_SEQPTR_FIRST", 17: "HP_ERR_SEQPTR_LAST",
+    9: "HP_ERR_SHARDED", 10: "HP_ERR_QUANT", 16: "HP_ERR_SEQPTR_FIRST", 17: "HP_ERR_SEQPTR_LAST",
     18: "HP_ERR_SEQPTR_ORDER", 19: "HP_ERR_PAGE_RANGE", 20: "HP_ERR_SEQ_LEN",
     21: "HP_ERR_TOTAL_TOKENS", 32: "HP_ERR_HIP",
 }
@@ -63,6 +64,17 @@ CODE = {v: k for k, v in STATUS.items()}
 HP_INDEX_U32, HP_INDEX_U64 = 0x00, 0x01
 DTYPE = {"i8": 1, "u8": 2, "f16": 3, "bf16": 4, "f32": 5, "f64": 6}
 HP_FLAG_CHECKED, HP_FLAG_ZERO_TAIL, HP_FLAG_STREAM = 1, 2, 4
+# Quantization scheme tags (include/hp.h, HP_QUANT_*).
+QUANT_SCHEME = {"per_tensor": 0x01, "per_channel": 0x02, "per_block_affine": 0x03}
+
+
+class HpQuant(ctypes.Structure):
+    """Mirror of ``hp_quant`` (include/hp.h)."""
+    _fields_ = [
+        ("scheme", ctypes.c_uint32), ("axis", ctypes.c_uint32),
+        ("block_size", ctypes.c_uint64),
+        ("scales", ctypes.c_void_p), ("zero_points", ctypes.c_void_p),
+    ]
 
 
 class HpDesc(ctypes.Structure):
@@ -99,6 +111,9 @@ _lib.hp_scatter.restype = ctypes.c_int
 _lib.hp_scatter.argtypes = [_P, _vp, _vp, _vp, _sz, _u32, _vp]
 _lib.hp_gather_dequant.restype = ctypes.c_int
 _lib.hp_gather_dequant.argtypes = [_P, _vp, _u32, _vp, _sz, _u32, _vp]
+_lib.hp_gather_dequant_q.restype = ctypes.c_int
+_lib.hp_gather_dequant_q.argtypes = [_P, ctypes.POINTER(HpQuant), _vp, _u32, _vp, _sz, _u32,
+                                     _vp]
 _lib.hp_status_str.restype = ctypes.c_char_p
 _lib.hp_status_str.argtypes = [ctypes.c_int]
 _lib.hp_last_hip_error.restype = ctypes.c_char_p
@@ -292,6 +307,25 @@ def gather_dequant(desc, out, *, checked=False, workspace=None, stream=None):
     _check(_lib.hp_gather_dequant(p, _ptr(out), DTYPE["bf16"], ws, n,
                                   HP_FLAG_CHECKED if checked else 0,
                                   _stream(stream, desc.device)), "hp_gather_dequant")
+    return out
+
+
+def gather_dequant_q(desc, out, scheme, scales, *, axis=0, block_size=None, zero_points=None,
+                     checked=False, workspace=None, stream=None):
+    """out[T, H, D] (bfloat16) <- dequantised logical tensor of an int8 or
+    uint8 pool under a quantization scheme ("per_tensor", "per_channel" with
+    axis 1 or 2, "per_block_affine" with axis 0 and block_size = page size).
+    scales: float32 device tensor; zero_points: device tensor of the pool's
+    element type, or None. desc.scales is not used."""
+    T = out.shape[0]
+    p = desc.with_tokens(T)
+    ws, n = _workspace(desc, T, workspace)
+    q = HpQuant(QUANT_SCHEME[scheme] if isinstance(scheme, str) else int(scheme),
+                int(axis), int(desc.c.page_size if block_size is None else block_size),
+                _ptr(scales), _ptr(zero_points))
+    _check(_lib.hp_gather_dequant_q(p, ctypes.byref(q), _ptr(out), DTYPE["bf16"], ws, n,
+                                    HP_FLAG_CHECKED if checked else 0,
+                                    _stream(stream, desc.device)), "hp_gather_dequant_q")
     return out
 
 

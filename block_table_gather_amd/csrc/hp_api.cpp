@@ -202,8 +202,18 @@ uint32_t widest_vec(uint64_t row_bytes, const Members &m, uint32_t maxv, uint32_
     return 1;
 }
 
+// A dequant scheme other than the per-slot, symmetric, int8 fast path.
+struct QuantSpec {
+    bool ext;            // use the general dequant kernel
+    uint32_t mode;       // 0 per-slot, 1 per-tensor, 2 per-head, 3 per-head_dim
+    bool is_unsigned;
+    const float *scales;
+    const void *zero_points;
+};
+
 hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const Members &m,
-                 const void *seq_start, uint32_t flags, void *ws, hipStream_t stream) {
+                 const void *seq_start, uint32_t flags, void *ws, hipStream_t stream,
+                 const QuantSpec *q = nullptr) {
     const bool zero_tail = (flags & HP_FLAG_ZERO_TAIL) != 0;
     hp::CopyJob j = {};
     j.op = op;
@@ -265,6 +275,15 @@ hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const Members &
     j.workspace = ws ? static_cast<unsigned char *>(ws) + kValidateBytes : nullptr;
     j.vec_bytes = op == hp::Op::Dequant ? widest_vec(g.row_bytes, m, 8, 2)
                                         : widest_vec(g.row_bytes, m, 16, 1);
+    if (q) {
+        j.quant_ext = q->ext;
+        j.quant_mode = q->mode;
+        j.quant_unsigned = q->is_unsigned;
+        j.quant_scales = q->scales;
+        j.zero_points = q->zero_points;
+        j.head_dim = d->head_dim;
+        j.quant_channels = q->mode == 2 ? d->num_heads : q->mode == 3 ? d->head_dim : 0;
+    }
     const hipError_t e = hp::launch_copy(j, stream);
     return e == hipSuccess ? HP_OK : hip_failed(e);
 }
@@ -588,6 +607,62 @@ hp_status hp_gather_dequant_batch(const hp_desc *desc, uint32_t count, void *con
     return launch(&d, g, hp::Op::Dequant, m, nullptr, flags, workspace, (hipStream_t)stream);
 }
 
+hp_status hp_gather_dequant_q(const hp_desc *desc, const hp_quant *quant, void *out,
+                              uint32_t out_dtype, void *workspace, size_t workspace_bytes,
+                              uint32_t flags, void *stream) {
+    Geometry g;
+    bool done;
+    if (!desc || !quant)
+        return HP_ERR_NULL;
+    hp_desc d = *desc;
+    d.scales = quant->scales;  // the scheme's scales replace the descriptor's
+    hp_status st = check_desc(&d, &g);
+    if (st != HP_OK)
+        return st;
+    if ((d.dtype != HP_DTYPE_I8 && d.dtype != HP_DTYPE_U8) || out_dtype != HP_DTYPE_BF16)
+        return HP_ERR_DTYPE;
+    uint32_t mode;
+    switch (quant->scheme) {
+    case HP_QUANT_PER_TENSOR: mode = 1; break;
+    case HP_QUANT_PER_CHANNEL:
+        if (quant->axis != 1 && quant->axis != 2)
+            return HP_ERR_QUANT;
+        mode = quant->axis == 1 ? 2 : 3;
+        break;
+    case HP_QUANT_PER_BLOCK_AFFINE:
+        if (quant->axis != 0 || quant->block_size != d.page_size)
+            return HP_ERR_QUANT;
+        mode = 0;
+        break;
+    default: return HP_ERR_QUANT;
+    }
+    if (!quant->scales || (d.total_tokens && !out))
+        return HP_ERR_NULL;
+    if (!aligned(quant->scales, 64) || !aligned(quant->zero_points, 64) || !aligned(out, 2))
+        return HP_ERR_ALIGN;
+    const uint64_t out_bytes = d.total_tokens * g.row_bytes * 2;
+    const uint64_t n_params = mode == 0 ? d.num_pages * d.page_size
+                              : mode == 1 ? 1 : mode == 2 ? d.num_heads : d.head_dim;
+    if (overlaps(out, out_bytes, d.page_pool, g.pool_bytes) ||
+        overlaps(out, out_bytes, quant->scales, n_params * 4) ||
+        overlaps(out, out_bytes, quant->zero_points, n_params))
+        return HP_ERR_ARG;
+    st = prologue(&d, g, flags, HP_FLAG_CHECKED, nullptr, workspace, workspace_bytes,
+                  (hipStream_t)stream, &done);
+    if (st != HP_OK || done)
+        return st;
+    void *pool = d.page_pool;
+    const float *scales = quant->scales;
+    const Members m = {1, &pool, &out, &scales};
+    QuantSpec q;
+    q.ext = !(mode == 0 && !quant->zero_points && d.dtype == HP_DTYPE_I8);
+    q.mode = mode;
+    q.is_unsigned = d.dtype == HP_DTYPE_U8;
+    q.scales = quant->scales;
+    q.zero_points = quant->zero_points;
+    return launch(&d, g, hp::Op::Dequant, m, nullptr, flags, workspace, (hipStream_t)stream, &q);
+}
+
 hp_status hp_copy_pages(const hp_desc *desc, const void *src_pages, const void *dst_pages,
                         uint64_t count, void *workspace, size_t workspace_bytes, uint32_t flags,
                         void *stream) {
@@ -622,6 +697,7 @@ const char *hp_status_str(int status) {
     case HP_ERR_ALIGN: return "HP_ERR_ALIGN: buffer misaligned";
     case HP_ERR_WORKSPACE: return "HP_ERR_WORKSPACE: workspace missing or too small";
     case HP_ERR_SHARDED: return "HP_ERR_SHARDED: block-paged tensors cannot be sharded";
+    case HP_ERR_QUANT: return "HP_ERR_QUANT: quantization scheme not accepted on block-paged";
     case HP_ERR_SEQPTR_FIRST: return "HP_ERR_SEQPTR_FIRST: seq_ptr[0] != 0";
     case HP_ERR_SEQPTR_LAST: return "HP_ERR_SEQPTR_LAST: seq_ptr[num_seqs] != block_table length";
     case HP_ERR_SEQPTR_ORDER: return "HP_ERR_SEQPTR_ORDER: seq_ptr decreases";

@@ -82,6 +82,16 @@ struct CopyJob {
     const float *const *scales;  // [count] per-slot scales (dequant), else null
     void *workspace;        // plan arrays when num_seqs > kFusedMaxSeqs
     uint32_t vec_bytes;     // widest vector width every span allows
+    // Dequant under a general scheme (single pool): 0 = per-slot scales from
+    // `scales` (the fast path when there is no zero point and q is signed),
+    // 1 = per-tensor, 2 = per-head, 3 = per-head_dim parameters.
+    bool quant_ext;
+    uint32_t quant_mode;
+    bool quant_unsigned;    // uint8 pool (else int8)
+    const float *quant_scales;   // per-tensor / per-channel scales
+    const void *zero_points;     // same count as the scales, pool element type; may be null
+    uint32_t head_dim;
+    uint32_t quant_channels;     // per-channel table entries (modes 2, 3)
 };
 
 // Copy-on-write page copy over `count` pools that share the page IDs.

@@ -108,6 +108,13 @@ struct Args {
     uint32_t vecs_per_row;    // dequant: input vectors per row
     Div div_vpr, div_rpc, div_page, div_upp;  // by vecs_per_row, rows_per_unit,
                                               // page_size, units_per_page
+    // General dequant scheme (see CopyJob): signedness and parameters.
+    uint32_t quant_unsigned;
+    const float *quant_scales;
+    const void *zero_points;
+    uint32_t head_dim;
+    uint32_t quant_channels;  // entries of a per-channel table
+    Div div_hd;
     // Pool m of the launch is moved by grid row m (blockIdx.y).
     unsigned char *pool[kMaxBatch];   // scatter writes it, gather/dequant read it
     unsigned char *rows[kMaxBatch];   // the logical tensor of pool m
@@ -269,10 +276,13 @@ __device__ __forceinline__ void zero_span(unsigned char *__restrict__ dst, uint3
 
 // fp32 -> bf16 bits, round to nearest even (gfx950 has a hardware
 // conversion with IEEE rounding for this type).
+// The pair converts as one vector, which maps to a single v_cvt_pk_bf16_f32
+// (lo in the low half).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const bf16x2 v = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ uint16_t to_bf16(float x) {
     __bf16 a = (__bf16)x;
@@ -359,16 +369,256 @@ __device__ __forceinline__ uint32_t group_order(uint32_t b, uint32_t groups) {
 #endif
 }
 
+// ---- dequant under any accepted scheme ----------------------------------------
+//
+// [Hurray] Per-scheme composition: out = bf16(fp32(q - zp) * scale). q - zp
+// is an integer of at most 9 bits, so the float difference below is exact and
+// the product rounds once, as the definition asks. A uint8 pool takes the
+// signed path with the top bit of both q and zp flipped: (q - 128) - (zp - 128)
+// is the same difference. Without zero points zp is 0 (-128 after the flip).
+// QM: 0 per-slot, 1 per-tensor, 2 per-head, 3 per-head_dim parameters.
+
+// Zero point k as a float, with the flip applied.
+__device__ __forceinline__ float zp_at(const Args &a, uint64_t k, uint32_t flip) {
+    const uint32_t b = a.zero_points ? static_cast<const uint8_t *>(a.zero_points)[k] : 0u;
+    return sbyte(b ^ flip, 0);
+}
+
+// The VIN bytes of an input vector as 32-bit words (low bytes first).
+template <int VIN>
+__device__ __forceinline__ void to_words(const typename Vec<VIN>::T &v, uint32_t (&w)[(VIN + 3) / 4]) {
+    if constexpr (VIN == 8) {
+        w[0] = v.x;
+        w[1] = v.y;
+    } else {
+        w[0] = (uint32_t)v;
+    }
+}
+
+// VIN consecutive scales starting at p (p aligned to 4 * VIN bytes). The
+// vector is copied whole: clang's __builtin_bit_cast of an ext-vector element
+// (v.y) reads element 0, so elements are never bit-cast one by one.
+template <int VIN>
+__device__ __forceinline__ void load_scales(const float *__restrict__ p, float (&o)[VIN]) {
+    if constexpr (VIN >= 4) {
+#pragma unroll
+        for (int c = 0; c < VIN / 4; ++c) {
+            const u32x4 v = reinterpret_cast<const u32x4 *>(p)[c];
+            __builtin_memcpy(&o[4 * c], &v, sizeof v);
+        }
+    } else if constexpr (VIN == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
+        __builtin_memcpy(&o[0], &v, sizeof v);
+    } else {
+        o[0] = p[0];
+    }
+}
+
+// One channel's scale and zero point (flipped, as a float): the per-channel
+// tables are staged in LDS in this form when they have at most
+// kQuantLdsMax entries.
+struct QParam {
+    float scale, zp;
+};
+constexpr uint32_t kQuantLdsMax = 2048;
+
+// QM 2 and 3 read the staged table; QM 4 and 5 are the same schemes (per-head,
+// per-head_dim) with the parameters read from global memory.
+constexpr int channel_axis(int qm) { return qm == 4 ? 2 : qm == 5 ? 3 : qm; }
+
+// VIN consecutive table entries (LDS, 16-byte aligned when VIN >= 2).
+template <int VIN>
+__device__ __forceinline__ void lds_params(const QParam *t, float (&sc)[VIN], float (&zf)[VIN]) {
+    QParam e[VIN];
+    if constexpr (VIN >= 2) {
+#pragma unroll
+        for (int c = 0; c < VIN / 2; ++c) {
+            const u32x4 v = reinterpret_cast<const u32x4 *>(t)[c];
+            __builtin_memcpy(&e[2 * c], &v, sizeof v);
+        }
+    } else {
+        e[0] = t[0];
+    }
+#pragma unroll
+    for (int k = 0; k < VIN; ++k) {
+        sc[k] = e[k].scale;
+        zf[k] = e[k].zp;
+    }
+}
+
+// Scales and (flipped) zero points of the VIN elements that start at element
+// e0 of a row, for the per-channel schemes. When head_dim is a multiple of
+// VIN the vector lies inside one head: one parameter (per-head) or VIN
+// consecutive ones (per-head_dim); otherwise each element finds its own.
+template <int VIN, int QM>
+__device__ __forceinline__ void channel_params(const Args &a, const QParam *tab, uint32_t e0,
+                                               uint32_t flip, float (&sc)[VIN], float (&zf)[VIN]) {
+    constexpr int AX = channel_axis(QM);
+    constexpr bool IN_LDS = QM == 2 || QM == 3;
+    const uint32_t D = a.head_dim;
+    auto one = [&](uint32_t c, float &sv, float &zv) {
+        if constexpr (IN_LDS) {
+            const QParam p = tab[c];
+            sv = p.scale;
+            zv = p.zp;
+        } else {
+            sv = a.quant_scales[c];
+            zv = zp_at(a, c, flip);
+        }
+    };
+    if ((D & (VIN - 1)) == 0) {
+        const uint32_t h = udiv32(e0, a.div_hd);
+        if constexpr (AX == 2) {
+            float sv, zv;
+            one(h, sv, zv);
+#pragma unroll
+            for (int k = 0; k < VIN; ++k) {
+                sc[k] = sv;
+                zf[k] = zv;
+            }
+        } else if constexpr (IN_LDS) {
+            lds_params<VIN>(tab + (e0 - h * D), sc, zf);
+        } else {
+            const uint32_t d0 = e0 - h * D;
+            load_scales<VIN>(a.quant_scales + d0, sc);
+            uint32_t zw[(VIN + 3) / 4] = {};
+            if (a.zero_points)
+                to_words<VIN>(*reinterpret_cast<const typename Vec<VIN>::T *>(
+                                  static_cast<const uint8_t *>(a.zero_points) + d0),
+                              zw);
+#pragma unroll
+            for (int k = 0; k < VIN; ++k)
+                zf[k] = sbyte(zw[k / 4] ^ (flip * 0x01010101u), k % 4);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < VIN; ++k) {
+            const uint32_t e = e0 + k;
+            const uint32_t h = udiv32(e, a.div_hd);
+            one(AX == 2 ? h : e - h * D, sc[k], zf[k]);
+        }
+    }
+}
+
+// One tile of kDequantUnroll vectors per thread starting at vector `base`.
+// FULL: every vector of the tile is in range, so loads and stores need no
+// guard and the compiler keeps all loads in flight at once; the tail tile
+// (FULL = false) checks each index.
+template <int VIN, int QM, bool FULL>
+__device__ __forceinline__ void dequant_tile(const Args &a, const typename Vec<VIN>::T *__restrict__ s,
+                                             unsigned char *__restrict__ dst, uint32_t base,
+                                             uint32_t n, float my_scale, float my_zp, float t_scale,
+                                             float t_zp, uint32_t flip, const QParam *tab) {
+    using VI = typename Vec<VIN>::T;
+    using VO = typename Vec<2 * VIN>::T;  // VIN bf16 values
+    VI q[kDequantUnroll];
+#pragma unroll
+    for (int j = 0; j < kDequantUnroll; ++j) {
+        const uint32_t i = base + j * kThreads;
+        if (FULL || i < n)
+            q[j] = ld_stream<false>(s + i);
+    }
+    const uint32_t fw = flip * 0x01010101u;
+#pragma unroll
+    for (int j = 0; j < kDequantUnroll; ++j) {
+        const uint32_t i = base + j * kThreads;
+        const uint32_t row = udiv32(i, a.div_vpr);
+        float rs = 0.0f, rz = 0.0f;
+        if constexpr (QM == 0) {  // every lane takes part in the shuffles
+            rs = __shfl(my_scale, (int)row, 64);
+            rz = __shfl(my_zp, (int)row, 64);
+        }
+        if (!FULL && i >= n)
+            continue;
+        float sc[VIN], zf[VIN];
+        if constexpr (QM == 0 || QM == 1) {
+#pragma unroll
+            for (int k = 0; k < VIN; ++k) {
+                sc[k] = QM == 0 ? rs : t_scale;
+                zf[k] = QM == 0 ? rz : t_zp;
+            }
+        } else {
+            channel_params<VIN, QM>(a, tab, (i - row * a.vecs_per_row) * VIN, flip, sc, zf);
+        }
+        uint32_t w[(VIN + 3) / 4];
+        to_words<VIN>(q[j], w);
+        if constexpr (VIN == 1) {
+            st_stream(to_bf16((sbyte(w[0] ^ fw, 0) - zf[0]) * sc[0]),
+                      reinterpret_cast<uint16_t *>(dst) + i);
+        } else {
+            uint32_t o[VIN / 2];
+#pragma unroll
+            for (int k = 0; k < VIN; k += 2)
+                o[k / 2] = pack_bf16x2((sbyte(w[k / 4] ^ fw, k % 4) - zf[k]) * sc[k],
+                                       (sbyte(w[k / 4] ^ fw, k % 4 + 1) - zf[k + 1]) * sc[k + 1]);
+            VO packed;
+            __builtin_memcpy(&packed, o, sizeof packed);
+            st_stream(packed, reinterpret_cast<VO *>(dst) + i);
+        }
+    }
+}
+
+// Dequantises `rows` rows (rows <= 64) of a unit. Per-slot parameters are held
+// one per lane and fetched by shuffle. `slot0` is the global slot index
+// (phys * page_size + slot) of the unit's first row and `slot_scales` its
+// scale (per-slot scheme only); `tab` is the staged channel table (QM 2, 3).
+template <int VIN, int QM>
+__device__ __forceinline__ void dequant_span_q(const Args &a, const unsigned char *__restrict__ src,
+                                               const float *__restrict__ slot_scales,
+                                               uint64_t slot0, unsigned char *__restrict__ dst,
+                                               uint32_t rows, const QParam *tab) {
+    using VI = typename Vec<VIN>::T;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t flip = a.quant_unsigned ? 0x80u : 0u;
+    float my_scale = 0.0f, my_zp = 0.0f, t_scale = 0.0f, t_zp = 0.0f;
+    if constexpr (QM == 0) {
+        if (lane < rows) {
+            my_scale = slot_scales[lane];
+            my_zp = zp_at(a, slot0 + lane, flip);
+        }
+    } else if constexpr (QM == 1) {
+        t_scale = a.quant_scales[0];
+        t_zp = zp_at(a, 0, flip);
+    }
+    const uint32_t n = rows * a.vecs_per_row;
+    const VI *s = reinterpret_cast<const VI *>(src);
+    constexpr uint32_t kTile = kThreads * kDequantUnroll;
+    uint32_t b0 = 0;
+    for (; b0 + kTile <= n; b0 += kTile)
+        dequant_tile<VIN, QM, true>(a, s, dst, b0 + threadIdx.x, n, my_scale, my_zp, t_scale, t_zp,
+                                    flip, tab);
+    if (b0 < n)
+        dequant_tile<VIN, QM, false>(a, s, dst, b0 + threadIdx.x, n, my_scale, my_zp, t_scale, t_zp,
+                                     flip, tab);
+}
+
+// Bytes of the fused path's LDS sequence table (8 + 4 bytes per sequence),
+// rounded up so that what follows it is 16-byte aligned.
+__host__ __device__ constexpr size_t lds_table_bytes(uint32_t S) {
+    return (12 * (size_t)S + 15) & ~size_t(15);
+}
+
 // ---- the copy kernel -----------------------------------------------------------
 
 // One kernel for all three moves. FUSED: per-sequence offsets rebuilt in LDS
 // (dynamic LDS = 8*S + 4*S bytes); otherwise read from the plan arrays.
-template <typename IdxT, Op OP, int VEC, bool FUSED, bool NTL>
+template <typename IdxT, Op OP, int VEC, bool FUSED, bool NTL, int QM = -1>
 __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const uint32_t S = a.num_seqs;
     const uint32_t *unit_end;
     const uint64_t *tok_begin;
+    // Per-channel dequant parameters, staged once per workgroup after the
+    // sequence table (QM 2, 3).
+    const QParam *tab = nullptr;
+    if constexpr (QM == 2 || QM == 3) {
+        QParam *t = reinterpret_cast<QParam *>(lds + (FUSED ? lds_table_bytes(S) : 0));
+        const uint32_t flip = a.quant_unsigned ? 0x80u : 0u;
+        for (uint32_t c = threadIdx.x; c < a.quant_channels; c += kThreads)
+            t[c] = QParam{a.quant_scales[c], zp_at(a, c, flip)};
+        __syncthreads();
+        tab = t;
+    }
     if constexpr (FUSED) {
         uint64_t *tb = reinterpret_cast<uint64_t *>(lds);
         uint32_t *ue = reinterpret_cast<uint32_t *>(lds + 8 * (size_t)S);
@@ -451,6 +701,9 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
             unsigned char *to = rowsp + (tb + t0) * a.out_row_bytes;
             if constexpr (OP == Op::Gather) {
                 copy_span<VEC, NTL>(from, to, rows * a.row_bytes);
+            } else if constexpr (QM >= 0) {
+                const float *sl = QM == 0 ? a.scales[blockIdx.y] + phys * P + slot0 : nullptr;
+                dequant_span_q<VEC, QM>(a, from, sl, phys * P + slot0, to, rows, tab);
             } else {
                 dequant_span<VEC>(a, from, a.scales[blockIdx.y] + phys * P + slot0, to, rows);
             }
@@ -631,12 +884,13 @@ __global__ __launch_bounds__(256) void check_pages_kernel(const void *src_pages,
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-template <typename IdxT, Op OP, int VEC, bool NTL>
+template <typename IdxT, Op OP, int VEC, bool NTL, int QM = -1>
 hipError_t launch_vec(const Args &a, bool fused, dim3 grid, uint32_t plan_chunks,
                       uint32_t *unit_end, uint64_t *tok_begin, hipStream_t stream) {
+    const size_t qlds = (QM == 2 || QM == 3) ? sizeof(QParam) * (size_t)a.quant_channels : 0;
     if (fused) {
-        const size_t lds = 12 * (size_t)a.num_seqs;
-        hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, true, NTL>), grid, dim3(kThreads), lds,
+        const size_t lds = lds_table_bytes(a.num_seqs) + qlds;
+        hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, true, NTL, QM>), grid, dim3(kThreads), lds,
                            stream, a);
         return hipGetLastError();
     }
@@ -655,7 +909,8 @@ hipError_t launch_vec(const Args &a, bool fused, dim3 grid, uint32_t plan_chunks
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, false, NTL>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, false, NTL, QM>), grid, dim3(kThreads), qlds,
+                       stream, a);
     return hipGetLastError();
 }
 
@@ -665,15 +920,19 @@ hipError_t launch_vec(const Args &a, bool fused, dim3 grid, uint32_t plan_chunks
 // dequant's 1:2 read:write mix reads through the cache.
 template <typename IdxT, Op OP, int VEC>
 hipError_t launch_policy(const Args &a, bool ntl, bool fused, dim3 grid, uint32_t chunks,
-                         uint32_t *ue, uint64_t *tb, hipStream_t st) {
-    if constexpr (OP == Op::Gather) {
-        if (ntl)
-            return launch_vec<IdxT, OP, VEC, true>(a, fused, grid, chunks, ue, tb, st);
-        if (OP == Op::Scatter && ntl)
-            return launch_vec<IdxT, OP, VEC, true>(a, fused, grid, chunks, ue, tb, st);
-        return launch_vec<IdxT, OP, VEC, false>(a, fused, grid, chunks, ue, tb, st);
+                         uint32_t *ue, uint64_t *tb, hipStream_t st, int qm) {
+    if constexpr (OP == Op::Dequant) {
+        switch (qm) {
+        case 0: return launch_vec<IdxT, OP, VEC, false, 0>(a, fused, grid, chunks, ue, tb, st);
+        case 1: return launch_vec<IdxT, OP, VEC, false, 1>(a, fused, grid, chunks, ue, tb, st);
+        case 2: return launch_vec<IdxT, OP, VEC, false, 2>(a, fused, grid, chunks, ue, tb, st);
+        case 3: return launch_vec<IdxT, OP, VEC, false, 3>(a, fused, grid, chunks, ue, tb, st);
+        case 4: return launch_vec<IdxT, OP, VEC, false, 4>(a, fused, grid, chunks, ue, tb, st);
+        case 5: return launch_vec<IdxT, OP, VEC, false, 5>(a, fused, grid, chunks, ue, tb, st);
+        default: return launch_vec<IdxT, OP, VEC, false>(a, fused, grid, chunks, ue, tb, st);
+        }
     } else {
-        if (OP == Op::Scatter && ntl)
+        if (ntl)
             return launch_vec<IdxT, OP, VEC, true>(a, fused, grid, chunks, ue, tb, st);
         return launch_vec<IdxT, OP, VEC, false>(a, fused, grid, chunks, ue, tb, st);
     }
@@ -681,35 +940,35 @@ hipError_t launch_policy(const Args &a, bool ntl, bool fused, dim3 grid, uint32_
 
 template <typename IdxT, Op OP>
 hipError_t launch_op(const Args &a, uint32_t vec, bool ntl, bool fused, dim3 grid,
-                     uint32_t chunks, uint32_t *ue, uint64_t *tb, hipStream_t st) {
+                     uint32_t chunks, uint32_t *ue, uint64_t *tb, hipStream_t st, int qm) {
     if constexpr (OP == Op::Dequant) {
         switch (vec) {
-        case 8: return launch_policy<IdxT, OP, 8>(a, ntl, fused, grid, chunks, ue, tb, st);
-        case 4: return launch_policy<IdxT, OP, 4>(a, ntl, fused, grid, chunks, ue, tb, st);
-        case 2: return launch_policy<IdxT, OP, 2>(a, ntl, fused, grid, chunks, ue, tb, st);
-        default: return launch_policy<IdxT, OP, 1>(a, ntl, fused, grid, chunks, ue, tb, st);
+        case 8: return launch_policy<IdxT, OP, 8>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
+        case 4: return launch_policy<IdxT, OP, 4>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
+        case 2: return launch_policy<IdxT, OP, 2>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
+        default: return launch_policy<IdxT, OP, 1>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
         }
     } else {
         switch (vec) {
-        case 16: return launch_policy<IdxT, OP, 16>(a, ntl, fused, grid, chunks, ue, tb, st);
-        case 8: return launch_policy<IdxT, OP, 8>(a, ntl, fused, grid, chunks, ue, tb, st);
-        case 4: return launch_policy<IdxT, OP, 4>(a, ntl, fused, grid, chunks, ue, tb, st);
-        case 2: return launch_policy<IdxT, OP, 2>(a, ntl, fused, grid, chunks, ue, tb, st);
-        default: return launch_policy<IdxT, OP, 1>(a, ntl, fused, grid, chunks, ue, tb, st);
+        case 16: return launch_policy<IdxT, OP, 16>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
+        case 8: return launch_policy<IdxT, OP, 8>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
+        case 4: return launch_policy<IdxT, OP, 4>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
+        case 2: return launch_policy<IdxT, OP, 2>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
+        default: return launch_policy<IdxT, OP, 1>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
         }
     }
 }
 
 template <typename IdxT>
 hipError_t launch_idx(const Args &a, Op op, uint32_t vec, bool ntl, bool fused, dim3 grid,
-                      uint32_t chunks, uint32_t *ue, uint64_t *tb, hipStream_t st) {
+                      uint32_t chunks, uint32_t *ue, uint64_t *tb, hipStream_t st, int qm) {
     switch (op) {
     case Op::Gather:
-        return launch_op<IdxT, Op::Gather>(a, vec, ntl, fused, grid, chunks, ue, tb, st);
+        return launch_op<IdxT, Op::Gather>(a, vec, ntl, fused, grid, chunks, ue, tb, st, -1);
     case Op::Scatter:
-        return launch_op<IdxT, Op::Scatter>(a, vec, ntl, fused, grid, chunks, ue, tb, st);
+        return launch_op<IdxT, Op::Scatter>(a, vec, ntl, fused, grid, chunks, ue, tb, st, -1);
     default:
-        return launch_op<IdxT, Op::Dequant>(a, vec, ntl, fused, grid, chunks, ue, tb, st);
+        return launch_op<IdxT, Op::Dequant>(a, vec, ntl, fused, grid, chunks, ue, tb, st, qm);
     }
 }
 
@@ -752,6 +1011,15 @@ hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
     if (job.op == Op::Dequant)
         a.vecs_per_row = (uint32_t)(job.row_bytes / job.vec_bytes);
     a.div_vpr = make_div(a.vecs_per_row ? a.vecs_per_row : 1);
+    a.quant_unsigned = job.quant_unsigned ? 1u : 0u;
+    a.quant_channels = job.quant_channels;
+    int qm = job.quant_ext ? (int)job.quant_mode : -1;
+    if (qm >= 2 && job.quant_channels > kQuantLdsMax)
+        qm += 2;  // table too large for LDS: read it from global memory
+    a.quant_scales = job.quant_scales;
+    a.zero_points = job.zero_points;
+    a.head_dim = job.head_dim ? job.head_dim : 1;
+    a.div_hd = make_div(a.head_dim);
     a.div_rpc = make_div(job.rows_per_unit);
     a.div_page = make_div(job.page_size);
     a.div_upp = make_div(a.units_per_page);
@@ -783,9 +1051,9 @@ hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
         const dim3 g(grid, n);
         const hipError_t e =
             job.idx64 ? launch_idx<uint64_t>(a, job.op, job.vec_bytes, job.load_nt, fused, g, chunks,
-                                             ue, tb, stream)
+                                             ue, tb, stream, qm)
                       : launch_idx<uint32_t>(a, job.op, job.vec_bytes, job.load_nt, fused, g, chunks,
-                                             ue, tb, stream);
+                                             ue, tb, stream, qm);
         if (e != hipSuccess)
             return e;
     }

@@ -57,6 +57,8 @@ typedef enum hp_status {
                                  Alignment) or other buffer not element aligned */
     HP_ERR_WORKSPACE = 8,     /* workspace NULL or smaller than hp_workspace_bytes */
     HP_ERR_SHARDED = 9,       /* a shard descriptor is attached ([Hurray] Sharding) */
+    HP_ERR_QUANT = 10,        /* quantization scheme a block-paged reader must reject
+                                 ([Hurray] Per-scheme composition) */
     HP_ERR_SEQPTR_FIRST = 16, /* seq_ptr[0] != 0                     (invariant 1) */
     HP_ERR_SEQPTR_LAST = 17,  /* seq_ptr[num_seqs] != num_block_entries (invariant 1) */
     HP_ERR_SEQPTR_ORDER = 18, /* seq_ptr[s] > seq_ptr[s+1]           (invariant 2) */
@@ -188,6 +190,40 @@ hp_status hp_scatter(const hp_desc *desc, const void *src, const void *seq_start
 hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype,
                             void *workspace, size_t workspace_bytes, uint32_t flags,
                             void *stream);
+
+/* ---- Dequant-gather under any quantization scheme -------------------------
+ *
+ * [Hurray] Quantization Compatibility, Per-scheme composition. Schemes, by the
+ * spec's scheme tags, and where the parameter of element (t, h, d) of
+ * sequence s lives:
+ *   HP_QUANT_PER_TENSOR (0x01)        scales[0]
+ *   HP_QUANT_PER_CHANNEL (0x02)       axis 1: scales[h] (num_heads entries);
+ *                                     axis 2: scales[d] (head_dim entries);
+ *                                     axis 0 (the paged axis) is rejected
+ *   HP_QUANT_PER_BLOCK_AFFINE (0x03)  axis 0 and block_size == page_size only:
+ *                                     scales[phys_page*page_size + t % page_size]
+ * and likewise zero_points (NULL: symmetric). The pool is int8 (HP_DTYPE_I8)
+ * or uint8 (HP_DTYPE_U8); zero points have the pool's element type. Each
+ * output element is
+ *   bf16_rne( fp32(q - zp) * scale )
+ * with q - zp exact in integers and one IEEE binary32 multiply (the formulas
+ * of the scheme document the spec defers to are not given; this affine form
+ * with the symmetric case zp = 0 is the reading used). A rejected scheme
+ * returns HP_ERR_QUANT. desc->scales is not used. scales and zero_points are
+ * DEVICE buffers, 64-byte aligned. Other arguments as hp_gather_dequant. */
+enum { HP_QUANT_PER_TENSOR = 0x01, HP_QUANT_PER_CHANNEL = 0x02, HP_QUANT_PER_BLOCK_AFFINE = 0x03 };
+
+typedef struct hp_quant {
+    uint32_t scheme;          /* HP_QUANT_* */
+    uint32_t axis;            /* 1 or 2 for per-channel; 0 for per-block-affine */
+    uint64_t block_size;      /* per-block-affine: must equal page_size */
+    const float *scales;      /* device; count as listed above */
+    const void *zero_points;  /* device, or NULL for a symmetric scheme */
+} hp_quant;
+
+hp_status hp_gather_dequant_q(const hp_desc *desc, const hp_quant *quant, void *out,
+                              uint32_t out_dtype, void *workspace, size_t workspace_bytes,
+                              uint32_t flags, void *stream);
 
 /* ---- Batched moves over pools that share one block table ------------------
  *

@@ -74,6 +74,12 @@ def _load():
     lib.oracle_gather_dequant_rows.restype = _u64
     lib.oracle_gather_dequant_rows.argtypes = [_vp, _vp, _u64, _u64, _u64, _vp, _vp,
                                                _vp, _u64, _vp, _u64, _vp]
+    lib.oracle_quant_accepts.restype = ctypes.c_int
+    lib.oracle_quant_accepts.argtypes = [ctypes.c_uint32, ctypes.c_uint32, _u64, _u64]
+    lib.oracle_gather_dequant_scheme.restype = None
+    lib.oracle_gather_dequant_scheme.argtypes = [_vp, ctypes.c_int, ctypes.c_uint32,
+                                                 ctypes.c_uint32, _vp, _vp, _u64, _u64, _u64,
+                                                 _vp, _vp, _vp, _u64, _vp]
     lib.oracle_copy_pages.restype = None
     lib.oracle_copy_pages.argtypes = [_vp, _u64, _u64, _u64, _u64, _vp, _vp, _vp, _u64]
     lib.oracle_payload.restype = ctypes.c_int
@@ -214,6 +220,34 @@ def gather_dequant_rows(pool, scales, rows, *, page_size, num_heads, head_dim,
                                              _ptr(sl), len(sl), _ptr(rw), len(rw),
                                              _ptr(out))
     assert missing == 0
+    return out
+
+
+SCHEMES = {"per_tensor": 0x01, "per_channel": 0x02, "per_block_affine": 0x03}
+
+
+def quant_accepts(scheme, axis, block_size, page_size):
+    """[Hurray] Per-scheme composition: may a reader accept this scheme?"""
+    return bool(_load().oracle_quant_accepts(SCHEMES[scheme], axis, block_size, page_size))
+
+
+def gather_dequant_scheme(pool, scheme, axis, scales, zero_points=None, *, page_size,
+                          num_heads, head_dim, block_table, seq_ptr, seq_lens):
+    """bf16 bits [T, H, D] of bf16(fp32(q - zp) * scale) under `scheme`; the
+    pool is int8 or uint8 (its numpy dtype decides), zero points likewise."""
+    lib = _load()
+    pool = np.ascontiguousarray(pool)
+    assert pool.dtype in (np.int8, np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    zp = None if zero_points is None else np.ascontiguousarray(zero_points, dtype=pool.dtype)
+    bt, sp, sl = _idx(block_table), _idx(seq_ptr), _idx(seq_lens)
+    total = int(sl.sum()) if len(sl) else 0
+    out = np.empty((total, num_heads, head_dim), dtype=np.uint16)
+    lib.oracle_gather_dequant_scheme(_ptr(pool), int(pool.dtype == np.int8), SCHEMES[scheme],
+                                     axis, _ptr(scales), _ptr(zp), page_size, num_heads,
+                                     head_dim, _ptr(bt) if len(bt) else None, _ptr(sp),
+                                     _ptr(sl) if len(sl) else None, len(sl),
+                                     _ptr(out) if out.size else None)
     return out
 
 

@@ -333,6 +333,60 @@ uint64_t oracle_gather_dequant_rows(const int8_t *page_pool, const float *scales
     return missing;
 }
 
+int oracle_quant_accepts(uint32_t scheme, uint32_t axis, uint64_t block_size,
+                         uint64_t page_size)
+{
+    if (scheme == ORACLE_PER_TENSOR)
+        return 1;
+    if (scheme == ORACLE_PER_CHANNEL)
+        return axis == 1 || axis == 2;
+    if (scheme == ORACLE_PER_BLOCK_AFFINE)
+        return axis == 0 && block_size == page_size;
+    return 0;
+}
+
+void oracle_gather_dequant_scheme(const void *page_pool, int q_signed, uint32_t scheme,
+                                  uint32_t axis, const float *scales, const void *zero_points,
+                                  uint64_t page_size, uint64_t num_heads, uint64_t head_dim,
+                                  const uint64_t *block_table, const uint64_t *seq_ptr,
+                                  const uint64_t *seq_lens, uint64_t num_seqs, uint16_t *out)
+{
+    const int8_t *qs = (const int8_t *)page_pool;
+    const uint8_t *qu = (const uint8_t *)page_pool;
+    const int8_t *zs = (const int8_t *)zero_points;
+    const uint8_t *zu = (const uint8_t *)zero_points;
+    uint64_t row = 0;
+    uint64_t s, t, h, d;
+
+    for (s = 0; s < num_seqs; s++) {
+        for (t = 0; t < seq_lens[s]; t++) {
+            uint64_t phys = block_table[seq_ptr[s] + t / page_size];
+            for (h = 0; h < num_heads; h++) {
+                for (d = 0; d < head_dim; d++) {
+                    uint64_t src = pool_index(block_table, seq_ptr, s, t, h, d, page_size,
+                                              num_heads, head_dim);
+                    /* parameter position of this element under the scheme */
+                    uint64_t k = 0;
+                    int32_t q, zp = 0;
+                    double exact;
+                    if (scheme == ORACLE_PER_CHANNEL)
+                        k = axis == 1 ? h : d;
+                    else if (scheme == ORACLE_PER_BLOCK_AFFINE)
+                        k = phys * page_size + t % page_size;
+                    q = q_signed ? (int32_t)qs[src] : (int32_t)qu[src];
+                    if (zero_points)
+                        zp = q_signed ? (int32_t)zs[k] : (int32_t)zu[k];
+                    /* q - zp is an exact small integer; times the scale exactly
+                     * in binary64, then one rounding to binary32 and one to bf16 */
+                    exact = (double)(q - zp) * (double)scales[k];
+                    out[(row * num_heads + h) * head_dim + d] = oracle_bf16_rne((float)exact);
+                }
+            }
+            row++;
+        }
+    }
+}
+
 /* Copy-on-write page copy: page by page, slot by slot, element by element,
  * in the order the copies are listed. */
 void oracle_copy_pages(void *page_pool, uint64_t elem_bytes, uint64_t page_size,

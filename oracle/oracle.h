@@ -116,6 +116,38 @@ uint64_t oracle_gather_dequant_rows(const int8_t *page_pool, const float *scales
                                     uint64_t num_seqs, const uint64_t *rows,
                                     uint64_t rows_count, uint16_t *out);
 
+/* Quantization schemes ([Hurray] Quantization Compatibility, Per-scheme
+ * composition; the scheme tags are the spec's):
+ *   0x01 per-tensor        one scale (and zero point) for the whole tensor
+ *   0x02 per-channel       axis 1: one per head; axis 2: one per head_dim index
+ *   0x03 per-block-affine  axis 0 with block_size == page_size: one per page
+ *                          slot, scales[phys * page_size + offset] */
+enum oracle_scheme {
+    ORACLE_PER_TENSOR = 0x01,
+    ORACLE_PER_CHANNEL = 0x02,
+    ORACLE_PER_BLOCK_AFFINE = 0x03
+};
+
+/* Whether a reader accepts the scheme on a block-paged tensor ([Hurray]
+ * Per-scheme composition: per-block-affine needs axis 0 and block_size ==
+ * page_size; per-channel composes on axis 1 or 2, axis 0 is forbidden).
+ * Returns 1 if accepted, 0 if it must be rejected. */
+int oracle_quant_accepts(uint32_t scheme, uint32_t axis, uint64_t block_size,
+                         uint64_t page_size);
+
+/* Dequant-gather under any accepted scheme: for every logical element,
+ *   out = bf16( fp32(q - zp) * scale )
+ * with q the pool element (int8 if q_signed, else uint8), zp the zero point
+ * of the same parameter position (0 when zero_points is NULL; same element
+ * type as the pool), q - zp exact in integers, one IEEE binary32 multiply and
+ * one round to nearest even into bf16 ([Hurray] Element Lookup: dequantize
+ * with the scale and zero point of the active scheme). */
+void oracle_gather_dequant_scheme(const void *page_pool, int q_signed, uint32_t scheme,
+                                  uint32_t axis, const float *scales, const void *zero_points,
+                                  uint64_t page_size, uint64_t num_heads, uint64_t head_dim,
+                                  const uint64_t *block_table, const uint64_t *seq_ptr,
+                                  const uint64_t *seq_lens, uint64_t num_seqs, uint16_t *out);
+
 /* Copy-on-write page copy ([Day51] "Copy-on-write for beam search and prefix
  * sharing": a shared block is copied before one request modifies it;
  * [Hurray] Per-page-slot parameters: a page carries its own scales). For

@@ -26,7 +26,7 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"hp_workspace_bytes", "hp_validate", "hp_gather", "hp_scatter",
                           "hp_gather_dequant", "hp_status_str", "hp_last_hip_error",
                           "hp_gather_batch", "hp_scatter_batch", "hp_gather_dequant_batch",
-                          "hp_copy_pages", "hp_copy_pages_batch"}
+                          "hp_copy_pages", "hp_copy_pages_batch", "hp_gather_dequant_q"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -134,6 +134,62 @@ def test_dequant_rejections():
     assert call(q, out=None) == S["HP_ERR_NULL"]
     assert call(q, out=OUT + 1) == S["HP_ERR_ALIGN"]
     assert call(q, out=ALIGNED + 0x500000) == S["HP_ERR_ARG"]          # overlaps scales
+
+
+def quant(scheme, axis=0, block_size=16, scales=ALIGNED + 0x500000, zero_points=None):
+    return hp.HpQuant(hp.QUANT_SCHEME[scheme] if isinstance(scheme, str) else scheme, axis,
+                      block_size, scales, zero_points)
+
+
+def dq_q(d, q, out=OUT, od=None, flags=0):
+    od = hp.DTYPE["bf16"] if od is None else od
+    return L.hp_gather_dequant_q(ctypes.byref(d) if d is not None else None,
+                                 ctypes.byref(q) if q is not None else None,
+                                 out, od, None, 0, flags, None)
+
+
+@pytest.mark.parametrize("scheme,axis,block,code", [
+    ("per_tensor", 0, 16, "HP_OK"),
+    ("per_tensor", 2, 7, "HP_OK"),                 # axis and block size are not used
+    ("per_channel", 1, 16, "HP_OK"),
+    ("per_channel", 2, 16, "HP_OK"),
+    ("per_channel", 0, 16, "HP_ERR_QUANT"),        # channel along the paged axis
+    ("per_channel", 3, 16, "HP_ERR_QUANT"),
+    ("per_block_affine", 0, 16, "HP_OK"),
+    ("per_block_affine", 0, 8, "HP_ERR_QUANT"),    # block must equal the page
+    ("per_block_affine", 0, 32, "HP_ERR_QUANT"),
+    ("per_block_affine", 1, 16, "HP_ERR_QUANT"),   # blocks not along the paged axis
+    (0x04, 0, 16, "HP_ERR_QUANT"),                 # unknown scheme tag
+    (0x00, 0, 16, "HP_ERR_QUANT"),
+])
+def test_quant_scheme_acceptance(scheme, axis, block, code):
+    """The composition rules; an accepted scheme with total_tokens == 0 returns
+    HP_OK before touching the device."""
+    d = desc(dtype=hp.DTYPE["i8"], total_tokens=0)
+    assert dq_q(d, quant(scheme, axis, block)) == S[code]
+    assert dq_q(desc(dtype=hp.DTYPE["u8"], total_tokens=0), quant(scheme, axis, block)) == S[code]
+
+
+def test_quant_rejections():
+    q8 = desc(dtype=hp.DTYPE["i8"])
+    pt = quant("per_tensor")
+    assert dq_q(None, pt) == S["HP_ERR_NULL"]
+    assert dq_q(q8, None) == S["HP_ERR_NULL"]
+    assert dq_q(desc(), pt) == S["HP_ERR_DTYPE"]                       # f16 pool
+    assert dq_q(q8, pt, od=hp.DTYPE["f32"]) == S["HP_ERR_DTYPE"]
+    assert dq_q(q8, quant("per_tensor", scales=None)) == S["HP_ERR_NULL"]
+    assert dq_q(q8, quant("per_tensor", scales=ALIGNED + 0x500004)) == S["HP_ERR_ALIGN"]
+    assert dq_q(q8, quant("per_tensor", zero_points=ALIGNED + 0x600001)) == S["HP_ERR_ALIGN"]
+    assert dq_q(q8, pt, out=None) == S["HP_ERR_NULL"]
+    assert dq_q(q8, pt, out=OUT + 1) == S["HP_ERR_ALIGN"]
+    assert dq_q(q8, pt, out=ALIGNED + 0x500000) == S["HP_ERR_ARG"]    # overlaps scales
+    assert dq_q(q8, quant("per_tensor", zero_points=OUT + 128)) == S["HP_ERR_ARG"]
+    assert dq_q(q8, pt, out=ALIGNED + 64) == S["HP_ERR_ARG"]          # overlaps the pool
+    assert dq_q(q8, pt, flags=hp.HP_FLAG_STREAM) == S["HP_ERR_ARG"]
+    assert dq_q(q8, pt, flags=hp.HP_FLAG_CHECKED) == S["HP_ERR_WORKSPACE"]
+    # the descriptor's own scales play no part
+    assert dq_q(desc(dtype=hp.DTYPE["i8"], scales=ALIGNED + 0x500004, total_tokens=0), pt) == \
+        S["HP_OK"]
 
 
 def test_workspace_bytes():

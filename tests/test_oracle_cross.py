@@ -188,3 +188,55 @@ def test_copy_pages_brute(seed):
                                    [int(x) for x in dst])
     assert got.tolist() == ref
     assert got_sc.tolist() == ref_sc
+
+
+QUANT_CASES = [("per_tensor", 0), ("per_channel", 1), ("per_channel", 2),
+               ("per_block_affine", 0)]
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("scheme,axis", QUANT_CASES)
+@pytest.mark.parametrize("signed", [True, False])
+@pytest.mark.parametrize("with_zp", [False, True])
+def test_dequant_schemes_match_library_arithmetic(seed, scheme, axis, signed, with_zp):
+    """bf16(fp32(q - zp) * scale) under each scheme equals torch CPU's
+    ((q - zp).float() * scale).to(bfloat16), with the scheme's parameter
+    broadcast over the logical tensor."""
+    w = workloads.random_small(6000 + seed, dtypes=("i8",))
+    rng = np.random.default_rng(seed)
+    N, P, H, D = w.num_pages, w.page_size, w.num_heads, w.head_dim
+    qdt = np.int8 if signed else np.uint8
+    lo, hi = (-128, 128) if signed else (0, 256)
+    pool = rng.integers(lo, hi, size=(N, P, H, D)).astype(qdt)
+    n = {"per_tensor": 1, "per_channel": H if axis == 1 else D, "per_block_affine": N * P}[scheme]
+    scales = rng.uniform(1e-3, 1e-1, n).astype(np.float32)
+    zp = rng.integers(lo, hi, n).astype(qdt) if with_zp else None
+    kw = dict(page_size=P, num_heads=H, head_dim=D, block_table=w.block_table,
+              seq_ptr=w.seq_ptr, seq_lens=w.seq_lens)
+    got = oracle.gather_dequant_scheme(pool, scheme, axis, scales, zp, **kw)
+    ids = torch.from_numpy(_slot_ids(w))
+    q = torch.from_numpy(pool.reshape(-1, H, D).astype(np.int32))[ids]
+    s = torch.from_numpy(scales)
+    z = torch.from_numpy(zp.astype(np.int32)) if with_zp else torch.zeros(n, dtype=torch.int32)
+    if scheme == "per_tensor":
+        sb, zb = s.view(1, 1, 1), z.view(1, 1, 1)
+    elif scheme == "per_channel" and axis == 1:
+        sb, zb = s.view(1, H, 1), z.view(1, H, 1)
+    elif scheme == "per_channel":
+        sb, zb = s.view(1, 1, D), z.view(1, 1, D)
+    else:
+        sb, zb = s[ids].view(-1, 1, 1), z[ids].view(-1, 1, 1)
+    ref = ((q - zb).float() * sb).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(got.view(np.int16), ref)
+
+
+def test_dequant_scheme_per_block_affine_is_the_per_slot_path():
+    """Per-block-affine on axis 0 with block_size == page_size coincides with
+    the per-page-slot parameters ([Hurray] Per-scheme composition)."""
+    w = workloads.random_small(6100, dtypes=("i8",))
+    pool = w.make_pool("cpu").numpy()
+    scales = w.make_scales("cpu").numpy()
+    kw = dict(page_size=w.page_size, num_heads=w.num_heads, head_dim=w.head_dim,
+              block_table=w.block_table, seq_ptr=w.seq_ptr, seq_lens=w.seq_lens)
+    assert np.array_equal(oracle.gather_dequant_scheme(pool, "per_block_affine", 0, scales, **kw),
+                          oracle.gather_dequant(pool, scales, **kw))

@@ -347,3 +347,19 @@ def test_day51_copy_on_write_keeps_the_other_request_intact():
     assert np.all(after[48] == 0x7777)                       # E's new token
     assert np.array_equal(pool3[1], pool[1])                 # the shared page untouched
     assert np.array_equal(pool3[4, 8], new_row[0])           # slot 24 mod 16 of the copy
+
+
+@pytest.mark.parametrize("scheme,axis,block,accept", [
+    ("per_tensor", 0, 0, True),          # composes normally
+    ("per_channel", 1, 0, True),         # num_heads axis
+    ("per_channel", 2, 0, True),         # head_dim axis
+    ("per_channel", 0, 0, False),        # paged axis: forbidden
+    ("per_block_affine", 0, 16, True),   # axis 0, block_size == page_size
+    ("per_block_affine", 0, 8, False),   # block_size != page_size: must reject
+    ("per_block_affine", 1, 16, False),  # axis != 0: must reject
+    ("per_block_affine", 2, 16, False),
+])
+def test_hurray_scheme_composition_rules(scheme, axis, block, accept):
+    """[Hurray] Per-scheme composition: which quantization schemes a reader
+    accepts on a block-paged tensor with page_size 16."""
+    assert oracle.quant_accepts(scheme, axis, block, 16) == accept
