@@ -47,12 +47,12 @@ CSRC = os.path.join(ROOT, "block_table_gather_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("hp_kernels.hip", "hp_api.cpp", "hp_internal.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "gather_copy_kernel_decode_traffic.json")
-GATHER_KERNEL = "copy_kernel<unsigned int, (hp::Op)0, 16, true, true>"
+GATHER_KERNEL = "copy_kernel<unsigned int, (hp::Op)0, 16, true, true, -1>"
 KERNEL_LABELS = {
-    "copy_kernel<unsigned int, (hp::Op)0, 16, true, true>": "gather (u32, 16 B vectors, fused, streaming loads)",
-    "copy_kernel<unsigned int, (hp::Op)1, 16, true, true>": "scatter (u32, 16 B vectors, fused, streamed source)",
-    "copy_kernel<unsigned int, (hp::Op)1, 16, true, false>": "scatter (u32, 16 B vectors, fused)",
-    "copy_kernel<unsigned int, (hp::Op)2, 8, true, false>": "dequant-gather (u32, 8 B int8 vectors, fused)",
+    "copy_kernel<unsigned int, (hp::Op)0, 16, true, true, -1>": "gather (u32, 16 B vectors, fused, streaming loads)",
+    "copy_kernel<unsigned int, (hp::Op)1, 16, true, true, -1>": "scatter (u32, 16 B vectors, fused, streamed source)",
+    "copy_kernel<unsigned int, (hp::Op)1, 16, true, false, -1>": "scatter (u32, 16 B vectors, fused)",
+    "copy_kernel<unsigned int, (hp::Op)2, 8, true, false, -1>": "dequant-gather (u32, 8 B int8 vectors, fused)",
     "validate_kernel<unsigned int>": "validator (u32)",
     "validate_init_kernel": "validator init",
 }
