@@ -13,7 +13,8 @@ and calls the plain C element loops of ``oracle.c``, which cite the pages:
 * [Day51]  "Visualize PagedAttention block layout"
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
-``tests/test_oracle_pins.py`` and ``tests/test_oracle_cross.py``.
+``tests/test_oracle_pins.py``, ``tests/test_oracle_cross.py`` and
+``tests/test_oracle_attention.py``.
 """
 import ctypes
 import os
@@ -84,6 +85,11 @@ def _load():
     lib.oracle_copy_pages.argtypes = [_vp, _u64, _u64, _u64, _u64, _vp, _vp, _vp, _u64]
     lib.oracle_payload.restype = ctypes.c_int
     lib.oracle_payload.argtypes = [_u64] * 7 + [_vp]
+    lib.oracle_decode.restype = None
+    lib.oracle_decode.argtypes = [ctypes.c_uint32, _vp, _u64, _vp]
+    lib.oracle_paged_attention.restype = ctypes.c_int
+    lib.oracle_paged_attention.argtypes = [_vp, _vp, _vp, ctypes.c_uint32, _u64, _u64, _u64,
+                                           _u64, ctypes.c_double, _vp, _vp, _vp, _u64, _vp]
     _lib = lib
     return lib
 
@@ -263,6 +269,45 @@ def copy_pages(pool, src_pages, dst_pages, *, page_size, num_heads, head_dim, sc
                           _ptr(src) if len(src) else None, _ptr(dst) if len(dst) else None,
                           len(src))
     return result, sc
+
+
+# Element types of the attention oracle (oracle.h, enum oracle_float_type).
+FLOAT_TYPES = {"f16": 3, "bf16": 4, "f32": 5}
+
+
+def decode(bits, elem_type):
+    """Exact float64 values of stored f16 / bf16 (uint16 bit patterns) or f32
+    (uint32 bit patterns) elements."""
+    bits = np.ascontiguousarray(bits)
+    out = np.empty(bits.shape, dtype=np.float64)
+    if bits.size:
+        _load().oracle_decode(FLOAT_TYPES[elem_type], _ptr(bits), bits.size, _ptr(out))
+    return out
+
+
+def paged_attention(q, k_pool, v_pool, elem_type, *, page_size, num_kv_heads, head_dim,
+                    block_table, seq_ptr, seq_lens, scale):
+    """Decode attention over the block-paged K/V cache, float64
+    [num_seqs, num_q_heads, head_dim]. q: [num_seqs, num_q_heads, head_dim] and
+    the pools [num_pages, page_size, num_kv_heads, head_dim], all as bit
+    patterns (uint16 for f16/bf16, uint32 for f32) of `elem_type`."""
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    k_pool, v_pool = np.ascontiguousarray(k_pool), np.ascontiguousarray(v_pool)
+    assert q.ndim == 3 and q.shape[2] == head_dim
+    S, Hq = q.shape[0], q.shape[1]
+    bt, sp, sl = _idx(block_table), _idx(seq_ptr), _idx(seq_lens)
+    assert len(sp) == S + 1 and len(sl) == S
+    out = np.empty((S, Hq, head_dim), dtype=np.float64)
+    if S == 0:
+        return out
+    rc = lib.oracle_paged_attention(_ptr(q), _ptr(k_pool), _ptr(v_pool), FLOAT_TYPES[elem_type],
+                                    page_size, num_kv_heads, head_dim, Hq, float(scale),
+                                    _ptr(bt) if len(bt) else None, _ptr(sp), _ptr(sl), S,
+                                    _ptr(out))
+    if rc != 0:
+        raise ValueError("num_q_heads must be a positive multiple of num_kv_heads")
+    return out
 
 
 PAYLOAD_FIELDS = ("reserved_pages", "active_pages", "allocated_slots", "live_slots",

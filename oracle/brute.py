@@ -7,6 +7,7 @@ expands each sequence's block-table slice into the list of (page, slot) pairs
 the slice covers, in order, and reads the live prefix of that list. The pool
 is treated as a nested Python list [num_pages][page_size][num_heads][head_dim].
 """
+import math
 
 
 def slot_list(block_table, seq_ptr, s, page_size):
@@ -86,3 +87,29 @@ def copy_pages(pool4, scales, src_pages, dst_pages):
         if sc is not None:
             sc[dst * page_size:(dst + 1) * page_size] = sc[src * page_size:(src + 1) * page_size]
     return pool, sc
+
+
+def attention(q, k_pool4, v_pool4, block_table, seq_ptr, seq_lens, scale):
+    """Decode attention with plain Python floats: q is [S][Hq][D], the pools
+    [N][P][Hkv][D]. Query head hq reads kv head hq // (Hq // Hkv); scores
+    are scale * q.k, weights exp(score - max), output the weighted mean of
+    the values; a sequence without tokens gives zeros."""
+    page_size = len(k_pool4[0])
+    out = []
+    for s in range(len(seq_lens)):
+        slots = slot_list(block_table, seq_ptr, s, page_size)[: seq_lens[s]]
+        heads = []
+        for hq, qv in enumerate(q[s]):
+            hkv = hq // (len(q[s]) // len(k_pool4[0][0]))
+            if not slots:
+                heads.append([0.0] * len(qv))
+                continue
+            scores = [scale * math.fsum(a * b for a, b in zip(qv, k_pool4[p][i][hkv]))
+                      for p, i in slots]
+            top = max(scores)
+            w = [math.exp(x - top) for x in scores]
+            total = math.fsum(w)
+            heads.append([math.fsum(wt * v_pool4[p][i][hkv][d] for wt, (p, i) in zip(w, slots))
+                          / total for d in range(len(qv))])
+        out.append(heads)
+    return out

@@ -12,13 +12,13 @@ SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 # No fast-math, no FMA contraction: the dequantisation step must be the exact
-# product rounded once to binary32.
+# product rounded once to binary32, and the attention sums are plain binary64.
 CFLAGS = ["-O2", "-std=gnu11", "-fPIC", "-shared", "-fno-fast-math",
           "-ffp-contract=off", "-Wall", "-Wextra", "-Werror"]
 
 
 def build(verbose=False):
-    cmd = ["gcc", *CFLAGS, "-o", LIB + ".tmp", SRC]
+    cmd = ["gcc", *CFLAGS, "-o", LIB + ".tmp", SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

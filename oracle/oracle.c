@@ -18,6 +18,8 @@
  */
 #include "oracle.h"
 
+#include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* [Hurray] Element Lookup:
@@ -413,6 +415,119 @@ void oracle_copy_pages(void *page_pool, uint64_t elem_bytes, uint64_t page_size,
                     scales[src_pages[i] * page_size + slot];
         }
     }
+}
+
+/* IEEE 754 binary16: sign bit, 5-bit exponent biased by 15, 10-bit
+ * fraction. Exponent 0 holds zero and the subnormals f * 2^-24; exponent 31
+ * holds the infinities (f = 0) and NaNs. Otherwise the value is
+ * (1024 + f) * 2^(e - 25). */
+static double half_value(uint16_t b)
+{
+    int e = (b >> 10) & 31;
+    int f = b & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return (b >> 15) ? -v : v;
+}
+
+/* bfloat16 is the upper 16 bits of a binary32. */
+static double bf16_value(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double element_value(uint32_t elem_type, const void *base, uint64_t i)
+{
+    if (elem_type == ORACLE_F32) {
+        float f;
+        memcpy(&f, (const unsigned char *)base + 4 * i, sizeof f);
+        return (double)f;
+    }
+    uint16_t b;
+    memcpy(&b, (const unsigned char *)base + 2 * i, sizeof b);
+    return elem_type == ORACLE_F16 ? half_value(b) : bf16_value(b);
+}
+
+void oracle_decode(uint32_t elem_type, const void *src, uint64_t n, double *out)
+{
+    uint64_t i;
+    for (i = 0; i < n; i++)
+        out[i] = element_value(elem_type, src, i);
+}
+
+/* Softmax attention of one query row over a sequence's cached tokens, the
+ * keys and values found through the block table one token at a time. */
+int oracle_paged_attention(const void *q, const void *k_pool, const void *v_pool,
+                           uint32_t elem_type, uint64_t page_size, uint64_t num_kv_heads,
+                           uint64_t head_dim, uint64_t num_q_heads, double scale,
+                           const uint64_t *block_table, const uint64_t *seq_ptr,
+                           const uint64_t *seq_lens, uint64_t num_seqs, double *out)
+{
+    uint64_t s, hq, t, d, group, max_len = 0;
+    double *x;
+
+    if (!page_size || !num_kv_heads || !head_dim || !num_q_heads ||
+        num_q_heads % num_kv_heads)
+        return -1;
+    group = num_q_heads / num_kv_heads;
+    for (s = 0; s < num_seqs; s++)
+        if (seq_lens[s] > max_len)
+            max_len = seq_lens[s];
+    x = (double *)malloc((max_len ? max_len : 1) * sizeof(double));
+    if (!x)
+        return -1;
+
+    for (s = 0; s < num_seqs; s++) {
+        uint64_t L = seq_lens[s];
+        for (hq = 0; hq < num_q_heads; hq++) {
+            uint64_t hkv = hq / group;
+            double *o = out + (s * num_q_heads + hq) * head_dim;
+            double m = -INFINITY, denom = 0.0;
+            if (L == 0) {
+                for (d = 0; d < head_dim; d++)
+                    o[d] = 0.0;
+                continue;
+            }
+            /* scores x_t = scale * q . k_t */
+            for (t = 0; t < L; t++) {
+                double dot = 0.0;
+                for (d = 0; d < head_dim; d++) {
+                    double qv = element_value(elem_type, q,
+                                              (s * num_q_heads + hq) * head_dim + d);
+                    double kv = element_value(elem_type, k_pool,
+                                              pool_index(block_table, seq_ptr, s, t, hkv, d,
+                                                         page_size, num_kv_heads, head_dim));
+                    dot += qv * kv;
+                }
+                x[t] = scale * dot;
+                if (x[t] > m)
+                    m = x[t];
+            }
+            /* weights relative to the largest score, then the weighted mean */
+            for (t = 0; t < L; t++) {
+                x[t] = exp(x[t] - m);
+                denom += x[t];
+            }
+            for (d = 0; d < head_dim; d++) {
+                double num = 0.0;
+                for (t = 0; t < L; t++)
+                    num += x[t] * element_value(elem_type, v_pool,
+                                                pool_index(block_table, seq_ptr, s, t, hkv, d,
+                                                           page_size, num_kv_heads, head_dim));
+                o[d] = num / denom;
+            }
+        }
+    }
+    free(x);
+    return 0;
 }
 
 /* [Rust20] "Count live rows and two kinds of unused payload": with

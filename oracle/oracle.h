@@ -159,6 +159,39 @@ void oracle_copy_pages(void *page_pool, uint64_t elem_bytes, uint64_t page_size,
                        const uint64_t *src_pages, const uint64_t *dst_pages,
                        uint64_t count);
 
+/* Element types of the attention oracle's inputs (IEEE binary16, bfloat16 =
+ * the high half of a binary32, binary32). */
+enum oracle_float_type {
+    ORACLE_F16 = 3,
+    ORACLE_BF16 = 4,
+    ORACLE_F32 = 5
+};
+
+/* Exact binary64 values of n stored elements of the given type (NaN stays
+ * NaN, infinities and subnormals are kept). */
+void oracle_decode(uint32_t elem_type, const void *src, uint64_t n, double *out);
+
+/* Decode attention over a block-paged K/V cache ([Day51] "How the attention
+ * kernel uses the block table": for each head the kernel walks the sequence's
+ * blocks through the table; [Rust20] "Keep token order across cache pages":
+ * paging changes only where rows are stored, not the dot products or the
+ * weighted sums). For sequence s and query head hq, with kv head
+ * hkv = hq / (num_q_heads / num_kv_heads) and the L = seq_lens[s] cached
+ * tokens t read through the table ([Hurray] Element Lookup):
+ *   x_t = scale * sum_d q[s][hq][d] * K[t][hkv][d]
+ *   w_t = exp(x_t - max_t x_t)
+ *   out[s][hq][d] = sum_t w_t * V[t][hkv][d] / sum_t w_t
+ * all in binary64 from the exact input values. A sequence with no tokens
+ * gives zeros. q is [num_seqs, num_q_heads, head_dim]; k_pool and v_pool are
+ * [num_pages, page_size, num_kv_heads, head_dim], all of elem_type; out is
+ * [num_seqs, num_q_heads, head_dim]. Returns 0, or -1 when num_q_heads is not
+ * a multiple of num_kv_heads or a size is zero. */
+int oracle_paged_attention(const void *q, const void *k_pool, const void *v_pool,
+                           uint32_t elem_type, uint64_t page_size, uint64_t num_kv_heads,
+                           uint64_t head_dim, uint64_t num_q_heads, double scale,
+                           const uint64_t *block_table, const uint64_t *seq_ptr,
+                           const uint64_t *seq_lens, uint64_t num_seqs, double *out);
+
 /* [Rust20] "Count live rows and two kinds of unused payload": buffer-length
  * payload of one layer's K and V arrays. out[] receives, in order:
  *  0 reserved pages      1 active pages
