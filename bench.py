@@ -44,7 +44,8 @@ sys.path.insert(0, ROOT)
 METRIC = "achieved HBM GB/s (and % of peak) for paged gather/scatter, tokens/s"
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "block_table_gather_amd", "csrc")
-KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("hp_kernels.hip", "hp_api.cpp", "hp_internal.h")]
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("hp_kernels.hip", "hp_api.cpp", "hp_internal.h",
+                                                  "hp_device.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "gather_copy_kernel_decode_traffic.json")
 GATHER_KERNEL = "copy_kernel<unsigned int, (hp::Op)0, 16, true, true, -1>"
@@ -253,6 +254,64 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir):
 
 
 # ---- batched moves (optional) ----------------------------------------------------
+
+def attention_extras(hp, torch, np, dev, stream, reps):
+    """Decode attention reading K and V through the block table: the decode
+    batch (64 sequences, 32 kv heads x 128 fp16, one query head per kv head,
+    streaming loads) and the prefix-sharing batch (256 sequences, 8 kv heads x
+    128 bf16, 32 query heads, cached loads since 64 prefix pages are read by
+    every sequence). Algorithmic bytes: every live K and V row read once (the
+    prefix pages once per sequence that uses them, as logical bytes), the
+    queries read and the fp32 output written."""
+    import workloads
+    res = {}
+    for name, w, group, streaming in (("decode_mha_f16", workloads.decode(), 1, True),
+                                      ("prefix_gqa4_bf16", workloads.prefix(), 4, False)):
+        k_pool = w.make_pool(dev)
+        v_pool = dataclasses.replace(w, seed=w.seed * 7 + 3).make_pool(dev)
+
+        def idx(a):
+            return torch.from_numpy(np.asarray(a, dtype=np.uint32).view(np.int32).copy()).to(dev)
+
+        desc = hp.Descriptor(k_pool, idx(w.block_table), idx(w.seq_ptr), idx(w.seq_lens))
+        T, S, H, D = w.total_tokens, w.num_seqs, w.num_heads, w.head_dim
+        Hq = H * group
+        g = torch.Generator(device=dev).manual_seed(9)
+        q = torch.randn((S, Hq, D), generator=g, device=dev).to(k_pool.dtype)
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+        ws = torch.empty(hp.attention_workspace_bytes(desc, T, Hq), dtype=torch.uint8, device=dev)
+        L = hp.lib()
+        pd = desc.with_tokens(T)
+        args = (pd, v_pool.data_ptr(), q.data_ptr(), Hq, ctypes.c_float(1.0 / D ** 0.5),
+                out.data_ptr(), hp.DTYPE["f32"], ws.data_ptr(), ws.numel(),
+                hp.HP_FLAG_STREAM if streaming else 0, stream.cuda_stream)
+
+        def call():
+            if L.hp_paged_attention(*args) != 0:
+                raise SystemExit("hp_paged_attention failed")
+
+        call()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            call()
+        b.record(stream)
+        b.synchronize()
+        ms = a.elapsed_time(b) / reps
+        nbytes = 2 * T * H * D * 2 + S * Hq * D * 2 + S * Hq * D * 4
+        unique = (len(np.unique(w.block_table)) * w.page_size * H * D * 2 * 2 if not streaming
+                  else None)
+        res[name] = {"sequences": S, "tokens": T, "kv_heads": H, "q_heads": Hq, "head_dim": D,
+                     "algorithmic_bytes": nbytes, "launch_us": round(ms * 1e3, 1),
+                     "gb_per_s": round(nbytes / (ms / 1e3) / 1e9, 1),
+                     "tokens_per_s": round(T / (ms / 1e3), 1)}
+        if unique is not None:
+            res[name]["unique_kv_bytes"] = unique
+        del k_pool, v_pool, q, out, ws
+        torch.cuda.empty_cache()
+    return res
+
 
 def batched_append(hp, torch, np, dev, stream, reps):
     """One decode step's KV append for a 32-layer model: each of the decode
@@ -559,6 +618,7 @@ def main():
                              "gb_per_s": round(qb / (t_q / 1e3) / 1e9, 1)}
         del qout
         result["extras"] = {
+            "attention": attention_extras(hp, torch, np, dev, stream, args.kernel_reps),
             "dequant_schemes": schemes,
             "batched_append": batched_append(hp, torch, np, dev, stream, args.kernel_reps),
             "copy_pages": {"workload": "1,024 pages of the decode pool (16 x 32 x 128 fp16 = "

@@ -22,7 +22,7 @@ import os
 import torch  # noqa: F401,E402
 
 __all__ = ["Descriptor", "HpError", "gather", "scatter", "gather_dequant", "validate",
-           "gather_dequant_q", "QUANT_SCHEME",
+           "gather_dequant_q", "QUANT_SCHEME", "paged_attention", "attention_workspace_bytes",
            "gather_batch", "scatter_batch", "gather_dequant_batch", "copy_pages",
            "copy_pages_batch", "workspace_bytes",
            "status_str", "last_hip_error", "lib", "LIB_PATH", "STATUS"]
@@ -114,6 +114,11 @@ _lib.hp_gather_dequant.argtypes = [_P, _vp, _u32, _vp, _sz, _u32, _vp]
 _lib.hp_gather_dequant_q.restype = ctypes.c_int
 _lib.hp_gather_dequant_q.argtypes = [_P, ctypes.POINTER(HpQuant), _vp, _u32, _vp, _sz, _u32,
                                      _vp]
+_lib.hp_paged_attention.restype = ctypes.c_int
+_lib.hp_paged_attention.argtypes = [_P, _vp, _vp, _u32, ctypes.c_float, _vp, _u32, _vp, _sz,
+                                    _u32, _vp]
+_lib.hp_attention_workspace_bytes.restype = _sz
+_lib.hp_attention_workspace_bytes.argtypes = [_P, _u32]
 _lib.hp_status_str.restype = ctypes.c_char_p
 _lib.hp_status_str.argtypes = [ctypes.c_int]
 _lib.hp_last_hip_error.restype = ctypes.c_char_p
@@ -326,6 +331,36 @@ def gather_dequant_q(desc, out, scheme, scales, *, axis=0, block_size=None, zero
     _check(_lib.hp_gather_dequant_q(p, ctypes.byref(q), _ptr(out), DTYPE["bf16"], ws, n,
                                     HP_FLAG_CHECKED if checked else 0,
                                     _stream(stream, desc.device)), "hp_gather_dequant_q")
+    return out
+
+
+def attention_workspace_bytes(desc, total_tokens, num_q_heads):
+    """Workspace bytes of paged_attention (0 for an unsupported shape)."""
+    return int(_lib.hp_attention_workspace_bytes(desc.with_tokens(total_tokens), num_q_heads))
+
+
+def paged_attention(desc, v_pool, q, out, *, total_tokens, scale=None, checked=False,
+                    streaming=False, workspace=None, stream=None):
+    """out[S, Hq, D] (float32) <- decode attention of q[S, Hq, D] over the K
+    cache of `desc` (its page_pool) and the V pool `v_pool`, both read
+    through desc's block table. total_tokens: the sum of the token counts.
+    scale defaults to 1/sqrt(head_dim). A workspace is allocated through
+    torch when none is given."""
+    Hq = q.shape[1]
+    p = desc.with_tokens(total_tokens)
+    n = int(_lib.hp_attention_workspace_bytes(p, Hq))
+    if workspace is None and n:
+        workspace = _torch().empty(n, dtype=_torch().uint8, device=q.device)
+        desc._ws = workspace  # keep alive until the next call on this descriptor
+    if scale is None:
+        scale = 1.0 / float(desc.c.head_dim) ** 0.5
+    _check(_lib.hp_paged_attention(p, _ptr(v_pool), _ptr(q), Hq, float(scale), _ptr(out),
+                                   DTYPE["f32"], _ptr(workspace),
+                                   workspace.numel() * workspace.element_size()
+                                   if workspace is not None else 0,
+                                   (HP_FLAG_CHECKED if checked else 0) |
+                                   (HP_FLAG_STREAM if streaming else 0),
+                                   _stream(stream, desc.device)), "hp_paged_attention")
     return out
 
 

@@ -15,7 +15,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = [os.path.join(CSRC, "hp_api.cpp"), os.path.join(CSRC, "hp_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "hp_api.cpp"), os.path.join(CSRC, "hp_kernels.hip"),
+           os.path.join(CSRC, "hp_attention.hip")]
 LIB = os.path.join(HERE, "libhp.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -34,14 +35,29 @@ FLAGS = [
 
 
 def build(verbose=False, defines=(), out=None):
+    """Compile every source to an object in parallel, then link the library."""
     out = out or LIB
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *defines, "-o", tmp]
-    for src in SOURCES:
-        cmd += ["-x", "hip", src]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    objs = [f"{tmp}.{os.path.basename(src)}.o" for src in SOURCES]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    procs = []
+    for src, obj in zip(SOURCES, objs):
+        cmd = [HIPCC, *compile_flags, *defines, "-c", "-x", "hip", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd)))
+    failed = [cmd for cmd, p in procs if p.wait() != 0]
+    try:
+        if failed:
+            raise subprocess.CalledProcessError(1, failed[0])
+        link = [HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.run(link, check=True)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
     os.replace(tmp, out)
     return out
 

@@ -663,6 +663,102 @@ hp_status hp_gather_dequant_q(const hp_desc *desc, const hp_quant *quant, void *
     return launch(&d, g, hp::Op::Dequant, m, nullptr, flags, workspace, (hipStream_t)stream, &q);
 }
 
+// Shape checks of hp_paged_attention beyond the descriptor's own.
+hp_status check_attention(const hp_desc *d, uint32_t num_q_heads) {
+    if (d->dtype != HP_DTYPE_F16 && d->dtype != HP_DTYPE_BF16)
+        return HP_ERR_DTYPE;
+    const uint32_t D = d->head_dim;
+    if (D != 8 && D != 16 && D != 32 && D != 64 && D != 128 && D != 256)
+        return HP_ERR_ARG;
+    if (!num_q_heads || num_q_heads % d->num_heads)
+        return HP_ERR_ARG;
+    const uint32_t G = num_q_heads / d->num_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return HP_ERR_ARG;
+    // grid limits: grid x = units + num_seqs, grid y = head groups; Hq * D
+    // indexes one sequence's output in 32 bits
+    if (d->page_size > 65536 || d->num_seqs >= (1ull << 31) ||
+        (uint64_t)num_q_heads * D >= (1ull << 31))
+        return HP_ERR_ARG;
+    const hp::AttentionShape sh =
+        hp::attention_shape(d->num_seqs, d->total_tokens, d->page_size, d->num_heads, D);
+    if (sh.cap_units + d->num_seqs >= (1ull << 31) || sh.head_groups > 65535)
+        return HP_ERR_ARG;
+    return HP_OK;
+}
+
+size_t hp_attention_workspace_bytes(const hp_desc *desc, uint32_t num_q_heads) {
+    Geometry g;
+    if (!desc || check_desc(desc, &g) != HP_OK || check_attention(desc, num_q_heads) != HP_OK)
+        return 0;
+    return hp::attention_workspace_bytes(desc->num_seqs, desc->total_tokens, desc->page_size,
+                                         desc->num_heads, desc->head_dim, num_q_heads);
+}
+
+hp_status hp_paged_attention(const hp_desc *desc, const void *v_pool, const void *q,
+                             uint32_t num_q_heads, float scale, void *out, uint32_t out_dtype,
+                             void *workspace, size_t workspace_bytes, uint32_t flags,
+                             void *stream) {
+    Geometry g;
+    hp_status st = check_desc(desc, &g);
+    if (st != HP_OK)
+        return st;
+    if (out_dtype != HP_DTYPE_F32)
+        return HP_ERR_DTYPE;
+    if ((st = check_attention(desc, num_q_heads)) != HP_OK)
+        return st;
+    if (flags & ~(uint32_t)(HP_FLAG_CHECKED | HP_FLAG_STREAM))
+        return HP_ERR_ARG;
+    const uint64_t S = desc->num_seqs, D = desc->head_dim;
+    if (S && (!v_pool || !q || !out))
+        return HP_ERR_NULL;
+    if (!aligned(v_pool, 64) || !aligned(q, 16) || !aligned(out, 16))
+        return HP_ERR_ALIGN;
+    const uint64_t need = hp::attention_workspace_bytes(S, desc->total_tokens, desc->page_size,
+                                                        desc->num_heads, D, num_q_heads);
+    if ((st = check_workspace(workspace, workspace_bytes, need)) != HP_OK)
+        return st;
+    if (!aligned(workspace, 256))
+        return HP_ERR_ALIGN;
+    const uint64_t q_bytes = S * num_q_heads * D * 2, out_bytes = S * num_q_heads * D * 4;
+    const void *reads[3] = {desc->page_pool, v_pool, q};
+    const uint64_t read_bytes[3] = {g.pool_bytes, g.pool_bytes, q_bytes};
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(out, out_bytes, reads[i], read_bytes[i]) ||
+            overlaps(workspace, need, reads[i], read_bytes[i]))
+            return HP_ERR_ARG;
+    if (overlaps(out, out_bytes, workspace, need))
+        return HP_ERR_ARG;
+    if (flags & HP_FLAG_CHECKED) {
+        hp_validate_result r;
+        if ((st = run_validate(desc, nullptr, workspace, &r, (hipStream_t)stream)) != HP_OK)
+            return st;
+    }
+    if (!S)
+        return HP_OK;
+    hp::AttentionJob j = {};
+    j.idx64 = desc->index_type == HP_INDEX_U64;
+    j.bf16 = desc->dtype == HP_DTYPE_BF16;
+    j.stream_loads = flags & HP_FLAG_STREAM;
+    j.num_seqs = (uint32_t)S;
+    j.page_size = desc->page_size;
+    j.num_kv_heads = desc->num_heads;
+    j.num_q_heads = num_q_heads;
+    j.head_dim = desc->head_dim;
+    j.total_tokens = desc->total_tokens;
+    j.k_pool = desc->page_pool;
+    j.v_pool = v_pool;
+    j.q = q;
+    j.block_table = desc->block_table;
+    j.seq_ptr = desc->seq_ptr;
+    j.seq_lens = desc->seq_lens;
+    j.out = static_cast<float *>(out);
+    j.scale = scale;
+    j.workspace = workspace;
+    const hipError_t e = hp::launch_attention(j, (hipStream_t)stream);
+    return e == hipSuccess ? HP_OK : hip_failed(e);
+}
+
 hp_status hp_copy_pages(const hp_desc *desc, const void *src_pages, const void *dst_pages,
                         uint64_t count, void *workspace, size_t workspace_bytes, uint32_t flags,
                         void *stream) {

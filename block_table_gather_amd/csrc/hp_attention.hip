@@ -1,0 +1,624 @@
+// hp_attention.hip -- decode attention that reads K and V through the block
+// table, for gfx950.
+//
+// What is computed ("Visualize PagedAttention block layout", How the attention
+// kernel uses the block table; "Keep token order across cache pages": paging
+// decides where rows are stored, not what attention computes): for each
+// sequence s and query head hq, with kv head h = hq / G (G = Hq / Hkv query
+// heads share one kv head),
+//   x_t = scale * q[s][hq] . K[t][h],  out[s][hq] = sum_t e^{x_t} V[t][h] / sum_t e^{x_t}
+// over the sequence's L_s cached tokens, whose rows are found through the
+// block table as in "Block-Paged Layout -- Hurray Format Specification",
+// Element Lookup. A sequence with no tokens gives zeros.
+//
+// Design (HBM-bound: each cached K/V byte is read once; the contraction is a
+// dot product per token and head, so it runs on the vector ALUs in fp32):
+//  * A sequence is cut into units of U tokens (U a multiple of the page size,
+//    chosen on the host so that the grid has a few thousand workgroups). A
+//    plan kernel turns the token counts into the running unit count
+//    unit_end[s] and the sequence of every unit, so a workgroup finds its
+//    sequence with one load.
+//  * Workgroup (unit, head group) covers up to 256 / (D / 8) kv heads. D / 8
+//    lanes hold one head row (16 bytes each: 8 fp16/bf16 values), so one
+//    token's row of those heads is one contiguous read. When the kv heads do
+//    not fill the workgroup, the spare lane groups take other tokens of the
+//    unit (token lanes) and their softmax states are merged through LDS.
+//  * The unit's page IDs are staged in LDS once. Each lane group streams
+//    batches of tokens: all K and V loads of a batch are issued before any is
+//    used; q . k runs on v_dot2 (two 16-bit products per instruction, fp32
+//    accumulation) and is summed across the head's lanes with DPP row
+//    operations; an online softmax (running max, base 2) rescales the
+//    accumulator once per batch.
+//  * Each unit writes (max, sum of weights, unnormalised weighted sum of V)
+//    per query head to the workspace, and a combine kernel merges a
+//    sequence's units and divides. A sequence held by one unit is normalised
+//    and written directly by its workgroup, and spare workgroups write the
+//    zeros of sequences without tokens. (Merging in the last unit to finish
+//    needs an agent-scope release per workgroup, which writes the XCD's L2
+//    back; it measured 3x slower than the second launch.)
+#include "hp_device.h"
+#include "hp_internal.h"
+
+#include <stdint.h>
+
+namespace hp {
+namespace {
+
+constexpr uint32_t kAttnThreads = 256;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct F16 {
+    static constexpr bool bf16 = false;
+};
+struct BF16 {
+    static constexpr bool bf16 = true;
+};
+
+struct AArgs {
+    const unsigned char *k_pool, *v_pool, *q;
+    const void *block_table, *seq_ptr, *seq_lens;
+    const uint32_t *unit_end, *unit_seq;
+    float *part_ml;    // [cap_units][Hq][2]: running max (base 2), sum of weights
+    float *part_acc;   // [cap_units][Hq][D]: unnormalised weighted sum of V
+    float *out;        // [S][Hq][D]
+    uint32_t num_seqs, page_size, num_kv_heads, num_q_heads, head_dim;
+    uint32_t unit_tokens, unit_pages, heads_per_group, token_lanes;
+    float qscale;      // softmax scale * log2(e)
+    Div div_page;
+};
+
+// 8 stored values (one 16-byte vector) as floats; exact.
+template <typename ET>
+__device__ __forceinline__ void unpack8(const u32x4 &v, float (&f)[8]) {
+    uint32_t w[4];
+    __builtin_memcpy(w, &v, sizeof w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (ET::bf16) {
+            f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+            f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+        } else {
+            f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
+            f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+        }
+    }
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const unsigned char *p) {
+    const u32x4 *v = reinterpret_cast<const u32x4 *>(p);
+    if constexpr (NT)
+        return __builtin_nontemporal_load(v);
+    else
+        return *v;
+}
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// x from another lane of the same 16-lane row, by a DPP pattern (a plain
+// VALU operand, no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the LPH lanes of a lane group (aligned groups of LPH lanes); every
+// lane of the group gets the same value, since each step adds a lane's value
+// to its partner's and IEEE addition is commutative.
+template <int LPH>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (LPH >= 2)
+        x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (LPH >= 4)
+        x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (LPH >= 8)
+        x += dpp<0x141>(x);  // row_half_mirror: the other quad of the 8 lanes
+    if constexpr (LPH >= 16)
+        x += dpp<0x140>(x);  // row_mirror: the other 8 lanes of the 16-lane row
+    if constexpr (LPH >= 32)
+        x += __shfl_xor(x, 16, 64);
+    return x;
+}
+
+// Sum over the 8 stored elements of q (packed) times k (packed), fp32
+// accumulation: v_dot2 takes two 16-bit products per instruction.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short bf16x2_bits __attribute__((ext_vector_type(2)));
+template <typename ET>
+__device__ __forceinline__ float dot8(const uint32_t (&q)[4], const u32x4 &k) {
+    uint32_t w[4];
+    __builtin_memcpy(w, &k, sizeof w);
+    float d = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (ET::bf16)
+            d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_bits, q[i]),
+                                                __builtin_bit_cast(bf16x2_bits, w[i]), d, false);
+        else
+            d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q[i]),
+                                       __builtin_bit_cast(f16x2, w[i]), d, false);
+    }
+    return d;
+}
+
+// Tokens per batch of one lane group: all their K and V loads are in flight
+// together. Fewer for larger groups, whose query and accumulator registers
+// grow with G.
+#ifndef HP_ATTN_BATCH_LARGE_GROUP
+#define HP_ATTN_BATCH_LARGE_GROUP 4
+#endif
+template <int G>
+constexpr int batch_tokens() {
+    return G <= 2 ? 8 : (G == 4 ? 4 : HP_ATTN_BATCH_LARGE_GROUP);
+}
+
+template <typename ET, typename IdxT, int LPH, int G, bool NT>
+__global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
+    // No implicit multiply-add fusion: each fused step below is an explicit
+    // fma, and a score must round before its max is subtracted, so that the
+    // largest score weighs exactly exp2(0) = 1.
+#pragma clang fp contract(off)
+    constexpr int TB = batch_tokens<G>();
+    constexpr uint32_t NG = kAttnThreads / LPH;  // lane groups
+    constexpr uint32_t D = LPH * 8;
+    extern __shared__ __align__(16) unsigned char lds[];
+    uint64_t *pages = reinterpret_cast<uint64_t *>(lds);                      // [unit_pages]
+    float *red = reinterpret_cast<float *>(lds + 8 * (size_t)a.unit_pages);  // token-lane merge
+
+    const uint32_t S = a.num_seqs;
+    const uint32_t g = blockIdx.x;
+    const uint32_t total = uni(a.unit_end[S - 1]);
+    const uint32_t Hq = a.num_q_heads, Hkv = a.num_kv_heads, P = a.page_size;
+    const uint32_t hpw = a.heads_per_group;
+    const uint32_t hq0 = blockIdx.y * hpw * G;  // this group's first query head
+    const uint32_t nq = (min32(Hkv, (blockIdx.y + 1) * hpw) - blockIdx.y * hpw) * G;
+    if (g >= total) {
+        // spare workgroups: workgroup total + s writes the zeros of sequence s
+        // when it has no token (no unit would write them)
+        const uint32_t se = g - total;
+        if (se >= S || ld_idx<IdxT>(a.seq_lens, se) != 0)
+            return;
+        float *o = a.out + ((uint64_t)se * Hq + hq0) * D;
+        for (uint32_t e = threadIdx.x; e < nq * D; e += kAttnThreads)
+            o[e] = 0.0f;
+        return;
+    }
+    const uint32_t s = uni(a.unit_seq[g]);
+    const uint32_t u0 = s ? uni(a.unit_end[s - 1]) : 0;
+    const uint64_t L = uni64(ld_idx<IdxT>(a.seq_lens, s));
+    const uint64_t sp0 = uni64(ld_idx<IdxT>(a.seq_ptr, s));
+    const uint64_t t0 = (uint64_t)(g - u0) * a.unit_tokens;  // a multiple of the page size
+    const uint32_t n = (uint32_t)min64(L - t0, a.unit_tokens);
+    const uint64_t pg0 = t0 / a.page_size;
+    const uint32_t npg = udiv32(n + a.page_size - 1, a.div_page);
+    for (uint32_t i = threadIdx.x; i < npg; i += kAttnThreads)
+        pages[i] = ld_idx<IdxT>(a.block_table, sp0 + pg0 + i);
+    __syncthreads();
+
+    const uint32_t lane = threadIdx.x;
+    const uint32_t lg = lane / LPH, r = lane % LPH;
+    const uint32_t TL = a.token_lanes;
+    const uint32_t hl = lg % hpw, tl = lg / hpw;
+    const uint32_t h = blockIdx.y * hpw + hl;
+    const bool active = tl < TL && h < Hkv;
+
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+        m[gi] = -__builtin_inff();
+        l[gi] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[gi][e] = 0.0f;
+    }
+
+    if (active) {
+        uint32_t qp[G][4];  // the query's 8 elements of this lane, packed as stored
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            const uint64_t qo = (((uint64_t)s * Hq + (uint64_t)h * G + gi) * D + r * 8) * 2;
+            const u32x4 v = ld16<false>(a.q + qo);
+            __builtin_memcpy(qp[gi], &v, 16);
+        }
+        const uint64_t head_off = ((uint64_t)h * D + r * 8) * 2;
+        const uint64_t slot_bytes = (uint64_t)Hkv * D * 2;
+        // each batch starts with a token in range, so its running max is finite
+        for (uint32_t jb = 0; jb + tl < n; jb += TB * TL) {
+            u32x4 kq[TB], vq[TB];
+            bool ok[TB];
+#pragma unroll
+            for (int i = 0; i < TB; ++i) {
+                const uint32_t j = jb + tl + i * TL;
+                ok[i] = j < n;
+                const uint32_t jj = ok[i] ? j : n - 1;  // always a real row: loads need no guard
+                const uint32_t pj = udiv32(jj, a.div_page);
+                const uint64_t row = pages[pj] * P + (jj - pj * P);
+                const uint64_t off = row * slot_bytes + head_off;
+                kq[i] = ld16<NT>(a.k_pool + off);
+                vq[i] = ld16<NT>(a.v_pool + off);
+            }
+            float x[G][TB];
+#pragma unroll
+            for (int i = 0; i < TB; ++i) {
+#pragma unroll
+                for (int gi = 0; gi < G; ++gi) {
+                    const float dot = group_sum<LPH>(dot8<ET>(qp[gi], kq[i])) * a.qscale;
+                    x[gi][i] = ok[i] ? dot : -__builtin_inff();
+                }
+            }
+            float p[G][TB];
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+                float mx = m[gi];
+#pragma unroll
+                for (int i = 0; i < TB; ++i)
+                    mx = __builtin_fmaxf(mx, x[gi][i]);
+                // mx is finite (the batch's first token is in range); m may be -inf
+                const float corr = exp2_hw(m[gi] - mx);
+                float ps = 0.0f;
+#pragma unroll
+                for (int i = 0; i < TB; ++i) {
+                    p[gi][i] = ok[i] ? exp2_hw(x[gi][i] - mx) : 0.0f;
+                    ps += p[gi][i];
+                }
+                l[gi] = l[gi] * corr + ps;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[gi][e] *= corr;
+                m[gi] = mx;
+            }
+#pragma unroll
+            for (int i = 0; i < TB; ++i) {
+                float vf[8];
+                unpack8<ET>(vq[i], vf);
+#pragma unroll
+                for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[gi][e] = __builtin_fmaf(p[gi][i], vf[e], acc[gi][e]);
+            }
+        }
+    }
+
+    // Merge the token lanes of each head into token lane 0.
+    if (TL > 1) {
+        float *rml = red;                  // [NG][2]
+        float *racc = red + 2 * NG;        // [NG][D]
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            if (active && tl > 0) {
+                if (r == 0) {
+                    rml[2 * lg] = m[gi];
+                    rml[2 * lg + 1] = l[gi];
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    racc[lg * D + r * 8 + e] = acc[gi][e];
+            }
+            __syncthreads();
+            if (active && tl == 0) {
+                float M = m[gi];
+                for (uint32_t t2 = 1; t2 < TL; ++t2)
+                    M = __builtin_fmaxf(M, rml[2 * (t2 * hpw + hl)]);
+                const float c0 = exp2_hw(m[gi] - M);
+                l[gi] *= c0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[gi][e] *= c0;
+                for (uint32_t t2 = 1; t2 < TL; ++t2) {
+                    const uint32_t o = t2 * hpw + hl;
+                    const float mo = rml[2 * o];
+                    // a token lane that saw no token has max -inf and weight 0
+                    const float c = mo == -__builtin_inff() ? 0.0f : exp2_hw(mo - M);
+                    l[gi] = __builtin_fmaf(rml[2 * o + 1], c, l[gi]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[gi][e] = __builtin_fmaf(racc[o * D + r * 8 + e], c, acc[gi][e]);
+                }
+                m[gi] = M;
+            }
+            __syncthreads();
+        }
+    }
+
+    const uint32_t units = uni(a.unit_end[s]) - u0;
+    if (units == 1) {
+        // the sequence's only unit: normalise and write the output directly
+        if (active && tl == 0) {
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+                float *dst = a.out + ((uint64_t)s * Hq + (uint64_t)h * G + gi) * D + r * 8;
+                float o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    o[e] = acc[gi][e] / l[gi];
+                u32x4 lo, hi;
+                __builtin_memcpy(&lo, &o[0], 16);
+                __builtin_memcpy(&hi, &o[4], 16);
+                reinterpret_cast<u32x4 *>(dst)[0] = lo;
+                reinterpret_cast<u32x4 *>(dst)[1] = hi;
+            }
+        }
+        return;
+    }
+
+    if (active && tl == 0) {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            const uint64_t idx = (uint64_t)g * Hq + (uint64_t)h * G + gi;
+            float *dst = a.part_acc + idx * D + r * 8;
+            u32x4 lo, hi;
+            __builtin_memcpy(&lo, &acc[gi][0], 16);
+            __builtin_memcpy(&hi, &acc[gi][4], 16);
+            reinterpret_cast<u32x4 *>(dst)[0] = lo;
+            reinterpret_cast<u32x4 *>(dst)[1] = hi;
+            if (r == 0) {
+                a.part_ml[2 * idx] = m[gi];
+                a.part_ml[2 * idx + 1] = l[gi];
+            }
+        }
+    }
+}
+
+// Running unit count per sequence, unit_end[s] = sum over s' <= s of
+// ceil(L_s' / U) (capped at the workspace's unit capacity), and the sequence
+// of every unit, unit_seq[u]. One workgroup.
+template <typename IdxT>
+__global__ __launch_bounds__(kAttnThreads) void attention_plan_kernel(const void *seq_lens,
+                                                                      uint32_t S, uint32_t U,
+                                                                      uint32_t cap,
+                                                                      uint32_t *unit_end,
+                                                                      uint32_t *unit_seq) {
+    __shared__ uint64_t wave_sum[kAttnThreads / 64];
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t running = 0;
+    for (uint32_t base = 0; base < S; base += kAttnThreads) {
+        const uint32_t i = base + threadIdx.x;
+        uint64_t v = 0;
+        if (i < S) {
+            const uint64_t len = ld_idx<IdxT>(seq_lens, i);
+            v = len / U + (len % U != 0);
+        }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint64_t y = __shfl_up(v, o, 64);
+            if (lane >= (uint32_t)o)
+                v += y;
+        }
+        if (lane == 63)
+            wave_sum[wave] = v;
+        __syncthreads();
+        uint64_t before = running;
+        for (uint32_t w = 0; w < wave; ++w)
+            before += wave_sum[w];
+        if (i < S)
+            unit_end[i] = (uint32_t)min64(before + v, cap);
+        for (uint32_t w = 0; w < kAttnThreads / 64; ++w)
+            running += wave_sum[w];
+        __syncthreads();
+    }
+    // unit -> sequence map: the workgroup's own unit_end stores are visible to
+    // it after the barrier above
+    const uint32_t total = S ? unit_end[S - 1] : 0;
+    for (uint32_t u = threadIdx.x; u < total; u += kAttnThreads) {
+        uint32_t lo = 0, hi = S - 1;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (unit_end[mid] > u)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        unit_seq[u] = lo;
+    }
+}
+
+struct CArgs {
+    const uint32_t *unit_end;
+    const float *part_ml, *part_acc;
+    float *out;
+    uint32_t num_q_heads, head_dim;
+    Div div_d;
+};
+
+// out[s][hq][d] of a sequence held by several units: the units' partial
+// results merged with max-shifted weights, then divided. One pass over the
+// units, kBatch at a time so that their loads are in flight together.
+// Sequences of zero or one unit were written by the attention kernel.
+__global__ __launch_bounds__(kAttnThreads) void attention_combine_kernel(CArgs c) {
+    constexpr uint32_t kBatch = 16;
+    const uint32_t s = blockIdx.x;
+    const uint32_t u0 = s ? c.unit_end[s - 1] : 0, u1 = c.unit_end[s];
+    if (u1 - u0 < 2)
+        return;
+    const uint32_t i = blockIdx.y * kAttnThreads + threadIdx.x;
+    const uint32_t Hq = c.num_q_heads, D = c.head_dim;
+    if (i >= Hq * D)
+        return;
+    const uint32_t hq = udiv32(i, c.div_d), d = i - hq * D;
+    float M = -__builtin_inff(), lsum = 0.0f, num = 0.0f;
+    for (uint32_t ub = u0; ub < u1; ub += kBatch) {
+        float mv[kBatch], lv[kBatch], av[kBatch];
+#pragma unroll
+        for (uint32_t k = 0; k < kBatch; ++k) {
+            const uint32_t u = ub + k < u1 ? ub + k : u1 - 1;  // repeats get weight 0 below
+            const uint64_t idx = (uint64_t)u * Hq + hq;
+            mv[k] = c.part_ml[2 * idx];
+            lv[k] = c.part_ml[2 * idx + 1];
+            av[k] = c.part_acc[idx * D + d];
+        }
+        float Mn = M;
+#pragma unroll
+        for (uint32_t k = 0; k < kBatch; ++k)
+            Mn = __builtin_fmaxf(Mn, mv[k]);
+        const float cs = exp2_hw(M - Mn);  // M = -inf on the first batch: 0
+        lsum *= cs;
+        num *= cs;
+#pragma unroll
+        for (uint32_t k = 0; k < kBatch; ++k) {
+            const float w = ub + k < u1 ? exp2_hw(mv[k] - Mn) : 0.0f;
+            lsum = __builtin_fmaf(lv[k], w, lsum);
+            num = __builtin_fmaf(av[k], w, num);
+        }
+        M = Mn;
+    }
+    c.out[(uint64_t)s * Hq * D + i] = num / lsum;
+}
+
+// ---- host side ----------------------------------------------------------------
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+template <typename ET, typename IdxT, int LPH, int G>
+hipError_t launch_attention_t(const AArgs &a, const AttentionShape &sh, bool nt,
+                              hipStream_t stream) {
+    const dim3 grid((uint32_t)(sh.cap_units + a.num_seqs), sh.head_groups);
+    const uint32_t ng = kAttnThreads / LPH;
+    const size_t lds = 8 * (size_t)a.unit_pages +
+                       (sh.token_lanes > 1 ? 4 * (size_t)ng * (2 + LPH * 8) : 0);
+    if (nt)
+        hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, G, true>), grid, dim3(kAttnThreads),
+                           lds, stream, a);
+    else
+        hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, G, false>), grid, dim3(kAttnThreads),
+                           lds, stream, a);
+    return hipGetLastError();
+}
+
+template <typename ET, typename IdxT, int LPH>
+hipError_t launch_attention_g(const AArgs &a, const AttentionShape &sh, uint32_t G, bool nt,
+                              hipStream_t st) {
+    switch (G) {
+    case 1: return launch_attention_t<ET, IdxT, LPH, 1>(a, sh, nt, st);
+    case 2: return launch_attention_t<ET, IdxT, LPH, 2>(a, sh, nt, st);
+    case 4: return launch_attention_t<ET, IdxT, LPH, 4>(a, sh, nt, st);
+    default: return launch_attention_t<ET, IdxT, LPH, 8>(a, sh, nt, st);
+    }
+}
+
+template <typename ET, typename IdxT>
+hipError_t launch_attention_d(const AArgs &a, const AttentionShape &sh, uint32_t G, bool nt,
+                              hipStream_t st) {
+    switch (a.head_dim) {
+    case 8: return launch_attention_g<ET, IdxT, 1>(a, sh, G, nt, st);
+    case 16: return launch_attention_g<ET, IdxT, 2>(a, sh, G, nt, st);
+    case 32: return launch_attention_g<ET, IdxT, 4>(a, sh, G, nt, st);
+    case 64: return launch_attention_g<ET, IdxT, 8>(a, sh, G, nt, st);
+    case 128: return launch_attention_g<ET, IdxT, 16>(a, sh, G, nt, st);
+    default: return launch_attention_g<ET, IdxT, 32>(a, sh, G, nt, st);
+    }
+}
+
+template <typename ET>
+hipError_t launch_attention_i(const AArgs &a, const AttentionShape &sh, uint32_t G, bool idx64,
+                              bool nt, hipStream_t st) {
+    return idx64 ? launch_attention_d<ET, uint64_t>(a, sh, G, nt, st)
+                 : launch_attention_d<ET, uint32_t>(a, sh, G, nt, st);
+}
+
+struct WsLayout {
+    uint64_t unit_end, unit_seq, ml, acc, end;
+};
+
+WsLayout ws_layout(uint64_t S, uint64_t Hq, uint64_t D, uint64_t cap) {
+    WsLayout w;
+    w.unit_end = 256;  // the validator's words come first
+    w.unit_seq = w.unit_end + align256(4 * S);
+    w.ml = w.unit_seq + align256(4 * cap);
+    w.acc = w.ml + align256(8 * cap * Hq);
+    w.end = w.acc + align256(4 * cap * Hq * D);
+    return w;
+}
+
+} // namespace
+
+AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
+                               uint32_t num_kv_heads, uint32_t head_dim) {
+    AttentionShape sh;
+    const uint32_t lph = head_dim / 8;
+    const uint32_t ng = kAttnThreads / lph;
+    sh.heads_per_group = num_kv_heads < ng ? num_kv_heads : ng;
+    sh.token_lanes = ng / sh.heads_per_group;
+    sh.head_groups = (num_kv_heads + sh.heads_per_group - 1) / sh.heads_per_group;
+    // Pages to visit (at most), spread over about kAttnTargetGroups workgroups.
+    const uint64_t pages = total_tokens / page_size + num_seqs;
+    uint64_t upages = (pages * sh.head_groups + kAttnTargetGroups - 1) / kAttnTargetGroups;
+    if (upages < 1)
+        upages = 1;
+    if (upages > kAttnMaxUnitPages)
+        upages = kAttnMaxUnitPages;
+    sh.unit_pages = (uint32_t)upages;
+    sh.unit_tokens = (uint32_t)(upages * page_size);
+    sh.cap_units = total_tokens / sh.unit_tokens + num_seqs;
+    return sh;
+}
+
+uint64_t attention_workspace_bytes(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
+                                   uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads) {
+    const AttentionShape sh =
+        attention_shape(num_seqs, total_tokens, page_size, num_kv_heads, head_dim);
+    return ws_layout(num_seqs, num_q_heads, head_dim, sh.cap_units).end;
+}
+
+hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
+    (void)hipGetLastError();  // clear errors left by earlier calls that are not ours
+    const AttentionShape sh = attention_shape(job.num_seqs, job.total_tokens, job.page_size,
+                                              job.num_kv_heads, job.head_dim);
+    const WsLayout wl = ws_layout(job.num_seqs, job.num_q_heads, job.head_dim, sh.cap_units);
+    unsigned char *ws = static_cast<unsigned char *>(job.workspace);
+    uint32_t *unit_end = reinterpret_cast<uint32_t *>(ws + wl.unit_end);
+    uint32_t *unit_seq = reinterpret_cast<uint32_t *>(ws + wl.unit_seq);
+
+    hipLaunchKernelGGL(job.idx64 ? attention_plan_kernel<uint64_t> : attention_plan_kernel<uint32_t>,
+                       dim3(1), dim3(kAttnThreads), 0, stream, job.seq_lens, job.num_seqs,
+                       sh.unit_tokens, (uint32_t)sh.cap_units, unit_end, unit_seq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+
+    AArgs a = {};
+    a.k_pool = static_cast<const unsigned char *>(job.k_pool);
+    a.v_pool = static_cast<const unsigned char *>(job.v_pool);
+    a.q = static_cast<const unsigned char *>(job.q);
+    a.block_table = job.block_table;
+    a.seq_ptr = job.seq_ptr;
+    a.seq_lens = job.seq_lens;
+    a.unit_end = unit_end;
+    a.unit_seq = unit_seq;
+    a.part_ml = reinterpret_cast<float *>(ws + wl.ml);
+    a.part_acc = reinterpret_cast<float *>(ws + wl.acc);
+    a.out = job.out;
+    a.num_seqs = job.num_seqs;
+    a.page_size = job.page_size;
+    a.num_kv_heads = job.num_kv_heads;
+    a.num_q_heads = job.num_q_heads;
+    a.head_dim = job.head_dim;
+    a.unit_tokens = sh.unit_tokens;
+    a.unit_pages = sh.unit_pages;
+    a.heads_per_group = sh.heads_per_group;
+    a.token_lanes = sh.token_lanes;
+    a.qscale = job.scale * 1.4426950408889634f;  // log2(e)
+    a.div_page = make_div(job.page_size);
+    const uint32_t G = job.num_q_heads / job.num_kv_heads;
+    e = job.bf16 ? launch_attention_i<BF16>(a, sh, G, job.idx64, job.stream_loads, stream)
+                 : launch_attention_i<F16>(a, sh, G, job.idx64, job.stream_loads, stream);
+    if (e != hipSuccess)
+        return e;
+
+    CArgs c = {};
+    c.unit_end = unit_end;
+    c.part_ml = a.part_ml;
+    c.part_acc = a.part_acc;
+    c.out = job.out;
+    c.num_q_heads = job.num_q_heads;
+    c.head_dim = job.head_dim;
+    c.div_d = make_div(job.head_dim);
+    const uint32_t per_seq = job.num_q_heads * job.head_dim;
+    hipLaunchKernelGGL(attention_combine_kernel,
+                       dim3(job.num_seqs, (per_seq + kAttnThreads - 1) / kAttnThreads),
+                       dim3(kAttnThreads), 0, stream, c);
+    return hipGetLastError();
+}
+
+} // namespace hp

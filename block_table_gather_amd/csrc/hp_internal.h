@@ -123,6 +123,40 @@ struct ValidateJob {
     void *workspace; // >= 16 bytes: [0] min key, [1] token sum
 };
 
+// Decode attention over a block-paged K/V cache (hp_attention.hip).
+// Workgroups aimed at per launch (a unit holds enough pages to reach about
+// this many), and the most pages one unit may hold.
+#ifndef HP_ATTN_TARGET_GROUPS
+#define HP_ATTN_TARGET_GROUPS 2048
+#endif
+constexpr uint64_t kAttnTargetGroups = HP_ATTN_TARGET_GROUPS;
+constexpr uint64_t kAttnMaxUnitPages = 256;
+
+struct AttentionShape {
+    uint32_t heads_per_group;  // kv heads of one workgroup
+    uint32_t token_lanes;      // lane groups per head (spare lanes take other tokens)
+    uint32_t head_groups;      // grid rows
+    uint32_t unit_pages, unit_tokens;
+    uint64_t cap_units;        // grid columns: units of the largest batch with total_tokens
+};
+
+struct AttentionJob {
+    bool idx64, bf16, stream_loads;
+    uint32_t num_seqs, page_size, num_kv_heads, num_q_heads, head_dim;
+    uint64_t total_tokens;
+    const void *k_pool, *v_pool, *q;
+    const void *block_table, *seq_ptr, *seq_lens;
+    float *out;
+    float scale;
+    void *workspace;  // attention_workspace_bytes(...)
+};
+
+AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
+                               uint32_t num_kv_heads, uint32_t head_dim);
+uint64_t attention_workspace_bytes(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
+                                   uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads);
+hipError_t launch_attention(const AttentionJob &job, hipStream_t stream);
+
 // Workspace layout for the plan arrays (num_seqs > kFusedMaxSeqs).
 uint64_t plan_workspace_bytes(uint64_t num_seqs);
 

@@ -31,6 +31,7 @@
 //  * Dequant reads 8 int8 values per lane and writes 8 bf16 values (16 B) per
 //    lane, so both sides stay fully coalesced; the unit's per-slot scales sit
 //    one per lane and are fetched with a cross-lane shuffle.
+#include "hp_device.h"
 #include "hp_internal.h"
 
 #include <stdint.h>
@@ -78,15 +79,6 @@ __device__ __forceinline__ void st_stream(V v, V *p) {
 #endif
 }
 
-// Division by a launch-invariant 32-bit divisor d as a multiply and a shift:
-// q = (umulhi(n, mul) + n) >> shift with shift = ceil(log2 d) and
-// mul = floor(2^32 (2^shift - d) / d) + 1, exact for every 32-bit n
-// (Granlund and Montgomery, "Division by invariant integers using
-// multiplication", 1994).
-struct Div {
-    uint32_t d, mul, shift;
-};
-
 // Device-side view of a launch. Offsets inside one unit are 32-bit (the host
 // guarantees rows_per_unit * row bytes < 2^31); page and row bases are 64-bit.
 struct Args {
@@ -120,32 +112,6 @@ struct Args {
     unsigned char *rows[kMaxBatch];   // the logical tensor of pool m
     const float *scales[kMaxBatch];   // dequant: per-slot scales of pool m
 };
-
-__device__ __forceinline__ uint64_t min64(uint64_t a, uint64_t b) { return a < b ? a : b; }
-__device__ __forceinline__ uint32_t min32(uint32_t a, uint32_t b) { return a < b ? a : b; }
-
-__device__ __forceinline__ uint32_t uni(uint32_t x) {
-    return __builtin_amdgcn_readfirstlane(x);
-}
-__device__ __forceinline__ uint64_t uni64(uint64_t x) {
-    uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-    uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint32_t udiv32(uint32_t n, Div f) {
-    return (uint32_t)(((uint64_t)__umulhi(n, f.mul) + n) >> f.shift);
-}
-__device__ __forceinline__ uint64_t udiv(uint64_t n, Div f) {
-    if ((n >> 32) == 0)
-        return udiv32((uint32_t)n, f);
-    return n / f.d;
-}
-
-template <typename IdxT>
-__device__ __forceinline__ uint64_t ld_idx(const void *p, uint64_t i) {
-    return (uint64_t)static_cast<const IdxT *>(p)[i];
-}
 
 // Units (token runs) of sequence s. Gather/dequant: ceil(L / rpc) runs
 // starting at token 0. Scatter: the rpc-aligned windows of positions
@@ -970,17 +936,6 @@ hipError_t launch_idx(const Args &a, Op op, uint32_t vec, bool ntl, bool fused, 
     default:
         return launch_op<IdxT, Op::Dequant>(a, vec, ntl, fused, grid, chunks, ue, tb, st, qm);
     }
-}
-
-Div make_div(uint32_t d) {
-    Div f;
-    f.d = d;
-    f.shift = 0;
-    while ((1ull << f.shift) < d)
-        ++f.shift;
-    const unsigned __int128 num = ((unsigned __int128)1 << 32) * (((uint64_t)1 << f.shift) - d);
-    f.mul = (uint32_t)(num / d + 1);
-    return f;
 }
 
 } // namespace

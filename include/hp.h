@@ -282,6 +282,49 @@ hp_status hp_copy_pages_batch(const hp_desc *desc, uint32_t num_pools, void *con
                               uint64_t count, void *workspace, size_t workspace_bytes,
                               uint32_t flags, void *stream);
 
+/* ---- Decode attention through the block table ------------------------------
+ *
+ * [Day51] "How the attention kernel uses the block table": attention reads a
+ * sequence's keys and values block by block through its table; [Rust20]
+ * "Keep token order across cache pages": paging changes where rows are
+ * stored, not the dot products or the weighted sums. For sequence s and query
+ * head hq, with G = num_q_heads / num_heads query heads per kv head and kv
+ * head h = hq / G,
+ *   x_t = scale * sum_d q[s][hq][d] * K[t][h][d]
+ *   out[s][hq][d] = sum_t exp(x_t) * V[t][h][d] / sum_t exp(x_t)
+ * over the L_s = seq_lens[s] cached tokens t, whose K and V rows sit at
+ * [Hurray] Element Lookup's position in the two pools. A sequence with no
+ * tokens gives zeros.
+ *
+ * desc      the K cache: its page_pool is the K pool; num_heads is the number
+ *           of kv heads; dtype HP_DTYPE_F16 or HP_DTYPE_BF16; head_dim one of
+ *           8, 16, 32, 64, 128, 256; page_size at most 65,536; total_tokens
+ *           must be the sum of the counts (it sizes the grid and workspace).
+ * v_pool    DEVICE, the V pool: same geometry, dtype and block table as K
+ *           ([Hurray] Description: one descriptor per kv_role), 64-byte aligned.
+ * q         DEVICE [num_seqs, num_q_heads, head_dim] of the pool's dtype,
+ *           16-byte aligned.
+ * num_q_heads  a multiple G of num_heads with G in {1, 2, 4, 8}.
+ * scale     the softmax scale (1/sqrt(head_dim) in the usual form).
+ * out       DEVICE [num_seqs, num_q_heads, head_dim] fp32 (out_dtype
+ *           HP_DTYPE_F32), 16-byte aligned.
+ * workspace DEVICE, 256-byte aligned, at least
+ *           hp_attention_workspace_bytes(desc, num_q_heads) bytes (per-unit
+ *           partial results); it may not overlap any other buffer.
+ * Arithmetic is fp32 with an online softmax in base 2; the result differs
+ * from the exact one by rounding only. Flags: HP_FLAG_CHECKED (validate
+ * first), HP_FLAG_STREAM (no page is read twice in this call: non-temporal
+ * loads). Asynchronous on `stream`. */
+hp_status hp_paged_attention(const hp_desc *desc, const void *v_pool, const void *q,
+                             uint32_t num_q_heads, float scale, void *out, uint32_t out_dtype,
+                             void *workspace, size_t workspace_bytes, uint32_t flags,
+                             void *stream);
+
+/* Workspace bytes hp_paged_attention needs for this descriptor (its
+ * num_seqs, total_tokens and geometry); 0 for an invalid descriptor or an
+ * unsupported shape. */
+size_t hp_attention_workspace_bytes(const hp_desc *desc, uint32_t num_q_heads);
+
 /* Static, human-readable name of a status code. */
 const char *hp_status_str(int status);
 

@@ -26,7 +26,8 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"hp_workspace_bytes", "hp_validate", "hp_gather", "hp_scatter",
                           "hp_gather_dequant", "hp_status_str", "hp_last_hip_error",
                           "hp_gather_batch", "hp_scatter_batch", "hp_gather_dequant_batch",
-                          "hp_copy_pages", "hp_copy_pages_batch", "hp_gather_dequant_q"}
+                          "hp_copy_pages", "hp_copy_pages_batch", "hp_gather_dequant_q",
+                          "hp_paged_attention", "hp_attention_workspace_bytes"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -190,6 +191,60 @@ def test_quant_rejections():
     # the descriptor's own scales play no part
     assert dq_q(desc(dtype=hp.DTYPE["i8"], scales=ALIGNED + 0x500004, total_tokens=0), pt) == \
         S["HP_OK"]
+
+
+def attn(d, v=ALIGNED + 0x40000000, q=ALIGNED + 0x50000000, hq=8, out=OUT, od=None, ws=None,
+         n=None, flags=0):
+    od = hp.DTYPE["f32"] if od is None else od
+    if ws is None:
+        ws = ALIGNED + 0x200000000
+        n = 1 << 30 if n is None else n
+    return L.hp_paged_attention(ctypes.byref(d) if d is not None else None, v, q, hq, 0.125,
+                                out, od, ws, n or 0, flags, None)
+
+
+def test_attention_rejections():
+    d = desc(num_seqs=0, num_block_entries=0, total_tokens=0)     # accepted shape, no work
+    assert attn(d) == S["HP_OK"]
+    assert attn(None) == S["HP_ERR_NULL"]
+    f = desc()
+    assert attn(desc(dtype=hp.DTYPE["f32"])) == S["HP_ERR_DTYPE"]
+    assert attn(desc(dtype=hp.DTYPE["i8"])) == S["HP_ERR_DTYPE"]
+    assert attn(f, od=hp.DTYPE["bf16"]) == S["HP_ERR_DTYPE"]
+    assert attn(desc(head_dim=24)) == S["HP_ERR_ARG"]              # not a supported width
+    assert attn(desc(head_dim=512)) == S["HP_ERR_ARG"]
+    assert attn(f, hq=6) == S["HP_ERR_ARG"]                        # not a multiple of 4 kv heads
+    assert attn(f, hq=12) == S["HP_ERR_ARG"]                       # group 3
+    assert attn(f, hq=0) == S["HP_ERR_ARG"]
+    assert attn(desc(page_size=1 << 17)) == S["HP_ERR_ARG"]
+    assert attn(f, flags=hp.HP_FLAG_ZERO_TAIL) == S["HP_ERR_ARG"]
+    assert attn(f, v=None) == S["HP_ERR_NULL"]
+    assert attn(f, q=None) == S["HP_ERR_NULL"]
+    assert attn(f, out=None) == S["HP_ERR_NULL"]
+    assert attn(f, v=ALIGNED + 0x40000020) == S["HP_ERR_ALIGN"]
+    assert attn(f, q=ALIGNED + 0x50000008) == S["HP_ERR_ALIGN"]
+    assert attn(f, out=OUT + 4) == S["HP_ERR_ALIGN"]
+    assert attn(f, ws=None, n=0) == S["HP_ERR_WORKSPACE"]
+    need = L.hp_attention_workspace_bytes(ctypes.byref(f), 8)
+    assert need > 256
+    assert attn(f, n=need - 1) == S["HP_ERR_WORKSPACE"]
+    assert attn(f, ws=ALIGNED + 0x200000000 + 64, n=need) == S["HP_ERR_ALIGN"]
+    assert attn(f, out=ALIGNED + 64) == S["HP_ERR_ARG"]            # out overlaps the K pool
+    assert attn(f, out=ALIGNED + 0x40000000) == S["HP_ERR_ARG"]    # out overlaps the V pool
+    assert attn(f, ws=ALIGNED + 0x50000000, n=need) == S["HP_ERR_ARG"]  # workspace over q
+    assert attn(f, out=ALIGNED + 0x200000000) == S["HP_ERR_ARG"]   # out over the workspace
+
+
+def test_attention_workspace_bytes():
+    f = desc()
+    assert L.hp_attention_workspace_bytes(None, 8) == 0
+    assert L.hp_attention_workspace_bytes(ctypes.byref(desc(dtype=hp.DTYPE["i8"])), 8) == 0
+    assert L.hp_attention_workspace_bytes(ctypes.byref(f), 6) == 0
+    a = L.hp_attention_workspace_bytes(ctypes.byref(f), 8)
+    b = L.hp_attention_workspace_bytes(ctypes.byref(f), 16)
+    assert 0 < a < b
+    big = desc(total_tokens=1 << 20, num_pages=1 << 17)
+    assert L.hp_attention_workspace_bytes(ctypes.byref(big), 8) > a
 
 
 def test_workspace_bytes():

@@ -1,0 +1,305 @@
+"""GPU parity of the decode attention over the block-paged K/V cache.
+
+The HIP path (fp32 arithmetic, online softmax in base 2, units merged by a
+combine kernel) is compared with the oracle (binary64) on the same seeded
+inputs. The bound per (sequence, query head) follows from fp32 rounding:
+
+* each score x_t = scale * q . k_t is off by at most E = (D + 16) u A, where
+  A = max_t sum_d |scale q_d k_td| and u = 2^-24 (the dot product's D
+  products and sums, the pre-scaled query, the base-2 conversion);
+* the weights are then off by a factor within e^{+-E} relative to each
+  other, and the exp2 evaluations, per-batch rescalings and fp32 sums over
+  the L tokens add at most (3L + 16) u relative error;
+* a convex combination of the value rows whose weights are perturbed by a
+  relative delta moves by at most about 2 delta max|v|.
+
+So |gpu - exact| <= 2.5 (2E + (3L + 16) u) max_t |v_t|, written in
+`tolerance`. Structured cases check exact results where the arithmetic is
+exact: one token gives its value row bit for bit; identical keys give equal
+weights, so the output is the mean of the values.
+"""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import OnDevice, host_bits, idx_tensor, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+U = 2.0 ** -24
+TORCH = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def hp():
+    import block_table_gather_amd
+    return block_table_gather_amd
+
+
+def _vals(bits, dtype):
+    return oracle.decode(bits, dtype)
+
+
+def make_inputs(w, group, seed, v_seed=None):
+    """K pool (the workload's pool), a V pool of the same table and queries,
+    all on the GPU from seeded generators."""
+    d = OnDevice(w)
+    v = dataclasses.replace(w, seed=w.seed * 7 + 3 if v_seed is None else v_seed)
+    v_pool = v.make_pool(DEV)
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    q = torch.randn((w.num_seqs, w.num_heads * group, w.head_dim), generator=g, device=DEV,
+                    dtype=torch.float32).to(TORCH[w.dtype])
+    return d, v_pool, q
+
+
+def slot_ids(w, seqs=None):
+    """Flat slot index of every token of the listed sequences, per sequence."""
+    out = []
+    for s in (range(w.num_seqs) if seqs is None else seqs):
+        base = int(w.seq_ptr[s])
+        t = np.arange(int(w.seq_lens[s]), dtype=np.int64)
+        phys = w.block_table[base + t // w.page_size].astype(np.int64)
+        out.append(phys * w.page_size + t % w.page_size)
+    return out
+
+
+def tolerance(w, qv, kv, vv, scale, group, seqs):
+    """Per (sequence, query head) bound of the module docstring. qv: float64
+    [len(seqs), Hq, D]; kv, vv: float64 [N*P, Hkv, D]."""
+    D = w.head_dim
+    tol = np.zeros(qv.shape[:2])
+    for i, ids in enumerate(slot_ids(w, seqs)):
+        L = len(ids)
+        if L == 0:
+            continue
+        Ks = kv[ids]                               # [L, Hkv, D]
+        Vs = vv[ids]
+        for hq in range(qv.shape[1]):
+            h = hq // group
+            A = np.max(np.abs(scale * qv[i, hq][None, :] * Ks[:, h, :]).sum(axis=1))
+            vmax = np.max(np.abs(Vs[:, h, :]))
+            delta = 2 * (D + 16) * U * A + (3 * L + 16) * U
+            tol[i, hq] = 2.5 * delta * vmax
+    return tol
+
+
+def oracle_attention(w, q_bits, k_bits, v_bits, scale, seqs=None):
+    """The oracle on the listed sequences (each with its own slice of the
+    table)."""
+    if seqs is None:
+        seqs = list(range(w.num_seqs))
+    sp = w.seq_ptr.astype(np.int64)
+    bt = (np.concatenate([w.block_table[sp[s]:sp[s + 1]] for s in seqs])
+          if seqs else np.zeros(0, np.uint64))
+    counts = [int(sp[s + 1] - sp[s]) for s in seqs]
+    sub_sp = np.concatenate([[0], np.cumsum(counts)]).astype(np.uint64)
+    return oracle.paged_attention(q_bits[seqs], k_bits, v_bits, w.dtype, page_size=w.page_size,
+                                  num_kv_heads=w.num_heads, head_dim=w.head_dim, block_table=bt,
+                                  seq_ptr=sub_sp, seq_lens=w.seq_lens[seqs], scale=scale)
+
+
+def check(w, got, q, d, v_pool, group, scale, seqs=None, what=""):
+    seqs = list(range(w.num_seqs)) if seqs is None else seqs
+    qb, kb, vb = host_bits(q), host_bits(d.pool), host_bits(v_pool)
+    want = oracle_attention(w, qb, kb, vb, scale, seqs)
+    shape = (-1, w.num_heads, w.head_dim)
+    tol = tolerance(w, _vals(qb[seqs], w.dtype), _vals(kb, w.dtype).reshape(shape),
+                    _vals(vb, w.dtype).reshape(shape), scale, group, seqs)
+    g = got[seqs].astype(np.float64)
+    assert not np.isnan(g).any(), f"{what}: NaN in the output"
+    err = np.abs(g - want).max(axis=2)
+    ratio = float(np.max(err / np.maximum(tol, 1e-300))) if err.size else 0.0
+    say(f"{what}: max error {float(err.max()) if err.size else 0:.3e}, "
+        f"max error / bound {ratio:.3e}")
+    bad = np.argwhere(err > tol)
+    assert not len(bad), (f"{what}: {len(bad)} (seq, head) pairs over the bound; first "
+                          f"{bad[:4].tolist()} err {err[tuple(bad[0])]:.3e} "
+                          f"tol {tol[tuple(bad[0])]:.3e}")
+
+
+def run(hp, d, v_pool, q, w, scale, **kw):
+    out = torch.full((w.num_seqs, q.shape[1], w.head_dim), float("nan"), device=DEV,
+                     dtype=torch.float32)
+    hp.paged_attention(d.desc, v_pool, q, out, total_tokens=w.total_tokens, scale=scale, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+CASES = [
+    # (dtype, head_dim, group, kv heads, page sizes)
+    ("f16", 128, 1, 8, (16,)),
+    ("bf16", 128, 4, 8, (16,)),
+    ("f16", 64, 2, 4, (8, 16)),
+    ("bf16", 256, 1, 2, (16, 32)),
+    ("f16", 32, 8, 1, (1, 3)),
+    ("bf16", 16, 1, 20, (4,)),
+    ("f16", 8, 4, 3, (5,)),
+    ("bf16", 128, 8, 2, (16,)),
+    ("f16", 128, 2, 40, (16,)),        # 3 head groups, the last one partial
+    ("bf16", 64, 1, 1, (2, 16)),       # one kv head: many token lanes
+    ("f16", 256, 4, 5, (8,)),
+    ("bf16", 8, 2, 64, (3,)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("seed", range(3))
+def test_attention_random(hp, case, seed):
+    dtype, D, group, hkv, pages = CASES[case]
+    w = workloads.random_small(1100 + 10 * case + seed, max_seqs=12, max_len=300,
+                               page_sizes=pages, heads=(hkv,), dims=(D,), dtypes=(dtype,))
+    say("attention", case, seed, group, w.describe())
+    d, v_pool, q = make_inputs(w, group, 1200 + case * 10 + seed)
+    scale = 1.0 / math.sqrt(D)
+    out = run(hp, d, v_pool, q, w, scale)
+    check(w, out.cpu().numpy(), q, d, v_pool, group, scale, what=f"case {case} seed {seed}")
+
+
+def test_attention_single_token_is_exact(hp):
+    """One cached token: its weight is exactly 1 and the output is its value
+    row, bit for bit."""
+    w = workloads.random_small(1300, max_seqs=20, max_len=40, page_sizes=(16,), heads=(4,),
+                               dims=(128,), dtypes=("bf16",))
+    w.seq_lens[:] = np.minimum(w.seq_lens, 1)
+    say("attention single token", w.describe())
+    d, v_pool, q = make_inputs(w, 2, 1301)
+    out = run(hp, d, v_pool, q, w, 0.09).cpu().numpy()
+    vv = _vals(host_bits(v_pool), "bf16").reshape(-1, w.num_heads, w.head_dim)
+    for s in range(w.num_seqs):
+        if w.seq_lens[s] == 0:
+            assert np.all(out[s] == 0)
+            continue
+        row = int(w.block_table[int(w.seq_ptr[s])]) * w.page_size
+        for hq in range(8):
+            got, want = out[s, hq].astype(np.float64), vv[row, hq // 2]
+            bad = np.flatnonzero(got != want)
+            assert not len(bad), (f"seq {s} head {hq}: {len(bad)} differ, first {bad[:4]}: "
+                                  f"got {got[bad[:4]]} want {want[bad[:4]]}")
+
+
+def test_attention_equal_keys_give_the_mean(hp):
+    """Identical keys: every weight is exactly 1, so the output is the mean of
+    the value rows (fp32 sums of L terms)."""
+    w = workloads.random_small(1310, max_seqs=10, max_len=500, page_sizes=(16,), heads=(8,),
+                               dims=(128,), dtypes=("f16",))
+    say("attention equal keys", w.describe())
+    d, v_pool, q = make_inputs(w, 1, 1311)
+    g = torch.Generator(device=DEV).manual_seed(1312)
+    krow = torch.randn(w.head_dim, generator=g, device=DEV).to(torch.float16)
+    d.pool.copy_(krow.expand_as(d.pool))
+    out = run(hp, d, v_pool, q, w, 0.1).cpu().numpy()
+    vv = _vals(host_bits(v_pool), "f16").reshape(-1, w.num_heads, w.head_dim)
+    for s, ids in enumerate(slot_ids(w)):
+        if len(ids):
+            mean = vv[ids].mean(axis=0)
+            bound = (2 * len(ids) + 8) * U * np.abs(vv[ids]).max()
+            assert np.abs(out[s] - mean).max() <= bound
+
+
+def test_attention_constant_values(hp):
+    """Every value row the same vector c: the output is c up to the rounding
+    of sum_t p_t c / sum_t p_t."""
+    w = workloads.random_small(1320, max_seqs=10, max_len=500, page_sizes=(8,), heads=(2,),
+                               dims=(64,), dtypes=("bf16",))
+    say("attention constant values", w.describe())
+    d, v_pool, q = make_inputs(w, 4, 1321)
+    c = torch.linspace(-3, 3, 64, device=DEV).to(torch.bfloat16)
+    v_pool.copy_(c.expand_as(v_pool))
+    out = run(hp, d, v_pool, q, w, 0.125).cpu().numpy()
+    cv = c.float().cpu().numpy().astype(np.float64)
+    for s in range(w.num_seqs):
+        L = int(w.seq_lens[s])
+        if L:
+            assert np.abs(out[s] - cv).max() <= (4 * L + 16) * U * 3.0
+
+
+def test_attention_streaming_and_repeat_are_bit_identical(hp):
+    w = workloads.random_small(1330, max_seqs=12, max_len=300, page_sizes=(16,), heads=(8,),
+                               dims=(128,), dtypes=("f16",), alias=False)
+    say("attention streaming", w.describe())
+    d, v_pool, q = make_inputs(w, 4, 1331)
+    a = run(hp, d, v_pool, q, w, 0.088)
+    b = run(hp, d, v_pool, q, w, 0.088, streaming=True)
+    c = run(hp, d, v_pool, q, w, 0.088)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(a.view(torch.int32), c.view(torch.int32))
+
+
+def test_attention_empty_and_short_sequences(hp):
+    """Sequences of 0..3 tokens next to long ones; one kv head, so most lane
+    groups of a workgroup are token lanes that see no token."""
+    rng = np.random.default_rng(1340)
+    lens = np.array([0, 1, 2, 3, 0, 700, 1, 0, 33], dtype=np.uint32)
+    P = 16
+    counts = (lens + P - 1) // P
+    K = int(counts.sum())
+    bt = rng.permutation(K + 5)[:K].astype(np.uint32)
+    sp = np.concatenate([[0], np.cumsum(counts)]).astype(np.uint32)
+    w = workloads.Workload("short", "bf16", P, 1, 128, K + 5, np.uint32, bt, sp, lens, seed=1340)
+    say("attention short", w.describe())
+    d, v_pool, q = make_inputs(w, 8, 1341)
+    out = run(hp, d, v_pool, q, w, 0.088)
+    res = out.cpu().numpy()
+    assert np.all(res[lens == 0] == 0)
+    check(w, res, q, d, v_pool, 8, 0.088, what="short")
+
+
+def test_attention_checked_rejects_bad_table(hp):
+    w = workloads.random_small(1350, max_seqs=6, max_len=60, page_sizes=(16,), heads=(2,),
+                               dims=(64,), dtypes=("f16",))
+    while len(w.block_table) == 0:
+        w = workloads.random_small(int(w.seed) + 1, max_seqs=6, max_len=60, page_sizes=(16,),
+                                   heads=(2,), dims=(64,), dtypes=("f16",))
+    say("attention checked", w.describe())
+    d, v_pool, q = make_inputs(w, 1, 1351)
+    bad = w.block_table.copy()
+    bad[-1] = w.num_pages                       # one page ID past the pool
+    bt = idx_tensor(bad.astype(w.index_dtype), DEV)
+    desc = hp.Descriptor(d.pool, bt, d.sp, d.sl)
+    out = torch.zeros((w.num_seqs, 2, 64), device=DEV)
+    with pytest.raises(hp.HpError, match="HP_ERR_PAGE_RANGE"):
+        hp.paged_attention(desc, v_pool, q, out, total_tokens=w.total_tokens, checked=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out) == 0
+
+
+def _sample(w, count, seed):
+    rng = np.random.default_rng(seed)
+    S = w.num_seqs
+    pick = {0, S - 1, int(np.argmax(w.seq_lens))}
+    pick |= set(rng.choice(S, size=min(count, S), replace=False).tolist())
+    return sorted(pick)
+
+
+def test_attention_decode_workload(hp):
+    """64 sequences of 1..2048 tokens, 32 kv heads x 128 fp16 (one query head
+    per kv head), in the launch shape the benchmark uses (streaming loads);
+    nine sequences (the first, the last, the longest and six at random)
+    against the oracle."""
+    w = workloads.decode()
+    say("attention decode full", w.describe())
+    d, v_pool, q = make_inputs(w, 1, 1400)
+    scale = 1.0 / math.sqrt(128)
+    out = run(hp, d, v_pool, q, w, scale, streaming=True).cpu().numpy()
+    check(w, out, q, d, v_pool, 1, scale, seqs=_sample(w, 6, 1401), what="decode")
+    del d, v_pool
+    torch.cuda.empty_cache()
+
+
+def test_attention_prefix_workload_gqa(hp):
+    """256 sequences sharing 64 prefix pages, 8 kv heads x 128 bf16 and 32
+    query heads (groups of 4); cached loads, since the prefix pages are read
+    by every sequence."""
+    w = workloads.prefix()
+    say("attention prefix full", w.describe())
+    d, v_pool, q = make_inputs(w, 4, 1410)
+    scale = 1.0 / math.sqrt(128)
+    out = run(hp, d, v_pool, q, w, scale).cpu().numpy()
+    check(w, out, q, d, v_pool, 4, scale, seqs=_sample(w, 5, 1411), what="prefix")
+    del d, v_pool
+    torch.cuda.empty_cache()
