@@ -14,10 +14,11 @@
 // Design (HBM-bound: each cached K/V byte is read once; the contraction is a
 // dot product per token and head, so it runs on the vector ALUs in fp32):
 //  * A sequence is cut into units of U tokens (U a multiple of the page size,
-//    chosen on the host so that the grid has a few thousand workgroups). A
-//    plan kernel turns the token counts into the running unit count
-//    unit_end[s] and the sequence of every unit, so a workgroup finds its
-//    sequence with one load.
+//    chosen on the host so that the grid has one to a few thousand
+//    workgroups). Up to kAttnFusedSeqs sequences every workgroup rebuilds the
+//    running unit count unit_end[s] in LDS from the token counts and finds
+//    its sequence by binary search there; beyond that a plan kernel writes
+//    unit_end and the sequence of every unit to the workspace.
 //  * Workgroup (unit, head group) covers up to 256 / (D / 8) kv heads. D / 8
 //    lanes hold one head row (16 bytes each: 8 fp16/bf16 values), so one
 //    token's row of those heads is one contiguous read. When the kv heads do
@@ -63,6 +64,8 @@ struct AArgs {
     float *out;        // [S][Hq][D]
     uint32_t num_seqs, page_size, num_kv_heads, num_q_heads, head_dim;
     uint32_t unit_tokens, unit_pages, heads_per_group, token_lanes;
+    uint32_t cap_units;
+    uint32_t fused;    // the unit table is rebuilt in LDS (no plan kernel)
     float qscale;      // softmax scale * log2(e)
     Div div_page;
 };
@@ -106,8 +109,17 @@ __device__ __forceinline__ float dpp(float x) {
 // Sum over the LPH lanes of a lane group (aligned groups of LPH lanes); every
 // lane of the group gets the same value, since each step adds a lane's value
 // to its partner's and IEEE addition is commutative.
-template <int LPH>
+template <int LPH, bool SHFL>
 __device__ __forceinline__ float group_sum(float x) {
+    if constexpr (SHFL) {
+        // through the LDS crossbar, beside the VALU: measured faster with one
+        // query head per kv head, where few independent sums can hide the DPP
+        // hazards
+#pragma unroll
+        for (int o = LPH / 2; o >= 1; o >>= 1)
+            x += __shfl_xor(x, o, 64);
+        return x;
+    }
     if constexpr (LPH >= 2)
         x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
     if constexpr (LPH >= 4)
@@ -153,6 +165,47 @@ constexpr int batch_tokens() {
     return G <= 2 ? 8 : (G == 4 ? 4 : HP_ATTN_BATCH_LARGE_GROUP);
 }
 
+// Units of sequence s: ceil(L_s / U).
+template <typename IdxT>
+__device__ __forceinline__ uint32_t units_of_seq(const void *seq_lens, uint32_t s, uint32_t U) {
+    const uint64_t len = ld_idx<IdxT>(seq_lens, s);
+    return (uint32_t)(len / U + (len % U != 0));
+}
+
+// unit_end[s] for all S sequences into LDS (inclusive running unit count,
+// capped at cap), by the whole workgroup: each thread sums a contiguous run
+// of sequences, a shuffle scan per wave and the wave totals through LDS give
+// each run's start. Ends with a barrier.
+template <typename IdxT>
+__device__ __forceinline__ void unit_scan_lds(const void *seq_lens, uint32_t S, uint32_t U,
+                                              uint32_t cap, uint32_t *ue) {
+    __shared__ uint32_t wave_sum[kAttnThreads / 64];
+    const uint32_t per = (S + kAttnThreads - 1) / kAttnThreads;
+    const uint32_t i0 = min32(S, threadIdx.x * per), i1 = min32(S, i0 + per);
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t v = 0;
+    for (uint32_t i = i0; i < i1; ++i)
+        v += units_of_seq<IdxT>(seq_lens, i, U);
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o, 64);
+        if (lane >= (uint32_t)o)
+            incl += y;
+    }
+    if (lane == 63)
+        wave_sum[wave] = incl;
+    __syncthreads();
+    uint32_t run = incl - v;
+    for (uint32_t w = 0; w < wave; ++w)
+        run += wave_sum[w];
+    for (uint32_t i = i0; i < i1; ++i) {
+        run += units_of_seq<IdxT>(seq_lens, i, U);
+        ue[i] = min32(run, cap);
+    }
+    __syncthreads();
+}
+
 template <typename ET, typename IdxT, int LPH, int G, bool NT>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
     // No implicit multiply-add fusion: each fused step below is an explicit
@@ -163,12 +216,20 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
     constexpr uint32_t NG = kAttnThreads / LPH;  // lane groups
     constexpr uint32_t D = LPH * 8;
     extern __shared__ __align__(16) unsigned char lds[];
-    uint64_t *pages = reinterpret_cast<uint64_t *>(lds);                      // [unit_pages]
-    float *red = reinterpret_cast<float *>(lds + 8 * (size_t)a.unit_pages);  // token-lane merge
-
     const uint32_t S = a.num_seqs;
+    // LDS: [unit_end (fused)] [page IDs of the unit] [token-lane merge]
+    const size_t ue_bytes = a.fused ? ((4 * (size_t)S + 15) & ~(size_t)15) : 0;
+    uint32_t *ue_lds = reinterpret_cast<uint32_t *>(lds);
+    uint64_t *pages = reinterpret_cast<uint64_t *>(lds + ue_bytes);
+    float *red = reinterpret_cast<float *>(lds + ue_bytes + 8 * (size_t)a.unit_pages);
+    const uint32_t *unit_end = a.unit_end;
+    if (a.fused) {
+        unit_scan_lds<IdxT>(a.seq_lens, S, a.unit_tokens, a.cap_units, ue_lds);
+        unit_end = ue_lds;
+    }
+
     const uint32_t g = blockIdx.x;
-    const uint32_t total = uni(a.unit_end[S - 1]);
+    const uint32_t total = uni(unit_end[S - 1]);
     const uint32_t Hq = a.num_q_heads, Hkv = a.num_kv_heads, P = a.page_size;
     const uint32_t hpw = a.heads_per_group;
     const uint32_t hq0 = blockIdx.y * hpw * G;  // this group's first query head
@@ -184,11 +245,26 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
             o[e] = 0.0f;
         return;
     }
-    const uint32_t s = uni(a.unit_seq[g]);
-    const uint32_t u0 = s ? uni(a.unit_end[s - 1]) : 0;
+    uint32_t s;
+    if (a.fused) {
+        uint32_t lo = 0, hi = S - 1;  // first sequence whose units reach past g
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (ue_lds[mid] > g)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        s = uni(lo);
+    } else {
+        s = uni(a.unit_seq[g]);
+    }
+    const uint32_t u0 = s ? uni(unit_end[s - 1]) : 0;
     const uint64_t L = uni64(ld_idx<IdxT>(a.seq_lens, s));
     const uint64_t sp0 = uni64(ld_idx<IdxT>(a.seq_ptr, s));
     const uint64_t t0 = (uint64_t)(g - u0) * a.unit_tokens;  // a multiple of the page size
+    if (t0 >= L)
+        return;  // only when total_tokens disagrees with the counts: read nothing
     const uint32_t n = (uint32_t)min64(L - t0, a.unit_tokens);
     const uint64_t pg0 = t0 / a.page_size;
     const uint32_t npg = udiv32(n + a.page_size - 1, a.div_page);
@@ -243,7 +319,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
             for (int i = 0; i < TB; ++i) {
 #pragma unroll
                 for (int gi = 0; gi < G; ++gi) {
-                    const float dot = group_sum<LPH>(dot8<ET>(qp[gi], kq[i])) * a.qscale;
+                    const float dot = group_sum<LPH, G == 1>(dot8<ET>(qp[gi], kq[i])) * a.qscale;
                     x[gi][i] = ok[i] ? dot : -__builtin_inff();
                 }
             }
@@ -322,7 +398,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
         }
     }
 
-    const uint32_t units = uni(a.unit_end[s]) - u0;
+    const uint32_t units = uni(unit_end[s]) - u0;
     if (units == 1) {
         // the sequence's only unit: normalise and write the output directly
         if (active && tl == 0) {
@@ -415,21 +491,50 @@ __global__ __launch_bounds__(kAttnThreads) void attention_plan_kernel(const void
 }
 
 struct CArgs {
-    const uint32_t *unit_end;
+    const uint32_t *unit_end;  // null: count the units here (fused)
+    const void *seq_lens;
     const float *part_ml, *part_acc;
     float *out;
-    uint32_t num_q_heads, head_dim;
+    uint32_t num_q_heads, head_dim, unit_tokens, cap_units;
     Div div_d;
 };
+
+// [first, end) units of sequence s, counted by the workgroup from the token
+// counts (a block sum over the sequences before s) when there is no plan.
+template <typename IdxT>
+__device__ __forceinline__ void seq_units(const CArgs &c, uint32_t s, uint32_t &u0, uint32_t &u1) {
+    if (c.unit_end) {
+        u0 = s ? c.unit_end[s - 1] : 0;
+        u1 = c.unit_end[s];
+        return;
+    }
+    __shared__ uint32_t wave_sum[kAttnThreads / 64];
+    uint32_t v = 0;
+    for (uint32_t i = threadIdx.x; i < s; i += kAttnThreads)
+        v += units_of_seq<IdxT>(c.seq_lens, i, c.unit_tokens);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    if ((threadIdx.x & 63) == 0)
+        wave_sum[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t before = 0;
+    for (uint32_t w = 0; w < kAttnThreads / 64; ++w)
+        before += wave_sum[w];
+    u0 = min32(before, c.cap_units);
+    u1 = min32(before + units_of_seq<IdxT>(c.seq_lens, s, c.unit_tokens), c.cap_units);
+}
 
 // out[s][hq][d] of a sequence held by several units: the units' partial
 // results merged with max-shifted weights, then divided. One pass over the
 // units, kBatch at a time so that their loads are in flight together.
 // Sequences of zero or one unit were written by the attention kernel.
+template <typename IdxT>
 __global__ __launch_bounds__(kAttnThreads) void attention_combine_kernel(CArgs c) {
     constexpr uint32_t kBatch = 16;
     const uint32_t s = blockIdx.x;
-    const uint32_t u0 = s ? c.unit_end[s - 1] : 0, u1 = c.unit_end[s];
+    uint32_t u0, u1;
+    seq_units<IdxT>(c, s, u0, u1);
     if (u1 - u0 < 2)
         return;
     const uint32_t i = blockIdx.y * kAttnThreads + threadIdx.x;
@@ -475,7 +580,8 @@ hipError_t launch_attention_t(const AArgs &a, const AttentionShape &sh, bool nt,
                               hipStream_t stream) {
     const dim3 grid((uint32_t)(sh.cap_units + a.num_seqs), sh.head_groups);
     const uint32_t ng = kAttnThreads / LPH;
-    const size_t lds = 8 * (size_t)a.unit_pages +
+    const size_t lds = (a.fused ? ((4 * (size_t)a.num_seqs + 15) & ~(size_t)15) : 0) +
+                       8 * (size_t)a.unit_pages +
                        (sh.token_lanes > 1 ? 4 * (size_t)ng * (2 + LPH * 8) : 0);
     if (nt)
         hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, G, true>), grid, dim3(kAttnThreads),
@@ -534,7 +640,7 @@ WsLayout ws_layout(uint64_t S, uint64_t Hq, uint64_t D, uint64_t cap) {
 } // namespace
 
 AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
-                               uint32_t num_kv_heads, uint32_t head_dim) {
+                               uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads) {
     AttentionShape sh;
     const uint32_t lph = head_dim / 8;
     const uint32_t ng = kAttnThreads / lph;
@@ -543,7 +649,11 @@ AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_
     sh.head_groups = (num_kv_heads + sh.heads_per_group - 1) / sh.heads_per_group;
     // Pages to visit (at most), spread over about kAttnTargetGroups workgroups.
     const uint64_t pages = total_tokens / page_size + num_seqs;
-    uint64_t upages = (pages * sh.head_groups + kAttnTargetGroups - 1) / kAttnTargetGroups;
+    // one query head per kv head: few, long units; grouped heads (more
+    // arithmetic per byte) spread over more workgroups
+    const uint64_t target = num_q_heads == num_kv_heads ? kAttnTargetGroupsMha
+                                                        : kAttnTargetGroupsGqa;
+    uint64_t upages = (pages * sh.head_groups + target - 1) / target;
     if (upages < 1)
         upages = 1;
     if (upages > kAttnMaxUnitPages)
@@ -557,25 +667,29 @@ AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_
 uint64_t attention_workspace_bytes(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
                                    uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads) {
     const AttentionShape sh =
-        attention_shape(num_seqs, total_tokens, page_size, num_kv_heads, head_dim);
+        attention_shape(num_seqs, total_tokens, page_size, num_kv_heads, head_dim, num_q_heads);
     return ws_layout(num_seqs, num_q_heads, head_dim, sh.cap_units).end;
 }
 
 hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
     (void)hipGetLastError();  // clear errors left by earlier calls that are not ours
     const AttentionShape sh = attention_shape(job.num_seqs, job.total_tokens, job.page_size,
-                                              job.num_kv_heads, job.head_dim);
+                                              job.num_kv_heads, job.head_dim, job.num_q_heads);
     const WsLayout wl = ws_layout(job.num_seqs, job.num_q_heads, job.head_dim, sh.cap_units);
     unsigned char *ws = static_cast<unsigned char *>(job.workspace);
     uint32_t *unit_end = reinterpret_cast<uint32_t *>(ws + wl.unit_end);
     uint32_t *unit_seq = reinterpret_cast<uint32_t *>(ws + wl.unit_seq);
 
-    hipLaunchKernelGGL(job.idx64 ? attention_plan_kernel<uint64_t> : attention_plan_kernel<uint32_t>,
-                       dim3(1), dim3(kAttnThreads), 0, stream, job.seq_lens, job.num_seqs,
-                       sh.unit_tokens, (uint32_t)sh.cap_units, unit_end, unit_seq);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
+    const bool fused = job.num_seqs <= kAttnFusedSeqs;
+    hipError_t e = hipSuccess;
+    if (!fused) {
+        hipLaunchKernelGGL(job.idx64 ? attention_plan_kernel<uint64_t>
+                                     : attention_plan_kernel<uint32_t>,
+                           dim3(1), dim3(kAttnThreads), 0, stream, job.seq_lens, job.num_seqs,
+                           sh.unit_tokens, (uint32_t)sh.cap_units, unit_end, unit_seq);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
 
     AArgs a = {};
     a.k_pool = static_cast<const unsigned char *>(job.k_pool);
@@ -598,6 +712,8 @@ hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
     a.unit_pages = sh.unit_pages;
     a.heads_per_group = sh.heads_per_group;
     a.token_lanes = sh.token_lanes;
+    a.cap_units = (uint32_t)sh.cap_units;
+    a.fused = fused;
     a.qscale = job.scale * 1.4426950408889634f;  // log2(e)
     a.div_page = make_div(job.page_size);
     const uint32_t G = job.num_q_heads / job.num_kv_heads;
@@ -607,7 +723,10 @@ hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
         return e;
 
     CArgs c = {};
-    c.unit_end = unit_end;
+    c.unit_end = fused ? nullptr : unit_end;
+    c.seq_lens = job.seq_lens;
+    c.unit_tokens = sh.unit_tokens;
+    c.cap_units = (uint32_t)sh.cap_units;
     c.part_ml = a.part_ml;
     c.part_acc = a.part_acc;
     c.out = job.out;
@@ -615,7 +734,8 @@ hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
     c.head_dim = job.head_dim;
     c.div_d = make_div(job.head_dim);
     const uint32_t per_seq = job.num_q_heads * job.head_dim;
-    hipLaunchKernelGGL(attention_combine_kernel,
+    hipLaunchKernelGGL(job.idx64 ? attention_combine_kernel<uint64_t>
+                                 : attention_combine_kernel<uint32_t>,
                        dim3(job.num_seqs, (per_seq + kAttnThreads - 1) / kAttnThreads),
                        dim3(kAttnThreads), 0, stream, c);
     return hipGetLastError();

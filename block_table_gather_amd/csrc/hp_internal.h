@@ -126,11 +126,18 @@ struct ValidateJob {
 // Decode attention over a block-paged K/V cache (hp_attention.hip).
 // Workgroups aimed at per launch (a unit holds enough pages to reach about
 // this many), and the most pages one unit may hold.
-#ifndef HP_ATTN_TARGET_GROUPS
-#define HP_ATTN_TARGET_GROUPS 2048
+#ifndef HP_ATTN_TARGET_GROUPS_MHA
+#define HP_ATTN_TARGET_GROUPS_MHA 1024
 #endif
-constexpr uint64_t kAttnTargetGroups = HP_ATTN_TARGET_GROUPS;
+#ifndef HP_ATTN_TARGET_GROUPS_GQA
+#define HP_ATTN_TARGET_GROUPS_GQA 3072
+#endif
+constexpr uint64_t kAttnTargetGroupsMha = HP_ATTN_TARGET_GROUPS_MHA;
+constexpr uint64_t kAttnTargetGroupsGqa = HP_ATTN_TARGET_GROUPS_GQA;
 constexpr uint64_t kAttnMaxUnitPages = 256;
+// Up to this many sequences the attention kernels count units themselves
+// (unit table in LDS, 4 bytes per sequence); beyond it a plan kernel runs.
+constexpr uint32_t kAttnFusedSeqs = 4096;
 
 struct AttentionShape {
     uint32_t heads_per_group;  // kv heads of one workgroup
@@ -152,7 +159,7 @@ struct AttentionJob {
 };
 
 AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
-                               uint32_t num_kv_heads, uint32_t head_dim);
+                               uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads);
 uint64_t attention_workspace_bytes(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
                                    uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads);
 hipError_t launch_attention(const AttentionJob &job, hipStream_t stream);

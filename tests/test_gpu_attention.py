@@ -249,6 +249,24 @@ def test_attention_empty_and_short_sequences(hp):
     check(w, res, q, d, v_pool, 8, 0.088, what="short")
 
 
+def test_attention_many_sequences_plan_path(hp):
+    """More sequences than the attention kernels count themselves: the plan
+    kernel writes the unit table and the unit -> sequence map."""
+    rng = np.random.default_rng(1360)
+    S, P = 4600, 4
+    lens = rng.integers(0, 24, size=S).astype(np.uint32)
+    counts = (lens + P - 1) // P
+    K = int(counts.sum())
+    bt = rng.permutation(K + 7)[:K].astype(np.uint32)
+    sp = np.concatenate([[0], np.cumsum(counts)]).astype(np.uint32)
+    w = workloads.Workload("plan", "bf16", P, 2, 64, K + 7, np.uint32, bt, sp, lens, seed=1360)
+    say("attention plan path", w.describe())
+    d, v_pool, q = make_inputs(w, 2, 1361)
+    out = run(hp, d, v_pool, q, w, 0.125).cpu().numpy()
+    assert np.all(out[lens == 0] == 0)
+    check(w, out, q, d, v_pool, 2, 0.125, what="plan path")
+
+
 def test_attention_checked_rejects_bad_table(hp):
     w = workloads.random_small(1350, max_seqs=6, max_len=60, page_sizes=(16,), heads=(2,),
                                dims=(64,), dtypes=("f16",))
