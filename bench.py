@@ -63,6 +63,10 @@ TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -
 PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/prof_{d} -o {d} -- "
            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-reference-copies "
            "--copy-calibration")
+ATTN_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_attn_trace -o trace "
+                  "-- python3 bench.py --attention-only")
+ATTN_PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/prof_attn_{d} -o {d} -- "
+                "python3 bench.py --attention-only --kernel-reps 3 --copy-calibration")
 
 
 def kernel_source_hash():
@@ -253,6 +257,104 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir):
     print(json.dumps(traffic))
 
 
+def _csv_rows(d, pattern):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one {pattern} under {d}, found {files}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _calibration(rows, counter):
+    """Mean counter value of the three 1 GiB calibration copies (the runtime
+    copy kernel's largest grids in the run)."""
+    vals = [(int(r["Grid_Size"]), float(r["Counter_Value"])) for r in rows
+            if r["Counter_Name"] == counter and r["Kernel_Name"] == "__amd_rocclr_copyBuffer"]
+    g = max(x[0] for x in vals)
+    big = [v for gs, v in vals if gs == g]
+    if len(big) != 3:
+        raise SystemExit(f"expected the 3 calibration copies, found {len(big)}")
+    return sum(big) / 3
+
+
+def summarize_attention(trace_dir, fetch_dir, write_dir):
+    """Kernel durations and calibrated HBM traffic of the attention kernels
+    (bench.py --attention-only runs) into profiles/."""
+    import numpy as np
+    import workloads
+    algo = {}
+    for w, group in ((workloads.decode(), 1), (workloads.prefix(), 4)):
+        Hq = w.num_heads * group
+        algo[w.dtype] = (w.name, 2 * w.total_tokens * w.num_heads * w.head_dim * 2
+                         + w.num_seqs * Hq * w.head_dim * 6)
+    lines = ["# Kernel durations: decode attention through the block table (rocprofv3)", "",
+             "Command (from the repository root, on one MI355X):", "", f"    {ATTN_TRACE_CMD}", "",
+             "The decode batch (64 sequences, 32 kv heads x 128 f16, one query head per kv",
+             "head, streaming loads) and the prefix-sharing batch (256 sequences, 8 kv heads",
+             "x 128 bf16, 32 query heads), each called 21 times. Durations in microseconds;",
+             "the combine kernel's rows are per workload (grid size).", "",
+             "| kernel | calls | avg us | min us | max us | algorithmic GB | GB/s at avg |",
+             "|---|---|---|---|---|---|---|"]
+    trace = _csv_rows(trace_dir, "*kernel_trace.csv")
+    groups = {}
+    for r in trace:
+        if "attention" not in r["Kernel_Name"]:
+            continue
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    for (name, grid), ts in sorted(groups.items()):
+        gb = gbs = ""
+        if name.startswith("attention_kernel<"):
+            wl, nbytes = algo["bf16" if "BF16" in name else "f16"]
+            gb = f"{nbytes / 1e9:.4f}"
+            gbs = f"{nbytes / (np.mean(ts) * 1e3):.0f}"
+        lines.append(f"| `{name}` (grid {grid}) | {len(ts)} | {np.mean(ts):.1f} | {min(ts):.1f} | "
+                     f"{max(ts):.1f} | {gb} | {gbs} |")
+    with open(os.path.join(PROFILES, "attention_decode_prefix_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    fetch = _csv_rows(fetch_dir, "*counter_collection.csv")
+    write = _csv_rows(write_dir, "*counter_collection.csv")
+    ff = CALIBRATION_BYTES / (_calibration(fetch, "FETCH_SIZE") * 1024)
+    wf = CALIBRATION_BYTES / (_calibration(write, "WRITE_SIZE") * 1024)
+
+    def per_launch(rows, counter):
+        agg = {}
+        for r in rows:
+            if r["Counter_Name"] == counter and "attention" in r["Kernel_Name"]:
+                key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+                agg.setdefault(key, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    fk, wk = per_launch(fetch, "FETCH_SIZE"), per_launch(write, "WRITE_SIZE")
+    out = ["# HBM traffic per launch: attention kernels (rocprofv3 counters)", "",
+           "Two counter passes, each in its own run (commands from the repository root):", "",
+           f"    {ATTN_PMC_CMD.format(c='FETCH_SIZE', d='fetch')}",
+           f"    {ATTN_PMC_CMD.format(c='WRITE_SIZE', d='write')}", "",
+           "Calibrated with three plain 1 GiB device copies in the same runs: bytes =",
+           f"FETCH_SIZE x 1024 x {ff:.4f} and WRITE_SIZE x 1024 x {wf:.4f}. The counters see",
+           "the L2's traffic to the fabric, Infinity Cache hits included: the prefix batch's",
+           "64 shared pages are read by every sequence but mostly served by the caches.",
+           "Algorithmic bytes: every live K and V row read once (shared prefix pages once per",
+           "sequence), the queries read and the fp32 output written. The attention kernels'",
+           "writes are the per-unit partial results the combine kernel reads.", "",
+           "| kernel | read GB | write GB | algorithmic GB |", "|---|---|---|---|"]
+    for key in sorted(fk):
+        if key not in wk:
+            continue
+        name = key[0]
+        rb, wb = fk[key] * 1024 * ff, wk[key] * 1024 * wf
+        gb = ""
+        if name.startswith("attention_kernel<"):
+            gb = f"{algo['bf16' if 'BF16' in name else 'f16'][1] / 1e9:.4f}"
+        out.append(f"| `{name}` (grid {key[1]}) | {rb / 1e9:.4f} | {wb / 1e9:.4f} | {gb} |")
+    with open(os.path.join(PROFILES, "attention_decode_prefix_hbm_traffic.md"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(lines + [""] + out))
+
+
 # ---- batched moves (optional) ----------------------------------------------------
 
 def attention_extras(hp, torch, np, dev, stream, reps):
@@ -383,6 +485,16 @@ def batched_append(hp, torch, np, dev, stream, reps):
 
 # ---- the benchmark -------------------------------------------------------------
 
+def calibration_copies(torch, dev):
+    """Three plain 1 GiB device copies: the counter runs' calibration."""
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -399,9 +511,15 @@ def main():
     ap.add_argument("--no-reference-copies", action="store_true",
                     help="skip the identity-table gather and runtime copy (profiling runs)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"))
+    ap.add_argument("--attention-only", action="store_true",
+                    help="only the decode-attention measurements (profiling runs)")
+    ap.add_argument("--summarize-attention", nargs=3, metavar=("TRACE", "FETCH", "WRITE"))
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles)
+        return
+    if args.summarize_attention:
+        summarize_attention(*args.summarize_attention)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -417,6 +535,13 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.attention_only:
+        if args.copy_calibration:
+            calibration_copies(torch, dev)
+        stream = torch.cuda.current_stream(dev)
+        print(json.dumps({"attention": attention_extras(hp, torch, np, dev, stream,
+                                                        args.kernel_reps)}), flush=True)
+        return
     w = workloads.decode()
     T, S, K = w.total_tokens, w.num_seqs, w.num_block_entries
     H, D = w.num_heads, w.head_dim
@@ -482,12 +607,7 @@ def main():
             events.append(ev)
 
     if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+        calibration_copies(torch, dev)
 
     for _ in range(args.warmup):
         step(False)

@@ -537,21 +537,23 @@ __global__ __launch_bounds__(kAttnThreads) void attention_combine_kernel(CArgs c
     seq_units<IdxT>(c, s, u0, u1);
     if (u1 - u0 < 2)
         return;
-    const uint32_t i = blockIdx.y * kAttnThreads + threadIdx.x;
+    // each thread: 4 consecutive outputs of one query head (head_dim % 8 == 0)
+    const uint32_t i = (blockIdx.y * kAttnThreads + threadIdx.x) * 4;
     const uint32_t Hq = c.num_q_heads, D = c.head_dim;
     if (i >= Hq * D)
         return;
     const uint32_t hq = udiv32(i, c.div_d), d = i - hq * D;
-    float M = -__builtin_inff(), lsum = 0.0f, num = 0.0f;
+    float M = -__builtin_inff(), lsum = 0.0f, num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (uint32_t ub = u0; ub < u1; ub += kBatch) {
-        float mv[kBatch], lv[kBatch], av[kBatch];
+        float mv[kBatch], lv[kBatch];
+        u32x4 av[kBatch];
 #pragma unroll
         for (uint32_t k = 0; k < kBatch; ++k) {
             const uint32_t u = ub + k < u1 ? ub + k : u1 - 1;  // repeats get weight 0 below
             const uint64_t idx = (uint64_t)u * Hq + hq;
             mv[k] = c.part_ml[2 * idx];
             lv[k] = c.part_ml[2 * idx + 1];
-            av[k] = c.part_acc[idx * D + d];
+            av[k] = *reinterpret_cast<const u32x4 *>(c.part_acc + idx * D + d);
         }
         float Mn = M;
 #pragma unroll
@@ -559,16 +561,28 @@ __global__ __launch_bounds__(kAttnThreads) void attention_combine_kernel(CArgs c
             Mn = __builtin_fmaxf(Mn, mv[k]);
         const float cs = exp2_hw(M - Mn);  // M = -inf on the first batch: 0
         lsum *= cs;
-        num *= cs;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            num[e] *= cs;
 #pragma unroll
         for (uint32_t k = 0; k < kBatch; ++k) {
             const float w = ub + k < u1 ? exp2_hw(mv[k] - Mn) : 0.0f;
+            float a4[4];
+            __builtin_memcpy(a4, &av[k], 16);
             lsum = __builtin_fmaf(lv[k], w, lsum);
-            num = __builtin_fmaf(av[k], w, num);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                num[e] = __builtin_fmaf(a4[e], w, num[e]);
         }
         M = Mn;
     }
-    c.out[(uint64_t)s * Hq * D + i] = num / lsum;
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        o[e] = num[e] / lsum;
+    u32x4 ov;
+    __builtin_memcpy(&ov, o, 16);
+    *reinterpret_cast<u32x4 *>(c.out + (uint64_t)s * Hq * D + i) = ov;
 }
 
 // ---- host side ----------------------------------------------------------------
@@ -733,7 +747,7 @@ hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
     c.num_q_heads = job.num_q_heads;
     c.head_dim = job.head_dim;
     c.div_d = make_div(job.head_dim);
-    const uint32_t per_seq = job.num_q_heads * job.head_dim;
+    const uint32_t per_seq = job.num_q_heads * job.head_dim / 4;  // 4 outputs per thread
     hipLaunchKernelGGL(job.idx64 ? attention_combine_kernel<uint64_t>
                                  : attention_combine_kernel<uint32_t>,
                        dim3(job.num_seqs, (per_seq + kAttnThreads - 1) / kAttnThreads),
