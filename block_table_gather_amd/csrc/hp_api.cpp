@@ -672,9 +672,6 @@ hp_status check_attention(const hp_desc *d, uint32_t num_q_heads) {
         return HP_ERR_ARG;
     if (!num_q_heads || num_q_heads % d->num_heads)
         return HP_ERR_ARG;
-    const uint32_t G = num_q_heads / d->num_heads;
-    if (G != 1 && G != 2 && G != 4 && G != 8)
-        return HP_ERR_ARG;
     // grid limits: grid x = units + num_seqs, grid y = head groups; Hq * D
     // indexes one sequence's output in 32 bits
     if (d->page_size > 65536 || d->num_seqs >= (1ull << 31) ||
@@ -683,7 +680,8 @@ hp_status check_attention(const hp_desc *d, uint32_t num_q_heads) {
     const hp::AttentionShape sh =
         hp::attention_shape(d->num_seqs, d->total_tokens, d->page_size, d->num_heads, D,
                             num_q_heads);
-    if (sh.cap_units + d->num_seqs >= (1ull << 31) || sh.head_groups > 65535)
+    if (sh.cap_units + d->num_seqs >= (1ull << 31) || sh.head_groups > 65535 ||
+        (num_q_heads / d->num_heads + 7) / 8 > 65535)
         return HP_ERR_ARG;
     return HP_OK;
 }

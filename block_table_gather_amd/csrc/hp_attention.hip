@@ -19,7 +19,8 @@
 //    running unit count unit_end[s] in LDS from the token counts and finds
 //    its sequence by binary search there; beyond that a plan kernel writes
 //    unit_end and the sequence of every unit to the workspace.
-//  * Workgroup (unit, head group) covers up to 256 / (D / 8) kv heads. D / 8
+//  * Workgroup (unit, head group, query chunk) covers up to 256 / (D / 8) kv
+//    heads and up to 8 of each kv head's query heads. D / 8
 //    lanes hold one head row (16 bytes each: 8 fp16/bf16 values), so one
 //    token's row of those heads is one contiguous read. When the kv heads do
 //    not fill the workgroup, the spare lane groups take other tokens of the
@@ -65,6 +66,7 @@ struct AArgs {
     uint32_t num_seqs, page_size, num_kv_heads, num_q_heads, head_dim;
     uint32_t unit_tokens, unit_pages, heads_per_group, token_lanes;
     uint32_t cap_units;
+    uint32_t group;    // G: query heads per kv head (any positive value)
     uint32_t fused;    // the unit table is rebuilt in LDS (no plan kernel)
     float qscale;      // softmax scale * log2(e)
     Div div_page;
@@ -160,9 +162,9 @@ __device__ __forceinline__ float dot8(const uint32_t (&q)[4], const u32x4 &k) {
 #ifndef HP_ATTN_BATCH_LARGE_GROUP
 #define HP_ATTN_BATCH_LARGE_GROUP 4
 #endif
-template <int G>
+template <int GT>
 constexpr int batch_tokens() {
-    return G <= 2 ? 8 : (G == 4 ? 4 : HP_ATTN_BATCH_LARGE_GROUP);
+    return GT <= 2 ? 8 : (GT == 4 ? 4 : HP_ATTN_BATCH_LARGE_GROUP);
 }
 
 // Units of sequence s: ceil(L_s / U).
@@ -206,13 +208,15 @@ __device__ __forceinline__ void unit_scan_lds(const void *seq_lens, uint32_t S, 
     __syncthreads();
 }
 
-template <typename ET, typename IdxT, int LPH, int G, bool NT>
+// GT query-head slots per lane group (1, 2, 4 or 8 >= G, or 8 with grid z
+// chunks of 8 query heads when G > 8); slots past G are computed and dropped.
+template <typename ET, typename IdxT, int LPH, int GT, bool NT>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
     // No implicit multiply-add fusion: each fused step below is an explicit
     // fma, and a score must round before its max is subtracted, so that the
     // largest score weighs exactly exp2(0) = 1.
 #pragma clang fp contract(off)
-    constexpr int TB = batch_tokens<G>();
+    constexpr int TB = batch_tokens<GT>();
     constexpr uint32_t NG = kAttnThreads / LPH;  // lane groups
     constexpr uint32_t D = LPH * 8;
     extern __shared__ __align__(16) unsigned char lds[];
@@ -231,14 +235,15 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
     const uint32_t g = blockIdx.x;
     const uint32_t total = uni(unit_end[S - 1]);
     const uint32_t Hq = a.num_q_heads, Hkv = a.num_kv_heads, P = a.page_size;
-    const uint32_t hpw = a.heads_per_group;
+    const uint32_t hpw = a.heads_per_group, G = a.group;
     const uint32_t hq0 = blockIdx.y * hpw * G;  // this group's first query head
     const uint32_t nq = (min32(Hkv, (blockIdx.y + 1) * hpw) - blockIdx.y * hpw) * G;
+    const uint32_t gz = blockIdx.z * GT;          // first slot's offset in the kv head's group
     if (g >= total) {
         // spare workgroups: workgroup total + s writes the zeros of sequence s
         // when it has no token (no unit would write them)
         const uint32_t se = g - total;
-        if (se >= S || ld_idx<IdxT>(a.seq_lens, se) != 0)
+        if (se >= S || blockIdx.z != 0 || ld_idx<IdxT>(a.seq_lens, se) != 0)
             return;
         float *o = a.out + ((uint64_t)se * Hq + hq0) * D;
         for (uint32_t e = threadIdx.x; e < nq * D; e += kAttnThreads)
@@ -279,9 +284,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
     const uint32_t h = blockIdx.y * hpw + hl;
     const bool active = tl < TL && h < Hkv;
 
-    float m[G], l[G], acc[G][8];
+    float m[GT], l[GT], acc[GT][8];
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
+    for (int gi = 0; gi < GT; ++gi) {
         m[gi] = -__builtin_inff();
         l[gi] = 0.0f;
 #pragma unroll
@@ -290,10 +295,11 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
     }
 
     if (active) {
-        uint32_t qp[G][4];  // the query's 8 elements of this lane, packed as stored
+        uint32_t qp[GT][4];  // the query's 8 elements of this lane, packed as stored
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) {
-            const uint64_t qo = (((uint64_t)s * Hq + (uint64_t)h * G + gi) * D + r * 8) * 2;
+        for (int gi = 0; gi < GT; ++gi) {
+            const uint32_t c = min32(gz + gi, G - 1);  // slots past G repeat the last head
+            const uint64_t qo = (((uint64_t)s * Hq + (uint64_t)h * G + c) * D + r * 8) * 2;
             const u32x4 v = ld16<false>(a.q + qo);
             __builtin_memcpy(qp[gi], &v, 16);
         }
@@ -314,18 +320,18 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
                 kq[i] = ld16<NT>(a.k_pool + off);
                 vq[i] = ld16<NT>(a.v_pool + off);
             }
-            float x[G][TB];
+            float x[GT][TB];
 #pragma unroll
             for (int i = 0; i < TB; ++i) {
 #pragma unroll
-                for (int gi = 0; gi < G; ++gi) {
-                    const float dot = group_sum<LPH, G == 1>(dot8<ET>(qp[gi], kq[i])) * a.qscale;
+                for (int gi = 0; gi < GT; ++gi) {
+                    const float dot = group_sum<LPH, GT == 1>(dot8<ET>(qp[gi], kq[i])) * a.qscale;
                     x[gi][i] = ok[i] ? dot : -__builtin_inff();
                 }
             }
-            float p[G][TB];
+            float p[GT][TB];
 #pragma unroll
-            for (int gi = 0; gi < G; ++gi) {
+            for (int gi = 0; gi < GT; ++gi) {
                 float mx = m[gi];
 #pragma unroll
                 for (int i = 0; i < TB; ++i)
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
                 float vf[8];
                 unpack8<ET>(vq[i], vf);
 #pragma unroll
-                for (int gi = 0; gi < G; ++gi)
+                for (int gi = 0; gi < GT; ++gi)
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         acc[gi][e] = __builtin_fmaf(p[gi][i], vf[e], acc[gi][e]);
@@ -362,7 +368,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
         float *rml = red;                  // [NG][2]
         float *racc = red + 2 * NG;        // [NG][D]
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) {
+        for (int gi = 0; gi < GT; ++gi) {
+            if (gz + gi >= G)
+                break;  // uniform: slots past G are not merged
             if (active && tl > 0) {
                 if (r == 0) {
                     rml[2 * lg] = m[gi];
@@ -403,8 +411,10 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
         // the sequence's only unit: normalise and write the output directly
         if (active && tl == 0) {
 #pragma unroll
-            for (int gi = 0; gi < G; ++gi) {
-                float *dst = a.out + ((uint64_t)s * Hq + (uint64_t)h * G + gi) * D + r * 8;
+            for (int gi = 0; gi < GT; ++gi) {
+                if (gz + gi >= G)
+                    break;
+                float *dst = a.out + ((uint64_t)s * Hq + (uint64_t)h * G + gz + gi) * D + r * 8;
                 float o[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
@@ -421,8 +431,10 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
 
     if (active && tl == 0) {
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) {
-            const uint64_t idx = (uint64_t)g * Hq + (uint64_t)h * G + gi;
+        for (int gi = 0; gi < GT; ++gi) {
+            if (gz + gi >= G)
+                break;
+            const uint64_t idx = (uint64_t)g * Hq + (uint64_t)h * G + gz + gi;
             float *dst = a.part_acc + idx * D + r * 8;
             u32x4 lo, hi;
             __builtin_memcpy(&lo, &acc[gi][0], 16);
@@ -587,21 +599,25 @@ __global__ __launch_bounds__(kAttnThreads) void attention_combine_kernel(CArgs c
 
 // ---- host side ----------------------------------------------------------------
 
+// Query-head slots per lane group for G query heads per kv head.
+uint32_t group_slots(uint32_t G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
+
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-template <typename ET, typename IdxT, int LPH, int G>
+template <typename ET, typename IdxT, int LPH, int GT>
 hipError_t launch_attention_t(const AArgs &a, const AttentionShape &sh, bool nt,
                               hipStream_t stream) {
-    const dim3 grid((uint32_t)(sh.cap_units + a.num_seqs), sh.head_groups);
+    const dim3 grid((uint32_t)(sh.cap_units + a.num_seqs), sh.head_groups,
+                    (a.group + GT - 1) / GT);
     const uint32_t ng = kAttnThreads / LPH;
     const size_t lds = (a.fused ? ((4 * (size_t)a.num_seqs + 15) & ~(size_t)15) : 0) +
                        8 * (size_t)a.unit_pages +
                        (sh.token_lanes > 1 ? 4 * (size_t)ng * (2 + LPH * 8) : 0);
     if (nt)
-        hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, G, true>), grid, dim3(kAttnThreads),
+        hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, GT, true>), grid, dim3(kAttnThreads),
                            lds, stream, a);
     else
-        hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, G, false>), grid, dim3(kAttnThreads),
+        hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, GT, false>), grid, dim3(kAttnThreads),
                            lds, stream, a);
     return hipGetLastError();
 }
@@ -609,7 +625,7 @@ hipError_t launch_attention_t(const AArgs &a, const AttentionShape &sh, bool nt,
 template <typename ET, typename IdxT, int LPH>
 hipError_t launch_attention_g(const AArgs &a, const AttentionShape &sh, uint32_t G, bool nt,
                               hipStream_t st) {
-    switch (G) {
+    switch (group_slots(G)) {
     case 1: return launch_attention_t<ET, IdxT, LPH, 1>(a, sh, nt, st);
     case 2: return launch_attention_t<ET, IdxT, LPH, 2>(a, sh, nt, st);
     case 4: return launch_attention_t<ET, IdxT, LPH, 4>(a, sh, nt, st);
@@ -668,6 +684,12 @@ AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_
     const uint64_t target = num_q_heads == num_kv_heads ? kAttnTargetGroupsMha
                                                         : kAttnTargetGroupsGqa;
     uint64_t upages = (pages * sh.head_groups + target - 1) / target;
+    // each unit writes (D + 2) floats per query head it covers: keep that a
+    // small share of the unit's K/V bytes (2 D per token and kv head)
+    const uint64_t min_tokens = kAttnMinUnitTokensPerSlot * group_slots(num_q_heads / num_kv_heads);
+    const uint64_t min_pages = (min_tokens + page_size - 1) / page_size;
+    if (upages < min_pages)
+        upages = min_pages;
     if (upages < 1)
         upages = 1;
     if (upages > kAttnMaxUnitPages)
@@ -727,6 +749,7 @@ hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
     a.heads_per_group = sh.heads_per_group;
     a.token_lanes = sh.token_lanes;
     a.cap_units = (uint32_t)sh.cap_units;
+    a.group = job.num_q_heads / job.num_kv_heads;
     a.fused = fused;
     a.qscale = job.scale * 1.4426950408889634f;  // log2(e)
     a.div_page = make_div(job.page_size);

@@ -135,6 +135,11 @@ struct ValidateJob {
 constexpr uint64_t kAttnTargetGroupsMha = HP_ATTN_TARGET_GROUPS_MHA;
 constexpr uint64_t kAttnTargetGroupsGqa = HP_ATTN_TARGET_GROUPS_GQA;
 constexpr uint64_t kAttnMaxUnitPages = 256;
+// Smallest unit, in tokens per query-head slot of a lane group.
+#ifndef HP_ATTN_MIN_UNIT_TOKENS_PER_SLOT
+#define HP_ATTN_MIN_UNIT_TOKENS_PER_SLOT 8
+#endif
+constexpr uint64_t kAttnMinUnitTokensPerSlot = HP_ATTN_MIN_UNIT_TOKENS_PER_SLOT;
 // Up to this many sequences the attention kernels count units themselves
 // (unit table in LDS, 4 bytes per sequence); beyond it a plan kernel runs.
 constexpr uint32_t kAttnFusedSeqs = 4096;

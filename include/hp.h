@@ -304,7 +304,7 @@ hp_status hp_copy_pages_batch(const hp_desc *desc, uint32_t num_pools, void *con
  *           ([Hurray] Description: one descriptor per kv_role), 64-byte aligned.
  * q         DEVICE [num_seqs, num_q_heads, head_dim] of the pool's dtype,
  *           16-byte aligned.
- * num_q_heads  a multiple G of num_heads with G in {1, 2, 4, 8}.
+ * num_q_heads  a multiple G of num_heads (any G >= 1).
  * scale     the softmax scale (1/sqrt(head_dim) in the usual form).
  * out       DEVICE [num_seqs, num_q_heads, head_dim] fp32 (out_dtype
  *           HP_DTYPE_F32), 16-byte aligned.

@@ -214,7 +214,6 @@ def test_attention_rejections():
     assert attn(desc(head_dim=24)) == S["HP_ERR_ARG"]              # not a supported width
     assert attn(desc(head_dim=512)) == S["HP_ERR_ARG"]
     assert attn(f, hq=6) == S["HP_ERR_ARG"]                        # not a multiple of 4 kv heads
-    assert attn(f, hq=12) == S["HP_ERR_ARG"]                       # group 3
     assert attn(f, hq=0) == S["HP_ERR_ARG"]
     assert attn(desc(page_size=1 << 17)) == S["HP_ERR_ARG"]
     assert attn(f, flags=hp.HP_FLAG_ZERO_TAIL) == S["HP_ERR_ARG"]
@@ -240,6 +239,8 @@ def test_attention_workspace_bytes():
     assert L.hp_attention_workspace_bytes(None, 8) == 0
     assert L.hp_attention_workspace_bytes(ctypes.byref(desc(dtype=hp.DTYPE["i8"])), 8) == 0
     assert L.hp_attention_workspace_bytes(ctypes.byref(f), 6) == 0
+    for hq in (4, 12, 20, 28, 44, 256):                            # any group size is accepted
+        assert L.hp_attention_workspace_bytes(ctypes.byref(f), hq) > 0
     a = L.hp_attention_workspace_bytes(ctypes.byref(f), 8)
     b = L.hp_attention_workspace_bytes(ctypes.byref(f), 16)
     assert 0 < a < b

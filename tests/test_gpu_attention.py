@@ -144,6 +144,11 @@ CASES = [
     ("bf16", 64, 1, 1, (2, 16)),       # one kv head: many token lanes
     ("f16", 256, 4, 5, (8,)),
     ("bf16", 8, 2, 64, (3,)),
+    ("f16", 128, 3, 4, (16,)),         # group sizes that are not a power of two
+    ("bf16", 64, 5, 2, (8,)),
+    ("f16", 128, 7, 4, (16,)),
+    ("bf16", 128, 12, 2, (16,)),       # more than 8 query heads per kv head: chunks of 8
+    ("f16", 32, 16, 1, (4,)),
 ]
 
 
