@@ -326,3 +326,24 @@ def test_attention_prefix_workload_gqa(hp):
     check(w, out, q, d, v_pool, 4, scale, seqs=_sample(w, 5, 1411), what="prefix")
     del d, v_pool
     torch.cuda.empty_cache()
+
+
+def test_attention_pools_beyond_4gib(hp):
+    """K and V pools of 150,000 pages x 16 x 8 x 128 bf16 (4.9 GB each) with a
+    uint64 table whose pages lie mostly past the 4 GiB byte offset: 64-bit row
+    offsets, 24 sequences against the oracle."""
+    rng = np.random.default_rng(1500)
+    N, P, H, D = 150_000, 16, 8, 128
+    lens = rng.integers(1, 700, size=24)
+    counts = (lens + P - 1) // P
+    high = rng.permutation(np.arange(140_000, N))[: int(counts.sum())]
+    high[::5] = rng.integers(0, 500, size=len(high[::5]))  # a few low pages too
+    w = workloads.Workload("pool5g", "bf16", P, H, D, N, np.uint64, high.astype(np.uint64),
+                           np.concatenate([[0], np.cumsum(counts)]).astype(np.uint64),
+                           lens.astype(np.uint64), seed=1500)
+    say("attention pools > 4 GiB", w.describe())
+    d, v_pool, q = make_inputs(w, 4, 1501)
+    out = run(hp, d, v_pool, q, w, 0.088, streaming=True).cpu().numpy()
+    check(w, out, q, d, v_pool, 4, 0.088, what="pools > 4 GiB")
+    del d, v_pool
+    torch.cuda.empty_cache()
