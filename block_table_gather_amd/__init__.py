@@ -266,13 +266,22 @@ def _workspace(desc, total_tokens, workspace):
     return ws.data_ptr(), n
 
 
-def validate(desc, total_tokens, seq_start=None, *, workspace=None, stream=None):
-    """Runs hp_validate; returns (status name, index). Synchronous."""
-    res = HpValidateResult()
+def validate(desc, total_tokens, seq_start=None, *, workspace=None, stream=None, result=None):
+    """Runs hp_validate; returns (status name, index). Synchronous.
+
+    result: optional 16-byte pinned host tensor to receive the result words
+    (the library writes small descriptors' results there directly);
+    default: a host struct."""
     p = desc.with_tokens(total_tokens)
     ws, n = _workspace(desc, total_tokens, workspace)
-    code = _lib.hp_validate(p, _ptr(seq_start), ws, n, ctypes.byref(res),
-                            _stream(stream, desc.device))
+    if result is None:
+        res = HpValidateResult()
+        res_p = ctypes.byref(res)
+    else:
+        assert result.numel() * result.element_size() == ctypes.sizeof(HpValidateResult)
+        res = HpValidateResult.from_address(result.data_ptr())
+        res_p = ctypes.pointer(res)
+    code = _lib.hp_validate(p, _ptr(seq_start), ws, n, res_p, _stream(stream, desc.device))
     name = STATUS.get(code, str(code))
     if name == "HP_ERR_HIP":
         raise HpError(code, "hp_validate")

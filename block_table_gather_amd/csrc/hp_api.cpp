@@ -133,14 +133,22 @@ hp_status run_validate(const hp_desc *d, const void *seq_start, void *ws,
     j.seq_lens = d->seq_lens;
     j.seq_start = seq_start;
     j.workspace = ws;
+    // The two result words land in the caller's result struct (16 bytes, like
+    // them) and are decoded in place after the wait. When the struct is
+    // pinned host memory the GPU can reach, a small descriptor's check writes
+    // them there itself; otherwise they are copied from the workspace.
+    static_assert(sizeof(hp_validate_result) == 2 * sizeof(uint64_t), "result layout");
+    j.result = nullptr;
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, res) == hipSuccess && attr.type == hipMemoryTypeHost &&
+        attr.devicePointer)
+        j.result = attr.devicePointer;
+    (void)hipGetLastError();  // an unregistered pointer leaves an error behind
     hipError_t e = hp::launch_validate(j, stream);
     if (e != hipSuccess)
         return hip_failed(e);
-    // The two result words are copied straight into the caller's result
-    // struct (16 bytes, like them), so that a result in pinned host memory
-    // takes a direct DMA; they are decoded in place after the wait.
-    static_assert(sizeof(hp_validate_result) == 2 * sizeof(uint64_t), "result layout");
-    if ((e = hipMemcpyAsync(res, ws, sizeof(hp_validate_result), hipMemcpyDeviceToHost,
+    if (!hp::validate_writes_result(j) &&
+        (e = hipMemcpyAsync(res, ws, sizeof(hp_validate_result), hipMemcpyDeviceToHost,
                             stream)) != hipSuccess)
         return hip_failed(e);
     if ((e = hipStreamSynchronize(stream)) != hipSuccess)

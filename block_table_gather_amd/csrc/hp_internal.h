@@ -121,7 +121,18 @@ struct ValidateJob {
     uint64_t num_pages, page_size, num_seqs, num_block_entries;
     const void *block_table, *seq_ptr, *seq_lens, *seq_start;
     void *workspace; // >= 16 bytes: [0] min key, [1] token sum
+    // Where the two words go when one workgroup does the whole check
+    // (descriptors of at most kValidateOneItems items): device-visible
+    // pinned host memory, or null for the workspace.
+    void *result;
 };
+constexpr uint64_t kValidateOneItems = 1 << 16;
+// True when launch_validate writes the words to job.result itself.
+inline bool validate_writes_result(const ValidateJob &job) {
+    const uint64_t n = job.num_block_entries > job.num_seqs + 1 ? job.num_block_entries
+                                                                 : job.num_seqs + 1;
+    return job.result && n <= kValidateOneItems;
+}
 
 // Decode attention over a block-paged K/V cache (hp_attention.hip).
 // Workgroups aimed at per launch (a unit holds enough pages to reach about

@@ -747,6 +747,44 @@ __device__ __forceinline__ unsigned long long vkey(uint64_t rank, uint64_t index
     return (rank << kKeyShift) | index;
 }
 
+// The checks that name item i (of max(K, S + 1) items), folded into the
+// thread's smallest (check, index) key and its token sum.
+template <typename IdxT>
+__device__ __forceinline__ void validate_item(const VArgs &a, uint64_t i, unsigned long long &key,
+                                              unsigned long long &sum) {
+    const uint64_t S = a.num_seqs, K = a.num_block_entries;
+    if (i == 0) {
+        if (ld_idx<IdxT>(a.seq_ptr, 0) != 0)
+            key = min64(key, vkey(kRankSeqPtrFirst, 0));
+        if (ld_idx<IdxT>(a.seq_ptr, S) != K)
+            key = min64(key, vkey(kRankSeqPtrLast, S));
+    }
+    if (i < S) {
+        const uint64_t p0 = ld_idx<IdxT>(a.seq_ptr, i), p1 = ld_idx<IdxT>(a.seq_ptr, i + 1);
+        if (p0 > p1)
+            key = min64(key, vkey(kRankSeqPtrOrder, i));
+        const uint64_t len = ld_idx<IdxT>(a.seq_lens, i);
+        const uint64_t st = a.seq_start ? ld_idx<IdxT>(a.seq_start, i) : 0;
+        if (p0 <= p1) {
+            const uint64_t slice = p1 - p0;
+            const uint64_t cap = __umul64hi(slice, a.page_size) ? ~0ull : slice * a.page_size;
+            if (st > cap || len > cap - st)
+                key = min64(key, vkey(kRankSeqLen, i));
+        }
+        sum += len;
+    }
+    if (i < K && ld_idx<IdxT>(a.block_table, i) >= a.num_pages)
+        key = min64(key, vkey(kRankPageRange, i));
+}
+
+__device__ __forceinline__ void wave_fold(unsigned long long &key, unsigned long long &sum) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        key = min64(key, (unsigned long long)__shfl_xor(key, off, 64));
+        sum += (unsigned long long)__shfl_xor(sum, off, 64);
+    }
+}
+
 // One pass over max(K, S+1) items. Each item evaluates the checks that name
 // its index; the smallest (check, index) key wins through atomicMin, which
 // makes the report independent of scheduling.
@@ -756,40 +794,44 @@ __global__ __launch_bounds__(256) void validate_kernel(VArgs a) {
     const uint64_t n = K > S + 1 ? K : S + 1;
     unsigned long long key = ~0ull, sum = 0;
     for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (uint64_t)gridDim.x * blockDim.x) {
-        if (i == 0) {
-            if (ld_idx<IdxT>(a.seq_ptr, 0) != 0)
-                key = min64(key, vkey(kRankSeqPtrFirst, 0));
-            if (ld_idx<IdxT>(a.seq_ptr, S) != K)
-                key = min64(key, vkey(kRankSeqPtrLast, S));
-        }
-        if (i < S) {
-            const uint64_t p0 = ld_idx<IdxT>(a.seq_ptr, i), p1 = ld_idx<IdxT>(a.seq_ptr, i + 1);
-            if (p0 > p1)
-                key = min64(key, vkey(kRankSeqPtrOrder, i));
-            const uint64_t len = ld_idx<IdxT>(a.seq_lens, i);
-            const uint64_t st = a.seq_start ? ld_idx<IdxT>(a.seq_start, i) : 0;
-            if (p0 <= p1) {
-                const uint64_t slice = p1 - p0;
-                const uint64_t cap = __umul64hi(slice, a.page_size) ? ~0ull : slice * a.page_size;
-                if (st > cap || len > cap - st)
-                    key = min64(key, vkey(kRankSeqLen, i));
-            }
-            sum += len;
-        }
-        if (i < K && ld_idx<IdxT>(a.block_table, i) >= a.num_pages)
-            key = min64(key, vkey(kRankPageRange, i));
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        key = min64(key, (unsigned long long)__shfl_xor(key, off, 64));
-        sum += (unsigned long long)__shfl_xor(sum, off, 64);
-    }
+         i += (uint64_t)gridDim.x * blockDim.x)
+        validate_item<IdxT>(a, i, key, sum);
+    wave_fold(key, sum);
     if ((threadIdx.x & 63) == 0) {
         if (key != ~0ull)
             atomicMin(&a.ws[0], key);
         if (sum)
             atomicAdd(&a.ws[1], sum);
+    }
+}
+
+// Small descriptors: one workgroup evaluates every item and writes both result
+// words itself, so no clearing kernel and no atomics are needed. `out` is
+// the workspace or pinned host memory; system-scope stores make the words
+// visible to the host once the kernel has finished.
+constexpr uint32_t kValidateOneThreads = 1024;
+template <typename IdxT>
+__global__ __launch_bounds__(kValidateOneThreads) void validate_one_kernel(VArgs a,
+                                                                           unsigned long long *out) {
+    __shared__ unsigned long long wkey[kValidateOneThreads / 64], wsum[kValidateOneThreads / 64];
+    const uint64_t S = a.num_seqs, K = a.num_block_entries;
+    const uint64_t n = K > S + 1 ? K : S + 1;
+    unsigned long long key = ~0ull, sum = 0;
+    for (uint64_t i = threadIdx.x; i < n; i += kValidateOneThreads)
+        validate_item<IdxT>(a, i, key, sum);
+    wave_fold(key, sum);
+    if ((threadIdx.x & 63) == 0) {
+        wkey[threadIdx.x >> 6] = key;
+        wsum[threadIdx.x >> 6] = sum;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (uint32_t w = 1; w < kValidateOneThreads / 64; ++w) {
+            key = min64(key, wkey[w]);
+            sum += wsum[w];
+        }
+        __hip_atomic_store(&out[0], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(&out[1], sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 }
 
@@ -1087,12 +1129,23 @@ hipError_t launch_validate(const ValidateJob &job, hipStream_t stream) {
     a.num_seqs = job.num_seqs;
     a.num_block_entries = job.num_block_entries;
     (void)hipGetLastError();  // see launch_copy
+    const uint64_t n = job.num_block_entries > job.num_seqs + 1 ? job.num_block_entries
+                                                                 : job.num_seqs + 1;
+    if (n <= kValidateOneItems) {
+        unsigned long long *out = static_cast<unsigned long long *>(job.result ? job.result
+                                                                               : job.workspace);
+        if (job.idx64)
+            hipLaunchKernelGGL(validate_one_kernel<uint64_t>, dim3(1), dim3(kValidateOneThreads),
+                               0, stream, a, out);
+        else
+            hipLaunchKernelGGL(validate_one_kernel<uint32_t>, dim3(1), dim3(kValidateOneThreads),
+                               0, stream, a, out);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(validate_init_kernel, dim3(1), dim3(64), 0, stream, a.ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const uint64_t n = job.num_block_entries > job.num_seqs + 1 ? job.num_block_entries
-                                                                 : job.num_seqs + 1;
     uint64_t blocks = (n + 255) / 256;
     if (blocks > 4096)
         blocks = 4096;

@@ -148,10 +148,12 @@ size_t hp_workspace_bytes(const hp_desc *desc);
  * The first failing check in that order is reported, with its smallest
  * failing index, so the result is deterministic. Aliased page IDs are
  * allowed ([Hurray] Prefix Sharing) and not checked.
- * Synchronous: enqueues on `stream`, copies 16 bytes back into *result and
- * waits for the stream. `result` is a host pointer and may be NULL; in pinned
- * host memory (hipHostMalloc) the copy back is a direct DMA, which saves
- * tens of microseconds per call. Returns result->code. */
+ * Synchronous: enqueues on `stream`, brings 16 bytes back into *result and
+ * waits for the stream. `result` is a host pointer and may be NULL. In pinned
+ * host memory (hipHostMalloc) a descriptor of at most 65,536 items (table
+ * entries or sequences) is checked by one workgroup that writes the result
+ * there itself, with no copy; otherwise the words are copied from the
+ * workspace. Returns result->code. */
 hp_status hp_validate(const hp_desc *desc, const void *seq_start, void *workspace,
                       size_t workspace_bytes, hp_validate_result *result,
                       void *stream);

@@ -307,10 +307,13 @@ NAMES = {"valid": "HP_OK", "seq_ptr_first": "HP_ERR_SEQPTR_FIRST",
          "total_tokens": "HP_ERR_TOTAL_TOKENS"}
 
 
+@pytest.mark.parametrize("pinned", [False, True])
 @pytest.mark.parametrize("seed", range(80))
-def test_validate_matches_oracle(hp, seed):
+def test_validate_matches_oracle(hp, seed, pinned):
+    """Pageable result: the words come through the workspace; pinned result:
+    the one-workgroup check writes them into host memory itself."""
     w, bt, sp, sl, T = _corrupt(seed)
-    say("validate", seed)
+    say("validate", seed, pinned)
     dt = w.index_dtype
     pool = torch.empty((max(w.num_pages, 1), w.page_size, w.num_heads, w.head_dim),
                        dtype=torch.float16, device=DEV)
@@ -319,7 +322,10 @@ def test_validate_matches_oracle(hp, seed):
     tsl = idx_tensor(np.array(sl, dtype=dt), DEV)
     tss = idx_tensor(w.seq_start.astype(dt), DEV) if w.seq_start is not None else None
     desc = hp.Descriptor(pool, tbt, tsp, tsl, num_pages=w.num_pages)
-    got = hp.validate(desc, T, tss)
+    result = None
+    if pinned:
+        result = torch.full((2,), -1, dtype=torch.int64, pin_memory=True)  # stale words
+    got = hp.validate(desc, T, tss, result=result)
     want = oracle.validate(rank=3, paged_axis=0, num_pages=w.num_pages, page_size=w.page_size,
                            block_table=bt, seq_ptr=sp, seq_lens=sl, total_tokens=T,
                            seq_start=w.seq_start)
@@ -338,3 +344,5 @@ def test_validate_large_block_table_first_index(hp):
     pool = torch.empty((1000, 4, 1, 16), dtype=torch.int8, device=DEV)
     desc = hp.Descriptor(pool, idx_tensor(bt, DEV), idx_tensor(sp, DEV), idx_tensor(sl, DEV))
     assert hp.validate(desc, K * 4) == ("HP_ERR_PAGE_RANGE", 123_457)
+    pinned = torch.zeros(2, dtype=torch.int64, pin_memory=True)
+    assert hp.validate(desc, K * 4, result=pinned) == ("HP_ERR_PAGE_RANGE", 123_457)
