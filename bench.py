@@ -57,6 +57,7 @@ KERNEL_LABELS = {
     "copy_kernel<unsigned int, (hp::Op)1, 16, true, true, -1>": "scatter (u32, 16 B vectors, fused, streamed source)",
     "copy_kernel<unsigned int, (hp::Op)1, 16, true, false, -1>": "scatter (u32, 16 B vectors, fused)",
     "copy_kernel<unsigned int, (hp::Op)2, 8, true, false, -1>": "dequant-gather (u32, 8 B int8 vectors, fused)",
+    "validate_one_kernel<unsigned int>": "validator, one workgroup (u32)",
     "validate_kernel<unsigned int>": "validator (u32)",
     "validate_init_kernel": "validator init",
 }
@@ -180,7 +181,10 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir):
             gather_avg = avg
         lines.append(f"| `{short}` | {KERNEL_LABELS[short]} | {r['Calls']} | {avg:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
-    lines += ["", "Other kernels in the trace are PyTorch's input generation (random values,",
+    lines += ["", "The validator runs on a second stream beside the moves (the next step's",
+              "check), so its durations include time it shares the GPU with them; alone it",
+              "takes the minimum shown.",
+              "", "Other kernels in the trace are PyTorch's input generation (random values,",
               "fills, index_put) and the runtime's copies; they are outside the timed step."]
     with open(os.path.join(PROFILES, "decode_step_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
