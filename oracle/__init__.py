@@ -85,6 +85,11 @@ def _load():
     lib.oracle_copy_pages.argtypes = [_vp, _u64, _u64, _u64, _u64, _vp, _vp, _vp, _u64]
     lib.oracle_payload.restype = ctypes.c_int
     lib.oracle_payload.argtypes = [_u64] * 7 + [_vp]
+    lib.oracle_quantize_row.restype = None
+    lib.oracle_quantize_row.argtypes = [_vp, _u64, ctypes.c_int, _vp, _vp, _vp]
+    lib.oracle_scatter_quant.restype = None
+    lib.oracle_scatter_quant.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_uint32, _u64, _u64, _u64,
+                                         _vp, _vp, _vp, _vp, _u64, ctypes.c_int]
     lib.oracle_decode.restype = None
     lib.oracle_decode.argtypes = [ctypes.c_uint32, _vp, _u64, _vp]
     lib.oracle_paged_attention.restype = ctypes.c_int
@@ -308,6 +313,38 @@ def paged_attention(q, k_pool, v_pool, elem_type, *, page_size, num_kv_heads, he
     if rc != 0:
         raise ValueError("num_q_heads must be a positive multiple of num_kv_heads")
     return out
+
+
+def quantize_row(x, asym=False):
+    """(codes, scale, zero point) of one row of float32 values (see
+    oracle_quantize_row): int8 codes, or uint8 codes and a zero point."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    q = np.empty(x.size, dtype=np.uint8 if asym else np.int8)
+    sc = np.zeros(1, dtype=np.float32)
+    zp = np.zeros(1, dtype=np.uint8)
+    _load().oracle_quantize_row(_ptr(x), x.size, int(asym), _ptr(q), _ptr(sc), _ptr(zp))
+    return q, np.float32(sc[0]), (int(zp[0]) if asym else None)
+
+
+def scatter_quant(pool, scales, src, src_type, *, page_size, num_heads, head_dim, block_table,
+                  seq_ptr, seq_lens, seq_start=None, zero_points=None, zero_tail=False):
+    """Quantize-on-scatter into copies of pool (int8, or uint8 with
+    zero_points), scales (float32 [N*P]) and zero_points (uint8 [N*P]);
+    returns (pool, scales, zero_points or None). src: [T, H, D] bit patterns
+    of src_type ("f16", "bf16", "f32")."""
+    lib = _load()
+    pool = np.array(pool, copy=True, order="C")
+    assert pool.dtype == (np.uint8 if zero_points is not None else np.int8)
+    sc = np.array(scales, dtype=np.float32, copy=True)
+    zp = None if zero_points is None else np.array(zero_points, dtype=np.uint8, copy=True)
+    src = np.ascontiguousarray(src)
+    bt, sp, sl = _idx(block_table), _idx(seq_ptr), _idx(seq_lens)
+    ss = None if seq_start is None else _idx(seq_start)
+    lib.oracle_scatter_quant(_ptr(pool), _ptr(sc), _ptr(zp), _ptr(src) if src.size else None,
+                             FLOAT_TYPES[src_type], page_size, num_heads, head_dim,
+                             _ptr(bt) if len(bt) else None, _ptr(sp), _ptr(sl) if len(sl) else None,
+                             _ptr(ss), len(sl), int(zero_tail))
+    return pool, sc, zp
 
 
 PAYLOAD_FIELDS = ("reserved_pages", "active_pages", "allocated_slots", "live_slots",

@@ -530,6 +530,111 @@ int oracle_paged_attention(const void *q, const void *k_pool, const void *v_pool
     return 0;
 }
 
+/* One binary32 value as rint would give it, clamped to [lo, hi] (exact: the
+ * bounds are integers). */
+static float clamp_rint(float v, float lo, float hi)
+{
+    float r = rintf(v);
+    return r < lo ? lo : (r > hi ? hi : r);
+}
+
+void oracle_quantize_row(const float *x, uint64_t n, int asym, void *q, float *scale,
+                         uint8_t *zero_point)
+{
+    uint64_t i;
+    if (!asym) {
+        int8_t *out = (int8_t *)q;
+        float amax = 0.0f, sc;
+        for (i = 0; i < n; i++) {
+            float a = fabsf(x[i]);
+            if (a > amax)
+                amax = a;
+        }
+        sc = amax / 127.0f;
+        *scale = sc;
+        for (i = 0; i < n; i++)
+            out[i] = sc == 0.0f ? 0 : (int8_t)clamp_rint(x[i] / sc, -127.0f, 127.0f);
+    } else {
+        uint8_t *out = (uint8_t *)q;
+        float lo = 0.0f, hi = 0.0f, sc, z;
+        for (i = 0; i < n; i++) {
+            if (x[i] < lo)
+                lo = x[i];
+            if (x[i] > hi)
+                hi = x[i];
+        }
+        sc = (hi - lo) / 255.0f;
+        z = sc == 0.0f ? 0.0f : clamp_rint(-lo / sc, 0.0f, 255.0f);
+        *scale = sc;
+        *zero_point = (uint8_t)z;
+        for (i = 0; i < n; i++) {
+            if (sc == 0.0f) {
+                out[i] = 0;
+            } else {
+                float c = rintf(x[i] / sc) + z; /* small integers: exact */
+                out[i] = (uint8_t)(c < 0.0f ? 0.0f : (c > 255.0f ? 255.0f : c));
+            }
+        }
+    }
+}
+
+void oracle_scatter_quant(void *page_pool, float *scales, uint8_t *zero_points,
+                          const void *src, uint32_t src_type, uint64_t page_size,
+                          uint64_t num_heads, uint64_t head_dim, const uint64_t *block_table,
+                          const uint64_t *seq_ptr, const uint64_t *seq_lens,
+                          const uint64_t *seq_start, uint64_t num_seqs, int zero_tail)
+{
+    unsigned char *pool = (unsigned char *)page_pool;
+    const uint64_t n = num_heads * head_dim;
+    float *x = (float *)malloc((n ? n : 1) * sizeof(float));
+    unsigned char *codes = (unsigned char *)malloc(n ? n : 1);
+    uint64_t row = 0;
+    uint64_t s, i, h, d, e;
+
+    if (!x || !codes) {
+        free(x);
+        free(codes);
+        return;
+    }
+    for (s = 0; s < num_seqs; s++) {
+        uint64_t start = seq_start ? seq_start[s] : 0;
+        for (i = 0; i < seq_lens[s]; i++) {
+            uint64_t t = start + i;
+            uint64_t phys = block_table[seq_ptr[s] + t / page_size];
+            uint64_t slot = phys * page_size + t % page_size;
+            float sc;
+            uint8_t zp = 0;
+            for (e = 0; e < n; e++)
+                x[e] = (float)element_value(src_type, src, row * n + e);
+            oracle_quantize_row(x, n, zero_points != NULL, codes, &sc, &zp);
+            for (h = 0; h < num_heads; h++)
+                for (d = 0; d < head_dim; d++)
+                    pool[pool_index(block_table, seq_ptr, s, t, h, d, page_size, num_heads,
+                                    head_dim)] = codes[h * head_dim + d];
+            scales[slot] = sc;
+            if (zero_points)
+                zero_points[slot] = zp;
+            row++;
+        }
+        if (zero_tail && seq_lens[s] > 0) {
+            uint64_t t;
+            for (t = start + seq_lens[s]; t % page_size != 0; t++) {
+                uint64_t phys = block_table[seq_ptr[s] + t / page_size];
+                uint64_t slot = phys * page_size + t % page_size;
+                for (h = 0; h < num_heads; h++)
+                    for (d = 0; d < head_dim; d++)
+                        pool[pool_index(block_table, seq_ptr, s, t, h, d, page_size,
+                                        num_heads, head_dim)] = 0;
+                scales[slot] = 0.0f;
+                if (zero_points)
+                    zero_points[slot] = 0;
+            }
+        }
+    }
+    free(x);
+    free(codes);
+}
+
 /* [Rust20] "Count live rows and two kinds of unused payload": with
  * U = 2*B*H_kv*d slots per token position (K and V), A = ceil(n/P) active
  * pages and ceil(C/P)*P reserved positions,

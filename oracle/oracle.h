@@ -192,6 +192,33 @@ int oracle_paged_attention(const void *q, const void *k_pool, const void *v_pool
                            const uint64_t *block_table, const uint64_t *seq_ptr,
                            const uint64_t *seq_lens, uint64_t num_seqs, double *out);
 
+/* Quantization of one slot's row on write (quantize-on-scatter). The pages
+ * fix only where the parameters live ([Hurray] Per-page-slot parameters: one
+ * scale, and one zero point for an asymmetric scheme, per physical slot); the
+ * scheme document with the formulas is not among them. Reading, with every
+ * step one binary32 operation rounded to nearest even:
+ *   symmetric int8 (asym = 0): amax = max |x|; scale = amax / 127;
+ *     q = clamp(rint(x / scale), -127, 127); amax = 0 gives scale 0, q 0.
+ *   asymmetric uint8 (asym = 1): lo = min(0, min x), hi = max(0, max x);
+ *     scale = (hi - lo) / 255; z = clamp(rint(-lo / scale), 0, 255);
+ *     q = clamp(rint(x / scale) + z, 0, 255); hi = lo gives scale 0, z 0, q 0.
+ * x: n binary32 values; q: n int8 (symmetric) or uint8 (asymmetric) codes. */
+void oracle_quantize_row(const float *x, uint64_t n, int asym, void *q, float *scale,
+                         uint8_t *zero_point);
+
+/* Quantize-on-scatter: oracle_scatter's element placement, with each new
+ * token's row (num_heads * head_dim values of src_type ORACLE_F16 / BF16 /
+ * F32, converted exactly to binary32) quantized by oracle_quantize_row; the
+ * codes go to the pool, the scale to scales[phys * page_size + slot] and, when
+ * zero_points is not NULL (asymmetric, uint8 pool), the zero point likewise.
+ * With zero_tail the slots of the last written page past the final position
+ * get zero codes, scale 0 and zero point 0. */
+void oracle_scatter_quant(void *page_pool, float *scales, uint8_t *zero_points,
+                          const void *src, uint32_t src_type, uint64_t page_size,
+                          uint64_t num_heads, uint64_t head_dim, const uint64_t *block_table,
+                          const uint64_t *seq_ptr, const uint64_t *seq_lens,
+                          const uint64_t *seq_start, uint64_t num_seqs, int zero_tail);
+
 /* [Rust20] "Count live rows and two kinds of unused payload": buffer-length
  * payload of one layer's K and V arrays. out[] receives, in order:
  *  0 reserved pages      1 active pages
