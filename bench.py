@@ -766,7 +766,22 @@ def main():
             schemes[name] = {"algorithmic_bytes": qb, "launch_us": round(t_q * 1e3, 1),
                              "gb_per_s": round(qb / (t_q / 1e3) / 1e9, 1)}
         del qout
+        # quantize-on-scatter: the decode batch's fp16 rows written into an
+        # int8 pool (symmetric) and a uint8 pool with zero points (asymmetric)
+        qw_pool = torch.empty_like(qpool)
+        qw_sc = torch.zeros(wq.num_pages * 16, device=dev)
+        qw_zp = torch.zeros(wq.num_pages * 16, dtype=torch.uint8, device=dev)
+        quant_write = {}
+        for name, pool_t, zp in (("int8_symmetric", qw_pool, None),
+                                 ("uint8_zero_points", qw_pool.view(torch.uint8), qw_zp)):
+            qd = hp.Descriptor(pool_t, bt, sp, sl, scales=qw_sc)
+            t_w = back_to_back(lambda: hp.scatter_quant(qd, out, zero_points=zp, stream=stream))
+            qb = T * H * D * 3 + 4 * T + (T if zp is not None else 0)
+            quant_write[name] = {"algorithmic_bytes": qb, "launch_us": round(t_w * 1e3, 1),
+                                 "gb_per_s": round(qb / (t_w / 1e3) / 1e9, 1)}
+        del qw_pool
         result["extras"] = {
+            "quantize_on_scatter": quant_write,
             "attention": attention_extras(hp, torch, np, dev, stream, args.kernel_reps),
             "dequant_schemes": schemes,
             "batched_append": batched_append(hp, torch, np, dev, stream, args.kernel_reps),

@@ -23,6 +23,7 @@ import torch  # noqa: F401,E402
 
 __all__ = ["Descriptor", "HpError", "gather", "scatter", "gather_dequant", "validate",
            "gather_dequant_q", "QUANT_SCHEME", "paged_attention", "attention_workspace_bytes",
+           "scatter_quant",
            "gather_batch", "scatter_batch", "gather_dequant_batch", "copy_pages",
            "copy_pages_batch", "workspace_bytes",
            "status_str", "last_hip_error", "lib", "LIB_PATH", "STATUS"]
@@ -114,6 +115,8 @@ _lib.hp_gather_dequant.argtypes = [_P, _vp, _u32, _vp, _sz, _u32, _vp]
 _lib.hp_gather_dequant_q.restype = ctypes.c_int
 _lib.hp_gather_dequant_q.argtypes = [_P, ctypes.POINTER(HpQuant), _vp, _u32, _vp, _sz, _u32,
                                      _vp]
+_lib.hp_scatter_quant.restype = ctypes.c_int
+_lib.hp_scatter_quant.argtypes = [_P, _vp, _u32, _vp, _vp, _vp, _sz, _u32, _vp]
 _lib.hp_paged_attention.restype = ctypes.c_int
 _lib.hp_paged_attention.argtypes = [_P, _vp, _vp, _u32, ctypes.c_float, _vp, _u32, _vp, _sz,
                                     _u32, _vp]
@@ -341,6 +344,20 @@ def gather_dequant_q(desc, out, scheme, scales, *, axis=0, block_size=None, zero
                                     HP_FLAG_CHECKED if checked else 0,
                                     _stream(stream, desc.device)), "hp_gather_dequant_q")
     return out
+
+
+def scatter_quant(desc, src, seq_start=None, *, zero_points=None, zero_tail=False,
+                  checked=False, workspace=None, stream=None):
+    """Quantizes src[T, H, D] (f16, bf16 or f32) into desc's int8 pool
+    (symmetric) or uint8 pool (asymmetric, with zero_points: uint8 per slot),
+    writing each written slot's scale into desc.scales."""
+    T = src.shape[0]
+    p = desc.with_tokens(T)
+    ws, n = _workspace(desc, T, workspace)
+    flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_ZERO_TAIL if zero_tail else 0)
+    _check(_lib.hp_scatter_quant(p, _ptr(src), _dtype_code(src), _ptr(zero_points),
+                                 _ptr(seq_start), ws, n, flags, _stream(stream, desc.device)),
+           "hp_scatter_quant")
 
 
 def attention_workspace_bytes(desc, total_tokens, num_q_heads):

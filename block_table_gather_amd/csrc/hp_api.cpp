@@ -519,6 +519,87 @@ hp_status hp_scatter(const hp_desc *desc, const void *src, const void *seq_start
     return launch(desc, g, hp::Op::Scatter, m, seq_start, flags, workspace, (hipStream_t)stream);
 }
 
+hp_status hp_scatter_quant(const hp_desc *desc, const void *src, uint32_t src_dtype,
+                           void *zero_points, const void *seq_start, void *workspace,
+                           size_t workspace_bytes, uint32_t flags, void *stream) {
+    Geometry g;
+    bool done;
+    hp_status st = check_desc(desc, &g);
+    if (st != HP_OK)
+        return st;
+    const bool asym = desc->dtype == HP_DTYPE_U8;
+    if (desc->dtype != HP_DTYPE_I8 && !asym)
+        return HP_ERR_DTYPE;
+    uint32_t src_code, src_bytes;
+    switch (src_dtype) {
+    case HP_DTYPE_F16: src_code = 0; src_bytes = 2; break;
+    case HP_DTYPE_BF16: src_code = 1; src_bytes = 2; break;
+    case HP_DTYPE_F32: src_code = 2; src_bytes = 4; break;
+    default: return HP_ERR_DTYPE;
+    }
+    if (!asym && zero_points)
+        return HP_ERR_ARG;  // int8 pools are symmetric: no zero points
+    if (desc->num_pages && (!desc->scales || (asym && !zero_points)))
+        return HP_ERR_NULL;
+    if (desc->total_tokens && !src)
+        return HP_ERR_NULL;
+    if (!aligned(src, src_bytes) || !aligned(zero_points, 64))
+        return HP_ERR_ALIGN;
+    const uint64_t n = g.row_bytes;  // one byte per value
+    const uint64_t src_row = n * src_bytes, slots = desc->num_pages * desc->page_size;
+    const void *written[3] = {desc->page_pool, desc->scales, zero_points};
+    const uint64_t wbytes[3] = {g.pool_bytes, 4 * slots, asym ? slots : 0};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(src, desc->total_tokens * src_row, written[i], wbytes[i]))
+            return HP_ERR_ARG;
+        for (int k = i + 1; k < 3; ++k)
+            if (overlaps(written[i], wbytes[i], written[k], wbytes[k]))
+                return HP_ERR_ARG;
+    }
+    st = prologue(desc, g, flags, HP_FLAG_CHECKED | HP_FLAG_ZERO_TAIL, seq_start, workspace,
+                  workspace_bytes, (hipStream_t)stream, &done);
+    if (st != HP_OK || done)
+        return st;
+    const bool zero_tail = (flags & HP_FLAG_ZERO_TAIL) != 0;
+    void *pool = desc->page_pool;
+    void *rows = const_cast<void *>(src);  // read, never written
+    hp::CopyJob j = {};
+    j.op = hp::Op::ScatterQuant;
+    j.idx64 = desc->index_type == HP_INDEX_U64;
+    j.zero_tail = zero_tail;
+    j.elem_bytes = 1;
+    j.page_size = desc->page_size;
+    j.num_seqs = desc->num_seqs;
+    j.total_tokens = desc->total_tokens;
+    j.row_bytes = n;
+    j.out_row_bytes = src_row;
+    // a unit is up to one row per wave (4 waves), consecutive slots of a page
+    j.rows_per_unit = rows_per_unit(desc->page_size, 1, hp::kThreads / 64, 0xffffffffu);
+    j.units_per_group = 1;
+    const uint64_t upp = desc->page_size / j.rows_per_unit;
+    j.unit_bound = desc->total_tokens / j.rows_per_unit +
+                   desc->num_seqs * (2 + (zero_tail ? upp : 0));
+    if (j.unit_bound >= (1ull << 32) - hp::kMaxUnitsPerGroup)
+        return HP_ERR_ARG;
+    j.block_table = desc->block_table;
+    j.seq_ptr = desc->seq_ptr;
+    j.seq_lens = desc->seq_lens;
+    j.seq_start = seq_start;
+    j.count = 1;
+    j.pools = &pool;
+    j.rows = &rows;
+    j.workspace = workspace ? static_cast<unsigned char *>(workspace) + kValidateBytes : nullptr;
+    // 8 values per vector when rows and the source allow 16-byte (or 2 x 16)
+    // loads and 8-byte code stores; single values otherwise
+    j.vec_bytes = (n % 8 == 0 && aligned(src, 16)) ? 16 : 1;
+    j.qs_src = src_code;
+    j.qs_asym = asym;
+    j.qs_scales = const_cast<float *>(desc->scales);
+    j.qs_zero_points = static_cast<uint8_t *>(zero_points);
+    const hipError_t e = hp::launch_copy(j, (hipStream_t)stream);
+    return e == hipSuccess ? HP_OK : hip_failed(e);
+}
+
 hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype, void *workspace,
                             size_t workspace_bytes, uint32_t flags, void *stream) {
     Geometry g;

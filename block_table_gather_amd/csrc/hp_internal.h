@@ -55,7 +55,9 @@ constexpr uint32_t kMaxUnitsPerGroup = 16;
 // pointers travel in the kernel arguments. Larger batches take more launches.
 constexpr uint32_t kMaxBatch = 32;
 
-enum class Op : int { Gather = 0, Scatter = 1, Dequant = 2 };
+enum class Op : int { Gather = 0, Scatter = 1, Dequant = 2, ScatterQuant = 3 };
+// Moves that write the pool (and so take seq_start and tail zeroing).
+constexpr bool writes_pool(Op op) { return op == Op::Scatter || op == Op::ScatterQuant; }
 
 // Everything a copy launch needs; filled and checked on the host.
 struct CopyJob {
@@ -92,6 +94,13 @@ struct CopyJob {
     const void *zero_points;     // same count as the scales, pool element type; may be null
     uint32_t head_dim;
     uint32_t quant_channels;     // per-channel table entries (modes 2, 3)
+    // Quantize-on-scatter (op ScatterQuant, single pool): source element type
+    // (0 f16, 1 bf16, 2 f32), asymmetric (uint8 pool with zero points), and the
+    // per-slot parameters it writes.
+    uint32_t qs_src;
+    bool qs_asym;
+    float *qs_scales;
+    uint8_t *qs_zero_points;
 };
 
 // Copy-on-write page copy over `count` pools that share the page IDs.

@@ -107,6 +107,9 @@ struct Args {
     uint32_t head_dim;
     uint32_t quant_channels;  // entries of a per-channel table
     Div div_hd;
+    // Quantize-on-scatter: the per-slot parameters it writes.
+    float *qs_scales;
+    uint8_t *qs_zero_points;
     // Pool m of the launch is moved by grid row m (blockIdx.y).
     unsigned char *pool[kMaxBatch];   // scatter writes it, gather/dequant read it
     unsigned char *rows[kMaxBatch];   // the logical tensor of pool m
@@ -120,7 +123,7 @@ struct Args {
 template <Op OP>
 __device__ __forceinline__ uint64_t units_of(const Args &a, uint64_t len, uint64_t start) {
     const uint64_t rpc = a.rows_per_unit;
-    if (OP != Op::Scatter)
+    if (!writes_pool(OP))
         return udiv(len + rpc - 1, a.div_rpc);
     if (len == 0)
         return 0;
@@ -185,7 +188,7 @@ __device__ __forceinline__ void scan_range(const Args &a, uint32_t s0, uint32_t 
     uint64_t u = 0, t = 0;
     for (uint32_t i = i0; i < i1; ++i) {
         const uint64_t len = ld_idx<IdxT>(a.seq_lens, i);
-        const uint64_t st = (OP == Op::Scatter && a.seq_start) ? ld_idx<IdxT>(a.seq_start, i) : 0;
+        const uint64_t st = (writes_pool(OP) && a.seq_start) ? ld_idx<IdxT>(a.seq_start, i) : 0;
         u += units_of<OP>(a, len, st);
         t += len;
     }
@@ -195,7 +198,7 @@ __device__ __forceinline__ void scan_range(const Args &a, uint32_t s0, uint32_t 
     t += tbase;
     for (uint32_t i = i0; i < i1; ++i) {
         const uint64_t len = ld_idx<IdxT>(a.seq_lens, i);
-        const uint64_t st = (OP == Op::Scatter && a.seq_start) ? ld_idx<IdxT>(a.seq_start, i) : 0;
+        const uint64_t st = (writes_pool(OP) && a.seq_start) ? ld_idx<IdxT>(a.seq_start, i) : 0;
         u += units_of<OP>(a, len, st);
         unit_end[i] = (UE)u;
         tok_begin[i] = (TB)t;
@@ -558,6 +561,150 @@ __device__ __forceinline__ void dequant_span_q(const Args &a, const unsigned cha
                                      flip, tab);
 }
 
+// ---- quantize-on-scatter --------------------------------------------------------
+//
+// One written slot's row (n = row_bytes values, source element type SRC:
+// 0 f16, 1 bf16, 2 f32) quantized by the whole workgroup ([Hurray] Per-page-
+// slot parameters: the scale, and for an asymmetric scheme the zero point,
+// of physical slot phys * page_size + slot). Reading of the formulas, every
+// step one binary32 operation rounded to nearest even:
+//   symmetric int8:   scale = amax / 127, q = clamp(rint(x / scale), -127, 127)
+//   asymmetric uint8: lo = min(0, x), hi = max(0, x), scale = (hi - lo) / 255,
+//                     z = clamp(rint(-lo / scale), 0, 255),
+//                     q = clamp(rint(x / scale) + z, 0, 255)
+// and a zero scale gives zero codes (and zero point). Division is the IEEE
+// division (__fdiv_rn), rint rounds half to even.
+
+constexpr int kQuantKeep = 8;  // vectors per lane held in registers between the passes
+
+template <int SRC, int VE>
+__device__ __forceinline__ void load_row_vec(const unsigned char *row, uint32_t i, float (&f)[VE]) {
+    if constexpr (VE == 1) {
+        if constexpr (SRC == 2) {
+            f[0] = reinterpret_cast<const float *>(row)[i];
+        } else {
+            const uint16_t b = reinterpret_cast<const uint16_t *>(row)[i];
+            f[0] = SRC == 1 ? __builtin_bit_cast(float, (uint32_t)b << 16)
+                            : (float)__builtin_bit_cast(_Float16, b);
+        }
+    } else if constexpr (SRC == 2) {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(row) + 2 * i;
+        const u32x4 v0 = ld_stream<true>(p), v1 = ld_stream<true>(p + 1);
+        __builtin_memcpy(&f[0], &v0, 16);
+        __builtin_memcpy(&f[4], &v1, 16);
+    } else {
+        const u32x4 v = ld_stream<true>(reinterpret_cast<const u32x4 *>(row) + i);
+        uint32_t w[4];
+        __builtin_memcpy(w, &v, 16);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if constexpr (SRC == 1) {
+                f[2 * k] = __builtin_bit_cast(float, w[k] << 16);
+                f[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
+            } else {
+                f[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] & 0xffffu));
+                f[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] >> 16));
+            }
+        }
+    }
+}
+
+template <bool ASYM, int VE>
+__device__ __forceinline__ void store_codes(unsigned char *dst, uint32_t i, const float (&f)[VE],
+                                            float sc, float z) {
+    uint8_t c[VE];
+#pragma unroll
+    for (int k = 0; k < VE; ++k) {
+        float q = 0.0f;
+        if (sc != 0.0f) {
+            q = __builtin_rintf(__fdiv_rn(f[k], sc));
+            q = ASYM ? __builtin_fminf(__builtin_fmaxf(q + z, 0.0f), 255.0f)
+                     : __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
+        }
+        c[k] = ASYM ? (uint8_t)(int32_t)q : (uint8_t)(int8_t)(int32_t)q;
+    }
+    if constexpr (VE == 8) {
+        u32x2 v;
+        __builtin_memcpy(&v, c, 8);
+        st_stream(v, reinterpret_cast<u32x2 *>(dst) + i);
+    } else {
+        st_stream(c[0], dst + i);
+    }
+}
+
+// One row per wave: the row's values are spread over the wave's 64 lanes, the
+// first kQuantKeep vectors of each lane stay in registers between the two
+// passes (the rest are read again), and the row's extremes are combined
+// with shuffles alone.
+template <int VEC, int QM>
+__device__ __forceinline__ void quant_row(const Args &a, const unsigned char *__restrict__ src,
+                                          unsigned char *__restrict__ dst, uint64_t slot) {
+#pragma clang fp contract(off)
+    constexpr int SRC = QM >> 1;
+    constexpr bool ASYM = QM & 1;
+    constexpr int VE = VEC == 16 ? 8 : 1;  // values per vector
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t nv = a.row_bytes / VE;
+    float keep[kQuantKeep][VE];
+    float lo = 0.0f, hi = 0.0f;  // symmetric: hi is the largest |x|
+#pragma unroll
+    for (int k = 0; k < kQuantKeep; ++k) {
+        const uint32_t i = lane + k * 64;
+        if (i < nv) {
+            load_row_vec<SRC, VE>(src, i, keep[k]);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                if constexpr (ASYM) {
+                    lo = __builtin_fminf(lo, keep[k][e]);
+                    hi = __builtin_fmaxf(hi, keep[k][e]);
+                } else {
+                    hi = __builtin_fmaxf(hi, __builtin_fabsf(keep[k][e]));
+                }
+            }
+        }
+    }
+    for (uint32_t i = lane + kQuantKeep * 64; i < nv; i += 64) {
+        float f[VE];
+        load_row_vec<SRC, VE>(src, i, f);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            if constexpr (ASYM) {
+                lo = __builtin_fminf(lo, f[e]);
+                hi = __builtin_fmaxf(hi, f[e]);
+            } else {
+                hi = __builtin_fmaxf(hi, __builtin_fabsf(f[e]));
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        if constexpr (ASYM)
+            lo = __builtin_fminf(lo, __shfl_xor(lo, o, 64));
+        hi = __builtin_fmaxf(hi, __shfl_xor(hi, o, 64));
+    }
+    const float sc = ASYM ? __fdiv_rn(hi - lo, 255.0f) : __fdiv_rn(hi, 127.0f);
+    const float z = (ASYM && sc != 0.0f)
+                        ? __builtin_fminf(__builtin_fmaxf(__builtin_rintf(__fdiv_rn(-lo, sc)), 0.0f),
+                                          255.0f)
+                        : 0.0f;
+#pragma unroll
+    for (int k = 0; k < kQuantKeep; ++k) {
+        const uint32_t i = lane + k * 64;
+        if (i < nv)
+            store_codes<ASYM, VE>(dst, i, keep[k], sc, z);
+    }
+    for (uint32_t i = lane + kQuantKeep * 64; i < nv; i += 64) {
+        float f[VE];
+        load_row_vec<SRC, VE>(src, i, f);
+        store_codes<ASYM, VE>(dst, i, f, sc, z);
+    }
+    if (lane == 0) {
+        a.qs_scales[slot] = sc;
+        if constexpr (ASYM)
+            a.qs_zero_points[slot] = (uint8_t)(int32_t)z;
+    }
+}
+
 // Bytes of the fused path's LDS sequence table (8 + 4 bytes per sequence),
 // rounded up so that what follows it is 16-byte aligned.
 __host__ __device__ constexpr size_t lds_table_bytes(uint32_t S) {
@@ -577,7 +724,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
     // Per-channel dequant parameters, staged once per workgroup after the
     // sequence table (QM 2, 3).
     const QParam *tab = nullptr;
-    if constexpr (QM == 2 || QM == 3) {
+    if constexpr (OP == Op::Dequant && (QM == 2 || QM == 3)) {
         QParam *t = reinterpret_cast<QParam *>(lds + (FUSED ? lds_table_bytes(S) : 0));
         const uint32_t flip = a.quant_unsigned ? 0x80u : 0u;
         for (uint32_t c = threadIdx.x; c < a.quant_channels; c += kThreads)
@@ -623,7 +770,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
         tb = uni64(tok_begin[q]);
         len = uni64(ld_idx<IdxT>(a.seq_lens, q));
         sp = uni64(ld_idx<IdxT>(a.seq_ptr, q));
-        start = (OP == Op::Scatter && a.seq_start) ? uni64(ld_idx<IdxT>(a.seq_start, q)) : 0;
+        start = (writes_pool(OP) && a.seq_start) ? uni64(ld_idx<IdxT>(a.seq_start, q)) : 0;
     };
     load_seq(s);
 
@@ -633,7 +780,38 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
             load_seq(s);
         }
         const uint32_t u = g - ubeg;
-        if constexpr (OP == Op::Scatter) {
+        if constexpr (OP == Op::ScatterQuant) {
+            // Window w of rows_per_unit positions (at most one per wave): wave
+            // k quantizes the new token at position w * rpc + k, or clears it
+            // when it is a tail slot.
+            const uint64_t w = udiv(start, a.div_rpc) + u;
+            const uint64_t q = udiv(w, a.div_upp);
+            const uint64_t phys = uni64(ld_idx<IdxT>(a.block_table, sp + q));
+            const uint32_t k = threadIdx.x >> 6;
+            const uint64_t pos = w * rpc + k;
+            const uint64_t end = start + len;
+            const uint64_t slot = phys * P + (pos - q * P);
+            if (k < rpc && pos >= start && pos < end) {
+                quant_row<VEC, QM>(a, rowsp + (tb + (pos - start)) * a.out_row_bytes,
+                                   pool + slot * a.row_bytes, slot);
+            } else if (k < rpc && a.zero_tail && pos >= end &&
+                       pos < udiv(end + P - 1, a.div_page) * P) {
+                const uint32_t lane = threadIdx.x & 63;
+                unsigned char *row = pool + slot * a.row_bytes;
+                if (a.row_bytes % 16 == 0) {
+                    for (uint32_t i = lane; i < a.row_bytes / 16; i += 64)
+                        st_stream(u32x4(0), reinterpret_cast<u32x4 *>(row) + i);
+                } else {
+                    for (uint32_t i = lane; i < a.row_bytes; i += 64)
+                        st_stream((unsigned char)0, row + i);
+                }
+                if (lane == 0) {
+                    a.qs_scales[slot] = 0.0f;
+                    if (QM & 1)
+                        a.qs_zero_points[slot] = 0;
+                }
+            }
+        } else if constexpr (OP == Op::Scatter) {
             // Window w of absolute positions [w*rpc, (w+1)*rpc) of sequence s.
             const uint64_t w = udiv(start, a.div_rpc) + u;
             const uint64_t pos0 = w * rpc;
@@ -689,7 +867,7 @@ __global__ __launch_bounds__(kThreads) void plan_sum_kernel(Args a) {
     uint64_t u = 0, t = 0;
     for (uint32_t i = i0; i < i1; ++i) {
         const uint64_t len = ld_idx<IdxT>(a.seq_lens, i);
-        const uint64_t st = (OP == Op::Scatter && a.seq_start) ? ld_idx<IdxT>(a.seq_start, i) : 0;
+        const uint64_t st = (writes_pool(OP) && a.seq_start) ? ld_idx<IdxT>(a.seq_start, i) : 0;
         u += units_of<OP>(a, len, st);
         t += len;
     }
@@ -895,7 +1073,8 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 template <typename IdxT, Op OP, int VEC, bool NTL, int QM = -1>
 hipError_t launch_vec(const Args &a, bool fused, dim3 grid, uint32_t plan_chunks,
                       uint32_t *unit_end, uint64_t *tok_begin, hipStream_t stream) {
-    const size_t qlds = (QM == 2 || QM == 3) ? sizeof(QParam) * (size_t)a.quant_channels : 0;
+    const size_t qlds =
+        (OP == Op::Dequant && (QM == 2 || QM == 3)) ? sizeof(QParam) * (size_t)a.quant_channels : 0;
     if (fused) {
         const size_t lds = lds_table_bytes(a.num_seqs) + qlds;
         hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, true, NTL, QM>), grid, dim3(kThreads), lds,
@@ -929,7 +1108,16 @@ hipError_t launch_vec(const Args &a, bool fused, dim3 grid, uint32_t plan_chunks
 template <typename IdxT, Op OP, int VEC>
 hipError_t launch_policy(const Args &a, bool ntl, bool fused, dim3 grid, uint32_t chunks,
                          uint32_t *ue, uint64_t *tb, hipStream_t st, int qm) {
-    if constexpr (OP == Op::Dequant) {
+    if constexpr (OP == Op::ScatterQuant) {
+        switch (qm) {  // source type * 2 + asymmetric
+        case 0: return launch_vec<IdxT, OP, VEC, false, 0>(a, fused, grid, chunks, ue, tb, st);
+        case 1: return launch_vec<IdxT, OP, VEC, false, 1>(a, fused, grid, chunks, ue, tb, st);
+        case 2: return launch_vec<IdxT, OP, VEC, false, 2>(a, fused, grid, chunks, ue, tb, st);
+        case 3: return launch_vec<IdxT, OP, VEC, false, 3>(a, fused, grid, chunks, ue, tb, st);
+        case 4: return launch_vec<IdxT, OP, VEC, false, 4>(a, fused, grid, chunks, ue, tb, st);
+        default: return launch_vec<IdxT, OP, VEC, false, 5>(a, fused, grid, chunks, ue, tb, st);
+        }
+    } else if constexpr (OP == Op::Dequant) {
         switch (qm) {
         case 0: return launch_vec<IdxT, OP, VEC, false, 0>(a, fused, grid, chunks, ue, tb, st);
         case 1: return launch_vec<IdxT, OP, VEC, false, 1>(a, fused, grid, chunks, ue, tb, st);
@@ -949,7 +1137,11 @@ hipError_t launch_policy(const Args &a, bool ntl, bool fused, dim3 grid, uint32_
 template <typename IdxT, Op OP>
 hipError_t launch_op(const Args &a, uint32_t vec, bool ntl, bool fused, dim3 grid,
                      uint32_t chunks, uint32_t *ue, uint64_t *tb, hipStream_t st, int qm) {
-    if constexpr (OP == Op::Dequant) {
+    if constexpr (OP == Op::ScatterQuant) {
+        if (vec == 16)  // 8 values per vector
+            return launch_policy<IdxT, OP, 16>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
+        return launch_policy<IdxT, OP, 1>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
+    } else if constexpr (OP == Op::Dequant) {
         switch (vec) {
         case 8: return launch_policy<IdxT, OP, 8>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
         case 4: return launch_policy<IdxT, OP, 4>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
@@ -975,6 +1167,8 @@ hipError_t launch_idx(const Args &a, Op op, uint32_t vec, bool ntl, bool fused, 
         return launch_op<IdxT, Op::Gather>(a, vec, ntl, fused, grid, chunks, ue, tb, st, -1);
     case Op::Scatter:
         return launch_op<IdxT, Op::Scatter>(a, vec, ntl, fused, grid, chunks, ue, tb, st, -1);
+    case Op::ScatterQuant:
+        return launch_op<IdxT, Op::ScatterQuant>(a, vec, ntl, fused, grid, chunks, ue, tb, st, qm);
     default:
         return launch_op<IdxT, Op::Dequant>(a, vec, ntl, fused, grid, chunks, ue, tb, st, qm);
     }
@@ -1013,6 +1207,10 @@ hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
     int qm = job.quant_ext ? (int)job.quant_mode : -1;
     if (qm >= 2 && job.quant_channels > kQuantLdsMax)
         qm += 2;  // table too large for LDS: read it from global memory
+    if (job.op == Op::ScatterQuant)
+        qm = (int)job.qs_src * 2 + (job.qs_asym ? 1 : 0);
+    a.qs_scales = job.qs_scales;
+    a.qs_zero_points = job.qs_zero_points;
     a.quant_scales = job.quant_scales;
     a.zero_points = job.zero_points;
     a.head_dim = job.head_dim ? job.head_dim : 1;

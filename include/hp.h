@@ -193,6 +193,34 @@ hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype,
                             void *workspace, size_t workspace_bytes, uint32_t flags,
                             void *stream);
 
+/* ---- Quantize-on-scatter ----------------------------------------------------
+ *
+ * [Hurray] Per-page-slot parameters: a quantized page carries one scale (and,
+ * for an asymmetric scheme, one zero point) per physical slot. This is the
+ * scatter of hp_scatter for a quantized pool: each new token's row of
+ * num_heads * head_dim values is quantized on its own and its codes, scale
+ * and zero point are written to its slot. The formulas belong to a scheme
+ * document that is not given; the reading used (each step one IEEE binary32
+ * operation, round to nearest even):
+ *   int8 pool (symmetric, zero_points NULL):
+ *     scale = max|x| / 127, q = clamp(rint(x / scale), -127, 127)
+ *   uint8 pool (asymmetric, zero_points required):
+ *     lo = min(0, min x), hi = max(0, max x), scale = (hi - lo) / 255,
+ *     z = clamp(rint(-lo / scale), 0, 255), q = clamp(rint(x / scale) + z, 0, 255)
+ * and a zero scale gives zero codes and zero point. hp_gather_dequant_q with
+ * the per-block-affine scheme (or hp_gather_dequant for int8) reads them back.
+ *
+ * desc        the quantized pool (dtype HP_DTYPE_I8 or HP_DTYPE_U8); desc->scales
+ *             (fp32, num_pages * page_size) is WRITTEN at every written slot.
+ * src         DEVICE [total_tokens, num_heads, head_dim] of src_dtype
+ *             (HP_DTYPE_F16, HP_DTYPE_BF16 or HP_DTYPE_F32), element aligned.
+ * zero_points DEVICE uint8 [num_pages * page_size], 64-byte aligned (uint8 pools).
+ * seq_start, workspace, flags (HP_FLAG_CHECKED, HP_FLAG_ZERO_TAIL: tail slots
+ * get zero codes, scale 0 and zero point 0) and errors as hp_scatter. */
+hp_status hp_scatter_quant(const hp_desc *desc, const void *src, uint32_t src_dtype,
+                           void *zero_points, const void *seq_start, void *workspace,
+                           size_t workspace_bytes, uint32_t flags, void *stream);
+
 /* ---- Dequant-gather under any quantization scheme -------------------------
  *
  * [Hurray] Quantization Compatibility, Per-scheme composition. Schemes, by the

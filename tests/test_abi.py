@@ -27,7 +27,8 @@ def test_every_declared_symbol_is_exported():
                           "hp_gather_dequant", "hp_status_str", "hp_last_hip_error",
                           "hp_gather_batch", "hp_scatter_batch", "hp_gather_dequant_batch",
                           "hp_copy_pages", "hp_copy_pages_batch", "hp_gather_dequant_q",
-                          "hp_paged_attention", "hp_attention_workspace_bytes"}
+                          "hp_paged_attention", "hp_attention_workspace_bytes",
+                          "hp_scatter_quant"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -246,6 +247,38 @@ def test_attention_workspace_bytes():
     assert 0 < a < b
     big = desc(total_tokens=1 << 20, num_pages=1 << 17)
     assert L.hp_attention_workspace_bytes(ctypes.byref(big), 8) > a
+
+
+def sq(d, src=OUT, sdt=None, zp=None, flags=0):
+    sdt = hp.DTYPE["f16"] if sdt is None else sdt
+    return L.hp_scatter_quant(ctypes.byref(d) if d is not None else None, src, sdt, zp, None,
+                              None, 0, flags, None)
+
+
+def test_scatter_quant_rejections():
+    i8 = desc(dtype=hp.DTYPE["i8"], scales=ALIGNED + 0x500000)
+    u8 = desc(dtype=hp.DTYPE["u8"], scales=ALIGNED + 0x500000)
+    ZP = ALIGNED + 0x600000
+    assert sq(None) == S["HP_ERR_NULL"]
+    assert sq(desc(scales=ALIGNED + 0x500000)) == S["HP_ERR_DTYPE"]   # f16 pool
+    assert sq(i8, sdt=hp.DTYPE["i8"]) == S["HP_ERR_DTYPE"]           # int8 source
+    assert sq(i8, sdt=hp.DTYPE["f64"]) == S["HP_ERR_DTYPE"]
+    assert sq(i8, zp=ZP) == S["HP_ERR_ARG"]                           # symmetric: no zero points
+    assert sq(u8) == S["HP_ERR_NULL"]                                 # asymmetric needs them
+    assert sq(desc(dtype=hp.DTYPE["i8"])) == S["HP_ERR_NULL"]         # no scales
+    assert sq(i8, src=None) == S["HP_ERR_NULL"]
+    assert sq(i8, src=OUT + 1) == S["HP_ERR_ALIGN"]
+    assert sq(i8, src=OUT + 2, sdt=hp.DTYPE["f32"]) == S["HP_ERR_ALIGN"]
+    assert sq(u8, zp=ZP + 8) == S["HP_ERR_ALIGN"]
+    assert sq(i8, src=ALIGNED + 0x400) == S["HP_ERR_ARG"]             # source over the pool
+    assert sq(i8, src=ALIGNED + 0x500000) == S["HP_ERR_ARG"]          # source over the scales
+    assert sq(u8, zp=ALIGNED + 0x500000) == S["HP_ERR_ARG"]           # zero points over scales
+    assert sq(u8, zp=ALIGNED) == S["HP_ERR_ARG"]                      # zero points over the pool
+    assert sq(i8, flags=hp.HP_FLAG_STREAM) == S["HP_ERR_ARG"]
+    assert sq(i8, flags=hp.HP_FLAG_CHECKED) == S["HP_ERR_WORKSPACE"]
+    empty = desc(dtype=hp.DTYPE["i8"], scales=ALIGNED + 0x500000, num_seqs=0,
+                 num_block_entries=0, total_tokens=0)
+    assert sq(empty, src=None) == S["HP_OK"]                          # nothing to write
 
 
 def test_workspace_bytes():
