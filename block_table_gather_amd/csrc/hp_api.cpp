@@ -573,9 +573,10 @@ hp_status hp_scatter_quant(const hp_desc *desc, const void *src, uint32_t src_dt
     j.total_tokens = desc->total_tokens;
     j.row_bytes = n;
     j.out_row_bytes = src_row;
-    // a unit is up to one row per wave (4 waves), consecutive slots of a page
-    j.rows_per_unit = rows_per_unit(desc->page_size, 1, hp::kThreads / 64, 0xffffffffu);
-    j.units_per_group = 1;
+    // a unit is a run of consecutive slots of a page; each wave quantizes
+    // whole rows of it
+    j.rows_per_unit = rows_per_unit(desc->page_size, 1, HP_QUANT_UNIT_ROWS, 0xffffffffu);
+    j.units_per_group = HP_QUANT_UNITS_PER_GROUP;
     const uint64_t upp = desc->page_size / j.rows_per_unit;
     j.unit_bound = desc->total_tokens / j.rows_per_unit +
                    desc->num_seqs * (2 + (zero_tail ? upp : 0));

@@ -38,6 +38,14 @@ namespace hp {
 #ifndef HP_SCATTER_STREAM_UNIT_BYTES
 #define HP_SCATTER_STREAM_UNIT_BYTES 8192
 #endif
+// Quantize-on-scatter: rows (slots of one page) per work unit; the
+// workgroup's waves take them in turn.
+#ifndef HP_QUANT_UNIT_ROWS
+#define HP_QUANT_UNIT_ROWS 8
+#endif
+#ifndef HP_QUANT_UNITS_PER_GROUP
+#define HP_QUANT_UNITS_PER_GROUP 1
+#endif
 #ifndef HP_DEQUANT_UNITS_PER_GROUP
 #define HP_DEQUANT_UNITS_PER_GROUP 1
 #endif

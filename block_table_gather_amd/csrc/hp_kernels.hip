@@ -609,18 +609,35 @@ __device__ __forceinline__ void load_row_vec(const unsigned char *row, uint32_t 
     }
 }
 
-template <bool ASYM, int VE>
+// Quotients x / s rounded to nearest even, as one IEEE binary32 division
+// would give them. FAST: y is RN(1/s); the first remainder step makes the
+// product x * y a faithful quotient, and by Markstein's theorem (correctly
+// rounded reciprocal, faithful quotient, exact FMA remainder) the second
+// step rounds it correctly. This holds for s in [2^-100, 2^100] and for
+// quotients of magnitude at least 1/4 (smaller ones round to code 0 on
+// either path); s == 0 with y == 0 gives 0 for every finite x. Any other
+// scale takes the division itself.
+template <bool FAST>
+__device__ __forceinline__ float quotient(float x, float s, float y) {
+#pragma clang fp contract(off)
+    if constexpr (FAST) {
+        const float q0 = x * y;
+        const float q1 = __builtin_fmaf(__builtin_fmaf(-s, q0, x), y, q0);
+        return __builtin_fmaf(__builtin_fmaf(-s, q1, x), y, q1);
+    } else {
+        return __fdiv_rn(x, s);
+    }
+}
+
+template <bool ASYM, int VE, bool FAST>
 __device__ __forceinline__ void store_codes(unsigned char *dst, uint32_t i, const float (&f)[VE],
-                                            float sc, float z) {
+                                            float s, float y, float z) {
     uint8_t c[VE];
 #pragma unroll
     for (int k = 0; k < VE; ++k) {
-        float q = 0.0f;
-        if (sc != 0.0f) {
-            q = __builtin_rintf(__fdiv_rn(f[k], sc));
-            q = ASYM ? __builtin_fminf(__builtin_fmaxf(q + z, 0.0f), 255.0f)
-                     : __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
-        }
+        float q = __builtin_rintf(quotient<FAST>(f[k], s, y));
+        q = ASYM ? __builtin_fminf(__builtin_fmaxf(q + z, 0.0f), 255.0f)
+                 : __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
         c[k] = ASYM ? (uint8_t)(int32_t)q : (uint8_t)(int8_t)(int32_t)q;
     }
     if constexpr (VE == 8) {
@@ -632,10 +649,51 @@ __device__ __forceinline__ void store_codes(unsigned char *dst, uint32_t i, cons
     }
 }
 
+template <bool ASYM, int VE>
+__device__ __forceinline__ void fold_extremes(const float (&f)[VE], float &lo, float &hi) {
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+        if constexpr (ASYM) {
+            lo = __builtin_fminf(lo, f[e]);
+            hi = __builtin_fmaxf(hi, f[e]);
+        } else {
+            hi = __builtin_fmaxf(hi, __builtin_fabsf(f[e]));
+        }
+    }
+}
+
+constexpr int kQuantReread = 4;  // vectors per lane in flight when a row is read again
+
+// Writes the codes of a row whose extremes are known: the kept vectors
+// first, then the rest of the row, read again kQuantReread vectors per lane
+// at a time. An index past the row is clamped to the row's last vector for
+// the load and for the store alike: that lane writes the same codes to the
+// same bytes as the lane that owns them, so no access is predicated and the
+// stores of a lane need not wait for each other.
+template <int SRC, bool ASYM, int VE, bool FAST>
+__device__ __forceinline__ void emit_row(const unsigned char *__restrict__ src,
+                                         unsigned char *__restrict__ dst, uint32_t nv,
+                                         uint32_t lane, const float (&keep)[kQuantKeep][VE],
+                                         float s, float y, float z) {
+#pragma unroll
+    for (int k = 0; k < kQuantKeep; ++k)
+        store_codes<ASYM, VE, FAST>(dst, min32(lane + k * 64, nv - 1), keep[k], s, y, z);
+    for (uint32_t b = kQuantKeep * 64; b < nv; b += kQuantReread * 64) {
+        float f[kQuantReread][VE];
+#pragma unroll
+        for (int k = 0; k < kQuantReread; ++k)
+            load_row_vec<SRC, VE>(src, min32(b + lane + k * 64, nv - 1), f[k]);
+#pragma unroll
+        for (int k = 0; k < kQuantReread; ++k)
+            store_codes<ASYM, VE, FAST>(dst, min32(b + lane + k * 64, nv - 1), f[k], s, y, z);
+    }
+}
+
 // One row per wave: the row's values are spread over the wave's 64 lanes, the
 // first kQuantKeep vectors of each lane stay in registers between the two
 // passes (the rest are read again), and the row's extremes are combined
-// with shuffles alone.
+// with shuffles alone. Loads are never predicated, so each lane's loads are
+// all in flight together.
 template <int VEC, int QM>
 __device__ __forceinline__ void quant_row(const Args &a, const unsigned char *__restrict__ src,
                                           unsigned char *__restrict__ dst, uint64_t slot) {
@@ -644,37 +702,24 @@ __device__ __forceinline__ void quant_row(const Args &a, const unsigned char *__
     constexpr bool ASYM = QM & 1;
     constexpr int VE = VEC == 16 ? 8 : 1;  // values per vector
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t nv = a.row_bytes / VE;
+    const uint32_t nv = a.row_bytes / VE;  // at least 1
     float keep[kQuantKeep][VE];
     float lo = 0.0f, hi = 0.0f;  // symmetric: hi is the largest |x|
+    // a clamped index repeats the row's last vector: it cannot move an extreme
 #pragma unroll
-    for (int k = 0; k < kQuantKeep; ++k) {
-        const uint32_t i = lane + k * 64;
-        if (i < nv) {
-            load_row_vec<SRC, VE>(src, i, keep[k]);
+    for (int k = 0; k < kQuantKeep; ++k)
+        load_row_vec<SRC, VE>(src, min32(lane + k * 64, nv - 1), keep[k]);
 #pragma unroll
-            for (int e = 0; e < VE; ++e) {
-                if constexpr (ASYM) {
-                    lo = __builtin_fminf(lo, keep[k][e]);
-                    hi = __builtin_fmaxf(hi, keep[k][e]);
-                } else {
-                    hi = __builtin_fmaxf(hi, __builtin_fabsf(keep[k][e]));
-                }
-            }
-        }
-    }
-    for (uint32_t i = lane + kQuantKeep * 64; i < nv; i += 64) {
-        float f[VE];
-        load_row_vec<SRC, VE>(src, i, f);
+    for (int k = 0; k < kQuantKeep; ++k)
+        fold_extremes<ASYM, VE>(keep[k], lo, hi);
+    for (uint32_t b = kQuantKeep * 64; b < nv; b += kQuantReread * 64) {
+        float f[kQuantReread][VE];
 #pragma unroll
-        for (int e = 0; e < VE; ++e) {
-            if constexpr (ASYM) {
-                lo = __builtin_fminf(lo, f[e]);
-                hi = __builtin_fmaxf(hi, f[e]);
-            } else {
-                hi = __builtin_fmaxf(hi, __builtin_fabsf(f[e]));
-            }
-        }
+        for (int k = 0; k < kQuantReread; ++k)
+            load_row_vec<SRC, VE>(src, min32(b + lane + k * 64, nv - 1), f[k]);
+#pragma unroll
+        for (int k = 0; k < kQuantReread; ++k)
+            fold_extremes<ASYM, VE>(f[k], lo, hi);
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -682,21 +727,19 @@ __device__ __forceinline__ void quant_row(const Args &a, const unsigned char *__
             lo = __builtin_fminf(lo, __shfl_xor(lo, o, 64));
         hi = __builtin_fmaxf(hi, __shfl_xor(hi, o, 64));
     }
+    // every lane holds the same extremes: make them wave-uniform
+    lo = __builtin_bit_cast(float, uni(__builtin_bit_cast(uint32_t, lo)));
+    hi = __builtin_bit_cast(float, uni(__builtin_bit_cast(uint32_t, hi)));
     const float sc = ASYM ? __fdiv_rn(hi - lo, 255.0f) : __fdiv_rn(hi, 127.0f);
     const float z = (ASYM && sc != 0.0f)
                         ? __builtin_fminf(__builtin_fmaxf(__builtin_rintf(__fdiv_rn(-lo, sc)), 0.0f),
                                           255.0f)
                         : 0.0f;
-#pragma unroll
-    for (int k = 0; k < kQuantKeep; ++k) {
-        const uint32_t i = lane + k * 64;
-        if (i < nv)
-            store_codes<ASYM, VE>(dst, i, keep[k], sc, z);
-    }
-    for (uint32_t i = lane + kQuantKeep * 64; i < nv; i += 64) {
-        float f[VE];
-        load_row_vec<SRC, VE>(src, i, f);
-        store_codes<ASYM, VE>(dst, i, f, sc, z);
+    if (sc == 0.0f || (sc >= 0x1p-100f && sc <= 0x1p100f)) {
+        const float y = sc == 0.0f ? 0.0f : __fdiv_rn(1.0f, sc);
+        emit_row<SRC, ASYM, VE, true>(src, dst, nv, lane, keep, sc, y, z);
+    } else {
+        emit_row<SRC, ASYM, VE, false>(src, dst, nv, lane, keep, sc, 0.0f, z);
     }
     if (lane == 0) {
         a.qs_scales[slot] = sc;
@@ -781,34 +824,35 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
         }
         const uint32_t u = g - ubeg;
         if constexpr (OP == Op::ScatterQuant) {
-            // Window w of rows_per_unit positions (at most one per wave): wave
-            // k quantizes the new token at position w * rpc + k, or clears it
-            // when it is a tail slot.
+            // Window w of rows_per_unit positions of one page: wave k takes
+            // positions w * rpc + k, + k + waves, ... and quantizes each new
+            // token there, or clears it when it is a tail slot.
             const uint64_t w = udiv(start, a.div_rpc) + u;
             const uint64_t q = udiv(w, a.div_upp);
             const uint64_t phys = uni64(ld_idx<IdxT>(a.block_table, sp + q));
-            const uint32_t k = threadIdx.x >> 6;
-            const uint64_t pos = w * rpc + k;
             const uint64_t end = start + len;
-            const uint64_t slot = phys * P + (pos - q * P);
-            if (k < rpc && pos >= start && pos < end) {
-                quant_row<VEC, QM>(a, rowsp + (tb + (pos - start)) * a.out_row_bytes,
-                                   pool + slot * a.row_bytes, slot);
-            } else if (k < rpc && a.zero_tail && pos >= end &&
-                       pos < udiv(end + P - 1, a.div_page) * P) {
-                const uint32_t lane = threadIdx.x & 63;
+            const uint64_t zend = a.zero_tail ? udiv(end + P - 1, a.div_page) * P : end;
+            const uint32_t lane = threadIdx.x & 63;
+            for (uint32_t r = threadIdx.x >> 6; r < rpc; r += kThreads / 64) {
+                const uint64_t pos = w * rpc + r;
+                const uint64_t slot = phys * P + (pos - q * P);
                 unsigned char *row = pool + slot * a.row_bytes;
-                if (a.row_bytes % 16 == 0) {
-                    for (uint32_t i = lane; i < a.row_bytes / 16; i += 64)
-                        st_stream(u32x4(0), reinterpret_cast<u32x4 *>(row) + i);
-                } else {
-                    for (uint32_t i = lane; i < a.row_bytes; i += 64)
-                        st_stream((unsigned char)0, row + i);
-                }
-                if (lane == 0) {
-                    a.qs_scales[slot] = 0.0f;
-                    if (QM & 1)
-                        a.qs_zero_points[slot] = 0;
+                if (pos >= start && pos < end) {
+                    quant_row<VEC, QM>(a, rowsp + (tb + (pos - start)) * a.out_row_bytes, row,
+                                       slot);
+                } else if (pos >= end && pos < zend) {
+                    if (a.row_bytes % 16 == 0) {
+                        for (uint32_t i = lane; i < a.row_bytes / 16; i += 64)
+                            st_stream(u32x4(0), reinterpret_cast<u32x4 *>(row) + i);
+                    } else {
+                        for (uint32_t i = lane; i < a.row_bytes; i += 64)
+                            st_stream((unsigned char)0, row + i);
+                    }
+                    if (lane == 0) {
+                        a.qs_scales[slot] = 0.0f;
+                        if (QM & 1)
+                            a.qs_zero_points[slot] = 0;
+                    }
                 }
             }
         } else if constexpr (OP == Op::Scatter) {

@@ -22,9 +22,9 @@ def hp():
     return block_table_gather_amd
 
 
-def run_case(hp, w, src_type, asym, zero_tail, seed, scale_src=1.0):
-    """Quant-scatter a seeded source into a pool of random codes and
-    parameters; compare the whole pool, scales and zero points."""
+def run_case(hp, w, src_type, asym, zero_tail, seed, scale_src=1.0, src=None):
+    """Quant-scatter a seeded source (or the given one) into a pool of random
+    codes and parameters; compare the whole pool, scales and zero points."""
     qw = dataclasses.replace(w, dtype="u8" if asym else "i8", values="normal", seed=seed)
     d = OnDevice(qw)
     N, P = w.num_pages, w.page_size
@@ -32,8 +32,9 @@ def run_case(hp, w, src_type, asym, zero_tail, seed, scale_src=1.0):
     scales = torch.rand(N * P, generator=g, device=DEV) + 1.0
     zps = (torch.randint(0, 256, (N * P,), generator=g, device=DEV, dtype=torch.int32)
            .to(torch.uint8) if asym else None)
-    src = (torch.randn((w.total_tokens, w.num_heads, w.head_dim), generator=g, device=DEV)
-           * scale_src).to(SRC[src_type])
+    if src is None:
+        src = (torch.randn((w.total_tokens, w.num_heads, w.head_dim), generator=g, device=DEV)
+               * scale_src).to(SRC[src_type])
     desc = hp.Descriptor(d.pool, d.bt, d.sp, d.sl, scales=scales)
     want_pool, want_sc, want_zp = oracle.scatter_quant(
         host_bits(d.pool).view(np.uint8 if asym else np.int8), scales.cpu().numpy(),
@@ -124,3 +125,47 @@ def test_scatter_quant_then_dequant_round_trip(hp):
     step = (x.max(1).values.clamp(min=0) - x.min(1).values.clamp(max=0)) / 255
     err = (back.float().reshape(w.total_tokens, -1) - x).abs().max(1).values
     assert bool(torch.all(err <= step * 1.001 + x.abs().max(1).values * 2.0 ** -8))
+
+
+def near_tie_rows(rng, count, n, asym):
+    """f32 rows whose quotients x / scale sit within a few ulps of a
+    half-integer or an integer: the row's extremes fix the scale (computed
+    here in binary32 the way the quantizer does), the other values are
+    RN((k + 1/2) * scale) or RN(k * scale) moved by -4..4 ulps."""
+    rows = np.empty((count, n), np.float32)
+    for r in range(count):
+        mag = np.float32(np.exp2(rng.uniform(-60, 60)))
+        if asym:
+            lo = -mag * np.float32(rng.uniform(0.2, 1.0))
+            hi = mag * np.float32(rng.uniform(0.2, 1.0))
+            sc = (hi - lo) / np.float32(255)
+            span = min(-lo, hi)
+        else:
+            amax = mag
+            sc = amax / np.float32(127)
+            span = amax
+        kmax = int(np.floor(float(span) / float(sc))) - 1
+        k = rng.integers(-kmax, kmax, n).astype(np.float64) + rng.integers(0, 2, n) * 0.5
+        x = (k * float(sc)).astype(np.float32)
+        m = np.maximum(np.abs(x).view(np.int32) + rng.integers(-4, 5, n).astype(np.int32), 0)
+        x = np.copysign(m.view(np.float32), x)
+        x = np.clip(x, -span, span)
+        if asym:
+            x[0], x[1] = lo, hi
+        else:
+            x[0] = amax if rng.integers(2) else -amax
+        rows[r] = x
+    return rows
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_scatter_quant_near_ties(hp, asym):
+    """Quotients next to the rounding boundaries, where an approximate
+    division would pick the neighbouring code."""
+    w = workloads.random_small(1770 + asym, max_seqs=16, max_len=120, page_sizes=(16,),
+                               heads=(4,), dims=(128,), alias=False, with_start=True)
+    say("scatter quant near ties", asym, w.describe())
+    rng = np.random.default_rng(1771 + asym)
+    rows = near_tie_rows(rng, w.total_tokens, w.num_heads * w.head_dim, asym)
+    src = torch.from_numpy(rows.reshape(w.total_tokens, w.num_heads, w.head_dim)).to(DEV)
+    run_case(hp, w, "f32", asym, True, 1772, src=src)
