@@ -71,6 +71,10 @@ ATTN_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_at
                   "-- python3 bench.py --attention-only")
 ATTN_PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/prof_attn_{d} -o {d} -- "
                 "python3 bench.py --attention-only --kernel-reps 3 --copy-calibration")
+QW_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_qw_trace -o trace "
+                "-- python3 bench.py --quant-write-only")
+QW_PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/prof_qw_{d} -o {d} -- "
+              "python3 bench.py --quant-write-only --kernel-reps 3 --copy-calibration")
 
 
 def kernel_source_hash():
@@ -362,6 +366,119 @@ def summarize_attention(trace_dir, fetch_dir, write_dir):
     print("\n".join(lines + [""] + out))
 
 
+def quant_write_extras(hp, torch, np, dev, stream, reps):
+    """Quantize-on-scatter on the decode batch: its fp16 rows (63,540 tokens,
+    32 heads x 128) written into an int8 pool (symmetric, a scale per slot)
+    and a uint8 pool (a scale and a zero point per slot). Algorithmic bytes:
+    every row read (2 bytes a value) and its codes written (1 byte a value),
+    plus 4 bytes of scale (and 1 of zero point) per token."""
+    import workloads
+    w = workloads.decode()
+    T, H, D = w.total_tokens, w.num_heads, w.head_dim
+
+    def idx(a):
+        return torch.from_numpy(np.asarray(a, dtype=np.uint32).view(np.int32).copy()).to(dev)
+
+    bt, sp, sl = idx(w.block_table), idx(w.seq_ptr), idx(w.seq_lens)
+    g = torch.Generator(device=dev).manual_seed(10)
+    src = torch.randn((T, H, D), generator=g, device=dev).to(torch.float16)
+    pool = torch.empty((w.num_pages, w.page_size, H, D), dtype=torch.int8, device=dev)
+    sc = torch.zeros(w.num_pages * w.page_size, device=dev)
+    zp = torch.zeros(w.num_pages * w.page_size, dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(hp.workspace_bytes(hp.Descriptor(pool, bt, sp, sl), T), 256),
+                     dtype=torch.uint8, device=dev)
+    res = {}
+    for name, pool_t, z in (("int8_symmetric", pool, None),
+                            ("uint8_zero_points", pool.view(torch.uint8), zp)):
+        qd = hp.Descriptor(pool_t, bt, sp, sl, scales=sc)
+
+        def call():
+            hp.scatter_quant(qd, src, zero_points=z, workspace=ws, stream=stream)
+
+        call()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            call()
+        b.record(stream)
+        b.synchronize()
+        ms = a.elapsed_time(b) / reps
+        nbytes = T * H * D * 3 + 4 * T + (T if z is not None else 0)
+        res[name] = {"algorithmic_bytes": nbytes, "launch_us": round(ms * 1e3, 1),
+                     "gb_per_s": round(nbytes / (ms / 1e3) / 1e9, 1)}
+    del pool, src
+    return res
+
+
+def summarize_quant_write(trace_dir, fetch_dir, write_dir):
+    """Kernel durations and calibrated HBM traffic of the quantize-on-scatter
+    kernels (bench.py --quant-write-only runs) into profiles/."""
+    import numpy as np
+    import workloads
+    w = workloads.decode()
+    T, n = w.total_tokens, w.num_heads * w.head_dim
+    algo = {0: 3 * T * n + 4 * T, 1: 3 * T * n + 5 * T}  # by the kernel's asymmetric bit
+
+    def asym_of(name):
+        # QM template argument = source * 2 + asymmetric; the f16 source is 0
+        return int(name.rstrip(">").rsplit(",", 1)[1]) & 1
+
+    trace = _csv_rows(trace_dir, "*kernel_trace.csv")
+    groups = {}
+    for r in trace:
+        name = _short(r["Kernel_Name"])
+        if "(hp::Op)3" not in name:
+            continue
+        groups.setdefault(name, []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# Kernel durations: quantize-on-scatter, decode batch (rocprofv3 kernel trace)", "",
+             "Command (from the repository root, on one MI355X):", "", f"    {QW_TRACE_CMD}", "",
+             "The decode batch's fp16 rows (63,540 tokens, 32 heads x 128) quantized into an",
+             "int8 pool (symmetric: a scale per slot) and a uint8 pool (a scale and a zero point",
+             "per slot), each call made 21 times. Durations in microseconds.", "",
+             "| kernel | calls | avg us | min us | max us | algorithmic GB | GB/s at avg |",
+             "|---|---|---|---|---|---|---|"]
+    for name, ts in sorted(groups.items()):
+        nbytes = algo[asym_of(name)]
+        lines.append(f"| `{name}` | {len(ts)} | {np.mean(ts):.1f} | {min(ts):.1f} | "
+                     f"{max(ts):.1f} | {nbytes / 1e9:.4f} | {nbytes / (np.mean(ts) * 1e3):.0f} |")
+    with open(os.path.join(PROFILES, "quant_write_decode_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    fetch = _csv_rows(fetch_dir, "*counter_collection.csv")
+    write = _csv_rows(write_dir, "*counter_collection.csv")
+    ff = CALIBRATION_BYTES / (_calibration(fetch, "FETCH_SIZE") * 1024)
+    wf = CALIBRATION_BYTES / (_calibration(write, "WRITE_SIZE") * 1024)
+
+    def per_launch(rows, counter):
+        agg = {}
+        for r in rows:
+            name = _short(r["Kernel_Name"])
+            if r["Counter_Name"] == counter and "(hp::Op)3" in name:
+                agg.setdefault(name, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    fk, wk = per_launch(fetch, "FETCH_SIZE"), per_launch(write, "WRITE_SIZE")
+    out = ["# HBM traffic per launch: quantize-on-scatter, decode batch (rocprofv3 counters)", "",
+           "Two counter passes, each in its own run (commands from the repository root):", "",
+           f"    {QW_PMC_CMD.format(c='FETCH_SIZE', d='fetch')}",
+           f"    {QW_PMC_CMD.format(c='WRITE_SIZE', d='write')}", "",
+           "Calibrated with three plain 1 GiB device copies in the same runs: bytes =",
+           f"FETCH_SIZE x 1024 x {ff:.4f} and WRITE_SIZE x 1024 x {wf:.4f}.",
+           "Algorithmic bytes: every fp16 row read once, its int8 codes written once, and",
+           "4 bytes of scale (plus 1 of zero point) written per token.", "",
+           "| kernel | read GB | write GB | total GB | algorithmic GB |", "|---|---|---|---|---|"]
+    for name in sorted(fk):
+        if name not in wk:
+            continue
+        rb, wb = fk[name] * 1024 * ff, wk[name] * 1024 * wf
+        out.append(f"| `{name}` | {rb / 1e9:.4f} | {wb / 1e9:.4f} | {(rb + wb) / 1e9:.4f} | "
+                   f"{algo[asym_of(name)] / 1e9:.4f} |")
+    with open(os.path.join(PROFILES, "quant_write_decode_hbm_traffic.md"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(lines + [""] + out))
+
+
 # ---- batched moves (optional) ----------------------------------------------------
 
 def attention_extras(hp, torch, np, dev, stream, reps):
@@ -521,12 +638,18 @@ def main():
     ap.add_argument("--attention-only", action="store_true",
                     help="only the decode-attention measurements (profiling runs)")
     ap.add_argument("--summarize-attention", nargs=3, metavar=("TRACE", "FETCH", "WRITE"))
+    ap.add_argument("--quant-write-only", action="store_true",
+                    help="only the quantize-on-scatter measurements (profiling runs)")
+    ap.add_argument("--summarize-quant-write", nargs=3, metavar=("TRACE", "FETCH", "WRITE"))
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles)
         return
     if args.summarize_attention:
         summarize_attention(*args.summarize_attention)
+        return
+    if args.summarize_quant_write:
+        summarize_quant_write(*args.summarize_quant_write)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -548,6 +671,13 @@ def main():
         stream = torch.cuda.current_stream(dev)
         print(json.dumps({"attention": attention_extras(hp, torch, np, dev, stream,
                                                         args.kernel_reps)}), flush=True)
+        return
+    if args.quant_write_only:
+        if args.copy_calibration:
+            calibration_copies(torch, dev)
+        stream = torch.cuda.current_stream(dev)
+        print(json.dumps({"quantize_on_scatter": quant_write_extras(
+            hp, torch, np, dev, stream, args.kernel_reps)}), flush=True)
         return
     w = workloads.decode()
     T, S, K = w.total_tokens, w.num_seqs, w.num_block_entries
@@ -766,22 +896,9 @@ def main():
             schemes[name] = {"algorithmic_bytes": qb, "launch_us": round(t_q * 1e3, 1),
                              "gb_per_s": round(qb / (t_q / 1e3) / 1e9, 1)}
         del qout
-        # quantize-on-scatter: the decode batch's fp16 rows written into an
-        # int8 pool (symmetric) and a uint8 pool with zero points (asymmetric)
-        qw_pool = torch.empty_like(qpool)
-        qw_sc = torch.zeros(wq.num_pages * 16, device=dev)
-        qw_zp = torch.zeros(wq.num_pages * 16, dtype=torch.uint8, device=dev)
-        quant_write = {}
-        for name, pool_t, zp in (("int8_symmetric", qw_pool, None),
-                                 ("uint8_zero_points", qw_pool.view(torch.uint8), qw_zp)):
-            qd = hp.Descriptor(pool_t, bt, sp, sl, scales=qw_sc)
-            t_w = back_to_back(lambda: hp.scatter_quant(qd, out, zero_points=zp, stream=stream))
-            qb = T * H * D * 3 + 4 * T + (T if zp is not None else 0)
-            quant_write[name] = {"algorithmic_bytes": qb, "launch_us": round(t_w * 1e3, 1),
-                                 "gb_per_s": round(qb / (t_w / 1e3) / 1e9, 1)}
-        del qw_pool
         result["extras"] = {
-            "quantize_on_scatter": quant_write,
+            "quantize_on_scatter": quant_write_extras(hp, torch, np, dev, stream,
+                                                      args.kernel_reps),
             "attention": attention_extras(hp, torch, np, dev, stream, args.kernel_reps),
             "dequant_schemes": schemes,
             "batched_append": batched_append(hp, torch, np, dev, stream, args.kernel_reps),

@@ -577,25 +577,43 @@ __device__ __forceinline__ void dequant_span_q(const Args &a, const unsigned cha
 
 constexpr int kQuantKeep = 8;  // vectors per lane held in registers between the passes
 
+// Raw bits of one vector of a source row (8 values: 16 bytes of f16/bf16 or
+// 32 of f32), or of a single value. A row's kept vectors are held in this
+// form and unpacked to binary32 where they are used: 4 registers per vector
+// of 16-bit values instead of 8.
 template <int SRC, int VE>
-__device__ __forceinline__ void load_row_vec(const unsigned char *row, uint32_t i, float (&f)[VE]) {
+struct QVec {
+    u32x4 w[(VE == 8 && SRC == 2) ? 2 : 1];
+};
+template <int SRC, int VE>
+__device__ __forceinline__ QVec<SRC, VE> load_qvec(const unsigned char *row, uint32_t i) {
+    QVec<SRC, VE> v;
     if constexpr (VE == 1) {
-        if constexpr (SRC == 2) {
-            f[0] = reinterpret_cast<const float *>(row)[i];
-        } else {
-            const uint16_t b = reinterpret_cast<const uint16_t *>(row)[i];
-            f[0] = SRC == 1 ? __builtin_bit_cast(float, (uint32_t)b << 16)
-                            : (float)__builtin_bit_cast(_Float16, b);
-        }
+        v.w[0] = u32x4(0);
+        v.w[0].x = SRC == 2 ? reinterpret_cast<const uint32_t *>(row)[i]
+                            : (uint32_t)reinterpret_cast<const uint16_t *>(row)[i];
     } else if constexpr (SRC == 2) {
         const u32x4 *p = reinterpret_cast<const u32x4 *>(row) + 2 * i;
-        const u32x4 v0 = ld_stream<true>(p), v1 = ld_stream<true>(p + 1);
-        __builtin_memcpy(&f[0], &v0, 16);
-        __builtin_memcpy(&f[4], &v1, 16);
+        v.w[0] = ld_stream<true>(p);
+        v.w[1] = ld_stream<true>(p + 1);
     } else {
-        const u32x4 v = ld_stream<true>(reinterpret_cast<const u32x4 *>(row) + i);
+        v.w[0] = ld_stream<true>(reinterpret_cast<const u32x4 *>(row) + i);
+    }
+    return v;
+}
+template <int SRC, int VE>
+__device__ __forceinline__ void unpack_qvec(const QVec<SRC, VE> &v, float (&f)[VE]) {
+    if constexpr (VE == 1) {
+        const uint32_t h = v.w[0].x;
+        f[0] = SRC == 2 ? __builtin_bit_cast(float, h)
+             : SRC == 1 ? __builtin_bit_cast(float, h << 16)
+                        : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+    } else if constexpr (SRC == 2) {
+        __builtin_memcpy(&f[0], &v.w[0], 16);
+        __builtin_memcpy(&f[4], &v.w[1], 16);
+    } else {
         uint32_t w[4];
-        __builtin_memcpy(w, &v, 16);
+        __builtin_memcpy(w, &v.w[0], 16);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if constexpr (SRC == 1) {
@@ -607,6 +625,10 @@ __device__ __forceinline__ void load_row_vec(const unsigned char *row, uint32_t 
             }
         }
     }
+}
+template <int SRC, int VE>
+__device__ __forceinline__ void load_row_vec(const unsigned char *row, uint32_t i, float (&f)[VE]) {
+    unpack_qvec<SRC, VE>(load_qvec<SRC, VE>(row, i), f);
 }
 
 // Quotients x / s rounded to nearest even, as one IEEE binary32 division
@@ -629,23 +651,50 @@ __device__ __forceinline__ float quotient(float x, float s, float y) {
     }
 }
 
+// The code of one value in the low byte of the result: the quotient's
+// nearest integer (ties to even), plus the zero point, clamped. Adding
+// 1.5 * 2^23 to a binary32 value of magnitude below 2^22 rounds it to an
+// integer, ties to even (the sum's ulp is 1 and 1.5 * 2^23 is even), and
+// leaves that integer in the sum's low bits; quotients here stay below 2^9
+// in magnitude (|x| is at most about 255 scales). Symmetric codes are
+// clamped first, which gives the same integer since the bounds are integers.
+// zb is the bit pattern of 1.5 * 2^23 minus the zero point.
+template <bool ASYM, bool FAST>
+__device__ __forceinline__ uint32_t code_bits(float x, float s, float y, int32_t zb) {
+#pragma clang fp contract(off)
+    constexpr float kRound = 0x1.8p23f;
+    const float q = quotient<FAST>(x, s, y);
+    if constexpr (ASYM) {
+        const int32_t c = (int32_t)__builtin_bit_cast(uint32_t, q + kRound) - zb;
+        return (uint32_t)(c < 0 ? 0 : (c > 255 ? 255 : c));
+    } else {
+        const float t = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
+        return __builtin_bit_cast(uint32_t, t + kRound);  // low byte: two's complement
+    }
+}
+
+// Low bytes of a, b, c, d as one word (a in byte 0).
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c,
+                                                   uint32_t d) {
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
 template <bool ASYM, int VE, bool FAST>
 __device__ __forceinline__ void store_codes(unsigned char *dst, uint32_t i, const float (&f)[VE],
-                                            float s, float y, float z) {
-    uint8_t c[VE];
+                                            float s, float y, int32_t zb) {
+    uint32_t c[VE];
 #pragma unroll
-    for (int k = 0; k < VE; ++k) {
-        float q = __builtin_rintf(quotient<FAST>(f[k], s, y));
-        q = ASYM ? __builtin_fminf(__builtin_fmaxf(q + z, 0.0f), 255.0f)
-                 : __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
-        c[k] = ASYM ? (uint8_t)(int32_t)q : (uint8_t)(int8_t)(int32_t)q;
-    }
+    for (int k = 0; k < VE; ++k)
+        c[k] = code_bits<ASYM, FAST>(f[k], s, y, zb);
     if constexpr (VE == 8) {
         u32x2 v;
-        __builtin_memcpy(&v, c, 8);
+        v.x = pack_low_bytes(c[0], c[1], c[2], c[3]);
+        v.y = pack_low_bytes(c[4], c[5], c[6], c[7]);
         st_stream(v, reinterpret_cast<u32x2 *>(dst) + i);
     } else {
-        st_stream(c[0], dst + i);
+        st_stream((unsigned char)c[0], dst + i);
     }
 }
 
@@ -673,11 +722,20 @@ constexpr int kQuantReread = 4;  // vectors per lane in flight when a row is rea
 template <int SRC, bool ASYM, int VE, bool FAST>
 __device__ __forceinline__ void emit_row(const unsigned char *__restrict__ src,
                                          unsigned char *__restrict__ dst, uint32_t nv,
-                                         uint32_t lane, const float (&keep)[kQuantKeep][VE],
-                                         float s, float y, float z) {
+                                         uint32_t lane, const QVec<SRC, VE> (&keep)[kQuantKeep],
+                                         float s, float y, int32_t zb) {
 #pragma unroll
-    for (int k = 0; k < kQuantKeep; ++k)
-        store_codes<ASYM, VE, FAST>(dst, min32(lane + k * 64, nv - 1), keep[k], s, y, z);
+    for (int k = 0; k < kQuantKeep; ++k) {
+        // unpack again: an empty asm hides that the first pass already did,
+        // so the compiler keeps the raw words rather than 8 binary32 values
+        QVec<SRC, VE> v = keep[k];
+#pragma unroll
+        for (int j = 0; j < (int)(sizeof(v.w) / sizeof(v.w[0])); ++j)
+            asm volatile("" : "+v"(v.w[j]));
+        float f[VE];
+        unpack_qvec<SRC, VE>(v, f);
+        store_codes<ASYM, VE, FAST>(dst, min32(lane + k * 64, nv - 1), f, s, y, zb);
+    }
     for (uint32_t b = kQuantKeep * 64; b < nv; b += kQuantReread * 64) {
         float f[kQuantReread][VE];
 #pragma unroll
@@ -685,7 +743,7 @@ __device__ __forceinline__ void emit_row(const unsigned char *__restrict__ src,
             load_row_vec<SRC, VE>(src, min32(b + lane + k * 64, nv - 1), f[k]);
 #pragma unroll
         for (int k = 0; k < kQuantReread; ++k)
-            store_codes<ASYM, VE, FAST>(dst, min32(b + lane + k * 64, nv - 1), f[k], s, y, z);
+            store_codes<ASYM, VE, FAST>(dst, min32(b + lane + k * 64, nv - 1), f[k], s, y, zb);
     }
 }
 
@@ -703,15 +761,18 @@ __device__ __forceinline__ void quant_row(const Args &a, const unsigned char *__
     constexpr int VE = VEC == 16 ? 8 : 1;  // values per vector
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t nv = a.row_bytes / VE;  // at least 1
-    float keep[kQuantKeep][VE];
+    QVec<SRC, VE> keep[kQuantKeep];
     float lo = 0.0f, hi = 0.0f;  // symmetric: hi is the largest |x|
     // a clamped index repeats the row's last vector: it cannot move an extreme
 #pragma unroll
     for (int k = 0; k < kQuantKeep; ++k)
-        load_row_vec<SRC, VE>(src, min32(lane + k * 64, nv - 1), keep[k]);
+        keep[k] = load_qvec<SRC, VE>(src, min32(lane + k * 64, nv - 1));
 #pragma unroll
-    for (int k = 0; k < kQuantKeep; ++k)
-        fold_extremes<ASYM, VE>(keep[k], lo, hi);
+    for (int k = 0; k < kQuantKeep; ++k) {
+        float f[VE];
+        unpack_qvec<SRC, VE>(keep[k], f);
+        fold_extremes<ASYM, VE>(f, lo, hi);
+    }
     for (uint32_t b = kQuantKeep * 64; b < nv; b += kQuantReread * 64) {
         float f[kQuantReread][VE];
 #pragma unroll
@@ -735,11 +796,19 @@ __device__ __forceinline__ void quant_row(const Args &a, const unsigned char *__
                         ? __builtin_fminf(__builtin_fmaxf(__builtin_rintf(__fdiv_rn(-lo, sc)), 0.0f),
                                           255.0f)
                         : 0.0f;
+    const int32_t zb = (int32_t)__builtin_bit_cast(uint32_t, 0x1.8p23f) - (int32_t)z;
     if (sc == 0.0f || (sc >= 0x1p-100f && sc <= 0x1p100f)) {
         const float y = sc == 0.0f ? 0.0f : __fdiv_rn(1.0f, sc);
-        emit_row<SRC, ASYM, VE, true>(src, dst, nv, lane, keep, sc, y, z);
+        emit_row<SRC, ASYM, VE, true>(src, dst, nv, lane, keep, sc, y, zb);
     } else {
-        emit_row<SRC, ASYM, VE, false>(src, dst, nv, lane, keep, sc, 0.0f, z);
+        // scales this small or large are rare: read the row again, one
+        // vector at a time, and divide
+#pragma unroll 1
+        for (uint32_t i = lane; i < nv; i += 64) {
+            float f[VE];
+            load_row_vec<SRC, VE>(src, i, f);
+            store_codes<ASYM, VE, false>(dst, i, f, sc, 0.0f, zb);
+        }
     }
     if (lane == 0) {
         a.qs_scales[slot] = sc;
