@@ -207,8 +207,9 @@ hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype,
  *   uint8 pool (asymmetric, zero_points required):
  *     lo = min(0, min x), hi = max(0, max x), scale = (hi - lo) / 255,
  *     z = clamp(rint(-lo / scale), 0, 255), q = clamp(rint(x / scale) + z, 0, 255)
- * and a zero scale gives zero codes and zero point. hp_gather_dequant_q with
- * the per-block-affine scheme (or hp_gather_dequant for int8) reads them back.
+ * and a zero scale gives zero codes and zero point. Rows holding NaN or an
+ * infinity get unspecified codes. hp_gather_dequant_q with the
+ * per-block-affine scheme (or hp_gather_dequant for int8) reads them back.
  *
  * desc        the quantized pool (dtype HP_DTYPE_I8 or HP_DTYPE_U8); desc->scales
  *             (fp32, num_pages * page_size) is WRITTEN at every written slot.
