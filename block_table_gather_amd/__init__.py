@@ -218,6 +218,10 @@ class Descriptor:
         self.seq_lens, self.scales = seq_lens, scales
         self.c = HpDesc()
         c = self.c
+        # The struct holds raw device pointers into these tensors; the
+        # reference from the struct back to this object keeps them alive for
+        # as long as any handle from with_tokens() exists.
+        c._owner = self
         c.rank, c.paged_axis = rank, paged_axis
         c.index_type = _index_code(seq_ptr) if index_type is None else index_type
         c.dtype = _dtype_code(page_pool) if dtype is None else dtype
@@ -242,6 +246,8 @@ class Descriptor:
         return self.seq_ptr.device
 
     def with_tokens(self, total_tokens):
+        """The C descriptor (by reference) with total_tokens set. The handle
+        keeps this descriptor, and so its tensors, alive."""
         self.c.total_tokens = int(total_tokens)
         return ctypes.byref(self.c)
 

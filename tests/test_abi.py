@@ -368,3 +368,29 @@ def test_copy_pages_rejections():
     assert cb(_arr(P1, None)) == S["HP_ERR_NULL"]
     assert cb(_arr(P1, P2 + 8)) == S["HP_ERR_ALIGN"]
     assert cb(_arr(P1, P2), n=0) == S["HP_OK"]
+
+
+def test_descriptor_handle_keeps_tensors_alive():
+    """The handle from with_tokens() carries raw pointers into the descriptor's
+    tensors, so it keeps them alive even when the Descriptor object and every
+    other reference are gone (a freed index tensor would be handed to the next
+    allocation, and its pointer would then name foreign data)."""
+    import gc
+    import weakref
+
+    import numpy as np
+    import torch
+
+    def idx(a):
+        return torch.from_numpy(np.asarray(a, np.uint32).view(np.int32).copy())
+
+    pool = torch.zeros((4, 16, 2, 8), dtype=torch.float16)
+    bt = idx([0, 1])
+    alive = weakref.ref(bt)
+    handle = hp.Descriptor(pool, bt, idx([0, 2]), idx([20])).with_tokens(20)
+    del bt
+    gc.collect()
+    assert alive() is not None
+    del handle
+    gc.collect()
+    assert alive() is None
