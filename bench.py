@@ -53,12 +53,16 @@ KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("hp_kernels.hip", "hp_api.cpp"
                                                   "hp_device.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "gather_copy_kernel_decode_traffic.json")
-GATHER_KERNEL = "copy_kernel<unsigned int, (hp::Op)0, 16, true, true, -1>"
+GATHER_KERNEL = "copy_kernel<unsigned int, (hp::Op)0, 16, true, true, -1, 2>"
 KERNEL_LABELS = {
-    "copy_kernel<unsigned int, (hp::Op)0, 16, true, true, -1>": "gather (u32, 16 B vectors, fused, streaming loads)",
-    "copy_kernel<unsigned int, (hp::Op)1, 16, true, true, -1>": "scatter (u32, 16 B vectors, fused, streamed source)",
-    "copy_kernel<unsigned int, (hp::Op)1, 16, true, false, -1>": "scatter (u32, 16 B vectors, fused)",
-    "copy_kernel<unsigned int, (hp::Op)2, 8, true, false, -1>": "dequant-gather (u32, 8 B int8 vectors, fused)",
+    "copy_kernel<unsigned int, (hp::Op)0, 16, true, true, -1, 2>":
+        "gather (u32, 16 B vectors, fused, streaming loads, 2 loads per lane)",
+    "copy_kernel<unsigned int, (hp::Op)1, 16, true, true, -1, 2>":
+        "scatter (u32, 16 B vectors, fused, streamed source, 2 loads per lane)",
+    "copy_kernel<unsigned int, (hp::Op)1, 16, true, false, -1, 8>":
+        "scatter (u32, 16 B vectors, fused, 8 loads per lane)",
+    "copy_kernel<unsigned int, (hp::Op)2, 8, true, false, -1, 8>":
+        "dequant-gather (u32, 8 B int8 vectors, fused)",
     "validate_one_kernel<unsigned int>": "validator, one workgroup (u32)",
     "validate_kernel<unsigned int>": "validator (u32)",
     "validate_init_kernel": "validator init",

@@ -240,6 +240,9 @@ hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const Members &
     switch (op) {
     case hp::Op::Gather:
         unit_bytes = HP_GATHER_UNIT_BYTES;
+        if (d->num_seqs <= hp::kFusedMaxSeqs &&
+            d->num_seqs * HP_GATHER_UNIT_BYTES_PER_SEQ > unit_bytes)
+            unit_bytes = d->num_seqs * HP_GATHER_UNIT_BYTES_PER_SEQ;
         j.units_per_group = HP_GATHER_UNITS_PER_GROUP;
         j.load_nt = (flags & HP_FLAG_STREAM) != 0;
         break;

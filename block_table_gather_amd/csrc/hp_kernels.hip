@@ -207,30 +207,134 @@ __device__ __forceinline__ void scan_range(const Args &a, uint32_t s0, uint32_t 
     __syncthreads();
 }
 
+// Gather and scatter workgroups find their first unit's sequence inside the
+// fused scan (fused_scan_locate); dequant and quantize-on-scatter search the
+// scanned table afterwards. Measured on MI355X on the decode batch: the
+// in-scan lookup gains 5 % on gather and scatter (8 KB units) and loses
+// 0.5 % on dequant, whose larger units make the lookup a smaller share.
+constexpr bool locate_in_scan(Op op) { return op == Op::Gather || op == Op::Scatter; }
+
+// What a workgroup needs about the sequence that holds its first unit.
+struct FirstSeq {
+    uint64_t len, sp, start, tb;
+    uint32_t s, ubeg, uend, pad;
+};
+
+// Sequences per thread whose count, start and seq_ptr stay in registers
+// between the two passes of the fused scan (up to kThreads * this many
+// sequences; beyond, the second pass reads them again).
+constexpr uint32_t kScanRegs = 4;
+
+// The fused scan of a copy workgroup: writes unit_end[s] and tok_begin[s] for
+// every sequence, like scan_range, and the thread whose sequence holds unit
+// g0 also writes that sequence's values to `first`. The workgroup then starts
+// moving after one pass of loads (counts and seq_ptr together) and two
+// barriers, with no search and no further load. Ends with a barrier.
+template <typename IdxT, Op OP>
+__device__ __forceinline__ void fused_scan_locate(const Args &a, uint32_t S, uint32_t g0,
+                                                  uint32_t *unit_end, uint64_t *tok_begin,
+                                                  FirstSeq *first) {
+    const uint32_t per = (S + kThreads - 1) / kThreads;  // wave-uniform
+    const uint32_t i0 = min32(S, threadIdx.x * per);
+    const uint32_t i1 = min32(S, (threadIdx.x + 1) * per);
+    const bool with_start = writes_pool(OP) && a.seq_start;
+    uint64_t u = 0, t = 0;
+    uint64_t lenr[kScanRegs], str[kScanRegs], spr[kScanRegs];
+    if (per <= kScanRegs) {
+        // Loads of every held sequence at once (an index past S re-reads the
+        // last entry; its values are not used).
+#pragma unroll
+        for (uint32_t k = 0; k < kScanRegs; ++k) {
+            if (k < per) {
+                const uint32_t i = min32(i0 + k, S - 1);
+                lenr[k] = ld_idx<IdxT>(a.seq_lens, i);
+                str[k] = with_start ? ld_idx<IdxT>(a.seq_start, i) : 0;
+                spr[k] = ld_idx<IdxT>(a.seq_ptr, i);
+            }
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < kScanRegs; ++k) {
+            if (i0 + k < i1) {
+                u += units_of<OP>(a, lenr[k], str[k]);
+                t += lenr[k];
+            }
+        }
+    } else {
+        for (uint32_t i = i0; i < i1; ++i) {
+            const uint64_t len = ld_idx<IdxT>(a.seq_lens, i);
+            u += units_of<OP>(a, len, with_start ? ld_idx<IdxT>(a.seq_start, i) : 0);
+            t += len;
+        }
+    }
+    uint64_t tu, tt;
+    group_exclusive_scan(u, t, tu, tt);
+    if (per <= kScanRegs) {
+#pragma unroll
+        for (uint32_t k = 0; k < kScanRegs; ++k) {
+            const uint32_t i = i0 + k;
+            if (i < i1) {
+                const uint64_t ub = u;
+                u += units_of<OP>(a, lenr[k], str[k]);
+                unit_end[i] = (uint32_t)u;
+                tok_begin[i] = t;
+                if (g0 >= ub && g0 < u)
+                    *first = FirstSeq{lenr[k], spr[k], str[k], t, i, (uint32_t)ub, (uint32_t)u, 0};
+                t += lenr[k];
+            }
+        }
+    } else {
+        for (uint32_t i = i0; i < i1; ++i) {
+            const uint64_t len = ld_idx<IdxT>(a.seq_lens, i);
+            const uint64_t st = with_start ? ld_idx<IdxT>(a.seq_start, i) : 0;
+            const uint64_t ub = u;
+            u += units_of<OP>(a, len, st);
+            unit_end[i] = (uint32_t)u;
+            tok_begin[i] = t;
+            if (g0 >= ub && g0 < u)
+                *first = FirstSeq{len, ld_idx<IdxT>(a.seq_ptr, i), st, t, i, (uint32_t)ub,
+                                  (uint32_t)u, 0};
+            t += len;
+        }
+    }
+    __syncthreads();
+}
+
 // ---- span movers -------------------------------------------------------------
 
-template <int VEC, bool NTL>
-__device__ __forceinline__ void copy_span(const unsigned char *__restrict__ src,
-                                          unsigned char *__restrict__ dst, uint32_t nbytes) {
+// U loads per lane in flight, then the U stores; U * kThreads vectors per
+// round.
+template <int U, int VEC, bool NTL>
+__device__ __forceinline__ void copy_rounds(const typename Vec<VEC>::T *__restrict__ s,
+                                            typename Vec<VEC>::T *__restrict__ d, uint32_t n) {
     using V = typename Vec<VEC>::T;
-    const V *s = reinterpret_cast<const V *>(src);
-    V *d = reinterpret_cast<V *>(dst);
-    const uint32_t n = nbytes / VEC;
-    for (uint32_t base = threadIdx.x; base < n; base += kThreads * kCopyUnroll) {
-        V tmp[kCopyUnroll];
+    for (uint32_t base = threadIdx.x; base < n; base += kThreads * U) {
+        V tmp[U];
 #pragma unroll
-        for (int j = 0; j < kCopyUnroll; ++j) {
+        for (int j = 0; j < U; ++j) {
             const uint32_t i = base + j * kThreads;
             if (i < n)
                 tmp[j] = ld_stream<NTL>(s + i);
         }
 #pragma unroll
-        for (int j = 0; j < kCopyUnroll; ++j) {
+        for (int j = 0; j < U; ++j) {
             const uint32_t i = base + j * kThreads;
             if (i < n)
                 st_stream(tmp[j], d + i);
         }
     }
+}
+
+// U loads in flight per lane. The launch picks the smallest U of 2, 4, 8
+// that covers one work unit: loads past a unit's end sat behind branches
+// that still cost issue slots and waits (decode batch, 8 KB units: U = 2 is
+// 5 % ahead of U = 8 on gather and scatter, and a run-time choice between the
+// two bodies inside one kernel lost that again).
+template <int U, int VEC, bool NTL>
+__device__ __forceinline__ void copy_span(const unsigned char *__restrict__ src,
+                                          unsigned char *__restrict__ dst, uint32_t nbytes) {
+    using V = typename Vec<VEC>::T;
+    copy_rounds<U, VEC, NTL>(reinterpret_cast<const V *>(src), reinterpret_cast<V *>(dst),
+                             nbytes / VEC);
 }
 
 template <int VEC>
@@ -827,7 +931,7 @@ __host__ __device__ constexpr size_t lds_table_bytes(uint32_t S) {
 
 // One kernel for all three moves. FUSED: per-sequence offsets rebuilt in LDS
 // (dynamic LDS = 8*S + 4*S bytes); otherwise read from the plan arrays.
-template <typename IdxT, Op OP, int VEC, bool FUSED, bool NTL, int QM = -1>
+template <typename IdxT, Op OP, int VEC, bool FUSED, bool NTL, int QM = -1, int U = kCopyUnroll>
 __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const uint32_t S = a.num_seqs;
@@ -844,10 +948,15 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
         __syncthreads();
         tab = t;
     }
+    const uint32_t g0 = group_order(blockIdx.x, gridDim.x) * a.units_per_group;
+    __shared__ FirstSeq first;
     if constexpr (FUSED) {
         uint64_t *tb = reinterpret_cast<uint64_t *>(lds);
         uint32_t *ue = reinterpret_cast<uint32_t *>(lds + 8 * (size_t)S);
-        scan_range<IdxT, OP>(a, 0, S, 0, 0, ue, tb);
+        if constexpr (locate_in_scan(OP))
+            fused_scan_locate<IdxT, OP>(a, S, g0, ue, tb, &first);
+        else
+            scan_range<IdxT, OP>(a, 0, S, 0, 0, ue, tb);
         unit_end = ue;
         tok_begin = tb;
     } else {
@@ -855,26 +964,14 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
         tok_begin = a.g_tok_begin;
     }
     const uint32_t total = uni(unit_end[S - 1]);
-    const uint32_t g0 = group_order(blockIdx.x, gridDim.x) * a.units_per_group;
     if (g0 >= total)
         return;
     const uint32_t g1 = min32(g0 + a.units_per_group, total);
 
-    // First sequence whose units reach past g0.
-    uint32_t lo = 0, hi = S - 1;
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (unit_end[mid] > g0)
-            hi = mid;
-        else
-            lo = mid + 1;
-    }
-    uint32_t s = uni(lo);
-
     const uint32_t P = a.page_size, rpc = a.rows_per_unit;
     unsigned char *const pool = a.pool[blockIdx.y];
     unsigned char *const rowsp = a.rows[blockIdx.y];
-    uint32_t ubeg = 0, uend = 0;
+    uint32_t s = 0, ubeg = 0, uend = 0;
     uint64_t len = 0, sp = 0, start = 0, tb = 0;
     auto load_seq = [&](uint32_t q) {
         ubeg = q ? uni(unit_end[q - 1]) : 0;
@@ -884,7 +981,29 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
         sp = uni64(ld_idx<IdxT>(a.seq_ptr, q));
         start = (writes_pool(OP) && a.seq_start) ? uni64(ld_idx<IdxT>(a.seq_start, q)) : 0;
     };
-    load_seq(s);
+    if (FUSED && locate_in_scan(OP)) {
+        // Written by the thread whose sequence holds unit g0 (g0 < total, so
+        // there is one).
+        s = uni(first.s);
+        ubeg = uni(first.ubeg);
+        uend = uni(first.uend);
+        tb = uni64(first.tb);
+        len = uni64(first.len);
+        sp = uni64(first.sp);
+        start = uni64(first.start);
+    } else {
+        // First sequence whose units reach past g0.
+        uint32_t lo = 0, hi = S - 1;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (unit_end[mid] > g0)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        s = uni(lo);
+        load_seq(s);
+    }
 
     for (uint32_t g = g0; g < g1; ++g) {
         while (g >= uend) {
@@ -937,7 +1056,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
             const uint64_t wb = pos0 + rpc < end ? pos0 + rpc : end;
             if (wa < wb) {
                 const unsigned char *from = rowsp + (tb + (wa - start)) * a.row_bytes;
-                copy_span<VEC, NTL>(from, page + (slot0 + (uint32_t)(wa - pos0)) * a.row_bytes,
+                copy_span<U, VEC, NTL>(from, page + (slot0 + (uint32_t)(wa - pos0)) * a.row_bytes,
                                (uint32_t)(wb - wa) * a.row_bytes);
             }
             if (a.zero_tail) {
@@ -957,7 +1076,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
             const unsigned char *from = pool + (phys * P + slot0) * a.row_bytes;
             unsigned char *to = rowsp + (tb + t0) * a.out_row_bytes;
             if constexpr (OP == Op::Gather) {
-                copy_span<VEC, NTL>(from, to, rows * a.row_bytes);
+                copy_span<U, VEC, NTL>(from, to, rows * a.row_bytes);
             } else if constexpr (QM >= 0) {
                 const float *sl = QM == 0 ? a.scales[blockIdx.y] + phys * P + slot0 : nullptr;
                 dequant_span_q<VEC, QM>(a, from, sl, phys * P + slot0, to, rows, tab);
@@ -1153,7 +1272,8 @@ __global__ __launch_bounds__(kThreads) void copy_pages_kernel(PArgs a) {
     const uint64_t off = (uint64_t)c * kPageChunkBytes;
     const uint64_t left = a.page_bytes - off;
     const uint32_t n = (uint32_t)(left < kPageChunkBytes ? left : kPageChunkBytes);
-    copy_span<VEC, true>(pool + src * a.page_bytes + off, pool + dst * a.page_bytes + off, n);
+    copy_span<kCopyUnroll, VEC, true>(pool + src * a.page_bytes + off, pool + dst * a.page_bytes + off,
+                                      n);
     float *scales = a.scales[blockIdx.y];
     if (scales && c == 0) {
         for (uint32_t t = threadIdx.x; t < a.page_size; t += kThreads)
@@ -1183,14 +1303,14 @@ __global__ __launch_bounds__(256) void check_pages_kernel(const void *src_pages,
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-template <typename IdxT, Op OP, int VEC, bool NTL, int QM = -1>
+template <typename IdxT, Op OP, int VEC, bool NTL, int QM = -1, int U = kCopyUnroll>
 hipError_t launch_vec(const Args &a, bool fused, dim3 grid, uint32_t plan_chunks,
                       uint32_t *unit_end, uint64_t *tok_begin, hipStream_t stream) {
     const size_t qlds =
         (OP == Op::Dequant && (QM == 2 || QM == 3)) ? sizeof(QParam) * (size_t)a.quant_channels : 0;
     if (fused) {
         const size_t lds = lds_table_bytes(a.num_seqs) + qlds;
-        hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, true, NTL, QM>), grid, dim3(kThreads), lds,
+        hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, true, NTL, QM, U>), grid, dim3(kThreads), lds,
                            stream, a);
         return hipGetLastError();
     }
@@ -1209,7 +1329,7 @@ hipError_t launch_vec(const Args &a, bool fused, dim3 grid, uint32_t plan_chunks
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, false, NTL, QM>), grid, dim3(kThreads), qlds,
+    hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, false, NTL, QM, U>), grid, dim3(kThreads), qlds,
                        stream, a);
     return hipGetLastError();
 }
@@ -1220,7 +1340,7 @@ hipError_t launch_vec(const Args &a, bool fused, dim3 grid, uint32_t plan_chunks
 // dequant's 1:2 read:write mix reads through the cache.
 template <typename IdxT, Op OP, int VEC>
 hipError_t launch_policy(const Args &a, bool ntl, bool fused, dim3 grid, uint32_t chunks,
-                         uint32_t *ue, uint64_t *tb, hipStream_t st, int qm) {
+                         uint32_t *ue, uint64_t *tb, hipStream_t st, int qm, int u) {
     if constexpr (OP == Op::ScatterQuant) {
         switch (qm) {  // source type * 2 + asymmetric
         case 0: return launch_vec<IdxT, OP, VEC, false, 0>(a, fused, grid, chunks, ue, tb, st);
@@ -1240,6 +1360,20 @@ hipError_t launch_policy(const Args &a, bool ntl, bool fused, dim3 grid, uint32_
         case 5: return launch_vec<IdxT, OP, VEC, false, 5>(a, fused, grid, chunks, ue, tb, st);
         default: return launch_vec<IdxT, OP, VEC, false>(a, fused, grid, chunks, ue, tb, st);
         }
+    } else if constexpr (VEC == 16) {
+        // u: loads in flight per lane, the smallest of 2, 4, 8 covering a unit
+        if (ntl) {
+            if (u == 2)
+                return launch_vec<IdxT, OP, VEC, true, -1, 2>(a, fused, grid, chunks, ue, tb, st);
+            if (u == 4)
+                return launch_vec<IdxT, OP, VEC, true, -1, 4>(a, fused, grid, chunks, ue, tb, st);
+            return launch_vec<IdxT, OP, VEC, true, -1, 8>(a, fused, grid, chunks, ue, tb, st);
+        }
+        if (u == 2)
+            return launch_vec<IdxT, OP, VEC, false, -1, 2>(a, fused, grid, chunks, ue, tb, st);
+        if (u == 4)
+            return launch_vec<IdxT, OP, VEC, false, -1, 4>(a, fused, grid, chunks, ue, tb, st);
+        return launch_vec<IdxT, OP, VEC, false, -1, 8>(a, fused, grid, chunks, ue, tb, st);
     } else {
         if (ntl)
             return launch_vec<IdxT, OP, VEC, true>(a, fused, grid, chunks, ue, tb, st);
@@ -1249,41 +1383,41 @@ hipError_t launch_policy(const Args &a, bool ntl, bool fused, dim3 grid, uint32_
 
 template <typename IdxT, Op OP>
 hipError_t launch_op(const Args &a, uint32_t vec, bool ntl, bool fused, dim3 grid,
-                     uint32_t chunks, uint32_t *ue, uint64_t *tb, hipStream_t st, int qm) {
+                     uint32_t chunks, uint32_t *ue, uint64_t *tb, hipStream_t st, int qm, int u) {
     if constexpr (OP == Op::ScatterQuant) {
         if (vec == 16)  // 8 values per vector
-            return launch_policy<IdxT, OP, 16>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
-        return launch_policy<IdxT, OP, 1>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
+            return launch_policy<IdxT, OP, 16>(a, ntl, fused, grid, chunks, ue, tb, st, qm, u);
+        return launch_policy<IdxT, OP, 1>(a, ntl, fused, grid, chunks, ue, tb, st, qm, u);
     } else if constexpr (OP == Op::Dequant) {
         switch (vec) {
-        case 8: return launch_policy<IdxT, OP, 8>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
-        case 4: return launch_policy<IdxT, OP, 4>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
-        case 2: return launch_policy<IdxT, OP, 2>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
-        default: return launch_policy<IdxT, OP, 1>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
+        case 8: return launch_policy<IdxT, OP, 8>(a, ntl, fused, grid, chunks, ue, tb, st, qm, u);
+        case 4: return launch_policy<IdxT, OP, 4>(a, ntl, fused, grid, chunks, ue, tb, st, qm, u);
+        case 2: return launch_policy<IdxT, OP, 2>(a, ntl, fused, grid, chunks, ue, tb, st, qm, u);
+        default: return launch_policy<IdxT, OP, 1>(a, ntl, fused, grid, chunks, ue, tb, st, qm, u);
         }
     } else {
         switch (vec) {
-        case 16: return launch_policy<IdxT, OP, 16>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
-        case 8: return launch_policy<IdxT, OP, 8>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
-        case 4: return launch_policy<IdxT, OP, 4>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
-        case 2: return launch_policy<IdxT, OP, 2>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
-        default: return launch_policy<IdxT, OP, 1>(a, ntl, fused, grid, chunks, ue, tb, st, qm);
+        case 16: return launch_policy<IdxT, OP, 16>(a, ntl, fused, grid, chunks, ue, tb, st, qm, u);
+        case 8: return launch_policy<IdxT, OP, 8>(a, ntl, fused, grid, chunks, ue, tb, st, qm, u);
+        case 4: return launch_policy<IdxT, OP, 4>(a, ntl, fused, grid, chunks, ue, tb, st, qm, u);
+        case 2: return launch_policy<IdxT, OP, 2>(a, ntl, fused, grid, chunks, ue, tb, st, qm, u);
+        default: return launch_policy<IdxT, OP, 1>(a, ntl, fused, grid, chunks, ue, tb, st, qm, u);
         }
     }
 }
 
 template <typename IdxT>
 hipError_t launch_idx(const Args &a, Op op, uint32_t vec, bool ntl, bool fused, dim3 grid,
-                      uint32_t chunks, uint32_t *ue, uint64_t *tb, hipStream_t st, int qm) {
+                      uint32_t chunks, uint32_t *ue, uint64_t *tb, hipStream_t st, int qm, int u) {
     switch (op) {
     case Op::Gather:
-        return launch_op<IdxT, Op::Gather>(a, vec, ntl, fused, grid, chunks, ue, tb, st, -1);
+        return launch_op<IdxT, Op::Gather>(a, vec, ntl, fused, grid, chunks, ue, tb, st, -1, u);
     case Op::Scatter:
-        return launch_op<IdxT, Op::Scatter>(a, vec, ntl, fused, grid, chunks, ue, tb, st, -1);
+        return launch_op<IdxT, Op::Scatter>(a, vec, ntl, fused, grid, chunks, ue, tb, st, -1, u);
     case Op::ScatterQuant:
-        return launch_op<IdxT, Op::ScatterQuant>(a, vec, ntl, fused, grid, chunks, ue, tb, st, qm);
+        return launch_op<IdxT, Op::ScatterQuant>(a, vec, ntl, fused, grid, chunks, ue, tb, st, qm, u);
     default:
-        return launch_op<IdxT, Op::Dequant>(a, vec, ntl, fused, grid, chunks, ue, tb, st, qm);
+        return launch_op<IdxT, Op::Dequant>(a, vec, ntl, fused, grid, chunks, ue, tb, st, qm, u);
     }
 }
 
@@ -1347,6 +1481,11 @@ hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
         a.g_unit_end = ue;
         a.g_tok_begin = tb;
     }
+    // Loads in flight per lane for a gather or scatter with 16-byte vectors:
+    // the smallest of 2, 4, 8 that covers one unit.
+    const uint64_t per_lane = (job.rows_per_unit * job.row_bytes + (uint64_t)kThreads * 16 - 1) /
+                              ((uint64_t)kThreads * 16);
+    const int u = per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : 8;
     // The plan arrays depend only on the shared table: the plan kernels run
     // with the first launch only, later launches of a large batch reuse them.
     for (uint32_t first = 0; first < job.count; first += kMaxBatch, chunks = 0) {
@@ -1359,9 +1498,9 @@ hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
         const dim3 g(grid, n);
         const hipError_t e =
             job.idx64 ? launch_idx<uint64_t>(a, job.op, job.vec_bytes, job.load_nt, fused, g, chunks,
-                                             ue, tb, stream, qm)
+                                             ue, tb, stream, qm, u)
                       : launch_idx<uint32_t>(a, job.op, job.vec_bytes, job.load_nt, fused, g, chunks,
-                                             ue, tb, stream, qm);
+                                             ue, tb, stream, qm, u);
         if (e != hipSuccess)
             return e;
     }
