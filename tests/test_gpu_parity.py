@@ -227,6 +227,61 @@ def test_scatter_plan_path(hp):
     assert_bits_equal(host_bits(d.pool), want, "plan path")
 
 
+# ---- 1,025 .. 4,096 sequences: the fused scan with more than 4 sequences per thread ------------
+#
+# Up to 1,024 sequences each scan thread keeps its sequences' counts in
+# registers between the scan's two passes; above that it reads them again, and
+# with 64 bytes of unit per sequence the units grow to whole pages (several
+# rounds of the copy loop). These sizes still take the fused (one-launch) path.
+
+FUSED_MANY = [(1025, 16), (2500, 64), (4096, 16)]
+
+
+def fused_many(seed, S, P, **kw):
+    args = dict(max_len=24, page_sizes=(P,), heads=(8,), dims=(128,), dtypes=("bf16",),
+                num_seqs=S)
+    args.update(kw)
+    return workloads.random_small(seed, **args)
+
+
+@pytest.mark.parametrize("S,P", FUSED_MANY)
+def test_gather_fused_many_sequences(hp, S, P):
+    w = fused_many(9100 + S, S, P)
+    say("gather fused many", S, P, w.describe())
+    d = OnDevice(w)
+    for streaming in (False, True):
+        out = d.empty_out()
+        hp.gather(d.desc, out, streaming=streaming)
+        torch.cuda.synchronize()
+        assert_bits_equal(host_bits(out), oracle_gather(d), f"S={S} P={P} streaming={streaming}")
+
+
+@pytest.mark.parametrize("S,P", FUSED_MANY)
+def test_scatter_fused_many_sequences(hp, S, P):
+    w = fused_many(9200 + S, S, P, alias=False, with_start=True)
+    say("scatter fused many", S, P, w.describe())
+    d = OnDevice(w)
+    src = w.make_src(DEV)
+    want = oracle.scatter(host_bits(d.pool), host_bits(src), zero_tail=True,
+                          **d.oracle_kw(with_start=True))
+    hp.scatter(d.desc, src, d.ss, zero_tail=True)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_bits(d.pool), want, f"S={S} P={P}")
+
+
+@pytest.mark.parametrize("S,P", FUSED_MANY)
+def test_dequant_fused_many_sequences(hp, S, P):
+    w = fused_many(9300 + S, S, P, dtypes=("i8",))
+    say("dequant fused many", S, P, w.describe())
+    d = OnDevice(w)
+    out = d.empty_out(dtype=torch.bfloat16)
+    hp.gather_dequant(d.desc, out)
+    torch.cuda.synchronize()
+    want = oracle.gather_dequant(host_bits(d.pool).view(np.int8), d.scales.cpu().numpy(),
+                                 **d.oracle_kw())
+    bf16_bits_equal(host_bits(out), want, f"S={S} P={P}")
+
+
 # ---- dequant-gather --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("seed", range(30))

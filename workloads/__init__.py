@@ -267,16 +267,18 @@ def by_name(name):
 def random_small(seed, *, max_seqs=5, max_len=40, page_sizes=(1, 2, 3, 4, 5, 8, 16),
                  heads=(1, 2, 3), dims=(1, 2, 4, 8), dtypes=("f16", "bf16", "f32", "i8",
                                                             "u8", "f64"),
-                 alias=True, spare_pages=True, index_dtype=None, with_start=False):
+                 alias=True, spare_pages=True, index_dtype=None, with_start=False,
+                 num_seqs=None):
     """A small, valid descriptor: random lengths (zero allowed), page size,
     heads, dims and dtype; optional aliasing of pages between sequences,
-    optional spare pages at the end of a slice and optional start offsets."""
+    optional spare pages at the end of a slice and optional start offsets.
+    num_seqs fixes the sequence count (else it is drawn in 0..max_seqs)."""
     rng = np.random.default_rng(seed)
     P = int(rng.choice(page_sizes))
     H = int(rng.choice(heads))
     D = int(rng.choice(dims))
     dtype = str(rng.choice(list(dtypes)))
-    S = int(rng.integers(0, max_seqs + 1))
+    S = int(rng.integers(0, max_seqs + 1)) if num_seqs is None else int(num_seqs)
     lens = rng.integers(0, max_len + 1, size=S)
     start = rng.integers(0, 2 * P + 1, size=S) if with_start else np.zeros(S, np.int64)
     need = _pages_for(lens + start, P)
