@@ -47,9 +47,10 @@ namespace hp {
 #define HP_SCATTER_STREAM_UNIT_BYTES 8192
 #endif
 // Quantize-on-scatter: rows (slots of one page) per work unit; the
-// workgroup's waves take them in turn.
+// workgroup's waves take them in turn. Four (one row per wave) measured 5 %
+// ahead of 8 and 7 % ahead of 16 on the decode batch.
 #ifndef HP_QUANT_UNIT_ROWS
-#define HP_QUANT_UNIT_ROWS 8
+#define HP_QUANT_UNIT_ROWS 4
 #endif
 #ifndef HP_QUANT_UNITS_PER_GROUP
 #define HP_QUANT_UNITS_PER_GROUP 1

@@ -426,8 +426,9 @@ __device__ __forceinline__ void dequant_span(const Args &a, const unsigned char 
 // land on one XCD take one contiguous range of work units (a bijection on
 // [0, groups)), so neighbouring units of one page share that XCD's L2.
 // Measured on MI355X (decode batch, same-box A/B): the streamed scatter gains
-// 4 % (random 128 KB pages written); the gather loses 0.7 % and the small
-// cached scatter of an append 2x, so only the streamed scatter takes it.
+// 4 % and quantize-on-scatter 1-3 % (both write random pages); the gather
+// loses 0.7 % and the small cached scatter of an append 2x, so only those two
+// take it.
 template <bool REMAP>
 __device__ __forceinline__ uint32_t group_order(uint32_t b, uint32_t groups) {
     if constexpr (REMAP) {
@@ -949,7 +950,8 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
         tab = t;
     }
     const uint32_t g0 =
-        group_order<OP == Op::Scatter && NTL>(blockIdx.x, gridDim.x) * a.units_per_group;
+        group_order<(OP == Op::Scatter && NTL) || OP == Op::ScatterQuant>(blockIdx.x, gridDim.x) *
+        a.units_per_group;
     __shared__ FirstSeq first;
     if constexpr (FUSED) {
         uint64_t *tb = reinterpret_cast<uint64_t *>(lds);
