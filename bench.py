@@ -323,7 +323,7 @@ def summarize_attention(trace_dir, fetch_dir, write_dir):
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     for (name, grid), ts in sorted(groups.items()):
         gb = gbs = ""
-        if name.startswith("attention_kernel<"):
+        if name.startswith(("attention_kernel<", "attention_mfma_kernel<")):
             wl, nbytes = algo["bf16" if "BF16" in name else "f16"]
             gb = f"{nbytes / 1e9:.4f}"
             gbs = f"{nbytes / (np.mean(ts) * 1e3):.0f}"
@@ -364,7 +364,7 @@ def summarize_attention(trace_dir, fetch_dir, write_dir):
         name = key[0]
         rb, wb = fk[key] * 1024 * ff, wk[key] * 1024 * wf
         gb = ""
-        if name.startswith("attention_kernel<"):
+        if name.startswith(("attention_kernel<", "attention_mfma_kernel<")):
             gb = f"{algo['bf16' if 'BF16' in name else 'f16'][1] / 1e9:.4f}"
         out.append(f"| `{name}` (grid {key[1]}) | {rb / 1e9:.4f} | {wb / 1e9:.4f} | {gb} |")
     with open(os.path.join(PROFILES, "attention_decode_prefix_hbm_traffic.md"), "w") as f:
@@ -487,18 +487,22 @@ def summarize_quant_write(trace_dir, fetch_dir, write_dir):
 
 # ---- batched moves (optional) ----------------------------------------------------
 
-def attention_extras(hp, torch, np, dev, stream, reps):
+def attention_extras(hp, torch, np, dev, stream, reps, gqa8=False):
     """Decode attention reading K and V through the block table: the decode
     batch (64 sequences, 32 kv heads x 128 fp16, one query head per kv head,
     streaming loads) and the prefix-sharing batch (256 sequences, 8 kv heads x
     128 bf16, 32 query heads, cached loads since 64 prefix pages are read by
-    every sequence). Algorithmic bytes: every live K and V row read once (the
-    prefix pages once per sequence that uses them, as logical bytes), the
-    queries read and the fp32 output written."""
+    every sequence); with gqa8, the prefix batch with 64 query heads too.
+    Algorithmic bytes: every live K and V row read once (the prefix pages once
+    per sequence that uses them, as logical bytes), the queries read and the
+    fp32 output written."""
     import workloads
     res = {}
-    for name, w, group, streaming in (("decode_mha_f16", workloads.decode(), 1, True),
-                                      ("prefix_gqa4_bf16", workloads.prefix(), 4, False)):
+    cases = [("decode_mha_f16", workloads.decode(), 1, True),
+             ("prefix_gqa4_bf16", workloads.prefix(), 4, False)]
+    if gqa8:
+        cases.append(("prefix_gqa8_bf16", workloads.prefix(), 8, False))
+    for name, w, group, streaming in cases:
         k_pool = w.make_pool(dev)
         v_pool = dataclasses.replace(w, seed=w.seed * 7 + 3).make_pool(dev)
 
@@ -910,7 +914,8 @@ def main():
         result["extras"] = {
             "quantize_on_scatter": quant_write_extras(hp, torch, np, dev, stream,
                                                       args.kernel_reps),
-            "attention": attention_extras(hp, torch, np, dev, stream, args.kernel_reps),
+            "attention": attention_extras(hp, torch, np, dev, stream, args.kernel_reps,
+                                          gqa8=True),
             "dequant_schemes": schemes,
             "batched_append": batched_append(hp, torch, np, dev, stream, args.kernel_reps),
             "copy_pages": {"workload": "1,024 pages of the decode pool (16 x 32 x 128 fp16 = "

@@ -149,6 +149,11 @@ CASES = [
     ("f16", 128, 7, 4, (16,)),
     ("bf16", 128, 12, 2, (16,)),       # more than 8 query heads per kv head: chunks of 8
     ("f16", 32, 16, 1, (4,)),
+    # grouped heads on the matrix cores (G >= 3, head_dim 64 or 128)
+    ("bf16", 128, 20, 2, (16,)),       # two row chunks of 16 query heads (16 + 4)
+    ("f16", 64, 3, 6, (8, 16)),        # 4 + 2 kv heads: two idle waves in the last group
+    ("bf16", 128, 4, 1, (16,)),        # one kv head: three idle waves
+    ("f16", 128, 16, 4, (1, 3)),       # full 16 rows; 1- and 3-token pages inside a tile
 ]
 
 
@@ -165,14 +170,15 @@ def test_attention_random(hp, case, seed):
     check(w, out.cpu().numpy(), q, d, v_pool, group, scale, what=f"case {case} seed {seed}")
 
 
-def test_attention_single_token_is_exact(hp):
+@pytest.mark.parametrize("group", [2, 4, 8])
+def test_attention_single_token_is_exact(hp, group):
     """One cached token: its weight is exactly 1 and the output is its value
-    row, bit for bit."""
+    row, bit for bit (vector path at G = 2, matrix cores at 4 and 8)."""
     w = workloads.random_small(1300, max_seqs=20, max_len=40, page_sizes=(16,), heads=(4,),
                                dims=(128,), dtypes=("bf16",))
     w.seq_lens[:] = np.minimum(w.seq_lens, 1)
-    say("attention single token", w.describe())
-    d, v_pool, q = make_inputs(w, 2, 1301)
+    say("attention single token", group, w.describe())
+    d, v_pool, q = make_inputs(w, group, 1301)
     out = run(hp, d, v_pool, q, w, 0.09).cpu().numpy()
     vv = _vals(host_bits(v_pool), "bf16").reshape(-1, w.num_heads, w.head_dim)
     for s in range(w.num_seqs):
@@ -180,20 +186,22 @@ def test_attention_single_token_is_exact(hp):
             assert np.all(out[s] == 0)
             continue
         row = int(w.block_table[int(w.seq_ptr[s])]) * w.page_size
-        for hq in range(8):
-            got, want = out[s, hq].astype(np.float64), vv[row, hq // 2]
+        for hq in range(4 * group):
+            got, want = out[s, hq].astype(np.float64), vv[row, hq // group]
             bad = np.flatnonzero(got != want)
             assert not len(bad), (f"seq {s} head {hq}: {len(bad)} differ, first {bad[:4]}: "
                                   f"got {got[bad[:4]]} want {want[bad[:4]]}")
 
 
-def test_attention_equal_keys_give_the_mean(hp):
+@pytest.mark.parametrize("group", [1, 4])
+def test_attention_equal_keys_give_the_mean(hp, group):
     """Identical keys: every weight is exactly 1, so the output is the mean of
-    the value rows (fp32 sums of L terms)."""
+    the value rows (fp32 sums of L terms; vector path at G = 1, matrix cores
+    at G = 4)."""
     w = workloads.random_small(1310, max_seqs=10, max_len=500, page_sizes=(16,), heads=(8,),
                                dims=(128,), dtypes=("f16",))
-    say("attention equal keys", w.describe())
-    d, v_pool, q = make_inputs(w, 1, 1311)
+    say("attention equal keys", group, w.describe())
+    d, v_pool, q = make_inputs(w, group, 1311)
     g = torch.Generator(device=DEV).manual_seed(1312)
     krow = torch.randn(w.head_dim, generator=g, device=DEV).to(torch.float16)
     d.pool.copy_(krow.expand_as(d.pool))
@@ -201,9 +209,10 @@ def test_attention_equal_keys_give_the_mean(hp):
     vv = _vals(host_bits(v_pool), "f16").reshape(-1, w.num_heads, w.head_dim)
     for s, ids in enumerate(slot_ids(w)):
         if len(ids):
-            mean = vv[ids].mean(axis=0)
+            mean = vv[ids].mean(axis=0)  # [H, D]; query head hq reads kv head hq // group
             bound = (2 * len(ids) + 8) * U * np.abs(vv[ids]).max()
-            assert np.abs(out[s] - mean).max() <= bound
+            got = out[s].reshape(w.num_heads, group, w.head_dim)
+            assert np.abs(got - mean[:, None, :]).max() <= bound
 
 
 def test_attention_constant_values(hp):
