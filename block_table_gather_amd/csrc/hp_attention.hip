@@ -625,11 +625,13 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
     for (uint32_t db = 0; db < DB; ++db)
         o[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (uint32_t tb = 0; tb < n; tb += kMfmaTile) {
-        // K operands of the two 16-token blocks: token tb + 16 b + c16 (the
-        // last token again past n: a real row, masked below)
-        V8 kb[2][KK];
-        u32x4 vc[VCH];
+    // K operands of the two 16-token blocks of tile tb: token tb + 16 b + c16
+    // (the last token again past n: a real row, masked below); V chunk
+    // 64 c + lane is token (64 c + lane) / (D / 8) of the tile, 16 bytes at
+    // dims 8 ((64 c + lane) % (D / 8)).
+    V8 kb[2][KK];
+    u32x4 vc[VCH];
+    auto load_k = [&](uint32_t tb) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const uint32_t j = min32(tb + 16 * b + c16, n - 1);
@@ -638,8 +640,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
             for (uint32_t kk = 0; kk < KK; ++kk)
                 kb[b][kk] = __builtin_bit_cast(V8, ld16<NT>(kr + kk * 64));
         }
-        // V chunks: chunk 64 c + lane is token (64 c + lane) / (D / 8) of the
-        // tile, 16 bytes at dims 8 ((64 c + lane) % (D / 8))
+    };
+    auto load_v = [&](uint32_t tb) {
 #pragma unroll
         for (uint32_t c = 0; c < VCH; ++c) {
             const uint32_t ch = 64 * c + lane;
@@ -647,6 +649,15 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
             const uint32_t j = min32(tb + jt, n - 1);
             vc[c] = ld16<NT>(a.v_pool + row_of(j) * slot_bytes + head_off + 16 * dc);
         }
+    };
+    // Software pipeline: tile tb + 32's K loads follow tile tb's score
+    // products (which free the K registers), and its V loads follow tile tb's
+    // V writes to LDS, so they are in flight during the softmax and the
+    // weights x V products.
+    load_k(0);
+    load_v(0);
+    for (uint32_t tb = 0; tb < n; tb += kMfmaTile) {
+        const bool more = tb + kMfmaTile < n;
         // scores: lane holds rows 4 grp + i of token tb + 16 b + c16
         float x[2][4];
 #pragma unroll
@@ -660,6 +671,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
             for (int i = 0; i < 4; ++i)
                 x[b][i] = ok ? acc[i] * a.qscale : -__builtin_inff();
         }
+        if (more)
+            load_k(tb + kMfmaTile);
         // online softmax per row (the tile's first token is in range, so the
         // new maximum is finite)
         float p[2][4];
@@ -695,6 +708,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
             *reinterpret_cast<u32x4 *>(vt + jt * VRB + 16 * dc) = vc[c];
         }
         wave_lds_sync();
+        if (more)
+            load_v(tb + kMfmaTile);
         // weights as three A operands whose sum is the binary32 weight
         V8 pa[3];
         {
