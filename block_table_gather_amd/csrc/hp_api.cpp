@@ -770,12 +770,14 @@ hp_status check_attention(const hp_desc *d, uint32_t num_q_heads) {
     if (d->page_size > 65536 || d->num_seqs >= (1ull << 31) ||
         (uint64_t)num_q_heads * D >= (1ull << 31))
         return HP_ERR_ARG;
-    const hp::AttentionShape sh =
-        hp::attention_shape(d->num_seqs, d->total_tokens, d->page_size, d->num_heads, D,
-                            num_q_heads);
-    if (sh.cap_units + d->num_seqs >= (1ull << 31) || sh.head_groups > 65535 ||
-        (num_q_heads / d->num_heads + 7) / 8 > 65535)
-        return HP_ERR_ARG;
+    for (int stream = 0; stream < 2; ++stream) {  // the launch shape may follow the hint
+        const hp::AttentionShape sh =
+            hp::attention_shape(d->num_seqs, d->total_tokens, d->page_size, d->num_heads, D,
+                                num_q_heads, stream != 0);
+        if (sh.cap_units + d->num_seqs >= (1ull << 31) || sh.head_groups > 65535 ||
+            (num_q_heads / d->num_heads + 7) / 8 > 65535)
+            return HP_ERR_ARG;
+    }
     return HP_OK;
 }
 

@@ -922,15 +922,18 @@ __global__ __launch_bounds__(kAttnThreads) void attention_combine_kernel(CArgs c
 // Query-head slots per lane group for G query heads per kv head.
 uint32_t group_slots(uint32_t G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
 
-// Three or more query heads per kv head with head_dim 64 or 128 take the
-// matrix-core kernel. Measured on MI355X against the vector kernel: 1.4x
-// faster at G = 4 and 1.9x at G = 8 (prefix batch), 4 % faster to 8 % slower
-// at G = 2, where the vector kernel needs no padding.
+// Grouped query heads with head_dim 64 or 128 take the matrix-core kernel
+// from three query heads per kv head, and at two when the loads stream (each
+// page read once, so HBM bounds the call). Measured on MI355X against the
+// vector kernel: 1.4x faster at G = 4 and 1.9x at G = 8 (prefix batch); at
+// G = 2, 12 % faster on the streamed decode batch but 8 % slower on the
+// prefix batch, whose shared pages come from the caches.
 #ifndef HP_ATTN_MFMA_MIN_GROUP
 #define HP_ATTN_MFMA_MIN_GROUP 3
 #endif
-bool attention_mfma(uint32_t G, uint32_t D) {
-    return G >= HP_ATTN_MFMA_MIN_GROUP && (D == 64 || D == 128);
+bool attention_mfma(uint32_t G, uint32_t D, bool stream) {
+    const uint32_t min_group = stream && HP_ATTN_MFMA_MIN_GROUP > 2 ? 2 : HP_ATTN_MFMA_MIN_GROUP;
+    return G >= min_group && (D == 64 || D == 128);
 }
 
 template <typename ET, typename IdxT, int D>
@@ -997,7 +1000,7 @@ hipError_t launch_attention_d(const AArgs &a, const AttentionShape &sh, uint32_t
 template <typename ET>
 hipError_t launch_attention_i(const AArgs &a, const AttentionShape &sh, uint32_t G, bool idx64,
                               bool nt, hipStream_t st) {
-    if (attention_mfma(G, a.head_dim)) {
+    if (attention_mfma(G, a.head_dim, nt)) {
         if (a.head_dim == 64)
             return idx64 ? launch_attention_mfma<ET, uint64_t, 64>(a, sh, nt, st)
                          : launch_attention_mfma<ET, uint32_t, 64>(a, sh, nt, st);
@@ -1025,10 +1028,12 @@ WsLayout ws_layout(uint64_t S, uint64_t Hq, uint64_t D, uint64_t cap) {
 } // namespace
 
 AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
-                               uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads) {
+                               uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads,
+                               bool stream_loads) {
     AttentionShape sh;
     const uint32_t G = num_q_heads / num_kv_heads;
-    if (attention_mfma(G, head_dim)) {
+    const bool mfma = attention_mfma(G, head_dim, stream_loads);
+    if (mfma) {
         // one wave per kv head, four kv heads per workgroup
         sh.heads_per_group = kMfmaWaves;
         sh.token_lanes = 1;
@@ -1049,7 +1054,7 @@ AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_
     // each unit writes (D + 2) floats per query head it covers: keep that a
     // small share of the unit's K/V bytes (2 D per token and kv head)
     uint64_t min_tokens = kAttnMinUnitTokensPerSlot * group_slots(num_q_heads / num_kv_heads);
-    if (attention_mfma(G, head_dim) && min_tokens < 2 * kMfmaTile)
+    if (mfma && min_tokens < 2 * kMfmaTile)
         min_tokens = 2 * kMfmaTile;  // at least two matrix tiles per unit
     const uint64_t min_pages = (min_tokens + page_size - 1) / page_size;
     if (upages < min_pages)
@@ -1066,15 +1071,21 @@ AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_
 
 uint64_t attention_workspace_bytes(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
                                    uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads) {
-    const AttentionShape sh =
-        attention_shape(num_seqs, total_tokens, page_size, num_kv_heads, head_dim, num_q_heads);
-    return ws_layout(num_seqs, num_q_heads, head_dim, sh.cap_units).end;
+    uint64_t need = 0;
+    for (int stream = 0; stream < 2; ++stream) {
+        const AttentionShape sh = attention_shape(num_seqs, total_tokens, page_size, num_kv_heads,
+                                                  head_dim, num_q_heads, stream != 0);
+        const uint64_t n = ws_layout(num_seqs, num_q_heads, head_dim, sh.cap_units).end;
+        need = n > need ? n : need;
+    }
+    return need;
 }
 
 hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
     (void)hipGetLastError();  // clear errors left by earlier calls that are not ours
     const AttentionShape sh = attention_shape(job.num_seqs, job.total_tokens, job.page_size,
-                                              job.num_kv_heads, job.head_dim, job.num_q_heads);
+                                              job.num_kv_heads, job.head_dim, job.num_q_heads,
+                                              job.stream_loads);
     const WsLayout wl = ws_layout(job.num_seqs, job.num_q_heads, job.head_dim, sh.cap_units);
     unsigned char *ws = static_cast<unsigned char *>(job.workspace);
     uint32_t *unit_end = reinterpret_cast<uint32_t *>(ws + wl.unit_end);

@@ -201,7 +201,10 @@ struct AttentionJob {
 };
 
 AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
-                               uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads);
+                               uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads,
+                               bool stream_loads);
+// The workspace covers the launch shape with and without streaming loads
+// (the streaming hint can choose the kernel).
 uint64_t attention_workspace_bytes(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
                                    uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads);
 hipError_t launch_attention(const AttentionJob &job, hipStream_t stream);

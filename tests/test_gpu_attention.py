@@ -244,6 +244,19 @@ def test_attention_streaming_and_repeat_are_bit_identical(hp):
     assert torch.equal(a.view(torch.int32), c.view(torch.int32))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_attention_g2_streaming_and_cached(hp, D):
+    """Two query heads per kv head: with streaming loads the matrix-core kernel
+    runs, without them the vector kernel; both against the oracle."""
+    w = workloads.random_small(1335 + D, max_seqs=12, max_len=400, page_sizes=(16,), heads=(6,),
+                               dims=(D,), dtypes=("bf16",), alias=False)
+    say("attention G=2 streaming and cached", D, w.describe())
+    d, v_pool, q = make_inputs(w, 2, 1336 + D)
+    for streaming in (True, False):
+        out = run(hp, d, v_pool, q, w, 0.09, streaming=streaming).cpu().numpy()
+        check(w, out, q, d, v_pool, 2, 0.09, what=f"G=2 D={D} streaming={streaming}")
+
+
 def test_attention_empty_and_short_sequences(hp):
     """Sequences of 0..3 tokens next to long ones; one kv head, so most lane
     groups of a workgroup are token lanes that see no token."""
