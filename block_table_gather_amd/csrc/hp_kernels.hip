@@ -13,7 +13,9 @@
 //    one sequence inside one page, on both sides of the move. The work unit
 //    is such a run: `rows_per_unit` consecutive tokens (a divisor of P, so a
 //    unit never crosses a page), i.e. one block-table entry and one
-//    contiguous span of up to ~32 KB.
+//    contiguous span; the host sizes it per move (8 KB and up for gather,
+//    growing with the sequence count; 8 or 32 KB for scatter; 32 KB of
+//    output for dequant).
 //  * Work units are numbered sequence by sequence. Each workgroup owns
 //    `units_per_group` consecutive units. To map a unit to its sequence it
 //    needs, per sequence, the running unit count and the running token count
@@ -22,12 +24,15 @@
 //    from the token counts (a 64-lane shuffle scan per wave, wave totals
 //    combined through LDS), so one launch does everything; above it, a plan
 //    pass writes them to the workspace and the copy kernel reads them there.
-//  * The block-table entry of a unit is read once per unit into a scalar
-//    register; the sequence's scalars are reloaded only when the walk moves
-//    to the next sequence.
+//  * Gather and scatter workgroups learn their first unit's sequence inside
+//    the fused scan (the owning thread publishes it through LDS); the others
+//    search the scanned table. The block-table entry of a unit is read once
+//    per unit into a scalar register; the sequence's scalars are reloaded
+//    only when the walk moves to the next sequence.
 //  * Copies are 16-byte vector loads and non-temporal 16-byte vector stores,
-//    unrolled so each lane keeps several loads in flight; narrower vectors
-//    are used only when a row size or pointer forbids 16 bytes.
+//    2, 4 or 8 loads per lane in flight (the smallest that covers a unit);
+//    narrower vectors are used only when a row size or pointer forbids 16
+//    bytes.
 //  * Dequant reads 8 int8 values per lane and writes 8 bf16 values (16 B) per
 //    lane, so both sides stay fully coalesced; the unit's per-slot scales sit
 //    one per lane and are fetched with a cross-lane shuffle.
