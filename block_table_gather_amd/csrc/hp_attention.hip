@@ -931,6 +931,15 @@ uint32_t group_slots(uint32_t G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 :
 #ifndef HP_ATTN_MFMA_MIN_GROUP
 #define HP_ATTN_MFMA_MIN_GROUP 3
 #endif
+// Workgroups aimed at with one query head per kv head and cached loads.
+// Measured on MI355X (prefix batch, 8 kv heads): 4,096 runs 16 % faster than
+// 1,024; with streaming loads (decode batch) 1,024 stays best (4,096: 14 %
+// slower).
+#ifndef HP_ATTN_TARGET_GROUPS_MHA_CACHED
+#define HP_ATTN_TARGET_GROUPS_MHA_CACHED 4096
+#endif
+constexpr uint64_t kAttnTargetGroupsMhaCached = HP_ATTN_TARGET_GROUPS_MHA_CACHED;
+
 bool attention_mfma(uint32_t G, uint32_t D, bool stream) {
     const uint32_t min_group = stream && HP_ATTN_MFMA_MIN_GROUP > 2 ? 2 : HP_ATTN_MFMA_MIN_GROUP;
     return G >= min_group && (D == 64 || D == 128);
@@ -1046,10 +1055,13 @@ AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_
     sh.head_groups = (num_kv_heads + sh.heads_per_group - 1) / sh.heads_per_group;
     // Pages to visit (at most), spread over about kAttnTargetGroups workgroups.
     const uint64_t pages = total_tokens / page_size + num_seqs;
-    // one query head per kv head: few, long units; grouped heads (more
-    // arithmetic per byte) spread over more workgroups
-    const uint64_t target = num_q_heads == num_kv_heads ? kAttnTargetGroupsMha
-                                                        : kAttnTargetGroupsGqa;
+    // one query head per kv head: few, long units when the loads stream
+    // (HBM bounds the call), more and shorter ones when they are served from
+    // the caches; grouped heads (more arithmetic per byte) spread over more
+    // workgroups
+    const uint64_t target = num_q_heads != num_kv_heads ? kAttnTargetGroupsGqa
+                            : stream_loads              ? kAttnTargetGroupsMha
+                                                        : kAttnTargetGroupsMhaCached;
     uint64_t upages = (pages * sh.head_groups + target - 1) / target;
     // each unit writes (D + 2) floats per query head it covers: keep that a
     // small share of the unit's K/V bytes (2 D per token and kv head)
