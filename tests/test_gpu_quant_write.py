@@ -91,6 +91,48 @@ def test_scatter_quant_scales_spread(hp):
     run_case(hp, w, "f32", True, False, 1742, scale_src=1e30)
 
 
+def test_scatter_quant_scales_spread_16bit(hp):
+    """bf16 rows of tiny and huge values: scales outside [2^-100, 2^100],
+    where each value is divided by the scale."""
+    w = workloads.random_small(1745, max_seqs=10, max_len=100, page_sizes=(8,), heads=(2,),
+                               dims=(64,), alias=False, with_start=True)
+    say("scatter quant spread bf16", w.describe())
+    run_case(hp, w, "bf16", False, True, 1746, scale_src=1e-30)
+    run_case(hp, w, "bf16", True, False, 1747, scale_src=1e36)
+
+
+# 16-bit source rows that a wave holds whole in registers (at most 4,096
+# values): page sizes give units of 1, 2, 3 and 4 rows (so some waves of a
+# workgroup have no row), rows run from 8 values to the largest such row.
+PIPE_SHAPES = [(1, 3, 16), (2, 1, 8), (3, 2, 64), (5, 4, 128), (8, 8, 512), (16, 32, 128)]
+PIPE_MODES = [("f16", False, True), ("bf16", True, True), ("f16", True, False),
+              ("bf16", False, False)]
+
+
+@pytest.mark.parametrize("shape", PIPE_SHAPES)
+@pytest.mark.parametrize("src_type,asym,zero_tail", PIPE_MODES)
+def test_scatter_quant_unit_shapes(hp, shape, src_type, asym, zero_tail):
+    P, H, D = shape
+    seed = 1780 + 13 * P + H + D
+    w = workloads.random_small(seed, max_len=max(9, 120000 // (H * D)), page_sizes=(P,),
+                               heads=(H,), dims=(D,), alias=False, with_start=True,
+                               num_seqs=7 + P)
+    say("scatter quant unit shapes", shape, src_type, asym, zero_tail, w.describe())
+    run_case(hp, w, src_type, asym, zero_tail, seed + 1)
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_scatter_quant_decode_full(hp, asym):
+    """The decode batch at full size (63,540 fp16 rows of 32 x 128 values,
+    12,000 pages), launched as the benchmark launches it: whole pool, scales
+    and zero points against the oracle."""
+    w = workloads.decode()
+    say("scatter quant decode full", asym, w.describe())
+    run_case(hp, w, "f16", asym, False, 1790 + asym)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
 def test_scatter_quant_plan_path(hp):
     """More sequences than the fused LDS table: the plan kernels run first."""
     rng = np.random.default_rng(1750)
