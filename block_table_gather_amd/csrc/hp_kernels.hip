@@ -217,7 +217,9 @@ __device__ __forceinline__ void scan_range(const Args &a, uint32_t s0, uint32_t 
 // scanned table afterwards. Measured on MI355X on the decode batch: the
 // in-scan lookup gains 5 % on gather and scatter (8 KB units) and loses
 // 0.5 % on dequant, whose larger units make the lookup a smaller share.
-constexpr bool locate_in_scan(Op op) { return op == Op::Gather || op == Op::Scatter; }
+constexpr bool locate_in_scan(Op op) {
+    return op == Op::Gather || op == Op::Scatter || op == Op::ScatterQuant;
+}
 
 // What a workgroup needs about the sequence that holds its first unit.
 struct FirstSeq {
