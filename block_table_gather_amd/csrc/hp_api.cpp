@@ -576,9 +576,16 @@ hp_status hp_scatter_quant(const hp_desc *desc, const void *src, uint32_t src_dt
     j.total_tokens = desc->total_tokens;
     j.row_bytes = n;
     j.out_row_bytes = src_row;
-    // a unit is a run of consecutive slots of a page; each wave quantizes
-    // whole rows of it
-    j.rows_per_unit = rows_per_unit(desc->page_size, 1, HP_QUANT_UNIT_ROWS, 0xffffffffu);
+    // 8 values per vector when rows and the source allow 16-byte (or 2 x 16)
+    // loads and 8-byte code stores; single values otherwise
+    j.vec_bytes = (n % 8 == 0 && aligned(src, 16)) ? 16 : 1;
+    // With 16-byte vectors and few sequences a unit is one slot, quantized by
+    // a one-wave workgroup; otherwise a unit is a run of consecutive slots of
+    // a page and each wave of the workgroup quantizes whole rows of it.
+    j.qs_wave_groups = j.vec_bytes == 16 && desc->num_seqs <= hp::kQuantWaveMaxSeqs;
+    j.rows_per_unit = j.qs_wave_groups
+                          ? 1
+                          : rows_per_unit(desc->page_size, 1, HP_QUANT_UNIT_ROWS, 0xffffffffu);
     j.units_per_group = HP_QUANT_UNITS_PER_GROUP;
     const uint64_t upp = desc->page_size / j.rows_per_unit;
     j.unit_bound = desc->total_tokens / j.rows_per_unit +
@@ -593,9 +600,6 @@ hp_status hp_scatter_quant(const hp_desc *desc, const void *src, uint32_t src_dt
     j.pools = &pool;
     j.rows = &rows;
     j.workspace = workspace ? static_cast<unsigned char *>(workspace) + kValidateBytes : nullptr;
-    // 8 values per vector when rows and the source allow 16-byte (or 2 x 16)
-    // loads and 8-byte code stores; single values otherwise
-    j.vec_bytes = (n % 8 == 0 && aligned(src, 16)) ? 16 : 1;
     j.qs_src = src_code;
     j.qs_asym = asym;
     j.qs_scales = const_cast<float *>(desc->scales);

@@ -68,6 +68,10 @@ constexpr uint64_t kFusedMaxSeqs = HP_FUSED_MAX_SEQS;
 constexpr uint32_t kThreads = HP_THREADS;     // threads per copy workgroup
 constexpr uint32_t kPlanChunk = 2048;         // sequences per plan workgroup
 constexpr uint32_t kMaxUnitsPerGroup = 16;
+// Sequences a one-wave quantize-on-scatter workgroup scans from registers
+// (64 lanes x 4): more would make every one-slot workgroup read the counts
+// twice.
+constexpr uint32_t kQuantWaveMaxSeqs = 256;
 // Pools moved by one launch of a batched call (one grid row each); the
 // pointers travel in the kernel arguments. Larger batches take more launches.
 constexpr uint32_t kMaxBatch = 32;
@@ -116,6 +120,9 @@ struct CopyJob {
     // per-slot parameters it writes.
     uint32_t qs_src;
     bool qs_asym;
+    // one 64-thread workgroup per slot (rows_per_unit 1), else four waves
+    // per workgroup with a row each
+    bool qs_wave_groups;
     float *qs_scales;
     uint8_t *qs_zero_points;
 };

@@ -140,11 +140,12 @@ __device__ __forceinline__ uint64_t units_of(const Args &a, uint64_t len, uint64
     return w1 - w0;
 }
 
-// Exclusive scan of (units, tokens) over the workgroup's threads. Returns the
-// thread's exclusive prefix; `total_*` receives the workgroup totals.
+// Exclusive scan of (units, tokens) over the workgroup's NTH threads. Returns
+// the thread's exclusive prefix; `total_*` receives the workgroup totals.
+template <uint32_t NTH = kThreads>
 __device__ __forceinline__ void group_exclusive_scan(uint64_t &u, uint64_t &t,
                                                      uint64_t &total_u, uint64_t &total_t) {
-    __shared__ uint64_t wave_u[kThreads / 64], wave_t[kThreads / 64];
+    __shared__ uint64_t wave_u[NTH / 64], wave_t[NTH / 64];
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint64_t ui = u, ti = t;
 #pragma unroll
@@ -165,7 +166,7 @@ __device__ __forceinline__ void group_exclusive_scan(uint64_t &u, uint64_t &t,
     total_u = 0;
     total_t = 0;
 #pragma unroll
-    for (uint32_t w = 0; w < kThreads / 64; ++w) {
+    for (uint32_t w = 0; w < NTH / 64; ++w) {
         if (w < wave) {
             bu += wave_u[w];
             bt += wave_t[w];
@@ -180,14 +181,14 @@ __device__ __forceinline__ void group_exclusive_scan(uint64_t &u, uint64_t &t,
 
 // Writes unit_end[s] (inclusive running unit count) and tok_begin[s]
 // (exclusive running token count) for s in [s0, s1), starting from the given
-// bases. Each thread takes a contiguous run of ceil((s1-s0)/kThreads)
+// bases. Each of the NTH threads takes a contiguous run of ceil((s1-s0)/NTH)
 // sequences. Ends with a barrier.
-template <typename IdxT, Op OP, typename UE, typename TB>
+template <typename IdxT, Op OP, uint32_t NTH = kThreads, typename UE, typename TB>
 __device__ __forceinline__ void scan_range(const Args &a, uint32_t s0, uint32_t s1,
                                            uint64_t ubase, uint64_t tbase, UE *unit_end,
                                            TB *tok_begin) {
     const uint32_t n = s1 - s0;
-    const uint32_t per = (n + kThreads - 1) / kThreads;
+    const uint32_t per = (n + NTH - 1) / NTH;
     const uint32_t i0 = s0 + min32(n, threadIdx.x * per);
     const uint32_t i1 = s0 + min32(n, (threadIdx.x + 1) * per);
     uint64_t u = 0, t = 0;
@@ -198,7 +199,7 @@ __device__ __forceinline__ void scan_range(const Args &a, uint32_t s0, uint32_t 
         t += len;
     }
     uint64_t tu, tt;
-    group_exclusive_scan(u, t, tu, tt);
+    group_exclusive_scan<NTH>(u, t, tu, tt);
     u += ubase;
     t += tbase;
     for (uint32_t i = i0; i < i1; ++i) {
@@ -217,6 +218,13 @@ __device__ __forceinline__ void scan_range(const Args &a, uint32_t s0, uint32_t 
 // scanned table afterwards. Measured on MI355X on the decode batch: the
 // in-scan lookup gains 5 % on gather and scatter (8 KB units) and loses
 // 0.5 % on dequant, whose larger units make the lookup a smaller share.
+// Threads per copy workgroup: quantize-on-scatter with U = 1 runs one wave
+// per workgroup, one slot each (rows are then scheduled one by one instead of
+// four to a workgroup); every other instance runs kThreads.
+constexpr uint32_t block_threads(Op op, int u) {
+    return (op == Op::ScatterQuant && u == 1) ? 64u : kThreads;
+}
+
 constexpr bool locate_in_scan(Op op) {
     return op == Op::Gather || op == Op::Scatter || op == Op::ScatterQuant;
 }
@@ -228,7 +236,7 @@ struct FirstSeq {
 };
 
 // Sequences per thread whose count, start and seq_ptr stay in registers
-// between the two passes of the fused scan (up to kThreads * this many
+// between the two passes of the fused scan (up to threads * this many
 // sequences; beyond, the second pass reads them again).
 constexpr uint32_t kScanRegs = 4;
 
@@ -237,11 +245,11 @@ constexpr uint32_t kScanRegs = 4;
 // g0 also writes that sequence's values to `first`. The workgroup then starts
 // moving after one pass of loads (counts and seq_ptr together) and two
 // barriers, with no search and no further load. Ends with a barrier.
-template <typename IdxT, Op OP>
+template <typename IdxT, Op OP, uint32_t NTH = kThreads>
 __device__ __forceinline__ void fused_scan_locate(const Args &a, uint32_t S, uint32_t g0,
                                                   uint32_t *unit_end, uint64_t *tok_begin,
                                                   FirstSeq *first) {
-    const uint32_t per = (S + kThreads - 1) / kThreads;  // wave-uniform
+    const uint32_t per = (S + NTH - 1) / NTH;  // wave-uniform
     const uint32_t i0 = min32(S, threadIdx.x * per);
     const uint32_t i1 = min32(S, (threadIdx.x + 1) * per);
     const bool with_start = writes_pool(OP) && a.seq_start;
@@ -274,7 +282,7 @@ __device__ __forceinline__ void fused_scan_locate(const Args &a, uint32_t S, uin
         }
     }
     uint64_t tu, tt;
-    group_exclusive_scan(u, t, tu, tt);
+    group_exclusive_scan<NTH>(u, t, tu, tt);
     if (per <= kScanRegs) {
 #pragma unroll
         for (uint32_t k = 0; k < kScanRegs; ++k) {
@@ -940,7 +948,8 @@ __host__ __device__ constexpr size_t lds_table_bytes(uint32_t S) {
 // One kernel for all three moves. FUSED: per-sequence offsets rebuilt in LDS
 // (dynamic LDS = 8*S + 4*S bytes); otherwise read from the plan arrays.
 template <typename IdxT, Op OP, int VEC, bool FUSED, bool NTL, int QM = -1, int U = kCopyUnroll>
-__global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
+__global__ __launch_bounds__(block_threads(OP, U)) void copy_kernel(Args a) {
+    constexpr uint32_t NTH = block_threads(OP, U);
     extern __shared__ __align__(16) unsigned char lds[];
     const uint32_t S = a.num_seqs;
     const uint32_t *unit_end;
@@ -951,7 +960,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
     if constexpr (OP == Op::Dequant && (QM == 2 || QM == 3)) {
         QParam *t = reinterpret_cast<QParam *>(lds + (FUSED ? lds_table_bytes(S) : 0));
         const uint32_t flip = a.quant_unsigned ? 0x80u : 0u;
-        for (uint32_t c = threadIdx.x; c < a.quant_channels; c += kThreads)
+        for (uint32_t c = threadIdx.x; c < a.quant_channels; c += NTH)
             t[c] = QParam{a.quant_scales[c], zp_at(a, c, flip)};
         __syncthreads();
         tab = t;
@@ -964,9 +973,9 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
         uint64_t *tb = reinterpret_cast<uint64_t *>(lds);
         uint32_t *ue = reinterpret_cast<uint32_t *>(lds + 8 * (size_t)S);
         if constexpr (locate_in_scan(OP))
-            fused_scan_locate<IdxT, OP>(a, S, g0, ue, tb, &first);
+            fused_scan_locate<IdxT, OP, NTH>(a, S, g0, ue, tb, &first);
         else
-            scan_range<IdxT, OP>(a, 0, S, 0, 0, ue, tb);
+            scan_range<IdxT, OP, NTH>(a, 0, S, 0, 0, ue, tb);
         unit_end = ue;
         tok_begin = tb;
     } else {
@@ -1031,7 +1040,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(Args a) {
             const uint64_t end = start + len;
             const uint64_t zend = a.zero_tail ? udiv(end + P - 1, a.div_page) * P : end;
             const uint32_t lane = threadIdx.x & 63;
-            for (uint32_t r = threadIdx.x >> 6; r < rpc; r += kThreads / 64) {
+            for (uint32_t r = threadIdx.x >> 6; r < rpc; r += NTH / 64) {
                 const uint64_t pos = w * rpc + r;
                 const uint64_t slot = phys * P + (pos - q * P);
                 unsigned char *row = pool + slot * a.row_bytes;
@@ -1320,7 +1329,8 @@ hipError_t launch_vec(const Args &a, bool fused, dim3 grid, uint32_t plan_chunks
         (OP == Op::Dequant && (QM == 2 || QM == 3)) ? sizeof(QParam) * (size_t)a.quant_channels : 0;
     if (fused) {
         const size_t lds = lds_table_bytes(a.num_seqs) + qlds;
-        hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, true, NTL, QM, U>), grid, dim3(kThreads), lds,
+        hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, true, NTL, QM, U>), grid,
+                           dim3(block_threads(OP, U)), lds,
                            stream, a);
         return hipGetLastError();
     }
@@ -1339,9 +1349,24 @@ hipError_t launch_vec(const Args &a, bool fused, dim3 grid, uint32_t plan_chunks
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, false, NTL, QM, U>), grid, dim3(kThreads), qlds,
+    hipLaunchKernelGGL((copy_kernel<IdxT, OP, VEC, false, NTL, QM, U>), grid,
+                       dim3(block_threads(OP, U)), qlds,
                        stream, a);
     return hipGetLastError();
+}
+
+template <typename IdxT, int VEC, int U>
+hipError_t launch_quant(const Args &a, bool fused, dim3 grid, uint32_t chunks, uint32_t *ue,
+                        uint64_t *tb, hipStream_t st, int qm) {
+    constexpr Op OP = Op::ScatterQuant;
+    switch (qm) {  // source type * 2 + asymmetric
+    case 0: return launch_vec<IdxT, OP, VEC, false, 0, U>(a, fused, grid, chunks, ue, tb, st);
+    case 1: return launch_vec<IdxT, OP, VEC, false, 1, U>(a, fused, grid, chunks, ue, tb, st);
+    case 2: return launch_vec<IdxT, OP, VEC, false, 2, U>(a, fused, grid, chunks, ue, tb, st);
+    case 3: return launch_vec<IdxT, OP, VEC, false, 3, U>(a, fused, grid, chunks, ue, tb, st);
+    case 4: return launch_vec<IdxT, OP, VEC, false, 4, U>(a, fused, grid, chunks, ue, tb, st);
+    default: return launch_vec<IdxT, OP, VEC, false, 5, U>(a, fused, grid, chunks, ue, tb, st);
+    }
 }
 
 // Load policy per move (chosen on the host, measured on MI355X): a gather
@@ -1352,14 +1377,12 @@ template <typename IdxT, Op OP, int VEC>
 hipError_t launch_policy(const Args &a, bool ntl, bool fused, dim3 grid, uint32_t chunks,
                          uint32_t *ue, uint64_t *tb, hipStream_t st, int qm, int u) {
     if constexpr (OP == Op::ScatterQuant) {
-        switch (qm) {  // source type * 2 + asymmetric
-        case 0: return launch_vec<IdxT, OP, VEC, false, 0>(a, fused, grid, chunks, ue, tb, st);
-        case 1: return launch_vec<IdxT, OP, VEC, false, 1>(a, fused, grid, chunks, ue, tb, st);
-        case 2: return launch_vec<IdxT, OP, VEC, false, 2>(a, fused, grid, chunks, ue, tb, st);
-        case 3: return launch_vec<IdxT, OP, VEC, false, 3>(a, fused, grid, chunks, ue, tb, st);
-        case 4: return launch_vec<IdxT, OP, VEC, false, 4>(a, fused, grid, chunks, ue, tb, st);
-        default: return launch_vec<IdxT, OP, VEC, false, 5>(a, fused, grid, chunks, ue, tb, st);
+        if constexpr (VEC == 16) {
+            if (u == 1)  // one wave per workgroup, one slot each
+                return launch_quant<IdxT, VEC, 1>(a, fused, grid, chunks, ue, tb, st, qm);
         }
+        // four waves per workgroup, a row each (U = 8)
+        return launch_quant<IdxT, VEC, 8>(a, fused, grid, chunks, ue, tb, st, qm);
     } else if constexpr (OP == Op::Dequant) {
         switch (qm) {
         case 0: return launch_vec<IdxT, OP, VEC, false, 0>(a, fused, grid, chunks, ue, tb, st);
@@ -1495,7 +1518,11 @@ hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
     // the smallest of 2, 4, 8 that covers one unit.
     const uint64_t per_lane = (job.rows_per_unit * job.row_bytes + (uint64_t)kThreads * 16 - 1) /
                               ((uint64_t)kThreads * 16);
-    const int u = per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : 8;
+    // Quantize-on-scatter: 1 for one wave per workgroup, else 8.
+    const int u = job.op == Op::ScatterQuant ? (job.qs_wave_groups ? 1 : 8)
+                  : per_lane <= 2                ? 2
+                  : per_lane <= 4                ? 4
+                                                 : 8;
     // The plan arrays depend only on the shared table: the plan kernels run
     // with the first launch only, later launches of a large batch reuse them.
     for (uint32_t first = 0; first < job.count; first += kMaxBatch, chunks = 0) {
