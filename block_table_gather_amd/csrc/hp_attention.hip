@@ -42,6 +42,7 @@
 #include "hp_internal.h"
 
 #include <stdint.h>
+#include <type_traits>
 
 namespace hp {
 namespace {
@@ -654,10 +655,12 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
     // products (which free the K registers), and its V loads follow tile tb's
     // V writes to LDS, so they are in flight during the softmax and the
     // weights x V products.
-    load_k(0);
-    load_v(0);
-    for (uint32_t tb = 0; tb < n; tb += kMfmaTile) {
-        const bool more = tb + kMfmaTile < n;
+    // One 32-token tile; MORE: the next tile's loads are issued inside it.
+    // The last tile is a separate copy (no prefetch) so that the loop body
+    // has no branch around its loads: the wait for a tile's K then leaves
+    // its V loads in flight.
+    auto tile = [&](uint32_t tb, auto more_tag) {
+        constexpr bool more = decltype(more_tag)::value;
         // scores: lane holds rows 4 grp + i of token tb + 16 b + c16
         float x[2][4];
 #pragma unroll
@@ -671,7 +674,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
             for (int i = 0; i < 4; ++i)
                 x[b][i] = ok ? acc[i] * a.qscale : -__builtin_inff();
         }
-        if (more)
+        if constexpr (more)
             load_k(tb + kMfmaTile);
         // online softmax per row (the tile's first token is in range, so the
         // new maximum is finite)
@@ -708,7 +711,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
             *reinterpret_cast<u32x4 *>(vt + jt * VRB + 16 * dc) = vc[c];
         }
         wave_lds_sync();
-        if (more)
+        if constexpr (more)
             load_v(tb + kMfmaTile);
         // weights as three A operands whose sum is the binary32 weight
         V8 pa[3];
@@ -740,7 +743,13 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
             for (int k = 0; k < 3; ++k)
                 o[db] = M::mma(pa[k], vb, o[db]);
         }
-    }
+    };
+    load_k(0);
+    load_v(0);
+    uint32_t tb = 0;
+    for (; tb + kMfmaTile < n; tb += kMfmaTile)
+        tile(tb, std::integral_constant<bool, true>());
+    tile(tb, std::integral_constant<bool, false>());  // n >= 1: the unit's last tile
 
     // rows 4 grp + i: query head gz + 4 grp + i of kv head h, column 16 db + c16
     const uint32_t units = uni(unit_end[s]) - u0;
