@@ -24,9 +24,9 @@
 //    from the token counts (a 64-lane shuffle scan per wave, wave totals
 //    combined through LDS), so one launch does everything; above it, a plan
 //    pass writes them to the workspace and the copy kernel reads them there.
-//  * Gather and scatter workgroups learn their first unit's sequence inside
-//    the fused scan (the owning thread publishes it through LDS); the others
-//    search the scanned table. The block-table entry of a unit is read once
+//  * Gather, scatter and quantize-on-scatter workgroups learn their first
+//    unit's sequence inside the fused scan (the owning thread publishes it
+//    through LDS); dequant searches the scanned table. The block-table entry of a unit is read once
 //    per unit into a scalar register; the sequence's scalars are reloaded
 //    only when the walk moves to the next sequence.
 //  * Copies are 16-byte vector loads and non-temporal 16-byte vector stores,
@@ -36,6 +36,10 @@
 //  * Dequant reads 8 int8 values per lane and writes 8 bf16 values (16 B) per
 //    lane, so both sides stay fully coalesced; the unit's per-slot scales sit
 //    one per lane and are fetched with a cross-lane shuffle.
+//  * Quantize-on-scatter: a wave quantizes a whole row, its extremes first
+//    (combined with shuffles) and then its codes. With 16-byte vectors and
+//    at most 256 sequences a workgroup is one wave and its unit one slot;
+//    otherwise four waves take a unit of up to 4 slots, a row each.
 #include "hp_device.h"
 #include "hp_internal.h"
 
