@@ -133,11 +133,11 @@ def test_scatter_quant_decode_full(hp, asym):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("num_seqs", [200, 256, 1025, 4096])
+@pytest.mark.parametrize("num_seqs", [200, 256, 257, 1025, 4096])
 def test_scatter_quant_fused_many(hp, num_seqs):
     """Up to the fused table's 4,096 sequences: up to 256 a one-wave
-    workgroup takes each slot, its lanes holding up to 4 sequences each; past
-    that four waves take a run of slots, and past 1,024 each scan thread reads
+    workgroup takes each slot, its lanes holding up to 4 sequences each; from
+    257 four waves take a run of slots, and past 1,024 each scan thread reads
     its sequences again when it finds the workgroup's first unit."""
     w = workloads.random_small(1795 + num_seqs, max_len=24, page_sizes=(4, 16), heads=(2,),
                                dims=(64,), alias=False, with_start=True, num_seqs=num_seqs)
