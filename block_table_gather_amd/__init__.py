@@ -263,14 +263,34 @@ def workspace_bytes(desc, total_tokens=0):
     return int(_lib.hp_workspace_bytes(desc.with_tokens(total_tokens)))
 
 
-def _workspace(desc, total_tokens, workspace):
+def _torch_stream(stream, device):
+    """The torch stream object a call runs on (None: the current stream)."""
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _own_workspace(n, device, stream):
+    """A workspace the binding allocates for one call. The caching allocator
+    hands out blocks per stream, so the block is recorded on the call's
+    stream: it is not reused by other work until that stream has passed the
+    call, even after the binding drops it."""
+    torch = _torch()
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    ws.record_stream(_torch_stream(stream, device))
+    return ws
+
+
+def _workspace(desc, total_tokens, workspace, stream=None):
     if workspace is not None:
         return workspace.data_ptr(), workspace.numel() * workspace.element_size()
     n = workspace_bytes(desc, total_tokens)
     if n == 0:
         return None, 0
-    torch = _torch()
-    ws = torch.empty(n, dtype=torch.uint8, device=desc.device)
+    ws = _own_workspace(n, desc.device, stream)
     desc._ws = ws  # keep alive until the next call on this descriptor
     return ws.data_ptr(), n
 
@@ -282,7 +302,7 @@ def validate(desc, total_tokens, seq_start=None, *, workspace=None, stream=None,
     (the library writes small descriptors' results there directly);
     default: a host struct."""
     p = desc.with_tokens(total_tokens)
-    ws, n = _workspace(desc, total_tokens, workspace)
+    ws, n = _workspace(desc, total_tokens, workspace, stream)
     if result is None:
         res = HpValidateResult()
         res_p = ctypes.byref(res)
@@ -304,7 +324,7 @@ def gather(desc, out, *, checked=False, streaming=False, workspace=None, stream=
     the pool is read with non-temporal loads; the result is the same."""
     T = out.shape[0]
     p = desc.with_tokens(T)
-    ws, n = _workspace(desc, T, workspace)
+    ws, n = _workspace(desc, T, workspace, stream)
     flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_STREAM if streaming else 0)
     _check(_lib.hp_gather(p, _ptr(out), ws, n, flags, _stream(stream, desc.device)),
            "hp_gather")
@@ -316,7 +336,7 @@ def scatter(desc, src, seq_start=None, *, zero_tail=False, checked=False, worksp
     """Writes src[T, H, D] (T = src.shape[0]) into the pool."""
     T = src.shape[0]
     p = desc.with_tokens(T)
-    ws, n = _workspace(desc, T, workspace)
+    ws, n = _workspace(desc, T, workspace, stream)
     flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_ZERO_TAIL if zero_tail else 0)
     _check(_lib.hp_scatter(p, _ptr(src), _ptr(seq_start), ws, n, flags,
                            _stream(stream, desc.device)), "hp_scatter")
@@ -326,7 +346,7 @@ def gather_dequant(desc, out, *, checked=False, workspace=None, stream=None):
     """out[T, H, D] (bfloat16) <- dequantised logical tensor of an int8 pool."""
     T = out.shape[0]
     p = desc.with_tokens(T)
-    ws, n = _workspace(desc, T, workspace)
+    ws, n = _workspace(desc, T, workspace, stream)
     _check(_lib.hp_gather_dequant(p, _ptr(out), DTYPE["bf16"], ws, n,
                                   HP_FLAG_CHECKED if checked else 0,
                                   _stream(stream, desc.device)), "hp_gather_dequant")
@@ -342,7 +362,7 @@ def gather_dequant_q(desc, out, scheme, scales, *, axis=0, block_size=None, zero
     element type, or None. desc.scales is not used."""
     T = out.shape[0]
     p = desc.with_tokens(T)
-    ws, n = _workspace(desc, T, workspace)
+    ws, n = _workspace(desc, T, workspace, stream)
     q = HpQuant(QUANT_SCHEME[scheme] if isinstance(scheme, str) else int(scheme),
                 int(axis), int(desc.c.page_size if block_size is None else block_size),
                 _ptr(scales), _ptr(zero_points))
@@ -359,7 +379,7 @@ def scatter_quant(desc, src, seq_start=None, *, zero_points=None, zero_tail=Fals
     writing each written slot's scale into desc.scales."""
     T = src.shape[0]
     p = desc.with_tokens(T)
-    ws, n = _workspace(desc, T, workspace)
+    ws, n = _workspace(desc, T, workspace, stream)
     flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_ZERO_TAIL if zero_tail else 0)
     _check(_lib.hp_scatter_quant(p, _ptr(src), _dtype_code(src), _ptr(zero_points),
                                  _ptr(seq_start), ws, n, flags, _stream(stream, desc.device)),
@@ -382,7 +402,7 @@ def paged_attention(desc, v_pool, q, out, *, total_tokens, scale=None, checked=F
     p = desc.with_tokens(total_tokens)
     n = int(_lib.hp_attention_workspace_bytes(p, Hq))
     if workspace is None and n:
-        workspace = _torch().empty(n, dtype=_torch().uint8, device=q.device)
+        workspace = _own_workspace(n, q.device, stream)
         desc._ws = workspace  # keep alive until the next call on this descriptor
     if scale is None:
         scale = 1.0 / float(desc.c.head_dim) ** 0.5
@@ -409,7 +429,7 @@ def gather_batch(desc, pools, outs, *, checked=False, streaming=False, workspace
     page_pool is ignored). T = outs[0].shape[0]."""
     T = outs[0].shape[0] if len(outs) else 0
     p = desc.with_tokens(T)
-    ws, n = _workspace(desc, T, workspace)
+    ws, n = _workspace(desc, T, workspace, stream)
     pa, oa = _ptr_array(pools), _ptr_array(outs)
     flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_STREAM if streaming else 0)
     _check(_lib.hp_gather_batch(p, len(pools), pa, oa, ws, n, flags,
@@ -422,7 +442,7 @@ def scatter_batch(desc, pools, srcs, seq_start=None, *, zero_tail=False, checked
     """Writes srcs[i][T, H, D] into pools[i] through desc's table."""
     T = srcs[0].shape[0] if len(srcs) else 0
     p = desc.with_tokens(T)
-    ws, n = _workspace(desc, T, workspace)
+    ws, n = _workspace(desc, T, workspace, stream)
     pa, sa = _ptr_array(pools), _ptr_array(srcs)
     flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_ZERO_TAIL if zero_tail else 0)
     _check(_lib.hp_scatter_batch(p, len(pools), pa, sa, _ptr(seq_start), ws, n, flags,
@@ -434,7 +454,7 @@ def gather_dequant_batch(desc, pools, scales, outs, *, checked=False, workspace=
     """outs[i] (bf16) <- dequantised gather of int8 pools[i] with scales[i]."""
     T = outs[0].shape[0] if len(outs) else 0
     p = desc.with_tokens(T)
-    ws, n = _workspace(desc, T, workspace)
+    ws, n = _workspace(desc, T, workspace, stream)
     pa, sa, oa = _ptr_array(pools), _ptr_array(scales), _ptr_array(outs)
     _check(_lib.hp_gather_dequant_batch(p, len(pools), pa, sa, oa, DTYPE["bf16"], ws, n,
                                         HP_FLAG_CHECKED if checked else 0,
@@ -451,7 +471,7 @@ def copy_pages(desc, src_pages, dst_pages, *, checked=False, workspace=None, str
     if dst_pages.numel() != n:
         raise ValueError("src_pages and dst_pages differ in length")
     p = desc.with_tokens(0)
-    ws, wn = _workspace(desc, 0, workspace)
+    ws, wn = _workspace(desc, 0, workspace, stream)
     _check(_lib.hp_copy_pages(p, _ptr(src_pages), _ptr(dst_pages), n, ws, wn,
                               HP_FLAG_CHECKED if checked else 0, _stream(stream, desc.device)),
            "hp_copy_pages")
@@ -464,7 +484,7 @@ def copy_pages_batch(desc, pools, scales, src_pages, dst_pages, *, checked=False
     if dst_pages.numel() != n:
         raise ValueError("src_pages and dst_pages differ in length")
     p = desc.with_tokens(0)
-    ws, wn = _workspace(desc, 0, workspace)
+    ws, wn = _workspace(desc, 0, workspace, stream)
     pa = _ptr_array(pools)
     sa = _ptr_array(scales) if scales is not None else None
     _check(_lib.hp_copy_pages_batch(p, len(pools), pa, sa, _ptr(src_pages), _ptr(dst_pages), n,

@@ -1071,7 +1071,9 @@ __global__ __launch_bounds__(block_threads(OP, U)) void copy_kernel(Args a) {
             const uint64_t w = udiv(start, a.div_rpc) + u;
             const uint64_t pos0 = w * rpc;
             const uint64_t q = udiv(w, a.div_upp);
-            const uint32_t slot0 = (uint32_t)(pos0 - q * P);
+            // slot of the window's first position in its page; byte offsets
+            // inside a page are 64-bit (a page may exceed 4 GiB)
+            const uint64_t slot0 = pos0 - q * P;
             const uint64_t phys = uni64(ld_idx<IdxT>(a.block_table, sp + q));
             const uint64_t end = start + len;
             unsigned char *page = pool + phys * P * a.row_bytes;
@@ -1079,7 +1081,7 @@ __global__ __launch_bounds__(block_threads(OP, U)) void copy_kernel(Args a) {
             const uint64_t wb = pos0 + rpc < end ? pos0 + rpc : end;
             if (wa < wb) {
                 const unsigned char *from = rowsp + (tb + (wa - start)) * a.row_bytes;
-                copy_span<U, VEC, NTL>(from, page + (slot0 + (uint32_t)(wa - pos0)) * a.row_bytes,
+                copy_span<U, VEC, NTL>(from, page + (slot0 + (wa - pos0)) * a.row_bytes,
                                (uint32_t)(wb - wa) * a.row_bytes);
             }
             if (a.zero_tail) {
@@ -1087,7 +1089,7 @@ __global__ __launch_bounds__(block_threads(OP, U)) void copy_kernel(Args a) {
                 const uint64_t za = pos0 > end ? pos0 : end;
                 const uint64_t zb = pos0 + rpc < zend ? pos0 + rpc : zend;
                 if (za < zb)
-                    zero_span<VEC>(page + (slot0 + (uint32_t)(za - pos0)) * a.row_bytes,
+                    zero_span<VEC>(page + (slot0 + (za - pos0)) * a.row_bytes,
                                    (uint32_t)(zb - za) * a.row_bytes);
             }
         } else {

@@ -1,7 +1,7 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times: whole-output bit comparisons where the oracle finishes in
-seconds, oracle rows computed one by one (sampled) for the 1.6M-token int8
-pool, plus properties that hold at any size."""
+benchmark times: whole-output bit comparisons (the 1.6M-token int8 pool in
+ranges of sequences, each against the oracle on its own slice of the
+table), plus properties that hold at any size."""
 import numpy as np
 import pytest
 import torch
@@ -89,41 +89,57 @@ def test_append_scatter_zero_tail(hp):
     _free()
 
 
-def _sample_rows(w, n, seed):
-    rng = np.random.default_rng(seed)
-    T = w.total_tokens
-    starts = np.concatenate([[0], np.cumsum(w.seq_lens.astype(np.int64))])
-    edges = np.concatenate([starts[:-1], starts[1:] - 1])
-    edges = edges[(edges >= 0) & (edges < T)]
-    return np.unique(np.concatenate([rng.integers(0, T, size=n), edges]))
+def _seq_chunks(w, per):
+    """(first sequence, end sequence, first row, end row) of consecutive
+    sequence ranges of `per` sequences each, covering the whole batch."""
+    tok = np.concatenate([[0], np.cumsum(w.seq_lens.astype(np.int64))])
+    for s0 in range(0, w.num_seqs, per):
+        s1 = min(s0 + per, w.num_seqs)
+        yield s0, s1, int(tok[s0]), int(tok[s1])
+
+
+def _sub_kw(w, s0, s1):
+    """Oracle arguments for sequences [s0, s1) on their own: their slice of
+    the block table, seq_ptr rebased to 0 and their counts."""
+    sp = w.seq_ptr.astype(np.int64)
+    return dict(page_size=w.page_size, num_heads=w.num_heads, head_dim=w.head_dim,
+                block_table=w.block_table[sp[s0]: sp[s1]],
+                seq_ptr=(sp[s0: s1 + 1] - sp[s0]).astype(np.uint64),
+                seq_lens=w.seq_lens[s0:s1])
 
 
 def test_quant_dequant_and_raw_gather(hp):
     """1,024 log-normal sequences over a 200,000-page int8 pool with per-slot
-    scales and a uint64 table: dequant rows sampled against the oracle
-    (random rows plus every sequence's first and last row), and the raw int8
-    gather of the same descriptor the same way."""
+    scales and a uint64 table: every one of the 1.65M dequantised rows, and
+    every row of the raw int8 gather of the same descriptor, against the
+    oracle. The oracle runs on ranges of 64 sequences (each with its own
+    slice of the table), compared with the matching rows of the one GPU
+    launch over the whole batch."""
     w = workloads.quant()
     say("quant full", w.describe())
     d = OnDevice(w)
     assert hp.validate(d.desc, w.total_tokens) == ("HP_OK", 0)
+    pool_host = host_bits(d.pool).view(np.int8)
+    scales = d.scales.cpu().numpy()
     out = d.empty_out(dtype=torch.bfloat16)
     hp.gather_dequant(d.desc, out)
     torch.cuda.synchronize()
-    rows = _sample_rows(w, 40000, 1)
-    pool_host = host_bits(d.pool).view(np.int8)
-    scales = d.scales.cpu().numpy()
-    want = oracle.gather_dequant_rows(pool_host, scales, rows, **d.oracle_kw())
-    got = host_bits(out[torch.from_numpy(rows).to(DEV)])
-    bf16_bits_equal(got, want, "quant dequant")
+    rows = 0
+    for s0, s1, r0, r1 in _seq_chunks(w, 64):
+        want = oracle.gather_dequant(pool_host, scales, **_sub_kw(w, s0, s1))
+        bf16_bits_equal(host_bits(out[r0:r1]), want, f"quant dequant, sequences {s0}..{s1 - 1}")
+        rows += r1 - r0
+    assert rows == w.total_tokens
     del out
     _free()
     raw = d.empty_out()
     hp.gather(d.desc, raw)
     torch.cuda.synchronize()
-    want_raw = oracle.gather_rows(pool_host, rows, **d.oracle_kw())
-    assert_bits_equal(host_bits(raw[torch.from_numpy(rows).to(DEV)]), want_raw.view(np.uint8),
-                      "quant raw gather")
+    for s0, s1, r0, r1 in _seq_chunks(w, 64):
+        want_raw = oracle.gather(pool_host, **_sub_kw(w, s0, s1))
+        assert_bits_equal(host_bits(raw[r0:r1]), want_raw.view(np.uint8),
+                          f"quant raw gather, sequences {s0}..{s1 - 1}")
+    say("quant full: all", w.total_tokens, "rows bit-exact (dequant and raw gather)")
     del d, raw
     _free()
 
@@ -178,4 +194,34 @@ def test_large_ragged_scatter_streams(hp, zero_tail):
     torch.cuda.synchronize()
     assert_bits_equal(host_bits(d.pool), want, "large scatter")
     del d, src, want
+    _free()
+
+
+def test_scatter_into_a_page_beyond_4gib(hp):
+    """One page of 524,288 slots x 16 KiB rows (8 GiB, f16 64 heads x 128): a
+    scatter of 16 rows starting at slot 300,000, whose byte offset inside the
+    page (4.9e9) does not fit 32 bits, with the page's tail zeroed. The rows
+    land at their slot, the tail is zero, and every other byte keeps the
+    sentinel (in particular the slots a 32-bit offset would wrap to)."""
+    P, H, D, start, n = 524_288, 64, 128, 300_000, 16
+    row = H * D  # f16 elements
+    pool = torch.empty((1, P, H, D), dtype=torch.float16, device=DEV)
+    sentinel = workloads.SENTINEL_BITS[2]
+    fill = workloads._signed(sentinel, 2)
+    pool.view(torch.int16).fill_(fill)
+    say("scatter, page beyond 4 GiB", P * row * 2, "bytes per page")
+    w = workloads.Workload("bigpage", "f16", P, H, D, 1, np.uint64, np.zeros(1, np.uint64),
+                           np.array([0, 1], np.uint64), np.array([n], np.uint64),
+                           seq_start=np.array([start], np.uint64), seed=45)
+    d = OnDevice(w, pool=pool)
+    src = w.make_src(DEV)
+    hp.scatter(d.desc, src, d.ss, zero_tail=True)
+    torch.cuda.synchronize()
+    flat = pool.view(torch.int16).view(P, row)
+    assert torch.equal(flat[start: start + n], src.view(torch.int16).view(n, row))
+    assert bool((flat[start + n:] == 0).all())
+    assert bool((flat[:start] == fill).all())
+    wrapped = (start * row * 2) % (1 << 32) // (row * 2)
+    assert wrapped < start and bool((flat[wrapped: wrapped + n] == fill).all())
+    del pool, flat, d, src
     _free()

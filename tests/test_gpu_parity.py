@@ -85,6 +85,34 @@ def test_gather_many_sequences_plan_path(hp):
     assert_bits_equal(host_bits(out), oracle_gather(d), "plan path")
 
 
+def test_plan_path_on_a_side_stream(hp):
+    """The plan path's workspace, allocated by the binding, on a stream other
+    than the current one: it is recorded on the call's stream, so the
+    caching allocator keeps it for that stream's work. Gather and scatter
+    there, then compare after the stream finished."""
+    w = workloads.random_small(78, max_seqs=9000, max_len=40, page_sizes=(4, 16),
+                               heads=(2,), dims=(64,), dtypes=("bf16",), num_seqs=5000,
+                               alias=False)
+    say("plan path, side stream", w.describe())
+    d = OnDevice(w)
+    out = d.empty_out()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        blank = torch.zeros_like(d.pool)
+    d2 = OnDevice(w, pool=blank)
+    hp.gather(d.desc, out, stream=side)
+    hp.scatter(d2.desc, out, stream=side)
+    # work on the current stream meanwhile, allocating as it goes
+    junk = [torch.ones(1 << 16, device=DEV) for _ in range(8)]
+    side.synchronize()
+    want = oracle_gather(d)
+    assert_bits_equal(host_bits(out), want, "plan path gather, side stream")
+    want_pool = oracle.scatter(host_bits(torch.zeros_like(d.pool)), want, **d.oracle_kw())
+    assert_bits_equal(host_bits(blank), want_pool, "plan path scatter, side stream")
+    del junk
+
+
 @pytest.mark.parametrize("case", ["odd_row", "row6", "page1", "misaligned_out"])
 def test_gather_vector_width_fallbacks(hp, case):
     """Rows whose byte size is not a multiple of 16, a one-token page, and an
