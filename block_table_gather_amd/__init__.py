@@ -22,6 +22,7 @@ import os
 import torch  # noqa: F401,E402
 
 __all__ = ["Descriptor", "HpError", "gather", "scatter", "gather_dequant", "validate",
+           "validate_async", "validate_verdict",
            "gather_dequant_q", "QUANT_SCHEME", "paged_attention", "attention_workspace_bytes",
            "scatter_quant",
            "gather_batch", "scatter_batch", "gather_dequant_batch", "copy_pages",
@@ -64,7 +65,7 @@ STATUS = {
 CODE = {v: k for k, v in STATUS.items()}
 HP_INDEX_U32, HP_INDEX_U64 = 0x00, 0x01
 DTYPE = {"i8": 1, "u8": 2, "f16": 3, "bf16": 4, "f32": 5, "f64": 6}
-HP_FLAG_CHECKED, HP_FLAG_ZERO_TAIL, HP_FLAG_STREAM = 1, 2, 4
+HP_FLAG_CHECKED, HP_FLAG_ZERO_TAIL, HP_FLAG_STREAM, HP_FLAG_GATED = 1, 2, 4, 8
 # Quantization scheme tags (include/hp.h, HP_QUANT_*).
 QUANT_SCHEME = {"per_tensor": 0x01, "per_channel": 0x02, "per_block_affine": 0x03}
 
@@ -106,6 +107,10 @@ _lib.hp_workspace_bytes.restype = _sz
 _lib.hp_workspace_bytes.argtypes = [_P]
 _lib.hp_validate.restype = ctypes.c_int
 _lib.hp_validate.argtypes = [_P, _vp, _vp, _sz, ctypes.POINTER(HpValidateResult), _vp]
+_lib.hp_validate_async.restype = ctypes.c_int
+_lib.hp_validate_async.argtypes = [_P, _vp, _vp, _sz, _vp]
+_lib.hp_validate_verdict.restype = ctypes.c_int
+_lib.hp_validate_verdict.argtypes = [_P, _vp, ctypes.POINTER(HpValidateResult)]
 _lib.hp_gather.restype = ctypes.c_int
 _lib.hp_gather.argtypes = [_P, _vp, _vp, _sz, _u32, _vp]
 _lib.hp_scatter.restype = ctypes.c_int
@@ -317,7 +322,37 @@ def validate(desc, total_tokens, seq_start=None, *, workspace=None, stream=None,
     return name, int(res.index)
 
 
-def gather(desc, out, *, checked=False, streaming=False, workspace=None, stream=None):
+def validate_async(desc, total_tokens, seq_start=None, *, workspace, stream=None):
+    """Enqueues hp_validate_async: the verdict stays in the first 16 bytes of
+    `workspace` (a device tensor of at least 256 bytes), where moves called
+    with gated=True on that workspace read it. Returns at once."""
+    p = desc.with_tokens(total_tokens)
+    _check(_lib.hp_validate_async(p, _ptr(seq_start), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(),
+                                  _stream(stream, desc.device)), "hp_validate_async")
+
+
+def validate_verdict(desc, total_tokens, workspace):
+    """(status name, index) of the verdict hp_validate_async left in
+    `workspace` (copied back here; the caller orders this after the check,
+    e.g. by synchronizing its stream)."""
+    words = workspace[:16].cpu().numpy().tobytes()
+    res = HpValidateResult()
+    buf = ctypes.create_string_buffer(words, 16)
+    _lib.hp_validate_verdict(desc.with_tokens(total_tokens), buf, ctypes.byref(res))
+    return STATUS.get(res.code, str(res.code)), int(res.index)
+
+
+def _flags(checked=False, gated=False, **named):
+    f = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_GATED if gated else 0)
+    for name, on in named.items():
+        if on:
+            f |= {"streaming": HP_FLAG_STREAM, "zero_tail": HP_FLAG_ZERO_TAIL}[name]
+    return f
+
+
+def gather(desc, out, *, checked=False, streaming=False, workspace=None, stream=None,
+           gated=False):
     """out[T, H, D] <- the logical tensor (T = out.shape[0]).
 
     streaming: hint that no pool page is read twice (slices do not alias), so
@@ -325,36 +360,35 @@ def gather(desc, out, *, checked=False, streaming=False, workspace=None, stream=
     T = out.shape[0]
     p = desc.with_tokens(T)
     ws, n = _workspace(desc, T, workspace, stream)
-    flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_STREAM if streaming else 0)
+    flags = _flags(checked, gated, streaming=streaming)
     _check(_lib.hp_gather(p, _ptr(out), ws, n, flags, _stream(stream, desc.device)),
            "hp_gather")
     return out
 
 
 def scatter(desc, src, seq_start=None, *, zero_tail=False, checked=False, workspace=None,
-            stream=None):
+            stream=None, gated=False):
     """Writes src[T, H, D] (T = src.shape[0]) into the pool."""
     T = src.shape[0]
     p = desc.with_tokens(T)
     ws, n = _workspace(desc, T, workspace, stream)
-    flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_ZERO_TAIL if zero_tail else 0)
+    flags = _flags(checked, gated, zero_tail=zero_tail)
     _check(_lib.hp_scatter(p, _ptr(src), _ptr(seq_start), ws, n, flags,
                            _stream(stream, desc.device)), "hp_scatter")
 
 
-def gather_dequant(desc, out, *, checked=False, workspace=None, stream=None):
+def gather_dequant(desc, out, *, checked=False, workspace=None, stream=None, gated=False):
     """out[T, H, D] (bfloat16) <- dequantised logical tensor of an int8 pool."""
     T = out.shape[0]
     p = desc.with_tokens(T)
     ws, n = _workspace(desc, T, workspace, stream)
-    _check(_lib.hp_gather_dequant(p, _ptr(out), DTYPE["bf16"], ws, n,
-                                  HP_FLAG_CHECKED if checked else 0,
+    _check(_lib.hp_gather_dequant(p, _ptr(out), DTYPE["bf16"], ws, n, _flags(checked, gated),
                                   _stream(stream, desc.device)), "hp_gather_dequant")
     return out
 
 
 def gather_dequant_q(desc, out, scheme, scales, *, axis=0, block_size=None, zero_points=None,
-                     checked=False, workspace=None, stream=None):
+                     checked=False, workspace=None, stream=None, gated=False):
     """out[T, H, D] (bfloat16) <- dequantised logical tensor of an int8 or
     uint8 pool under a quantization scheme ("per_tensor", "per_channel" with
     axis 1 or 2, "per_block_affine" with axis 0 and block_size = page size).
@@ -367,20 +401,20 @@ def gather_dequant_q(desc, out, scheme, scales, *, axis=0, block_size=None, zero
                 int(axis), int(desc.c.page_size if block_size is None else block_size),
                 _ptr(scales), _ptr(zero_points))
     _check(_lib.hp_gather_dequant_q(p, ctypes.byref(q), _ptr(out), DTYPE["bf16"], ws, n,
-                                    HP_FLAG_CHECKED if checked else 0,
+                                    _flags(checked, gated),
                                     _stream(stream, desc.device)), "hp_gather_dequant_q")
     return out
 
 
 def scatter_quant(desc, src, seq_start=None, *, zero_points=None, zero_tail=False,
-                  checked=False, workspace=None, stream=None):
+                  checked=False, workspace=None, stream=None, gated=False):
     """Quantizes src[T, H, D] (f16, bf16 or f32) into desc's int8 pool
     (symmetric) or uint8 pool (asymmetric, with zero_points: uint8 per slot),
     writing each written slot's scale into desc.scales."""
     T = src.shape[0]
     p = desc.with_tokens(T)
     ws, n = _workspace(desc, T, workspace, stream)
-    flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_ZERO_TAIL if zero_tail else 0)
+    flags = _flags(checked, gated, zero_tail=zero_tail)
     _check(_lib.hp_scatter_quant(p, _ptr(src), _dtype_code(src), _ptr(zero_points),
                                  _ptr(seq_start), ws, n, flags, _stream(stream, desc.device)),
            "hp_scatter_quant")
@@ -424,40 +458,40 @@ def _ptr_array(tensors):
 
 
 def gather_batch(desc, pools, outs, *, checked=False, streaming=False, workspace=None,
-                 stream=None):
+                 stream=None, gated=False):
     """outs[i][T, H, D] <- gather of pools[i] through desc's table (desc's own
     page_pool is ignored). T = outs[0].shape[0]."""
     T = outs[0].shape[0] if len(outs) else 0
     p = desc.with_tokens(T)
     ws, n = _workspace(desc, T, workspace, stream)
     pa, oa = _ptr_array(pools), _ptr_array(outs)
-    flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_STREAM if streaming else 0)
+    flags = _flags(checked, gated, streaming=streaming)
     _check(_lib.hp_gather_batch(p, len(pools), pa, oa, ws, n, flags,
                                 _stream(stream, desc.device)), "hp_gather_batch")
     return outs
 
 
 def scatter_batch(desc, pools, srcs, seq_start=None, *, zero_tail=False, checked=False,
-                  workspace=None, stream=None):
+                  workspace=None, stream=None, gated=False):
     """Writes srcs[i][T, H, D] into pools[i] through desc's table."""
     T = srcs[0].shape[0] if len(srcs) else 0
     p = desc.with_tokens(T)
     ws, n = _workspace(desc, T, workspace, stream)
     pa, sa = _ptr_array(pools), _ptr_array(srcs)
-    flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_ZERO_TAIL if zero_tail else 0)
+    flags = _flags(checked, gated, zero_tail=zero_tail)
     _check(_lib.hp_scatter_batch(p, len(pools), pa, sa, _ptr(seq_start), ws, n, flags,
                                  _stream(stream, desc.device)), "hp_scatter_batch")
 
 
 def gather_dequant_batch(desc, pools, scales, outs, *, checked=False, workspace=None,
-                         stream=None):
+                         stream=None, gated=False):
     """outs[i] (bf16) <- dequantised gather of int8 pools[i] with scales[i]."""
     T = outs[0].shape[0] if len(outs) else 0
     p = desc.with_tokens(T)
     ws, n = _workspace(desc, T, workspace, stream)
     pa, sa, oa = _ptr_array(pools), _ptr_array(scales), _ptr_array(outs)
     _check(_lib.hp_gather_dequant_batch(p, len(pools), pa, sa, oa, DTYPE["bf16"], ws, n,
-                                        HP_FLAG_CHECKED if checked else 0,
+                                        _flags(checked, gated),
                                         _stream(stream, desc.device)),
            "hp_gather_dequant_batch")
     return outs

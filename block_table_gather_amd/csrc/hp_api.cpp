@@ -120,8 +120,27 @@ uint64_t plan_bytes(const hp_desc *d) {
     return d->num_seqs > hp::kFusedMaxSeqs ? hp::plan_workspace_bytes(d->num_seqs) : 0;
 }
 
-hp_status run_validate(const hp_desc *d, const void *seq_start, void *ws,
-                       hp_validate_result *res, hipStream_t stream) {
+// The validator's two words (smallest failing key, all ones if none; the sum
+// of the token counts) as a status and index.
+hp_status decode_verdict(const uint64_t words[2], uint64_t total_tokens,
+                         hp_validate_result *res) {
+    res->code = HP_OK;
+    res->reserved = 0;
+    res->index = 0;
+    if (words[0] != ~0ull) {
+        static const hp_status by_rank[] = {HP_OK, HP_ERR_SEQPTR_FIRST, HP_ERR_SEQPTR_LAST,
+                                            HP_ERR_SEQPTR_ORDER, HP_ERR_PAGE_RANGE,
+                                            HP_ERR_SEQ_LEN};
+        const uint64_t rank = words[0] >> hp::kKeyShift;
+        res->code = rank >= 1 && rank <= 5 ? by_rank[rank] : HP_ERR_HIP;
+        res->index = words[0] & kMaxIndex;
+    } else if (words[1] != total_tokens) {
+        res->code = HP_ERR_TOTAL_TOKENS;
+    }
+    return (hp_status)res->code;
+}
+
+hp::ValidateJob validate_job(const hp_desc *d, const void *seq_start, void *ws) {
     hp::ValidateJob j;
     j.idx64 = d->index_type == HP_INDEX_U64;
     j.num_pages = d->num_pages;
@@ -133,6 +152,13 @@ hp_status run_validate(const hp_desc *d, const void *seq_start, void *ws,
     j.seq_lens = d->seq_lens;
     j.seq_start = seq_start;
     j.workspace = ws;
+    j.result = nullptr;
+    return j;
+}
+
+hp_status run_validate(const hp_desc *d, const void *seq_start, void *ws,
+                       hp_validate_result *res, hipStream_t stream) {
+    hp::ValidateJob j = validate_job(d, seq_start, ws);
     // The two result words land in the caller's result struct (16 bytes, like
     // them) and are decoded in place after the wait. When the struct is
     // pinned host memory the GPU can reach, a small descriptor's check writes
@@ -155,20 +181,7 @@ hp_status run_validate(const hp_desc *d, const void *seq_start, void *ws,
         return hip_failed(e);
     uint64_t host[2];
     memcpy(host, res, sizeof host);
-    res->code = HP_OK;
-    res->reserved = 0;
-    res->index = 0;
-    if (host[0] != ~0ull) {
-        static const hp_status by_rank[] = {HP_OK, HP_ERR_SEQPTR_FIRST, HP_ERR_SEQPTR_LAST,
-                                            HP_ERR_SEQPTR_ORDER, HP_ERR_PAGE_RANGE,
-                                            HP_ERR_SEQ_LEN};
-        const uint64_t rank = host[0] >> hp::kKeyShift;
-        res->code = rank >= 1 && rank <= 5 ? by_rank[rank] : HP_ERR_HIP;
-        res->index = host[0] & kMaxIndex;
-    } else if (host[1] != d->total_tokens) {
-        res->code = HP_ERR_TOTAL_TOKENS;
-    }
-    return (hp_status)res->code;
+    return decode_verdict(host, d->total_tokens, res);
 }
 
 // Largest divisor of P whose run of rows fits the target unit size (at least
@@ -286,6 +299,10 @@ hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const Members &
     j.workspace = ws ? static_cast<unsigned char *>(ws) + kValidateBytes : nullptr;
     j.vec_bytes = op == hp::Op::Dequant ? widest_vec(g.row_bytes, m, 8, 2)
                                         : widest_vec(g.row_bytes, m, 16, 1);
+    if (flags & HP_FLAG_GATED) {
+        j.gate = static_cast<const unsigned long long *>(ws);
+        j.gate_tokens = d->total_tokens;
+    }
     if (q) {
         j.quant_ext = q->ext;
         j.quant_mode = q->mode;
@@ -306,13 +323,16 @@ hp_status prologue(const hp_desc *d, const Geometry &g, uint32_t flags, uint32_t
                    const void *seq_start, void *ws, size_t ws_bytes, hipStream_t stream,
                    bool *done) {
     *done = false;
-    if (flags & ~allowed)
+    if (flags & ~(allowed | HP_FLAG_GATED))
         return HP_ERR_ARG;
+    const bool checked = flags & HP_FLAG_CHECKED;
+    const bool gated = flags & HP_FLAG_GATED;
+    if (checked && gated)
+        return HP_ERR_ARG;  // one of the two ways of validating
     if (!aligned(seq_start, g.idx_bytes))
         return HP_ERR_ALIGN;
-    const bool checked = flags & HP_FLAG_CHECKED;
     const bool fused = d->num_seqs <= hp::kFusedMaxSeqs;
-    const uint64_t need = (checked || !fused) ? kValidateBytes + plan_bytes(d) : 0;
+    const uint64_t need = (checked || gated || !fused) ? kValidateBytes + plan_bytes(d) : 0;
     hp_status st = check_workspace(ws, ws_bytes, need);
     if (st != HP_OK)
         return st;
@@ -477,6 +497,30 @@ hp_status hp_validate(const hp_desc *desc, const void *seq_start, void *workspac
     return run_validate(desc, seq_start, workspace, res, (hipStream_t)stream);
 }
 
+hp_status hp_validate_async(const hp_desc *desc, const void *seq_start, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    Geometry g;
+    hp_status st = check_desc(desc, &g);
+    if (st != HP_OK)
+        return st;
+    if (!aligned(seq_start, g.idx_bytes))
+        return HP_ERR_ALIGN;
+    if ((st = check_workspace(workspace, workspace_bytes, kValidateBytes)) != HP_OK)
+        return st;
+    const hipError_t e =
+        hp::launch_validate(validate_job(desc, seq_start, workspace), (hipStream_t)stream);
+    return e == hipSuccess ? HP_OK : hip_failed(e);
+}
+
+hp_status hp_validate_verdict(const hp_desc *desc, const void *words,
+                              hp_validate_result *result) {
+    if (!desc || !words || !result)
+        return HP_ERR_NULL;
+    uint64_t w[2];
+    memcpy(w, words, sizeof w);
+    return decode_verdict(w, desc->total_tokens, result);
+}
+
 hp_status hp_gather(const hp_desc *desc, void *out, void *workspace, size_t workspace_bytes,
                     uint32_t flags, void *stream) {
     Geometry g;
@@ -604,6 +648,10 @@ hp_status hp_scatter_quant(const hp_desc *desc, const void *src, uint32_t src_dt
     j.qs_asym = asym;
     j.qs_scales = const_cast<float *>(desc->scales);
     j.qs_zero_points = static_cast<uint8_t *>(zero_points);
+    if (flags & HP_FLAG_GATED) {
+        j.gate = static_cast<const unsigned long long *>(workspace);
+        j.gate_tokens = desc->total_tokens;
+    }
     const hipError_t e = hp::launch_copy(j, (hipStream_t)stream);
     return e == hipSuccess ? HP_OK : hip_failed(e);
 }

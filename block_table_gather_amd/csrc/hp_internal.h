@@ -125,6 +125,12 @@ struct CopyJob {
     bool qs_wave_groups;
     float *qs_scales;
     uint8_t *qs_zero_points;
+    // Gated move: the two verdict words an enqueued validation left on the
+    // device (smallest failing key, all ones if none; token sum). The copy
+    // kernel writes nothing unless the key is all ones and the sum equals
+    // gate_tokens. Null: not gated.
+    const unsigned long long *gate;
+    uint64_t gate_tokens;
 };
 
 // Copy-on-write page copy over `count` pools that share the page IDs.

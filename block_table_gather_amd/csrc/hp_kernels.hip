@@ -119,6 +119,9 @@ struct Args {
     // Quantize-on-scatter: the per-slot parameters it writes.
     float *qs_scales;
     uint8_t *qs_zero_points;
+    // Gated moves: the verdict words of an enqueued validation, or null.
+    const unsigned long long *gate;
+    uint64_t gate_tokens;
     // Pool m of the launch is moved by grid row m (blockIdx.y).
     unsigned char *pool[kMaxBatch];   // scatter writes it, gather/dequant read it
     unsigned char *rows[kMaxBatch];   // the logical tensor of pool m
@@ -969,6 +972,16 @@ __global__ __launch_bounds__(block_threads(OP, U)) void copy_kernel(Args a) {
         __syncthreads();
         tab = t;
     }
+    // A gated launch reads the verdict of the validation enqueued before it
+    // ([Hurray] Storage Invariants: a violating descriptor is rejected). The
+    // words are loaded here, beside the scan's loads, and tested before the
+    // first unit: a rejected launch reads no block-table entry, pool row or
+    // logical row and writes nothing.
+    uint64_t gate_key = ~0ull, gate_sum = a.gate_tokens;
+    if (a.gate) {
+        gate_key = a.gate[0];
+        gate_sum = a.gate[1];
+    }
     const uint32_t g0 =
         group_order<(OP == Op::Scatter && NTL) || OP == Op::ScatterQuant>(blockIdx.x, gridDim.x) *
         a.units_per_group;
@@ -988,6 +1001,8 @@ __global__ __launch_bounds__(block_threads(OP, U)) void copy_kernel(Args a) {
     }
     const uint32_t total = uni(unit_end[S - 1]);
     if (g0 >= total)
+        return;
+    if (uni64(gate_key) != ~0ull || uni64(gate_sum) != a.gate_tokens)
         return;
     const uint32_t g1 = min32(g0 + a.units_per_group, total);
 
@@ -1497,6 +1512,8 @@ hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
         qm = (int)job.qs_src * 2 + (job.qs_asym ? 1 : 0);
     a.qs_scales = job.qs_scales;
     a.qs_zero_points = job.qs_zero_points;
+    a.gate = job.gate;
+    a.gate_tokens = job.gate_tokens;
     a.quant_scales = job.quant_scales;
     a.zero_points = job.zero_points;
     a.head_dim = job.head_dim ? job.head_dim : 1;

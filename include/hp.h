@@ -26,9 +26,11 @@
  *   - gather / scatter / gather_dequant are permissive readers ([Hurray]
  *     Storage Invariants permits a permissive mode): they trust the data
  *     invariants unless HP_FLAG_CHECKED is given, in which case hp_validate
- *     runs first (synchronously) and its code is returned without writing.
- *     Unchecked calls on a descriptor that violates (1)-(3) or the
- *     token-count bound have undefined results.
+ *     runs first (synchronously) and its code is returned without writing;
+ *     with HP_FLAG_GATED the device checks the verdict of an earlier
+ *     hp_validate_async on the same workspace and writes nothing on a
+ *     violation, with no host wait. Unchecked calls on a descriptor that
+ *     violates (1)-(3) or the token-count bound have undefined results.
  *   - An empty batch (num_seqs = 0, seq_ptr = [0], block_table may be NULL;
  *     [Hurray] Buffer Table note) is valid; calls on it enqueue nothing.
  */
@@ -87,11 +89,17 @@ enum {
     HP_FLAG_ZERO_TAIL = 1u << 1, /* scatter: zero the slots of each sequence's last
                                     written page past its last new token ([Hurray]
                                     Partial trailing page: a writer should zero them) */
-    HP_FLAG_STREAM = 1u << 2     /* gather: performance hint that no pool page is read
+    HP_FLAG_STREAM = 1u << 2,    /* gather: performance hint that no pool page is read
                                     twice by this call (the slices do not alias, [Hurray]
                                     Prefix Sharing); the pool is then read with
                                     non-temporal loads. Results are identical with or
                                     without it; with aliased pages it is only slower. */
+    HP_FLAG_GATED = 1u << 3      /* gather, scatter, dequant-gather and their batched and
+                                    quantized forms: the verdict that hp_validate_async
+                                    left in the head of `workspace` decides, on the
+                                    device, whether the call writes anything (see
+                                    hp_validate_async). Not combined with
+                                    HP_FLAG_CHECKED. */
 };
 
 /* A block-paged descriptor for one {kv_role, layer_index} pair ([Hurray]
@@ -158,13 +166,48 @@ hp_status hp_validate(const hp_desc *desc, const void *seq_start, void *workspac
                       size_t workspace_bytes, hp_validate_result *result,
                       void *stream);
 
+/* Enqueue-only validation ([Hurray] Storage Invariants: a reader validates
+ * (1)-(3) and (6) and rejects a descriptor that violates them). The checks,
+ * their order and the first-failure rule are those of hp_validate, and the
+ * host checks happen the same way (rank, paged_axis, shard, sizes, with the
+ * same error codes), but nothing waits: the device leaves its verdict, two
+ * 64-bit words (the smallest failing (check, index) key, all ones when no
+ * check failed, and the sum of seq_lens), in bytes [0, 16) of `workspace`
+ * when `stream` reaches the work.
+ *
+ * A later move on the same workspace with HP_FLAG_GATED, ordered after this
+ * call (same stream, or an event), reads the words on the device and writes
+ * nothing at all (no output row, pool slot, scale or zero point) unless no
+ * check failed and the sum equals that move's total_tokens. So "a rejected
+ * descriptor is never moved" holds with no host round trip between batches.
+ * The host learns the verdict only if it asks: copy the 16 bytes back and
+ * pass them to hp_validate_verdict.
+ *
+ * workspace  DEVICE, 8-byte aligned, at least 256 bytes (hp_workspace_bytes
+ *            of the moves covers it); the words stay there until the next
+ *            validation on that workspace. Moves read the head only when
+ *            gated. A gated move with no validation before it on its
+ *            workspace reads whatever the head holds.
+ * seq_start  as in hp_validate (NULL: all starts 0; pass a scatter's starts
+ *            to check its windows).
+ * Returns HP_OK once enqueued, a host-side argument error, or HP_ERR_HIP. */
+hp_status hp_validate_async(const hp_desc *desc, const void *seq_start, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* Decodes the 16 verdict bytes of hp_validate_async (`words`, HOST memory,
+ * e.g. copied back from the workspace head) into *result, exactly as
+ * hp_validate reports it, for the descriptor's total_tokens. Returns
+ * result->code; HP_ERR_NULL if a pointer is NULL. Host only. */
+hp_status hp_validate_verdict(const hp_desc *desc, const void *words,
+                              hp_validate_result *result);
+
 /* Gather ([Hurray] Element Lookup, Logical Shape): writes the logical tensor
  *   out[(sum_{s'<s} seq_lens[s']) + t][h][d] = page_pool[flat(s, t, h, d)]
  * for every s < S, t < seq_lens[s], as a bit copy. `out` is a device buffer
  * of T*H*D elements of desc->dtype, element aligned, not overlapping
  * page_pool. No slot at or past a sequence's token count is read ([Hurray]
  * Partial trailing page). Slices may alias pages. Asynchronous.
- * Flags: HP_FLAG_CHECKED, HP_FLAG_STREAM. */
+ * Flags: HP_FLAG_CHECKED or HP_FLAG_GATED, HP_FLAG_STREAM. */
 hp_status hp_gather(const hp_desc *desc, void *out, void *workspace,
                     size_t workspace_bytes, uint32_t flags, void *stream);
 
@@ -178,7 +221,8 @@ hp_status hp_gather(const hp_desc *desc, void *out, void *workspace,
  * Partial trailing page). Destinations of different rows must be distinct
  * slots (aliased pages must be copied before they are written); otherwise
  * the result is undefined. Asynchronous.
- * Flags: HP_FLAG_CHECKED (validates with seq_start), HP_FLAG_ZERO_TAIL. */
+ * Flags: HP_FLAG_CHECKED (validates with seq_start) or HP_FLAG_GATED,
+ * HP_FLAG_ZERO_TAIL. */
 hp_status hp_scatter(const hp_desc *desc, const void *src, const void *seq_start,
                      void *workspace, size_t workspace_bytes, uint32_t flags,
                      void *stream);
@@ -188,7 +232,7 @@ hp_status hp_scatter(const hp_desc *desc, const void *src, const void *seq_start
  *   out[row][h][d] = bf16_rne( fp32(q) * scales[phys_page*P + t % P] )
  * one IEEE binary32 multiply, then round to nearest even into bfloat16; rows
  * as in hp_gather. out_dtype must be HP_DTYPE_BF16; `out` holds T*H*D bf16
- * values, 2-byte aligned. Asynchronous. Flags: HP_FLAG_CHECKED. */
+ * values, 2-byte aligned. Asynchronous. Flags: HP_FLAG_CHECKED or HP_FLAG_GATED. */
 hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype,
                             void *workspace, size_t workspace_bytes, uint32_t flags,
                             void *stream);
@@ -216,7 +260,7 @@ hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype,
  * src         DEVICE [total_tokens, num_heads, head_dim] of src_dtype
  *             (HP_DTYPE_F16, HP_DTYPE_BF16 or HP_DTYPE_F32), element aligned.
  * zero_points DEVICE uint8 [num_pages * page_size], 64-byte aligned (uint8 pools).
- * seq_start, workspace, flags (HP_FLAG_CHECKED, HP_FLAG_ZERO_TAIL: tail slots
+ * seq_start, workspace, flags (HP_FLAG_CHECKED or HP_FLAG_GATED, HP_FLAG_ZERO_TAIL: tail slots
  * get zero codes, scale 0 and zero point 0) and errors as hp_scatter. */
 hp_status hp_scatter_quant(const hp_desc *desc, const void *src, uint32_t src_dtype,
                            void *zero_points, const void *seq_start, void *workspace,

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
                           "hp_gather_batch", "hp_scatter_batch", "hp_gather_dequant_batch",
                           "hp_copy_pages", "hp_copy_pages_batch", "hp_gather_dequant_q",
                           "hp_paged_attention", "hp_attention_workspace_bytes",
-                          "hp_scatter_quant"}
+                          "hp_scatter_quant", "hp_validate_async", "hp_validate_verdict"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -109,7 +109,7 @@ def test_call_buffer_rejections():
     assert gather(d, out=None) == S["HP_ERR_NULL"]
     assert gather(d, out=OUT + 1) == S["HP_ERR_ALIGN"]
     assert gather(d, out=ALIGNED + 64) == S["HP_ERR_ARG"]            # overlaps the pool
-    assert gather(d, flags=8) == S["HP_ERR_ARG"]                     # unknown flag
+    assert gather(d, flags=16) == S["HP_ERR_ARG"]                    # unknown flag
     assert L.hp_scatter(ctypes.byref(d), OUT, None, None, 0, hp.HP_FLAG_STREAM, None) == \
         S["HP_ERR_ARG"]                                              # gather-only hint
     assert gather(d, flags=hp.HP_FLAG_ZERO_TAIL) == S["HP_ERR_ARG"]  # scatter-only flag
@@ -119,7 +119,7 @@ def test_call_buffer_rejections():
     sc = ctypes.byref(d)
     assert L.hp_scatter(sc, None, None, None, 0, 0, None) == S["HP_ERR_NULL"]
     assert L.hp_scatter(sc, OUT, ALIGNED + 0x400002, None, 0, 0, None) == S["HP_ERR_ALIGN"]
-    assert L.hp_scatter(sc, OUT, None, None, 0, 8, None) == S["HP_ERR_ARG"]
+    assert L.hp_scatter(sc, OUT, None, None, 0, 16, None) == S["HP_ERR_ARG"]
     res = hp.HpValidateResult()
     assert L.hp_validate(sc, None, None, 0, ctypes.byref(res), None) == S["HP_ERR_WORKSPACE"]
     assert L.hp_validate(sc, None, OUT, 16, ctypes.byref(res), None) == S["HP_ERR_WORKSPACE"]
@@ -321,7 +321,7 @@ def test_batch_rejections():
     assert g(2, _arr(P1, P2), _arr(O1, O2 + 1)) == S["HP_ERR_ALIGN"]
     assert g(2, _arr(P1, P2), _arr(O1, O1 + 64)) == S["HP_ERR_ARG"]     # outputs overlap
     assert g(2, _arr(P1, P2), _arr(O1, P2 + 256)) == S["HP_ERR_ARG"]    # output inside a pool
-    assert g(2, _arr(P1, P2), _arr(O1, O2), flags=8) == S["HP_ERR_ARG"]
+    assert g(2, _arr(P1, P2), _arr(O1, O2), flags=16) == S["HP_ERR_ARG"]
     assert g(2, _arr(P1, P2), _arr(O1, O2), flags=hp.HP_FLAG_CHECKED) == S["HP_ERR_WORKSPACE"]
     bad = desc(rank=2)
     assert L.hp_gather_batch(ctypes.byref(bad), 2, _arr(P1, P2), _arr(O1, O2), None, 0, 0,
@@ -394,3 +394,49 @@ def test_descriptor_handle_keeps_tensors_alive():
     del handle
     gc.collect()
     assert alive() is None
+
+
+def test_gated_and_async_validation_rejections():
+    """The gated form needs the workspace that holds the verdict, and is not
+    combined with the synchronous check; hp_validate_async checks the
+    descriptor on the host like hp_validate."""
+    d = desc()
+    G, C = hp.HP_FLAG_GATED, hp.HP_FLAG_CHECKED
+    assert gather(d, flags=G) == S["HP_ERR_WORKSPACE"]
+    assert gather(d, ws=OUT + 0x100000, n=255, flags=G) == S["HP_ERR_WORKSPACE"]
+    assert gather(d, ws=OUT + 0x100004, n=4096, flags=G) == S["HP_ERR_ALIGN"]
+    assert gather(d, ws=OUT + 0x100000, n=4096, flags=G | C) == S["HP_ERR_ARG"]
+    assert L.hp_scatter(ctypes.byref(d), OUT, None, None, 0, G, None) == S["HP_ERR_WORKSPACE"]
+    q = desc(dtype=hp.DTYPE["i8"], scales=ALIGNED + 0x500000)
+    assert L.hp_gather_dequant(ctypes.byref(q), OUT, hp.DTYPE["bf16"], None, 0, G, None) == \
+        S["HP_ERR_WORKSPACE"]
+    va = L.hp_validate_async
+    assert va(None, None, OUT, 4096, None) == S["HP_ERR_NULL"]
+    assert va(ctypes.byref(desc(rank=2)), None, OUT, 4096, None) == S["HP_ERR_RANK"]
+    assert va(ctypes.byref(d), None, None, 0, None) == S["HP_ERR_WORKSPACE"]
+    assert va(ctypes.byref(d), None, OUT, 255, None) == S["HP_ERR_WORKSPACE"]
+    assert va(ctypes.byref(d), ALIGNED + 0x400002, OUT, 4096, None) == S["HP_ERR_ALIGN"]
+    # attention and page copies are not gated
+    assert L.hp_copy_pages(ctypes.byref(d), ALIGNED, ALIGNED, 1, OUT, 4096, G, None) == \
+        S["HP_ERR_ARG"]
+
+
+def test_validate_verdict_decoding():
+    """hp_validate_verdict reads the two words the device check leaves: the
+    smallest failing (check, index) key and the token sum."""
+    d = desc()  # total_tokens = 114
+    res = hp.HpValidateResult()
+
+    def verdict(key, total):
+        words = (ctypes.c_uint64 * 2)(key, total)
+        return L.hp_validate_verdict(ctypes.byref(d), words, ctypes.byref(res)), res.index
+
+    ones = (1 << 64) - 1
+    assert verdict(ones, 114) == (S["HP_OK"], 0)
+    assert verdict(ones, 113) == (S["HP_ERR_TOTAL_TOKENS"], 0)
+    assert verdict((1 << 56) | 0, 114) == (S["HP_ERR_SEQPTR_FIRST"], 0)
+    assert verdict((2 << 56) | 3, 114) == (S["HP_ERR_SEQPTR_LAST"], 3)
+    assert verdict((3 << 56) | 7, 114) == (S["HP_ERR_SEQPTR_ORDER"], 7)
+    assert verdict((4 << 56) | 9, 0) == (S["HP_ERR_PAGE_RANGE"], 9)
+    assert verdict((5 << 56) | 2, 114) == (S["HP_ERR_SEQ_LEN"], 2)
+    assert L.hp_validate_verdict(ctypes.byref(d), None, ctypes.byref(res)) == S["HP_ERR_NULL"]
