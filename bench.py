@@ -5,15 +5,17 @@ One step is one pass of every stage of the path over one batch of the decode
 workload (64 sequences, lengths uniform in 1..2048, page_size 16, 32 heads x
 128 fp16, 12,000-page pool, uint32 block table of unique pages):
 
-  1. hp_validate        storage invariants of the descriptor (synchronous, on a
-                        second stream: the next step's descriptor is checked
-                        while this step's moves run, and the next moves are
-                        enqueued only after that check returned HP_OK);
+  1. hp_validate_async  storage invariants of the descriptor, enqueued on the
+                        moves' stream; its verdict stays on the device;
   2. hp_gather          pool -> logical [T, 32, 128] fp16 tensor (streaming hint:
                         the table names each page once);
   3. hp_scatter         that tensor back into its slots (the write direction);
   4. hp_gather_dequant  the same table over an int8 copy of the pool with one
                         fp32 scale per slot -> bf16 [T, 32, 128].
+
+The moves are gated (HP_FLAG_GATED): each reads its step's verdict on the
+device and would write nothing for a rejected descriptor, so no host round
+trip sits between steps.
 
 Inputs are resident in HBM before timing starts. `value` is the step's
 algorithmic bytes (each live row read once and written once per move, one
@@ -22,15 +24,22 @@ scale per row, the validator's metadata reads) over the wall-clock step time
 
 Per-kernel launch durations come from HIP events on the launch stream around
 back-to-back launches of each kernel (the GPU stays busy, so the interval is
-kernel time); `roofline` uses the gather kernel's. The per-stage times inside
-the step (`ops[*].in_step_ms`) are event intervals on the moves' stream, and
-the host's wall time of each hp_validate call, taken in a separate run of 20
-steps after the timed ones (events between the moves would slow the timed
-steps). The CPU oracle is timed on the host on a
-bounded prefix of the same batch (single-threaded, as it stands).
+kernel time); `roofline` uses the gather kernel's, and adds the rocprofv3
+averages of the committed kernel trace when it was taken on the current
+kernel sources.
+
+`configs` times every workload's moves on its own: tiny (gather + scatter),
+decode (gather, scatter, dequant), prefix sharing (gather; unique and
+logical bytes), append (scatter with tail zeroing) and the quantized large
+pool (dequant, raw gather). Before each of `--flush-iters` iterations a
+1 GiB buffer is read through to evict the caches; HIP events bracket the call;
+median, p10 and p90 are reported. The CPU oracle is timed on the host on the
+same work: one thread on a bounded prefix of the sequences, and every
+sequence split into balanced ranges over one thread per core.
 
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                  [--no-configs] [--extras]
   python bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR
       (writes the rocprofv3 summaries under profiles/)
 """
@@ -68,11 +77,13 @@ KERNEL_LABELS = {
     "validate_init_kernel": "validator init",
 }
 CALIBRATION_BYTES = 1 << 30
+TRACE_STEPS, TRACE_WARMUP = 50, 5
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o trace -- "
-             "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-reference-copies")
+             f"python3 bench.py --steps {TRACE_STEPS} --warmup {TRACE_WARMUP} --no-cpu-baseline "
+             "--no-reference-copies --no-configs")
 PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/prof_{d} -o {d} -- "
            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-reference-copies "
-           "--copy-calibration")
+           "--no-configs --copy-calibration")
 ATTN_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_attn_trace -o trace "
                   "-- python3 bench.py --attention-only")
 ATTN_PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/prof_attn_{d} -o {d} -- "
@@ -114,42 +125,109 @@ def traffic_for():
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, pool_h, qpool_h, scales_h, seconds):
-    """The oracle, single-threaded, on the longest prefix of sequences that fits
-    the time budget; returns GB/s of the same algorithmic bytes."""
-    import numpy as np
-    import oracle
-    lens = w.seq_lens.astype(np.int64)
-    kw = dict(page_size=w.page_size, num_heads=w.num_heads, head_dim=w.head_dim)
+# ---- CPU oracle legs ---------------------------------------------------------------
 
-    def run(n):
-        sp = w.seq_ptr[: n + 1]
-        bt = w.block_table[: int(sp[-1])]
-        sl = w.seq_lens[:n]
-        T = int(lens[:n].sum())
+def cpu_info():
+    """(cores this process may run on, CPU model name)."""
+    cores = len(os.sched_getaffinity(0))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
+def cpu_threads():
+    """Threads of the all-core leg: every core of the affinity mask, within
+    the OMP_NUM_THREADS share when the machine sets one."""
+    cores, _ = cpu_info()
+    lim = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(cores, int(lim))) if lim.isdigit() and int(lim) > 0 else cores
+
+
+def seq_ranges(lens, n):
+    """Split sequences into at most n contiguous ranges of about equal tokens."""
+    import numpy as np
+    lens = np.asarray(lens, dtype=np.int64)
+    S = len(lens)
+    if S == 0:
+        return []
+    cum = np.cumsum(lens)
+    cuts = {0, S}
+    for i in range(1, n):
+        cuts.add(min(S, int(np.searchsorted(cum, cum[-1] * i / n, side="left")) + 1))
+    cuts = sorted(cuts)
+    return [(a, b) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+
+
+def sub_desc(w, s0, s1):
+    """Oracle arguments for sequences [s0, s1) alone: their slice of the table,
+    seq_ptr rebased to 0, their counts (and starts)."""
+    import numpy as np
+    sp = w.seq_ptr.astype(np.int64)
+    kw = dict(page_size=w.page_size, num_heads=w.num_heads, head_dim=w.head_dim,
+              block_table=w.block_table[sp[s0]: sp[s1]],
+              seq_ptr=(sp[s0: s1 + 1] - sp[s0]).astype(np.uint64),
+              seq_lens=w.seq_lens[s0:s1])
+    if w.seq_start is not None:
+        kw["seq_start"] = w.seq_start[s0:s1]
+    return kw
+
+
+def cpu_legs(w, run, nbytes, seconds):
+    """Times the oracle, as it stands, on the host: `run(s0, s1)` does the
+    work of sequences [s0, s1) (plain oracle calls on that range alone);
+    `nbytes(s0, s1)` gives its algorithmic bytes.
+
+    single_thread: one thread on the longest prefix of sequences that fits
+    about `seconds`; all_cores: every sequence, split into balanced ranges
+    run concurrently by one thread per core (the oracle's C loops release
+    the interpreter lock)."""
+    import concurrent.futures
+    import numpy as np
+    lens = w.seq_lens.astype(np.int64)
+    S = len(lens)
+
+    def timed(s1):
         t0 = time.perf_counter()
-        oracle.validate(rank=3, paged_axis=0, num_pages=w.num_pages, page_size=w.page_size,
-                        block_table=bt, seq_ptr=sp, seq_lens=sl, total_tokens=T)
-        out = oracle.gather(pool_h, block_table=bt, seq_ptr=sp, seq_lens=sl, **kw)
-        oracle.scatter(pool_h, out, block_table=bt, seq_ptr=sp, seq_lens=sl, in_place=True,
-                       **kw)
-        oracle.gather_dequant(qpool_h, scales_h, block_table=bt, seq_ptr=sp, seq_lens=sl, **kw)
-        return time.perf_counter() - t0, T, n, len(bt)
+        run(0, s1)
+        return time.perf_counter() - t0
 
     n = 1
-    dt, T, n, K = run(n)
-    while dt < seconds / 8 and n < w.num_seqs:
-        n = min(w.num_seqs, n * 4)
-        dt, T, n, K = run(n)
-    if dt < seconds / 2 and n < w.num_seqs:
-        target_T = T * seconds / dt
-        n = max(1, min(int(np.searchsorted(np.cumsum(lens), target_T)) + 1, w.num_seqs))
-        dt, T, n, K = run(n)
-    b = sum(step_bytes(T, n, K, w.num_heads, w.head_dim).values())
-    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 2), "tokens_per_s": round(T / dt, 1),
-            "sample": f"first {n} of {w.num_seqs} sequences ({T} of {w.total_tokens} tokens), "
-                      "one step: validate + gather + scatter + dequant-gather, single thread"}
+    dt = timed(n)
+    while dt < seconds / 8 and n < S:
+        n = min(S, n * 4)
+        dt = timed(n)
+    if dt < seconds / 2 and n < S:
+        T = int(lens[:n].sum())
+        target = T * seconds / 2 / max(dt, 1e-9)
+        n = max(1, min(int(np.searchsorted(np.cumsum(lens), target)) + 1, S))
+        dt = timed(n)
+    T1 = int(lens[:n].sum())
+    b1 = nbytes(0, n)
+    threads = cpu_threads()
+    ranges = seq_ranges(lens, threads)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(ranges)) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda r: run(*r), ranges))
+        dt_all = time.perf_counter() - t0
+    b_all = nbytes(0, S)
+    T = int(lens.sum())
+    cores, model = cpu_info()
+    return {
+        "single_thread": {"value": round(b1 / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                          "seconds": round(dt, 3), "tokens_per_s": round(T1 / dt, 1),
+                          "sample": f"first {n} of {S} sequences ({T1} of {T} tokens)"},
+        "all_cores": {"value": round(b_all / dt_all / 1e9, 4), "unit": "GB/s",
+                      "cores": len(ranges), "seconds": round(dt_all, 3),
+                      "tokens_per_s": round(T / dt_all, 1),
+                      "sample": f"all {S} sequences in {len(ranges)} ranges, one thread each"},
+        "affinity_cores": cores, "cpu_model": model}
 
 
 # ---- rocprofv3 summaries --------------------------------------------------------
@@ -174,30 +252,44 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir):
         with open(files[0]) as f:
             return list(csv.DictReader(f))
 
-    stats = one(trace_dir, "*kernel_stats.csv")
+    trace = one(trace_dir, "*kernel_trace.csv")
+    launches = {}
+    for r in trace:
+        short = _short(r["Kernel_Name"])
+        if short in KERNEL_LABELS:
+            launches.setdefault(short, []).append(
+                (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) -
+                                             int(r["Start_Timestamp"])) / 1e3))
+    n_step = TRACE_STEPS + TRACE_WARMUP
     lines = ["# Kernel durations: decode-batch bench step (rocprofv3 kernel trace)", "",
              "Command (from the repository root, on one MI355X):", "",
              f"    {TRACE_CMD}", "",
-             "All launches of the run (50 timed + 5 warm-up steps, plus the back-to-back",
-             "kernel-timing launches of each move). Durations in microseconds.", "",
-             "| kernel | what | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
-    gather_avg = None
-    for r in stats:
-        short = _short(r["Name"])
-        if short not in KERNEL_LABELS:
-            continue
-        avg = float(r["AverageNs"]) / 1e3
-        if short == GATHER_KERNEL:
-            gather_avg = avg
-        lines.append(f"| `{short}` | {KERNEL_LABELS[short]} | {r['Calls']} | {avg:.1f} | "
-                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
-    lines += ["", "The validator runs on a second stream beside the moves (the next step's",
-              "check), so its durations include time it shares the GPU with them; alone it",
-              "takes the minimum shown.",
+             f"Each move runs once per step ({TRACE_WARMUP} warm-up + {TRACE_STEPS} timed "
+             "steps), then 21 times back to back",
+             "for the event timing. `step` averages the first kind, `back-to-back` the second.",
+             "Durations in microseconds.", "",
+             "| kernel | what | calls | avg | min | max | step avg | back-to-back avg |",
+             "|---|---|---|---|---|---|---|---|"]
+    gather = None
+    for short in sorted(launches, key=lambda k: KERNEL_LABELS[k]):
+        ts = [d for _, d in sorted(launches[short])]
+        avg = sum(ts) / len(ts)
+        step = b2b = ""
+        if not short.startswith("validate") and len(ts) > n_step:
+            st, bb = ts[:n_step], ts[n_step:]
+            step, b2b = f"{sum(st) / len(st):.1f}", f"{sum(bb) / len(bb):.1f}"
+            if short == GATHER_KERNEL:
+                gather = (avg, sum(st) / len(st), sum(bb) / len(bb))
+        lines.append(f"| `{short}` | {KERNEL_LABELS[short]} | {len(ts)} | {avg:.1f} | "
+                     f"{min(ts):.1f} | {max(ts):.1f} | {step} | {b2b} |")
+    lines += ["", "The validator (`hp_validate_async`) runs in line before each step's moves.",
               "", "Other kernels in the trace are PyTorch's input generation (random values,",
               "fills, index_put) and the runtime's copies; they are outside the timed step."]
     with open(os.path.join(PROFILES, "decode_step_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
+    if gather is None:
+        raise SystemExit("gather kernel not found in the kernel trace")
+    gather_avg = gather[0]
 
     def per_kernel(rows, counter):
         agg = {}
@@ -267,6 +359,10 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir):
                     "fetch_factor": f_factor, "write_factor": w_factor,
                     "calibration_bytes": CALIBRATION_BYTES,
                     "rocprof_avg_launch_us": gather_avg,
+                    "rocprof_avg_step_us": gather[1],
+                    "rocprof_avg_back_to_back_us": gather[2],
+                    "algorithmic_bytes_per_launch": 1041039360,
+                    "trace_command": TRACE_CMD,
                     "commands": [PMC_CMD.format(c="FETCH_SIZE", d="fetch"),
                                  PMC_CMD.format(c="WRITE_SIZE", d="write")]})
     with open(TRAFFIC_FILE, "w") as f:
@@ -372,12 +468,14 @@ def summarize_attention(trace_dir, fetch_dir, write_dir):
     print("\n".join(lines + [""] + out))
 
 
-def quant_write_extras(hp, torch, np, dev, stream, reps):
+def quant_write_extras(hp, torch, np, dev, stream, reps, rounds=6):
     """Quantize-on-scatter on the decode batch: its fp16 rows (63,540 tokens,
     32 heads x 128) written into an int8 pool (symmetric, a scale per slot)
     and a uint8 pool (a scale and a zero point per slot). Algorithmic bytes:
     every row read (2 bytes a value) and its codes written (1 byte a value),
-    plus 4 bytes of scale (and 1 of zero point) per token."""
+    plus 4 bytes of scale (and 1 of zero point) per token. The two forms are
+    timed in alternating order over `rounds` rounds of `reps` back-to-back
+    calls each (neither always runs second); the median round is reported."""
     import workloads
     w = workloads.decode()
     T, H, D = w.total_tokens, w.num_heads, w.head_dim
@@ -393,25 +491,34 @@ def quant_write_extras(hp, torch, np, dev, stream, reps):
     zp = torch.zeros(w.num_pages * w.page_size, dtype=torch.uint8, device=dev)
     ws = torch.empty(max(hp.workspace_bytes(hp.Descriptor(pool, bt, sp, sl), T), 256),
                      dtype=torch.uint8, device=dev)
-    res = {}
+    forms = {}
     for name, pool_t, z in (("int8_symmetric", pool, None),
                             ("uint8_zero_points", pool.view(torch.uint8), zp)):
         qd = hp.Descriptor(pool_t, bt, sp, sl, scales=sc)
+        forms[name] = (qd, z, T * H * D * 3 + 4 * T + (T if z is not None else 0))
+    times = {name: [] for name in forms}
+    for r in range(rounds):
+        order = list(forms) if r % 2 == 0 else list(forms)[::-1]
+        for name in order:
+            qd, z, _ = forms[name]
 
-        def call():
-            hp.scatter_quant(qd, src, zero_points=z, workspace=ws, stream=stream)
+            def call():
+                hp.scatter_quant(qd, src, zero_points=z, workspace=ws, stream=stream)
 
-        call()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
             call()
-        b.record(stream)
-        b.synchronize()
-        ms = a.elapsed_time(b) / reps
-        nbytes = T * H * D * 3 + 4 * T + (T if z is not None else 0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                call()
+            b.record(stream)
+            b.synchronize()
+            times[name].append(a.elapsed_time(b) / reps)
+    res = {}
+    for name, (_, _, nbytes) in forms.items():
+        ms = float(np.median(times[name]))
         res[name] = {"algorithmic_bytes": nbytes, "launch_us": round(ms * 1e3, 1),
-                     "gb_per_s": round(nbytes / (ms / 1e3) / 1e9, 1)}
+                     "gb_per_s": round(nbytes / (ms / 1e3) / 1e9, 1),
+                     "rounds_us": [round(t * 1e3, 1) for t in times[name]]}
     del pool, src
     return res
 
@@ -629,19 +736,378 @@ def calibration_copies(torch, dev):
     del a, b
 
 
+def rocprof_gather():
+    """The gather kernel's rocprof averages from the committed summary, when it
+    was taken on the current kernel sources: over every launch of the
+    profiled run, over its step launches, and over its back-to-back
+    launches (the ones the event timing uses)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    algo = t.get("algorithmic_bytes_per_launch", 1041039360)
+    out = {}
+    for key, name in (("rocprof_avg_launch_us", "all"), ("rocprof_avg_step_us", "step"),
+                      ("rocprof_avg_back_to_back_us", "back_to_back")):
+        us = t.get(key)
+        if us:
+            gbs = algo / (us * 1e-6) / 1e9
+            out[f"rocprof_{name}_avg_ms"] = round(us / 1e3, 4)
+            out[f"rocprof_{name}_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+    if out:
+        out["rocprof_from"] = os.path.relpath(TRAFFIC_FILE, ROOT)
+    return out
+
+
+def side_paths(hp, torch, np, dev, stream, args, w, wq, desc, qdesc, pool):
+    """The side paths on the decode batch's pools: copy-on-write page copy,
+    dequant under each quantization scheme, quantize-on-scatter, decode
+    attention, and the batched KV append."""
+    T, H, D = w.total_tokens, w.num_heads, w.head_dim
+
+    def idx(a):
+        return idx_on(torch, np, np.asarray(a).astype(np.uint32), dev)
+
+    def back_to_back(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        a.record(stream)
+        for _ in range(args.kernel_reps):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / args.kernel_reps
+
+    # copy-on-write page copy: 1,024 referenced pages of the decode pool
+    # (128 KiB each) into pages no sequence references
+    free_pages = np.setdiff1d(np.arange(w.num_pages), w.block_table.astype(np.int64))
+    rng = np.random.default_rng(6)
+    n_copy = 1024
+    src_p = idx(rng.choice(w.block_table.astype(np.int64), n_copy, replace=False))
+    dst_p = idx(rng.choice(free_pages, n_copy, replace=False))
+    t_copy = back_to_back(lambda: hp.copy_pages(desc, src_p, dst_p, stream=stream))
+    copy_bytes = 2 * n_copy * 16 * H * D * 2
+    # dequant-gather of the int8 pool under each quantization scheme, with
+    # zero points (the general kernel); per-slot is the step's
+    qout = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    zrng = np.random.default_rng(8)
+    schemes = {}
+    for name, scheme, axis, n_par, per_tok in (
+            ("per_tensor_zp", "per_tensor", 0, 1, 0),
+            ("per_channel_head_zp", "per_channel", 1, H, 0),
+            ("per_channel_head_dim_zp", "per_channel", 2, D, 0),
+            ("per_block_affine_zp", "per_block_affine", 0, wq.num_pages * 16, 5)):
+        sc = torch.from_numpy(zrng.uniform(1e-3, 1e-1, n_par).astype(np.float32)).to(dev)
+        zp = torch.from_numpy(zrng.integers(-128, 128, n_par).astype(np.int8)).to(dev)
+        t_q = back_to_back(lambda: hp.gather_dequant_q(qdesc, qout, scheme, sc, axis=axis,
+                                                       zero_points=zp, stream=stream))
+        qb = T * H * D * 3 + per_tok * T
+        schemes[name] = {"algorithmic_bytes": qb, "launch_us": round(t_q * 1e3, 1),
+                         "gb_per_s": round(qb / (t_q / 1e3) / 1e9, 1)}
+    del qout
+    return {
+        "quantize_on_scatter": quant_write_extras(hp, torch, np, dev, stream,
+                                                  args.kernel_reps),
+        "attention": attention_extras(hp, torch, np, dev, stream, args.kernel_reps, gqa8=True),
+        "dequant_schemes": schemes,
+        "batched_append": batched_append(hp, torch, np, dev, stream, args.kernel_reps),
+        "copy_pages": {"workload": "1,024 pages of the decode pool (16 x 32 x 128 fp16 = "
+                                   "128 KiB each) copied to unreferenced pages",
+                       "algorithmic_bytes": copy_bytes, "launch_us": round(t_copy * 1e3, 1),
+                       "gb_per_s": round(copy_bytes / (t_copy / 1e3) / 1e9, 1)}}
+
+
+FLUSH_BYTES = 1 << 30  # read between flushed iterations: evicts L2 and the MALL
+
+
+def idx_on(torch, np, a, dev):
+    """An index array (uint32 / uint64) as a device tensor of the same width."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32).copy()).to(dev)
+    return torch.from_numpy(a.astype(np.uint64).view(np.int64).copy()).to(dev)
+
+
+class OnGpu:
+    """A workload's descriptor tensors (pool, table, offsets, counts, starts,
+    optional scales) on the GPU, and the binding's descriptor over them."""
+
+    def __init__(self, hp, torch, np, w, dev, pool=None, scales=False):
+        self.pool = w.make_pool(dev) if pool is None else pool
+        self.bt = idx_on(torch, np, w.block_table.astype(w.index_dtype), dev)
+        self.sp = idx_on(torch, np, w.seq_ptr.astype(w.index_dtype), dev)
+        self.sl = idx_on(torch, np, w.seq_lens.astype(w.index_dtype), dev)
+        self.ss = (idx_on(torch, np, w.seq_start.astype(w.index_dtype), dev)
+                   if w.seq_start is not None else None)
+        self.scales = w.make_scales(dev) if scales else None
+        self.desc = hp.Descriptor(self.pool, self.bt, self.sp, self.sl, scales=self.scales)
+
+
+def flushed_times(torch, np, stream, call, iters, flush):
+    """Durations (us) of `call` over `iters` iterations; before each, the
+    1 GiB buffer `flush` is read through (a sum), then HIP events on the
+    call's stream bracket the call alone. A read leaves the L2s and the
+    Infinity Cache holding clean flush lines: the previous call's dirty
+    lines are written back during the flush, not during the timed call (a
+    write flush would leave up to 256 MB of dirty lines for the call to
+    write back)."""
+    call()
+    torch.cuda.synchronize()
+    words = flush.view(torch.int64)
+    pairs = []
+    for _ in range(iters):
+        words.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+
+
+def move_summary(np, nbytes, tokens, us, **extra_bytes):
+    """Median / p10 / p90 of flushed durations, with GB/s and tokens/s at the
+    median. extra_bytes: other byte counts of the same move (reported as GB/s
+    at the median under their own names)."""
+    med = float(np.median(us))
+    p10, p90 = (float(x) for x in np.percentile(us, [10, 90]))
+    gbs = nbytes / (med * 1e-6) / 1e9
+    r = {"algorithmic_bytes": int(nbytes), "iterations": len(us), "median_us": round(med, 2),
+         "p10_us": round(p10, 2), "p90_us": round(p90, 2), "gb_per_s": round(gbs, 1),
+         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+         "tokens_per_s": round(tokens / (med * 1e-6), 1)}
+    for name, b in extra_bytes.items():
+        r[name] = {"bytes": int(b), "gb_per_s": round(b / (med * 1e-6) / 1e9, 1)}
+    return r
+
+
+def token_slots(w, s0=0, s1=None):
+    """Flat pool slot (phys * P + t mod P) of every token of sequences [s0, s1)."""
+    import numpy as np
+    s1 = w.num_seqs if s1 is None else s1
+    lens = w.seq_lens[s0:s1].astype(np.int64)
+    if lens.sum() == 0:
+        return np.zeros(0, np.int64)
+    seq = np.repeat(np.arange(s0, s1), lens)
+    first = np.repeat(np.concatenate([[0], np.cumsum(lens)[:-1]]), lens)
+    t = np.arange(int(lens.sum())) - first
+    start = (w.seq_start[s0:s1].astype(np.int64) if w.seq_start is not None
+             else np.zeros(s1 - s0, np.int64))
+    t = t + np.repeat(start, lens)
+    phys = w.block_table[w.seq_ptr.astype(np.int64)[seq] + t // w.page_size].astype(np.int64)
+    return phys * w.page_size + t % w.page_size
+
+
+def tail_rows(w, s0=0, s1=None):
+    """Slots a tail-zeroing scatter clears: past each written sequence's last
+    new token, to the end of that page."""
+    import numpy as np
+    s1 = w.num_seqs if s1 is None else s1
+    lens = w.seq_lens[s0:s1].astype(np.int64)
+    start = (w.seq_start[s0:s1].astype(np.int64) if w.seq_start is not None
+             else np.zeros(s1 - s0, np.int64))
+    r = (start + lens) % w.page_size
+    return int(np.where((lens > 0) & (r != 0), w.page_size - r, 0).sum())
+
+
+def measure_configs(hp, torch, np, dev, iters, cpu_seconds, with_cpu):
+    """Each workload and the moves it names, timed with a 1 GiB flush between
+    iterations (median, p10, p90), and the oracle timed on the host on the
+    same work (single thread on a bounded prefix; all cores on everything)."""
+    import oracle
+    import workloads
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    L = hp.lib()
+    flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    res = {}
+
+    def ok(code, what):
+        if code != 0:
+            raise SystemExit(f"{what}: {hp.status_str(code)}")
+
+    def host(t):
+        eb = t.element_size()
+        return (t.contiguous().view(workloads.bits_dtype(eb)).cpu().numpy()
+                .view(workloads.np_bits_dtype(eb)))
+
+    def free():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    # -- tiny: gather to [114, 4, 8], scatter back into a blank pool
+    w = workloads.tiny()
+    g = OnGpu(hp, torch, np, w, dev)
+    T, R = w.total_tokens, w.row_bytes
+    out = torch.empty((T, w.num_heads, w.head_dim), dtype=g.pool.dtype, device=dev)
+    g2 = OnGpu(hp, torch, np, w, dev, pool=torch.zeros_like(g.pool))
+    pd, pb, o_p = g.desc.with_tokens(T), g2.desc.with_tokens(T), out.data_ptr()
+    e = {"workload": "tiny: 3 sequences of 40, 24, 50 tokens, page_size 16, 20-page pool, "
+                     "4 heads x 8 fp16; gather to [114, 4, 8] and scatter it back",
+         "tokens": T, "sequences": w.num_seqs,
+         "gather": move_summary(np, 2 * T * R, T, flushed_times(
+             torch, np, stream, lambda: ok(L.hp_gather(pd, o_p, None, 0, 0, sh), "gather"),
+             iters, flush)),
+         "scatter": move_summary(np, 2 * T * R, T, flushed_times(
+             torch, np, stream, lambda: ok(L.hp_scatter(pb, o_p, None, None, 0, 0, sh),
+                                           "scatter"), iters, flush))}
+    if with_cpu:
+        ph = host(g.pool)
+
+        def run(s0, s1):
+            kw = sub_desc(w, s0, s1)
+            o = oracle.gather(ph, **kw)
+            oracle.scatter(np.zeros_like(ph), o, **kw)
+        e["cpu_oracle"] = cpu_legs(w, run, lambda s0, s1: 4 * int(
+            w.seq_lens[s0:s1].astype(np.int64).sum()) * R, cpu_seconds)
+    res["tiny"] = e
+    del g, g2, out
+    free()
+
+    # -- decode: gather (streaming hint), scatter, int8 -> bf16 dequant
+    w = workloads.decode()
+    g = OnGpu(hp, torch, np, w, dev)
+    T, R, HD = w.total_tokens, w.row_bytes, w.num_heads * w.head_dim
+    wq = dataclasses.replace(w, name="decode-int8", dtype="i8", values="int8", with_scales=True)
+    gq = OnGpu(hp, torch, np, wq, dev, scales=True)
+    out = torch.empty((T, w.num_heads, w.head_dim), dtype=torch.float16, device=dev)
+    qout = torch.empty((T, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    pd, pq, o_p, q_p = g.desc.with_tokens(T), gq.desc.with_tokens(T), out.data_ptr(), qout.data_ptr()
+    bf16 = hp.DTYPE["bf16"]
+    res["decode"] = {
+        "workload": "decode batch: 64 sequences, lengths uniform 1..2048, page_size 16, 32 "
+                    "heads x 128 fp16, 12,000-page pool, uint32 table of unique pages; dequant "
+                    "over an int8 copy with one fp32 scale per slot",
+        "tokens": T, "sequences": w.num_seqs,
+        "gather": move_summary(np, 2 * T * R, T, flushed_times(
+            torch, np, stream,
+            lambda: ok(L.hp_gather(pd, o_p, None, 0, hp.HP_FLAG_STREAM, sh), "gather"),
+            iters, flush)),
+        "scatter": move_summary(np, 2 * T * R, T, flushed_times(
+            torch, np, stream, lambda: ok(L.hp_scatter(pd, o_p, None, None, 0, 0, sh),
+                                          "scatter"), iters, flush)),
+        "dequant": move_summary(np, 3 * T * HD + 4 * T, T, flushed_times(
+            torch, np, stream, lambda: ok(L.hp_gather_dequant(pq, q_p, bf16, None, 0, 0, sh),
+                                          "dequant"), iters, flush))}
+    del g, gq, out, qout
+    free()
+
+    # -- prefix: gather of 256 sequences that alias 64 leading pages
+    w = workloads.prefix()
+    g = OnGpu(hp, torch, np, w, dev)
+    T, R = w.total_tokens, w.row_bytes
+    out = torch.empty((T, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    pd, o_p = g.desc.with_tokens(T), out.data_ptr()
+    uniq = len(np.unique(token_slots(w)))
+    us = flushed_times(torch, np, stream,
+                       lambda: ok(L.hp_gather(pd, o_p, None, 0, 0, sh), "gather"), iters, flush)
+    e = {"workload": "prefix sharing: 256 sequences, a 1,024-token prefix on 64 shared pages "
+                     "plus private suffixes of 16..512 tokens, page_size 16, 8 heads x 128 "
+                     "bf16, 40,000-page pool; gather in logical order",
+         "tokens": T, "sequences": w.num_seqs, "unique_rows_read": uniq,
+         "gather": move_summary(np, (uniq + T) * R, T, us, logical=2 * T * R)}
+    e["gather"]["bytes_counted"] = ("unique: each distinct pool row read once plus every "
+                                    "output row written; logical: every row read per use")
+    if with_cpu:
+        ph = host(g.pool)
+        e["cpu_oracle"] = cpu_legs(
+            w, lambda s0, s1: oracle.gather(ph, **sub_desc(w, s0, s1)),
+            lambda s0, s1: (len(np.unique(token_slots(w, s0, s1))) +
+                            int(w.seq_lens[s0:s1].astype(np.int64).sum())) * R, cpu_seconds)
+        del ph
+    res["prefix"] = e
+    del g, out
+    free()
+
+    # -- append: 512 one-token appends + an 8,192-token prefill, tails zeroed
+    w = workloads.append()
+    g = OnGpu(hp, torch, np, w, dev)
+    T, R = w.total_tokens, w.row_bytes
+    src = w.make_src(dev)
+    pd, s_p, ss_p = g.desc.with_tokens(T), src.data_ptr(), g.ss.data_ptr()
+    nt = tail_rows(w)
+    us = flushed_times(torch, np, stream, lambda: ok(L.hp_scatter(
+        pd, s_p, ss_p, None, 0, hp.HP_FLAG_ZERO_TAIL, sh), "scatter"), iters, flush)
+    e = {"workload": "append: 512 decode sequences writing 1 token each into their partial "
+                     "trailing page plus one 8,192-token prefill into fresh pages, page_size "
+                     "16, 8 heads x 128 bf16, 60,000-page pool, unused trailing slots zeroed",
+         "tokens": T, "sequences": w.num_seqs, "tail_rows_zeroed": nt,
+         "scatter": move_summary(np, 2 * T * R + nt * R, T, us)}
+    if with_cpu:
+        ph = host(g.pool)
+        sh_src = host(src)
+        tok = np.concatenate([[0], np.cumsum(w.seq_lens.astype(np.int64))])
+
+        def run(s0, s1):
+            oracle.scatter(ph, sh_src[tok[s0]: tok[s1]], zero_tail=True, in_place=True,
+                           **sub_desc(w, s0, s1))
+        e["cpu_oracle"] = cpu_legs(
+            w, run, lambda s0, s1: (2 * int(w.seq_lens[s0:s1].astype(np.int64).sum())
+                                    + tail_rows(w, s0, s1)) * R, cpu_seconds)
+        del ph, sh_src
+    res["append"] = e
+    del g, src
+    free()
+
+    # -- quant: int8 pool of 200,000 pages, per-slot scales, uint64 table
+    w = workloads.quant()
+    g = OnGpu(hp, torch, np, w, dev, scales=True)
+    T, HD = w.total_tokens, w.num_heads * w.head_dim
+    qout = torch.empty((T, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    pd, q_p = g.desc.with_tokens(T), qout.data_ptr()
+    us = flushed_times(torch, np, stream, lambda: ok(L.hp_gather_dequant(
+        pd, q_p, bf16, None, 0, 0, sh), "dequant"), iters, flush)
+    e = {"workload": "quantized large pool: int8, 200,000 pages x 16 x 8 x 128, one fp32 scale "
+                     "per slot, uint64 table, 1,024 sequences with log-normal lengths capped "
+                     "at 8,192; gather + dequant to bf16",
+         "tokens": T, "sequences": w.num_seqs,
+         "dequant": move_summary(np, 3 * T * HD + 4 * T, T, us)}
+    del qout
+    free()
+    raw = torch.empty((T, w.num_heads, w.head_dim), dtype=torch.int8, device=dev)
+    r_p = raw.data_ptr()
+    e["raw_gather"] = move_summary(np, 2 * T * HD, T, flushed_times(
+        torch, np, stream, lambda: ok(L.hp_gather(pd, r_p, None, 0, hp.HP_FLAG_STREAM, sh),
+                                      "gather"), iters, flush))
+    del raw
+    free()
+    if with_cpu:
+        ph = host(g.pool).view(np.int8)
+        sc = g.scales.cpu().numpy()
+        e["cpu_oracle"] = cpu_legs(
+            w, lambda s0, s1: oracle.gather_dequant(ph, sc, **sub_desc(w, s0, s1)),
+            lambda s0, s1: (3 * HD + 4) * int(w.seq_lens[s0:s1].astype(np.int64).sum()),
+            cpu_seconds)
+        del ph, sc
+    res["quant"] = e
+    del g, flush
+    free()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=4.0,
+                    help="single-thread oracle budget per workload (a bounded prefix)")
     ap.add_argument("--kernel-reps", type=int, default=20,
                     help="back-to-back launches per kernel for the launch durations")
+    ap.add_argument("--flush-iters", type=int, default=50,
+                    help="flushed iterations per move in the per-workload table")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload table (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB device copies (counter calibration runs)")
     ap.add_argument("--extras", action="store_true",
-                    help="also measure the batched calls (decode-step KV append over 64 pools)")
+                    help="also measure the side paths (schemes, attention, batched append, "
+                         "page copy, quantize-on-scatter)")
     ap.add_argument("--no-reference-copies", action="store_true",
                     help="skip the identity-table gather and runtime copy (profiling runs)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"))
@@ -694,162 +1160,141 @@ def main():
     H, D = w.num_heads, w.head_dim
 
     def idx(a):
-        return torch.from_numpy(a.astype(np.uint32).view(np.int32).copy()).to(dev)
+        return idx_on(torch, np, a.astype(np.uint32), dev)
 
-    pool = w.make_pool(dev)
-    bt, sp, sl = idx(w.block_table), idx(w.seq_ptr), idx(w.seq_lens)
-    desc = hp.Descriptor(pool, bt, sp, sl)
+    g = OnGpu(hp, torch, np, w, dev)
+    pool, desc = g.pool, g.desc
     wq = dataclasses.replace(w, name="decode-int8", dtype="i8", values="int8",
                              with_scales=True)
-    qpool = wq.make_pool(dev)
-    scales = wq.make_scales(dev)
-    qdesc = hp.Descriptor(qpool, bt, sp, sl, scales=scales)
+    gq = OnGpu(hp, torch, np, wq, dev, scales=True)
+    qpool, scales, qdesc = gq.pool, gq.scales, gq.desc
     out = torch.empty((T, H, D), dtype=torch.float16, device=dev)
     qout = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(max(hp.workspace_bytes(desc, T), 256), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    if hp.validate(desc, T, workspace=ws) != ("HP_OK", 0):
+    main_s = torch.cuda.current_stream(dev)
+    if hp.validate(desc, T) != ("HP_OK", 0):
         raise SystemExit("bench descriptor failed validation")
 
     # Arguments marshalled once; each call below is one C-ABI call.
     L = hp.lib()
-    sh = stream.cuda_stream
+    sh = main_s.cuda_stream
     pd, pq = desc.with_tokens(T), qdesc.with_tokens(T)
-    wsp, wsn = ws.data_ptr(), ws.numel()
-    res_mem = torch.zeros(ctypes.sizeof(hp.HpValidateResult), dtype=torch.uint8,
-                          pin_memory=True)  # pinned: the check writes its result here
-    res = hp.HpValidateResult.from_address(res_mem.data_ptr())
-    pres = ctypes.byref(res)
     o_p, q_p = out.data_ptr(), qout.data_ptr()
     bf16 = hp.DTYPE["bf16"]
+    G = hp.HP_FLAG_GATED
 
-    # The validator runs on a stream of its own with its own workspace, so
-    # that checking the next step's descriptor overlaps this step's moves (as
-    # a serving loop would); the moves still start only after their
-    # descriptor's check has returned HP_OK.
-    vstream = torch.cuda.Stream(dev)
-    vws = torch.empty(256, dtype=torch.uint8, device=dev)
-    vsh, vwsp, vwsn = vstream.cuda_stream, vws.data_ptr(), vws.numel()
+    # Each step checks its descriptor with hp_validate_async on the moves'
+    # stream and the moves are gated on the verdict: no host round trip sits
+    # between steps, and a rejected descriptor would be moved by no kernel.
+    # (Checking the next step's descriptor on a second stream, with events
+    # ordering the moves after their check, measured slower: 531 against
+    # 475 us of kernels at 20 steps; the check alone takes about 4 us.)
+    ws = torch.empty(max(hp.workspace_bytes(desc, T), 256), dtype=torch.uint8, device=dev)
+    wsp, wsn = ws.data_ptr(), ws.numel()
 
     def do_validate():
-        if L.hp_validate(pd, None, vwsp, vwsn, pres, vsh) != 0:
-            raise SystemExit(f"hp_validate: {hp.status_str(res.code)}")
+        if L.hp_validate_async(pd, None, wsp, wsn, sh) != 0:
+            raise SystemExit("hp_validate_async failed")
 
     def do_gather():
-        if L.hp_gather(pd, o_p, wsp, wsn, hp.HP_FLAG_STREAM, sh) != 0:
+        if L.hp_gather(pd, o_p, wsp, wsn, hp.HP_FLAG_STREAM | G, sh) != 0:
             raise SystemExit("hp_gather failed")
 
     def do_scatter():
-        if L.hp_scatter(pd, o_p, None, wsp, wsn, 0, sh) != 0:
+        if L.hp_scatter(pd, o_p, None, wsp, wsn, G, sh) != 0:
             raise SystemExit("hp_scatter failed")
 
     def do_dequant():
-        if L.hp_gather_dequant(pq, q_p, bf16, wsp, wsn, 0, sh) != 0:
+        if L.hp_gather_dequant(pq, q_p, bf16, wsp, wsn, G, sh) != 0:
             raise SystemExit("hp_gather_dequant failed")
 
-    stages = [("validate", do_validate), ("gather", do_gather), ("scatter", do_scatter),
-              ("dequant", do_dequant)]
-    moves = stages[1:]
-    events, vtimes = [], []
+    moves = [("gather", do_gather), ("scatter", do_scatter), ("dequant", do_dequant)]
 
-    def run_steps(n, record):
-        """n steps: validate step 1's descriptor, then for each step enqueue its
-        moves and, while they run, validate the next step's descriptor."""
-        t = time.perf_counter()
-        do_validate()
-        if record:
-            vtimes.append(time.perf_counter() - t)
-        for k in range(n):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
-            for i, (_, fn) in enumerate(moves):
-                if record:
-                    ev[i].record(stream)
+    def run_steps(n):
+        for _ in range(n):
+            do_validate()
+            for _, fn in moves:
                 fn()
-            if record:
-                ev[3].record(stream)
-                events.append(ev)
-            if k + 1 < n:
-                t = time.perf_counter()
-                do_validate()
-                if record:
-                    vtimes.append(time.perf_counter() - t)
 
     if args.copy_calibration:
         calibration_copies(torch, dev)
 
-    run_steps(args.warmup, False)
-    torch.cuda.synchronize()
-    # The timed steps carry no instrumentation: timing events recorded between
-    # the moves cost about 18 us a step on this path (measured), so the
-    # per-stage breakdown comes from a separate, untimed run of the same steps.
-    t0 = time.perf_counter()
-    run_steps(args.steps, False)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    run_steps(min(args.steps, 20), True)
-    torch.cuda.synchronize()
-    in_step_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events]))
-                  for i, (n, _) in enumerate(moves)}
-    in_step_ms["validate"] = float(np.mean(vtimes)) * 1e3  # host wall time of the call
-
-    # Launch durations: back-to-back launches of each kernel between two events.
-    launch_ms = {}
-    for n, fn in stages[1:]:
+    # A fresh process's first ~20 steps run up to 15 % slower (measured: 545
+    # -> 499 us, then a steady ~478 us). So one pass of the per-kernel launch
+    # timings (discarded) and the reference copies run before the warm-up and
+    # timed steps, and the kept launch timings after them: both run on a GPU
+    # that has been running the path for a few tens of milliseconds.
+    def back_to_back(fn, s=main_s):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fn()
-        a.record(stream)
+        a.record(s)
         for _ in range(args.kernel_reps):
             fn()
-        b.record(stream)
+        b.record(s)
         b.synchronize()
-        launch_ms[n] = a.elapsed_time(b) / args.kernel_reps
+        return a.elapsed_time(b) / args.kernel_reps
+
+    # Launch durations: back-to-back launches of each step kernel (gated, as
+    # in the step) between two events on its stream.
+    def launch_times():
+        t = {n: back_to_back(fn) for n, fn in moves}
+        t["validate"] = back_to_back(do_validate)
+        return t
+
+    launch_times()
 
     # Reference copies of the gather's bytes: the same gather kernel on an
     # identity table (one sequence over pages 0..K-1: a contiguous copy) and
     # the runtime's plain device-to-device copy.
-    ident = hp.Descriptor(pool, idx(np.arange(K)), idx(np.array([0, K])), idx(np.array([K * 16])))
-    ident_out = torch.empty((K * 16, H, D), dtype=torch.float16, device=dev)
-    pi, io_p = ident.with_tokens(K * 16), ident_out.data_ptr()
-
-    def ident_gather():
-        if L.hp_gather(pi, io_p, wsp, wsn, hp.HP_FLAG_STREAM, sh) != 0:
-            raise SystemExit("hp_gather (identity table) failed")
-
-    def back_to_back(fn):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
-        a.record(stream)
-        for _ in range(args.kernel_reps):
-            fn()
-        b.record(stream)
-        b.synchronize()
-        return a.elapsed_time(b) / args.kernel_reps
-
     refs = None
     if not args.no_reference_copies:
+        ident = hp.Descriptor(pool, idx(np.arange(K)), idx(np.array([0, K])),
+                              idx(np.array([K * 16])))
+        ident_out = torch.empty((K * 16, H, D), dtype=torch.float16, device=dev)
+        pi, io_p = ident.with_tokens(K * 16), ident_out.data_ptr()
         ident_bytes = 2 * K * 16 * H * D * 2
         copy_src = pool.view(-1)[: K * 16 * H * D]
         copy_dst = ident_out.view(-1)
-        t_ident = back_to_back(ident_gather)
+        t_ident = back_to_back(lambda: L.hp_gather(pi, io_p, None, 0, hp.HP_FLAG_STREAM, sh))
         t_copy = back_to_back(lambda: copy_dst.copy_(copy_src))
         refs = {"identity_table_gather": round(ident_bytes / (t_ident / 1e3) / 1e9, 1),
                 "runtime_device_copy": round(ident_bytes / (t_copy / 1e3) / 1e9, 1),
                 "unit": "GB/s", "bytes": ident_bytes}
-    del ident_out
+        del ident_out
+
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(args.steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    verdict = hp.validate_verdict(desc, T, ws)
+    if verdict != ("HP_OK", 0):
+        raise SystemExit(f"the step's verdict: {verdict}")
+    launch_ms = launch_times()
 
     nbytes = step_bytes(T, S, K, H, D)
     total_bytes = sum(nbytes.values())
     value = total_bytes / (ms_per_step / 1e3) / 1e9
     ops = {}
-    for n, _ in stages:
-        ms = launch_ms.get(n)
-        ops[n] = {"in_step_ms": round(in_step_ms[n], 4), "algorithmic_bytes": nbytes[n]}
-        if ms is not None:
-            gbs = nbytes[n] / (ms / 1e3) / 1e9
-            ops[n].update({"launch_ms": round(ms, 4), "gb_per_s": round(gbs, 1),
+    for n in ("validate", "gather", "scatter", "dequant"):
+        ms = launch_ms[n]
+        gbs = nbytes[n] / (ms / 1e3) / 1e9
+        ops[n] = {"algorithmic_bytes": nbytes[n], "launch_ms": round(ms, 4)}
+        if n != "validate":
+            ops[n].update({"gb_per_s": round(gbs, 1),
                            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+    kernel_sum = sum(launch_ms.values())
     g_achieved = nbytes["gather"] / (launch_ms["gather"] / 1e3) / 1e9
+    roof = {"bound": "hbm", "kernel": GATHER_KERNEL + " (gather)",
+            "achieved": round(g_achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(g_achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(),
+            "algorithmic_bytes_per_launch": nbytes["gather"],
+            "avg_launch_ms": round(launch_ms["gather"], 4),
+            "avg_launch_from": "HIP events around back-to-back launches on the launch stream"}
+    prof = rocprof_gather()
+    if prof:
+        roof.update(prof)
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -866,69 +1311,65 @@ def main():
         "config": {"workload": "decode batch: 64 sequences, lengths uniform 1..2048, "
                                "page_size 16, 32 heads x 128 fp16, 12,000-page pool, uint32 "
                                "block table of unique pages (gather with the streaming "
-                               "hint); step = validate + gather + scatter + "
-                               "int8->bf16 dequant-gather of the same table (the next "
-                               "step's validation runs on a second stream beside the "
-                               "moves)",
+                               "hint); step = enqueue-only validation + gather + scatter + "
+                               "int8->bf16 dequant-gather of the same table, the moves gated "
+                               "on the device by the verdict",
                    "total_tokens": T, "num_seqs": S, "block_table_entries": K,
                    "step_algorithmic_bytes": total_bytes},
         "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "kernel_sum_ms": round(kernel_sum, 4),
+        "step_over_kernel_sum": round(ms_per_step / kernel_sum, 4),
         "ops": ops,
         "reference_copies": refs,
-        "roofline": {"bound": "hbm", "kernel": GATHER_KERNEL + " (gather)",
-                     "achieved": round(g_achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(g_achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for(),
-                     "algorithmic_bytes_per_launch": nbytes["gather"],
-                     "avg_launch_ms": round(launch_ms["gather"], 4)},
+        "roofline": roof,
     }
     if args.extras:
-        # copy-on-write page copy: 1,024 referenced pages of the decode pool
-        # (128 KiB each) into pages no sequence references
-        free = np.setdiff1d(np.arange(w.num_pages), w.block_table.astype(np.int64))
-        rng = np.random.default_rng(6)
-        n_copy = 1024
-        src_p = idx(rng.choice(w.block_table.astype(np.int64), n_copy, replace=False))
-        dst_p = idx(rng.choice(free, n_copy, replace=False))
-        t_copy = back_to_back(lambda: hp.copy_pages(desc, src_p, dst_p, stream=stream))
-        copy_bytes = 2 * n_copy * 16 * H * D * 2
-        # dequant-gather of the step's int8 pool under each quantization
-        # scheme, with zero points (the general kernel); per-slot is the step's
-        qout = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
-        zrng = np.random.default_rng(8)
-        schemes = {}
-        for name, scheme, axis, n_par, per_tok in (
-                ("per_tensor_zp", "per_tensor", 0, 1, 0),
-                ("per_channel_head_zp", "per_channel", 1, H, 0),
-                ("per_channel_head_dim_zp", "per_channel", 2, D, 0),
-                ("per_block_affine_zp", "per_block_affine", 0, wq.num_pages * 16, 5)):
-            sc = torch.from_numpy(zrng.uniform(1e-3, 1e-1, n_par).astype(np.float32)).to(dev)
-            zp = torch.from_numpy(zrng.integers(-128, 128, n_par).astype(np.int8)).to(dev)
-            t_q = back_to_back(lambda: hp.gather_dequant_q(qdesc, qout, scheme, sc, axis=axis,
-                                                           zero_points=zp, stream=stream))
-            qb = T * H * D * 3 + per_tok * T
-            schemes[name] = {"algorithmic_bytes": qb, "launch_us": round(t_q * 1e3, 1),
-                             "gb_per_s": round(qb / (t_q / 1e3) / 1e9, 1)}
-        del qout
-        result["extras"] = {
-            "quantize_on_scatter": quant_write_extras(hp, torch, np, dev, stream,
-                                                      args.kernel_reps),
-            "attention": attention_extras(hp, torch, np, dev, stream, args.kernel_reps,
-                                          gqa8=True),
-            "dequant_schemes": schemes,
-            "batched_append": batched_append(hp, torch, np, dev, stream, args.kernel_reps),
-            "copy_pages": {"workload": "1,024 pages of the decode pool (16 x 32 x 128 fp16 = "
-                                       "128 KiB each) copied to unreferenced pages",
-                           "algorithmic_bytes": copy_bytes, "launch_us": round(t_copy * 1e3, 1),
-                           "gb_per_s": round(copy_bytes / (t_copy / 1e3) / 1e9, 1)}}
+        result["extras"] = side_paths(hp, torch, np, dev, main_s, args, w, wq, desc, qdesc,
+                                      pool)
+    cpu = None
     if not args.no_cpu_baseline:
+        import oracle
         pool_h = pool.view(torch.int16).cpu().numpy().view(np.uint16)
         qpool_h = qpool.cpu().numpy()
         scales_h = scales.cpu().numpy()
-        result["cpu_baseline"] = cpu_baseline(w, pool_h, qpool_h, scales_h, args.cpu_seconds)
-    else:
-        result["cpu_baseline"] = None
+
+        def run(s0, s1):
+            kw = sub_desc(w, s0, s1)
+            Ts = int(w.seq_lens[s0:s1].astype(np.int64).sum())
+            oracle.validate(rank=3, paged_axis=0, num_pages=w.num_pages,
+                            page_size=w.page_size, block_table=kw["block_table"],
+                            seq_ptr=kw["seq_ptr"], seq_lens=kw["seq_lens"], total_tokens=Ts)
+            o = oracle.gather(pool_h, **kw)
+            oracle.scatter(pool_h, o, in_place=True, **kw)
+            oracle.gather_dequant(qpool_h, scales_h, **kw)
+
+        def step_b(s0, s1):
+            kw = sub_desc(w, s0, s1)
+            Ts = int(w.seq_lens[s0:s1].astype(np.int64).sum())
+            return sum(step_bytes(Ts, s1 - s0, len(kw["block_table"]), H, D).values())
+        legs = cpu_legs(w, run, step_b, args.cpu_seconds)
+        allc = legs["all_cores"]
+        cpu = {"value": allc["value"], "unit": "GB/s", "cores": allc["cores"], "kind": "oracle",
+               "sample": "the decode step (validate + gather + scatter + dequant-gather) on all "
+                         f"{S} sequences, split into {allc['cores']} balanced ranges run by one "
+                         "host thread each; single_thread: one thread on a prefix",
+               "seconds": allc["seconds"], "tokens_per_s": allc["tokens_per_s"],
+               "single_thread": legs["single_thread"],
+               "affinity_cores": legs["affinity_cores"], "cpu_model": legs["cpu_model"]}
+        del pool_h, qpool_h, scales_h
+    result["cpu_baseline"] = cpu
+    del g, gq, out, qout, pool, qpool, desc, qdesc
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        result["configs"] = measure_configs(hp, torch, np, dev, args.flush_iters,
+                                            args.cpu_seconds, not args.no_cpu_baseline)
+        if cpu is not None:
+            result["configs"]["decode"]["cpu_oracle"] = {
+                k: cpu[k] for k in ("single_thread", "affinity_cores", "cpu_model")}
+            result["configs"]["decode"]["cpu_oracle"]["all_cores"] = {
+                k: cpu[k] for k in ("value", "unit", "cores", "seconds", "tokens_per_s")}
     print(json.dumps(result), flush=True)
 
 
