@@ -392,6 +392,85 @@ def _calibration(rows, counter):
     return sum(big) / 3
 
 
+# Counter passes of the per-workload run (one rocprofv3 --pmc run each; every
+# pass stays within the per-block limits: at most 4 TCC, 4 TCP, 8 SQ and 2
+# GRBM counters).
+COUNTER_PASSES = {
+    "reqsize": "TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum "
+               "TCC_EA0_RDREQ_128B_sum TCP_UTCL1_TRANSLATION_MISS_sum "
+               "TCP_UTCL1_TRANSLATION_HIT_sum TCP_UTCL1_REQUEST_sum "
+               "TCP_UTCL1_STALL_MULTI_MISS_sum GRBM_GUI_ACTIVE",
+    "writes": "TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum TCC_HIT_sum TCC_MISS_sum "
+              "TCP_TCC_READ_REQ_sum TCP_TCC_READ_REQ_LATENCY_sum TCP_PENDING_STALL_CYCLES_sum",
+    "latency": "TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_RDREQ_DRAM_sum TCC_EA0_WRREQ_LEVEL_sum "
+               "TCC_EA0_WRREQ_DRAM_sum SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY",
+}
+COUNTER_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/prof_cnt_{d} -o {d} -- "
+               "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --flush-iters 3 "
+               "--copy-calibration")
+
+
+def summarize_counters(*dirs):
+    """Per-dispatch averages of the COUNTER_PASSES counters for every kernel
+    (and grid size) of the per-workload run, one directory per pass in the
+    order of COUNTER_PASSES, into profiles/workload_kernel_counters.md. Read
+    bytes from request sizes (32/64/128 B) are set beside FETCH_SIZE's
+    formula, which takes a request that is not 32 B as 64 B."""
+    names = list(COUNTER_PASSES)
+    if len(dirs) != len(names):
+        raise SystemExit(f"expected {len(names)} directories ({', '.join(names)})")
+    agg = {}
+    for d in dirs:
+        for r in _csv_rows(d, "*counter_collection.csv"):
+            short = _short(r["Kernel_Name"])
+            if not (short.startswith(("copy_kernel", "validate", "copy_pages", "__amd_rocclr"))):
+                continue
+            key = (short, int(r["Grid_Size"]))
+            agg.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    lines = ["# Counters per dispatch: every workload's moves (rocprofv3 --pmc)", "",
+             "One run per pass (commands from the repository root, on one MI355X):", ""]
+    for d in names:
+        lines.append(f"    {COUNTER_CMD.format(c=COUNTER_PASSES[d], d=d)}")
+    lines += ["", "Each dispatch is one move of one workload after a 1 GiB read flush (or the",
+              "decode step's launches, or a plain 1 GiB runtime copy: `__amd_rocclr_copyBuffer`",
+              "at the largest grid). Values are per-dispatch means over the run's dispatches",
+              "of that kernel and grid. Read bytes by request size = 32 x RDREQ_32B + 64 x",
+              "RDREQ_64B + 128 x RDREQ_128B; FETCH_SIZE's formula (no TCC_BUBBLE here)",
+              "counts every request that is not 32 B as 64 B. Write bytes = 32 x (WRREQ -",
+              "WRREQ_64B) + 64 x WRREQ_64B. Mean read latency = RDREQ_LEVEL / RDREQ (cycles),",
+              "UTCL1 miss rate = TRANSLATION_MISS / REQUEST.", "",
+              "| kernel (grid) | n | read MB (req sizes) | FETCH_SIZE-formula MB | 128 B share | "
+              "write MB | L2 hit | UTCL1 requests | UTCL1 misses | miss rate | EA read lat. cyc "
+              "| TCP-TCC read lat. cyc | GUI active cyc |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    rows = []
+    for (short, grid), c in sorted(agg.items()):
+        m = {k: sum(v) / len(v) for k, v in c.items()}
+        n = max(len(v) for v in c.values())
+        g = lambda k: m.get(k, float("nan"))
+        r32, r64, r128, rall = (g("TCC_EA0_RDREQ_32B_sum"), g("TCC_EA0_RDREQ_64B_sum"),
+                                g("TCC_EA0_RDREQ_128B_sum"), g("TCC_EA0_RDREQ_sum"))
+        read_b = 32 * r32 + 64 * r64 + 128 * r128
+        fetch_b = 32 * r32 + 64 * (rall - r32)
+        wr, wr64 = g("TCC_EA0_WRREQ_sum"), g("TCC_EA0_WRREQ_64B_sum")
+        write_b = 32 * (wr - wr64) + 64 * wr64
+        hit, miss = g("TCC_HIT_sum"), g("TCC_MISS_sum")
+        ureq, umiss = g("TCP_UTCL1_REQUEST_sum"), g("TCP_UTCL1_TRANSLATION_MISS_sum")
+        lat = g("TCC_EA0_RDREQ_LEVEL_sum") / rall if rall else float("nan")
+        tlat = g("TCP_TCC_READ_REQ_LATENCY_sum") / g("TCP_TCC_READ_REQ_sum")
+        rows.append((short, grid, n, read_b, fetch_b, r128 / rall if rall else 0, write_b,
+                     hit / (hit + miss) if hit + miss else float("nan"), ureq, umiss,
+                     umiss / ureq if ureq else float("nan"), lat, tlat, g("GRBM_GUI_ACTIVE")))
+    for (short, grid, n, rb, fb, s128, wb, hr, ureq, umiss, mr, lat, tlat, act) in rows:
+        lines.append(f"| `{short}` ({grid}) | {n} | {rb / 1e6:.1f} | {fb / 1e6:.1f} | {s128:.3f} | "
+                     f"{wb / 1e6:.1f} | {hr:.3f} | {ureq:.0f} | {umiss:.0f} | {mr:.4f} | "
+                     f"{lat:.0f} | {tlat:.0f} | {act:.0f} |")
+    with open(os.path.join(PROFILES, "workload_kernel_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_attention(trace_dir, fetch_dir, write_dir):
     """Kernel durations and calibrated HBM traffic of the attention kernels
     (bench.py --attention-only runs) into profiles/."""
@@ -925,6 +1004,14 @@ def measure_configs(hp, torch, np, dev, iters, cpu_seconds, with_cpu):
     L = hp.lib()
     flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     res = {}
+    keep = []
+
+    def workspace(desc, T):
+        """The workspace the binding would pass: hp_workspace_bytes (the plan
+        arrays of moves over many sequences, the validator's words)."""
+        ws = torch.empty(max(hp.workspace_bytes(desc, T), 256), dtype=torch.uint8, device=dev)
+        keep.append(ws)
+        return ws.data_ptr(), ws.numel()
 
     def ok(code, what):
         if code != 0:
@@ -946,14 +1033,15 @@ def measure_configs(hp, torch, np, dev, iters, cpu_seconds, with_cpu):
     out = torch.empty((T, w.num_heads, w.head_dim), dtype=g.pool.dtype, device=dev)
     g2 = OnGpu(hp, torch, np, w, dev, pool=torch.zeros_like(g.pool))
     pd, pb, o_p = g.desc.with_tokens(T), g2.desc.with_tokens(T), out.data_ptr()
+    wsp, wsn = workspace(g.desc, T)
     e = {"workload": "tiny: 3 sequences of 40, 24, 50 tokens, page_size 16, 20-page pool, "
                      "4 heads x 8 fp16; gather to [114, 4, 8] and scatter it back",
          "tokens": T, "sequences": w.num_seqs,
          "gather": move_summary(np, 2 * T * R, T, flushed_times(
-             torch, np, stream, lambda: ok(L.hp_gather(pd, o_p, None, 0, 0, sh), "gather"),
+             torch, np, stream, lambda: ok(L.hp_gather(pd, o_p, wsp, wsn, 0, sh), "gather"),
              iters, flush)),
          "scatter": move_summary(np, 2 * T * R, T, flushed_times(
-             torch, np, stream, lambda: ok(L.hp_scatter(pb, o_p, None, None, 0, 0, sh),
+             torch, np, stream, lambda: ok(L.hp_scatter(pb, o_p, None, wsp, wsn, 0, sh),
                                            "scatter"), iters, flush))}
     if with_cpu:
         ph = host(g.pool)
@@ -977,6 +1065,7 @@ def measure_configs(hp, torch, np, dev, iters, cpu_seconds, with_cpu):
     out = torch.empty((T, w.num_heads, w.head_dim), dtype=torch.float16, device=dev)
     qout = torch.empty((T, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
     pd, pq, o_p, q_p = g.desc.with_tokens(T), gq.desc.with_tokens(T), out.data_ptr(), qout.data_ptr()
+    wsp, wsn = workspace(g.desc, T)
     bf16 = hp.DTYPE["bf16"]
     res["decode"] = {
         "workload": "decode batch: 64 sequences, lengths uniform 1..2048, page_size 16, 32 "
@@ -985,13 +1074,13 @@ def measure_configs(hp, torch, np, dev, iters, cpu_seconds, with_cpu):
         "tokens": T, "sequences": w.num_seqs,
         "gather": move_summary(np, 2 * T * R, T, flushed_times(
             torch, np, stream,
-            lambda: ok(L.hp_gather(pd, o_p, None, 0, hp.HP_FLAG_STREAM, sh), "gather"),
+            lambda: ok(L.hp_gather(pd, o_p, wsp, wsn, hp.HP_FLAG_STREAM, sh), "gather"),
             iters, flush)),
         "scatter": move_summary(np, 2 * T * R, T, flushed_times(
-            torch, np, stream, lambda: ok(L.hp_scatter(pd, o_p, None, None, 0, 0, sh),
+            torch, np, stream, lambda: ok(L.hp_scatter(pd, o_p, None, wsp, wsn, 0, sh),
                                           "scatter"), iters, flush)),
         "dequant": move_summary(np, 3 * T * HD + 4 * T, T, flushed_times(
-            torch, np, stream, lambda: ok(L.hp_gather_dequant(pq, q_p, bf16, None, 0, 0, sh),
+            torch, np, stream, lambda: ok(L.hp_gather_dequant(pq, q_p, bf16, wsp, wsn, 0, sh),
                                           "dequant"), iters, flush))}
     del g, gq, out, qout
     free()
@@ -1002,9 +1091,10 @@ def measure_configs(hp, torch, np, dev, iters, cpu_seconds, with_cpu):
     T, R = w.total_tokens, w.row_bytes
     out = torch.empty((T, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
     pd, o_p = g.desc.with_tokens(T), out.data_ptr()
+    wsp, wsn = workspace(g.desc, T)
     uniq = len(np.unique(token_slots(w)))
     us = flushed_times(torch, np, stream,
-                       lambda: ok(L.hp_gather(pd, o_p, None, 0, 0, sh), "gather"), iters, flush)
+                       lambda: ok(L.hp_gather(pd, o_p, wsp, wsn, 0, sh), "gather"), iters, flush)
     e = {"workload": "prefix sharing: 256 sequences, a 1,024-token prefix on 64 shared pages "
                      "plus private suffixes of 16..512 tokens, page_size 16, 8 heads x 128 "
                      "bf16, 40,000-page pool; gather in logical order",
@@ -1029,9 +1119,10 @@ def measure_configs(hp, torch, np, dev, iters, cpu_seconds, with_cpu):
     T, R = w.total_tokens, w.row_bytes
     src = w.make_src(dev)
     pd, s_p, ss_p = g.desc.with_tokens(T), src.data_ptr(), g.ss.data_ptr()
+    wsp, wsn = workspace(g.desc, T)
     nt = tail_rows(w)
     us = flushed_times(torch, np, stream, lambda: ok(L.hp_scatter(
-        pd, s_p, ss_p, None, 0, hp.HP_FLAG_ZERO_TAIL, sh), "scatter"), iters, flush)
+        pd, s_p, ss_p, wsp, wsn, hp.HP_FLAG_ZERO_TAIL, sh), "scatter"), iters, flush)
     e = {"workload": "append: 512 decode sequences writing 1 token each into their partial "
                      "trailing page plus one 8,192-token prefill into fresh pages, page_size "
                      "16, 8 heads x 128 bf16, 60,000-page pool, unused trailing slots zeroed",
@@ -1059,8 +1150,9 @@ def measure_configs(hp, torch, np, dev, iters, cpu_seconds, with_cpu):
     T, HD = w.total_tokens, w.num_heads * w.head_dim
     qout = torch.empty((T, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
     pd, q_p = g.desc.with_tokens(T), qout.data_ptr()
+    wsp, wsn = workspace(g.desc, T)
     us = flushed_times(torch, np, stream, lambda: ok(L.hp_gather_dequant(
-        pd, q_p, bf16, None, 0, 0, sh), "dequant"), iters, flush)
+        pd, q_p, bf16, wsp, wsn, 0, sh), "dequant"), iters, flush)
     e = {"workload": "quantized large pool: int8, 200,000 pages x 16 x 8 x 128, one fp32 scale "
                      "per slot, uint64 table, 1,024 sequences with log-normal lengths capped "
                      "at 8,192; gather + dequant to bf16",
@@ -1071,7 +1163,7 @@ def measure_configs(hp, torch, np, dev, iters, cpu_seconds, with_cpu):
     raw = torch.empty((T, w.num_heads, w.head_dim), dtype=torch.int8, device=dev)
     r_p = raw.data_ptr()
     e["raw_gather"] = move_summary(np, 2 * T * HD, T, flushed_times(
-        torch, np, stream, lambda: ok(L.hp_gather(pd, r_p, None, 0, hp.HP_FLAG_STREAM, sh),
+        torch, np, stream, lambda: ok(L.hp_gather(pd, r_p, wsp, wsn, hp.HP_FLAG_STREAM, sh),
                                       "gather"), iters, flush))
     del raw
     free()
@@ -1117,7 +1209,12 @@ def main():
     ap.add_argument("--quant-write-only", action="store_true",
                     help="only the quantize-on-scatter measurements (profiling runs)")
     ap.add_argument("--summarize-quant-write", nargs=3, metavar=("TRACE", "FETCH", "WRITE"))
+    ap.add_argument("--summarize-counters", nargs=len(COUNTER_PASSES),
+                    metavar=tuple(k.upper() for k in COUNTER_PASSES))
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles)
         return
@@ -1240,6 +1337,7 @@ def main():
         t["validate"] = back_to_back(do_validate)
         return t
 
+    do_validate()  # the gated moves read this verdict (a fresh workspace holds none)
     launch_times()
 
     # Reference copies of the gather's bytes: the same gather kernel on an

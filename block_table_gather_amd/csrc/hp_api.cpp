@@ -116,8 +116,22 @@ hp_status check_workspace(const void *ws, size_t have, uint64_t need) {
     return HP_OK;
 }
 
+// Bytes of the plan arrays: needed above kFusedMaxSeqs sequences, and used by
+// choice from kPlanMinSeqs on (moves in HP_PLAN_OPS) when the caller's
+// workspace holds them.
 uint64_t plan_bytes(const hp_desc *d) {
-    return d->num_seqs > hp::kFusedMaxSeqs ? hp::plan_workspace_bytes(d->num_seqs) : 0;
+    return d->num_seqs >= hp::kPlanMinSeqs || d->num_seqs > hp::kFusedMaxSeqs
+               ? hp::plan_workspace_bytes(d->num_seqs)
+               : 0;
+}
+
+// Whether a move takes the plan path: always above kFusedMaxSeqs sequences;
+// from kPlanMinSeqs on it does when it is one of HP_PLAN_OPS and the
+// workspace holds the plan arrays.
+bool use_plan(const hp_desc *d, hp::Op op, const void *ws, size_t ws_bytes) {
+    if (d->num_seqs > hp::kFusedMaxSeqs)
+        return true;
+    return hp::plan_preferred(op, d->num_seqs) && ws && ws_bytes >= kValidateBytes + plan_bytes(d);
 }
 
 // The validator's two words (smallest failing key, all ones if none; the sum
@@ -233,8 +247,8 @@ struct QuantSpec {
 };
 
 hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const Members &m,
-                 const void *seq_start, uint32_t flags, void *ws, hipStream_t stream,
-                 const QuantSpec *q = nullptr) {
+                 const void *seq_start, uint32_t flags, void *ws, size_t ws_bytes,
+                 hipStream_t stream, const QuantSpec *q = nullptr) {
     const bool zero_tail = (flags & HP_FLAG_ZERO_TAIL) != 0;
     hp::CopyJob j = {};
     j.op = op;
@@ -249,12 +263,13 @@ hp_status launch(const hp_desc *d, const Geometry &g, hp::Op op, const Members &
     const uint64_t rmax = j.out_row_bytes > j.row_bytes ? j.out_row_bytes : j.row_bytes;
     // Per-move launch shape (measured on MI355X): target unit size, units per
     // workgroup, and whether the source is streamed with non-temporal loads.
+    j.plan = use_plan(d, op, ws, ws_bytes);
     uint64_t unit_bytes;
     switch (op) {
     case hp::Op::Gather:
+        // the fused scan's per-sequence reads are amortised over larger units
         unit_bytes = HP_GATHER_UNIT_BYTES;
-        if (d->num_seqs <= hp::kFusedMaxSeqs &&
-            d->num_seqs * HP_GATHER_UNIT_BYTES_PER_SEQ > unit_bytes)
+        if (!j.plan && d->num_seqs * HP_GATHER_UNIT_BYTES_PER_SEQ > unit_bytes)
             unit_bytes = d->num_seqs * HP_GATHER_UNIT_BYTES_PER_SEQ;
         j.units_per_group = HP_GATHER_UNITS_PER_GROUP;
         j.load_nt = (flags & HP_FLAG_STREAM) != 0;
@@ -332,7 +347,8 @@ hp_status prologue(const hp_desc *d, const Geometry &g, uint32_t flags, uint32_t
     if (!aligned(seq_start, g.idx_bytes))
         return HP_ERR_ALIGN;
     const bool fused = d->num_seqs <= hp::kFusedMaxSeqs;
-    const uint64_t need = (checked || gated || !fused) ? kValidateBytes + plan_bytes(d) : 0;
+    const uint64_t need = !fused ? kValidateBytes + plan_bytes(d)
+                                 : ((checked || gated) ? kValidateBytes : 0);
     hp_status st = check_workspace(ws, ws_bytes, need);
     if (st != HP_OK)
         return st;
@@ -540,7 +556,8 @@ hp_status hp_gather(const hp_desc *desc, void *out, void *workspace, size_t work
         return st;
     void *pool = desc->page_pool;
     const Members m = {1, &pool, &out, nullptr};
-    return launch(desc, g, hp::Op::Gather, m, nullptr, flags, workspace, (hipStream_t)stream);
+    return launch(desc, g, hp::Op::Gather, m, nullptr, flags, workspace, workspace_bytes,
+                  (hipStream_t)stream);
 }
 
 hp_status hp_scatter(const hp_desc *desc, const void *src, const void *seq_start,
@@ -563,7 +580,8 @@ hp_status hp_scatter(const hp_desc *desc, const void *src, const void *seq_start
     void *pool = desc->page_pool;
     void *rows = const_cast<void *>(src);  // read, never written
     const Members m = {1, &pool, &rows, nullptr};
-    return launch(desc, g, hp::Op::Scatter, m, seq_start, flags, workspace, (hipStream_t)stream);
+    return launch(desc, g, hp::Op::Scatter, m, seq_start, flags, workspace, workspace_bytes,
+                  (hipStream_t)stream);
 }
 
 hp_status hp_scatter_quant(const hp_desc *desc, const void *src, uint32_t src_dtype,
@@ -644,6 +662,7 @@ hp_status hp_scatter_quant(const hp_desc *desc, const void *src, uint32_t src_dt
     j.pools = &pool;
     j.rows = &rows;
     j.workspace = workspace ? static_cast<unsigned char *>(workspace) + kValidateBytes : nullptr;
+    j.plan = use_plan(desc, hp::Op::ScatterQuant, workspace, workspace_bytes);
     j.qs_src = src_code;
     j.qs_asym = asym;
     j.qs_scales = const_cast<float *>(desc->scales);
@@ -680,7 +699,8 @@ hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype, 
     void *pool = desc->page_pool;
     const float *scales = desc->scales;
     const Members m = {1, &pool, &out, &scales};
-    return launch(desc, g, hp::Op::Dequant, m, nullptr, flags, workspace, (hipStream_t)stream);
+    return launch(desc, g, hp::Op::Dequant, m, nullptr, flags, workspace, workspace_bytes,
+                  (hipStream_t)stream);
 }
 
 // ---- batched calls: several pools through one shared table --------------------
@@ -703,7 +723,8 @@ hp_status hp_gather_batch(const hp_desc *desc, uint32_t count, void *const *pool
     if (st != HP_OK || done)
         return st;
     const Members m = {count, pools, outs, nullptr};
-    return launch(&d, g, hp::Op::Gather, m, nullptr, flags, workspace, (hipStream_t)stream);
+    return launch(&d, g, hp::Op::Gather, m, nullptr, flags, workspace, workspace_bytes,
+                  (hipStream_t)stream);
 }
 
 hp_status hp_scatter_batch(const hp_desc *desc, uint32_t count, void *const *pools,
@@ -725,7 +746,8 @@ hp_status hp_scatter_batch(const hp_desc *desc, uint32_t count, void *const *poo
     if (st != HP_OK || done)
         return st;
     const Members m = {count, pools, rows, nullptr};
-    return launch(&d, g, hp::Op::Scatter, m, seq_start, flags, workspace, (hipStream_t)stream);
+    return launch(&d, g, hp::Op::Scatter, m, seq_start, flags, workspace, workspace_bytes,
+                  (hipStream_t)stream);
 }
 
 hp_status hp_gather_dequant_batch(const hp_desc *desc, uint32_t count, void *const *pools,
@@ -749,7 +771,8 @@ hp_status hp_gather_dequant_batch(const hp_desc *desc, uint32_t count, void *con
     if (st != HP_OK || done)
         return st;
     const Members m = {count, pools, outs, scales};
-    return launch(&d, g, hp::Op::Dequant, m, nullptr, flags, workspace, (hipStream_t)stream);
+    return launch(&d, g, hp::Op::Dequant, m, nullptr, flags, workspace, workspace_bytes,
+                  (hipStream_t)stream);
 }
 
 hp_status hp_gather_dequant_q(const hp_desc *desc, const hp_quant *quant, void *out,
@@ -805,7 +828,8 @@ hp_status hp_gather_dequant_q(const hp_desc *desc, const hp_quant *quant, void *
     q.is_unsigned = d.dtype == HP_DTYPE_U8;
     q.scales = quant->scales;
     q.zero_points = quant->zero_points;
-    return launch(&d, g, hp::Op::Dequant, m, nullptr, flags, workspace, (hipStream_t)stream, &q);
+    return launch(&d, g, hp::Op::Dequant, m, nullptr, flags, workspace, workspace_bytes,
+                  (hipStream_t)stream, &q);
 }
 
 // Shape checks of hp_paged_attention beyond the descriptor's own.

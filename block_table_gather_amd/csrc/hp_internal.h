@@ -65,6 +65,21 @@ namespace hp {
 #define HP_FUSED_MAX_SEQS 4096
 #endif
 constexpr uint64_t kFusedMaxSeqs = HP_FUSED_MAX_SEQS;
+// From this many sequences on, the moves in HP_PLAN_OPS (a bit per Op) take
+// the plan pass when the caller's workspace holds its arrays, even where the
+// fused scan would fit: each workgroup of the fused path reads and scans every
+// sequence's count (16 KB of metadata per 16 KB unit on the quantized batch's
+// 1,024 sequences); the plan pass writes the offsets once and each workgroup
+// binary-searches them. Measured on MI355X with cold caches: quantized-batch
+// gather 601 -> 553 us; the prefix batch (256 sequences) 152 -> 194 us the
+// other way, and the dequant 934 -> 955 us, so only the gather takes it.
+#ifndef HP_PLAN_MIN_SEQS
+#define HP_PLAN_MIN_SEQS 512
+#endif
+#ifndef HP_PLAN_OPS
+#define HP_PLAN_OPS 1
+#endif
+constexpr uint64_t kPlanMinSeqs = HP_PLAN_MIN_SEQS;
 constexpr uint32_t kThreads = HP_THREADS;     // threads per copy workgroup
 constexpr uint32_t kPlanChunk = 2048;         // sequences per plan workgroup
 constexpr uint32_t kMaxUnitsPerGroup = 16;
@@ -103,7 +118,8 @@ struct CopyJob {
     void *const *pools;     // [count] pools: gather/dequant read them, scatter writes
     void *const *rows;      // [count] logical tensors: gather/dequant write, scatter reads
     const float *const *scales;  // [count] per-slot scales (dequant), else null
-    void *workspace;        // plan arrays when num_seqs > kFusedMaxSeqs
+    void *workspace;        // plan arrays (plan path)
+    bool plan;              // take the plan path (always when num_seqs > kFusedMaxSeqs)
     uint32_t vec_bytes;     // widest vector width every span allows
     // Dequant under a general scheme (single pool): 0 = per-slot scales from
     // `scales` (the fast path when there is no zero point and q is signed),
@@ -222,8 +238,12 @@ uint64_t attention_workspace_bytes(uint64_t num_seqs, uint64_t total_tokens, uin
                                    uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads);
 hipError_t launch_attention(const AttentionJob &job, hipStream_t stream);
 
-// Workspace layout for the plan arrays (num_seqs > kFusedMaxSeqs).
+// Workspace bytes of the plan path: per-sequence offsets and chunk totals.
 uint64_t plan_workspace_bytes(uint64_t num_seqs);
+// Whether a move over num_seqs sequences may take the plan path by choice.
+constexpr bool plan_preferred(Op op, uint64_t num_seqs) {
+    return num_seqs >= kPlanMinSeqs && ((HP_PLAN_OPS >> static_cast<int>(op)) & 1);
+}
 
 hipError_t launch_copy(const CopyJob &job, hipStream_t stream);
 hipError_t launch_validate(const ValidateJob &job, hipStream_t stream);

@@ -1521,7 +1521,7 @@ hipError_t launch_copy(const CopyJob &job, hipStream_t stream) {
     a.div_rpc = make_div(job.rows_per_unit);
     a.div_page = make_div(job.page_size);
     a.div_upp = make_div(a.units_per_page);
-    const bool fused = job.num_seqs <= kFusedMaxSeqs;
+    const bool fused = !job.plan;
     const uint64_t grid64 = (job.unit_bound + job.units_per_group - 1) / job.units_per_group;
     const uint32_t grid = (uint32_t)grid64;
     uint32_t chunks = 0;

@@ -85,6 +85,28 @@ def test_gather_many_sequences_plan_path(hp):
     assert_bits_equal(host_bits(out), oracle_gather(d), "plan path")
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_gather_plan_by_choice(hp, seed):
+    """512..4096 sequences: with a workspace of hp_workspace_bytes the gather
+    takes the plan pass (per-sequence offsets and a unit -> sequence map
+    written once); without one, the fused scan. Both against the oracle."""
+    w = workloads.random_small(80 + seed, max_seqs=4096, max_len=60, page_sizes=(4, 16),
+                               heads=(1, 4), dims=(32, 128), dtypes=("bf16", "i8"),
+                               num_seqs=[512, 777, 2048, 4096][seed], with_start=False)
+    say("gather plan by choice", w.describe())
+    d = OnDevice(w)
+    want = oracle_gather(d)
+    for ws in (None, torch.empty(hp.workspace_bytes(d.desc, w.total_tokens), dtype=torch.uint8,
+                                 device=DEV)):
+        out = d.empty_out()
+        if ws is None:
+            hp.gather(d.desc, out, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+        else:
+            hp.gather(d.desc, out, workspace=ws)
+        torch.cuda.synchronize()
+        assert_bits_equal(host_bits(out), want, f"workspace {ws is not None}")
+
+
 def test_plan_path_on_a_side_stream(hp):
     """The plan path's workspace, allocated by the binding, on a stream other
     than the current one: it is recorded on the call's stream, so the
