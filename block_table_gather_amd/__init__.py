@@ -22,7 +22,7 @@ import os
 import torch  # noqa: F401,E402
 
 __all__ = ["Descriptor", "HpError", "gather", "scatter", "gather_dequant", "validate",
-           "validate_async", "validate_verdict",
+           "validate_async", "validate_verdict", "gather_static",
            "gather_dequant_q", "QUANT_SCHEME", "paged_attention", "attention_workspace_bytes",
            "scatter_quant",
            "gather_batch", "scatter_batch", "gather_dequant_batch", "copy_pages",
@@ -111,6 +111,8 @@ _lib.hp_validate_async.restype = ctypes.c_int
 _lib.hp_validate_async.argtypes = [_P, _vp, _vp, _sz, _vp]
 _lib.hp_validate_verdict.restype = ctypes.c_int
 _lib.hp_validate_verdict.argtypes = [_P, _vp, ctypes.POINTER(HpValidateResult)]
+_lib.hp_gather_static.restype = ctypes.c_int
+_lib.hp_gather_static.argtypes = [_P, _vp, _u32, _vp]
 _lib.hp_gather.restype = ctypes.c_int
 _lib.hp_gather.argtypes = [_P, _vp, _vp, _sz, _u32, _vp]
 _lib.hp_scatter.restype = ctypes.c_int
@@ -363,6 +365,15 @@ def gather(desc, out, *, checked=False, streaming=False, workspace=None, stream=
     flags = _flags(checked, gated, streaming=streaming)
     _check(_lib.hp_gather(p, _ptr(out), ws, n, flags, _stream(stream, desc.device)),
            "hp_gather")
+    return out
+
+
+def gather_static(desc, out, *, checked=False, streaming=False, stream=None):
+    """hp_gather_static: the gather with the library's own device workspace
+    (no allocation at all; calls on one GPU must not overlap)."""
+    p = desc.with_tokens(out.shape[0])
+    _check(_lib.hp_gather_static(p, _ptr(out), _flags(checked, False, streaming=streaming),
+                                 _stream(stream, desc.device)), "hp_gather_static")
     return out
 
 

@@ -8,6 +8,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 namespace {
 
 constexpr uint64_t kValidateBytes = 256;  // workspace head: validator key + sum
@@ -482,6 +484,46 @@ hp_status copy_pages_common(const hp_desc *desc, uint32_t num_pools, void *const
     return e == hipSuccess ? HP_OK : hip_failed(e);
 }
 
+// ---- the allocation-free gather ------------------------------------------------
+//
+// hp_gather_static keeps its workspace in this file-scope device array: the
+// validator's words (HP_FLAG_CHECKED) and the plan arrays of calls over many
+// sequences. Each GPU the library runs on holds its own copy until the
+// process ends. Host code never passes the array's name to a kernel or a
+// copy: it stands for a host-side shadow there. The device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+constexpr uint64_t kStaticMaxSeqs = 1u << 18;
+constexpr uint64_t kStaticScratchBytes = 256 + 0x300800;  // validator + plan at kStaticMaxSeqs
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct DeviceScratch {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+DeviceScratch g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch` (its device address), or null with
+// the HIP error in *e.
+void *device_scratch(hipError_t *e) {
+    int dev = 0;
+    if ((*e = hipGetDevice(&dev)) != hipSuccess)
+        return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *e = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    DeviceScratch &d = g_scratch[dev];
+    std::call_once(d.once, [&d] {
+        void *ptr = nullptr;
+        d.err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        d.ptr = d.err == hipSuccess ? ptr : nullptr;
+    });
+    *e = d.err;
+    return d.ptr;
+}
+
 } // namespace
 
 extern "C" {
@@ -558,6 +600,35 @@ hp_status hp_gather(const hp_desc *desc, void *out, void *workspace, size_t work
     const Members m = {1, &pool, &out, nullptr};
     return launch(desc, g, hp::Op::Gather, m, nullptr, flags, workspace, workspace_bytes,
                   (hipStream_t)stream);
+}
+
+hp_status hp_gather_static(const hp_desc *desc, void *out, uint32_t flags, void *stream) {
+    static_assert(kValidateBytes + 8 * kStaticMaxSeqs + 4 * kStaticMaxSeqs +
+                          16 * ((kStaticMaxSeqs + hp::kPlanChunk - 1) / hp::kPlanChunk) <=
+                      kStaticScratchBytes,
+                  "the static workspace holds the plan of kStaticMaxSeqs sequences");
+    Geometry g;
+    hp_status st = check_desc(desc, &g);
+    if (st != HP_OK)
+        return st;
+    if (flags & ~(uint32_t)(HP_FLAG_CHECKED | HP_FLAG_STREAM))
+        return HP_ERR_ARG;  // a gated call needs a verdict only the caller's workspace holds
+    if (desc->num_seqs > kStaticMaxSeqs ||
+        kValidateBytes + plan_bytes(desc) > kStaticScratchBytes)
+        return HP_ERR_WORKSPACE;
+    if (desc->total_tokens && !out)
+        return HP_ERR_NULL;
+    if (!aligned(out, g.elem_bytes))
+        return HP_ERR_ALIGN;
+    if (overlaps(out, desc->total_tokens * g.row_bytes, desc->page_pool, g.pool_bytes))
+        return HP_ERR_ARG;
+    if (desc->num_seqs == 0 || desc->total_tokens == 0)
+        return HP_OK;  // nothing to move: the device is not touched
+    hipError_t e;
+    void *ws = device_scratch(&e);
+    if (!ws)
+        return hip_failed(e);
+    return hp_gather(desc, out, ws, kStaticScratchBytes, flags, stream);
 }
 
 hp_status hp_scatter(const hp_desc *desc, const void *src, const void *seq_start,

@@ -211,6 +211,24 @@ hp_status hp_validate_verdict(const hp_desc *desc, const void *words,
 hp_status hp_gather(const hp_desc *desc, void *out, void *workspace,
                     size_t workspace_bytes, uint32_t flags, void *stream);
 
+/* Gather for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. The
+ * same move, flags and results as hp_gather, with no workspace argument: the
+ * workspace is a library-owned device array of about 3 MiB (each GPU the
+ * library runs on holds its own copy until the process ends). It holds the
+ * validator's words (HP_FLAG_CHECKED) and the plan arrays of calls over many
+ * sequences, at most 262,144 sequences (more: HP_ERR_WORKSPACE, nothing
+ * enqueued). The call allocates and frees nothing.
+ *
+ * Every call on one GPU shares that GPU's array, and the array keeps the last
+ * call's contents (everything a call reads there it first writes): calls
+ * that overlap on one GPU (concurrent streams, or host threads on one
+ * device) race and must not be made. `stream` must belong to the current
+ * device. Flags: HP_FLAG_CHECKED (synchronous, as in hp_gather),
+ * HP_FLAG_STREAM; HP_FLAG_GATED is rejected (HP_ERR_ARG), as is everything
+ * hp_gather rejects. */
+hp_status hp_gather_static(const hp_desc *desc, void *out, uint32_t flags, void *stream);
+
 /* Scatter: the inverse move. `src` holds T = sum(seq_lens) new rows
  * [T, H, D] of desc->dtype in logical order; the i-th new row of sequence s
  * is token seq_start[s] + i of that sequence and is written to

@@ -28,7 +28,8 @@ def test_every_declared_symbol_is_exported():
                           "hp_gather_batch", "hp_scatter_batch", "hp_gather_dequant_batch",
                           "hp_copy_pages", "hp_copy_pages_batch", "hp_gather_dequant_q",
                           "hp_paged_attention", "hp_attention_workspace_bytes",
-                          "hp_scatter_quant", "hp_validate_async", "hp_validate_verdict"}
+                          "hp_scatter_quant", "hp_validate_async", "hp_validate_verdict",
+                          "hp_gather_static"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -440,3 +441,22 @@ def test_validate_verdict_decoding():
     assert verdict((4 << 56) | 9, 0) == (S["HP_ERR_PAGE_RANGE"], 9)
     assert verdict((5 << 56) | 2, 114) == (S["HP_ERR_SEQ_LEN"], 2)
     assert L.hp_validate_verdict(ctypes.byref(d), None, ctypes.byref(res)) == S["HP_ERR_NULL"]
+
+
+def test_gather_static_rejections():
+    """The allocation-free gather checks everything on the host before it
+    touches the device: its size limit, the gated flag (the verdict it would
+    read lives in a caller's workspace), and what hp_gather rejects."""
+    gs = L.hp_gather_static
+    d = desc()
+    assert gs(None, OUT, 0, None) == S["HP_ERR_NULL"]
+    assert gs(ctypes.byref(desc(rank=2)), OUT, 0, None) == S["HP_ERR_RANK"]
+    assert gs(ctypes.byref(d), OUT, hp.HP_FLAG_GATED, None) == S["HP_ERR_ARG"]
+    assert gs(ctypes.byref(d), OUT, hp.HP_FLAG_ZERO_TAIL, None) == S["HP_ERR_ARG"]
+    assert gs(ctypes.byref(d), OUT + 1, 0, None) == S["HP_ERR_ALIGN"]
+    assert gs(ctypes.byref(d), ALIGNED + 64, 0, None) == S["HP_ERR_ARG"]      # overlaps the pool
+    big = desc(num_seqs=(1 << 18) + 1, num_block_entries=1 << 19, num_pages=1 << 19)
+    assert gs(ctypes.byref(big), OUT, 0, None) == S["HP_ERR_WORKSPACE"]
+    empty = desc(num_seqs=0, num_block_entries=0, block_table=None, seq_lens=None,
+                 total_tokens=0)
+    assert gs(ctypes.byref(empty), None, 0, None) == S["HP_OK"]             # nothing to move
