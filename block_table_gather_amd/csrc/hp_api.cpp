@@ -443,7 +443,7 @@ hp_status copy_pages_common(const hp_desc *desc, uint32_t num_pools, void *const
         return HP_ERR_NULL;
     if (!aligned(src_pages, g.idx_bytes) || !aligned(dst_pages, g.idx_bytes))
         return HP_ERR_ALIGN;
-    const uint64_t chunks = (page_bytes + 16383) / 16384;
+    const uint64_t chunks = (page_bytes + hp::kPageChunkBytes - 1) / hp::kPageChunkBytes;
     if (copies >= kMaxIndex || copies * chunks >= (1ull << 31))
         return HP_ERR_ARG;
     if (flags & HP_FLAG_CHECKED) {

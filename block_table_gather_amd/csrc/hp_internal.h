@@ -149,6 +149,17 @@ struct CopyJob {
     uint64_t gate_tokens;
 };
 
+// Bytes of one page a page-copy workgroup copies, and whether those
+// workgroups take chunks in XCD order (8 KiB in XCD order measured fastest:
+// see copy_pages_kernel).
+#ifndef HP_PAGE_CHUNK_BYTES
+#define HP_PAGE_CHUNK_BYTES 8192
+#endif
+#ifndef HP_PAGE_XCD
+#define HP_PAGE_XCD 1
+#endif
+constexpr uint32_t kPageChunkBytes = HP_PAGE_CHUNK_BYTES;
+
 // Copy-on-write page copy over `count` pools that share the page IDs.
 struct PageCopyJob {
     bool idx64;
