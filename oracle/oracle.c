@@ -106,7 +106,8 @@ int oracle_validate(uint32_t rank, uint32_t paged_axis, uint64_t num_pages,
             return ORACLE_SEQ_LEN;
         }
     }
-    /* total_tokens is the sum of the per-sequence token counts. */
+    /* [Hurray] Logical Shape: the logical tensor's first extent counts every
+     * sequence's tokens, so the counts must add up to total_tokens. */
     for (s = 0; s < num_seqs; s++)
         sum += seq_lens[s];
     if (sum != (unsigned __int128)total_tokens)

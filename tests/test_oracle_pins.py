@@ -27,13 +27,14 @@ def test_rust20_worked_example_scalar_indices():
     got = [oracle.element_index(bt, seq_ptr, 0, p, g["head"], g["feature"], P, strides)
            for p in g["positions"]]
     assert got == g["expected_scalar_index"]
-    # "each physical page occupies 1x2x3x2 = 12 scalar slots"; page 2 starts at 24
+    # [Rust20] Include the batch, shared head and feature: a page spans
+    # 1*2*3*2 = 12 scalars in each array, so page 2 starts at scalar 24
     assert strides[0] == g["page_slots"]
     assert oracle.element_index(bt, seq_ptr, 0, 0, 0, 0, P, strides) == g["page2_start"]
-    # "each token row in head 0 advances by 2 scalars"
+    # consecutive token rows of head 0 are 2 scalars apart (the feature width)
     assert (oracle.element_index(bt, seq_ptr, 0, 1, 0, 0, P, strides)
             - oracle.element_index(bt, seq_ptr, 0, 0, 0, 0, P, strides)) == g["row_step_head0"]
-    # "head 1 begins another 3x2=6 scalars into that page"
+    # head 1's rows start 3*2 = 6 scalars after head 0's within the page
     assert (oracle.element_index(bt, seq_ptr, 0, 0, 1, 0, P, strides)
             - g["page2_start"]) == g["head1_offset_in_page"]
     # positions 9..11 are the reserved, unfilled rows of physical page 1
