@@ -729,7 +729,12 @@ def attention_extras(hp, torch, np, dev, stream, reps, gqa8=False):
                      "gb_per_s": round(nbytes / (ms / 1e3) / 1e9, 1),
                      "tokens_per_s": round(T / (ms / 1e3), 1)}
         if unique is not None:
+            # the bytes a call must move at least when every distinct page is
+            # read once: the rate against the 8 TB/s roofline
+            ub = unique + S * Hq * D * 2 + S * Hq * D * 4
             res[name]["unique_kv_bytes"] = unique
+            res[name]["unique_gb_per_s"] = round(ub / (ms / 1e3) / 1e9, 1)
+            res[name]["unique_frac_of_8tbs"] = round(ub / (ms / 1e3) / 8e12, 3)
         del k_pool, v_pool, q, out, ws
         torch.cuda.empty_cache()
     return res
@@ -1243,7 +1248,8 @@ def main():
             calibration_copies(torch, dev)
         stream = torch.cuda.current_stream(dev)
         print(json.dumps({"attention": attention_extras(hp, torch, np, dev, stream,
-                                                        args.kernel_reps)}), flush=True)
+                                                        args.kernel_reps, gqa8=True)}),
+              flush=True)
         return
     if args.quant_write_only:
         if args.copy_calibration:

@@ -71,6 +71,13 @@ struct AArgs {
     uint32_t fused;    // the unit table is rebuilt in LDS (no plan kernel)
     float qscale;      // softmax scale * log2(e)
     Div div_page;
+    // Shared-prefix pass (cached loads, matrix-core path): the prefix plan's
+    // per-sequence shared pages and runs, and the shared pass's work items.
+    uint32_t shared;          // shared work items lead the grid; suffix units follow
+    uint32_t pg_area;         // LDS bytes of the staged page IDs (matrix-core kernel)
+    uint32_t chunk_pages;     // pages of one shared-pass work item
+    uint32_t seqs_per_block;  // sequences whose query heads share one MFMA row block
+    const uint32_t *pre_pages, *run_of, *work_seq0, *work_chunk, *nwork;
 };
 
 // 8 stored values (one 16-byte vector) as floats; exact.
@@ -458,8 +465,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
 // the G query heads as the 16 rows of the matrix (rows past G are zero and
 // dropped). One wave per kv head; a workgroup takes 4 kv heads of one unit.
 // Per tile of 32 tokens:
-//  * scores, two 16-token blocks: the lane's K operand is 16 contiguous bytes
-//    of one token's row, loaded straight from the pool;
+//  * scores, two 16-token blocks: K is loaded as whole head rows, staged in
+//    the wave's LDS tile buffer, and read from there into the B layout (16
+//    contiguous bytes of one token's row per lane);
 //  * per-row online softmax in base 2 on the accumulator layout (a lane holds
 //    4 rows of one token), row maxima and sums by DPP within 16-lane rows;
 //  * weights times V: the weights go through LDS into the A layout and are
@@ -521,7 +529,308 @@ __device__ __forceinline__ float row16_max(float x) {
 // compiler from moving memory accesses across).
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Query head of matrix row r (and the row of query head q): r = 4 (q % 4) +
+// q / 4, an involution on 0..15. A lane holds the accumulator rows 4 grp + i,
+// that is query heads 4 i + grp, so with G <= 4 (G <= 8) every live row sits
+// at i = 0 (i < 2) and the softmax of the others is skipped.
+__device__ __forceinline__ uint32_t row_head(uint32_t r) { return 4 * (r & 3) + (r >> 2); }
+
+// The unit's n tokens of kv head h against the query rows in qa: the online
+// softmax state m, l and the unnormalised output o of the rows this lane
+// holds (rows 4 grp + i for i < R, columns 16 db + c16). page_off: the byte
+// offsets in the pools of the unit's pages, staged in LDS. vt, pt: this
+// wave's V and weight tiles in LDS.
+template <typename ET, int D, bool NT, int R>
+__device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_off, uint32_t n,
+                                          uint32_t h,
+                                          const typename Mma<ET>::V8 (&qa)[D / 32],
+                                          unsigned char *vt, float *pt, float (&m)[4],
+                                          float (&l)[4], f32x4 (&o)[D / 16]) {
+#pragma clang fp contract(off)
+    using M = Mma<ET>;
+    using V8 = typename M::V8;
+    constexpr uint32_t KK = D / 32;  // MFMAs per 16-token score block
+    constexpr uint32_t DB = D / 16;  // 16-column blocks of the output
+    constexpr uint32_t VRB = v_row_bytes<D>();
+    const uint32_t lane = threadIdx.x & 63, P = a.page_size, Hkv = a.num_kv_heads;
+    const uint32_t c16 = lane & 15, grp = lane >> 4;
+    const uint32_t slot_bytes = Hkv * D * 2;
+    const uint32_t head_off = h * D * 2;
+
+    // Loads take whole head rows: chunk c of a tile is 16 bytes for each of
+    // the 64 lanes, lane L reading bytes 16 (L % (D / 8)) of the head row of
+    // token 4 c + L / (D / 8) (D = 128; the same form at D = 64), so a load
+    // covers a few complete 256-byte rows rather than 64-byte pieces of 16
+    // rows (half as many cache-line requests per byte; measured on MI355X,
+    // decode batch with four query heads per kv head: 244 us with the pieces,
+    // 198 us with whole rows for both K and V). K and V both go through the wave's
+    // tile buffer in LDS, K on to the B layout of the score product. Tokens
+    // past n repeat the last token (a real row; masked below).
+    V8 kb[2][KK];
+    u32x4 kc[2 * KK], vc[2 * KK];
+    auto load_rows = [&](const unsigned char *pool, uint32_t tb, u32x4 (&dst)[2 * KK]) {
+#pragma unroll
+        for (uint32_t c = 0; c < 2 * KK; ++c) {
+            const uint32_t ch = 64 * c + lane;
+            const uint32_t jt = ch / (D / 8), dc = ch % (D / 8);
+            const uint32_t j = min32(tb + jt, n - 1);
+            const uint32_t pj = udiv32(j, a.div_page);
+            dst[c] = ld16<NT>(pool + page_off[pj] + (uint64_t)(j - pj * P) * slot_bytes +
+                              head_off + 16 * dc);
+        }
+    };
+    auto store_rows = [&](const u32x4 (&src)[2 * KK]) {  // token-major rows of VRB bytes
+#pragma unroll
+        for (uint32_t c = 0; c < 2 * KK; ++c) {
+            const uint32_t ch = 64 * c + lane;
+            const uint32_t jt = ch / (D / 8), dc = ch % (D / 8);
+            *reinterpret_cast<u32x4 *>(vt + jt * VRB + 16 * dc) = src[c];
+        }
+    };
+    // K of the tile into the B layout: the lane's token 16 b + c16, bytes
+    // 64 kk + 16 grp of its row
+    auto stage_k = [&]() {
+        wave_lds_sync();  // the previous tile's reads of the buffer are done
+        store_rows(kc);
+        wave_lds_sync();
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (uint32_t kk = 0; kk < KK; ++kk)
+                kb[b][kk] = *reinterpret_cast<const V8 *>(vt + (16 * b + c16) * VRB + 64 * kk +
+                                                           16 * grp);
+    };
+    // Software pipeline: tile tb + 32's K loads follow tile tb's score
+    // products (which free the K registers), and its V loads follow tile tb's
+    // V writes to LDS, so they are in flight during the softmax and the
+    // weights x V products. The last tile is a separate copy (no prefetch)
+    // so that the loop body has no branch around its loads.
+    auto tile = [&](uint32_t tb, auto more_tag) {
+        constexpr bool more = decltype(more_tag)::value;
+        stage_k();
+        // scores: lane holds rows 4 grp + i of token tb + 16 b + c16
+        float x[2][4];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (uint32_t kk = 0; kk < KK; ++kk)
+                acc = M::mma(qa[kk], kb[b][kk], acc);
+            const bool ok = tb + 16 * b + c16 < n;
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+                x[b][i] = ok ? acc[i] * a.qscale : -__builtin_inff();
+        }
+        if constexpr (more)
+            load_rows(a.k_pool, tb + kMfmaTile, kc);
+        // online softmax per row (the tile's first token is in range, so the
+        // new maximum is finite). When no row's maximum grows the correction
+        // is exactly 1 and the rescaling is skipped (bit-identical).
+        float p[2][4], mx[4];
+        bool grow = false;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            mx[i] = __builtin_fmaxf(m[i], row16_max(__builtin_fmaxf(x[0][i], x[1][i])));
+            grow |= mx[i] != m[i];
+            p[0][i] = exp2_hw(x[0][i] - mx[i]);
+            p[1][i] = exp2_hw(x[1][i] - mx[i]);
+        }
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const float corr = exp2_hw(m[i] - mx[i]);
+                l[i] = l[i] * corr;
+#pragma unroll
+                for (uint32_t db = 0; db < DB; ++db)
+                    o[db][i] *= corr;
+                m[i] = mx[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            l[i] = l[i] + group_sum<16, false>(p[0][i] + p[1][i]);
+        // the previous tile's LDS reads are done before this tile's writes
+        wave_lds_sync();
+        // weights to LDS in the A layout: token t of the tile goes to column
+        // 8 (t % 4) + t / 4 (rows i >= R are not written: their output rows
+        // are never read)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const uint32_t t = 16 * b + c16;
+            const uint32_t col = 8 * (t & 3) + (t >> 2);
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+                pt[(4 * grp + i) * kPRow + col] = p[b][i];
+        }
+        // V tile to LDS (the buffer's K reads are done: the score products
+        // consumed them)
+        store_rows(vc);
+        wave_lds_sync();
+        if constexpr (more)
+            load_rows(a.v_pool, tb + kMfmaTile, vc);
+        // weights as three A operands whose sum is the binary32 weight
+        V8 pa[3];
+        {
+            float w[8];
+            __builtin_memcpy(&w[0], pt + c16 * kPRow + 8 * grp, 16);
+            __builtin_memcpy(&w[4], pt + c16 * kPRow + 8 * grp + 4, 16);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const auto hi = M::narrow(w[e]);
+                const float r1 = w[e] - (float)hi;
+                const auto mid = M::narrow(r1);
+                const float r2 = r1 - (float)mid;
+                pa[0][e] = hi;
+                pa[1][e] = mid;
+                pa[2][e] = M::narrow(r2);
+            }
+        }
+        // output += weights x V, 16 columns at a time; lane group grp reads
+        // tokens grp + 4 e of column 16 db + c16
+#pragma unroll
+        for (uint32_t db = 0; db < DB; ++db) {
+            V8 vb;
+            const unsigned char *vr = vt + (16 * db + c16) * 2 + grp * VRB;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                vb[e] = *reinterpret_cast<const typename M::E *>(vr + 4 * e * VRB);
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                o[db] = M::mma(pa[k], vb, o[db]);
+        }
+    };
+    load_rows(a.k_pool, 0, kc);
+    load_rows(a.v_pool, 0, vc);
+    uint32_t tb = 0;
+    for (; tb + kMfmaTile < n; tb += kMfmaTile)
+        tile(tb, std::integral_constant<bool, true>());
+    tile(tb, std::integral_constant<bool, false>());  // n >= 1: the unit's last tile
+}
+
+// ---- shared-prefix pass ---------------------------------------------------------
+//
+// [Hurray] Prefix Sharing: slices may name the same leading pages, and then
+// every sequence that shares them attends over the same K and V rows.
+// Sequences are taken in runs: consecutive sequences whose slices begin with
+// at least kMinSharedTokens tokens of identical full pages (both sequences'
+// counts cover them); a run's shared part is the shortest such common prefix
+// in it, which every member holds. For a run, the shared part is computed
+// once per kv head and chunk of chunk_pages pages: the matrix core's 16 rows
+// take the query heads of seqs_per_block sequences of the run (16 / G of them
+// with G query heads per kv head), so each K/V tile is read once for all of
+// them instead of once per sequence. A sequence's units are its shared chunks
+// followed by units over the tokens after the shared part; the shared pass
+// writes the partial results of the first kind into those units' slots, the
+// attention kernel the rest, and the combine kernel merges them as before.
+
+constexpr uint32_t kSharedChunkTokens = 256;  // tokens of one shared work item (about)
+constexpr uint32_t kMinSharedTokens = 64;     // two matrix tiles
+
+// Work item w: chunk work_chunk[w] of the run block that begins at sequence
+// work_seq0[w], for the kv heads of grid row y (and query-head chunk z when
+// G > 16). Called by whole workgroups.
 template <typename ET, typename IdxT, int D, bool NT>
+__device__ __forceinline__ void shared_item(const AArgs &a, uint32_t w, unsigned char *lds) {
+#pragma clang fp contract(off)
+    using M = Mma<ET>;
+    using V8 = typename M::V8;
+    constexpr uint32_t KK = D / 32;
+    constexpr uint32_t DB = D / 16;
+    const uint32_t s0 = uni(a.work_seq0[w]), c = uni(a.work_chunk[w]);
+    const uint32_t run = uni(a.run_of[s0]), C = uni(a.pre_pages[s0]);
+    const uint32_t S = a.num_seqs, Hq = a.num_q_heads, Hkv = a.num_kv_heads, P = a.page_size;
+    const uint32_t G = a.group, spb = a.seqs_per_block;
+    const uint32_t pg0 = c * a.chunk_pages;
+    const uint32_t npg = min32(C - pg0, a.chunk_pages);  // whole pages, all tokens live
+    const uint32_t n = npg * P;
+    uint64_t *pages = reinterpret_cast<uint64_t *>(lds);  // byte offsets of the pages
+    const uint64_t sp0 = uni64(ld_idx<IdxT>(a.seq_ptr, s0));
+    const uint64_t page_bytes = (uint64_t)P * Hkv * D * 2;
+    for (uint32_t i = threadIdx.x; i < npg; i += kAttnThreads)
+        pages[i] = ld_idx<IdxT>(a.block_table, sp0 + pg0 + i) * page_bytes;
+    __syncthreads();
+
+    const uint32_t wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const uint32_t h = blockIdx.y * kMfmaWaves + wave;
+    if (h >= Hkv)
+        return;  // no barrier follows
+    unsigned char *vt = lds + a.pg_area + wave * mfma_wave_lds<D>();
+    float *pt = reinterpret_cast<float *>(vt + kMfmaTile * v_row_bytes<D>());
+    const uint32_t c16 = lane & 15, grp = lane >> 4;
+    // Row r: with G <= 16, query head r % G of sequence s0 + r / G; with
+    // G > 16 (one sequence per block), query head 16 z + r of sequence s0. A
+    // row is live when its sequence belongs to the run.
+    auto row_seq = [&](uint32_t r, uint32_t &seq, uint32_t &qi) -> bool {
+        if (G <= kMfmaRows) {
+            const uint32_t k = r / G;
+            seq = s0 + k;
+            qi = r - k * G;
+            return k < spb && seq < S && a.run_of[seq] == run;
+        }
+        seq = s0;
+        qi = blockIdx.z * kMfmaRows + r;
+        return qi < G;
+    };
+    V8 qa[KK];
+    {
+        uint32_t seq, qi;
+        const bool live = row_seq(c16, seq, qi);
+        const uint64_t qo = live ? (((uint64_t)seq * Hq + (uint64_t)h * G + qi) * D + 8 * grp) * 2
+                                 : 0;
+#pragma unroll
+        for (uint32_t kk = 0; kk < KK; ++kk) {
+            u32x4 v = ld16<false>(a.q + qo + kk * 64);
+            if (!live)
+                v = u32x4(0);
+            qa[kk] = __builtin_bit_cast(V8, v);
+        }
+    }
+    float m[4], l[4];
+    f32x4 o[DB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m[i] = -__builtin_inff();
+        l[i] = 0.0f;
+    }
+#pragma unroll
+    for (uint32_t db = 0; db < DB; ++db)
+        o[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    mfma_span<ET, D, NT, 4>(a, pages, n, h, qa, vt, pt, m, l, o);
+
+    // row 4 grp + i: the partial result of chunk c goes to unit slot c of its
+    // sequence; a sequence whose only unit this is gets its output directly
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t seq, qi;
+        if (!row_seq(4 * grp + i, seq, qi))
+            continue;
+        const uint32_t u0 = seq ? a.unit_end[seq - 1] : 0, u1 = a.unit_end[seq];
+        if (u0 + c >= u1)
+            continue;  // units capped (total_tokens below the counts): no slot
+        const uint64_t hq = (uint64_t)h * G + qi;
+        if (u1 - u0 == 1) {
+            float *dst = a.out + ((uint64_t)seq * Hq + hq) * D + c16;
+#pragma unroll
+            for (uint32_t db = 0; db < DB; ++db)
+                dst[16 * db] = o[db][i] / l[i];
+        } else {
+            const uint64_t idx = (uint64_t)(u0 + c) * Hq + hq;
+            float *dst = a.part_acc + idx * D + c16;
+#pragma unroll
+            for (uint32_t db = 0; db < DB; ++db)
+                dst[16 * db] = o[db][i];
+            if (c16 == 0) {
+                a.part_ml[2 * idx] = m[i];
+                a.part_ml[2 * idx + 1] = l[i];
+            }
+        }
+    }
+}
+
+// R: accumulator rows per lane that hold query heads (1 for G <= 4, 2 for
+// G <= 8, else 4).
+template <typename ET, typename IdxT, int D, bool NT, int R>
 __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
 #pragma clang fp contract(off)
     using M = Mma<ET>;
@@ -529,20 +838,28 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
     constexpr uint32_t KK = D / 32;  // MFMAs per 16-token score block
     constexpr uint32_t DB = D / 16;  // 16-column blocks of the output
     constexpr uint32_t VRB = v_row_bytes<D>();
-    constexpr uint32_t VCH = kMfmaTile * D / 8 / 64;  // 16-byte V chunks per lane per tile
     extern __shared__ __align__(16) unsigned char lds[];
     const uint32_t S = a.num_seqs;
+    uint32_t g = blockIdx.x;
+    if (a.shared) {
+        // the shared-prefix work items come first, so that their reads (mostly
+        // served by the caches) overlap the units' HBM reads
+        const uint32_t nw = uni(*a.nwork);
+        if (g < nw) {
+            shared_item<ET, IdxT, D, NT>(a, g, lds);
+            return;
+        }
+        g -= nw;
+    }
     const size_t ue_bytes = a.fused ? ((4 * (size_t)S + 15) & ~(size_t)15) : 0;
     uint32_t *ue_lds = reinterpret_cast<uint32_t *>(lds);
     uint64_t *pages = reinterpret_cast<uint64_t *>(lds + ue_bytes);
-    const size_t pg_bytes = (8 * (size_t)a.unit_pages + 15) & ~(size_t)15;
     const uint32_t *unit_end = a.unit_end;
     if (a.fused) {
         unit_scan_lds<IdxT>(a.seq_lens, S, a.unit_tokens, a.cap_units, ue_lds);
         unit_end = ue_lds;
     }
 
-    const uint32_t g = blockIdx.x;
     const uint32_t total = uni(unit_end[S - 1]);
     const uint32_t Hq = a.num_q_heads, Hkv = a.num_kv_heads, P = a.page_size, G = a.group;
     const uint32_t gz = blockIdx.z * kMfmaRows;  // first query head of this chunk in the group
@@ -576,36 +893,41 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
     const uint32_t u0 = s ? uni(unit_end[s - 1]) : 0;
     const uint64_t L = uni64(ld_idx<IdxT>(a.seq_lens, s));
     const uint64_t sp0 = uni64(ld_idx<IdxT>(a.seq_ptr, s));
-    const uint64_t t0 = (uint64_t)(g - u0) * a.unit_tokens;
+    uint64_t t0 = (uint64_t)(g - u0) * a.unit_tokens;
+    if (a.shared) {
+        // the sequence's first units are its shared chunks, which the shared
+        // pass computes; the rest cover the tokens after the shared pages
+        const uint32_t sh = uni(a.pre_pages[s]);
+        const uint32_t nch = (sh + a.chunk_pages - 1) / a.chunk_pages;
+        if (g - u0 < nch)
+            return;
+        t0 = (uint64_t)sh * P + (uint64_t)(g - u0 - nch) * a.unit_tokens;
+    }
     if (t0 >= L)
         return;  // only when total_tokens disagrees with the counts: read nothing
     const uint32_t n = (uint32_t)min64(L - t0, a.unit_tokens);
     const uint64_t pg0 = t0 / P;
     const uint32_t npg = udiv32(n + P - 1, a.div_page);
+    const uint64_t page_bytes = (uint64_t)P * Hkv * D * 2;
     for (uint32_t i = threadIdx.x; i < npg; i += kAttnThreads)
-        pages[i] = ld_idx<IdxT>(a.block_table, sp0 + pg0 + i);
+        pages[i] = ld_idx<IdxT>(a.block_table, sp0 + pg0 + i) * page_bytes;  // byte offsets
     __syncthreads();
 
     const uint32_t wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const uint32_t h = blockIdx.y * kMfmaWaves + wave;
     if (h >= Hkv)
         return;  // no barrier follows
-    unsigned char *vt = lds + ue_bytes + pg_bytes + wave * mfma_wave_lds<D>();
+    unsigned char *vt = lds + ue_bytes + a.pg_area + wave * mfma_wave_lds<D>();
     float *pt = reinterpret_cast<float *>(vt + kMfmaTile * VRB);
     const uint32_t c16 = lane & 15, grp = lane >> 4;
-    const uint64_t slot_bytes = (uint64_t)Hkv * D * 2;
-    const uint64_t head_off = (uint64_t)h * D * 2;
-    auto row_of = [&](uint32_t j) -> uint64_t {  // pool row of unit token j (< n)
-        const uint32_t pj = udiv32(j, a.div_page);
-        return pages[pj] * P + (j - pj * P);
-    };
-
-    // Q as the A operand of the score product: row c16 is query head gz + c16
-    // of this kv head (zero past G); lane group grp holds dims 32 kk + 8 grp.
+    // Q as the A operand of the score product: row c16 is query head
+    // gz + row_head(c16) of this kv head (zero past G); lane group grp holds
+    // dims 32 kk + 8 grp.
     V8 qa[KK];
     {
-        const bool qrow = gz + c16 < G;
-        const uint64_t qo = (((uint64_t)s * Hq + (uint64_t)h * G + min32(gz + c16, G - 1)) * D +
+        const uint32_t qh = gz + row_head(c16);
+        const bool qrow = qh < G;
+        const uint64_t qo = (((uint64_t)s * Hq + (uint64_t)h * G + min32(qh, G - 1)) * D +
                              8 * grp) * 2;
 #pragma unroll
         for (uint32_t kk = 0; kk < KK; ++kk) {
@@ -626,136 +948,13 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
     for (uint32_t db = 0; db < DB; ++db)
         o[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // K operands of the two 16-token blocks of tile tb: token tb + 16 b + c16
-    // (the last token again past n: a real row, masked below); V chunk
-    // 64 c + lane is token (64 c + lane) / (D / 8) of the tile, 16 bytes at
-    // dims 8 ((64 c + lane) % (D / 8)).
-    V8 kb[2][KK];
-    u32x4 vc[VCH];
-    auto load_k = [&](uint32_t tb) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const uint32_t j = min32(tb + 16 * b + c16, n - 1);
-            const unsigned char *kr = a.k_pool + row_of(j) * slot_bytes + head_off + 16 * grp;
-#pragma unroll
-            for (uint32_t kk = 0; kk < KK; ++kk)
-                kb[b][kk] = __builtin_bit_cast(V8, ld16<NT>(kr + kk * 64));
-        }
-    };
-    auto load_v = [&](uint32_t tb) {
-#pragma unroll
-        for (uint32_t c = 0; c < VCH; ++c) {
-            const uint32_t ch = 64 * c + lane;
-            const uint32_t jt = ch / (D / 8), dc = ch % (D / 8);
-            const uint32_t j = min32(tb + jt, n - 1);
-            vc[c] = ld16<NT>(a.v_pool + row_of(j) * slot_bytes + head_off + 16 * dc);
-        }
-    };
-    // Software pipeline: tile tb + 32's K loads follow tile tb's score
-    // products (which free the K registers), and its V loads follow tile tb's
-    // V writes to LDS, so they are in flight during the softmax and the
-    // weights x V products.
-    // One 32-token tile; MORE: the next tile's loads are issued inside it.
-    // The last tile is a separate copy (no prefetch) so that the loop body
-    // has no branch around its loads: the wait for a tile's K then leaves
-    // its V loads in flight.
-    auto tile = [&](uint32_t tb, auto more_tag) {
-        constexpr bool more = decltype(more_tag)::value;
-        // scores: lane holds rows 4 grp + i of token tb + 16 b + c16
-        float x[2][4];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (uint32_t kk = 0; kk < KK; ++kk)
-                acc = M::mma(qa[kk], kb[b][kk], acc);
-            const bool ok = tb + 16 * b + c16 < n;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                x[b][i] = ok ? acc[i] * a.qscale : -__builtin_inff();
-        }
-        if constexpr (more)
-            load_k(tb + kMfmaTile);
-        // online softmax per row (the tile's first token is in range, so the
-        // new maximum is finite)
-        float p[2][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float mx = __builtin_fmaxf(m[i], row16_max(__builtin_fmaxf(x[0][i], x[1][i])));
-            const float corr = exp2_hw(m[i] - mx);
-            p[0][i] = exp2_hw(x[0][i] - mx);
-            p[1][i] = exp2_hw(x[1][i] - mx);
-            l[i] = l[i] * corr + group_sum<16, false>(p[0][i] + p[1][i]);
-            m[i] = mx;
-#pragma unroll
-            for (uint32_t db = 0; db < DB; ++db)
-                o[db][i] *= corr;
-        }
-        // the previous tile's LDS reads are done before this tile's writes
-        wave_lds_sync();
-        // weights to LDS in the A layout: token t of the tile goes to column
-        // 8 (t % 4) + t / 4
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const uint32_t t = 16 * b + c16;
-            const uint32_t col = 8 * (t & 3) + (t >> 2);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                pt[(4 * grp + i) * kPRow + col] = p[b][i];
-        }
-        // V tile to LDS, token-major
-#pragma unroll
-        for (uint32_t c = 0; c < VCH; ++c) {
-            const uint32_t ch = 64 * c + lane;
-            const uint32_t jt = ch / (D / 8), dc = ch % (D / 8);
-            *reinterpret_cast<u32x4 *>(vt + jt * VRB + 16 * dc) = vc[c];
-        }
-        wave_lds_sync();
-        if constexpr (more)
-            load_v(tb + kMfmaTile);
-        // weights as three A operands whose sum is the binary32 weight
-        V8 pa[3];
-        {
-            float w[8];
-            __builtin_memcpy(&w[0], pt + c16 * kPRow + 8 * grp, 16);
-            __builtin_memcpy(&w[4], pt + c16 * kPRow + 8 * grp + 4, 16);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const auto hi = M::narrow(w[e]);
-                const float r1 = w[e] - (float)hi;
-                const auto mid = M::narrow(r1);
-                const float r2 = r1 - (float)mid;
-                pa[0][e] = hi;
-                pa[1][e] = mid;
-                pa[2][e] = M::narrow(r2);
-            }
-        }
-        // output += weights x V, 16 columns at a time; lane group grp reads
-        // tokens grp + 4 e of column 16 db + c16
-#pragma unroll
-        for (uint32_t db = 0; db < DB; ++db) {
-            V8 vb;
-            const unsigned char *vr = vt + (16 * db + c16) * 2 + grp * VRB;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                vb[e] = *reinterpret_cast<const typename M::E *>(vr + 4 * e * VRB);
-#pragma unroll
-            for (int k = 0; k < 3; ++k)
-                o[db] = M::mma(pa[k], vb, o[db]);
-        }
-    };
-    load_k(0);
-    load_v(0);
-    uint32_t tb = 0;
-    for (; tb + kMfmaTile < n; tb += kMfmaTile)
-        tile(tb, std::integral_constant<bool, true>());
-    tile(tb, std::integral_constant<bool, false>());  // n >= 1: the unit's last tile
+    mfma_span<ET, D, NT, R>(a, pages, n, h, qa, vt, pt, m, l, o);
 
-    // rows 4 grp + i: query head gz + 4 grp + i of kv head h, column 16 db + c16
+    // rows 4 grp + i: query head gz + 4 i + grp of kv head h, column 16 db + c16
     const uint32_t units = uni(unit_end[s]) - u0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t qi = gz + 4 * grp + i;
+    for (int i = 0; i < R; ++i) {
+        const uint32_t qi = gz + 4 * i + grp;
         if (qi >= G)
             continue;
         const uint64_t hq = (uint64_t)h * G + qi;
@@ -775,6 +974,189 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
                 a.part_ml[2 * idx + 1] = l[i];
             }
         }
+    }
+}
+
+struct PlanArgs {
+    const void *block_table, *seq_ptr, *seq_lens;
+    uint32_t num_seqs, page_size, unit_tokens, chunk_pages, min_pages, seqs_per_block;
+    uint32_t cap_units, cap_work;
+    uint32_t *unit_end, *unit_seq, *pre_pages, *run_of, *run_first, *run_c;
+    uint32_t *work_seq0, *work_chunk, *nwork;
+};
+
+// Exclusive scan of v over the workgroup (one value per thread); *total gets
+// the sum. Every thread calls it.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *total) {
+    __shared__ uint32_t wave_sum[kAttnThreads / 64];
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o, 64);
+        if (lane >= (uint32_t)o)
+            incl += y;
+    }
+    if (lane == 63)
+        wave_sum[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+    for (uint32_t k = 0; k < kAttnThreads / 64; ++k) {
+        before += k < wave ? wave_sum[k] : 0;
+        all += wave_sum[k];
+    }
+    __syncthreads();  // wave_sum may be reused by the next call
+    *total = all;
+    return before + incl - v;
+}
+
+// Leading pages that sequence s > 0 has in common with sequence s - 1: equal
+// page IDs at the same positions of the two slices, counting only pages that
+// both sequences fill (and at most kMaxSharedPages), into pre_pages[s]; 0
+// for s = 0. One wave per sequence compares 64 x kLcpPerLane positions per
+// step.
+constexpr uint32_t kMaxSharedPages = 8192;
+constexpr uint32_t kLcpPerLane = 4;
+
+template <typename IdxT>
+__global__ __launch_bounds__(kAttnThreads) void attention_lcp_kernel(PlanArgs p) {
+    const uint32_t s = blockIdx.x * (kAttnThreads / 64) + (threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63;
+    if (s >= p.num_seqs)
+        return;
+    uint64_t lcp = 0;
+    if (s > 0) {
+        const uint32_t P = p.page_size;
+        const uint64_t a0 = uni64(ld_idx<IdxT>(p.seq_ptr, s - 1));
+        const uint64_t a1 = uni64(ld_idx<IdxT>(p.seq_ptr, s));
+        const uint64_t b1 = uni64(ld_idx<IdxT>(p.seq_ptr, s + 1));
+        uint64_t lim = uni64(ld_idx<IdxT>(p.seq_lens, s - 1)) / P;
+        lim = min64(lim, uni64(ld_idx<IdxT>(p.seq_lens, s)) / P);
+        lim = min64(lim, min64(a1 - a0, b1 - a1));
+        lim = min64(lim, kMaxSharedPages);
+        lcp = lim;
+        for (uint64_t base = 0; base < lim; base += 64 * kLcpPerLane) {
+            uint64_t x[kLcpPerLane], y[kLcpPerLane];
+#pragma unroll
+            for (uint32_t k = 0; k < kLcpPerLane; ++k) {
+                const uint64_t j = base + 64 * k + lane;
+                x[k] = j < lim ? ld_idx<IdxT>(p.block_table, a0 + j) : 0;
+                y[k] = j < lim ? ld_idx<IdxT>(p.block_table, a1 + j) : 0;
+            }
+            uint64_t first = ~0ull;
+#pragma unroll
+            for (uint32_t k = kLcpPerLane; k-- > 0;) {
+                const uint64_t mask = __ballot(x[k] != y[k]);
+                if (mask)
+                    first = base + 64 * k + (uint64_t)(__ffsll((long long)mask) - 1);
+            }
+            if (first != ~0ull) {
+                lcp = first;
+                break;
+            }
+        }
+    }
+    if (lane == 0)
+        p.pre_pages[s] = (uint32_t)lcp;
+}
+
+// The shared-prefix plan, one workgroup, after attention_lcp_kernel: runs of
+// sequences that share leading pages (a run starts where a sequence's count
+// of leading pages in common with its predecessor is below min_pages), each
+// sequence's shared pages (its run's smallest count; 0 for a run of one), the
+// units (shared chunks, then units over the rest) with unit_end and the unit
+// -> sequence map, and the shared pass's work items (a run block of
+// seqs_per_block sequences times the chunks of its shared pages).
+constexpr uint32_t kPlanLdsSeqs = 4096;  // unit_end kept in LDS for the map up to this
+
+template <typename IdxT>
+__global__ __launch_bounds__(kAttnThreads) void attention_prefix_plan_kernel(PlanArgs p) {
+    __shared__ uint32_t ue_lds[kPlanLdsSeqs];
+    const uint32_t S = p.num_seqs, P = p.page_size;
+    const bool in_lds = S <= kPlanLdsSeqs;
+    // 1. run ids and firsts from the common leading pages
+    uint32_t runs = 0;
+    for (uint32_t base = 0; base < S; base += kAttnThreads) {
+        const uint32_t s = base + threadIdx.x;
+        uint32_t lcp = 0, start = 0;
+        if (s < S) {
+            lcp = p.pre_pages[s];
+            start = (s == 0 || lcp < p.min_pages) ? 1u : 0u;
+        }
+        uint32_t tot;
+        const uint32_t before = block_exclusive_scan(start, &tot);
+        if (s < S) {
+            const uint32_t rid = runs + before + start - 1;
+            p.run_of[s] = rid;
+            if (start)
+                p.run_first[rid] = s;
+        }
+        runs += tot;
+    }
+    __syncthreads();
+    for (uint32_t r = threadIdx.x; r < runs; r += kAttnThreads)
+        p.run_c[r] = ~0u;
+    __syncthreads();
+    // 2. a run's shared pages: the smallest common count of its members
+    for (uint32_t s = threadIdx.x; s < S; s += kAttnThreads) {
+        const uint32_t rid = p.run_of[s];
+        if (p.run_first[rid] != s)
+            atomicMin(&p.run_c[rid], p.pre_pages[s]);
+    }
+    __syncthreads();
+    for (uint32_t s = threadIdx.x; s < S; s += kAttnThreads) {
+        const uint32_t cr = __hip_atomic_load(&p.run_c[p.run_of[s]], __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+        p.pre_pages[s] = cr == ~0u ? 0u : cr;
+    }
+    __syncthreads();
+    // 3. units and work items
+    uint32_t units = 0, work = 0;
+    for (uint32_t base = 0; base < S; base += kAttnThreads) {
+        const uint32_t s = base + threadIdx.x;
+        uint32_t nu = 0, nw = 0, nch = 0;
+        if (s < S) {
+            const uint32_t sh = p.pre_pages[s];
+            nch = (sh + p.chunk_pages - 1) / p.chunk_pages;
+            const uint64_t rest = ld_idx<IdxT>(p.seq_lens, s) - (uint64_t)sh * P;
+            nu = nch + (uint32_t)(rest / p.unit_tokens + (rest % p.unit_tokens != 0));
+            const uint32_t pos = s - p.run_first[p.run_of[s]];
+            if (sh && pos % p.seqs_per_block == 0)
+                nw = nch;
+        }
+        uint32_t tu, tw;
+        const uint32_t ub = block_exclusive_scan(nu, &tu);
+        const uint32_t wb = block_exclusive_scan(nw, &tw);
+        if (s < S) {
+            const uint32_t ue = min32(units + ub + nu, p.cap_units);
+            p.unit_end[s] = ue;
+            if (in_lds)
+                ue_lds[s] = ue;
+            for (uint32_t k = 0; k < nw && work + wb + k < p.cap_work; ++k) {
+                p.work_seq0[work + wb + k] = s;
+                p.work_chunk[work + wb + k] = k;
+            }
+        }
+        units += tu;
+        work += tw;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *p.nwork = min32(work, p.cap_work);
+    // 4. the unit -> sequence map (this workgroup's unit_end stores are
+    // visible to it after the barrier)
+    const uint32_t total = min32(units, p.cap_units);
+    const uint32_t *ue = in_lds ? ue_lds : p.unit_end;
+    for (uint32_t u = threadIdx.x; u < total; u += kAttnThreads) {
+        uint32_t lo = 0, hi = S - 1;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (ue[mid] > u)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        p.unit_seq[u] = lo;
     }
 }
 
@@ -954,21 +1336,31 @@ bool attention_mfma(uint32_t G, uint32_t D, bool stream) {
     return G >= min_group && (D == 64 || D == 128);
 }
 
-template <typename ET, typename IdxT, int D>
+template <typename ET, typename IdxT, int D, int R>
 hipError_t launch_attention_mfma(const AArgs &a, const AttentionShape &sh, bool nt,
                                  hipStream_t stream) {
-    const dim3 grid((uint32_t)(sh.cap_units + a.num_seqs), sh.head_groups,
-                    (a.group + kMfmaRows - 1) / kMfmaRows);
+    // shared work items (at most cap_work), units, then one spare per sequence
+    const dim3 grid((uint32_t)(sh.cap_units + a.num_seqs + (a.shared ? sh.cap_work : 0)),
+                    sh.head_groups, (a.group + kMfmaRows - 1) / kMfmaRows);
     const size_t lds = (a.fused ? ((4 * (size_t)a.num_seqs + 15) & ~(size_t)15) : 0) +
-                       ((8 * (size_t)a.unit_pages + 15) & ~(size_t)15) +
-                       kMfmaWaves * mfma_wave_lds<D>();
+                       a.pg_area + kMfmaWaves * mfma_wave_lds<D>();
     if (nt)
-        hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, true>), grid, dim3(kAttnThreads),
-                           lds, stream, a);
+        hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, true, R>), grid,
+                           dim3(kAttnThreads), lds, stream, a);
     else
-        hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, false>), grid, dim3(kAttnThreads),
-                           lds, stream, a);
+        hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, false, R>), grid,
+                           dim3(kAttnThreads), lds, stream, a);
     return hipGetLastError();
+}
+
+template <typename ET, typename IdxT, int D>
+hipError_t launch_mfma_r(const AArgs &a, const AttentionShape &sh, uint32_t G, bool nt,
+                         hipStream_t st) {
+    if (G <= 4)
+        return launch_attention_mfma<ET, IdxT, D, 1>(a, sh, nt, st);
+    if (G <= 8)
+        return launch_attention_mfma<ET, IdxT, D, 2>(a, sh, nt, st);
+    return launch_attention_mfma<ET, IdxT, D, 4>(a, sh, nt, st);
 }
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -1020,10 +1412,10 @@ hipError_t launch_attention_i(const AArgs &a, const AttentionShape &sh, uint32_t
                               bool nt, hipStream_t st) {
     if (attention_mfma(G, a.head_dim, nt)) {
         if (a.head_dim == 64)
-            return idx64 ? launch_attention_mfma<ET, uint64_t, 64>(a, sh, nt, st)
-                         : launch_attention_mfma<ET, uint32_t, 64>(a, sh, nt, st);
-        return idx64 ? launch_attention_mfma<ET, uint64_t, 128>(a, sh, nt, st)
-                     : launch_attention_mfma<ET, uint32_t, 128>(a, sh, nt, st);
+            return idx64 ? launch_mfma_r<ET, uint64_t, 64>(a, sh, G, nt, st)
+                         : launch_mfma_r<ET, uint32_t, 64>(a, sh, G, nt, st);
+        return idx64 ? launch_mfma_r<ET, uint64_t, 128>(a, sh, G, nt, st)
+                     : launch_mfma_r<ET, uint32_t, 128>(a, sh, G, nt, st);
     }
     return idx64 ? launch_attention_d<ET, uint64_t>(a, sh, G, nt, st)
                  : launch_attention_d<ET, uint32_t>(a, sh, G, nt, st);
@@ -1031,13 +1423,24 @@ hipError_t launch_attention_i(const AArgs &a, const AttentionShape &sh, uint32_t
 
 struct WsLayout {
     uint64_t unit_end, unit_seq, ml, acc, end;
+    // the prefix plan's arrays (shared-prefix pass only)
+    uint64_t pre_pages, run_of, run_first, run_c, work_seq0, work_chunk, nwork;
 };
 
-WsLayout ws_layout(uint64_t S, uint64_t Hq, uint64_t D, uint64_t cap) {
+WsLayout ws_layout(uint64_t S, uint64_t Hq, uint64_t D, const AttentionShape &sh) {
+    const uint64_t cap = sh.cap_units;
+    const uint64_t sS = sh.shared ? S : 0, sW = sh.shared ? sh.cap_work : 0;
     WsLayout w;
     w.unit_end = 256;  // the validator's words come first
     w.unit_seq = w.unit_end + align256(4 * S);
-    w.ml = w.unit_seq + align256(4 * cap);
+    w.pre_pages = w.unit_seq + align256(4 * cap);
+    w.run_of = w.pre_pages + align256(4 * sS);
+    w.run_first = w.run_of + align256(4 * sS);
+    w.run_c = w.run_first + align256(4 * sS);
+    w.work_seq0 = w.run_c + align256(4 * sS);
+    w.work_chunk = w.work_seq0 + align256(4 * sW);
+    w.nwork = w.work_chunk + align256(4 * sW);
+    w.ml = w.nwork + (sh.shared ? 256 : 0);
     w.acc = w.ml + align256(8 * cap * Hq);
     w.end = w.acc + align256(4 * cap * Hq * D);
     return w;
@@ -1087,6 +1490,19 @@ AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_
     sh.unit_pages = (uint32_t)upages;
     sh.unit_tokens = (uint32_t)(upages * page_size);
     sh.cap_units = total_tokens / sh.unit_tokens + num_seqs;
+    // The shared-prefix pass: on the matrix-core path when pages may be read
+    // more than once (no streaming hint) and there are sequences to share.
+    sh.shared = mfma && !stream_loads && num_seqs >= 2;
+    sh.chunk_pages = (kSharedChunkTokens + page_size - 1) / page_size;
+    sh.min_pages = (kMinSharedTokens + page_size - 1) / page_size;
+    sh.seqs_per_block = G <= kMfmaRows ? kMfmaRows / G : 1;
+    sh.cap_work = 0;
+    if (sh.shared) {
+        // shared chunks: at most ceil(L / chunk tokens) per sequence
+        const uint64_t chunk_tokens = (uint64_t)sh.chunk_pages * page_size;
+        sh.cap_work = total_tokens / chunk_tokens + num_seqs;
+        sh.cap_units += sh.cap_work;
+    }
     return sh;
 }
 
@@ -1096,7 +1512,7 @@ uint64_t attention_workspace_bytes(uint64_t num_seqs, uint64_t total_tokens, uin
     for (int stream = 0; stream < 2; ++stream) {
         const AttentionShape sh = attention_shape(num_seqs, total_tokens, page_size, num_kv_heads,
                                                   head_dim, num_q_heads, stream != 0);
-        const uint64_t n = ws_layout(num_seqs, num_q_heads, head_dim, sh.cap_units).end;
+        const uint64_t n = ws_layout(num_seqs, num_q_heads, head_dim, sh).end;
         need = n > need ? n : need;
     }
     return need;
@@ -1107,14 +1523,46 @@ hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
     const AttentionShape sh = attention_shape(job.num_seqs, job.total_tokens, job.page_size,
                                               job.num_kv_heads, job.head_dim, job.num_q_heads,
                                               job.stream_loads);
-    const WsLayout wl = ws_layout(job.num_seqs, job.num_q_heads, job.head_dim, sh.cap_units);
+    const WsLayout wl = ws_layout(job.num_seqs, job.num_q_heads, job.head_dim, sh);
     unsigned char *ws = static_cast<unsigned char *>(job.workspace);
     uint32_t *unit_end = reinterpret_cast<uint32_t *>(ws + wl.unit_end);
     uint32_t *unit_seq = reinterpret_cast<uint32_t *>(ws + wl.unit_seq);
+    auto at = [&](uint64_t off) { return reinterpret_cast<uint32_t *>(ws + off); };
 
-    const bool fused = job.num_seqs <= kAttnFusedSeqs;
+    const bool fused = job.num_seqs <= kAttnFusedSeqs && !sh.shared;
     hipError_t e = hipSuccess;
-    if (!fused) {
+    if (sh.shared) {
+        PlanArgs pa = {};
+        pa.block_table = job.block_table;
+        pa.seq_ptr = job.seq_ptr;
+        pa.seq_lens = job.seq_lens;
+        pa.num_seqs = job.num_seqs;
+        pa.page_size = job.page_size;
+        pa.unit_tokens = sh.unit_tokens;
+        pa.chunk_pages = sh.chunk_pages;
+        pa.min_pages = sh.min_pages;
+        pa.seqs_per_block = sh.seqs_per_block;
+        pa.cap_units = (uint32_t)sh.cap_units;
+        pa.cap_work = (uint32_t)sh.cap_work;
+        pa.unit_end = unit_end;
+        pa.unit_seq = unit_seq;
+        pa.pre_pages = at(wl.pre_pages);
+        pa.run_of = at(wl.run_of);
+        pa.run_first = at(wl.run_first);
+        pa.run_c = at(wl.run_c);
+        pa.work_seq0 = at(wl.work_seq0);
+        pa.work_chunk = at(wl.work_chunk);
+        pa.nwork = at(wl.nwork);
+        const uint32_t lcp_groups = (job.num_seqs + kAttnThreads / 64 - 1) / (kAttnThreads / 64);
+        hipLaunchKernelGGL(job.idx64 ? attention_lcp_kernel<uint64_t>
+                                     : attention_lcp_kernel<uint32_t>,
+                           dim3(lcp_groups), dim3(kAttnThreads), 0, stream, pa);
+        hipLaunchKernelGGL(job.idx64 ? attention_prefix_plan_kernel<uint64_t>
+                                     : attention_prefix_plan_kernel<uint32_t>,
+                           dim3(1), dim3(kAttnThreads), 0, stream, pa);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    } else if (!fused) {
         hipLaunchKernelGGL(job.idx64 ? attention_plan_kernel<uint64_t>
                                      : attention_plan_kernel<uint32_t>,
                            dim3(1), dim3(kAttnThreads), 0, stream, job.seq_lens, job.num_seqs,
@@ -1150,6 +1598,19 @@ hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
     a.qscale = job.scale * 1.4426950408889634f;  // log2(e)
     a.div_page = make_div(job.page_size);
     const uint32_t G = job.num_q_heads / job.num_kv_heads;
+    a.pg_area = (uint32_t)((8 * (uint64_t)(sh.shared && sh.chunk_pages > sh.unit_pages
+                                                ? sh.chunk_pages : sh.unit_pages) + 15) &
+                           ~uint64_t(15));
+    if (sh.shared) {
+        a.shared = 1;
+        a.chunk_pages = sh.chunk_pages;
+        a.seqs_per_block = sh.seqs_per_block;
+        a.pre_pages = at(wl.pre_pages);
+        a.run_of = at(wl.run_of);
+        a.work_seq0 = at(wl.work_seq0);
+        a.work_chunk = at(wl.work_chunk);
+        a.nwork = at(wl.nwork);
+    }
     e = job.bf16 ? launch_attention_i<BF16>(a, sh, G, job.idx64, job.stream_loads, stream)
                  : launch_attention_i<F16>(a, sh, G, job.idx64, job.stream_loads, stream);
     if (e != hipSuccess)

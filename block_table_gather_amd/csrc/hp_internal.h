@@ -227,6 +227,12 @@ struct AttentionShape {
     uint32_t head_groups;      // grid rows
     uint32_t unit_pages, unit_tokens;
     uint64_t cap_units;        // grid columns: units of the largest batch with total_tokens
+    // Shared-prefix pass (cached loads on the matrix-core path): pages of one
+    // shared chunk, sequences per row block, the least shared pages of a run,
+    // and the most work items the pass can have.
+    bool shared;
+    uint32_t chunk_pages, seqs_per_block, min_pages;
+    uint64_t cap_work;
 };
 
 struct AttentionJob {

@@ -360,3 +360,94 @@ def test_attention_pools_beyond_4gib(hp):
     check(w, out, q, d, v_pool, 4, 0.088, what="pools > 4 GiB")
     del d, v_pool
     torch.cuda.empty_cache()
+
+
+# ---- shared prefixes (the shared-prefix pass) ---------------------------------------------
+
+def shared_prefix_workload(seed, P, H, D, dtype, idx, runs):
+    """Runs of sequences whose slices begin with the same pages. runs: a list
+    of (sequences in the run, shared tokens, (min, max) suffix tokens); a run
+    of one is an unshared sequence. The shared tokens need not fill whole
+    pages: a partial last shared page is the run members' own page (copies of
+    the shared page's tokens are not needed: different pages, different
+    values). Pages are numbered in order of use, then permuted over the pool
+    (which holds exactly the pages used plus three spares)."""
+    rng = np.random.default_rng(seed)
+    slices, lens = [], []
+    nxt = 0
+    for n_seq, shared_tok, (lo, hi) in runs:
+        full = shared_tok // P
+        shared_pages = np.arange(nxt, nxt + full)
+        nxt += full
+        for _ in range(n_seq):
+            L = shared_tok + int(rng.integers(lo, hi + 1))
+            own = (L - full * P + P - 1) // P
+            slices.append(np.concatenate([shared_pages, np.arange(nxt, nxt + own)]))
+            nxt += own
+            lens.append(L)
+    num_pages = nxt + 3
+    perm = rng.permutation(num_pages)
+    bt = perm[np.concatenate(slices)].astype(idx)
+    sp = np.concatenate([[0], np.cumsum([len(x) for x in slices])]).astype(idx)
+    return workloads.Workload("shared", dtype, P, H, D, num_pages, idx, bt, sp,
+                              np.array(lens, dtype=idx), seed=seed)
+
+
+SHARED_CASES = [
+    # (dtype, head_dim, G, kv heads, page size, index type, runs)
+    ("bf16", 128, 4, 8, 16, np.uint32, [(12, 1024, (16, 300)), (1, 0, (5, 400)), (5, 512, (0, 40))]),
+    ("f16", 128, 8, 2, 16, np.uint64, [(7, 700, (1, 200)), (3, 64, (0, 0)), (1, 0, (1, 90))]),
+    ("bf16", 64, 3, 4, 8, np.uint32, [(11, 333, (0, 100)), (2, 256, (30, 30))]),
+    ("f16", 64, 16, 1, 16, np.uint32, [(3, 256, (0, 0)), (4, 1000, (1, 64))]),   # one sequence per block
+    ("bf16", 128, 32, 2, 16, np.uint64, [(3, 300, (1, 50)), (2, 48, (1, 50))]),   # G > 16; a run below 64 tokens
+    ("f16", 64, 5, 3, 5, np.uint32, [(9, 400, (0, 33)), (1, 0, (1, 1))]),         # odd page size
+    ("bf16", 128, 4, 4, 16, np.uint32, [(40, 2048, (1, 16))]),                    # long shared part, 8 chunks
+    ("f16", 64, 4, 1, 1, np.uint32, [(3, 9000, (0, 20)), (2, 100, (3, 9))]),      # 9,000 shared pages: past the comparison cap
+]
+
+
+@pytest.mark.parametrize("case", range(len(SHARED_CASES)))
+def test_attention_shared_prefixes(hp, case):
+    """Sequences in runs that share leading pages: with cached loads the
+    matrix-core path computes each run's shared part once per kv head and
+    chunk for several sequences at a time, the suffixes per sequence, and
+    merges them. Every sequence and query head against the oracle; the
+    streaming hint (which skips the shared pass) must give the same answer
+    within the same bound."""
+    dtype, D, G, H, P, idx, runs = SHARED_CASES[case]
+    w = shared_prefix_workload(1600 + case, P, H, D, dtype, idx, runs)
+    say("attention shared prefixes", case, w.describe(), runs)
+    d, v_pool, q = make_inputs(w, G, 1601 + case)
+    assert hp.validate(d.desc, w.total_tokens) == ("HP_OK", 0)
+    scale = 1.0 / math.sqrt(D)
+    out = run(hp, d, v_pool, q, w, scale).cpu().numpy()
+    check(w, out, q, d, v_pool, G, scale, what=f"shared {case}")
+    out_nt = run(hp, d, v_pool, q, w, scale, streaming=True).cpu().numpy()
+    check(w, out_nt, q, d, v_pool, G, scale, what=f"shared {case}, streamed")
+
+
+def test_attention_shared_exact_cases(hp):
+    """A shared part with one token's key repeated: every sequence of the run
+    whose suffix is empty and whose shared part holds identical keys gets the
+    mean of the shared values; a sequence held entirely by one shared chunk
+    is written by the shared pass directly."""
+    P, H, D, G = 16, 2, 64, 4
+    w = shared_prefix_workload(1650, P, H, D, "bf16", np.uint32, [(6, 128, (0, 0))])
+    say("attention shared exact", w.describe())
+    d, v_pool, q = make_inputs(w, G, 1651)
+    assert hp.validate(d.desc, w.total_tokens) == ("HP_OK", 0)
+    # identical keys on the shared pages: equal weights, so each output is the
+    # mean of the shared values
+    ids = np.unique(w.block_table.astype(np.int64))
+    kp = d.pool.view(torch.int16)
+    first = kp[int(ids[0]), 0].clone()
+    kp[torch.from_numpy(ids).to(DEV)] = first
+    torch.cuda.synchronize()
+    out = run(hp, d, v_pool, q, w, 0.2).cpu().numpy()
+    vals = _vals(host_bits(v_pool), "bf16").reshape(-1, H, D)
+    slots = slot_ids(w, [0])[0]
+    mean = vals[slots].mean(axis=0)  # [H, D]
+    # every weight is exactly 1: fp32 sums of L terms, then one division
+    bound = (2 * len(slots) + 8) * U * np.abs(vals[slots]).max()
+    got = out.reshape(w.num_seqs, H, G, D)
+    assert np.abs(got - mean[None, :, None, :]).max() <= bound
