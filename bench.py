@@ -476,19 +476,47 @@ def summarize_attention(trace_dir, fetch_dir, write_dir):
     (bench.py --attention-only runs) into profiles/."""
     import numpy as np
     import workloads
-    algo = {}
-    for w, group in ((workloads.decode(), 1), (workloads.prefix(), 4)):
+    dec, pre = workloads.decode(), workloads.prefix()
+    uniq = len(np.unique(pre.block_table)) * pre.page_size * pre.num_heads * pre.head_dim * 4
+
+    def algo(w, group, unique=None):
         Hq = w.num_heads * group
-        algo[w.dtype] = (w.name, 2 * w.total_tokens * w.num_heads * w.head_dim * 2
-                         + w.num_seqs * Hq * w.head_dim * 6)
+        io = w.num_seqs * Hq * w.head_dim * 6  # queries read (2 bytes), fp32 output written
+        logical = 2 * w.total_tokens * w.num_heads * w.head_dim * 2 + io
+        return logical, (unique + io if unique is not None else None)
+
+    # which workload a kernel row belongs to: the decode batch runs the vector
+    # kernel (fp16), the prefix batch the matrix-core kernel, whose last
+    # template argument is 1 with 4 query heads per kv head and 2 with 8
+    workload_of = {"attention_kernel<F16": ("decode, G = 1", algo(dec, 1)),
+                   "attention_mfma_kernel<BF16, unsigned int, 128, true, 1>":
+                       ("prefix, G = 4", algo(pre, 4, uniq)),
+                   "attention_mfma_kernel<BF16, unsigned int, 128, true, 2>":
+                       ("prefix, G = 8", algo(pre, 8, uniq))}
+
+    def match(name):
+        for k, v in workload_of.items():
+            if name.startswith(k):
+                return v
+        return None
+
     lines = ["# Kernel durations: decode attention through the block table (rocprofv3)", "",
              "Command (from the repository root, on one MI355X):", "", f"    {ATTN_TRACE_CMD}", "",
-             "The decode batch (64 sequences, 32 kv heads x 128 f16, one query head per kv",
-             "head, streaming loads) and the prefix-sharing batch (256 sequences, 8 kv heads",
-             "x 128 bf16, 32 query heads), each called 21 times. Durations in microseconds;",
-             "the combine kernel's rows are per workload (grid size).", "",
-             "| kernel | calls | avg us | min us | max us | algorithmic GB | GB/s at avg |",
-             "|---|---|---|---|---|---|---|"]
+             "Three workloads, each called 21 times: the decode batch (64 sequences, 32 kv",
+             "heads x 128 f16, one query head per kv head, streaming loads; vector kernel and",
+             "combine), and the prefix-sharing batch (256 sequences sharing 64 leading pages, 8",
+             "kv heads x 128 bf16) with 4 and with 8 query heads per kv head (cached loads:",
+             "the shared-prefix pass). A prefix call runs four kernels: the leading-page",
+             "comparison (one wave per sequence), the one-workgroup plan, the matrix-core",
+             "kernel (shared work items first in its grid, then the units over the pages after",
+             "the shared part) and the combine; the comparison and plan rows hold both prefix",
+             "workloads' calls (same grid). Durations in microseconds. Logical bytes count",
+             "every sequence's K/V rows (shared pages once per sequence); unique bytes count",
+             "each distinct page once (the least any call must read), both with the queries",
+             "read and the fp32 output written.", "",
+             "| kernel | calls | avg us | min us | max us | logical GB | unique GB | "
+             "unique GB/s at avg |",
+             "|---|---|---|---|---|---|---|---|"]
     trace = _csv_rows(trace_dir, "*kernel_trace.csv")
     groups = {}
     for r in trace:
@@ -497,13 +525,19 @@ def summarize_attention(trace_dir, fetch_dir, write_dir):
         key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]))
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     for (name, grid), ts in sorted(groups.items()):
-        gb = gbs = ""
-        if name.startswith(("attention_kernel<", "attention_mfma_kernel<")):
-            wl, nbytes = algo["bf16" if "BF16" in name else "f16"]
-            gb = f"{nbytes / 1e9:.4f}"
-            gbs = f"{nbytes / (np.mean(ts) * 1e3):.0f}"
+        lg = ug = ugs = ""
+        m = match(name)
+        if m is not None:
+            what, (logical, unique) = m
+            lg = f"{logical / 1e9:.4f} ({what})"
+            if unique is not None:
+                ug = f"{unique / 1e9:.4f}"
+                ugs = f"{unique / (np.mean(ts) * 1e3):.0f}"
+            else:
+                ug = lg.split()[0]
+                ugs = f"{logical / (np.mean(ts) * 1e3):.0f}"
         lines.append(f"| `{name}` (grid {grid}) | {len(ts)} | {np.mean(ts):.1f} | {min(ts):.1f} | "
-                     f"{max(ts):.1f} | {gb} | {gbs} |")
+                     f"{max(ts):.1f} | {lg} | {ug} | {ugs} |")
     with open(os.path.join(PROFILES, "attention_decode_prefix_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -527,11 +561,11 @@ def summarize_attention(trace_dir, fetch_dir, write_dir):
            f"    {ATTN_PMC_CMD.format(c='WRITE_SIZE', d='write')}", "",
            "Calibrated with three plain 1 GiB device copies in the same runs: bytes =",
            f"FETCH_SIZE x 1024 x {ff:.4f} and WRITE_SIZE x 1024 x {wf:.4f}. The counters see",
-           "the L2's traffic to the fabric, Infinity Cache hits included: the prefix batch's",
-           "64 shared pages are read by every sequence but mostly served by the caches.",
-           "Algorithmic bytes: every live K and V row read once (shared prefix pages once per",
-           "sequence), the queries read and the fp32 output written. The attention kernels'",
-           "writes are the per-unit partial results the combine kernel reads.", "",
+           "the L2's traffic to the fabric, Infinity Cache hits included. Algorithmic bytes:",
+           "decode, every live K and V row read once; prefix, every distinct page read once",
+           "(unique bytes); both with the queries read and the fp32 output written. The",
+           "attention kernels' writes include the per-unit partial results the combine",
+           "kernel reads.", "",
            "| kernel | read GB | write GB | algorithmic GB |", "|---|---|---|---|"]
     for key in sorted(fk):
         if key not in wk:
@@ -539,8 +573,10 @@ def summarize_attention(trace_dir, fetch_dir, write_dir):
         name = key[0]
         rb, wb = fk[key] * 1024 * ff, wk[key] * 1024 * wf
         gb = ""
-        if name.startswith(("attention_kernel<", "attention_mfma_kernel<")):
-            gb = f"{algo['bf16' if 'BF16' in name else 'f16'][1] / 1e9:.4f}"
+        m = match(name)
+        if m is not None:
+            what, (logical, unique) = m
+            gb = f"{(unique if unique is not None else logical) / 1e9:.4f} ({what})"
         out.append(f"| `{name}` (grid {key[1]}) | {rb / 1e9:.4f} | {wb / 1e9:.4f} | {gb} |")
     with open(os.path.join(PROFILES, "attention_decode_prefix_hbm_traffic.md"), "w") as f:
         f.write("\n".join(out) + "\n")

@@ -403,6 +403,7 @@ SHARED_CASES = [
     ("f16", 64, 5, 3, 5, np.uint32, [(9, 400, (0, 33)), (1, 0, (1, 1))]),         # odd page size
     ("bf16", 128, 4, 4, 16, np.uint32, [(40, 2048, (1, 16))]),                    # long shared part, 8 chunks
     ("f16", 64, 4, 1, 1, np.uint32, [(3, 9000, (0, 20)), (2, 100, (3, 9))]),      # 9,000 shared pages: past the comparison cap
+    ("bf16", 64, 4, 1, 16, np.uint32, [(100, 64, (0, 8))] * 26),                  # 2,600 sequences: the plan's arrays in the workspace
 ]
 
 
