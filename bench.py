@@ -489,6 +489,8 @@ def summarize_attention(trace_dir, fetch_dir, write_dir):
     # kernel (fp16), the prefix batch the matrix-core kernel, whose last
     # template argument is 1 with 4 query heads per kv head and 2 with 8
     workload_of = {"attention_kernel<F16": ("decode, G = 1", algo(dec, 1)),
+                   "attention_mfma_kernel<F16, unsigned int, 128, true, 1>":
+                       ("decode, G = 4", algo(dec, 4)),
                    "attention_mfma_kernel<BF16, unsigned int, 128, true, 1>":
                        ("prefix, G = 4", algo(pre, 4, uniq)),
                    "attention_mfma_kernel<BF16, unsigned int, 128, true, 2>":
@@ -502,11 +504,12 @@ def summarize_attention(trace_dir, fetch_dir, write_dir):
 
     lines = ["# Kernel durations: decode attention through the block table (rocprofv3)", "",
              "Command (from the repository root, on one MI355X):", "", f"    {ATTN_TRACE_CMD}", "",
-             "Three workloads, each called 21 times: the decode batch (64 sequences, 32 kv",
-             "heads x 128 f16, one query head per kv head, streaming loads; vector kernel and",
-             "combine), and the prefix-sharing batch (256 sequences sharing 64 leading pages, 8",
-             "kv heads x 128 bf16) with 4 and with 8 query heads per kv head (cached loads:",
-             "the shared-prefix pass). A prefix call runs four kernels: the leading-page",
+             "Four workloads, each called 21 times: the decode batch (64 sequences, 32 kv",
+             "heads x 128 f16, streaming loads) with one query head per kv head (vector kernel",
+             "and combine) and with four (matrix-core kernel and combine), and the",
+             "prefix-sharing batch (256 sequences sharing 64 leading pages, 8 kv heads x 128",
+             "bf16) with 4 and with 8 query heads per kv head (cached loads: the shared-prefix",
+             "pass). A prefix call runs four kernels: the leading-page",
              "comparison (one wave per sequence), the one-workgroup plan, the matrix-core",
              "kernel (shared work items first in its grid, then the units over the pages after",
              "the shared part) and the combine; the comparison and plan rows hold both prefix",
@@ -714,7 +717,8 @@ def attention_extras(hp, torch, np, dev, stream, reps, gqa8=False):
     batch (64 sequences, 32 kv heads x 128 fp16, one query head per kv head,
     streaming loads) and the prefix-sharing batch (256 sequences, 8 kv heads x
     128 bf16, 32 query heads, cached loads since 64 prefix pages are read by
-    every sequence); with gqa8, the prefix batch with 64 query heads too.
+    every sequence); with gqa8, the prefix batch with 64 query heads and the
+    decode batch with 128 (four per kv head, matrix cores) too.
     Algorithmic bytes: every live K and V row read once (the prefix pages once
     per sequence that uses them, as logical bytes), the queries read and the
     fp32 output written."""
@@ -724,6 +728,7 @@ def attention_extras(hp, torch, np, dev, stream, reps, gqa8=False):
              ("prefix_gqa4_bf16", workloads.prefix(), 4, False)]
     if gqa8:
         cases.append(("prefix_gqa8_bf16", workloads.prefix(), 8, False))
+        cases.append(("decode_gqa4_f16", workloads.decode(), 4, True))
     for name, w, group, streaming in cases:
         k_pool = w.make_pool(dev)
         v_pool = dataclasses.replace(w, seed=w.seed * 7 + 3).make_pool(dev)
