@@ -56,6 +56,9 @@ def _load():
     lib.oracle_validate.restype = ctypes.c_int
     lib.oracle_validate.argtypes = [ctypes.c_uint32, ctypes.c_uint32, _u64, _u64, _vp,
                                     _u64, _vp, _u64, _vp, _vp, _u64, _vp]
+    lib.oracle_disjoint_writes.restype = ctypes.c_int
+    lib.oracle_disjoint_writes.argtypes = [_u64, _u64, _vp, _vp, _u64, _vp, _vp, ctypes.c_int,
+                                           _vp]
     lib.oracle_gather.restype = None
     lib.oracle_gather.argtypes = [_vp, _u64, _u64, _u64, _u64, _vp, _vp, _vp, _u64,
                                   _vp, _vp]
@@ -130,6 +133,23 @@ def validate(*, rank, paged_axis, num_pages, page_size, block_table, seq_ptr,
                                num_seqs, _ptr(sl), _ptr(ss), total_tokens,
                                _ptr(index))
     return CHECKS[code], int(index[0])
+
+
+def disjoint_writes(*, num_pages, page_size, block_table, seq_ptr, seq_lens, seq_start=None,
+                    zero_tail=False):
+    """Whether a scatter's written slots are pairwise distinct: None if so,
+    else the smallest sequence index one of whose written slots is written
+    more than once. The descriptor must be valid."""
+    lib = _load()
+    bt, sp, sl = _idx(block_table), _idx(seq_ptr), _idx(seq_lens)
+    ss = None if seq_start is None else _idx(seq_start)
+    num_seqs = len(sp) - 1
+    assert len(sl) == num_seqs and (ss is None or len(ss) == num_seqs)
+    first = np.zeros(1, dtype=np.uint64)
+    found = lib.oracle_disjoint_writes(num_pages, page_size, _ptr(bt) if len(bt) else None,
+                                       _ptr(sp), num_seqs, _ptr(sl), _ptr(ss),
+                                       int(bool(zero_tail)), _ptr(first))
+    return int(first[0]) if found else None
 
 
 def _pool_geometry(pool, page_size, num_heads, head_dim):

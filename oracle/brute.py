@@ -76,6 +76,31 @@ def validate(rank, paged_axis, num_pages, page_size, block_table, seq_ptr, seq_l
     return fails
 
 
+def disjoint_writes(page_size, block_table, seq_ptr, seq_lens, seq_start=None,
+                    zero_tail=False):
+    """None if a scatter's written slots are pairwise distinct, else the
+    smallest sequence that writes a slot some write repeats (tokens' slots and,
+    with zero_tail, the rest of the last token's page)."""
+    writes = []
+    for s in range(len(seq_lens)):
+        start = 0 if seq_start is None else seq_start[s]
+        mine = [block_table[seq_ptr[s] + t // page_size] * page_size + t % page_size
+                for t in range(start, start + seq_lens[s])]
+        if zero_tail and seq_lens[s]:
+            last = start + seq_lens[s] - 1
+            page = block_table[seq_ptr[s] + last // page_size]
+            mine += [page * page_size + r for r in range(last % page_size + 1, page_size)]
+        writes.append(mine)
+    seen = {}
+    for mine in writes:
+        for slot in mine:
+            seen[slot] = seen.get(slot, 0) + 1
+    for s, mine in enumerate(writes):
+        if any(seen[slot] > 1 for slot in mine):
+            return s
+    return None
+
+
 def copy_pages(pool4, scales, src_pages, dst_pages):
     """Deep copy of pool4 (and of the flat scales list) with page dst_pages[i]
     replaced by page src_pages[i], applied in order."""

@@ -115,6 +115,76 @@ int oracle_validate(uint32_t rank, uint32_t paged_axis, uint64_t num_pages,
     return ORACLE_VALID;
 }
 
+/* Visits the slots sequence s writes in a scatter: its tokens' slots, then,
+ * with zero_tail, the slots after the last token in that token's page. */
+static void written_slots(uint64_t page_size, const uint64_t *block_table,
+                          const uint64_t *seq_ptr, const uint64_t *seq_lens,
+                          const uint64_t *seq_start, int zero_tail, uint64_t s,
+                          void (*visit)(uint64_t slot, void *ctx), void *ctx)
+{
+    uint64_t start = seq_start ? seq_start[s] : 0;
+    uint64_t t, r;
+    for (t = start; t < start + seq_lens[s]; t++)
+        visit(block_table[seq_ptr[s] + t / page_size] * page_size + t % page_size, ctx);
+    if (zero_tail && seq_lens[s] > 0) {
+        uint64_t last = start + seq_lens[s] - 1;
+        uint64_t page = block_table[seq_ptr[s] + last / page_size];
+        for (r = last % page_size + 1; r < page_size; r++)
+            visit(page * page_size + r, ctx);
+    }
+}
+
+static void count_write(uint64_t slot, void *ctx)
+{
+    unsigned char *count = (unsigned char *)ctx;
+    if (count[slot] < 2)
+        count[slot]++;
+}
+
+struct shared_probe {
+    const unsigned char *count;
+    int hit;
+};
+
+static void probe_write(uint64_t slot, void *ctx)
+{
+    struct shared_probe *p = (struct shared_probe *)ctx;
+    if (p->count[slot] >= 2)
+        p->hit = 1;
+}
+
+/* [Hurray] Prefix Sharing and Partial trailing page: count the writes of
+ * every slot over all sequences, then find the first sequence that writes a
+ * slot counted twice. */
+int oracle_disjoint_writes(uint64_t num_pages, uint64_t page_size,
+                           const uint64_t *block_table, const uint64_t *seq_ptr,
+                           uint64_t num_seqs, const uint64_t *seq_lens,
+                           const uint64_t *seq_start, int zero_tail,
+                           uint64_t *first_out)
+{
+    unsigned char *count = (unsigned char *)calloc(num_pages * page_size + 1, 1);
+    uint64_t s;
+    int found = 0;
+
+    *first_out = 0;
+    if (!count)
+        abort();
+    for (s = 0; s < num_seqs; s++)
+        written_slots(page_size, block_table, seq_ptr, seq_lens, seq_start, zero_tail, s,
+                      count_write, count);
+    for (s = 0; s < num_seqs && !found; s++) {
+        struct shared_probe p = {count, 0};
+        written_slots(page_size, block_table, seq_ptr, seq_lens, seq_start, zero_tail, s,
+                      probe_write, &p);
+        if (p.hit) {
+            *first_out = s;
+            found = 1;
+        }
+    }
+    free(count);
+    return found;
+}
+
 /* Gather in logical order: sequence by sequence, token by token, head by
  * head, dimension by dimension ([Hurray] Logical Shape, Element Lookup). Only
  * tokens t < L_s are visited, so no slot past a sequence's count is read

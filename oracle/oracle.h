@@ -62,6 +62,22 @@ int oracle_validate(uint32_t rank, uint32_t paged_axis, uint64_t num_pages,
                     const uint64_t *seq_start, uint64_t total_tokens,
                     uint64_t *index_out);
 
+/* Whether a scatter's writes land in distinct slots ([Hurray] Prefix Sharing:
+ * slices may name the same page, so two written rows, or a row and a zeroed
+ * tail slot, can share a slot; a scatter is defined only when they do not).
+ * The written slots of sequence s are those of tokens seq_start[s] ..
+ * seq_start[s] + seq_lens[s] - 1 and, with zero_tail and seq_lens[s] > 0, the
+ * slots after the last of them in its page ([Hurray] Partial trailing page).
+ * Returns 1 and writes to *first_out the smallest s one of whose written
+ * slots is written more than once (by any sequence, itself included), or
+ * returns 0 when every written slot is written once. The descriptor must
+ * pass oracle_validate with the same seq_start. seq_start may be NULL. */
+int oracle_disjoint_writes(uint64_t num_pages, uint64_t page_size,
+                           const uint64_t *block_table, const uint64_t *seq_ptr,
+                           uint64_t num_seqs, const uint64_t *seq_lens,
+                           const uint64_t *seq_start, int zero_tail,
+                           uint64_t *first_out);
+
 /* Gather: the logical [total_tokens, H, D] tensor, sequences concatenated in
  * index order, token t of sequence s at row (sum of earlier counts) + t.
  * A bit copy of elem_bytes per element. If slot_read_mark is not NULL it has

@@ -204,6 +204,97 @@ def test_validator_scatter_window():
     assert oracle.validate(**args, seq_start=[6, 0, 0]) == ("seq_len", 0)
 
 
+# ---- disjoint writes (a scatter's destinations) ------------------------------
+
+def _dw(P, bt, sp, lens, starts=None, zero_tail=False, N=None):
+    """Oracle and brute force together (they must agree)."""
+    N = (max(bt) + 1) if N is None else N
+    got = oracle.disjoint_writes(num_pages=N, page_size=P, block_table=bt, seq_ptr=sp,
+                                 seq_lens=lens, seq_start=starts, zero_tail=zero_tail)
+    assert got == brute.disjoint_writes(P, bt, sp, lens, starts, zero_tail)
+    return got
+
+
+def test_disjoint_writes_hurray_example():
+    """[Hurray] Example read as a scatter: sequence 1's slice names page 0,
+    which sequence 0 fills too, so both write slots 0-2 of page 0: sequence 0
+    is the first whose writes repeat. Writing only page 1 (sequence 0's
+    tokens 4-5) and page 0 (sequence 1) is disjoint."""
+    g = golden("hurray_example.json")
+    P, bt, sp, lens = g["page_size"], g["block_table"], g["seq_ptr"], g["seq_lens"]
+    assert _dw(P, bt, sp, lens, N=g["num_pages"]) == 0
+    assert _dw(P, bt, sp, [2, 3], starts=[4, 0], N=g["num_pages"]) is None
+    # with the tails zeroed, page 1's slots 2-3 are sequence 0's alone, but
+    # sequence 1's tail (slot 3 of page 0) is sequence 0's token 3 only when
+    # sequence 0 writes page 0
+    assert _dw(P, bt, sp, [2, 3], starts=[4, 0], zero_tail=True, N=g["num_pages"]) is None
+    assert _dw(P, bt, sp, [6, 3], zero_tail=True, N=g["num_pages"]) == 0
+
+
+def test_disjoint_writes_prefix_sharing_slices():
+    """[Hurray] Prefix Sharing slices [12,5,7,9] and [12,5,7,3]: writing both
+    sequences' full slices writes pages 12, 5 and 7 twice; appending to the
+    private last pages only (start 3 P) is disjoint."""
+    g = golden("hurray_prefix_sharing.json")
+    P = 2
+    bt = g["slices"][0] + g["slices"][1]
+    sp = [0, 4, 8]
+    assert _dw(P, bt, sp, [4 * P, 4 * P], N=16) == 0
+    assert _dw(P, bt, sp, [P, P], starts=[3 * P, 3 * P], N=16) is None
+    assert _dw(P, bt, sp, [1, 1], starts=[3 * P, 3 * P], zero_tail=True, N=16) is None
+
+
+def test_disjoint_writes_through_the_tail_only():
+    """Two windows of one page: tokens 0-1 (sequence 0) and 2-3 (sequence 1)
+    are disjoint, but zeroing sequence 0's tail writes slots 2-3 again."""
+    bt, sp = [5, 5], [0, 1, 2]
+    assert _dw(4, bt, sp, [2, 2], starts=[0, 2]) is None
+    assert _dw(4, bt, sp, [2, 2], starts=[0, 2], zero_tail=True) == 0
+    # swapped windows: sequence 0's last token ends the page (no tail), and
+    # sequence 1's tail rewrites sequence 0's slots, so 0 is still the first
+    # sequence with a repeated slot
+    assert _dw(4, bt, sp, [2, 2], starts=[2, 0]) is None
+    assert _dw(4, bt, sp, [2, 2], starts=[2, 0], zero_tail=True) == 0
+
+
+def test_disjoint_writes_page_repeated_in_one_slice():
+    """A slice that names page 3 twice writes its slots twice by itself."""
+    assert _dw(4, [1, 3, 3], [0, 1, 3], [4, 8]) == 1
+    assert _dw(4, [1, 3, 3], [0, 1, 3], [4, 4]) is None  # only the first page written
+
+
+def test_disjoint_writes_reports_the_smallest_sequence():
+    """Sequences 2 and 5 share page 7; the others are disjoint: 2."""
+    bt = [0, 1, 7, 3, 4, 7]
+    sp = list(range(7))
+    assert _dw(4, bt, sp, [4] * 6) == 2
+    assert _dw(4, bt, sp, [4, 4, 4, 4, 4, 0]) is None
+
+
+def test_disjoint_writes_brute_force():
+    """Random tiny scatters with aliased slices, start offsets and both tail
+    modes: the oracle agrees with the brute force (_dw asserts it)."""
+    rng = np.random.default_rng(77)
+    found = clean = 0
+    for _ in range(400):
+        P = int(rng.integers(1, 5))
+        N = int(rng.integers(1, 7))
+        S = int(rng.integers(1, 6))
+        counts = rng.integers(0, 4, size=S)
+        bt = [int(x) for x in rng.integers(0, N, size=int(counts.sum()))]
+        sp = [0] + [int(x) for x in np.cumsum(counts)]
+        lens, starts = [], []
+        for c in counts:
+            L = int(rng.integers(0, c * P + 1))
+            lens.append(L)
+            starts.append(int(rng.integers(0, c * P - L + 1)))
+        for zt in (False, True):
+            r = _dw(P, bt, sp, lens, starts, zt, N=N)
+            found += r is not None
+            clean += r is None
+    assert found > 100 and clean > 100
+
+
 # ---- byte accounting ---------------------------------------------------------
 
 def test_rust20_payload():
