@@ -22,7 +22,8 @@ import os
 import torch  # noqa: F401,E402
 
 __all__ = ["Descriptor", "HpError", "gather", "scatter", "gather_dequant", "validate",
-           "validate_async", "validate_verdict", "gather_static",
+           "validate_async", "validate_verdict", "gather_static", "validate_writes",
+           "disjoint_workspace_bytes",
            "gather_dequant_q", "QUANT_SCHEME", "paged_attention", "attention_workspace_bytes",
            "scatter_quant",
            "gather_batch", "scatter_batch", "gather_dequant_batch", "copy_pages",
@@ -60,12 +61,13 @@ STATUS = {
     5: "HP_ERR_INDEX_TYPE", 6: "HP_ERR_DTYPE", 7: "HP_ERR_ALIGN", 8: "HP_ERR_WORKSPACE",
     9: "HP_ERR_SHARDED", 10: "HP_ERR_QUANT", 16: "HP_ERR_SEQPTR_FIRST", 17: "HP_ERR_SEQPTR_LAST",
     18: "HP_ERR_SEQPTR_ORDER", 19: "HP_ERR_PAGE_RANGE", 20: "HP_ERR_SEQ_LEN",
-    21: "HP_ERR_TOTAL_TOKENS", 32: "HP_ERR_HIP",
+    21: "HP_ERR_TOTAL_TOKENS", 22: "HP_ERR_WRITE_ALIAS", 32: "HP_ERR_HIP",
 }
 CODE = {v: k for k, v in STATUS.items()}
 HP_INDEX_U32, HP_INDEX_U64 = 0x00, 0x01
 DTYPE = {"i8": 1, "u8": 2, "f16": 3, "bf16": 4, "f32": 5, "f64": 6}
 HP_FLAG_CHECKED, HP_FLAG_ZERO_TAIL, HP_FLAG_STREAM, HP_FLAG_GATED = 1, 2, 4, 8
+HP_FLAG_DISJOINT = 16
 # Quantization scheme tags (include/hp.h, HP_QUANT_*).
 QUANT_SCHEME = {"per_tensor": 0x01, "per_channel": 0x02, "per_block_affine": 0x03}
 
@@ -109,6 +111,11 @@ _lib.hp_validate.restype = ctypes.c_int
 _lib.hp_validate.argtypes = [_P, _vp, _vp, _sz, ctypes.POINTER(HpValidateResult), _vp]
 _lib.hp_validate_async.restype = ctypes.c_int
 _lib.hp_validate_async.argtypes = [_P, _vp, _vp, _sz, _vp]
+_lib.hp_validate_writes.restype = ctypes.c_int
+_lib.hp_validate_writes.argtypes = [_P, _vp, _u32, _vp, _sz, ctypes.POINTER(HpValidateResult),
+                                    _vp]
+_lib.hp_disjoint_workspace_bytes.restype = _sz
+_lib.hp_disjoint_workspace_bytes.argtypes = [_P]
 _lib.hp_validate_verdict.restype = ctypes.c_int
 _lib.hp_validate_verdict.argtypes = [_P, _vp, ctypes.POINTER(HpValidateResult)]
 _lib.hp_gather_static.restype = ctypes.c_int
@@ -291,10 +298,15 @@ def _own_workspace(n, device, stream):
     return ws
 
 
-def _workspace(desc, total_tokens, workspace, stream=None):
+def disjoint_workspace_bytes(desc, total_tokens=0):
+    """Workspace bytes of validate_writes and of scatters with disjoint=True."""
+    return int(_lib.hp_disjoint_workspace_bytes(desc.with_tokens(total_tokens)))
+
+
+def _workspace(desc, total_tokens, workspace, stream=None, disjoint=False):
     if workspace is not None:
         return workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    n = workspace_bytes(desc, total_tokens)
+    n = (disjoint_workspace_bytes if disjoint else workspace_bytes)(desc, total_tokens)
     if n == 0:
         return None, 0
     ws = _own_workspace(n, desc.device, stream)
@@ -324,6 +336,23 @@ def validate(desc, total_tokens, seq_start=None, *, workspace=None, stream=None,
     return name, int(res.index)
 
 
+def validate_writes(desc, total_tokens, seq_start=None, *, zero_tail=False, workspace=None,
+                    stream=None):
+    """Runs hp_validate_writes: the descriptor's checks, then whether a
+    scatter with these starts (and tail zeroing) writes every slot at most
+    once. Returns (status name, index); HP_ERR_WRITE_ALIAS names the smallest
+    clashing sequence. Synchronous."""
+    p = desc.with_tokens(total_tokens)
+    ws, n = _workspace(desc, total_tokens, workspace, stream, disjoint=True)
+    res = HpValidateResult()
+    code = _lib.hp_validate_writes(p, _ptr(seq_start), HP_FLAG_ZERO_TAIL if zero_tail else 0,
+                                   ws, n, ctypes.byref(res), _stream(stream, desc.device))
+    name = STATUS.get(code, str(code))
+    if name == "HP_ERR_HIP":
+        raise HpError(code, "hp_validate_writes")
+    return name, int(res.index)
+
+
 def validate_async(desc, total_tokens, seq_start=None, *, workspace, stream=None):
     """Enqueues hp_validate_async: the verdict stays in the first 16 bytes of
     `workspace` (a device tensor of at least 256 bytes), where moves called
@@ -349,7 +378,8 @@ def _flags(checked=False, gated=False, **named):
     f = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_GATED if gated else 0)
     for name, on in named.items():
         if on:
-            f |= {"streaming": HP_FLAG_STREAM, "zero_tail": HP_FLAG_ZERO_TAIL}[name]
+            f |= {"streaming": HP_FLAG_STREAM, "zero_tail": HP_FLAG_ZERO_TAIL,
+                  "disjoint": HP_FLAG_DISJOINT}[name]
     return f
 
 
@@ -378,12 +408,14 @@ def gather_static(desc, out, *, checked=False, streaming=False, stream=None):
 
 
 def scatter(desc, src, seq_start=None, *, zero_tail=False, checked=False, workspace=None,
-            stream=None, gated=False):
-    """Writes src[T, H, D] (T = src.shape[0]) into the pool."""
+            stream=None, gated=False, disjoint=False):
+    """Writes src[T, H, D] (T = src.shape[0]) into the pool. disjoint: checked,
+    and also rejected (HP_ERR_WRITE_ALIAS, nothing written) when two writes
+    would land in one slot."""
     T = src.shape[0]
     p = desc.with_tokens(T)
-    ws, n = _workspace(desc, T, workspace, stream)
-    flags = _flags(checked, gated, zero_tail=zero_tail)
+    ws, n = _workspace(desc, T, workspace, stream, disjoint)
+    flags = _flags(checked or disjoint, gated, zero_tail=zero_tail, disjoint=disjoint)
     _check(_lib.hp_scatter(p, _ptr(src), _ptr(seq_start), ws, n, flags,
                            _stream(stream, desc.device)), "hp_scatter")
 
@@ -418,14 +450,15 @@ def gather_dequant_q(desc, out, scheme, scales, *, axis=0, block_size=None, zero
 
 
 def scatter_quant(desc, src, seq_start=None, *, zero_points=None, zero_tail=False,
-                  checked=False, workspace=None, stream=None, gated=False):
+                  checked=False, workspace=None, stream=None, gated=False, disjoint=False):
     """Quantizes src[T, H, D] (f16, bf16 or f32) into desc's int8 pool
     (symmetric) or uint8 pool (asymmetric, with zero_points: uint8 per slot),
-    writing each written slot's scale into desc.scales."""
+    writing each written slot's scale into desc.scales. disjoint: as in
+    scatter."""
     T = src.shape[0]
     p = desc.with_tokens(T)
-    ws, n = _workspace(desc, T, workspace, stream)
-    flags = _flags(checked, gated, zero_tail=zero_tail)
+    ws, n = _workspace(desc, T, workspace, stream, disjoint)
+    flags = _flags(checked or disjoint, gated, zero_tail=zero_tail, disjoint=disjoint)
     _check(_lib.hp_scatter_quant(p, _ptr(src), _dtype_code(src), _ptr(zero_points),
                                  _ptr(seq_start), ws, n, flags, _stream(stream, desc.device)),
            "hp_scatter_quant")
@@ -483,13 +516,13 @@ def gather_batch(desc, pools, outs, *, checked=False, streaming=False, workspace
 
 
 def scatter_batch(desc, pools, srcs, seq_start=None, *, zero_tail=False, checked=False,
-                  workspace=None, stream=None, gated=False):
+                  workspace=None, stream=None, gated=False, disjoint=False):
     """Writes srcs[i][T, H, D] into pools[i] through desc's table."""
     T = srcs[0].shape[0] if len(srcs) else 0
     p = desc.with_tokens(T)
-    ws, n = _workspace(desc, T, workspace, stream)
+    ws, n = _workspace(desc, T, workspace, stream, disjoint)
     pa, sa = _ptr_array(pools), _ptr_array(srcs)
-    flags = _flags(checked, gated, zero_tail=zero_tail)
+    flags = _flags(checked or disjoint, gated, zero_tail=zero_tail, disjoint=disjoint)
     _check(_lib.hp_scatter_batch(p, len(pools), pa, sa, _ptr(seq_start), ws, n, flags,
                                  _stream(stream, desc.device)), "hp_scatter_batch")
 

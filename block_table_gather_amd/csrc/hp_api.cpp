@@ -200,6 +200,48 @@ hp_status run_validate(const hp_desc *d, const void *seq_start, void *ws,
     return decode_verdict(host, d->total_tokens, res);
 }
 
+// Bytes hp_validate_writes needs: the validator's words, the answer and the
+// two slot bitmaps, and never less than a move's workspace.
+uint64_t disjoint_bytes(const hp_desc *d) {
+    const uint64_t a = hp::disjoint_workspace_bytes(d->num_pages, d->page_size);
+    const uint64_t b = kValidateBytes + plan_bytes(d);
+    return a > b ? a : b;
+}
+
+// Write-disjointness on a validated descriptor: HP_ERR_WRITE_ALIAS with the
+// smallest clashing sequence, or HP_OK. Synchronous.
+hp_status run_disjoint(const hp_desc *d, const void *seq_start, bool zero_tail, void *ws,
+                       hp_validate_result *res, hipStream_t stream) {
+    hp::DisjointJob j;
+    j.idx64 = d->index_type == HP_INDEX_U64;
+    j.zero_tail = zero_tail;
+    j.num_pages = d->num_pages;
+    j.page_size = d->page_size;
+    j.num_seqs = d->num_seqs;
+    j.block_table = d->block_table;
+    j.seq_ptr = d->seq_ptr;
+    j.seq_lens = d->seq_lens;
+    j.seq_start = seq_start;
+    j.workspace = ws;
+    hipError_t e = hp::launch_disjoint(j, stream);
+    if (e != hipSuccess)
+        return hip_failed(e);
+    uint64_t answer = 0;
+    if ((e = hipMemcpyAsync(&answer, static_cast<unsigned char *>(ws) + hp::kDisjointAnswer,
+                            sizeof answer, hipMemcpyDeviceToHost, stream)) != hipSuccess)
+        return hip_failed(e);
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess)
+        return hip_failed(e);
+    res->code = HP_OK;
+    res->reserved = 0;
+    res->index = 0;
+    if (answer != ~0ull) {
+        res->code = HP_ERR_WRITE_ALIAS;
+        res->index = answer;
+    }
+    return (hp_status)res->code;
+}
+
 // Largest divisor of P whose run of rows fits the target unit size (at least
 // 1, at most `cap`).
 uint32_t rows_per_unit(uint32_t P, uint64_t row_bytes, uint64_t unit_bytes, uint32_t cap) {
@@ -344,13 +386,18 @@ hp_status prologue(const hp_desc *d, const Geometry &g, uint32_t flags, uint32_t
         return HP_ERR_ARG;
     const bool checked = flags & HP_FLAG_CHECKED;
     const bool gated = flags & HP_FLAG_GATED;
+    const bool disjoint = flags & HP_FLAG_DISJOINT;
     if (checked && gated)
         return HP_ERR_ARG;  // one of the two ways of validating
+    if (disjoint && !checked)
+        return HP_ERR_ARG;  // the clash check runs after the synchronous validation
     if (!aligned(seq_start, g.idx_bytes))
         return HP_ERR_ALIGN;
     const bool fused = d->num_seqs <= hp::kFusedMaxSeqs;
-    const uint64_t need = !fused ? kValidateBytes + plan_bytes(d)
-                                 : ((checked || gated) ? kValidateBytes : 0);
+    uint64_t need = !fused ? kValidateBytes + plan_bytes(d)
+                           : ((checked || gated) ? kValidateBytes : 0);
+    if (disjoint)
+        need = disjoint_bytes(d);
     hp_status st = check_workspace(ws, ws_bytes, need);
     if (st != HP_OK)
         return st;
@@ -358,6 +405,11 @@ hp_status prologue(const hp_desc *d, const Geometry &g, uint32_t flags, uint32_t
         hp_validate_result r;
         st = run_validate(d, seq_start, ws, &r, stream);
         if (st != HP_OK)
+            return st;
+        // the bitmaps share the plan's part of the workspace: the host has
+        // waited for the check before the move is enqueued
+        if (disjoint && (st = run_disjoint(d, seq_start, flags & HP_FLAG_ZERO_TAIL, ws, &r,
+                                           stream)) != HP_OK)
             return st;
     }
     *done = d->num_seqs == 0 || d->total_tokens == 0;
@@ -535,6 +587,39 @@ size_t hp_workspace_bytes(const hp_desc *desc) {
     return (size_t)(kValidateBytes + plan_bytes(desc));
 }
 
+size_t hp_disjoint_workspace_bytes(const hp_desc *desc) {
+    Geometry g;
+    if (check_desc(desc, &g) != HP_OK)
+        return 0;
+    return (size_t)disjoint_bytes(desc);
+}
+
+hp_status hp_validate_writes(const hp_desc *desc, const void *seq_start, uint32_t flags,
+                             void *workspace, size_t workspace_bytes,
+                             hp_validate_result *result, void *stream) {
+    hp_validate_result local;
+    hp_validate_result *res = result ? result : &local;
+    res->code = HP_OK;
+    res->reserved = 0;
+    res->index = 0;
+    Geometry g;
+    hp_status st = check_desc(desc, &g);
+    if (st == HP_OK && (flags & ~(uint32_t)HP_FLAG_ZERO_TAIL))
+        st = HP_ERR_ARG;
+    if (st == HP_OK && !aligned(seq_start, g.idx_bytes))
+        st = HP_ERR_ALIGN;
+    if (st == HP_OK)
+        st = check_workspace(workspace, workspace_bytes, disjoint_bytes(desc));
+    if (st != HP_OK) {
+        res->code = st;
+        return st;
+    }
+    if ((st = run_validate(desc, seq_start, workspace, res, (hipStream_t)stream)) != HP_OK)
+        return st;
+    return run_disjoint(desc, seq_start, flags & HP_FLAG_ZERO_TAIL, workspace, res,
+                        (hipStream_t)stream);
+}
+
 hp_status hp_validate(const hp_desc *desc, const void *seq_start, void *workspace,
                       size_t workspace_bytes, hp_validate_result *result, void *stream) {
     hp_validate_result local;
@@ -644,8 +729,8 @@ hp_status hp_scatter(const hp_desc *desc, const void *src, const void *seq_start
         return HP_ERR_ALIGN;
     if (overlaps(src, desc->total_tokens * g.row_bytes, desc->page_pool, g.pool_bytes))
         return HP_ERR_ARG;
-    st = prologue(desc, g, flags, HP_FLAG_CHECKED | HP_FLAG_ZERO_TAIL, seq_start, workspace,
-                  workspace_bytes, (hipStream_t)stream, &done);
+    st = prologue(desc, g, flags, HP_FLAG_CHECKED | HP_FLAG_ZERO_TAIL | HP_FLAG_DISJOINT,
+                  seq_start, workspace, workspace_bytes, (hipStream_t)stream, &done);
     if (st != HP_OK || done)
         return st;
     void *pool = desc->page_pool;
@@ -692,8 +777,8 @@ hp_status hp_scatter_quant(const hp_desc *desc, const void *src, uint32_t src_dt
             if (overlaps(written[i], wbytes[i], written[k], wbytes[k]))
                 return HP_ERR_ARG;
     }
-    st = prologue(desc, g, flags, HP_FLAG_CHECKED | HP_FLAG_ZERO_TAIL, seq_start, workspace,
-                  workspace_bytes, (hipStream_t)stream, &done);
+    st = prologue(desc, g, flags, HP_FLAG_CHECKED | HP_FLAG_ZERO_TAIL | HP_FLAG_DISJOINT,
+                  seq_start, workspace, workspace_bytes, (hipStream_t)stream, &done);
     if (st != HP_OK || done)
         return st;
     const bool zero_tail = (flags & HP_FLAG_ZERO_TAIL) != 0;
@@ -812,8 +897,8 @@ hp_status hp_scatter_batch(const hp_desc *desc, uint32_t count, void *const *poo
     hp_status st = check_batch(desc, count, pools, rows, nullptr, false, false, &d, &g);
     if (st != HP_OK)
         return st;
-    st = prologue(&d, g, flags, HP_FLAG_CHECKED | HP_FLAG_ZERO_TAIL, seq_start, workspace,
-                  workspace_bytes, (hipStream_t)stream, &done);
+    st = prologue(&d, g, flags, HP_FLAG_CHECKED | HP_FLAG_ZERO_TAIL | HP_FLAG_DISJOINT,
+                  seq_start, workspace, workspace_bytes, (hipStream_t)stream, &done);
     if (st != HP_OK || done)
         return st;
     const Members m = {count, pools, rows, nullptr};
@@ -1041,6 +1126,7 @@ const char *hp_status_str(int status) {
     case HP_ERR_PAGE_RANGE: return "HP_ERR_PAGE_RANGE: page ID out of range";
     case HP_ERR_SEQ_LEN: return "HP_ERR_SEQ_LEN: token count exceeds the sequence's pages";
     case HP_ERR_TOTAL_TOKENS: return "HP_ERR_TOTAL_TOKENS: seq_lens do not sum to total_tokens";
+    case HP_ERR_WRITE_ALIAS: return "HP_ERR_WRITE_ALIAS: a scatter would write a slot twice";
     case HP_ERR_HIP: return "HP_ERR_HIP: HIP runtime or launch failure";
     default: return "unknown hp_status";
     }

@@ -193,6 +193,25 @@ struct ValidateJob {
     void *result;
 };
 constexpr uint64_t kValidateOneItems = 1 << 16;
+
+// Write-disjointness of a scatter, on a descriptor that passed validation.
+// Workspace: [kDisjointAnswer, +8) the smallest clashing sequence (all ones
+// when none), then from kDisjointBitmaps two bitmaps of num_pages * page_size
+// bits (32-bit words).
+struct DisjointJob {
+    bool idx64, zero_tail;
+    uint64_t num_pages, page_size, num_seqs;
+    const void *block_table, *seq_ptr, *seq_lens, *seq_start;
+    void *workspace;
+};
+constexpr uint64_t kDisjointAnswer = 256;
+constexpr uint64_t kDisjointBitmaps = 512;
+inline uint64_t disjoint_words(uint64_t num_pages, uint64_t page_size) {
+    return (num_pages * page_size + 31) / 32;
+}
+inline uint64_t disjoint_workspace_bytes(uint64_t num_pages, uint64_t page_size) {
+    return kDisjointBitmaps + 8 * disjoint_words(num_pages, page_size);
+}
 // True when launch_validate writes the words to job.result itself.
 inline bool validate_writes_result(const ValidateJob &job) {
     const uint64_t n = job.num_block_entries > job.num_seqs + 1 ? job.num_block_entries
@@ -264,6 +283,7 @@ constexpr bool plan_preferred(Op op, uint64_t num_seqs) {
 
 hipError_t launch_copy(const CopyJob &job, hipStream_t stream);
 hipError_t launch_validate(const ValidateJob &job, hipStream_t stream);
+hipError_t launch_disjoint(const DisjointJob &job, hipStream_t stream);
 hipError_t launch_copy_pages(const PageCopyJob &job, hipStream_t stream);
 hipError_t launch_check_pages(const PageCheckJob &job, hipStream_t stream);
 

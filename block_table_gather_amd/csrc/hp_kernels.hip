@@ -1634,6 +1634,120 @@ hipError_t launch_check_pages(const PageCheckJob &job, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---- write-disjointness of a scatter ----------------------------------------------
+//
+// [Hurray] Prefix Sharing lets slices name the same page, so a scatter's rows
+// (or a row and a zeroed tail slot, [Hurray] Partial trailing page) can land
+// in one slot, and the result would then depend on the order of the writes.
+// On a descriptor that passed validation (every slot it names lies in the
+// pool) one pass marks each written slot in a bitmap of num_pages *
+// page_size bits and sets a second bitmap's bit for a slot it marks again;
+// a second pass takes the smallest sequence that writes a slot of the second
+// bitmap. A workgroup walks one sequence at a time.
+
+struct DArgs {
+    const void *block_table, *seq_ptr, *seq_lens, *seq_start;
+    uint32_t *seen, *twice;          // num_pages * page_size bits each
+    unsigned long long *answer;      // smallest clashing sequence, all ones if none
+    uint64_t page_size, num_seqs, words;
+    uint32_t zero_tail;
+};
+
+constexpr uint32_t kDisjointThreads = 256;
+
+__global__ __launch_bounds__(kDisjointThreads) void disjoint_clear_kernel(DArgs a) {
+    const uint64_t stride = (uint64_t)gridDim.x * kDisjointThreads;
+    for (uint64_t i = (uint64_t)blockIdx.x * kDisjointThreads + threadIdx.x; i < a.words;
+         i += stride) {
+        a.seen[i] = 0;
+        a.twice[i] = 0;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        *a.answer = ~0ull;
+}
+
+// f(slot) for every slot sequence s writes, spread over the workgroup's
+// threads: its tokens' slots, then (zero_tail) the rest of the last token's page.
+template <typename IdxT, typename F>
+__device__ __forceinline__ void for_written_slots(const DArgs &a, uint64_t s, F &&f) {
+    const uint64_t P = a.page_size;
+    const uint64_t start = a.seq_start ? ld_idx<IdxT>(a.seq_start, s) : 0;
+    const uint64_t L = ld_idx<IdxT>(a.seq_lens, s);
+    const uint64_t base = ld_idx<IdxT>(a.seq_ptr, s);
+    for (uint64_t i = threadIdx.x; i < L; i += kDisjointThreads) {
+        const uint64_t t = start + i;
+        f(ld_idx<IdxT>(a.block_table, base + t / P) * P + t % P);
+    }
+    if (a.zero_tail && L > 0) {
+        const uint64_t last = start + L - 1;
+        const uint64_t page = ld_idx<IdxT>(a.block_table, base + last / P);
+        for (uint64_t r = last % P + 1 + threadIdx.x; r < P; r += kDisjointThreads)
+            f(page * P + r);
+    }
+}
+
+template <typename IdxT>
+__global__ __launch_bounds__(kDisjointThreads) void disjoint_mark_kernel(DArgs a) {
+    for (uint64_t s = blockIdx.x; s < a.num_seqs; s += gridDim.x)
+        for_written_slots<IdxT>(a, s, [&](uint64_t slot) {
+            const uint32_t bit = 1u << (slot & 31);
+            if (atomicOr(&a.seen[slot >> 5], bit) & bit)
+                atomicOr(&a.twice[slot >> 5], bit);
+        });
+}
+
+template <typename IdxT>
+__global__ __launch_bounds__(kDisjointThreads) void disjoint_find_kernel(DArgs a) {
+    for (uint64_t s = blockIdx.x; s < a.num_seqs; s += gridDim.x) {
+        bool hit = false;
+        for_written_slots<IdxT>(a, s, [&](uint64_t slot) {
+            hit |= ((a.twice[slot >> 5] >> (slot & 31)) & 1u) != 0;
+        });
+        if (hit)
+            atomicMin(a.answer, (unsigned long long)s);
+    }
+}
+
+hipError_t launch_disjoint(const DisjointJob &job, hipStream_t stream) {
+    DArgs a;
+    unsigned char *ws = static_cast<unsigned char *>(job.workspace);
+    a.block_table = job.block_table;
+    a.seq_ptr = job.seq_ptr;
+    a.seq_lens = job.seq_lens;
+    a.seq_start = job.seq_start;
+    a.words = disjoint_words(job.num_pages, job.page_size);
+    a.seen = reinterpret_cast<uint32_t *>(ws + kDisjointBitmaps);
+    a.twice = a.seen + a.words;
+    a.answer = reinterpret_cast<unsigned long long *>(ws + kDisjointAnswer);
+    a.page_size = job.page_size;
+    a.num_seqs = job.num_seqs;
+    a.zero_tail = job.zero_tail;
+    (void)hipGetLastError();  // see launch_copy
+    uint64_t clear = (a.words + kDisjointThreads - 1) / kDisjointThreads;
+    clear = clear < 1 ? 1 : clear > 4096 ? 4096 : clear;
+    hipLaunchKernelGGL(disjoint_clear_kernel, dim3((uint32_t)clear), dim3(kDisjointThreads), 0,
+                       stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || job.num_seqs == 0)
+        return e;
+    const uint32_t groups = (uint32_t)(job.num_seqs < 65536 ? job.num_seqs : 65536);
+    if (job.idx64)
+        hipLaunchKernelGGL(disjoint_mark_kernel<uint64_t>, dim3(groups), dim3(kDisjointThreads),
+                           0, stream, a);
+    else
+        hipLaunchKernelGGL(disjoint_mark_kernel<uint32_t>, dim3(groups), dim3(kDisjointThreads),
+                           0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    if (job.idx64)
+        hipLaunchKernelGGL(disjoint_find_kernel<uint64_t>, dim3(groups), dim3(kDisjointThreads),
+                           0, stream, a);
+    else
+        hipLaunchKernelGGL(disjoint_find_kernel<uint32_t>, dim3(groups), dim3(kDisjointThreads),
+                           0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_validate(const ValidateJob &job, hipStream_t stream) {
     VArgs a;
     a.block_table = job.block_table;

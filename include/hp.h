@@ -69,6 +69,8 @@ typedef enum hp_status {
                                  ([Hurray] Partial trailing page: reads and writes
                                  are bounded by the slice and the token count) */
     HP_ERR_TOTAL_TOKENS = 21, /* sum of seq_lens != total_tokens ([Hurray] Logical Shape) */
+    HP_ERR_WRITE_ALIAS = 22,  /* a scatter would write one slot more than once
+                                 ([Hurray] Prefix Sharing; HP_FLAG_DISJOINT) */
     HP_ERR_HIP = 32           /* a HIP runtime call or kernel launch failed */
 } hp_status;
 
@@ -94,12 +96,19 @@ enum {
                                     Prefix Sharing); the pool is then read with
                                     non-temporal loads. Results are identical with or
                                     without it; with aliased pages it is only slower. */
-    HP_FLAG_GATED = 1u << 3      /* gather, scatter, dequant-gather and their batched and
+    HP_FLAG_GATED = 1u << 3,     /* gather, scatter, dequant-gather and their batched and
                                     quantized forms: the verdict that hp_validate_async
                                     left in the head of `workspace` decides, on the
                                     device, whether the call writes anything (see
                                     hp_validate_async). Not combined with
                                     HP_FLAG_CHECKED. */
+    HP_FLAG_DISJOINT = 1u << 4   /* scatter, quantize-on-scatter and the batched
+                                    scatter, with HP_FLAG_CHECKED only: after the
+                                    descriptor passes validation, also check that no
+                                    slot is written twice (hp_validate_writes); on a
+                                    clash return HP_ERR_WRITE_ALIAS and write nothing.
+                                    The workspace must hold
+                                    hp_disjoint_workspace_bytes(desc). */
 };
 
 /* A block-paged descriptor for one {kv_role, layer_index} pair ([Hurray]
@@ -194,6 +203,31 @@ hp_status hp_validate(const hp_desc *desc, const void *seq_start, void *workspac
 hp_status hp_validate_async(const hp_desc *desc, const void *seq_start, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* Bytes of device workspace that hp_validate_writes, and a scatter with
+ * HP_FLAG_DISJOINT, need on `desc`: 512 plus two bitmaps of num_pages *
+ * page_size bits, and at least hp_workspace_bytes(desc). 0 for an invalid
+ * descriptor. */
+size_t hp_disjoint_workspace_bytes(const hp_desc *desc);
+
+/* Write-disjointness of a scatter ([Hurray] Prefix Sharing: slices may name
+ * the same page, so two written rows, or a row and a zeroed tail slot of
+ * [Hurray] Partial trailing page, can land in one slot, and a scatter is
+ * defined only when they do not). First the checks of hp_validate, with
+ * seq_start; if they pass, the slots the scatter would write (token
+ * seq_start[s] + i of sequence s for i < seq_lens[s] and, with
+ * HP_FLAG_ZERO_TAIL in `flags`, the slots of the last token's page after it)
+ * are marked in a bitmap over the pool's slots. HP_ERR_WRITE_ALIAS is
+ * reported with index = the smallest sequence one of whose written slots is
+ * written more than once (by any sequence, itself included); HP_OK when every
+ * written slot is written once. Deterministic.
+ * Synchronous, like hp_validate: enqueues on `stream`, waits, writes *result
+ * (HOST, may be NULL) and returns result->code. workspace: DEVICE, 8-byte
+ * aligned, at least hp_disjoint_workspace_bytes(desc). flags: 0 or
+ * HP_FLAG_ZERO_TAIL. */
+hp_status hp_validate_writes(const hp_desc *desc, const void *seq_start, uint32_t flags,
+                             void *workspace, size_t workspace_bytes,
+                             hp_validate_result *result, void *stream);
+
 /* Decodes the 16 verdict bytes of hp_validate_async (`words`, HOST memory,
  * e.g. copied back from the workspace head) into *result, exactly as
  * hp_validate reports it, for the descriptor's total_tokens. Returns
@@ -238,9 +272,9 @@ hp_status hp_gather_static(const hp_desc *desc, void *out, uint32_t flags, void 
  * the last new token that come after it are set to zero bytes ([Hurray]
  * Partial trailing page). Destinations of different rows must be distinct
  * slots (aliased pages must be copied before they are written); otherwise
- * the result is undefined. Asynchronous.
- * Flags: HP_FLAG_CHECKED (validates with seq_start) or HP_FLAG_GATED,
- * HP_FLAG_ZERO_TAIL. */
+ * the result is undefined (HP_FLAG_DISJOINT checks it). Asynchronous.
+ * Flags: HP_FLAG_CHECKED (validates with seq_start; with HP_FLAG_DISJOINT
+ * also the distinct destinations) or HP_FLAG_GATED, HP_FLAG_ZERO_TAIL. */
 hp_status hp_scatter(const hp_desc *desc, const void *src, const void *seq_start,
                      void *workspace, size_t workspace_bytes, uint32_t flags,
                      void *stream);
@@ -278,8 +312,9 @@ hp_status hp_gather_dequant(const hp_desc *desc, void *out, uint32_t out_dtype,
  * src         DEVICE [total_tokens, num_heads, head_dim] of src_dtype
  *             (HP_DTYPE_F16, HP_DTYPE_BF16 or HP_DTYPE_F32), element aligned.
  * zero_points DEVICE uint8 [num_pages * page_size], 64-byte aligned (uint8 pools).
- * seq_start, workspace, flags (HP_FLAG_CHECKED or HP_FLAG_GATED, HP_FLAG_ZERO_TAIL: tail slots
- * get zero codes, scale 0 and zero point 0) and errors as hp_scatter. */
+ * seq_start, workspace, flags (HP_FLAG_CHECKED, with HP_FLAG_DISJOINT, or
+ * HP_FLAG_GATED; HP_FLAG_ZERO_TAIL: tail slots get zero codes, scale 0 and zero
+ * point 0) and errors as hp_scatter. */
 hp_status hp_scatter_quant(const hp_desc *desc, const void *src, uint32_t src_dtype,
                            void *zero_points, const void *seq_start, void *workspace,
                            size_t workspace_bytes, uint32_t flags, void *stream);

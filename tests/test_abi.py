@@ -29,7 +29,8 @@ def test_every_declared_symbol_is_exported():
                           "hp_copy_pages", "hp_copy_pages_batch", "hp_gather_dequant_q",
                           "hp_paged_attention", "hp_attention_workspace_bytes",
                           "hp_scatter_quant", "hp_validate_async", "hp_validate_verdict",
-                          "hp_gather_static"}
+                          "hp_gather_static", "hp_validate_writes",
+                          "hp_disjoint_workspace_bytes"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -460,3 +461,40 @@ def test_gather_static_rejections():
     empty = desc(num_seqs=0, num_block_entries=0, block_table=None, seq_lens=None,
                  total_tokens=0)
     assert gs(ctypes.byref(empty), None, 0, None) == S["HP_OK"]             # nothing to move
+
+
+def test_disjoint_writes_rejections():
+    """The write-disjointness check is part of the synchronous checked form
+    only, on the scatter calls, and needs the bitmaps' workspace; all of this
+    is decided on the host before the device is touched."""
+    d = desc()
+    C, D, G, Z = hp.HP_FLAG_CHECKED, hp.HP_FLAG_DISJOINT, hp.HP_FLAG_GATED, hp.HP_FLAG_ZERO_TAIL
+    need = L.hp_disjoint_workspace_bytes(ctypes.byref(d))
+    # 512 + two bitmaps of 20 pages x 16 slots (10 words each)
+    assert need == 512 + 8 * 10
+    assert L.hp_disjoint_workspace_bytes(None) == 0
+    assert L.hp_disjoint_workspace_bytes(ctypes.byref(desc(rank=2))) == 0
+    big = desc(num_seqs=5000, num_block_entries=20000, num_pages=20000)
+    assert L.hp_disjoint_workspace_bytes(ctypes.byref(big)) >= \
+        L.hp_workspace_bytes(ctypes.byref(big))
+    ws = OUT + 0x100000
+    sc = L.hp_scatter
+    assert sc(ctypes.byref(d), OUT, None, ws, 4096, D, None) == S["HP_ERR_ARG"]        # unchecked
+    assert sc(ctypes.byref(d), OUT, None, ws, 4096, D | G, None) == S["HP_ERR_ARG"]    # gated
+    assert sc(ctypes.byref(d), OUT, None, ws, need - 8, C | D, None) == S["HP_ERR_WORKSPACE"]
+    assert sc(ctypes.byref(d), OUT, None, ws, 256, C | D | Z, None) == S["HP_ERR_WORKSPACE"]
+    assert gather(d, ws=ws, n=4096, flags=C | D) == S["HP_ERR_ARG"]                     # not a scatter
+    q = desc(dtype=hp.DTYPE["i8"], scales=ALIGNED + 0x500000)
+    assert L.hp_gather_dequant(ctypes.byref(q), OUT, hp.DTYPE["bf16"], ws, 4096, C | D,
+                               None) == S["HP_ERR_ARG"]
+    assert sq(q, flags=D) == S["HP_ERR_ARG"]
+    vw = L.hp_validate_writes
+    res = hp.HpValidateResult()
+    assert vw(None, None, 0, ws, need, ctypes.byref(res), None) == S["HP_ERR_NULL"]
+    assert vw(ctypes.byref(d), None, C, ws, need, ctypes.byref(res), None) == S["HP_ERR_ARG"]
+    assert res.code == S["HP_ERR_ARG"]
+    assert vw(ctypes.byref(d), None, Z, ws, need - 1, None, None) == S["HP_ERR_WORKSPACE"]
+    assert vw(ctypes.byref(d), None, 0, ws + 4, need, None, None) == S["HP_ERR_ALIGN"]
+    assert vw(ctypes.byref(d), ALIGNED + 0x400002, 0, ws, need, None, None) == S["HP_ERR_ALIGN"]
+    assert vw(ctypes.byref(desc(paged_axis=1)), None, 0, ws, need, None, None) == \
+        S["HP_ERR_PAGED_AXIS"]
