@@ -725,7 +725,14 @@ __device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_o
 // results of the first kind into those units' slots, the attention kernel the
 // rest, and the combine kernel merges them as before.
 
-constexpr uint32_t kSharedChunkTokens = 256;  // tokens of one shared work item (about)
+// Tokens of one shared work item (about: whole pages). Measured on MI355X,
+// prefix batch (1,024 shared tokens), G = 4 / 8: 256 -> 112.8 / 146.7 us,
+// 512 -> 99.9 / 124.1 us (fewer partial results to merge), 1,024 -> 113.0 /
+// 132.1 us (too few work items to overlap the units).
+#ifndef HP_ATTN_SHARED_CHUNK_TOKENS
+#define HP_ATTN_SHARED_CHUNK_TOKENS 512
+#endif
+constexpr uint32_t kSharedChunkTokens = HP_ATTN_SHARED_CHUNK_TOKENS;
 constexpr uint32_t kMinSharedTokens = 64;     // two matrix tiles
 
 // One 32-token tile of a wave against K and V tiles in LDS (token-major
@@ -1630,7 +1637,8 @@ AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_
     // (HBM bounds the call), more and shorter ones when they are served from
     // the caches; grouped heads (more arithmetic per byte) spread over more
     // workgroups
-    const uint64_t target = num_q_heads != num_kv_heads ? kAttnTargetGroupsGqa
+    const uint64_t target = num_q_heads != num_kv_heads
+                                ? (stream_loads ? kAttnTargetGroupsGqaStream : kAttnTargetGroupsGqa)
                             : stream_loads              ? kAttnTargetGroupsMha
                                                         : kAttnTargetGroupsMhaCached;
     uint64_t upages = (pages * sh.head_groups + target - 1) / target;
