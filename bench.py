@@ -41,7 +41,8 @@ Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                   [--no-configs] [--extras]
   python bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR
-      (writes the rocprofv3 summaries under profiles/)
+      (writes the rocprofv3 summaries under profiles/; the rocprofv3 commands
+      below write their raw output under rocprof_out/)
 """
 import argparse
 import ctypes
@@ -78,19 +79,19 @@ KERNEL_LABELS = {
 }
 CALIBRATION_BYTES = 1 << 30
 TRACE_STEPS, TRACE_WARMUP = 50, 5
-TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o trace -- "
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d rocprof_out/prof_trace -o trace -- "
              f"python3 bench.py --steps {TRACE_STEPS} --warmup {TRACE_WARMUP} --no-cpu-baseline "
              "--no-reference-copies --no-configs")
-PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/prof_{d} -o {d} -- "
+PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d rocprof_out/prof_{d} -o {d} -- "
            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-reference-copies "
            "--no-configs --copy-calibration")
-ATTN_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_attn_trace -o trace "
+ATTN_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d rocprof_out/prof_attn_trace -o trace "
                   "-- python3 bench.py --attention-only")
-ATTN_PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/prof_attn_{d} -o {d} -- "
+ATTN_PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d rocprof_out/prof_attn_{d} -o {d} -- "
                 "python3 bench.py --attention-only --kernel-reps 3 --copy-calibration")
-QW_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_qw_trace -o trace "
+QW_TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d rocprof_out/prof_qw_trace -o trace "
                 "-- python3 bench.py --quant-write-only")
-QW_PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/prof_qw_{d} -o {d} -- "
+QW_PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d rocprof_out/prof_qw_{d} -o {d} -- "
               "python3 bench.py --quant-write-only --kernel-reps 3 --copy-calibration")
 
 
@@ -405,7 +406,7 @@ COUNTER_PASSES = {
     "latency": "TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_RDREQ_DRAM_sum TCC_EA0_WRREQ_LEVEL_sum "
                "TCC_EA0_WRREQ_DRAM_sum SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY",
 }
-COUNTER_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/prof_cnt_{d} -o {d} -- "
+COUNTER_CMD = ("rocprofv3 --pmc {c} -f csv -d rocprof_out/prof_cnt_{d} -o {d} -- "
                "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --flush-iters 3 "
                "--copy-calibration")
 
@@ -1272,9 +1273,9 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: --gpus {args.gpus} (WORLD_SIZE {world}) requested, but this build "
-              "measures one GPU only: the block-paged path has no multi-GPU code (see the "
-              "sharding notes in DESIGN.md).", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} (WORLD_SIZE {world}) requested, but the "
+              "benchmark measures one GPU only: the block-paged path has no multi-GPU code "
+              "(it would shard by heads, with no exchange, or by sequences).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
