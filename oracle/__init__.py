@@ -22,7 +22,8 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboracle.so")
+# HP_ORACLE_LIB names another build of the same source (the sanitizer test's)
+LIB_PATH = os.environ.get("HP_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 
 # Oracle check outcomes (oracle.h, enum oracle_check), by name.
 CHECKS = {

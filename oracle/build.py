@@ -26,5 +26,19 @@ def build(verbose=False):
     return LIB
 
 
+def build_sanitized(out, verbose=False):
+    """The same library built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (any report aborts), at `out`. Load it into a process that has the ASan
+    runtime preloaded (LD_PRELOAD), with HP_ORACLE_LIB=out."""
+    flags = [f for f in CFLAGS if f != "-O2"] + [
+        "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+        "-fno-sanitize-recover=all"]
+    cmd = ["gcc", *flags, "-o", out, SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
