@@ -31,6 +31,9 @@
 //    accumulation) and is summed across the head's lanes with DPP row
 //    operations; an online softmax (running max, base 2) rescales the
 //    accumulator once per batch.
+//  * With three or more query heads per kv head (two with streaming loads)
+//    and head_dim 64 or 128, the matrix-core kernel below takes the call
+//    instead; with cached loads its grid also carries the shared-prefix pass.
 //  * Each unit writes (max, sum of weights, unnormalised weighted sum of V)
 //    per query head to the workspace, and a combine kernel merges a
 //    sequence's units and divides. A sequence held by one unit is normalised
@@ -715,12 +718,12 @@ __device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_o
 // at least kMinSharedTokens tokens of identical full pages (both sequences'
 // counts cover them); a run's shared part is the shortest such common prefix
 // in it, which every member holds. The shared part is computed once per kv
-// head, 256-token chunk and item of seqs_per_block sequences of the run: the
-// workgroup's four waves take four row blocks (the query heads of 16 / G
-// sequences each, stacked as the matrix core's 16 rows; one sequence and 16
-// of its query heads per block when G > 16), and all 256 threads load each
-// K/V tile once, as whole head rows, into a double-buffered LDS tile that the
-// four waves read. A sequence's units are its shared chunks followed by units
+// head, chunk of kSharedChunkTokens tokens and item of seqs_per_block
+// sequences of the run: the workgroup's four waves take four row blocks (the
+// query heads of 16 / G sequences each, stacked as the matrix core's 16 rows;
+// one sequence and 16 of its query heads per block when G > 16), and all 256
+// threads load each K/V tile once, as whole head rows, into a double-buffered
+// LDS tile that the four waves read. A sequence's units are its shared chunks followed by units
 // over the tokens after the shared part; the shared pass writes the partial
 // results of the first kind into those units' slots, the attention kernel the
 // rest, and the combine kernel merges them as before.
