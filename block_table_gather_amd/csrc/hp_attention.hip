@@ -1418,28 +1418,18 @@ __device__ __forceinline__ void seq_units(const CArgs &c, uint32_t s, uint32_t &
 
 // out[s][hq][d] of a sequence held by several units: the units' partial
 // results merged with max-shifted weights, then divided. One pass over the
-// units, kBatch at a time so that their loads are in flight together.
-// Sequences of zero or one unit were written by the attention kernel.
-template <typename IdxT>
-__global__ __launch_bounds__(kAttnThreads) void attention_combine_kernel(CArgs c) {
-    constexpr uint32_t kBatch = 16;
-    const uint32_t s = blockIdx.x;
-    uint32_t u0, u1;
-    seq_units<IdxT>(c, s, u0, u1);
-    if (u1 - u0 < 2)
-        return;
-    // each thread: 4 consecutive outputs of one query head (head_dim % 8 == 0)
-    const uint32_t i = (blockIdx.y * kAttnThreads + threadIdx.x) * 4;
+// units, B at a time so that their loads are in flight together.
+template <uint32_t B>
+__device__ __forceinline__ void combine_units(const CArgs &c, uint32_t s, uint32_t u0, uint32_t u1,
+                                              uint32_t i) {
     const uint32_t Hq = c.num_q_heads, D = c.head_dim;
-    if (i >= Hq * D)
-        return;
     const uint32_t hq = udiv32(i, c.div_d), d = i - hq * D;
     float M = -__builtin_inff(), lsum = 0.0f, num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (uint32_t ub = u0; ub < u1; ub += kBatch) {
-        float mv[kBatch], lv[kBatch];
-        u32x4 av[kBatch];
+    for (uint32_t ub = u0; ub < u1; ub += B) {
+        float mv[B], lv[B];
+        u32x4 av[B];
 #pragma unroll
-        for (uint32_t k = 0; k < kBatch; ++k) {
+        for (uint32_t k = 0; k < B; ++k) {
             const uint32_t u = ub + k < u1 ? ub + k : u1 - 1;  // repeats get weight 0 below
             const uint64_t idx = (uint64_t)u * Hq + hq;
             mv[k] = c.part_ml[2 * idx];
@@ -1448,7 +1438,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_combine_kernel(CArgs c
         }
         float Mn = M;
 #pragma unroll
-        for (uint32_t k = 0; k < kBatch; ++k)
+        for (uint32_t k = 0; k < B; ++k)
             Mn = __builtin_fmaxf(Mn, mv[k]);
         const float cs = exp2_hw(M - Mn);  // M = -inf on the first batch: 0
         lsum *= cs;
@@ -1456,7 +1446,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_combine_kernel(CArgs c
         for (int e = 0; e < 4; ++e)
             num[e] *= cs;
 #pragma unroll
-        for (uint32_t k = 0; k < kBatch; ++k) {
+        for (uint32_t k = 0; k < B; ++k) {
             const float w = ub + k < u1 ? exp2_hw(mv[k] - Mn) : 0.0f;
             float a4[4];
             __builtin_memcpy(a4, &av[k], 16);
@@ -1474,6 +1464,29 @@ __global__ __launch_bounds__(kAttnThreads) void attention_combine_kernel(CArgs c
     u32x4 ov;
     __builtin_memcpy(&ov, o, 16);
     *reinterpret_cast<u32x4 *>(c.out + (uint64_t)s * Hq * D + i) = ov;
+}
+
+// Sequences of zero or one unit were written by the attention kernel. The
+// batch of units loaded together follows the sequence's unit count (the
+// same merge in the same order; only the loads of repeated units differ).
+template <typename IdxT>
+__global__ __launch_bounds__(kAttnThreads) void attention_combine_kernel(CArgs c) {
+    const uint32_t s = blockIdx.x;
+    uint32_t u0, u1;
+    seq_units<IdxT>(c, s, u0, u1);
+    if (u1 - u0 < 2)
+        return;
+    // each thread: 4 consecutive outputs of one query head (head_dim % 8 == 0)
+    const uint32_t i = (blockIdx.y * kAttnThreads + threadIdx.x) * 4;
+    if (i >= c.num_q_heads * c.head_dim)
+        return;
+    const uint32_t n = u1 - u0;
+    if (n <= 4)
+        combine_units<4>(c, s, u0, u1, i);
+    else if (n <= 8)
+        combine_units<8>(c, s, u0, u1, i);
+    else
+        combine_units<16>(c, s, u0, u1, i);
 }
 
 // ---- host side ----------------------------------------------------------------
