@@ -719,40 +719,57 @@ def attention_extras(hp, torch, np, dev, stream, reps, gqa8=False):
     streaming loads) and the prefix-sharing batch (256 sequences, 8 kv heads x
     128 bf16, 32 query heads, cached loads since 64 prefix pages are read by
     every sequence); with gqa8, the prefix batch with 64 query heads and the
-    decode batch with 128 (four per kv head, matrix cores) too.
+    decode batch with 128 (four per kv head, matrix cores) too, and three of
+    the workloads over int8 pools with per-slot scales (hp_paged_attention_q8,
+    bf16 queries).
     Algorithmic bytes: every live K and V row read once (the prefix pages once
-    per sequence that uses them, as logical bytes), the queries read and the
-    fp32 output written."""
+    per sequence that uses them, as logical bytes), with int8 pools each
+    row's scale once, the queries read and the fp32 output written."""
     import workloads
     res = {}
-    cases = [("decode_mha_f16", workloads.decode(), 1, True),
-             ("prefix_gqa4_bf16", workloads.prefix(), 4, False)]
+    cases = [("decode_mha_f16", workloads.decode(), 1, True, False),
+             ("prefix_gqa4_bf16", workloads.prefix(), 4, False, False)]
     if gqa8:
-        cases.append(("prefix_gqa8_bf16", workloads.prefix(), 8, False))
-        cases.append(("decode_gqa4_f16", workloads.decode(), 4, True))
-    for name, w, group, streaming in cases:
-        k_pool = w.make_pool(dev)
-        v_pool = dataclasses.replace(w, seed=w.seed * 7 + 3).make_pool(dev)
+        cases.append(("prefix_gqa8_bf16", workloads.prefix(), 8, False, False))
+        cases.append(("decode_gqa4_f16", workloads.decode(), 4, True, False))
+        cases.append(("decode_mha_int8", workloads.decode(), 1, True, True))
+        cases.append(("decode_gqa4_int8", workloads.decode(), 4, True, True))
+        cases.append(("prefix_gqa4_int8", workloads.prefix(), 4, False, True))
+    for name, w, group, streaming, q8 in cases:
+        if q8:
+            w = dataclasses.replace(w, dtype="i8", values="int8", with_scales=True)
+        vw = dataclasses.replace(w, seed=w.seed * 7 + 3)
+        k_pool, v_pool = w.make_pool(dev), vw.make_pool(dev)
+        k_sc = w.make_scales(dev) if q8 else None
+        v_sc = vw.make_scales(dev) if q8 else None
 
         def idx(a):
             return torch.from_numpy(np.asarray(a, dtype=np.uint32).view(np.int32).copy()).to(dev)
 
-        desc = hp.Descriptor(k_pool, idx(w.block_table), idx(w.seq_ptr), idx(w.seq_lens))
+        desc = hp.Descriptor(k_pool, idx(w.block_table), idx(w.seq_ptr), idx(w.seq_lens),
+                             scales=k_sc)
         T, S, H, D = w.total_tokens, w.num_seqs, w.num_heads, w.head_dim
         Hq = H * group
         g = torch.Generator(device=dev).manual_seed(9)
-        q = torch.randn((S, Hq, D), generator=g, device=dev).to(k_pool.dtype)
+        q = torch.randn((S, Hq, D), generator=g, device=dev).to(
+            torch.bfloat16 if q8 else k_pool.dtype)
         out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
         ws = torch.empty(hp.attention_workspace_bytes(desc, T, Hq), dtype=torch.uint8, device=dev)
         L = hp.lib()
         pd = desc.with_tokens(T)
-        args = (pd, v_pool.data_ptr(), q.data_ptr(), Hq, ctypes.c_float(1.0 / D ** 0.5),
-                out.data_ptr(), hp.DTYPE["f32"], ws.data_ptr(), ws.numel(),
+        tail = (q.data_ptr(), Hq, ctypes.c_float(1.0 / D ** 0.5), out.data_ptr(),
+                hp.DTYPE["f32"], ws.data_ptr(), ws.numel(),
                 hp.HP_FLAG_STREAM if streaming else 0, stream.cuda_stream)
+        if q8:
+            args = (pd, v_pool.data_ptr(), v_sc.data_ptr()) + tail
+            fn, fname = L.hp_paged_attention_q8, "hp_paged_attention_q8"
+        else:
+            args = (pd, v_pool.data_ptr()) + tail
+            fn, fname = L.hp_paged_attention, "hp_paged_attention"
 
         def call():
-            if L.hp_paged_attention(*args) != 0:
-                raise SystemExit("hp_paged_attention failed")
+            if fn(*args) != 0:
+                raise SystemExit(f"{fname} failed")
 
         call()
         torch.cuda.synchronize()
@@ -763,10 +780,13 @@ def attention_extras(hp, torch, np, dev, stream, reps, gqa8=False):
         b.record(stream)
         b.synchronize()
         ms = a.elapsed_time(b) / reps
-        nbytes = 2 * T * H * D * 2 + S * Hq * D * 2 + S * Hq * D * 4
-        unique = (len(np.unique(w.block_table)) * w.page_size * H * D * 2 * 2 if not streaming
+        eb = 1 if q8 else 2
+        row = H * D * eb + (4 if q8 else 0)   # one slot's K (or V) bytes, with its scale
+        nbytes = 2 * T * row + S * Hq * D * 2 + S * Hq * D * 4
+        unique = (len(np.unique(w.block_table)) * w.page_size * row * 2 if not streaming
                   else None)
         res[name] = {"sequences": S, "tokens": T, "kv_heads": H, "q_heads": Hq, "head_dim": D,
+                     "kv_dtype": "int8 + fp32 scale per slot" if q8 else w.dtype,
                      "algorithmic_bytes": nbytes, "launch_us": round(ms * 1e3, 1),
                      "gb_per_s": round(nbytes / (ms / 1e3) / 1e9, 1),
                      "tokens_per_s": round(T / (ms / 1e3), 1)}
@@ -777,7 +797,7 @@ def attention_extras(hp, torch, np, dev, stream, reps, gqa8=False):
             res[name]["unique_kv_bytes"] = unique
             res[name]["unique_gb_per_s"] = round(ub / (ms / 1e3) / 1e9, 1)
             res[name]["unique_frac_of_8tbs"] = round(ub / (ms / 1e3) / 8e12, 3)
-        del k_pool, v_pool, q, out, ws
+        del k_pool, v_pool, q, out, ws, k_sc, v_sc
         torch.cuda.empty_cache()
     return res
 

@@ -134,6 +134,9 @@ _lib.hp_scatter_quant.argtypes = [_P, _vp, _u32, _vp, _vp, _vp, _sz, _u32, _vp]
 _lib.hp_paged_attention.restype = ctypes.c_int
 _lib.hp_paged_attention.argtypes = [_P, _vp, _vp, _u32, ctypes.c_float, _vp, _u32, _vp, _sz,
                                     _u32, _vp]
+_lib.hp_paged_attention_q8.restype = ctypes.c_int
+_lib.hp_paged_attention_q8.argtypes = [_P, _vp, _vp, _vp, _u32, ctypes.c_float, _vp, _u32, _vp,
+                                       _sz, _u32, _vp]
 _lib.hp_attention_workspace_bytes.restype = _sz
 _lib.hp_attention_workspace_bytes.argtypes = [_P, _u32]
 _lib.hp_status_str.restype = ctypes.c_char_p
@@ -469,13 +472,8 @@ def attention_workspace_bytes(desc, total_tokens, num_q_heads):
     return int(_lib.hp_attention_workspace_bytes(desc.with_tokens(total_tokens), num_q_heads))
 
 
-def paged_attention(desc, v_pool, q, out, *, total_tokens, scale=None, checked=False,
-                    streaming=False, workspace=None, stream=None):
-    """out[S, Hq, D] (float32) <- decode attention of q[S, Hq, D] over the K
-    cache of `desc` (its page_pool) and the V pool `v_pool`, both read
-    through desc's block table. total_tokens: the sum of the token counts.
-    scale defaults to 1/sqrt(head_dim). A workspace is allocated through
-    torch when none is given."""
+def _attention(desc, v_pool, v_scales, q, out, total_tokens, scale, checked, streaming,
+               workspace, stream, q8):
     Hq = q.shape[1]
     p = desc.with_tokens(total_tokens)
     n = int(_lib.hp_attention_workspace_bytes(p, Hq))
@@ -484,14 +482,41 @@ def paged_attention(desc, v_pool, q, out, *, total_tokens, scale=None, checked=F
         desc._ws = workspace  # keep alive until the next call on this descriptor
     if scale is None:
         scale = 1.0 / float(desc.c.head_dim) ** 0.5
-    _check(_lib.hp_paged_attention(p, _ptr(v_pool), _ptr(q), Hq, float(scale), _ptr(out),
-                                   DTYPE["f32"], _ptr(workspace),
-                                   workspace.numel() * workspace.element_size()
-                                   if workspace is not None else 0,
-                                   (HP_FLAG_CHECKED if checked else 0) |
-                                   (HP_FLAG_STREAM if streaming else 0),
-                                   _stream(stream, desc.device)), "hp_paged_attention")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_STREAM if streaming else 0)
+    st = _stream(stream, desc.device)
+    if q8:
+        _check(_lib.hp_paged_attention_q8(p, _ptr(v_pool), _ptr(v_scales), _ptr(q), Hq,
+                                          float(scale), _ptr(out), DTYPE["f32"],
+                                          _ptr(workspace), ws_bytes, flags, st),
+               "hp_paged_attention_q8")
+    else:
+        _check(_lib.hp_paged_attention(p, _ptr(v_pool), _ptr(q), Hq, float(scale), _ptr(out),
+                                       DTYPE["f32"], _ptr(workspace), ws_bytes, flags, st),
+               "hp_paged_attention")
     return out
+
+
+def paged_attention(desc, v_pool, q, out, *, total_tokens, scale=None, checked=False,
+                    streaming=False, workspace=None, stream=None):
+    """out[S, Hq, D] (float32) <- decode attention of q[S, Hq, D] over the K
+    cache of `desc` (its page_pool) and the V pool `v_pool`, both read
+    through desc's block table. total_tokens: the sum of the token counts.
+    scale defaults to 1/sqrt(head_dim). A workspace is allocated through
+    torch when none is given."""
+    return _attention(desc, v_pool, None, q, out, total_tokens, scale, checked, streaming,
+                      workspace, stream, False)
+
+
+def paged_attention_q8(desc, v_pool, v_scales, q, out, *, total_tokens, scale=None,
+                       checked=False, streaming=False, workspace=None, stream=None):
+    """out[S, Hq, D] (float32) <- decode attention of bf16 q[S, Hq, D] over
+    int8 pools with one fp32 scale per slot: the K pool and K scales of `desc`
+    (its page_pool and scales), the V pool `v_pool` and `v_scales`. Equal bit
+    for bit to paged_attention over bf16 pools holding the dequantized values
+    (gather_dequant's rounding). Other arguments as paged_attention."""
+    return _attention(desc, v_pool, v_scales, q, out, total_tokens, scale, checked, streaming,
+                      workspace, stream, True)
 
 
 # ---- batched calls: several pools through the table of one descriptor -------

@@ -988,9 +988,10 @@ hp_status hp_gather_dequant_q(const hp_desc *desc, const hp_quant *quant, void *
                   (hipStream_t)stream, &q);
 }
 
-// Shape checks of hp_paged_attention beyond the descriptor's own.
-hp_status check_attention(const hp_desc *d, uint32_t num_q_heads) {
-    if (d->dtype != HP_DTYPE_F16 && d->dtype != HP_DTYPE_BF16)
+// Shape checks of the attention calls beyond the descriptor's own: the pool
+// type is f16 or bf16 (hp_paged_attention) or int8 (hp_paged_attention_q8).
+static hp_status check_attention(const hp_desc *d, uint32_t num_q_heads, bool q8) {
+    if (q8 ? d->dtype != HP_DTYPE_I8 : d->dtype != HP_DTYPE_F16 && d->dtype != HP_DTYPE_BF16)
         return HP_ERR_DTYPE;
     const uint32_t D = d->head_dim;
     if (D != 8 && D != 16 && D != 32 && D != 64 && D != 128 && D != 256)
@@ -1015,30 +1016,35 @@ hp_status check_attention(const hp_desc *d, uint32_t num_q_heads) {
 
 size_t hp_attention_workspace_bytes(const hp_desc *desc, uint32_t num_q_heads) {
     Geometry g;
-    if (!desc || check_desc(desc, &g) != HP_OK || check_attention(desc, num_q_heads) != HP_OK)
+    if (!desc || check_desc(desc, &g) != HP_OK ||
+        check_attention(desc, num_q_heads, desc->dtype == HP_DTYPE_I8) != HP_OK)
         return 0;
     return hp::attention_workspace_bytes(desc->num_seqs, desc->total_tokens, desc->page_size,
                                          desc->num_heads, desc->head_dim, num_q_heads);
 }
 
-hp_status hp_paged_attention(const hp_desc *desc, const void *v_pool, const void *q,
-                             uint32_t num_q_heads, float scale, void *out, uint32_t out_dtype,
-                             void *workspace, size_t workspace_bytes, uint32_t flags,
-                             void *stream) {
+// hp_paged_attention and hp_paged_attention_q8 (q8: int8 pools, the K
+// scales in desc->scales, the V scales in v_scales).
+static hp_status paged_attention(const hp_desc *desc, const void *v_pool,
+                                 const float *v_scales, const void *q, uint32_t num_q_heads,
+                                 float scale, void *out, uint32_t out_dtype, void *workspace,
+                                 size_t workspace_bytes, uint32_t flags, void *stream, bool q8) {
     Geometry g;
     hp_status st = check_desc(desc, &g);
     if (st != HP_OK)
         return st;
     if (out_dtype != HP_DTYPE_F32)
         return HP_ERR_DTYPE;
-    if ((st = check_attention(desc, num_q_heads)) != HP_OK)
+    if ((st = check_attention(desc, num_q_heads, q8)) != HP_OK)
         return st;
     if (flags & ~(uint32_t)(HP_FLAG_CHECKED | HP_FLAG_STREAM))
         return HP_ERR_ARG;
     const uint64_t S = desc->num_seqs, D = desc->head_dim;
     if (S && (!v_pool || !q || !out))
         return HP_ERR_NULL;
-    if (!aligned(v_pool, 64) || !aligned(q, 16) || !aligned(out, 16))
+    if (q8 && S && (!desc->scales || !v_scales))
+        return HP_ERR_NULL;
+    if (!aligned(v_pool, 64) || !aligned(q, 16) || !aligned(out, 16) || !aligned(v_scales, 64))
         return HP_ERR_ALIGN;
     const uint64_t need = hp::attention_workspace_bytes(S, desc->total_tokens, desc->page_size,
                                                         desc->num_heads, D, num_q_heads);
@@ -1047,9 +1053,11 @@ hp_status hp_paged_attention(const hp_desc *desc, const void *v_pool, const void
     if (!aligned(workspace, 256))
         return HP_ERR_ALIGN;
     const uint64_t q_bytes = S * num_q_heads * D * 2, out_bytes = S * num_q_heads * D * 4;
-    const void *reads[3] = {desc->page_pool, v_pool, q};
-    const uint64_t read_bytes[3] = {g.pool_bytes, g.pool_bytes, q_bytes};
-    for (int i = 0; i < 3; ++i)
+    const uint64_t scale_bytes = q8 ? desc->num_pages * desc->page_size * 4 : 0;
+    const void *reads[5] = {desc->page_pool, v_pool, q, desc->scales, v_scales};
+    const uint64_t read_bytes[5] = {g.pool_bytes, g.pool_bytes, q_bytes, scale_bytes,
+                                    scale_bytes};
+    for (int i = 0; i < 5; ++i)
         if (overlaps(out, out_bytes, reads[i], read_bytes[i]) ||
             overlaps(workspace, need, reads[i], read_bytes[i]))
             return HP_ERR_ARG;
@@ -1064,7 +1072,8 @@ hp_status hp_paged_attention(const hp_desc *desc, const void *v_pool, const void
         return HP_OK;
     hp::AttentionJob j = {};
     j.idx64 = desc->index_type == HP_INDEX_U64;
-    j.bf16 = desc->dtype == HP_DTYPE_BF16;
+    j.bf16 = desc->dtype == HP_DTYPE_BF16 || q8;
+    j.q8 = q8;
     j.stream_loads = flags & HP_FLAG_STREAM;
     j.num_seqs = (uint32_t)S;
     j.page_size = desc->page_size;
@@ -1078,11 +1087,31 @@ hp_status hp_paged_attention(const hp_desc *desc, const void *v_pool, const void
     j.block_table = desc->block_table;
     j.seq_ptr = desc->seq_ptr;
     j.seq_lens = desc->seq_lens;
+    if (q8) {
+        j.k_scales = desc->scales;
+        j.v_scales = v_scales;
+    }
     j.out = static_cast<float *>(out);
     j.scale = scale;
     j.workspace = workspace;
     const hipError_t e = hp::launch_attention(j, (hipStream_t)stream);
     return e == hipSuccess ? HP_OK : hip_failed(e);
+}
+
+hp_status hp_paged_attention(const hp_desc *desc, const void *v_pool, const void *q,
+                             uint32_t num_q_heads, float scale, void *out, uint32_t out_dtype,
+                             void *workspace, size_t workspace_bytes, uint32_t flags,
+                             void *stream) {
+    return paged_attention(desc, v_pool, nullptr, q, num_q_heads, scale, out, out_dtype,
+                           workspace, workspace_bytes, flags, stream, false);
+}
+
+hp_status hp_paged_attention_q8(const hp_desc *desc, const void *v_pool, const float *v_scales,
+                                const void *q, uint32_t num_q_heads, float scale, void *out,
+                                uint32_t out_dtype, void *workspace, size_t workspace_bytes,
+                                uint32_t flags, void *stream) {
+    return paged_attention(desc, v_pool, v_scales, q, num_q_heads, scale, out, out_dtype,
+                           workspace, workspace_bytes, flags, stream, true);
 }
 
 hp_status hp_copy_pages(const hp_desc *desc, const void *src_pages, const void *dst_pages,

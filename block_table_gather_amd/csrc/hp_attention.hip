@@ -52,6 +52,7 @@ namespace {
 
 constexpr uint32_t kAttnThreads = 256;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct F16 {
     static constexpr bool bf16 = false;
@@ -81,6 +82,8 @@ struct AArgs {
     uint32_t chunk_pages;     // pages of one shared-pass work item
     uint32_t seqs_per_block;  // sequences of one shared work item (four row blocks)
     const uint32_t *pre_pages, *run_of, *work_seq0, *work_chunk, *nwork;
+    // int8 pools: one fp32 scale per slot (page * page_size + slot) of each
+    const float *k_scales, *v_scales;
 };
 
 // 8 stored values (one 16-byte vector) as floats; exact.
@@ -108,6 +111,42 @@ __device__ __forceinline__ u32x4 ld16(const unsigned char *p) {
     else
         return *v;
 }
+
+template <bool NT>
+__device__ __forceinline__ u32x2 ld8(const unsigned char *p) {
+    const u32x2 *v = reinterpret_cast<const u32x2 *>(p);
+    if constexpr (NT)
+        return __builtin_nontemporal_load(v);
+    else
+        return *v;
+}
+
+// Attention over int8 pools with per-slot scales ([Hurray] Per-page-slot
+// parameters) reads each element as the dequant-gather writes it: the fp32
+// product of the code and its slot's scale, rounded to bf16 (round to
+// nearest even). The kernels load 8 codes and the scale, and turn them into
+// the 16-byte vector of 8 bf16 values that a bf16 pool would hold there, so
+// everything after the load is the bf16 path.
+struct Raw8 {
+    u32x2 v;  // 8 int8 codes
+    float s;  // their slot's scale
+};
+__device__ __forceinline__ u32x4 dequant8(const u32x2 &w, float s) {
+    u32x4 o;
+    o.x = pack_bf16x2(sbyte(w.x, 0) * s, sbyte(w.x, 1) * s);
+    o.y = pack_bf16x2(sbyte(w.x, 2) * s, sbyte(w.x, 3) * s);
+    o.z = pack_bf16x2(sbyte(w.y, 0) * s, sbyte(w.y, 1) * s);
+    o.w = pack_bf16x2(sbyte(w.y, 2) * s, sbyte(w.y, 3) * s);
+    return o;
+}
+__device__ __forceinline__ u32x4 bits8(const u32x4 &v) { return v; }
+__device__ __forceinline__ u32x4 bits8(const Raw8 &r) { return dequant8(r.v, r.s); }
+// Loaded form of 8 elements: the 16-bit values themselves, or codes + scale.
+template <bool Q8>
+using Loaded8 = std::conditional_t<Q8, Raw8, u32x4>;
+// Bytes per stored element.
+template <bool Q8>
+constexpr uint32_t elem_bytes() { return Q8 ? 1 : 2; }
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -221,7 +260,8 @@ __device__ __forceinline__ void unit_scan_lds(const void *seq_lens, uint32_t S, 
 
 // GT query-head slots per lane group (1, 2, 4 or 8 >= G, or 8 with grid z
 // chunks of 8 query heads when G > 8); slots past G are computed and dropped.
-template <typename ET, typename IdxT, int LPH, int GT, bool NT>
+// Q8: int8 pools with per-slot scales (ET is then BF16).
+template <typename ET, typename IdxT, int LPH, int GT, bool NT, bool Q8>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
     // No implicit multiply-add fusion: each fused step below is an explicit
     // fma, and a score must round before its max is subtracted, so that the
@@ -314,11 +354,11 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
             const u32x4 v = ld16<false>(a.q + qo);
             __builtin_memcpy(qp[gi], &v, 16);
         }
-        const uint64_t head_off = ((uint64_t)h * D + r * 8) * 2;
-        const uint64_t slot_bytes = (uint64_t)Hkv * D * 2;
+        const uint64_t head_off = ((uint64_t)h * D + r * 8) * elem_bytes<Q8>();
+        const uint64_t slot_bytes = (uint64_t)Hkv * D * elem_bytes<Q8>();
         // each batch starts with a token in range, so its running max is finite
         for (uint32_t jb = 0; jb + tl < n; jb += TB * TL) {
-            u32x4 kq[TB], vq[TB];
+            Loaded8<Q8> kq[TB], vq[TB];
             bool ok[TB];
 #pragma unroll
             for (int i = 0; i < TB; ++i) {
@@ -328,15 +368,21 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
                 const uint32_t pj = udiv32(jj, a.div_page);
                 const uint64_t row = pages[pj] * P + (jj - pj * P);
                 const uint64_t off = row * slot_bytes + head_off;
-                kq[i] = ld16<NT>(a.k_pool + off);
-                vq[i] = ld16<NT>(a.v_pool + off);
+                if constexpr (Q8) {
+                    kq[i] = Raw8{ld8<NT>(a.k_pool + off), a.k_scales[row]};
+                    vq[i] = Raw8{ld8<NT>(a.v_pool + off), a.v_scales[row]};
+                } else {
+                    kq[i] = ld16<NT>(a.k_pool + off);
+                    vq[i] = ld16<NT>(a.v_pool + off);
+                }
             }
             float x[GT][TB];
 #pragma unroll
             for (int i = 0; i < TB; ++i) {
+                const u32x4 kb = bits8(kq[i]);
 #pragma unroll
                 for (int gi = 0; gi < GT; ++gi) {
-                    const float dot = group_sum<LPH, GT == 1>(dot8<ET>(qp[gi], kq[i])) * a.qscale;
+                    const float dot = group_sum<LPH, GT == 1>(dot8<ET>(qp[gi], kb)) * a.qscale;
                     x[gi][i] = ok[i] ? dot : -__builtin_inff();
                 }
             }
@@ -364,7 +410,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
 #pragma unroll
             for (int i = 0; i < TB; ++i) {
                 float vf[8];
-                unpack8<ET>(vq[i], vf);
+                unpack8<ET>(bits8(vq[i]), vf);
 #pragma unroll
                 for (int gi = 0; gi < GT; ++gi)
 #pragma unroll
@@ -541,9 +587,10 @@ __device__ __forceinline__ uint32_t row_head(uint32_t r) { return 4 * (r & 3) + 
 // The unit's n tokens of kv head h against the query rows in qa: the online
 // softmax state m, l and the unnormalised output o of the rows this lane
 // holds (rows 4 grp + i for i < R, columns 16 db + c16). page_off: the byte
-// offsets in the pools of the unit's pages, staged in LDS. vt, pt: this
-// wave's V and weight tiles in LDS.
-template <typename ET, int D, bool NT, int R>
+// offsets in the pools of the unit's pages, staged in LDS (with Q8, int8
+// pools: the index of each page's first slot, page * page_size, which also
+// indexes the scales). vt, pt: this wave's V and weight tiles in LDS.
+template <typename ET, int D, bool NT, int R, bool Q8>
 __device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_off, uint32_t n,
                                           uint32_t h,
                                           const typename Mma<ET>::V8 (&qa)[D / 32],
@@ -557,8 +604,8 @@ __device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_o
     constexpr uint32_t VRB = v_row_bytes<D>();
     const uint32_t lane = threadIdx.x & 63, P = a.page_size, Hkv = a.num_kv_heads;
     const uint32_t c16 = lane & 15, grp = lane >> 4;
-    const uint32_t slot_bytes = Hkv * D * 2;
-    const uint32_t head_off = h * D * 2;
+    const uint32_t slot_bytes = Hkv * D * elem_bytes<Q8>();
+    const uint32_t head_off = h * D * elem_bytes<Q8>();
 
     // Loads take whole head rows: chunk c of a tile is 16 bytes for each of
     // the 64 lanes, lane L reading bytes 16 (L % (D / 8)) of the head row of
@@ -569,32 +616,55 @@ __device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_o
     // 198 us with whole rows for both K and V). K and V both go through the wave's
     // tile buffer in LDS, K on to the B layout of the score product. Tokens
     // past n repeat the last token (a real row; masked below).
+    // (int8 pools: 8 bytes of codes per chunk, and lane i < 32 loads the
+    // scale of the tile's token i; each chunk's codes take their token's
+    // scale from that lane and become the chunk's 16 bytes of bf16 on the way
+    // into LDS)
     V8 kb[2][KK];
-    u32x4 kc[2 * KK], vc[2 * KK];
-    auto load_rows = [&](const unsigned char *pool, uint32_t tb, u32x4 (&dst)[2 * KK]) {
+    constexpr uint32_t C16 = Q8 ? 1 : 2 * KK, C8 = Q8 ? 2 * KK : 1;
+    u32x4 kc[C16], vc[C16];
+    u32x2 kc8[C8], vc8[C8];
+    float ksc = 0.0f, vsc = 0.0f;
+    auto load_rows = [&](const unsigned char *pool, const float *scales, uint32_t tb,
+                         u32x4 (&d16)[C16], u32x2 (&d8)[C8], float &dsc) {
 #pragma unroll
         for (uint32_t c = 0; c < 2 * KK; ++c) {
             const uint32_t ch = 64 * c + lane;
             const uint32_t jt = ch / (D / 8), dc = ch % (D / 8);
             const uint32_t j = min32(tb + jt, n - 1);
             const uint32_t pj = udiv32(j, a.div_page);
-            dst[c] = ld16<NT>(pool + page_off[pj] + (uint64_t)(j - pj * P) * slot_bytes +
-                              head_off + 16 * dc);
+            if constexpr (Q8)
+                d8[c] = ld8<NT>(pool + (page_off[pj] + (j - pj * P)) * slot_bytes + head_off +
+                                8 * dc);
+            else
+                d16[c] = ld16<NT>(pool + page_off[pj] + (uint64_t)(j - pj * P) * slot_bytes +
+                                  head_off + 16 * dc);
+        }
+        if constexpr (Q8) {
+            const uint32_t j = min32(tb + (lane & (kMfmaTile - 1)), n - 1);
+            const uint32_t pj = udiv32(j, a.div_page);
+            dsc = scales[page_off[pj] + (j - pj * P)];
         }
     };
-    auto store_rows = [&](const u32x4 (&src)[2 * KK]) {  // token-major rows of VRB bytes
+    // token-major rows of VRB bytes
+    auto store_rows = [&](const u32x4 (&s16)[C16], const u32x2 (&s8)[C8], float sc) {
 #pragma unroll
         for (uint32_t c = 0; c < 2 * KK; ++c) {
             const uint32_t ch = 64 * c + lane;
             const uint32_t jt = ch / (D / 8), dc = ch % (D / 8);
-            *reinterpret_cast<u32x4 *>(vt + jt * VRB + 16 * dc) = src[c];
+            u32x4 v;
+            if constexpr (Q8)
+                v = dequant8(s8[c], __shfl(sc, (int)jt, 64));
+            else
+                v = s16[c];
+            *reinterpret_cast<u32x4 *>(vt + jt * VRB + 16 * dc) = v;
         }
     };
     // K of the tile into the B layout: the lane's token 16 b + c16, bytes
     // 64 kk + 16 grp of its row
     auto stage_k = [&]() {
         wave_lds_sync();  // the previous tile's reads of the buffer are done
-        store_rows(kc);
+        store_rows(kc, kc8, ksc);
         wave_lds_sync();
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -625,7 +695,7 @@ __device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_o
                 x[b][i] = ok ? acc[i] * a.qscale : -__builtin_inff();
         }
         if constexpr (more)
-            load_rows(a.k_pool, tb + kMfmaTile, kc);
+            load_rows(a.k_pool, a.k_scales, tb + kMfmaTile, kc, kc8, ksc);
         // online softmax per row (the tile's first token is in range, so the
         // new maximum is finite). When no row's maximum grows the correction
         // is exactly 1 and the rescaling is skipped (bit-identical).
@@ -667,10 +737,10 @@ __device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_o
         }
         // V tile to LDS (the buffer's K reads are done: the score products
         // consumed them)
-        store_rows(vc);
+        store_rows(vc, vc8, vsc);
         wave_lds_sync();
         if constexpr (more)
-            load_rows(a.v_pool, tb + kMfmaTile, vc);
+            load_rows(a.v_pool, a.v_scales, tb + kMfmaTile, vc, vc8, vsc);
         // weights as three A operands whose sum is the binary32 weight
         V8 pa[3];
         {
@@ -702,8 +772,8 @@ __device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_o
                 o[db] = M::mma(pa[k], vb, o[db]);
         }
     };
-    load_rows(a.k_pool, 0, kc);
-    load_rows(a.v_pool, 0, vc);
+    load_rows(a.k_pool, a.k_scales, 0, kc, kc8, ksc);
+    load_rows(a.v_pool, a.v_scales, 0, vc, vc8, vsc);
     uint32_t tb = 0;
     for (; tb + kMfmaTile < n; tb += kMfmaTile)
         tile(tb, std::integral_constant<bool, true>());
@@ -832,7 +902,7 @@ __device__ __forceinline__ void lds_tile(const AArgs &a, const unsigned char *kt
 // Work item w, kv head h: chunk work_chunk[w] of the item of seqs_per_block
 // sequences that begins at sequence work_seq0[w] (and query-head chunk z
 // when G > 16). Called by whole workgroups.
-template <typename ET, typename IdxT, int D>
+template <typename ET, typename IdxT, int D, bool Q8>
 __device__ __forceinline__ void shared_item(const AArgs &a, uint32_t w, uint32_t h,
                                             unsigned char *lds) {
 #pragma clang fp contract(off)
@@ -849,12 +919,13 @@ __device__ __forceinline__ void shared_item(const AArgs &a, uint32_t w, uint32_t
     const uint32_t pg0 = c * a.chunk_pages;
     const uint32_t npg = min32(C - pg0, a.chunk_pages);  // whole pages, all tokens live
     const uint32_t n = npg * P;
-    const uint32_t slot_bytes = Hkv * D * 2, head_off = h * D * 2;
-    uint64_t *pages = reinterpret_cast<uint64_t *>(lds);  // byte offsets of the pages
+    const uint32_t slot_bytes = Hkv * D * elem_bytes<Q8>(), head_off = h * D * elem_bytes<Q8>();
+    // byte offsets of the pages (int8 pools: their first slots)
+    uint64_t *pages = reinterpret_cast<uint64_t *>(lds);
     const uint64_t sp0 = uni64(ld_idx<IdxT>(a.seq_ptr, s0));
-    const uint64_t page_bytes = (uint64_t)P * slot_bytes;
+    const uint64_t page_mul = Q8 ? (uint64_t)P : (uint64_t)P * slot_bytes;
     for (uint32_t i = threadIdx.x; i < npg; i += kAttnThreads)
-        pages[i] = ld_idx<IdxT>(a.block_table, sp0 + pg0 + i) * page_bytes;
+        pages[i] = ld_idx<IdxT>(a.block_table, sp0 + pg0 + i) * page_mul;
     __syncthreads();
 
     // LDS: K and V tiles of two stages in the four wave regions (stage b: K
@@ -906,7 +977,8 @@ __device__ __forceinline__ void shared_item(const AArgs &a, uint32_t w, uint32_t
 
     // thread t loads chunk t + 256 e of the tile: 16 bytes of the head row of
     // token (t + 256 e) / (D / 8), so a wave's load covers whole rows
-    u32x4 kr[CPT], vr[CPT];
+    // (int8 pools: 8 bytes of codes and the slot's scale per chunk)
+    Loaded8<Q8> kr[CPT], vr[CPT];
     auto load = [&](uint32_t tb) {
 #pragma unroll
         for (uint32_t e = 0; e < CPT; ++e) {
@@ -914,10 +986,17 @@ __device__ __forceinline__ void shared_item(const AArgs &a, uint32_t w, uint32_t
             const uint32_t jt = ch / (D / 8), dc = ch % (D / 8);
             const uint32_t j = min32(tb + jt, n - 1);
             const uint32_t pj = udiv32(j, a.div_page);
-            const uint64_t off = pages[pj] + (uint64_t)(j - pj * P) * slot_bytes + head_off +
-                                 16 * dc;
-            kr[e] = ld16<false>(a.k_pool + off);
-            vr[e] = ld16<false>(a.v_pool + off);
+            if constexpr (Q8) {
+                const uint64_t slot = pages[pj] + (j - pj * P);
+                const uint64_t off = slot * slot_bytes + head_off + 8 * dc;
+                kr[e] = Raw8{ld8<false>(a.k_pool + off), a.k_scales[slot]};
+                vr[e] = Raw8{ld8<false>(a.v_pool + off), a.v_scales[slot]};
+            } else {
+                const uint64_t off = pages[pj] + (uint64_t)(j - pj * P) * slot_bytes +
+                                     head_off + 16 * dc;
+                kr[e] = ld16<false>(a.k_pool + off);
+                vr[e] = ld16<false>(a.v_pool + off);
+            }
         }
     };
     load(0);
@@ -928,8 +1007,8 @@ __device__ __forceinline__ void shared_item(const AArgs &a, uint32_t w, uint32_t
         for (uint32_t e = 0; e < CPT; ++e) {
             const uint32_t ch = threadIdx.x + kAttnThreads * e;
             const uint32_t jt = ch / (D / 8), dc = ch % (D / 8);
-            *reinterpret_cast<u32x4 *>(kt + jt * VRB + 16 * dc) = kr[e];
-            *reinterpret_cast<u32x4 *>(vt + jt * VRB + 16 * dc) = vr[e];
+            *reinterpret_cast<u32x4 *>(kt + jt * VRB + 16 * dc) = bits8(kr[e]);
+            *reinterpret_cast<u32x4 *>(vt + jt * VRB + 16 * dc) = bits8(vr[e]);
         }
         // the stage is written; every wave finished the tile that last used
         // the other stage before it reached this barrier
@@ -971,9 +1050,9 @@ __device__ __forceinline__ void shared_item(const AArgs &a, uint32_t w, uint32_t
 }
 
 // R: accumulator rows per lane that hold query heads (1 for G <= 4, 2 for
-// G <= 8, else 4).
-template <typename ET, typename IdxT, int D, bool NT, int R>
-__global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
+// G <= 8, else 4). Q8: int8 pools with per-slot scales (ET is then BF16).
+template <typename ET, typename IdxT, int D, bool NT, int R, bool Q8>
+__global__ __launch_bounds__(kAttnThreads, Q8 ? 2 : 1) void attention_mfma_kernel(AArgs a) {
 #pragma clang fp contract(off)
     using M = Mma<ET>;
     using V8 = typename M::V8;
@@ -992,7 +1071,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
         if (g < nw) {
             const uint32_t h = blockIdx.y * kMfmaWaves + g % kMfmaWaves;
             if (h < a.num_kv_heads)
-                shared_item<ET, IdxT, D>(a, g / kMfmaWaves, h, lds);
+                shared_item<ET, IdxT, D, Q8>(a, g / kMfmaWaves, h, lds);
             return;
         }
         g -= nw;
@@ -1065,9 +1144,10 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
     const uint32_t n = (uint32_t)min64(L - t0, (p_end - p_begin) * P);
     const uint64_t pg0 = t0 / P;
     const uint32_t npg = udiv32(n + P - 1, a.div_page);
-    const uint64_t page_bytes = (uint64_t)P * Hkv * D * 2;
+    // byte offsets of the pages (int8 pools: their first slots)
+    const uint64_t page_mul = Q8 ? (uint64_t)P : (uint64_t)P * Hkv * D * 2;
     for (uint32_t i = threadIdx.x; i < npg; i += kAttnThreads)
-        pages[i] = ld_idx<IdxT>(a.block_table, sp0 + pg0 + i) * page_bytes;  // byte offsets
+        pages[i] = ld_idx<IdxT>(a.block_table, sp0 + pg0 + i) * page_mul;
     __syncthreads();
 
     const uint32_t wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -1105,7 +1185,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AArgs a) {
     for (uint32_t db = 0; db < DB; ++db)
         o[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    mfma_span<ET, D, NT, R>(a, pages, n, h, qa, vt, pt, m, l, o);
+    mfma_span<ET, D, NT, R, Q8>(a, pages, n, h, qa, vt, pt, m, l, o);
 
     // rows 4 grp + i: query head gz + 4 i + grp of kv head h, column 16 db + c16
     const uint32_t units = uni(unit_end[s]) - u0;
@@ -1517,7 +1597,7 @@ bool attention_mfma(uint32_t G, uint32_t D, bool stream) {
     return G >= min_group && (D == 64 || D == 128);
 }
 
-template <typename ET, typename IdxT, int D, int R>
+template <typename ET, typename IdxT, int D, int R, bool Q8>
 hipError_t launch_attention_mfma(const AArgs &a, const AttentionShape &sh, bool nt,
                                  hipStream_t stream) {
     // shared work items (at most cap_work), units, then one spare per sequence
@@ -1527,27 +1607,27 @@ hipError_t launch_attention_mfma(const AArgs &a, const AttentionShape &sh, bool 
     const size_t lds = (a.fused ? ((4 * (size_t)a.num_seqs + 15) & ~(size_t)15) : 0) +
                        a.pg_area + kMfmaWaves * mfma_wave_lds<D>();
     if (nt)
-        hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, true, R>), grid,
+        hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, true, R, Q8>), grid,
                            dim3(kAttnThreads), lds, stream, a);
     else
-        hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, false, R>), grid,
+        hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, false, R, Q8>), grid,
                            dim3(kAttnThreads), lds, stream, a);
     return hipGetLastError();
 }
 
-template <typename ET, typename IdxT, int D>
+template <typename ET, typename IdxT, int D, bool Q8>
 hipError_t launch_mfma_r(const AArgs &a, const AttentionShape &sh, uint32_t G, bool nt,
                          hipStream_t st) {
     if (G <= 4)
-        return launch_attention_mfma<ET, IdxT, D, 1>(a, sh, nt, st);
+        return launch_attention_mfma<ET, IdxT, D, 1, Q8>(a, sh, nt, st);
     if (G <= 8)
-        return launch_attention_mfma<ET, IdxT, D, 2>(a, sh, nt, st);
-    return launch_attention_mfma<ET, IdxT, D, 4>(a, sh, nt, st);
+        return launch_attention_mfma<ET, IdxT, D, 2, Q8>(a, sh, nt, st);
+    return launch_attention_mfma<ET, IdxT, D, 4, Q8>(a, sh, nt, st);
 }
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-template <typename ET, typename IdxT, int LPH, int GT>
+template <typename ET, typename IdxT, int LPH, int GT, bool Q8>
 hipError_t launch_attention_t(const AArgs &a, const AttentionShape &sh, bool nt,
                               hipStream_t stream) {
     const dim3 grid((uint32_t)(sh.cap_units + a.num_seqs), sh.head_groups,
@@ -1557,50 +1637,52 @@ hipError_t launch_attention_t(const AArgs &a, const AttentionShape &sh, bool nt,
                        8 * (size_t)a.unit_pages +
                        (sh.token_lanes > 1 ? 4 * (size_t)ng * (2 + LPH * 8) : 0);
     if (nt)
-        hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, GT, true>), grid, dim3(kAttnThreads),
-                           lds, stream, a);
+        hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, GT, true, Q8>), grid,
+                           dim3(kAttnThreads), lds, stream, a);
     else
-        hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, GT, false>), grid, dim3(kAttnThreads),
-                           lds, stream, a);
+        hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, GT, false, Q8>), grid,
+                           dim3(kAttnThreads), lds, stream, a);
     return hipGetLastError();
 }
 
-template <typename ET, typename IdxT, int LPH>
+template <typename ET, typename IdxT, int LPH, bool Q8>
 hipError_t launch_attention_g(const AArgs &a, const AttentionShape &sh, uint32_t G, bool nt,
                               hipStream_t st) {
     switch (group_slots(G)) {
-    case 1: return launch_attention_t<ET, IdxT, LPH, 1>(a, sh, nt, st);
-    case 2: return launch_attention_t<ET, IdxT, LPH, 2>(a, sh, nt, st);
-    case 4: return launch_attention_t<ET, IdxT, LPH, 4>(a, sh, nt, st);
-    default: return launch_attention_t<ET, IdxT, LPH, 8>(a, sh, nt, st);
+    case 1: return launch_attention_t<ET, IdxT, LPH, 1, Q8>(a, sh, nt, st);
+    case 2: return launch_attention_t<ET, IdxT, LPH, 2, Q8>(a, sh, nt, st);
+    case 4: return launch_attention_t<ET, IdxT, LPH, 4, Q8>(a, sh, nt, st);
+    default: return launch_attention_t<ET, IdxT, LPH, 8, Q8>(a, sh, nt, st);
     }
 }
 
-template <typename ET, typename IdxT>
+template <typename ET, typename IdxT, bool Q8>
 hipError_t launch_attention_d(const AArgs &a, const AttentionShape &sh, uint32_t G, bool nt,
                               hipStream_t st) {
     switch (a.head_dim) {
-    case 8: return launch_attention_g<ET, IdxT, 1>(a, sh, G, nt, st);
-    case 16: return launch_attention_g<ET, IdxT, 2>(a, sh, G, nt, st);
-    case 32: return launch_attention_g<ET, IdxT, 4>(a, sh, G, nt, st);
-    case 64: return launch_attention_g<ET, IdxT, 8>(a, sh, G, nt, st);
-    case 128: return launch_attention_g<ET, IdxT, 16>(a, sh, G, nt, st);
-    default: return launch_attention_g<ET, IdxT, 32>(a, sh, G, nt, st);
+    case 8: return launch_attention_g<ET, IdxT, 1, Q8>(a, sh, G, nt, st);
+    case 16: return launch_attention_g<ET, IdxT, 2, Q8>(a, sh, G, nt, st);
+    case 32: return launch_attention_g<ET, IdxT, 4, Q8>(a, sh, G, nt, st);
+    case 64: return launch_attention_g<ET, IdxT, 8, Q8>(a, sh, G, nt, st);
+    case 128: return launch_attention_g<ET, IdxT, 16, Q8>(a, sh, G, nt, st);
+    default: return launch_attention_g<ET, IdxT, 32, Q8>(a, sh, G, nt, st);
     }
 }
 
-template <typename ET>
+// Q8: int8 pools with per-slot scales, computed as bf16 (ET = BF16).
+template <typename ET, bool Q8>
 hipError_t launch_attention_i(const AArgs &a, const AttentionShape &sh, uint32_t G, bool idx64,
                               bool nt, hipStream_t st) {
+    static_assert(!Q8 || ET::bf16, "int8 pools dequantise to bf16");
     if (attention_mfma(G, a.head_dim, nt)) {
         if (a.head_dim == 64)
-            return idx64 ? launch_mfma_r<ET, uint64_t, 64>(a, sh, G, nt, st)
-                         : launch_mfma_r<ET, uint32_t, 64>(a, sh, G, nt, st);
-        return idx64 ? launch_mfma_r<ET, uint64_t, 128>(a, sh, G, nt, st)
-                     : launch_mfma_r<ET, uint32_t, 128>(a, sh, G, nt, st);
+            return idx64 ? launch_mfma_r<ET, uint64_t, 64, Q8>(a, sh, G, nt, st)
+                         : launch_mfma_r<ET, uint32_t, 64, Q8>(a, sh, G, nt, st);
+        return idx64 ? launch_mfma_r<ET, uint64_t, 128, Q8>(a, sh, G, nt, st)
+                     : launch_mfma_r<ET, uint32_t, 128, Q8>(a, sh, G, nt, st);
     }
-    return idx64 ? launch_attention_d<ET, uint64_t>(a, sh, G, nt, st)
-                 : launch_attention_d<ET, uint32_t>(a, sh, G, nt, st);
+    return idx64 ? launch_attention_d<ET, uint64_t, Q8>(a, sh, G, nt, st)
+                 : launch_attention_d<ET, uint32_t, Q8>(a, sh, G, nt, st);
 }
 
 struct WsLayout {
@@ -1798,8 +1880,11 @@ hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
     // part, mostly read once: streaming loads (measured 1 to 2 % faster on
     // the prefix batch); the shared items keep cached loads.
     const bool nt = job.stream_loads || sh.shared;
-    e = job.bf16 ? launch_attention_i<BF16>(a, sh, G, job.idx64, nt, stream)
-                 : launch_attention_i<F16>(a, sh, G, job.idx64, nt, stream);
+    a.k_scales = job.k_scales;
+    a.v_scales = job.v_scales;
+    e = job.q8     ? launch_attention_i<BF16, true>(a, sh, G, job.idx64, nt, stream)
+        : job.bf16 ? launch_attention_i<BF16, false>(a, sh, G, job.idx64, nt, stream)
+                   : launch_attention_i<F16, false>(a, sh, G, job.idx64, nt, stream);
     if (e != hipSuccess)
         return e;
 

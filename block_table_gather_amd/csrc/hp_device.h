@@ -1,6 +1,6 @@
 // hp_device.h -- small helpers shared by the kernel files: division by a
 // launch-invariant divisor, index loads of either index type, wave-uniform
-// values. Not installed; not part of the ABI.
+// values, the int8 -> bf16 rounding. Not installed; not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -53,6 +53,25 @@ __device__ __forceinline__ uint64_t udiv(uint64_t n, Div f) {
 template <typename IdxT>
 __device__ __forceinline__ uint64_t ld_idx(const void *p, uint64_t i) {
     return (uint64_t)static_cast<const IdxT *>(p)[i];
+}
+
+// fp32 -> bf16 bits, round to nearest even (gfx950 converts with IEEE
+// rounding for this type). The pair converts as one vector, which maps to a
+// single v_cvt_pk_bf16_f32 (lo in the low half). Every int8 -> bf16
+// dequantisation in the library (the dequant-gathers and attention over an
+// int8 pool) rounds through these, so their results agree bit for bit.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
+}
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+    __bf16 a = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, a);
+}
+// Signed byte k of w, as a float (exact).
+__device__ __forceinline__ float sbyte(uint32_t w, int k) {
+    return (float)(int8_t)(w >> (8 * k));
 }
 
 } // namespace hp

@@ -264,9 +264,11 @@ struct AttentionShape {
 
 struct AttentionJob {
     bool idx64, bf16, stream_loads;
+    bool q8;  // int8 pools with per-slot scales, dequantised to bf16 (bf16 queries)
     uint32_t num_seqs, page_size, num_kv_heads, num_q_heads, head_dim;
     uint64_t total_tokens;
     const void *k_pool, *v_pool, *q;
+    const float *k_scales, *v_scales;  // q8 only: N * P each
     const void *block_table, *seq_ptr, *seq_lens;
     float *out;
     float scale;

@@ -369,24 +369,6 @@ __device__ __forceinline__ void zero_span(unsigned char *__restrict__ dst, uint3
         st_stream(z, d + i);
 }
 
-// fp32 -> bf16 bits, round to nearest even (gfx950 has a hardware
-// conversion with IEEE rounding for this type).
-// The pair converts as one vector, which maps to a single v_cvt_pk_bf16_f32
-// (lo in the low half).
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const bf16x2 v = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
-    return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ uint16_t to_bf16(float x) {
-    __bf16 a = (__bf16)x;
-    return __builtin_bit_cast(uint16_t, a);
-}
-__device__ __forceinline__ float sbyte(uint32_t w, int k) {
-    return (float)(int8_t)(w >> (8 * k));
-}
-
 // Dequantises `rows` rows of R_in int8 values into bf16. `scale_row` points at
 // the scale of the unit's first slot; rows <= 64, so lane r holds row r's
 // scale and every lane fetches its row's scale from that lane.

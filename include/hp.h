@@ -448,7 +448,36 @@ hp_status hp_paged_attention(const hp_desc *desc, const void *v_pool, const void
                              void *workspace, size_t workspace_bytes, uint32_t flags,
                              void *stream);
 
-/* Workspace bytes hp_paged_attention needs for this descriptor (its
+/* Decode attention over int8 K and V pools with one fp32 scale per slot.
+ *
+ * [Hurray] Per-page-slot parameters: the scale of a slot sits at
+ * scales[phys_page * page_size + t % page_size] and applies to every element
+ * of that slot's row; hp_gather_dequant turns an element into
+ * bf16_rne(fp32(code) * scale). This call computes exactly what
+ * hp_paged_attention computes on bf16 pools holding those dequantized values
+ * in every slot (same units, same arithmetic, so the results are equal bit
+ * for bit), without writing the bf16 pools: each element is dequantized as it
+ * is read.
+ *
+ * desc      the K cache: dtype HP_DTYPE_I8, its page_pool the int8 K pool and
+ *           its scales the K scales (num_pages * page_size fp32, 64-byte
+ *           aligned); other requirements as hp_paged_attention.
+ * v_pool    DEVICE, the int8 V pool: same geometry and block table as K,
+ *           64-byte aligned.
+ * v_scales  DEVICE, num_pages * page_size fp32 scales of the V pool, 64-byte
+ *           aligned.
+ * q         DEVICE [num_seqs, num_q_heads, head_dim] bf16, 16-byte aligned.
+ * The other arguments, the workspace (hp_attention_workspace_bytes with
+ * this descriptor), the flags and the errors are those of
+ * hp_paged_attention; NULL scales with a non-empty batch give HP_ERR_NULL,
+ * and neither out nor the workspace may overlap a scale buffer. */
+hp_status hp_paged_attention_q8(const hp_desc *desc, const void *v_pool, const float *v_scales,
+                                const void *q, uint32_t num_q_heads, float scale, void *out,
+                                uint32_t out_dtype, void *workspace, size_t workspace_bytes,
+                                uint32_t flags, void *stream);
+
+/* Workspace bytes hp_paged_attention (f16 or bf16 pools) or
+ * hp_paged_attention_q8 (int8 pools) needs for this descriptor (its
  * num_seqs, total_tokens and geometry); 0 for an invalid descriptor or an
  * unsupported shape. */
 size_t hp_attention_workspace_bytes(const hp_desc *desc, uint32_t num_q_heads);

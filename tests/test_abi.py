@@ -27,7 +27,8 @@ def test_every_declared_symbol_is_exported():
                           "hp_gather_dequant", "hp_status_str", "hp_last_hip_error",
                           "hp_gather_batch", "hp_scatter_batch", "hp_gather_dequant_batch",
                           "hp_copy_pages", "hp_copy_pages_batch", "hp_gather_dequant_q",
-                          "hp_paged_attention", "hp_attention_workspace_bytes",
+                          "hp_paged_attention", "hp_paged_attention_q8",
+                          "hp_attention_workspace_bytes",
                           "hp_scatter_quant", "hp_validate_async", "hp_validate_verdict",
                           "hp_gather_static", "hp_validate_writes",
                           "hp_disjoint_workspace_bytes"}
@@ -240,7 +241,10 @@ def test_attention_rejections():
 def test_attention_workspace_bytes():
     f = desc()
     assert L.hp_attention_workspace_bytes(None, 8) == 0
-    assert L.hp_attention_workspace_bytes(ctypes.byref(desc(dtype=hp.DTYPE["i8"])), 8) == 0
+    assert L.hp_attention_workspace_bytes(ctypes.byref(desc(dtype=hp.DTYPE["f32"])), 8) == 0
+    # int8 pools (hp_paged_attention_q8) need the same workspace as 16-bit ones
+    assert L.hp_attention_workspace_bytes(ctypes.byref(desc(dtype=hp.DTYPE["i8"])), 8) == \
+        L.hp_attention_workspace_bytes(ctypes.byref(f), 8)
     assert L.hp_attention_workspace_bytes(ctypes.byref(f), 6) == 0
     for hq in (4, 12, 20, 28, 44, 256):                            # any group size is accepted
         assert L.hp_attention_workspace_bytes(ctypes.byref(f), hq) > 0
@@ -249,6 +253,42 @@ def test_attention_workspace_bytes():
     assert 0 < a < b
     big = desc(total_tokens=1 << 20, num_pages=1 << 17)
     assert L.hp_attention_workspace_bytes(ctypes.byref(big), 8) > a
+
+
+KS = ALIGNED + 0x60000000   # K scales
+VS = ALIGNED + 0x70000000   # V scales
+
+
+def attn8(d, v=ALIGNED + 0x40000000, vs=VS, q=ALIGNED + 0x50000000, hq=8, out=OUT, ws=None,
+          n=None, flags=0):
+    if ws is None:
+        ws = ALIGNED + 0x200000000
+        n = 1 << 30 if n is None else n
+    return L.hp_paged_attention_q8(ctypes.byref(d) if d is not None else None, v, vs, q, hq,
+                                   0.125, out, hp.DTYPE["f32"], ws, n or 0, flags, None)
+
+
+def test_attention_q8_rejections():
+    f = desc(dtype=hp.DTYPE["i8"], scales=KS)
+    assert attn8(desc(dtype=hp.DTYPE["i8"], num_seqs=0, num_block_entries=0,
+                      total_tokens=0)) == S["HP_OK"]             # no work, scales not needed
+    assert attn8(None) == S["HP_ERR_NULL"]
+    assert attn8(desc(dtype=hp.DTYPE["f16"], scales=KS)) == S["HP_ERR_DTYPE"]
+    assert attn8(desc(dtype=hp.DTYPE["bf16"], scales=KS)) == S["HP_ERR_DTYPE"]
+    assert attn8(desc(dtype=hp.DTYPE["u8"], scales=KS)) == S["HP_ERR_DTYPE"]
+    assert attn8(desc(dtype=hp.DTYPE["i8"])) == S["HP_ERR_NULL"]     # no K scales
+    assert attn8(f, vs=None) == S["HP_ERR_NULL"]
+    assert attn8(f, v=None) == S["HP_ERR_NULL"]
+    assert attn8(f, vs=VS + 4) == S["HP_ERR_ALIGN"]
+    assert attn8(desc(dtype=hp.DTYPE["i8"], scales=KS + 4)) == S["HP_ERR_ALIGN"]
+    assert attn8(f, hq=6) == S["HP_ERR_ARG"]
+    assert attn8(f, flags=hp.HP_FLAG_GATED) == S["HP_ERR_ARG"]
+    need = L.hp_attention_workspace_bytes(ctypes.byref(f), 8)
+    assert attn8(f, n=need - 1) == S["HP_ERR_WORKSPACE"]
+    assert attn8(f, out=KS + 64) == S["HP_ERR_ARG"]               # out over the K scales
+    assert attn8(f, out=VS) == S["HP_ERR_ARG"]                    # out over the V scales
+    assert attn8(f, ws=VS - 256, n=need) == S["HP_ERR_ARG"]       # workspace over the V scales
+    assert attn8(f, out=ALIGNED + 64) == S["HP_ERR_ARG"]          # out over the K pool
 
 
 def sq(d, src=OUT, sdt=None, zp=None, flags=0):
