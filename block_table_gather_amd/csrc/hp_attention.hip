@@ -122,25 +122,33 @@ __device__ __forceinline__ u32x2 ld8(const unsigned char *p) {
 }
 
 // Attention over int8 pools with per-slot scales ([Hurray] Per-page-slot
-// parameters) reads each element as the dequant-gather writes it: the fp32
-// product of the code and its slot's scale, rounded to bf16 (round to
-// nearest even). The kernels load 8 codes and the scale, and turn them into
-// the 16-byte vector of 8 bf16 values that a bf16 pool would hold there, so
-// everything after the load is the bf16 path.
+// parameters: every element of a slot's row is its code times the slot's
+// scale). A token's scale is common to its whole row, so it comes out of the
+// sums: x_t = (scale * sK_t) * sum_d q_d c_td, and V enters as the weight
+// p_t * sV_t times the codes. The codes (|c| <= 128) are exact in bf16, so
+// the 16-bit products run on the codes themselves; the kernels load 8 codes
+// and the slot's scale.
 struct Raw8 {
     u32x2 v;  // 8 int8 codes
     float s;  // their slot's scale
 };
-__device__ __forceinline__ u32x4 dequant8(const u32x2 &w, float s) {
+// 8 int8 codes as the 16-byte vector of their bf16 values (exact).
+__device__ __forceinline__ u32x4 codes_bf16(const u32x2 &w) {
     u32x4 o;
-    o.x = pack_bf16x2(sbyte(w.x, 0) * s, sbyte(w.x, 1) * s);
-    o.y = pack_bf16x2(sbyte(w.x, 2) * s, sbyte(w.x, 3) * s);
-    o.z = pack_bf16x2(sbyte(w.y, 0) * s, sbyte(w.y, 1) * s);
-    o.w = pack_bf16x2(sbyte(w.y, 2) * s, sbyte(w.y, 3) * s);
+    o.x = pack_bf16x2(sbyte(w.x, 0), sbyte(w.x, 1));
+    o.y = pack_bf16x2(sbyte(w.x, 2), sbyte(w.x, 3));
+    o.z = pack_bf16x2(sbyte(w.y, 0), sbyte(w.y, 1));
+    o.w = pack_bf16x2(sbyte(w.y, 2), sbyte(w.y, 3));
     return o;
 }
 __device__ __forceinline__ u32x4 bits8(const u32x4 &v) { return v; }
-__device__ __forceinline__ u32x4 bits8(const Raw8 &r) { return dequant8(r.v, r.s); }
+__device__ __forceinline__ u32x4 bits8(const Raw8 &r) { return codes_bf16(r.v); }
+// The codes of a loaded int8 chunk.
+__device__ __forceinline__ u32x2 row_bits(const Raw8 &r) { return r.v; }
+__device__ __forceinline__ u32x2 row_bits(const u32x4 &v) { return u32x2{v.x, v.y}; }
+// The scale a token's score (or weight) takes: 1 for 16-bit pools.
+__device__ __forceinline__ float row_scale(const u32x4 &) { return 1.0f; }
+__device__ __forceinline__ float row_scale(const Raw8 &r) { return r.s; }
 // Loaded form of 8 elements: the 16-bit values themselves, or codes + scale.
 template <bool Q8>
 using Loaded8 = std::conditional_t<Q8, Raw8, u32x4>;
@@ -380,9 +388,11 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
 #pragma unroll
             for (int i = 0; i < TB; ++i) {
                 const u32x4 kb = bits8(kq[i]);
+                // int8 pools: the token's K scale joins the softmax scale
+                const float xs = Q8 ? a.qscale * row_scale(kq[i]) : a.qscale;
 #pragma unroll
                 for (int gi = 0; gi < GT; ++gi) {
-                    const float dot = group_sum<LPH, GT == 1>(dot8<ET>(qp[gi], kb)) * a.qscale;
+                    const float dot = group_sum<LPH, GT == 1>(dot8<ET>(qp[gi], kb)) * xs;
                     x[gi][i] = ok[i] ? dot : -__builtin_inff();
                 }
             }
@@ -410,12 +420,22 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
 #pragma unroll
             for (int i = 0; i < TB; ++i) {
                 float vf[8];
-                unpack8<ET>(bits8(vq[i]), vf);
+                if constexpr (Q8) {
 #pragma unroll
-                for (int gi = 0; gi < GT; ++gi)
+                    for (int e = 0; e < 8; ++e)  // the codes (exact)
+                        vf[e] = sbyte(e < 4 ? row_bits(vq[i]).x : row_bits(vq[i]).y, e & 3);
+                } else {
+                    unpack8<ET>(bits8(vq[i]), vf);
+                }
+#pragma unroll
+                for (int gi = 0; gi < GT; ++gi) {
+                    // int8 pools: the weight times the token's V scale (the sum
+                    // of weights l stays unscaled)
+                    const float pv = Q8 ? p[gi][i] * row_scale(vq[i]) : p[gi][i];
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        acc[gi][e] = __builtin_fmaf(p[gi][i], vf[e], acc[gi][e]);
+                        acc[gi][e] = __builtin_fmaf(pv, vf[e], acc[gi][e]);
+                }
             }
         }
     }
@@ -616,10 +636,9 @@ __device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_o
     // 198 us with whole rows for both K and V). K and V both go through the wave's
     // tile buffer in LDS, K on to the B layout of the score product. Tokens
     // past n repeat the last token (a real row; masked below).
-    // (int8 pools: 8 bytes of codes per chunk, and lane i < 32 loads the
-    // scale of the tile's token i; each chunk's codes take their token's
-    // scale from that lane and become the chunk's 16 bytes of bf16 on the way
-    // into LDS)
+    // (int8 pools: 8 bytes of codes per chunk, which become the chunk's 16
+    // bytes of bf16 on the way into LDS, and lane i < 32 loads the scale of
+    // the tile's token i, which the score and the weight of that token take)
     V8 kb[2][KK];
     constexpr uint32_t C16 = Q8 ? 1 : 2 * KK, C8 = Q8 ? 2 * KK : 1;
     u32x4 kc[C16], vc[C16];
@@ -647,14 +666,14 @@ __device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_o
         }
     };
     // token-major rows of VRB bytes
-    auto store_rows = [&](const u32x4 (&s16)[C16], const u32x2 (&s8)[C8], float sc) {
+    auto store_rows = [&](const u32x4 (&s16)[C16], const u32x2 (&s8)[C8]) {
 #pragma unroll
         for (uint32_t c = 0; c < 2 * KK; ++c) {
             const uint32_t ch = 64 * c + lane;
             const uint32_t jt = ch / (D / 8), dc = ch % (D / 8);
             u32x4 v;
             if constexpr (Q8)
-                v = dequant8(s8[c], __shfl(sc, (int)jt, 64));
+                v = codes_bf16(s8[c]);
             else
                 v = s16[c];
             *reinterpret_cast<u32x4 *>(vt + jt * VRB + 16 * dc) = v;
@@ -664,7 +683,7 @@ __device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_o
     // 64 kk + 16 grp of its row
     auto stage_k = [&]() {
         wave_lds_sync();  // the previous tile's reads of the buffer are done
-        store_rows(kc, kc8, ksc);
+        store_rows(kc, kc8);
         wave_lds_sync();
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -690,9 +709,11 @@ __device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_o
             for (uint32_t kk = 0; kk < KK; ++kk)
                 acc = M::mma(qa[kk], kb[b][kk], acc);
             const bool ok = tb + 16 * b + c16 < n;
+            // int8 pools: the K scale of token 16 b + c16 joins the softmax scale
+            const float xs = Q8 ? a.qscale * __shfl(ksc, (int)(16 * b + c16), 64) : a.qscale;
 #pragma unroll
             for (int i = 0; i < R; ++i)
-                x[b][i] = ok ? acc[i] * a.qscale : -__builtin_inff();
+                x[b][i] = ok ? acc[i] * xs : -__builtin_inff();
         }
         if constexpr (more)
             load_rows(a.k_pool, a.k_scales, tb + kMfmaTile, kc, kc8, ksc);
@@ -731,13 +752,15 @@ __device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_o
         for (int b = 0; b < 2; ++b) {
             const uint32_t t = 16 * b + c16;
             const uint32_t col = 8 * (t & 3) + (t >> 2);
+            // int8 pools: the weight times the token's V scale (l stays unscaled)
+            const float vs = Q8 ? __shfl(vsc, (int)t, 64) : 1.0f;
 #pragma unroll
             for (int i = 0; i < R; ++i)
-                pt[(4 * grp + i) * kPRow + col] = p[b][i];
+                pt[(4 * grp + i) * kPRow + col] = Q8 ? p[b][i] * vs : p[b][i];
         }
         // V tile to LDS (the buffer's K reads are done: the score products
         // consumed them)
-        store_rows(vc, vc8, vsc);
+        store_rows(vc, vc8);
         wave_lds_sync();
         if constexpr (more)
             load_rows(a.v_pool, a.v_scales, tb + kMfmaTile, vc, vc8, vsc);
@@ -810,10 +833,13 @@ constexpr uint32_t kMinSharedTokens = 64;     // two matrix tiles
 
 // One 32-token tile of a wave against K and V tiles in LDS (token-major
 // rows of v_row_bytes): the online softmax of all 16 rows, as in mfma_span.
-template <typename ET, int D>
+// Q8: the tiles hold int8 codes as bf16, and kss / vss the tile's 32 K and V
+// scales.
+template <typename ET, int D, bool Q8>
 __device__ __forceinline__ void lds_tile(const AArgs &a, const unsigned char *kt,
-                                         const unsigned char *vt, float *pt, uint32_t tb,
-                                         uint32_t n, const typename Mma<ET>::V8 (&qa)[D / 32],
+                                         const unsigned char *vt, const float *kss,
+                                         const float *vss, float *pt, uint32_t tb, uint32_t n,
+                                         const typename Mma<ET>::V8 (&qa)[D / 32],
                                          float (&m)[4], float (&l)[4], f32x4 (&o)[D / 16]) {
 #pragma clang fp contract(off)
     using M = Mma<ET>;
@@ -833,9 +859,10 @@ __device__ __forceinline__ void lds_tile(const AArgs &a, const unsigned char *kt
                                                        16 * grp),
                          acc);
         const bool ok = tb + 16 * b + c16 < n;
+        const float xs = Q8 ? a.qscale * kss[16 * b + c16] : a.qscale;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            x[b][i] = ok ? acc[i] * a.qscale : -__builtin_inff();
+            x[b][i] = ok ? acc[i] * xs : -__builtin_inff();
     }
     float p[2][4], mx[4];
     bool grow = false;
@@ -865,9 +892,10 @@ __device__ __forceinline__ void lds_tile(const AArgs &a, const unsigned char *kt
     for (int b = 0; b < 2; ++b) {
         const uint32_t t = 16 * b + c16;
         const uint32_t col = 8 * (t & 3) + (t >> 2);
+        const float vs = Q8 ? vss[t] : 1.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            pt[(4 * grp + i) * kPRow + col] = p[b][i];
+            pt[(4 * grp + i) * kPRow + col] = Q8 ? p[b][i] * vs : p[b][i];
     }
     wave_lds_sync();
     V8 pa[3];
@@ -933,6 +961,8 @@ __device__ __forceinline__ void shared_item(const AArgs &a, uint32_t w, uint32_t
     // region's tile
     unsigned char *region = lds + a.pg_area;
     constexpr uint32_t WL = (uint32_t)mfma_wave_lds<D>();
+    // int8 pools: the K and V scales of each stage's 32 tokens, after the tiles
+    float *scl = reinterpret_cast<float *>(region + kMfmaWaves * WL);  // [stage][K, V][32]
     const uint32_t wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
     float *pt = reinterpret_cast<float *>(region + wave * WL + kMfmaTile * VRB);
     const uint32_t c16 = lane & 15, grp = lane >> 4;
@@ -977,7 +1007,8 @@ __device__ __forceinline__ void shared_item(const AArgs &a, uint32_t w, uint32_t
 
     // thread t loads chunk t + 256 e of the tile: 16 bytes of the head row of
     // token (t + 256 e) / (D / 8), so a wave's load covers whole rows
-    // (int8 pools: 8 bytes of codes and the slot's scale per chunk)
+    // (int8 pools: 8 bytes of codes and the slot's scale per chunk; the
+    // codes go to LDS as bf16, each token's scales beside the tiles)
     Loaded8<Q8> kr[CPT], vr[CPT];
     auto load = [&](uint32_t tb) {
 #pragma unroll
@@ -1009,13 +1040,18 @@ __device__ __forceinline__ void shared_item(const AArgs &a, uint32_t w, uint32_t
             const uint32_t jt = ch / (D / 8), dc = ch % (D / 8);
             *reinterpret_cast<u32x4 *>(kt + jt * VRB + 16 * dc) = bits8(kr[e]);
             *reinterpret_cast<u32x4 *>(vt + jt * VRB + 16 * dc) = bits8(vr[e]);
+            if (Q8 && dc == 0) {
+                scl[(2 * stage) * kMfmaTile + jt] = row_scale(kr[e]);
+                scl[(2 * stage + 1) * kMfmaTile + jt] = row_scale(vr[e]);
+            }
         }
         // the stage is written; every wave finished the tile that last used
         // the other stage before it reached this barrier
         __syncthreads();
         if (tb + kMfmaTile < n)
             load(tb + kMfmaTile);
-        lds_tile<ET, D>(a, kt, vt, pt, tb, n, qa, m, l, o);
+        lds_tile<ET, D, Q8>(a, kt, vt, scl + (2 * stage) * kMfmaTile,
+                            scl + (2 * stage + 1) * kMfmaTile, pt, tb, n, qa, m, l, o);
         stage ^= 1;
     }
 
@@ -1604,8 +1640,10 @@ hipError_t launch_attention_mfma(const AArgs &a, const AttentionShape &sh, bool 
     const dim3 grid((uint32_t)(sh.cap_units + a.num_seqs +
                                (a.shared ? kMfmaWaves * sh.cap_work : 0)),
                     sh.head_groups, (a.group + kMfmaRows - 1) / kMfmaRows);
+    // (int8 pools: the shared pass keeps two stages of K and V scales too)
     const size_t lds = (a.fused ? ((4 * (size_t)a.num_seqs + 15) & ~(size_t)15) : 0) +
-                       a.pg_area + kMfmaWaves * mfma_wave_lds<D>();
+                       a.pg_area + kMfmaWaves * mfma_wave_lds<D>() +
+                       (Q8 ? 2 * 2 * kMfmaTile * sizeof(float) : 0);
     if (nt)
         hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, true, R, Q8>), grid,
                            dim3(kAttnThreads), lds, stream, a);

@@ -99,6 +99,9 @@ def _load():
     lib.oracle_paged_attention.restype = ctypes.c_int
     lib.oracle_paged_attention.argtypes = [_vp, _vp, _vp, ctypes.c_uint32, _u64, _u64, _u64,
                                            _u64, ctypes.c_double, _vp, _vp, _vp, _u64, _vp]
+    lib.oracle_paged_attention_q8.restype = ctypes.c_int
+    lib.oracle_paged_attention_q8.argtypes = [_vp, _vp, _vp, _vp, _vp, _u64, _u64, _u64, _u64,
+                                              ctypes.c_double, _vp, _vp, _vp, _u64, _vp]
     _lib = lib
     return lib
 
@@ -331,6 +334,37 @@ def paged_attention(q, k_pool, v_pool, elem_type, *, page_size, num_kv_heads, he
                                     page_size, num_kv_heads, head_dim, Hq, float(scale),
                                     _ptr(bt) if len(bt) else None, _ptr(sp), _ptr(sl), S,
                                     _ptr(out))
+    if rc != 0:
+        raise ValueError("num_q_heads must be a positive multiple of num_kv_heads")
+    return out
+
+
+def paged_attention_q8(q, k_pool, k_scales, v_pool, v_scales, *, page_size, num_kv_heads,
+                       head_dim, block_table, seq_ptr, seq_lens, scale):
+    """Decode attention over int8 K/V pools with one float32 scale per slot,
+    float64 [num_seqs, num_q_heads, head_dim]: every element's value is its
+    code times its slot's scale. q: bfloat16 bit patterns (uint16)
+    [num_seqs, num_q_heads, head_dim]; pools int8 [num_pages, page_size,
+    num_kv_heads, head_dim]; scales float32 [num_pages * page_size]."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k_pool = np.ascontiguousarray(k_pool).view(np.int8)
+    v_pool = np.ascontiguousarray(v_pool).view(np.int8)
+    k_scales = np.ascontiguousarray(k_scales, dtype=np.float32)
+    v_scales = np.ascontiguousarray(v_scales, dtype=np.float32)
+    assert q.ndim == 3 and q.shape[2] == head_dim
+    S, Hq = q.shape[0], q.shape[1]
+    bt, sp, sl = _idx(block_table), _idx(seq_ptr), _idx(seq_lens)
+    assert len(sp) == S + 1 and len(sl) == S
+    assert k_pool.size == v_pool.size and k_scales.size * num_kv_heads * head_dim == k_pool.size
+    assert v_scales.size == k_scales.size
+    out = np.empty((S, Hq, head_dim), dtype=np.float64)
+    if S == 0:
+        return out
+    rc = lib.oracle_paged_attention_q8(_ptr(q), _ptr(k_pool), _ptr(k_scales), _ptr(v_pool),
+                                       _ptr(v_scales), page_size, num_kv_heads, head_dim, Hq,
+                                       float(scale), _ptr(bt) if len(bt) else None, _ptr(sp),
+                                       _ptr(sl), S, _ptr(out))
     if rc != 0:
         raise ValueError("num_q_heads must be a positive multiple of num_kv_heads")
     return out

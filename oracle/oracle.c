@@ -534,13 +534,32 @@ void oracle_decode(uint32_t elem_type, const void *src, uint64_t n, double *out)
         out[i] = element_value(elem_type, src, i);
 }
 
+/* A K or V pool as the attention oracle reads it: stored floats of one
+ * element type, or (scales != NULL) int8 codes whose value is the code times
+ * its slot's scale ([Hurray] Per-page-slot parameters: one scale per
+ * physical slot, for every element of the slot's row; the product of an
+ * 8-bit code and a binary32 scale is exact in binary64). */
+struct kv_pool {
+    const void *base;
+    uint32_t elem_type;    /* ORACLE_F16 / BF16 / F32 (when scales is NULL) */
+    const float *scales;   /* int8 codes: num_pages * page_size scales */
+    uint64_t row_elems;    /* elements of one slot: num_kv_heads * head_dim */
+};
+
+static double kv_value(const struct kv_pool *p, uint64_t i)
+{
+    if (p->scales)
+        return (double)((const int8_t *)p->base)[i] * (double)p->scales[i / p->row_elems];
+    return element_value(p->elem_type, p->base, i);
+}
+
 /* Softmax attention of one query row over a sequence's cached tokens, the
  * keys and values found through the block table one token at a time. */
-int oracle_paged_attention(const void *q, const void *k_pool, const void *v_pool,
-                           uint32_t elem_type, uint64_t page_size, uint64_t num_kv_heads,
-                           uint64_t head_dim, uint64_t num_q_heads, double scale,
-                           const uint64_t *block_table, const uint64_t *seq_ptr,
-                           const uint64_t *seq_lens, uint64_t num_seqs, double *out)
+static int attention(const void *q, uint32_t q_type, const struct kv_pool *k,
+                     const struct kv_pool *v, uint64_t page_size, uint64_t num_kv_heads,
+                     uint64_t head_dim, uint64_t num_q_heads, double scale,
+                     const uint64_t *block_table, const uint64_t *seq_ptr,
+                     const uint64_t *seq_lens, uint64_t num_seqs, double *out)
 {
     uint64_t s, hq, t, d, group, max_len = 0;
     double *x;
@@ -571,11 +590,9 @@ int oracle_paged_attention(const void *q, const void *k_pool, const void *v_pool
             for (t = 0; t < L; t++) {
                 double dot = 0.0;
                 for (d = 0; d < head_dim; d++) {
-                    double qv = element_value(elem_type, q,
-                                              (s * num_q_heads + hq) * head_dim + d);
-                    double kv = element_value(elem_type, k_pool,
-                                              pool_index(block_table, seq_ptr, s, t, hkv, d,
-                                                         page_size, num_kv_heads, head_dim));
+                    double qv = element_value(q_type, q, (s * num_q_heads + hq) * head_dim + d);
+                    double kv = kv_value(k, pool_index(block_table, seq_ptr, s, t, hkv, d,
+                                                       page_size, num_kv_heads, head_dim));
                     dot += qv * kv;
                 }
                 x[t] = scale * dot;
@@ -590,15 +607,41 @@ int oracle_paged_attention(const void *q, const void *k_pool, const void *v_pool
             for (d = 0; d < head_dim; d++) {
                 double num = 0.0;
                 for (t = 0; t < L; t++)
-                    num += x[t] * element_value(elem_type, v_pool,
-                                                pool_index(block_table, seq_ptr, s, t, hkv, d,
-                                                           page_size, num_kv_heads, head_dim));
+                    num += x[t] * kv_value(v, pool_index(block_table, seq_ptr, s, t, hkv, d,
+                                                         page_size, num_kv_heads, head_dim));
                 o[d] = num / denom;
             }
         }
     }
     free(x);
     return 0;
+}
+
+int oracle_paged_attention(const void *q, const void *k_pool, const void *v_pool,
+                           uint32_t elem_type, uint64_t page_size, uint64_t num_kv_heads,
+                           uint64_t head_dim, uint64_t num_q_heads, double scale,
+                           const uint64_t *block_table, const uint64_t *seq_ptr,
+                           const uint64_t *seq_lens, uint64_t num_seqs, double *out)
+{
+    const struct kv_pool k = {k_pool, elem_type, NULL, num_kv_heads * head_dim};
+    const struct kv_pool v = {v_pool, elem_type, NULL, num_kv_heads * head_dim};
+    return attention(q, elem_type, &k, &v, page_size, num_kv_heads, head_dim, num_q_heads,
+                     scale, block_table, seq_ptr, seq_lens, num_seqs, out);
+}
+
+int oracle_paged_attention_q8(const void *q, const int8_t *k_pool, const float *k_scales,
+                              const int8_t *v_pool, const float *v_scales, uint64_t page_size,
+                              uint64_t num_kv_heads, uint64_t head_dim, uint64_t num_q_heads,
+                              double scale, const uint64_t *block_table,
+                              const uint64_t *seq_ptr, const uint64_t *seq_lens,
+                              uint64_t num_seqs, double *out)
+{
+    const struct kv_pool k = {k_pool, 0, k_scales, num_kv_heads * head_dim};
+    const struct kv_pool v = {v_pool, 0, v_scales, num_kv_heads * head_dim};
+    if (!k_scales || !v_scales)
+        return -1;
+    return attention(q, ORACLE_BF16, &k, &v, page_size, num_kv_heads, head_dim, num_q_heads,
+                     scale, block_table, seq_ptr, seq_lens, num_seqs, out);
 }
 
 /* One binary32 value as rint would give it, clamped to [lo, hi] (exact: the

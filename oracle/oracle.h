@@ -208,6 +208,19 @@ int oracle_paged_attention(const void *q, const void *k_pool, const void *v_pool
                            const uint64_t *block_table, const uint64_t *seq_ptr,
                            const uint64_t *seq_lens, uint64_t num_seqs, double *out);
 
+/* The same attention over int8 K and V pools with one binary32 scale per
+ * physical slot ([Hurray] Per-page-slot parameters: the value of every
+ * element of slot page * page_size + r is its code times scales[that slot]):
+ * K[t][hkv][d] = k_pool[...] * k_scales[slot of t], likewise V, both exact in
+ * binary64; q holds bfloat16 bit patterns. Returns -1 for the cases above or
+ * a NULL scale array. */
+int oracle_paged_attention_q8(const void *q, const int8_t *k_pool, const float *k_scales,
+                              const int8_t *v_pool, const float *v_scales, uint64_t page_size,
+                              uint64_t num_kv_heads, uint64_t head_dim, uint64_t num_q_heads,
+                              double scale, const uint64_t *block_table,
+                              const uint64_t *seq_ptr, const uint64_t *seq_lens,
+                              uint64_t num_seqs, double *out);
+
 /* Quantization of one slot's row on write (quantize-on-scatter). The pages
  * fix only where the parameters live ([Hurray] Per-page-slot parameters: one
  * scale, and one zero point for an asymmetric scheme, per physical slot); the

@@ -1,21 +1,20 @@
 """GPU parity of decode attention over int8 K/V pools with one fp32 scale per
 slot (hp_paged_attention_q8).
 
-The call is defined as hp_paged_attention over bf16 pools that hold, in every
-slot, the values hp_gather_dequant writes: bf16_rne(fp32(code) * scale). Each
-case checks, on the same seeded inputs:
+Every element's value is its code times its slot's scale ([Hurray]
+Per-page-slot parameters). The kernels take the scale out of each token's
+sums (x_t = scale sK_t q . c_t, weight p_t sV_t on the codes of V), which
+changes only the fp32 rounding. Each case checks, on the same seeded inputs:
 
-* the dequantized pools: hp_gather_dequant over an identity table (every slot
-  of every page, in pool order) against the oracle's gather_dequant, bit for
-  bit;
-* the int8 call against hp_paged_attention over those bf16 pools, bit for
-  bit (same units, same arithmetic);
-* the int8 call against the oracle's attention (binary64) over the oracle's
-  dequantized pools, within the fp32 bound of test_gpu_attention.
+* against the oracle (binary64 over code * scale), with slot scales drawn
+  from U[1e-3, 1e-1], within the fp32 bound of test_gpu_attention;
+* with slot scales that are powers of two, bit for bit against
+  hp_paged_attention over bf16 pools holding code * scale (which bf16 holds
+  exactly, written by hp_gather_dequant): scaling by a power of two commutes
+  with every rounding, so taking the scale out of the sums changes nothing.
 """
 import dataclasses
 import math
-import types
 
 import numpy as np
 import pytest
@@ -24,10 +23,11 @@ import torch
 import oracle
 import workloads
 from gpu_util import OnDevice, assert_bits_equal, host_bits, idx_tensor, say
-from test_gpu_attention import check, shared_prefix_workload
+from test_gpu_attention import shared_prefix_workload
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+U = 2.0 ** -24
 
 
 @pytest.fixture(scope="module")
@@ -36,17 +36,36 @@ def hp():
     return block_table_gather_amd
 
 
-def int8_inputs(w, group, seed):
+def pow2_scales(n, seed):
+    """Slot scales 2^-10 .. 2^-3, drawn per slot."""
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    e = torch.randint(-10, -2, (n,), generator=g, device=DEV)
+    return torch.ldexp(torch.ones(n, device=DEV), e)
+
+
+def int8_inputs(w, group, seed, pow2=False):
     """int8 K pool and K scales (the workload's), an int8 V pool and V scales
-    from another seed, bf16 queries."""
+    from another seed, bf16 queries. pow2: power-of-two scales."""
     w = dataclasses.replace(w, dtype="i8", values="int8", with_scales=True)
     d = OnDevice(w)
     v = dataclasses.replace(w, seed=w.seed * 7 + 3)
     v_pool, v_scales = v.make_pool(DEV), v.make_scales(DEV)
+    if pow2:
+        n = w.num_pages * w.page_size
+        d.scales.copy_(pow2_scales(n, seed + 1))
+        v_scales = pow2_scales(n, seed + 2)
     g = torch.Generator(device=DEV).manual_seed(seed)
     q = torch.randn((w.num_seqs, w.num_heads * group, w.head_dim), generator=g, device=DEV,
                     dtype=torch.float32).to(torch.bfloat16)
     return w, d, v_pool, v_scales, q
+
+
+def run_q8(hp, w, d, v_pool, v_scales, q, scale, streaming=False):
+    out = torch.full((w.num_seqs, q.shape[1], w.head_dim), float("nan"), device=DEV)
+    hp.paged_attention_q8(d.desc, v_pool, v_scales, q, out, total_tokens=w.total_tokens,
+                          scale=scale, streaming=streaming)
+    torch.cuda.synchronize()
+    return out
 
 
 def dequant_pool(hp, pool, scales):
@@ -62,42 +81,75 @@ def dequant_pool(hp, pool, scales):
     return out.view(N, P, H, D)
 
 
-def oracle_dequant_pool(pool_bits, scales):
-    N, P, H, D = pool_bits.shape
-    return oracle.gather_dequant(pool_bits.view(np.int8), scales, page_size=P, num_heads=H,
-                                 head_dim=D, block_table=np.arange(N, dtype=np.uint64),
-                                 seq_ptr=np.array([0, N], dtype=np.uint64),
-                                 seq_lens=np.array([N * P], dtype=np.uint64)).reshape(N, P, H, D)
+def slot_ids(w):
+    out = []
+    for s in range(w.num_seqs):
+        base = int(w.seq_ptr[s])
+        t = np.arange(int(w.seq_lens[s]), dtype=np.int64)
+        phys = w.block_table[base + t // w.page_size].astype(np.int64)
+        out.append(phys * w.page_size + t % w.page_size)
+    return out
 
 
-def run_pair(hp, w, d, v_pool, v_scales, q, scale, streaming=False):
-    """(int8 call, bf16 call over the dequantized pools, the bf16 pools)."""
-    out8 = torch.full((w.num_seqs, q.shape[1], w.head_dim), float("nan"), device=DEV)
-    hp.paged_attention_q8(d.desc, v_pool, v_scales, q, out8, total_tokens=w.total_tokens,
-                          scale=scale, streaming=streaming)
+def tolerance(w, qv, kc, ks, vc, vs, scale, group):
+    """The fp32 bound of test_gpu_attention per (sequence, query head), over
+    the float64 values code * scale of the slots each sequence holds (codes
+    kc, vc [slots, H, D], scales ks, vs [slots])."""
+    heads = np.arange(qv.shape[1]) // group
+    tol = np.zeros(qv.shape[:2])
+    for i, ids in enumerate(slot_ids(w)):
+        L = len(ids)
+        if L == 0:
+            continue
+        Ks = (kc[ids].astype(np.float64) * ks[ids].astype(np.float64)[:, None, None])[:, heads, :]
+        Vs = vc[ids].astype(np.float64) * vs[ids].astype(np.float64)[:, None, None]
+        A = np.abs(scale * qv[i][None, :, :] * Ks).sum(axis=2).max(axis=0)
+        vmax = np.abs(Vs).max(axis=(0, 2))[heads]
+        delta = 2 * (w.head_dim + 16) * U * A + (3 * L + 16) * U
+        tol[i] = 2.5 * delta * vmax
+    return tol
+
+
+def oracle_check(w, got, d, v_pool, v_scales, q, group, scale, what):
+    H, D = w.num_heads, w.head_dim
+    kc, vc = host_bits(d.pool).view(np.int8), host_bits(v_pool).view(np.int8)
+    ks, vs = d.scales.cpu().numpy(), v_scales.cpu().numpy()
+    qb = host_bits(q)
+    want = oracle.paged_attention_q8(qb, kc, ks, vc, vs, page_size=w.page_size,
+                                     num_kv_heads=H, head_dim=D, block_table=w.block_table,
+                                     seq_ptr=w.seq_ptr, seq_lens=w.seq_lens, scale=scale)
+    tol = tolerance(w, oracle.decode(qb, "bf16"), kc.reshape(-1, H, D), ks,
+                    vc.reshape(-1, H, D), vs, scale, group)
+    g = got.astype(np.float64)
+    assert not np.isnan(g).any(), f"{what}: NaN in the output"
+    err = np.abs(g - want).max(axis=2) if g.size else np.zeros(tol.shape)
+    ratio = float(np.max(err / np.maximum(tol, 1e-300))) if err.size else 0.0
+    say(f"{what}: max error {float(err.max()) if err.size else 0:.3e}, "
+        f"max error / bound {ratio:.3e}")
+    bad = np.argwhere(err > tol)
+    assert not len(bad), (f"{what}: {len(bad)} (seq, head) pairs over the bound; first "
+                          f"{bad[:4].tolist()}")
+
+
+def pow2_check(hp, w, d, v_pool, v_scales, q, scale, what, streaming=False):
+    """Power-of-two scales: equal, bit for bit, to the 16-bit call over bf16
+    pools holding code * scale."""
+    out8 = run_q8(hp, w, d, v_pool, v_scales, q, scale, streaming)
     kb, vb = dequant_pool(hp, d.pool, d.scales), dequant_pool(hp, v_pool, v_scales)
-    desc16 = hp.Descriptor(kb, d.bt, d.sp, d.sl)
     out16 = torch.full_like(out8, float("nan"))
-    hp.paged_attention(desc16, vb, q, out16, total_tokens=w.total_tokens, scale=scale,
-                       streaming=streaming)
+    hp.paged_attention(hp.Descriptor(kb, d.bt, d.sp, d.sl), vb, q, out16,
+                       total_tokens=w.total_tokens, scale=scale, streaming=streaming)
     torch.cuda.synchronize()
-    return out8, out16, kb, vb
-
-
-def full_check(hp, w, d, v_pool, v_scales, q, group, scale, what, streaming=False,
-               oracle_pools=True):
-    out8, out16, kb, vb = run_pair(hp, w, d, v_pool, v_scales, q, scale, streaming)
-    if oracle_pools:
-        assert_bits_equal(host_bits(kb), oracle_dequant_pool(host_bits(d.pool),
-                                                             d.scales.cpu().numpy()),
-                          f"{what}: K pool dequantized")
-        assert_bits_equal(host_bits(vb), oracle_dequant_pool(host_bits(v_pool),
-                                                             v_scales.cpu().numpy()),
-                          f"{what}: V pool dequantized")
     assert_bits_equal(host_bits(out8), host_bits(out16), f"{what}: int8 call vs bf16 call")
-    w16 = dataclasses.replace(w, dtype="bf16", values="normal", with_scales=False)
-    check(w16, out8.cpu().numpy(), q, types.SimpleNamespace(pool=kb), vb, group, scale,
-          what=what)
+
+
+def both_checks(hp, w0, group, seed, scale, what, streaming=False):
+    w, d, v_pool, v_scales, q = int8_inputs(w0, group, seed)
+    out = run_q8(hp, w, d, v_pool, v_scales, q, scale, streaming)
+    oracle_check(w, out.cpu().numpy(), d, v_pool, v_scales, q, group, scale, what)
+    w, d, v_pool, v_scales, q = int8_inputs(w0, group, seed, pow2=True)
+    pow2_check(hp, w, d, v_pool, v_scales, q, scale, what + " (power-of-two scales)",
+               streaming)
 
 
 CASES = [
@@ -125,9 +177,8 @@ def test_attention_q8_random(hp, case, seed):
     w = workloads.random_small(2100 + 10 * case + seed, max_seqs=12, max_len=300,
                                page_sizes=pages, heads=(hkv,), dims=(D,), dtypes=("i8",))
     say("attention int8", case, seed, group, w.describe())
-    w, d, v_pool, v_scales, q = int8_inputs(w, group, 2200 + 10 * case + seed)
-    full_check(hp, w, d, v_pool, v_scales, q, group, 1.0 / math.sqrt(D),
-               what=f"int8 case {case} seed {seed}")
+    both_checks(hp, w, group, 2200 + 10 * case + seed, 1.0 / math.sqrt(D),
+                what=f"int8 case {case} seed {seed}")
 
 
 @pytest.mark.parametrize("group", [1, 2, 4])
@@ -136,32 +187,35 @@ def test_attention_q8_streaming(hp, group):
     w = workloads.random_small(2300 + group, max_seqs=12, max_len=400, page_sizes=(16,),
                                heads=(6,), dims=(128,), dtypes=("i8",), alias=False)
     say("attention int8 streaming", group, w.describe())
-    w, d, v_pool, v_scales, q = int8_inputs(w, group, 2310 + group)
-    full_check(hp, w, d, v_pool, v_scales, q, group, 0.09, streaming=True,
-               what=f"int8 streaming G={group}")
+    both_checks(hp, w, group, 2310 + group, 0.09, what=f"int8 streaming G={group}",
+                streaming=True)
 
 
-def test_attention_q8_single_token_is_the_dequantized_row(hp):
-    """One cached token: the output is its dequantized value row, bit for bit."""
+@pytest.mark.parametrize("group", [1, 4])
+def test_attention_q8_single_token_is_its_value_row(hp, group):
+    """One cached token: its weight is 1, so the output is its value row,
+    the fp32 product code * scale (bit for bit on the vector path at G = 1;
+    within one ulp on the matrix cores at G = 4, which sum the weight's three
+    bf16 parts)."""
     w = workloads.random_small(2320, max_seqs=16, max_len=40, page_sizes=(16,), heads=(4,),
                                dims=(128,), dtypes=("i8",))
     w.seq_lens[:] = np.minimum(w.seq_lens, 1)
-    say("attention int8 single token", w.describe())
-    for group in (1, 4):
-        w, d, v_pool, v_scales, q = int8_inputs(w, group, 2321 + group)
-        out = torch.zeros((w.num_seqs, 4 * group, 128), device=DEV)
-        hp.paged_attention_q8(d.desc, v_pool, v_scales, q, out, total_tokens=w.total_tokens)
-        torch.cuda.synchronize()
-        vv = oracle.decode(oracle_dequant_pool(host_bits(v_pool), v_scales.cpu().numpy()),
-                           "bf16").reshape(-1, 4, 128)
-        got = out.cpu().numpy()
-        for s in range(w.num_seqs):
-            if w.seq_lens[s] == 0:
-                assert np.all(got[s] == 0)
-                continue
-            row = int(w.block_table[int(w.seq_ptr[s])]) * w.page_size
-            want = np.repeat(vv[row], group, axis=0)
-            assert np.array_equal(got[s].astype(np.float64), want), (group, s)
+    say("attention int8 single token", group, w.describe())
+    w, d, v_pool, v_scales, q = int8_inputs(w, group, 2321 + group)
+    out = run_q8(hp, w, d, v_pool, v_scales, q, 0.1).cpu().numpy()
+    codes = host_bits(v_pool).view(np.int8).reshape(-1, 4, 128)
+    sc = v_scales.cpu().numpy()
+    for s in range(w.num_seqs):
+        if w.seq_lens[s] == 0:
+            assert np.all(out[s] == 0)
+            continue
+        row = int(w.block_table[int(w.seq_ptr[s])]) * w.page_size
+        want = np.repeat(codes[row].astype(np.float32) * sc[row], group, axis=0)  # fp32 products
+        if group == 1:
+            assert np.array_equal(out[s], want), s
+        else:
+            ulp = np.spacing(np.abs(want))
+            assert np.all(np.abs(out[s] - want) <= ulp), s
 
 
 SHARED = [
@@ -179,9 +233,7 @@ def test_attention_q8_shared_prefixes(hp, case):
     D, G, H, P, idx, runs = SHARED[case]
     w = shared_prefix_workload(2400 + case, P, H, D, "i8", idx, runs)
     say("attention int8 shared prefixes", case, w.describe(), runs)
-    w, d, v_pool, v_scales, q = int8_inputs(w, G, 2410 + case)
-    full_check(hp, w, d, v_pool, v_scales, q, G, 1.0 / math.sqrt(D),
-               what=f"int8 shared {case}")
+    both_checks(hp, w, G, 2410 + case, 1.0 / math.sqrt(D), what=f"int8 shared {case}")
 
 
 def test_attention_q8_rejections(hp):
@@ -215,15 +267,15 @@ def test_attention_q8_rejections(hp):
     assert torch.count_nonzero(out) == 0
 
 
-def test_attention_q8_decode_workload(hp):
+@pytest.mark.parametrize("group", [1, 4])
+def test_attention_q8_decode_workload(hp, group):
     """The decode batch as int8 (64 sequences of 1..2048 tokens, 32 kv heads x
-    128, per-slot scales) with four query heads per kv head and streaming
-    loads: bit for bit against the bf16 call over the dequantized pools, and
-    every sequence and query head against the oracle."""
+    128, per-slot scales) with one and four query heads per kv head and
+    streaming loads, as the benchmark runs it: every sequence and query head
+    against the oracle, and bit for bit against the 16-bit call with
+    power-of-two scales."""
     w = workloads.decode()
-    say("attention int8 decode full", w.describe())
-    w, d, v_pool, v_scales, q = int8_inputs(w, 4, 2600)
-    full_check(hp, w, d, v_pool, v_scales, q, 4, 1.0 / math.sqrt(128), streaming=True,
-               what="int8 decode", oracle_pools=False)
-    del d, v_pool
+    say("attention int8 decode full", group, w.describe())
+    both_checks(hp, w, group, 2600 + group, 1.0 / math.sqrt(128), what=f"int8 decode G={group}",
+                streaming=True)
     torch.cuda.empty_cache()
