@@ -511,10 +511,10 @@ def paged_attention(desc, v_pool, q, out, *, total_tokens, scale=None, checked=F
 def paged_attention_q8(desc, v_pool, v_scales, q, out, *, total_tokens, scale=None,
                        checked=False, streaming=False, workspace=None, stream=None):
     """out[S, Hq, D] (float32) <- decode attention of bf16 q[S, Hq, D] over
-    int8 pools with one fp32 scale per slot: the K pool and K scales of `desc`
-    (its page_pool and scales), the V pool `v_pool` and `v_scales`. Equal bit
-    for bit to paged_attention over bf16 pools holding the dequantized values
-    (gather_dequant's rounding). Other arguments as paged_attention."""
+    int8 pools with one fp32 scale per slot, each element's value being its
+    code times its slot's scale: the K pool and K scales of `desc` (its
+    page_pool and scales), the V pool `v_pool` and `v_scales`. Other
+    arguments as paged_attention."""
     return _attention(desc, v_pool, v_scales, q, out, total_tokens, scale, checked, streaming,
                       workspace, stream, True)
 

@@ -452,12 +452,15 @@ hp_status hp_paged_attention(const hp_desc *desc, const void *v_pool, const void
  *
  * [Hurray] Per-page-slot parameters: the scale of a slot sits at
  * scales[phys_page * page_size + t % page_size] and applies to every element
- * of that slot's row; hp_gather_dequant turns an element into
- * bf16_rne(fp32(code) * scale). This call computes exactly what
- * hp_paged_attention computes on bf16 pools holding those dequantized values
- * in every slot (same units, same arithmetic, so the results are equal bit
- * for bit), without writing the bf16 pools: each element is dequantized as it
- * is read.
+ * of that slot's row, whose value is code * scale. This call computes
+ * hp_paged_attention's result over those values, with K[t] = cK_t * sK_t and
+ * V[t] = cV_t * sV_t:
+ *   x_t = (scale * sK_t) * sum_d q[s][hq][d] * cK_t[h][d]
+ *   out[s][hq][d] = sum_t (e^{x_t} sV_t) cV_t[h][d] / sum_t e^{x_t}
+ * in fp32 (the codes are exact in bf16, the queries bf16), so the result
+ * differs from the exact one by fp32 rounding only. With power-of-two scales
+ * it equals hp_paged_attention over bf16 pools holding code * scale bit for
+ * bit (hp_gather_dequant writes such pools).
  *
  * desc      the K cache: dtype HP_DTYPE_I8, its page_pool the int8 K pool and
  *           its scales the K scales (num_pages * page_size fp32, 64-byte
