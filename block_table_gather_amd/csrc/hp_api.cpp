@@ -1006,7 +1006,7 @@ static hp_status check_attention(const hp_desc *d, uint32_t num_q_heads, bool q8
     for (int stream = 0; stream < 2; ++stream) {  // the launch shape may follow the hint
         const hp::AttentionShape sh =
             hp::attention_shape(d->num_seqs, d->total_tokens, d->page_size, d->num_heads, D,
-                                num_q_heads, stream != 0);
+                                num_q_heads, stream != 0, q8);
         if (sh.cap_units + d->num_seqs >= (1ull << 31) || sh.head_groups > 65535 ||
             (num_q_heads / d->num_heads + 7) / 8 > 65535)
             return HP_ERR_ARG;

@@ -143,15 +143,33 @@ __device__ __forceinline__ u32x4 codes_bf16(const u32x2 &w) {
 }
 __device__ __forceinline__ u32x4 bits8(const u32x4 &v) { return v; }
 __device__ __forceinline__ u32x4 bits8(const Raw8 &r) { return codes_bf16(r.v); }
-// The codes of a loaded int8 chunk.
-__device__ __forceinline__ u32x2 row_bits(const Raw8 &r) { return r.v; }
-__device__ __forceinline__ u32x2 row_bits(const u32x4 &v) { return u32x2{v.x, v.y}; }
+// 16 codes and their slot's scale: one 16-byte load per lane (the vector
+// kernel's int8 layout for head_dim >= 16).
+struct Raw16 {
+    u32x4 v;
+    float s;
+};
+// Part k (8 elements) of a lane's loaded elements, as 16-bit values.
+__device__ __forceinline__ u32x4 part_bits(const u32x4 &v, int) { return v; }
+__device__ __forceinline__ u32x4 part_bits(const Raw8 &r, int) { return codes_bf16(r.v); }
+__device__ __forceinline__ u32x4 part_bits(const Raw16 &r, int k) {
+    return codes_bf16(k ? u32x2{r.v.z, r.v.w} : u32x2{r.v.x, r.v.y});
+}
+// Word w (4 codes) of a lane's loaded codes.
+__device__ __forceinline__ uint32_t code_word(const Raw8 &r, int w) { return w ? r.v.y : r.v.x; }
+__device__ __forceinline__ uint32_t code_word(const Raw16 &r, int w) {
+    return w == 0 ? r.v.x : w == 1 ? r.v.y : w == 2 ? r.v.z : r.v.w;
+}
+__device__ __forceinline__ float row_scale(const Raw16 &r) { return r.s; }
 // The scale a token's score (or weight) takes: 1 for 16-bit pools.
 __device__ __forceinline__ float row_scale(const u32x4 &) { return 1.0f; }
 __device__ __forceinline__ float row_scale(const Raw8 &r) { return r.s; }
 // Loaded form of 8 elements: the 16-bit values themselves, or codes + scale.
 template <bool Q8>
 using Loaded8 = std::conditional_t<Q8, Raw8, u32x4>;
+// Loaded form of a vector-kernel lane's EPL elements.
+template <bool Q8, int EPL>
+using LoadedE = std::conditional_t<!Q8, u32x4, std::conditional_t<EPL == 16, Raw16, Raw8>>;
 // Bytes per stored element.
 template <bool Q8>
 constexpr uint32_t elem_bytes() { return Q8 ? 1 : 2; }
@@ -198,10 +216,9 @@ __device__ __forceinline__ float group_sum(float x) {
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short bf16x2_bits __attribute__((ext_vector_type(2)));
 template <typename ET>
-__device__ __forceinline__ float dot8(const uint32_t (&q)[4], const u32x4 &k) {
+__device__ __forceinline__ float dot8(const uint32_t (&q)[4], const u32x4 &k, float d = 0.0f) {
     uint32_t w[4];
     __builtin_memcpy(w, &k, sizeof w);
-    float d = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if constexpr (ET::bf16)
@@ -268,8 +285,10 @@ __device__ __forceinline__ void unit_scan_lds(const void *seq_lens, uint32_t S, 
 
 // GT query-head slots per lane group (1, 2, 4 or 8 >= G, or 8 with grid z
 // chunks of 8 query heads when G > 8); slots past G are computed and dropped.
-// Q8: int8 pools with per-slot scales (ET is then BF16).
-template <typename ET, typename IdxT, int LPH, int GT, bool NT, bool Q8>
+// Q8: int8 pools with per-slot scales (ET is then BF16). EPL: elements per
+// lane, 8 (one 16-byte vector of 16-bit values, or 8 codes), or 16 codes
+// (one 16-byte load) for int8 pools with head_dim >= 16.
+template <typename ET, typename IdxT, int LPH, int GT, bool NT, bool Q8, int EPL>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
     // No implicit multiply-add fusion: each fused step below is an explicit
     // fma, and a score must round before its max is subtracted, so that the
@@ -277,7 +296,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
 #pragma clang fp contract(off)
     constexpr int TB = batch_tokens<GT>();
     constexpr uint32_t NG = kAttnThreads / LPH;  // lane groups
-    constexpr uint32_t D = LPH * 8;
+    constexpr uint32_t D = LPH * EPL;
+    constexpr int NP = EPL / 8;  // 8-element parts per lane
+    static_assert(EPL == 8 || (Q8 && EPL == 16), "16 elements per lane only for int8 pools");
     extern __shared__ __align__(16) unsigned char lds[];
     const uint32_t S = a.num_seqs;
     // LDS: [unit_end (fused)] [page IDs of the unit] [token-lane merge]
@@ -343,30 +364,33 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
     const uint32_t h = blockIdx.y * hpw + hl;
     const bool active = tl < TL && h < Hkv;
 
-    float m[GT], l[GT], acc[GT][8];
+    float m[GT], l[GT], acc[GT][EPL];
 #pragma unroll
     for (int gi = 0; gi < GT; ++gi) {
         m[gi] = -__builtin_inff();
         l[gi] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < EPL; ++e)
             acc[gi][e] = 0.0f;
     }
 
     if (active) {
-        uint32_t qp[GT][4];  // the query's 8 elements of this lane, packed as stored
+        uint32_t qp[GT][NP][4];  // the query's EPL elements of this lane, packed as stored
 #pragma unroll
         for (int gi = 0; gi < GT; ++gi) {
             const uint32_t c = min32(gz + gi, G - 1);  // slots past G repeat the last head
-            const uint64_t qo = (((uint64_t)s * Hq + (uint64_t)h * G + c) * D + r * 8) * 2;
-            const u32x4 v = ld16<false>(a.q + qo);
-            __builtin_memcpy(qp[gi], &v, 16);
+            const uint64_t qo = (((uint64_t)s * Hq + (uint64_t)h * G + c) * D + r * EPL) * 2;
+#pragma unroll
+            for (int k = 0; k < NP; ++k) {
+                const u32x4 v = ld16<false>(a.q + qo + 16 * k);
+                __builtin_memcpy(qp[gi][k], &v, 16);
+            }
         }
-        const uint64_t head_off = ((uint64_t)h * D + r * 8) * elem_bytes<Q8>();
+        const uint64_t head_off = ((uint64_t)h * D + r * EPL) * elem_bytes<Q8>();
         const uint64_t slot_bytes = (uint64_t)Hkv * D * elem_bytes<Q8>();
         // each batch starts with a token in range, so its running max is finite
         for (uint32_t jb = 0; jb + tl < n; jb += TB * TL) {
-            Loaded8<Q8> kq[TB], vq[TB];
+            LoadedE<Q8, EPL> kq[TB], vq[TB];
             bool ok[TB];
 #pragma unroll
             for (int i = 0; i < TB; ++i) {
@@ -376,7 +400,10 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
                 const uint32_t pj = udiv32(jj, a.div_page);
                 const uint64_t row = pages[pj] * P + (jj - pj * P);
                 const uint64_t off = row * slot_bytes + head_off;
-                if constexpr (Q8) {
+                if constexpr (Q8 && EPL == 16) {
+                    kq[i] = Raw16{ld16<NT>(a.k_pool + off), a.k_scales[row]};
+                    vq[i] = Raw16{ld16<NT>(a.v_pool + off), a.v_scales[row]};
+                } else if constexpr (Q8) {
                     kq[i] = Raw8{ld8<NT>(a.k_pool + off), a.k_scales[row]};
                     vq[i] = Raw8{ld8<NT>(a.v_pool + off), a.v_scales[row]};
                 } else {
@@ -387,12 +414,19 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
             float x[GT][TB];
 #pragma unroll
             for (int i = 0; i < TB; ++i) {
-                const u32x4 kb = bits8(kq[i]);
+                u32x4 kb[NP];
+#pragma unroll
+                for (int k = 0; k < NP; ++k)
+                    kb[k] = part_bits(kq[i], k);
                 // int8 pools: the token's K scale joins the softmax scale
                 const float xs = Q8 ? a.qscale * row_scale(kq[i]) : a.qscale;
 #pragma unroll
                 for (int gi = 0; gi < GT; ++gi) {
-                    const float dot = group_sum<LPH, GT == 1>(dot8<ET>(qp[gi], kb)) * xs;
+                    float d = dot8<ET>(qp[gi][0], kb[0]);
+#pragma unroll
+                    for (int k = 1; k < NP; ++k)
+                        d = dot8<ET>(qp[gi][k], kb[k], d);
+                    const float dot = group_sum<LPH, GT == 1>(d) * xs;
                     x[gi][i] = ok[i] ? dot : -__builtin_inff();
                 }
             }
@@ -413,19 +447,19 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
                 }
                 l[gi] = l[gi] * corr + ps;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+                for (int e = 0; e < EPL; ++e)
                     acc[gi][e] *= corr;
                 m[gi] = mx;
             }
 #pragma unroll
             for (int i = 0; i < TB; ++i) {
-                float vf[8];
+                float vf[EPL];
                 if constexpr (Q8) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)  // the codes (exact)
-                        vf[e] = sbyte(e < 4 ? row_bits(vq[i]).x : row_bits(vq[i]).y, e & 3);
+                    for (int e = 0; e < EPL; ++e)  // the codes (exact)
+                        vf[e] = sbyte(code_word(vq[i], e / 4), e & 3);
                 } else {
-                    unpack8<ET>(bits8(vq[i]), vf);
+                    unpack8<ET>(vq[i], vf);
                 }
 #pragma unroll
                 for (int gi = 0; gi < GT; ++gi) {
@@ -433,7 +467,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
                     // of weights l stays unscaled)
                     const float pv = Q8 ? p[gi][i] * row_scale(vq[i]) : p[gi][i];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
+                    for (int e = 0; e < EPL; ++e)
                         acc[gi][e] = __builtin_fmaf(pv, vf[e], acc[gi][e]);
                 }
             }
@@ -454,8 +488,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
                     rml[2 * lg + 1] = l[gi];
                 }
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    racc[lg * D + r * 8 + e] = acc[gi][e];
+                for (int e = 0; e < EPL; ++e)
+                    racc[lg * D + r * EPL + e] = acc[gi][e];
             }
             __syncthreads();
             if (active && tl == 0) {
@@ -465,7 +499,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
                 const float c0 = exp2_hw(m[gi] - M);
                 l[gi] *= c0;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+                for (int e = 0; e < EPL; ++e)
                     acc[gi][e] *= c0;
                 for (uint32_t t2 = 1; t2 < TL; ++t2) {
                     const uint32_t o = t2 * hpw + hl;
@@ -474,8 +508,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
                     const float c = mo == -__builtin_inff() ? 0.0f : exp2_hw(mo - M);
                     l[gi] = __builtin_fmaf(rml[2 * o + 1], c, l[gi]);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[gi][e] = __builtin_fmaf(racc[o * D + r * 8 + e], c, acc[gi][e]);
+                    for (int e = 0; e < EPL; ++e)
+                        acc[gi][e] = __builtin_fmaf(racc[o * D + r * EPL + e], c, acc[gi][e]);
                 }
                 m[gi] = M;
             }
@@ -491,16 +525,17 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
             for (int gi = 0; gi < GT; ++gi) {
                 if (gz + gi >= G)
                     break;
-                float *dst = a.out + ((uint64_t)s * Hq + (uint64_t)h * G + gz + gi) * D + r * 8;
-                float o[8];
+                float *dst = a.out + ((uint64_t)s * Hq + (uint64_t)h * G + gz + gi) * D + r * EPL;
+                float o[EPL];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+                for (int e = 0; e < EPL; ++e)
                     o[e] = acc[gi][e] / l[gi];
-                u32x4 lo, hi;
-                __builtin_memcpy(&lo, &o[0], 16);
-                __builtin_memcpy(&hi, &o[4], 16);
-                reinterpret_cast<u32x4 *>(dst)[0] = lo;
-                reinterpret_cast<u32x4 *>(dst)[1] = hi;
+#pragma unroll
+                for (int k = 0; k < EPL / 4; ++k) {
+                    u32x4 v;
+                    __builtin_memcpy(&v, &o[4 * k], 16);
+                    reinterpret_cast<u32x4 *>(dst)[k] = v;
+                }
             }
         }
         return;
@@ -512,12 +547,13 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AArgs a) {
             if (gz + gi >= G)
                 break;
             const uint64_t idx = (uint64_t)g * Hq + (uint64_t)h * G + gz + gi;
-            float *dst = a.part_acc + idx * D + r * 8;
-            u32x4 lo, hi;
-            __builtin_memcpy(&lo, &acc[gi][0], 16);
-            __builtin_memcpy(&hi, &acc[gi][4], 16);
-            reinterpret_cast<u32x4 *>(dst)[0] = lo;
-            reinterpret_cast<u32x4 *>(dst)[1] = hi;
+            float *dst = a.part_acc + idx * D + r * EPL;
+#pragma unroll
+            for (int k = 0; k < EPL / 4; ++k) {
+                u32x4 v;
+                __builtin_memcpy(&v, &acc[gi][4 * k], 16);
+                reinterpret_cast<u32x4 *>(dst)[k] = v;
+            }
             if (r == 0) {
                 a.part_ml[2 * idx] = m[gi];
                 a.part_ml[2 * idx + 1] = l[gi];
@@ -1610,6 +1646,14 @@ __global__ __launch_bounds__(kAttnThreads) void attention_combine_kernel(CArgs c
 // Query-head slots per lane group for G query heads per kv head.
 uint32_t group_slots(uint32_t G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8; }
 
+// Codes per lane of the vector kernel over int8 pools: 16 (one 16-byte load,
+// the bytes in flight of a 16-bit pool's lane) for one or two query heads
+// per kv head and head_dim >= 16; else 8 (the accumulators of 16 elements
+// for four or eight query-head slots would not fit in registers).
+uint32_t q8_lane_codes(uint32_t D, uint32_t G) {
+    return D >= 16 && group_slots(G) <= 2 ? 16 : 8;
+}
+
 // Grouped query heads with head_dim 64 or 128 take the matrix-core kernel
 // from three query heads per kv head, and at two when the loads stream (each
 // page read once, so HBM bounds the call). Measured on MI355X against the
@@ -1665,7 +1709,7 @@ hipError_t launch_mfma_r(const AArgs &a, const AttentionShape &sh, uint32_t G, b
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-template <typename ET, typename IdxT, int LPH, int GT, bool Q8>
+template <typename ET, typename IdxT, int LPH, int GT, bool Q8, int EPL>
 hipError_t launch_attention_t(const AArgs &a, const AttentionShape &sh, bool nt,
                               hipStream_t stream) {
     const dim3 grid((uint32_t)(sh.cap_units + a.num_seqs), sh.head_groups,
@@ -1673,37 +1717,53 @@ hipError_t launch_attention_t(const AArgs &a, const AttentionShape &sh, bool nt,
     const uint32_t ng = kAttnThreads / LPH;
     const size_t lds = (a.fused ? ((4 * (size_t)a.num_seqs + 15) & ~(size_t)15) : 0) +
                        8 * (size_t)a.unit_pages +
-                       (sh.token_lanes > 1 ? 4 * (size_t)ng * (2 + LPH * 8) : 0);
+                       (sh.token_lanes > 1 ? 4 * (size_t)ng * (2 + LPH * EPL) : 0);
     if (nt)
-        hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, GT, true, Q8>), grid,
+        hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, GT, true, Q8, EPL>), grid,
                            dim3(kAttnThreads), lds, stream, a);
     else
-        hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, GT, false, Q8>), grid,
+        hipLaunchKernelGGL((attention_kernel<ET, IdxT, LPH, GT, false, Q8, EPL>), grid,
                            dim3(kAttnThreads), lds, stream, a);
     return hipGetLastError();
 }
 
-template <typename ET, typename IdxT, int LPH, bool Q8>
+template <typename ET, typename IdxT, int LPH, bool Q8, int EPL>
 hipError_t launch_attention_g(const AArgs &a, const AttentionShape &sh, uint32_t G, bool nt,
                               hipStream_t st) {
+    if constexpr (EPL == 16) {  // one or two query heads per kv head
+        if (group_slots(G) == 1)
+            return launch_attention_t<ET, IdxT, LPH, 1, Q8, 16>(a, sh, nt, st);
+        return launch_attention_t<ET, IdxT, LPH, 2, Q8, 16>(a, sh, nt, st);
+    }
     switch (group_slots(G)) {
-    case 1: return launch_attention_t<ET, IdxT, LPH, 1, Q8>(a, sh, nt, st);
-    case 2: return launch_attention_t<ET, IdxT, LPH, 2, Q8>(a, sh, nt, st);
-    case 4: return launch_attention_t<ET, IdxT, LPH, 4, Q8>(a, sh, nt, st);
-    default: return launch_attention_t<ET, IdxT, LPH, 8, Q8>(a, sh, nt, st);
+    case 1: return launch_attention_t<ET, IdxT, LPH, 1, Q8, EPL>(a, sh, nt, st);
+    case 2: return launch_attention_t<ET, IdxT, LPH, 2, Q8, EPL>(a, sh, nt, st);
+    case 4: return launch_attention_t<ET, IdxT, LPH, 4, Q8, EPL>(a, sh, nt, st);
+    default: return launch_attention_t<ET, IdxT, LPH, 8, Q8, EPL>(a, sh, nt, st);
     }
 }
 
 template <typename ET, typename IdxT, bool Q8>
 hipError_t launch_attention_d(const AArgs &a, const AttentionShape &sh, uint32_t G, bool nt,
                               hipStream_t st) {
+    if constexpr (Q8) {
+        if (q8_lane_codes(a.head_dim, G) == 16) {
+            switch (a.head_dim) {
+            case 16: return launch_attention_g<ET, IdxT, 1, Q8, 16>(a, sh, G, nt, st);
+            case 32: return launch_attention_g<ET, IdxT, 2, Q8, 16>(a, sh, G, nt, st);
+            case 64: return launch_attention_g<ET, IdxT, 4, Q8, 16>(a, sh, G, nt, st);
+            case 128: return launch_attention_g<ET, IdxT, 8, Q8, 16>(a, sh, G, nt, st);
+            default: return launch_attention_g<ET, IdxT, 16, Q8, 16>(a, sh, G, nt, st);
+            }
+        }
+    }
     switch (a.head_dim) {
-    case 8: return launch_attention_g<ET, IdxT, 1, Q8>(a, sh, G, nt, st);
-    case 16: return launch_attention_g<ET, IdxT, 2, Q8>(a, sh, G, nt, st);
-    case 32: return launch_attention_g<ET, IdxT, 4, Q8>(a, sh, G, nt, st);
-    case 64: return launch_attention_g<ET, IdxT, 8, Q8>(a, sh, G, nt, st);
-    case 128: return launch_attention_g<ET, IdxT, 16, Q8>(a, sh, G, nt, st);
-    default: return launch_attention_g<ET, IdxT, 32, Q8>(a, sh, G, nt, st);
+    case 8: return launch_attention_g<ET, IdxT, 1, Q8, 8>(a, sh, G, nt, st);
+    case 16: return launch_attention_g<ET, IdxT, 2, Q8, 8>(a, sh, G, nt, st);
+    case 32: return launch_attention_g<ET, IdxT, 4, Q8, 8>(a, sh, G, nt, st);
+    case 64: return launch_attention_g<ET, IdxT, 8, Q8, 8>(a, sh, G, nt, st);
+    case 128: return launch_attention_g<ET, IdxT, 16, Q8, 8>(a, sh, G, nt, st);
+    default: return launch_attention_g<ET, IdxT, 32, Q8, 8>(a, sh, G, nt, st);
     }
 }
 
@@ -1752,7 +1812,7 @@ WsLayout ws_layout(uint64_t S, uint64_t Hq, uint64_t D, const AttentionShape &sh
 
 AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
                                uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads,
-                               bool stream_loads) {
+                               bool stream_loads, bool q8) {
     AttentionShape sh;
     const uint32_t G = num_q_heads / num_kv_heads;
     const bool mfma = attention_mfma(G, head_dim, stream_loads);
@@ -1761,7 +1821,8 @@ AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_
         sh.heads_per_group = kMfmaWaves;
         sh.token_lanes = 1;
     } else {
-        const uint32_t lph = head_dim / 8;
+        // lanes per head row: 8 elements each, or 16 int8 codes
+        const uint32_t lph = head_dim / (q8 ? q8_lane_codes(head_dim, G) : 8);
         const uint32_t ng = kAttnThreads / lph;
         sh.heads_per_group = num_kv_heads < ng ? num_kv_heads : ng;
         sh.token_lanes = ng / sh.heads_per_group;
@@ -1812,9 +1873,9 @@ AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_
 uint64_t attention_workspace_bytes(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
                                    uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads) {
     uint64_t need = 0;
-    for (int stream = 0; stream < 2; ++stream) {
+    for (int v = 0; v < 4; ++v) {  // with and without streaming loads, 16-bit and int8 pools
         const AttentionShape sh = attention_shape(num_seqs, total_tokens, page_size, num_kv_heads,
-                                                  head_dim, num_q_heads, stream != 0);
+                                                  head_dim, num_q_heads, v & 1, v & 2);
         const uint64_t n = ws_layout(num_seqs, num_q_heads, head_dim, sh).end;
         need = n > need ? n : need;
     }
@@ -1825,7 +1886,7 @@ hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
     (void)hipGetLastError();  // clear errors left by earlier calls that are not ours
     const AttentionShape sh = attention_shape(job.num_seqs, job.total_tokens, job.page_size,
                                               job.num_kv_heads, job.head_dim, job.num_q_heads,
-                                              job.stream_loads);
+                                              job.stream_loads, job.q8);
     const WsLayout wl = ws_layout(job.num_seqs, job.num_q_heads, job.head_dim, sh);
     unsigned char *ws = static_cast<unsigned char *>(job.workspace);
     uint32_t *unit_end = reinterpret_cast<uint32_t *>(ws + wl.unit_end);

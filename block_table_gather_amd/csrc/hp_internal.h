@@ -275,11 +275,12 @@ struct AttentionJob {
     void *workspace;  // attention_workspace_bytes(...)
 };
 
+// Launch shape of an attention call (q8: int8 pools).
 AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
                                uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads,
-                               bool stream_loads);
+                               bool stream_loads, bool q8);
 // The workspace covers the launch shape with and without streaming loads
-// (the streaming hint can choose the kernel).
+// (the streaming hint can choose the kernel), for 16-bit and int8 pools.
 uint64_t attention_workspace_bytes(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
                                    uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads);
 hipError_t launch_attention(const AttentionJob &job, hipStream_t stream);
