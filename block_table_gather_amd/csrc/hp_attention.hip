@@ -672,47 +672,61 @@ __device__ __forceinline__ void mfma_span(const AArgs &a, const uint64_t *page_o
     // 198 us with whole rows for both K and V). K and V both go through the wave's
     // tile buffer in LDS, K on to the B layout of the score product. Tokens
     // past n repeat the last token (a real row; masked below).
-    // (int8 pools: 8 bytes of codes per chunk, which become the chunk's 16
-    // bytes of bf16 on the way into LDS, and lane i < 32 loads the scale of
-    // the tile's token i, which the score and the weight of that token take)
+    // (int8 pools: chunk c is 16 codes for each lane, lane L reading codes
+    // 16 (L % (D / 16)) of the head row of token 8 c + L / (D / 16) (D = 128),
+    // which become 32 bytes of bf16 on the way into LDS; and lane i < 32
+    // loads the scale of the tile's token i, which the score and the weight
+    // of that token take)
     V8 kb[2][KK];
-    constexpr uint32_t C16 = Q8 ? 1 : 2 * KK, C8 = Q8 ? 2 * KK : 1;
+    constexpr uint32_t C16 = Q8 ? 1 : 2 * KK, C8 = Q8 ? KK : 1;
     u32x4 kc[C16], vc[C16];
-    u32x2 kc8[C8], vc8[C8];
+    u32x4 kc8[C8], vc8[C8];
     float ksc = 0.0f, vsc = 0.0f;
     auto load_rows = [&](const unsigned char *pool, const float *scales, uint32_t tb,
-                         u32x4 (&d16)[C16], u32x2 (&d8)[C8], float &dsc) {
-#pragma unroll
-        for (uint32_t c = 0; c < 2 * KK; ++c) {
-            const uint32_t ch = 64 * c + lane;
-            const uint32_t jt = ch / (D / 8), dc = ch % (D / 8);
-            const uint32_t j = min32(tb + jt, n - 1);
-            const uint32_t pj = udiv32(j, a.div_page);
-            if constexpr (Q8)
-                d8[c] = ld8<NT>(pool + (page_off[pj] + (j - pj * P)) * slot_bytes + head_off +
-                                8 * dc);
-            else
-                d16[c] = ld16<NT>(pool + page_off[pj] + (uint64_t)(j - pj * P) * slot_bytes +
-                                  head_off + 16 * dc);
-        }
+                         u32x4 (&d16)[C16], u32x4 (&d8)[C8], float &dsc) {
         if constexpr (Q8) {
+#pragma unroll
+            for (uint32_t c = 0; c < KK; ++c) {
+                const uint32_t ch = 64 * c + lane;
+                const uint32_t jt = ch / (D / 16), dc = ch % (D / 16);
+                const uint32_t j = min32(tb + jt, n - 1);
+                const uint32_t pj = udiv32(j, a.div_page);
+                d8[c] = ld16<NT>(pool + (page_off[pj] + (j - pj * P)) * slot_bytes + head_off +
+                                 16 * dc);
+            }
             const uint32_t j = min32(tb + (lane & (kMfmaTile - 1)), n - 1);
             const uint32_t pj = udiv32(j, a.div_page);
             dsc = scales[page_off[pj] + (j - pj * P)];
+        } else {
+#pragma unroll
+            for (uint32_t c = 0; c < 2 * KK; ++c) {
+                const uint32_t ch = 64 * c + lane;
+                const uint32_t jt = ch / (D / 8), dc = ch % (D / 8);
+                const uint32_t j = min32(tb + jt, n - 1);
+                const uint32_t pj = udiv32(j, a.div_page);
+                d16[c] = ld16<NT>(pool + page_off[pj] + (uint64_t)(j - pj * P) * slot_bytes +
+                                  head_off + 16 * dc);
+            }
         }
     };
     // token-major rows of VRB bytes
-    auto store_rows = [&](const u32x4 (&s16)[C16], const u32x2 (&s8)[C8]) {
+    auto store_rows = [&](const u32x4 (&s16)[C16], const u32x4 (&s8)[C8]) {
+        if constexpr (Q8) {
 #pragma unroll
-        for (uint32_t c = 0; c < 2 * KK; ++c) {
-            const uint32_t ch = 64 * c + lane;
-            const uint32_t jt = ch / (D / 8), dc = ch % (D / 8);
-            u32x4 v;
-            if constexpr (Q8)
-                v = codes_bf16(s8[c]);
-            else
-                v = s16[c];
-            *reinterpret_cast<u32x4 *>(vt + jt * VRB + 16 * dc) = v;
+            for (uint32_t c = 0; c < KK; ++c) {
+                const uint32_t ch = 64 * c + lane;
+                const uint32_t jt = ch / (D / 16), dc = ch % (D / 16);
+                u32x4 *dst = reinterpret_cast<u32x4 *>(vt + jt * VRB + 32 * dc);
+                dst[0] = codes_bf16(u32x2{s8[c].x, s8[c].y});
+                dst[1] = codes_bf16(u32x2{s8[c].z, s8[c].w});
+            }
+        } else {
+#pragma unroll
+            for (uint32_t c = 0; c < 2 * KK; ++c) {
+                const uint32_t ch = 64 * c + lane;
+                const uint32_t jt = ch / (D / 8), dc = ch % (D / 8);
+                *reinterpret_cast<u32x4 *>(vt + jt * VRB + 16 * dc) = s16[c];
+            }
         }
     };
     // K of the tile into the B layout: the lane's token 16 b + c16, bytes
