@@ -79,6 +79,7 @@ KERNEL_LABELS = {
 }
 CALIBRATION_BYTES = 1 << 30
 TRACE_STEPS, TRACE_WARMUP = 50, 5
+PRE_STEPS = 100  # untimed steps before the warm-up ones (about 50 ms on MI355X)
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d rocprof_out/prof_trace -o trace -- "
              f"python3 bench.py --steps {TRACE_STEPS} --warmup {TRACE_WARMUP} --no-cpu-baseline "
              "--no-reference-copies --no-configs")
@@ -478,59 +479,71 @@ def summarize_attention(trace_dir, fetch_dir, write_dir):
     import numpy as np
     import workloads
     dec, pre = workloads.decode(), workloads.prefix()
-    uniq = len(np.unique(pre.block_table)) * pre.page_size * pre.num_heads * pre.head_dim * 4
+    n_unique = len(np.unique(pre.block_table)) * pre.page_size
 
-    def algo(w, group, unique=None):
+    def algo(w, group, q8=False, unique=False):
+        """(logical, unique or None) algorithmic bytes of one call."""
         Hq = w.num_heads * group
         io = w.num_seqs * Hq * w.head_dim * 6  # queries read (2 bytes), fp32 output written
-        logical = 2 * w.total_tokens * w.num_heads * w.head_dim * 2 + io
-        return logical, (unique + io if unique is not None else None)
+        row = w.num_heads * w.head_dim * (1 if q8 else 2) + (4 if q8 else 0)  # K or V slot
+        logical = 2 * w.total_tokens * row + io
+        return logical, (2 * n_unique * row + io if unique else None)
 
-    # which workload a kernel row belongs to: the decode batch runs the vector
-    # kernel (fp16), the prefix batch the matrix-core kernel, whose last
-    # template argument is 1 with 4 query heads per kv head and 2 with 8
-    workload_of = {"attention_kernel<F16": ("decode, G = 1", algo(dec, 1)),
-                   "attention_mfma_kernel<F16, unsigned int, 128, true, 1>":
-                       ("decode, G = 4", algo(dec, 4)),
-                   "attention_mfma_kernel<BF16, unsigned int, 128, true, 1>":
-                       ("prefix, G = 4", algo(pre, 4, uniq)),
-                   "attention_mfma_kernel<BF16, unsigned int, 128, true, 2>":
-                       ("prefix, G = 8", algo(pre, 8, uniq))}
+    # The --attention-only run calls its workloads in this order, each with
+    # one main kernel (vector or matrix-core) of its own name and grid: the
+    # main-kernel groups of the trace, in order of first launch, are these.
+    order = [("decode, f16, G = 1", algo(dec, 1)),
+             ("prefix, bf16, G = 4", algo(pre, 4, unique=True)),
+             ("prefix, bf16, G = 8", algo(pre, 8, unique=True)),
+             ("decode, f16, G = 4", algo(dec, 4)),
+             ("decode, int8, G = 1", algo(dec, 1, q8=True)),
+             ("decode, int8, G = 4", algo(dec, 4, q8=True)),
+             ("prefix, int8, G = 4", algo(pre, 4, q8=True, unique=True))]
 
-    def match(name):
-        for k, v in workload_of.items():
-            if name.startswith(k):
-                return v
-        return None
-
-    lines = ["# Kernel durations: decode attention through the block table (rocprofv3)", "",
-             "Command (from the repository root, on one MI355X):", "", f"    {ATTN_TRACE_CMD}", "",
-             "Four workloads, each called 21 times: the decode batch (64 sequences, 32 kv",
-             "heads x 128 f16, streaming loads) with one query head per kv head (vector kernel",
-             "and combine) and with four (matrix-core kernel and combine), and the",
-             "prefix-sharing batch (256 sequences sharing 64 leading pages, 8 kv heads x 128",
-             "bf16) with 4 and with 8 query heads per kv head (cached loads: the shared-prefix",
-             "pass). A prefix call runs four kernels: the leading-page",
-             "comparison (one wave per sequence), the one-workgroup plan, the matrix-core",
-             "kernel (shared work items first in its grid, then the units over the pages after",
-             "the shared part) and the combine; the comparison and plan rows hold both prefix",
-             "workloads' calls (same grid). Durations in microseconds. Logical bytes count",
-             "every sequence's K/V rows (shared pages once per sequence); unique bytes count",
-             "each distinct page once (the least any call must read), both with the queries",
-             "read and the fp32 output written.", "",
-             "| kernel | calls | avg us | min us | max us | logical GB | unique GB | "
-             "unique GB/s at avg |",
-             "|---|---|---|---|---|---|---|---|"]
     trace = _csv_rows(trace_dir, "*kernel_trace.csv")
-    groups = {}
+    groups, first = {}, {}
     for r in trace:
         if "attention" not in r["Kernel_Name"]:
             continue
-        key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]))
-        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    for (name, grid), ts in sorted(groups.items()):
+        key = (_short(r["Kernel_Name"]),
+               int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+        t0 = int(r["Start_Timestamp"])
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - t0) / 1e3)
+        first[key] = min(first.get(key, t0), t0)
+    main = sorted((k for k in groups if k[0].startswith(("attention_kernel<",
+                                                            "attention_mfma_kernel<"))),
+                  key=lambda k: first[k])
+    if len(main) != len(order):
+        raise SystemExit(f"expected {len(order)} main attention kernels, found {len(main)}")
+    workload_of = dict(zip(main, order))
+
+    def match(key):
+        return workload_of.get(key)
+
+    lines = ["# Kernel durations: decode attention through the block table (rocprofv3)", "",
+             "Command (from the repository root, on one MI355X):", "", f"    {ATTN_TRACE_CMD}", "",
+             "Seven workloads, each called 21 times: the decode batch (64 sequences, 32 kv",
+             "heads x 128, streaming loads) over f16 pools with one query head per kv head",
+             "(vector kernel and combine) and with four (matrix-core kernel and combine); the",
+             "prefix-sharing batch (256 sequences sharing 64 leading pages, 8 kv heads x 128)",
+             "over bf16 pools with 4 and with 8 query heads per kv head (cached loads: the",
+             "shared-prefix pass); and over int8 pools with one fp32 scale per slot",
+             "(hp_paged_attention_q8, bf16 queries) the decode batch with 1 and 4 query heads",
+             "per kv head and the prefix batch with 4. A prefix call runs four kernels: the",
+             "leading-page comparison (one wave per sequence), the one-workgroup plan, the",
+             "matrix-core kernel (shared work items first in its grid, then the units over the",
+             "pages after the shared part) and the combine; the comparison and plan rows hold",
+             "the prefix workloads' calls (same grid). Durations in microseconds. Logical",
+             "bytes count every sequence's K/V rows (shared pages once per sequence; int8",
+             "rows with their slot scale); unique bytes count each distinct page once (the",
+             "least any call must read), both with the queries read and the fp32 output",
+             "written.", "",
+             "| kernel | calls | avg us | min us | max us | logical GB | unique GB | "
+             "unique GB/s at avg |",
+             "|---|---|---|---|---|---|---|---|"]
+    for (name, grid), ts in sorted(groups.items(), key=lambda kv: first[kv[0]]):
         lg = ug = ugs = ""
-        m = match(name)
+        m = match((name, grid))
         if m is not None:
             what, (logical, unique) = m
             lg = f"{logical / 1e9:.4f} ({what})"
@@ -577,7 +590,7 @@ def summarize_attention(trace_dir, fetch_dir, write_dir):
         name = key[0]
         rb, wb = fk[key] * 1024 * ff, wk[key] * 1024 * wf
         gb = ""
-        m = match(name)
+        m = match(key)
         if m is not None:
             what, (logical, unique) = m
             gb = f"{(unique if unique is not None else logical) / 1e9:.4f} ({what})"
@@ -1383,11 +1396,13 @@ def main():
     if args.copy_calibration:
         calibration_copies(torch, dev)
 
-    # A fresh process's first ~20 steps run up to 15 % slower (measured: 545
-    # -> 499 us, then a steady ~478 us). So one pass of the per-kernel launch
-    # timings (discarded) and the reference copies run before the warm-up and
-    # timed steps, and the kept launch timings after them: both run on a GPU
-    # that has been running the path for a few tens of milliseconds.
+    # A fresh process's first steps run slower, and the step time keeps
+    # falling for about 40 ms of load (a kernel trace of 55 steps after the
+    # launch-timing pass: 500 us for the first timed step, ~478 for the next
+    # twenty, ~472 from the 40th on). So one pass of the per-kernel launch
+    # timings (discarded), the reference copies and about 50 ms of untimed
+    # steps run before the W warm-up steps and the timed ones, and the kept
+    # launch timings after them.
     def back_to_back(fn, s=main_s):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fn()
@@ -1427,6 +1442,7 @@ def main():
                 "unit": "GB/s", "bytes": ident_bytes}
         del ident_out
 
+    run_steps(PRE_STEPS)  # about 50 ms of the step, untimed
     run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -1468,6 +1484,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "untimed_pre_steps": PRE_STEPS,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
