@@ -262,14 +262,19 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir):
             launches.setdefault(short, []).append(
                 (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) -
                                              int(r["Start_Timestamp"])) / 1e3))
-    n_step = TRACE_STEPS + TRACE_WARMUP
+    # per move, in launch order: 21 back-to-back launches (the discarded
+    # launch-timing pass), the untimed pre-pass steps, the warm-up and timed
+    # steps, then the 21 kept back-to-back launches
+    n_b2b, n_mid = 21, PRE_STEPS + TRACE_WARMUP + TRACE_STEPS
     lines = ["# Kernel durations: decode-batch bench step (rocprofv3 kernel trace)", "",
              "Command (from the repository root, on one MI355X):", "",
              f"    {TRACE_CMD}", "",
-             f"Each move runs once per step ({TRACE_WARMUP} warm-up + {TRACE_STEPS} timed "
-             "steps), then 21 times back to back",
-             "for the event timing. `step` averages the first kind, `back-to-back` the second.",
-             "Durations in microseconds.", "",
+             "Each move runs 21 times back to back (a launch-timing pass, discarded), once "
+             f"per step ({PRE_STEPS} untimed",
+             f"steps, {TRACE_WARMUP} warm-up, {TRACE_STEPS} timed), then 21 times back to "
+             "back for the event timing.",
+             f"`step` averages the {TRACE_STEPS} timed steps' launches, `back-to-back` the "
+             "last 21. Durations in microseconds.", "",
              "| kernel | what | calls | avg | min | max | step avg | back-to-back avg |",
              "|---|---|---|---|---|---|---|---|"]
     gather = None
@@ -277,8 +282,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir):
         ts = [d for _, d in sorted(launches[short])]
         avg = sum(ts) / len(ts)
         step = b2b = ""
-        if not short.startswith("validate") and len(ts) > n_step:
-            st, bb = ts[:n_step], ts[n_step:]
+        if not short.startswith("validate") and len(ts) == 2 * n_b2b + n_mid:
+            st, bb = ts[n_b2b + n_mid - TRACE_STEPS:n_b2b + n_mid], ts[-n_b2b:]
             step, b2b = f"{sum(st) / len(st):.1f}", f"{sum(bb) / len(bb):.1f}"
             if short == GATHER_KERNEL:
                 gather = (avg, sum(st) / len(st), sum(bb) / len(bb))
