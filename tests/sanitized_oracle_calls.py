@@ -88,6 +88,11 @@ for seed in range(60):
                            num_kv_heads=w.num_heads, head_dim=w.head_dim,
                            block_table=w.block_table, seq_ptr=w.seq_ptr, seq_lens=w.seq_lens,
                            scale=0.125)
+    # the same over int8 pools with per-slot scales
+    oracle.paged_attention_q8(q, qpool, scales, qpool, scales[::-1].copy(), page_size=w.page_size,
+                              num_kv_heads=w.num_heads, head_dim=w.head_dim,
+                              block_table=w.block_table, seq_ptr=w.seq_ptr,
+                              seq_lens=w.seq_lens, scale=0.125)
     calls += 1
 oracle.quantize_row(np.linspace(-3, 5, 33, dtype=np.float32), asym=True)
 oracle.bf16_rne(np.linspace(-1, 1, 17, dtype=np.float32))
