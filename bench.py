@@ -815,6 +815,21 @@ def attention_extras(hp, torch, np, dev, stream, reps, gqa8=False):
             res[name]["unique_kv_bytes"] = unique
             res[name]["unique_gb_per_s"] = round(ub / (ms / 1e3) / 1e9, 1)
             res[name]["unique_frac_of_8tbs"] = round(ub / (ms / 1e3) / 8e12, 3)
+            # the same call reusing a plan made once (hp_attention_plan, then
+            # HP_FLAG_PLANNED): what each layer after the first costs
+            if L.hp_attention_plan(pd, Hq, ws.data_ptr(), ws.numel(), 0, stream.cuda_stream):
+                raise SystemExit("hp_attention_plan failed")
+            args = args[:-2] + (args[-2] | hp.HP_FLAG_PLANNED, args[-1])
+            call()
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(reps):
+                call()
+            b.record(stream)
+            b.synchronize()
+            pms = a.elapsed_time(b) / reps
+            res[name]["planned_launch_us"] = round(pms * 1e3, 1)
+            res[name]["planned_unique_frac_of_8tbs"] = round(ub / (pms / 1e3) / 8e12, 3)
         del k_pool, v_pool, q, out, ws, k_sc, v_sc
         torch.cuda.empty_cache()
     return res

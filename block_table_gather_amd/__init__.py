@@ -68,6 +68,7 @@ HP_INDEX_U32, HP_INDEX_U64 = 0x00, 0x01
 DTYPE = {"i8": 1, "u8": 2, "f16": 3, "bf16": 4, "f32": 5, "f64": 6}
 HP_FLAG_CHECKED, HP_FLAG_ZERO_TAIL, HP_FLAG_STREAM, HP_FLAG_GATED = 1, 2, 4, 8
 HP_FLAG_DISJOINT = 16
+HP_FLAG_PLANNED = 32
 # Quantization scheme tags (include/hp.h, HP_QUANT_*).
 QUANT_SCHEME = {"per_tensor": 0x01, "per_channel": 0x02, "per_block_affine": 0x03}
 
@@ -139,6 +140,8 @@ _lib.hp_paged_attention_q8.argtypes = [_P, _vp, _vp, _vp, _u32, ctypes.c_float, 
                                        _sz, _u32, _vp]
 _lib.hp_attention_workspace_bytes.restype = _sz
 _lib.hp_attention_workspace_bytes.argtypes = [_P, _u32]
+_lib.hp_attention_plan.restype = ctypes.c_int
+_lib.hp_attention_plan.argtypes = [_P, _u32, _vp, _sz, _u32, _vp]
 _lib.hp_status_str.restype = ctypes.c_char_p
 _lib.hp_status_str.argtypes = [ctypes.c_int]
 _lib.hp_last_hip_error.restype = ctypes.c_char_p
@@ -472,18 +475,39 @@ def attention_workspace_bytes(desc, total_tokens, num_q_heads):
     return int(_lib.hp_attention_workspace_bytes(desc.with_tokens(total_tokens), num_q_heads))
 
 
+def attention_plan(desc, num_q_heads, *, total_tokens, checked=False, streaming=False,
+                   workspace=None, stream=None):
+    """Runs the attention calls' planning kernels alone into `workspace`
+    (allocated through torch when None) and returns it: pass it, with
+    planned=True, to paged_attention / paged_attention_q8 calls on the same
+    descriptor, query-head count and streaming setting (for instance one per
+    layer) and they skip their planning."""
+    p = desc.with_tokens(total_tokens)
+    n = int(_lib.hp_attention_workspace_bytes(p, num_q_heads))
+    if workspace is None:
+        workspace = _own_workspace(max(n, 256), desc.device, stream)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_STREAM if streaming else 0)
+    _check(_lib.hp_attention_plan(p, num_q_heads, _ptr(workspace), ws_bytes, flags,
+                                  _stream(stream, desc.device)), "hp_attention_plan")
+    return workspace
+
+
 def _attention(desc, v_pool, v_scales, q, out, total_tokens, scale, checked, streaming,
-               workspace, stream, q8):
+               workspace, stream, q8, planned=False):
     Hq = q.shape[1]
     p = desc.with_tokens(total_tokens)
     n = int(_lib.hp_attention_workspace_bytes(p, Hq))
+    if planned and workspace is None:
+        raise ValueError("planned=True needs the workspace attention_plan filled")
     if workspace is None and n:
         workspace = _own_workspace(n, q.device, stream)
         desc._ws = workspace  # keep alive until the next call on this descriptor
     if scale is None:
         scale = 1.0 / float(desc.c.head_dim) ** 0.5
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    flags = (HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_STREAM if streaming else 0)
+    flags = ((HP_FLAG_CHECKED if checked else 0) | (HP_FLAG_STREAM if streaming else 0) |
+             (HP_FLAG_PLANNED if planned else 0))
     st = _stream(stream, desc.device)
     if q8:
         _check(_lib.hp_paged_attention_q8(p, _ptr(v_pool), _ptr(v_scales), _ptr(q), Hq,
@@ -498,25 +522,27 @@ def _attention(desc, v_pool, v_scales, q, out, total_tokens, scale, checked, str
 
 
 def paged_attention(desc, v_pool, q, out, *, total_tokens, scale=None, checked=False,
-                    streaming=False, workspace=None, stream=None):
+                    streaming=False, workspace=None, stream=None, planned=False):
     """out[S, Hq, D] (float32) <- decode attention of q[S, Hq, D] over the K
     cache of `desc` (its page_pool) and the V pool `v_pool`, both read
     through desc's block table. total_tokens: the sum of the token counts.
     scale defaults to 1/sqrt(head_dim). A workspace is allocated through
-    torch when none is given."""
+    torch when none is given. planned: `workspace` holds the plan
+    attention_plan wrote for this descriptor and settings."""
     return _attention(desc, v_pool, None, q, out, total_tokens, scale, checked, streaming,
-                      workspace, stream, False)
+                      workspace, stream, False, planned)
 
 
 def paged_attention_q8(desc, v_pool, v_scales, q, out, *, total_tokens, scale=None,
-                       checked=False, streaming=False, workspace=None, stream=None):
+                       checked=False, streaming=False, workspace=None, stream=None,
+                       planned=False):
     """out[S, Hq, D] (float32) <- decode attention of bf16 q[S, Hq, D] over
     int8 pools with one fp32 scale per slot, each element's value being its
     code times its slot's scale: the K pool and K scales of `desc` (its
     page_pool and scales), the V pool `v_pool` and `v_scales`. Other
     arguments as paged_attention."""
     return _attention(desc, v_pool, v_scales, q, out, total_tokens, scale, checked, streaming,
-                      workspace, stream, True)
+                      workspace, stream, True, planned)
 
 
 # ---- batched calls: several pools through the table of one descriptor -------

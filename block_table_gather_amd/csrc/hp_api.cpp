@@ -1037,7 +1037,7 @@ static hp_status paged_attention(const hp_desc *desc, const void *v_pool,
         return HP_ERR_DTYPE;
     if ((st = check_attention(desc, num_q_heads, q8)) != HP_OK)
         return st;
-    if (flags & ~(uint32_t)(HP_FLAG_CHECKED | HP_FLAG_STREAM))
+    if (flags & ~(uint32_t)(HP_FLAG_CHECKED | HP_FLAG_STREAM | HP_FLAG_PLANNED))
         return HP_ERR_ARG;
     const uint64_t S = desc->num_seqs, D = desc->head_dim;
     if (S && (!v_pool || !q || !out))
@@ -1074,6 +1074,7 @@ static hp_status paged_attention(const hp_desc *desc, const void *v_pool,
     j.idx64 = desc->index_type == HP_INDEX_U64;
     j.bf16 = desc->dtype == HP_DTYPE_BF16 || q8;
     j.q8 = q8;
+    j.planned = flags & HP_FLAG_PLANNED;
     j.stream_loads = flags & HP_FLAG_STREAM;
     j.num_seqs = (uint32_t)S;
     j.page_size = desc->page_size;
@@ -1095,6 +1096,51 @@ static hp_status paged_attention(const hp_desc *desc, const void *v_pool,
     j.scale = scale;
     j.workspace = workspace;
     const hipError_t e = hp::launch_attention(j, (hipStream_t)stream);
+    return e == hipSuccess ? HP_OK : hip_failed(e);
+}
+
+hp_status hp_attention_plan(const hp_desc *desc, uint32_t num_q_heads, void *workspace,
+                            size_t workspace_bytes, uint32_t flags, void *stream) {
+    Geometry g;
+    hp_status st = check_desc(desc, &g);
+    if (st != HP_OK)
+        return st;
+    const bool q8 = desc->dtype == HP_DTYPE_I8;
+    if ((st = check_attention(desc, num_q_heads, q8)) != HP_OK)
+        return st;
+    if (flags & ~(uint32_t)(HP_FLAG_CHECKED | HP_FLAG_STREAM))
+        return HP_ERR_ARG;
+    const uint64_t S = desc->num_seqs;
+    const uint64_t need = hp::attention_workspace_bytes(S, desc->total_tokens, desc->page_size,
+                                                        desc->num_heads, desc->head_dim,
+                                                        num_q_heads);
+    if ((st = check_workspace(workspace, workspace_bytes, need)) != HP_OK)
+        return st;
+    if (!aligned(workspace, 256))
+        return HP_ERR_ALIGN;
+    if (flags & HP_FLAG_CHECKED) {
+        hp_validate_result r;
+        if ((st = run_validate(desc, nullptr, workspace, &r, (hipStream_t)stream)) != HP_OK)
+            return st;
+    }
+    if (!S)
+        return HP_OK;
+    hp::AttentionJob j = {};
+    j.idx64 = desc->index_type == HP_INDEX_U64;
+    j.bf16 = desc->dtype == HP_DTYPE_BF16 || q8;
+    j.q8 = q8;
+    j.stream_loads = flags & HP_FLAG_STREAM;
+    j.num_seqs = (uint32_t)S;
+    j.page_size = desc->page_size;
+    j.num_kv_heads = desc->num_heads;
+    j.num_q_heads = num_q_heads;
+    j.head_dim = desc->head_dim;
+    j.total_tokens = desc->total_tokens;
+    j.block_table = desc->block_table;
+    j.seq_ptr = desc->seq_ptr;
+    j.seq_lens = desc->seq_lens;
+    j.workspace = workspace;
+    const hipError_t e = hp::launch_attention_plan(j, (hipStream_t)stream);
     return e == hipSuccess ? HP_OK : hip_failed(e);
 }
 

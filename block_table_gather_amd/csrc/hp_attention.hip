@@ -1896,19 +1896,20 @@ uint64_t attention_workspace_bytes(uint64_t num_seqs, uint64_t total_tokens, uin
     return need;
 }
 
-hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
-    (void)hipGetLastError();  // clear errors left by earlier calls that are not ours
-    const AttentionShape sh = attention_shape(job.num_seqs, job.total_tokens, job.page_size,
-                                              job.num_kv_heads, job.head_dim, job.num_q_heads,
-                                              job.stream_loads, job.q8);
-    const WsLayout wl = ws_layout(job.num_seqs, job.num_q_heads, job.head_dim, sh);
+namespace {
+
+// The planning kernels of a call: with the shared-prefix pass, the leading-page
+// comparison and the prefix plan; above kAttnFusedSeqs sequences without it,
+// the unit plan; otherwise none (the attention kernels count units
+// themselves). Their results live in the workspace and depend only on the
+// table, the counts and the launch shape.
+hipError_t run_plan(const AttentionJob &job, const AttentionShape &sh, const WsLayout &wl,
+                    hipStream_t stream) {
     unsigned char *ws = static_cast<unsigned char *>(job.workspace);
     uint32_t *unit_end = reinterpret_cast<uint32_t *>(ws + wl.unit_end);
     uint32_t *unit_seq = reinterpret_cast<uint32_t *>(ws + wl.unit_seq);
     auto at = [&](uint64_t off) { return reinterpret_cast<uint32_t *>(ws + off); };
-
     const bool fused = job.num_seqs <= kAttnFusedSeqs && !sh.shared;
-    hipError_t e = hipSuccess;
     if (sh.shared) {
         PlanArgs pa = {};
         pa.block_table = job.block_table;
@@ -1938,16 +1939,44 @@ hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
         hipLaunchKernelGGL(job.idx64 ? attention_prefix_plan_kernel<uint64_t>
                                      : attention_prefix_plan_kernel<uint32_t>,
                            dim3(1), dim3(kAttnThreads), 0, stream, pa);
-        if ((e = hipGetLastError()) != hipSuccess)
-            return e;
-    } else if (!fused) {
+        return hipGetLastError();
+    }
+    if (!fused) {
         hipLaunchKernelGGL(job.idx64 ? attention_plan_kernel<uint64_t>
                                      : attention_plan_kernel<uint32_t>,
                            dim3(1), dim3(kAttnThreads), 0, stream, job.seq_lens, job.num_seqs,
                            sh.unit_tokens, (uint32_t)sh.cap_units, unit_end, unit_seq);
-        if ((e = hipGetLastError()) != hipSuccess)
-            return e;
+        return hipGetLastError();
     }
+    return hipSuccess;
+}
+
+} // namespace
+
+hipError_t launch_attention_plan(const AttentionJob &job, hipStream_t stream) {
+    (void)hipGetLastError();  // clear errors left by earlier calls that are not ours
+    const AttentionShape sh = attention_shape(job.num_seqs, job.total_tokens, job.page_size,
+                                              job.num_kv_heads, job.head_dim, job.num_q_heads,
+                                              job.stream_loads, job.q8);
+    return run_plan(job, sh, ws_layout(job.num_seqs, job.num_q_heads, job.head_dim, sh), stream);
+}
+
+hipError_t launch_attention(const AttentionJob &job, hipStream_t stream) {
+    (void)hipGetLastError();  // clear errors left by earlier calls that are not ours
+    const AttentionShape sh = attention_shape(job.num_seqs, job.total_tokens, job.page_size,
+                                              job.num_kv_heads, job.head_dim, job.num_q_heads,
+                                              job.stream_loads, job.q8);
+    const WsLayout wl = ws_layout(job.num_seqs, job.num_q_heads, job.head_dim, sh);
+    unsigned char *ws = static_cast<unsigned char *>(job.workspace);
+    uint32_t *unit_end = reinterpret_cast<uint32_t *>(ws + wl.unit_end);
+    uint32_t *unit_seq = reinterpret_cast<uint32_t *>(ws + wl.unit_seq);
+    auto at = [&](uint64_t off) { return reinterpret_cast<uint32_t *>(ws + off); };
+
+    const bool fused = job.num_seqs <= kAttnFusedSeqs && !sh.shared;
+    hipError_t e = hipSuccess;
+    // planned: the workspace holds this shape's plan from launch_attention_plan
+    if (!job.planned && (e = run_plan(job, sh, wl, stream)) != hipSuccess)
+        return e;
 
     AArgs a = {};
     a.k_pool = static_cast<const unsigned char *>(job.k_pool);

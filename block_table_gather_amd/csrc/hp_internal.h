@@ -264,7 +264,8 @@ struct AttentionShape {
 
 struct AttentionJob {
     bool idx64, bf16, stream_loads;
-    bool q8;  // int8 pools with per-slot scales, dequantised to bf16 (bf16 queries)
+    bool q8;       // int8 pools with per-slot scales (bf16 queries)
+    bool planned;  // the workspace already holds this call's plan (launch_attention_plan)
     uint32_t num_seqs, page_size, num_kv_heads, num_q_heads, head_dim;
     uint64_t total_tokens;
     const void *k_pool, *v_pool, *q;
@@ -284,6 +285,8 @@ AttentionShape attention_shape(uint64_t num_seqs, uint64_t total_tokens, uint32_
 uint64_t attention_workspace_bytes(uint64_t num_seqs, uint64_t total_tokens, uint32_t page_size,
                                    uint32_t num_kv_heads, uint32_t head_dim, uint32_t num_q_heads);
 hipError_t launch_attention(const AttentionJob &job, hipStream_t stream);
+// The planning kernels of launch_attention alone (none for some shapes).
+hipError_t launch_attention_plan(const AttentionJob &job, hipStream_t stream);
 
 // Workspace bytes of the plan path: per-sequence offsets and chunk totals.
 uint64_t plan_workspace_bytes(uint64_t num_seqs);

@@ -102,13 +102,20 @@ enum {
                                     device, whether the call writes anything (see
                                     hp_validate_async). Not combined with
                                     HP_FLAG_CHECKED. */
-    HP_FLAG_DISJOINT = 1u << 4   /* scatter, quantize-on-scatter and the batched
+    HP_FLAG_DISJOINT = 1u << 4,  /* scatter, quantize-on-scatter and the batched
                                     scatter, with HP_FLAG_CHECKED only: after the
                                     descriptor passes validation, also check that no
                                     slot is written twice (hp_validate_writes); on a
                                     clash return HP_ERR_WRITE_ALIAS and write nothing.
                                     The workspace must hold
                                     hp_disjoint_workspace_bytes(desc). */
+    HP_FLAG_PLANNED = 1u << 5    /* attention: the workspace already holds the plan
+                                    hp_attention_plan wrote for this descriptor
+                                    (table, counts, total_tokens unchanged since),
+                                    num_q_heads and HP_FLAG_STREAM setting, so the
+                                    call runs no planning kernel (one plan serves the
+                                    calls of every layer of one batch); results are
+                                    undefined if the plan is stale. */
 };
 
 /* A block-paged descriptor for one {kv_role, layer_index} pair ([Hurray]
@@ -442,7 +449,8 @@ hp_status hp_copy_pages_batch(const hp_desc *desc, uint32_t num_pools, void *con
  * Arithmetic is fp32 with an online softmax in base 2; the result differs
  * from the exact one by rounding only. Flags: HP_FLAG_CHECKED (validate
  * first), HP_FLAG_STREAM (no page is read twice in this call: non-temporal
- * loads). Asynchronous on `stream`. */
+ * loads), HP_FLAG_PLANNED (reuse the plan of hp_attention_plan). Asynchronous
+ * on `stream`. */
 hp_status hp_paged_attention(const hp_desc *desc, const void *v_pool, const void *q,
                              uint32_t num_q_heads, float scale, void *out, uint32_t out_dtype,
                              void *workspace, size_t workspace_bytes, uint32_t flags,
@@ -478,6 +486,23 @@ hp_status hp_paged_attention_q8(const hp_desc *desc, const void *v_pool, const f
                                 const void *q, uint32_t num_q_heads, float scale, void *out,
                                 uint32_t out_dtype, void *workspace, size_t workspace_bytes,
                                 uint32_t flags, void *stream);
+
+/* The planning kernels of hp_paged_attention / hp_paged_attention_q8 alone,
+ * into the workspace: for a batch whose sequences share leading pages
+ * ([Hurray] Prefix Sharing) the comparison of neighbouring slices and the
+ * shared-prefix plan, and above 4,096 sequences the unit plan; for other
+ * shapes nothing. The plan depends only on the table, the counts, the launch
+ * shape (num_q_heads, head_dim, the pool's element type and HP_FLAG_STREAM),
+ * not on the pools or queries, so the attention calls of every layer of one
+ * batch can pass HP_FLAG_PLANNED and reuse it.
+ * desc         as for the attention call (its dtype picks the int8 shape).
+ * workspace    DEVICE, 256-byte aligned, hp_attention_workspace_bytes bytes;
+ *              the later calls must pass the same workspace.
+ * flags        HP_FLAG_STREAM as the later calls will pass it; HP_FLAG_CHECKED
+ *              validates the descriptor first (synchronously).
+ * Asynchronous on `stream`. */
+hp_status hp_attention_plan(const hp_desc *desc, uint32_t num_q_heads, void *workspace,
+                            size_t workspace_bytes, uint32_t flags, void *stream);
 
 /* Workspace bytes hp_paged_attention (f16 or bf16 pools) or
  * hp_paged_attention_q8 (int8 pools) needs for this descriptor (its

@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
                           "hp_gather_dequant", "hp_status_str", "hp_last_hip_error",
                           "hp_gather_batch", "hp_scatter_batch", "hp_gather_dequant_batch",
                           "hp_copy_pages", "hp_copy_pages_batch", "hp_gather_dequant_q",
-                          "hp_paged_attention", "hp_paged_attention_q8",
+                          "hp_paged_attention", "hp_paged_attention_q8", "hp_attention_plan",
                           "hp_attention_workspace_bytes",
                           "hp_scatter_quant", "hp_validate_async", "hp_validate_verdict",
                           "hp_gather_static", "hp_validate_writes",
@@ -266,6 +266,28 @@ def attn8(d, v=ALIGNED + 0x40000000, vs=VS, q=ALIGNED + 0x50000000, hq=8, out=OU
         n = 1 << 30 if n is None else n
     return L.hp_paged_attention_q8(ctypes.byref(d) if d is not None else None, v, vs, q, hq,
                                    0.125, out, hp.DTYPE["f32"], ws, n or 0, flags, None)
+
+
+def test_attention_plan_rejections():
+    f = desc()
+    need = L.hp_attention_workspace_bytes(ctypes.byref(f), 8)
+    ws = ALIGNED + 0x200000000
+    plan = lambda d, hq=8, w=ws, n=need, flags=0: L.hp_attention_plan(
+        ctypes.byref(d) if d is not None else None, hq, w, n, flags, None)
+    assert plan(desc(num_seqs=0, num_block_entries=0, total_tokens=0)) == S["HP_OK"]
+    assert plan(None) == S["HP_ERR_NULL"]
+    assert plan(desc(dtype=hp.DTYPE["f32"])) == S["HP_ERR_DTYPE"]
+    assert plan(f, hq=6) == S["HP_ERR_ARG"]
+    assert plan(f, flags=hp.HP_FLAG_PLANNED) == S["HP_ERR_ARG"]
+    assert plan(f, flags=hp.HP_FLAG_GATED) == S["HP_ERR_ARG"]
+    assert plan(f, n=need - 1) == S["HP_ERR_WORKSPACE"]
+    assert plan(f, w=None, n=0) == S["HP_ERR_WORKSPACE"]
+    assert plan(f, w=ws + 64) == S["HP_ERR_ALIGN"]
+    # the attention calls take the flag
+    assert attn(desc(num_seqs=0, num_block_entries=0, total_tokens=0),
+                flags=hp.HP_FLAG_PLANNED) == S["HP_OK"]
+    assert attn8(desc(dtype=hp.DTYPE["i8"], num_seqs=0, num_block_entries=0, total_tokens=0),
+                 flags=hp.HP_FLAG_PLANNED) == S["HP_OK"]
 
 
 def test_attention_q8_rejections():
