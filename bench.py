@@ -527,7 +527,9 @@ def summarize_attention(trace_dir, fetch_dir, write_dir):
 
     lines = ["# Kernel durations: decode attention through the block table (rocprofv3)", "",
              "Command (from the repository root, on one MI355X):", "", f"    {ATTN_TRACE_CMD}", "",
-             "Seven workloads, each called 21 times: the decode batch (64 sequences, 32 kv",
+             "Seven workloads, each called 21 times (the prefix ones 21 more times reusing a",
+             "plan made once, HP_FLAG_PLANNED: no comparison or plan kernel in those calls):",
+             "the decode batch (64 sequences, 32 kv",
              "heads x 128, streaming loads) over f16 pools with one query head per kv head",
              "(vector kernel and combine) and with four (matrix-core kernel and combine); the",
              "prefix-sharing batch (256 sequences sharing 64 leading pages, 8 kv heads x 128)",
