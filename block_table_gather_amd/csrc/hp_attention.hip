@@ -1135,10 +1135,21 @@ __device__ __forceinline__ void shared_item(const AArgs &a, uint32_t w, uint32_t
     }
 }
 
+// Waves per SIMD the matrix-core kernel is built for when its grid carries
+// the shared-prefix pass (16-bit pools). Measured on MI355X, prefix batch:
+// three waves (a few registers spilled) against two, G = 4: 100.4 -> 95.3 us,
+// G = 8: 121.3 -> 110.0 us; the same bound on the streamed decode batch lost
+// 5 % (192.3 -> 202.3 us at G = 4), so only the grids with the pass take it.
+#ifndef HP_ATTN_SHARED_WAVES
+#define HP_ATTN_SHARED_WAVES 3
+#endif
+
 // R: accumulator rows per lane that hold query heads (1 for G <= 4, 2 for
 // G <= 8, else 4). Q8: int8 pools with per-slot scales (ET is then BF16).
-template <typename ET, typename IdxT, int D, bool NT, int R, bool Q8>
-__global__ __launch_bounds__(kAttnThreads, Q8 ? 2 : 1) void attention_mfma_kernel(AArgs a) {
+// SH: the grid carries the shared-prefix pass (a.shared).
+template <typename ET, typename IdxT, int D, bool NT, int R, bool Q8, bool SH>
+__global__ __launch_bounds__(kAttnThreads, Q8 ? 2 : (SH ? HP_ATTN_SHARED_WAVES : 1))
+void attention_mfma_kernel(AArgs a) {
 #pragma clang fp contract(off)
     using M = Mma<ET>;
     using V8 = typename M::V8;
@@ -1148,7 +1159,7 @@ __global__ __launch_bounds__(kAttnThreads, Q8 ? 2 : 1) void attention_mfma_kerne
     extern __shared__ __align__(16) unsigned char lds[];
     const uint32_t S = a.num_seqs;
     uint32_t g = blockIdx.x;
-    if (a.shared) {
+    if constexpr (SH) {
         // the shared-prefix work items come first, so that their reads (mostly
         // served by the caches) overlap the units' HBM reads
         // (one kv head per workgroup: kMfmaWaves workgroups per item and
@@ -1210,7 +1221,7 @@ __global__ __launch_bounds__(kAttnThreads, Q8 ? 2 : 1) void attention_mfma_kerne
     // ns = ceil(rest / unit_tokens), and at least one, as unit_tokens >= P).
     uint64_t sh_tokens = 0;
     uint32_t k = g - u0;
-    if (a.shared) {
+    if constexpr (SH) {
         const uint32_t sh = uni(a.pre_pages[s]);
         const uint32_t nch = (sh + a.chunk_pages - 1) / a.chunk_pages;
         if (k < nch)
@@ -1702,11 +1713,15 @@ hipError_t launch_attention_mfma(const AArgs &a, const AttentionShape &sh, bool 
     const size_t lds = (a.fused ? ((4 * (size_t)a.num_seqs + 15) & ~(size_t)15) : 0) +
                        a.pg_area + kMfmaWaves * mfma_wave_lds<D>() +
                        (Q8 ? 2 * 2 * kMfmaTile * sizeof(float) : 0);
-    if (nt)
-        hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, true, R, Q8>), grid,
+    // (the shared pass streams its units: nt is set whenever a.shared is)
+    if (a.shared)
+        hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, true, R, Q8, true>), grid,
+                           dim3(kAttnThreads), lds, stream, a);
+    else if (nt)
+        hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, true, R, Q8, false>), grid,
                            dim3(kAttnThreads), lds, stream, a);
     else
-        hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, false, R, Q8>), grid,
+        hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, false, R, Q8, false>), grid,
                            dim3(kAttnThreads), lds, stream, a);
     return hipGetLastError();
 }
