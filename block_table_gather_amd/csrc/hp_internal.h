@@ -150,13 +150,13 @@ struct CopyJob {
 };
 
 // Bytes of one page a page-copy workgroup copies, and whether those
-// workgroups take chunks in XCD order (8 KiB in XCD order measured fastest:
-// see copy_pages_kernel).
+// workgroups take chunks in XCD order (4 KiB in dispatch order measured
+// fastest: see copy_pages_kernel).
 #ifndef HP_PAGE_CHUNK_BYTES
-#define HP_PAGE_CHUNK_BYTES 8192
+#define HP_PAGE_CHUNK_BYTES 4096
 #endif
 #ifndef HP_PAGE_XCD
-#define HP_PAGE_XCD 1
+#define HP_PAGE_XCD 0
 #endif
 constexpr uint32_t kPageChunkBytes = HP_PAGE_CHUNK_BYTES;
 

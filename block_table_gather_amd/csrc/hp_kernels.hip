@@ -1279,13 +1279,15 @@ struct PArgs {
 };
 
 // Workgroup (x, m) copies chunk x % chunks_per_page of copy x / chunks_per_page
-// in pool m (x in XCD order: each XCD takes a contiguous range of chunks, so
-// a page's chunks share one L2); the chunk-0 workgroup also copies the page's
-// slot scales. Every copy reads a page and writes another one exactly once:
-// non-temporal both ways, U loads per lane in flight (exactly one chunk).
-// Measured on MI355X, 1,024 copies of 128 KiB pages with cold caches: 8 KiB
-// chunks in XCD order 50.5 us, 8 KiB in dispatch order 52.8, 16 KiB 57.8,
-// 32 KiB 69.2.
+// in pool m (x in dispatch order by default; HP_PAGE_XCD gives each XCD a
+// contiguous range of chunks instead); the chunk-0 workgroup also copies the
+// page's slot scales. Every copy reads a page and writes another one exactly
+// once: non-temporal both ways, U loads per lane in flight (exactly one chunk).
+// Measured on MI355X, 1,024 copies of 128 KiB pages, cold caches / back to
+// back: 4 KiB chunks in dispatch order 48.9 / 45.9 us, 4 KiB in XCD order
+// 50.4 / 45.2, 8 KiB in XCD order 50.4 / 47.8, 16 KiB 55.0 / 50.9; through a
+// contiguous table (pages 0..1023 to 1024..2047) 4 KiB in dispatch order
+// 48.5 / 45.2 us, in XCD order 52.7 / 49.1.
 template <typename IdxT, int VEC, int U>
 __global__ __launch_bounds__(kThreads) void copy_pages_kernel(PArgs a) {
     const uint64_t x = group_order<HP_PAGE_XCD != 0>(blockIdx.x, gridDim.x);
@@ -1560,8 +1562,9 @@ hipError_t launch_pages(PArgs &a, const PageCopyJob &job, hipStream_t stream) {
             a.pool[m] = static_cast<unsigned char *>(job.pools[first + m]);
             a.scales[m] = job.scales ? job.scales[first + m] : nullptr;
         }
-        // loads in flight per lane: the smallest of 2, 4, 8 that covers a chunk
+        // loads in flight per lane: the smallest of 1, 2, 4, 8 that covers a chunk
         constexpr int U = VEC < 16 ? kCopyUnroll
+                          : kPageChunkBytes <= kThreads * 16     ? 1
                           : kPageChunkBytes <= 2 * kThreads * 16 ? 2
                           : kPageChunkBytes <= 4 * kThreads * 16 ? 4
                                                                  : 8;

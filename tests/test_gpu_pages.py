@@ -118,3 +118,24 @@ def test_copy_on_write_scenario(hp):
     assert_bits_equal(got, want, "scenario")
     assert np.array_equal(got[:24], got[24:48])      # E's prefix == D's
     assert_bits_equal(host_bits(d.pool)[1], pool0[1], "shared page untouched")
+
+
+def test_copy_pages_decode_pool(hp):
+    """The decode pool at full size (12,000 pages of 16 x 32 x 128 fp16 =
+    128 KiB) in the benchmark's launch: 1,024 referenced pages copied to
+    pages no sequence references. The whole pool afterwards equals the
+    oracle's, bit for bit."""
+    w = workloads.decode()
+    say("copy pages decode pool", w.describe())
+    d = OnDevice(w)
+    free = np.setdiff1d(np.arange(w.num_pages), w.block_table.astype(np.int64))
+    rng = np.random.default_rng(6)
+    src = rng.choice(w.block_table.astype(np.int64), 1024, replace=False).astype(np.uint32)
+    dst = rng.choice(free, 1024, replace=False).astype(np.uint32)
+    before = host_bits(d.pool)
+    want, _ = oracle.copy_pages(before, src, dst, page_size=w.page_size,
+                                num_heads=w.num_heads, head_dim=w.head_dim)
+    del before
+    hp.copy_pages(d.desc, idx_tensor(src, DEV), idx_tensor(dst, DEV))
+    torch.cuda.synchronize()
+    assert_bits_equal(host_bits(d.pool), want, "pool")
