@@ -48,6 +48,39 @@
 #include <type_traits>
 
 namespace hp {
+
+// Workgroups aimed at per launch (a unit holds enough pages to reach about
+// this many), and the most pages one unit may hold.
+#ifndef HP_ATTN_TARGET_GROUPS_MHA
+#define HP_ATTN_TARGET_GROUPS_MHA 1024
+#endif
+// Grouped query heads with cached loads: measured on MI355X, prefix batch
+// (shared-prefix pass, three waves per SIMD), G = 4 / 8: 3,072 workgroups
+// 94.9 / 109.9 us, 4,096 93.4 / 107.5 us, 5,120 94.9 / 110.0 us, 6,144
+// 96.2 / 113.5 us.
+#ifndef HP_ATTN_TARGET_GROUPS_GQA
+#define HP_ATTN_TARGET_GROUPS_GQA 4096
+#endif
+constexpr uint64_t kAttnTargetGroupsMha = HP_ATTN_TARGET_GROUPS_MHA;
+constexpr uint64_t kAttnTargetGroupsGqa = HP_ATTN_TARGET_GROUPS_GQA;
+// Grouped query heads with streaming loads (pages read once) take longer
+// units: measured on MI355X, decode batch at G = 4 / 8, 3,072 workgroups
+// 196.4 / 212.3 us, 1,536 194.3 / 209.5 us, 1,024 195.8 / 212.0 us; with
+// cached loads (the prefix batch) 1,536 lost 6 %.
+#ifndef HP_ATTN_TARGET_GROUPS_GQA_STREAM
+#define HP_ATTN_TARGET_GROUPS_GQA_STREAM 1536
+#endif
+constexpr uint64_t kAttnTargetGroupsGqaStream = HP_ATTN_TARGET_GROUPS_GQA_STREAM;
+constexpr uint64_t kAttnMaxUnitPages = 256;
+// Smallest unit, in tokens per query-head slot of a lane group.
+#ifndef HP_ATTN_MIN_UNIT_TOKENS_PER_SLOT
+#define HP_ATTN_MIN_UNIT_TOKENS_PER_SLOT 8
+#endif
+constexpr uint64_t kAttnMinUnitTokensPerSlot = HP_ATTN_MIN_UNIT_TOKENS_PER_SLOT;
+// Up to this many sequences the attention kernels count units themselves
+// (unit table in LDS, 4 bytes per sequence); beyond it a plan kernel runs.
+constexpr uint32_t kAttnFusedSeqs = 4096;
+
 namespace {
 
 constexpr uint32_t kAttnThreads = 256;

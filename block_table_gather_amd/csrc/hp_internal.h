@@ -219,34 +219,8 @@ inline bool validate_writes_result(const ValidateJob &job) {
     return job.result && n <= kValidateOneItems;
 }
 
-// Decode attention over a block-paged K/V cache (hp_attention.hip).
-// Workgroups aimed at per launch (a unit holds enough pages to reach about
-// this many), and the most pages one unit may hold.
-#ifndef HP_ATTN_TARGET_GROUPS_MHA
-#define HP_ATTN_TARGET_GROUPS_MHA 1024
-#endif
-#ifndef HP_ATTN_TARGET_GROUPS_GQA
-#define HP_ATTN_TARGET_GROUPS_GQA 3072
-#endif
-constexpr uint64_t kAttnTargetGroupsMha = HP_ATTN_TARGET_GROUPS_MHA;
-constexpr uint64_t kAttnTargetGroupsGqa = HP_ATTN_TARGET_GROUPS_GQA;
-// Grouped query heads with streaming loads (pages read once) take longer
-// units: measured on MI355X, decode batch at G = 4 / 8, 3,072 workgroups
-// 196.4 / 212.3 us, 1,536 194.3 / 209.5 us, 1,024 195.8 / 212.0 us; with
-// cached loads (the prefix batch) 1,536 lost 6 %.
-#ifndef HP_ATTN_TARGET_GROUPS_GQA_STREAM
-#define HP_ATTN_TARGET_GROUPS_GQA_STREAM 1536
-#endif
-constexpr uint64_t kAttnTargetGroupsGqaStream = HP_ATTN_TARGET_GROUPS_GQA_STREAM;
-constexpr uint64_t kAttnMaxUnitPages = 256;
-// Smallest unit, in tokens per query-head slot of a lane group.
-#ifndef HP_ATTN_MIN_UNIT_TOKENS_PER_SLOT
-#define HP_ATTN_MIN_UNIT_TOKENS_PER_SLOT 8
-#endif
-constexpr uint64_t kAttnMinUnitTokensPerSlot = HP_ATTN_MIN_UNIT_TOKENS_PER_SLOT;
-// Up to this many sequences the attention kernels count units themselves
-// (unit table in LDS, 4 bytes per sequence); beyond it a plan kernel runs.
-constexpr uint32_t kAttnFusedSeqs = 4096;
+// Decode attention over a block-paged K/V cache (hp_attention.hip; its
+// launch-shape constants live there).
 
 struct AttentionShape {
     uint32_t heads_per_group;  // kv heads of one workgroup
