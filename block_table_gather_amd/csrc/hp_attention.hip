@@ -112,6 +112,9 @@ struct AArgs {
     // per-sequence shared pages and runs, and the shared pass's work items.
     uint32_t shared;          // shared work items lead the grid; suffix units follow
     uint32_t pg_area;         // LDS bytes of the staged page IDs (matrix-core kernel)
+    // Matrix-core grid with its head groups interleaved: blockIdx.x holds
+    // (work index, head group) as x * hg_il + y; 0: the head group is blockIdx.y.
+    uint32_t hg_il;
     uint32_t chunk_pages;     // pages of one shared-pass work item
     uint32_t seqs_per_block;  // sequences of one shared work item (four row blocks)
     const uint32_t *pre_pages, *run_of, *work_seq0, *work_chunk, *nwork;
@@ -1173,6 +1176,16 @@ __device__ __forceinline__ void shared_item(const AArgs &a, uint32_t w, uint32_t
 // three waves (a few registers spilled) against two, G = 4: 100.4 -> 95.3 us,
 // G = 8: 121.3 -> 110.0 us; the same bound on the streamed decode batch lost
 // 5 % (192.3 -> 202.3 us at G = 4), so only the grids with the pass take it.
+// Which matrix-core grids take their head groups interleaved in blockIdx.x
+// (bit 0: grids without the shared-prefix pass; bit 1: int8 grids with it).
+// Measured on MI355X, cold caches, against head groups in blockIdx.y: decode
+// batch G = 4 193.3 -> 189.4 us, G = 8 205.4 -> 201.9 us, int8 pools at G = 4
+// 122.3 -> 114.5 us; prefix batch over int8 pools 91.4 -> 84.4 us, but over
+// 16-bit pools at G = 8 108.3 -> 118.8 us (so not there). The vector kernel
+// (two head groups of 16 heads on the decode batch) measured no change.
+#ifndef HP_ATTN_HG_INTERLEAVE
+#define HP_ATTN_HG_INTERLEAVE 3
+#endif
 #ifndef HP_ATTN_SHARED_WAVES
 #define HP_ATTN_SHARED_WAVES 3
 #endif
@@ -1191,7 +1204,8 @@ void attention_mfma_kernel(AArgs a) {
     constexpr uint32_t VRB = v_row_bytes<D>();
     extern __shared__ __align__(16) unsigned char lds[];
     const uint32_t S = a.num_seqs;
-    uint32_t g = blockIdx.x;
+    const uint32_t by = a.hg_il ? blockIdx.x % a.hg_il : blockIdx.y;
+    uint32_t g = a.hg_il ? blockIdx.x / a.hg_il : blockIdx.x;
     if constexpr (SH) {
         // the shared-prefix work items come first, so that their reads (mostly
         // served by the caches) overlap the units' HBM reads
@@ -1199,7 +1213,7 @@ void attention_mfma_kernel(AArgs a) {
         // grid row)
         const uint32_t nw = uni(*a.nwork) * kMfmaWaves;
         if (g < nw) {
-            const uint32_t h = blockIdx.y * kMfmaWaves + g % kMfmaWaves;
+            const uint32_t h = by * kMfmaWaves + g % kMfmaWaves;
             if (h < a.num_kv_heads)
                 shared_item<ET, IdxT, D, Q8>(a, g / kMfmaWaves, h, lds);
             return;
@@ -1224,7 +1238,7 @@ void attention_mfma_kernel(AArgs a) {
         const uint32_t se = g - total;
         if (se >= S || blockIdx.z != 0 || ld_idx<IdxT>(a.seq_lens, se) != 0)
             return;
-        const uint32_t h0 = blockIdx.y * kMfmaWaves;
+        const uint32_t h0 = by * kMfmaWaves;
         const uint32_t nq = (min32(Hkv, h0 + kMfmaWaves) - h0) * G;
         float *o = a.out + ((uint64_t)se * Hq + (uint64_t)h0 * G) * D;
         for (uint32_t e = threadIdx.x; e < nq * D; e += kAttnThreads)
@@ -1281,7 +1295,7 @@ void attention_mfma_kernel(AArgs a) {
     __syncthreads();
 
     const uint32_t wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const uint32_t h = blockIdx.y * kMfmaWaves + wave;
+    const uint32_t h = by * kMfmaWaves + wave;
     if (h >= Hkv)
         return;  // no barrier follows
     unsigned char *vt = lds + ue_bytes + a.pg_area + wave * mfma_wave_lds<D>();
@@ -1739,9 +1753,18 @@ template <typename ET, typename IdxT, int D, int R, bool Q8>
 hipError_t launch_attention_mfma(const AArgs &a, const AttentionShape &sh, bool nt,
                                  hipStream_t stream) {
     // shared work items (at most cap_work), units, then one spare per sequence
-    const dim3 grid((uint32_t)(sh.cap_units + a.num_seqs +
-                               (a.shared ? kMfmaWaves * sh.cap_work : 0)),
-                    sh.head_groups, (a.group + kMfmaRows - 1) / kMfmaRows);
+    const uint64_t gx = sh.cap_units + a.num_seqs + (a.shared ? kMfmaWaves * sh.cap_work : 0);
+    const uint32_t gz = (a.group + kMfmaRows - 1) / kMfmaRows;
+    // Head groups interleaved (the head groups of one work index neighbours
+    // in the dispatch order, so that their pieces of each token row are read
+    // together) on the grids where it measured faster.
+    AArgs b = a;
+    const uint32_t il_bit = a.shared ? (Q8 ? 2u : 0u) : 1u;
+    const bool il = (HP_ATTN_HG_INTERLEAVE & il_bit) && sh.head_groups > 1 &&
+                    gx * sh.head_groups < (1ull << 31);
+    b.hg_il = il ? sh.head_groups : 0;
+    const dim3 grid = il ? dim3((uint32_t)(gx * sh.head_groups), 1, gz)
+                         : dim3((uint32_t)gx, sh.head_groups, gz);
     // (int8 pools: the shared pass keeps two stages of K and V scales too)
     const size_t lds = (a.fused ? ((4 * (size_t)a.num_seqs + 15) & ~(size_t)15) : 0) +
                        a.pg_area + kMfmaWaves * mfma_wave_lds<D>() +
@@ -1749,13 +1772,13 @@ hipError_t launch_attention_mfma(const AArgs &a, const AttentionShape &sh, bool 
     // (the shared pass streams its units: nt is set whenever a.shared is)
     if (a.shared)
         hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, true, R, Q8, true>), grid,
-                           dim3(kAttnThreads), lds, stream, a);
+                           dim3(kAttnThreads), lds, stream, b);
     else if (nt)
         hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, true, R, Q8, false>), grid,
-                           dim3(kAttnThreads), lds, stream, a);
+                           dim3(kAttnThreads), lds, stream, b);
     else
         hipLaunchKernelGGL((attention_mfma_kernel<ET, IdxT, D, false, R, Q8, false>), grid,
-                           dim3(kAttnThreads), lds, stream, a);
+                           dim3(kAttnThreads), lds, stream, b);
     return hipGetLastError();
 }
 
