@@ -64,11 +64,12 @@ namespace hp {
 constexpr uint64_t kAttnTargetGroupsMha = HP_ATTN_TARGET_GROUPS_MHA;
 constexpr uint64_t kAttnTargetGroupsGqa = HP_ATTN_TARGET_GROUPS_GQA;
 // Grouped query heads with streaming loads (pages read once) take longer
-// units: measured on MI355X, decode batch at G = 4 / 8, 3,072 workgroups
-// 196.4 / 212.3 us, 1,536 194.3 / 209.5 us, 1,024 195.8 / 212.0 us; with
-// cached loads (the prefix batch) 1,536 lost 6 %.
+// units: measured on MI355X, decode batch at G = 4 / 8 (int8 pools at G = 4),
+// grid with interleaved head groups, cold caches: 3,072 workgroups 191.6 /
+// 206.3 (117.7) us, 2,048 187.6 / 199.4 (113.1) us, 1,536 188.9 / 202.0
+// (114.7) us, 1,024 189.4 / 201.6 (116.1) us.
 #ifndef HP_ATTN_TARGET_GROUPS_GQA_STREAM
-#define HP_ATTN_TARGET_GROUPS_GQA_STREAM 1536
+#define HP_ATTN_TARGET_GROUPS_GQA_STREAM 2048
 #endif
 constexpr uint64_t kAttnTargetGroupsGqaStream = HP_ATTN_TARGET_GROUPS_GQA_STREAM;
 constexpr uint64_t kAttnMaxUnitPages = 256;
