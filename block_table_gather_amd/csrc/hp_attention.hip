@@ -1172,11 +1172,6 @@ __device__ __forceinline__ void shared_item(const AArgs &a, uint32_t w, uint32_t
     }
 }
 
-// Waves per SIMD the matrix-core kernel is built for when its grid carries
-// the shared-prefix pass (16-bit pools). Measured on MI355X, prefix batch:
-// three waves (a few registers spilled) against two, G = 4: 100.4 -> 95.3 us,
-// G = 8: 121.3 -> 110.0 us; the same bound on the streamed decode batch lost
-// 5 % (192.3 -> 202.3 us at G = 4), so only the grids with the pass take it.
 // Which matrix-core grids take their head groups interleaved in blockIdx.x
 // (bit 0: grids without the shared-prefix pass; bit 1: int8 grids with it).
 // Measured on MI355X, cold caches, against head groups in blockIdx.y: decode
@@ -1187,6 +1182,11 @@ __device__ __forceinline__ void shared_item(const AArgs &a, uint32_t w, uint32_t
 #ifndef HP_ATTN_HG_INTERLEAVE
 #define HP_ATTN_HG_INTERLEAVE 3
 #endif
+// Waves per SIMD the matrix-core kernel is built for when its grid carries
+// the shared-prefix pass (16-bit pools). Measured on MI355X, prefix batch:
+// three waves (a few registers spilled) against two, G = 4: 100.4 -> 95.3 us,
+// G = 8: 121.3 -> 110.0 us; the same bound on the streamed decode batch lost
+// 5 % (192.3 -> 202.3 us at G = 4), so only the grids with the pass take it.
 #ifndef HP_ATTN_SHARED_WAVES
 #define HP_ATTN_SHARED_WAVES 3
 #endif
