@@ -92,3 +92,18 @@ def bf16_bits_equal(got, want, what=""):
 
 def oracle_gather(d):
     return oracle.gather(host_bits(d.pool), **d.oracle_kw())
+
+
+def empty_seq_workload(dtype, seed):
+    """Nine sequences, four of them empty (the first, the last and two between;
+    two of the empty ones still name a page), ten kv heads of 128 with 16-token
+    pages: three head groups on the matrix cores, the last holding two kv heads."""
+    lens = np.array([0, 37, 0, 0, 130, 1, 0, 64, 0], np.uint32)
+    npg = [1, 3, 0, 1, 9, 1, 0, 4, 0]
+    sp = np.concatenate([[0], np.cumsum(npg)]).astype(np.uint32)
+    rng = np.random.default_rng(seed)
+    bt = rng.permutation(40)[: int(sp[-1])].astype(np.uint32)
+    values = "int8" if dtype == "i8" else "normal"
+    return workloads.Workload("empty-seqs", dtype, 16, 10, 128, 40, np.uint32, bt, sp, lens,
+                              values=values, with_scales=dtype == "i8", seed=seed)
+

@@ -27,7 +27,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import OnDevice, host_bits, idx_tensor, say
+from gpu_util import OnDevice, empty_seq_workload, host_bits, idx_tensor, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -452,3 +452,21 @@ def test_attention_shared_exact_cases(hp):
     bound = (2 * len(slots) + 8) * U * np.abs(vals[slots]).max()
     got = out.reshape(w.num_seqs, H, G, D)
     assert np.abs(got - mean[None, :, None, :]).max() <= bound
+
+
+@pytest.mark.parametrize("streaming", [False, True])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_attention_empty_sequences_three_head_groups(hp, dtype, streaming):
+    """Matrix-core grids (G = 4) with three head groups and empty sequences:
+    every head of an empty sequence is written as zeros (the output starts as
+    NaN), streamed (head groups interleaved in the grid) and cached (the grid
+    that carries the shared-prefix pass)."""
+    w = empty_seq_workload(dtype, 1500 + streaming)
+    say("attention empty sequences", dtype, streaming, w.describe())
+    d, v_pool, q = make_inputs(w, 4, 1510 + streaming)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    out = run(hp, d, v_pool, q, w, scale, streaming=streaming)
+    got = out.cpu().numpy()
+    for s in np.flatnonzero(w.seq_lens == 0):
+        assert np.all(got[s] == 0), f"sequence {s}"
+    check(w, got, q, d, v_pool, 4, scale, what=f"empty sequences {dtype} stream={streaming}")

@@ -27,7 +27,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import OnDevice, assert_bits_equal, host_bits, idx_tensor, say
+from gpu_util import OnDevice, assert_bits_equal, empty_seq_workload, host_bits, idx_tensor, say
 from test_gpu_attention import shared_prefix_workload
 
 pytestmark = pytest.mark.gpu
@@ -299,3 +299,14 @@ def test_attention_q8_decode_workload(hp, group):
     both_checks(hp, w, group, 2600 + group, 1.0 / math.sqrt(128), what=f"int8 decode G={group}",
                 streaming=True)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("streaming", [False, True])
+def test_attention_q8_empty_sequences_three_head_groups(hp, streaming):
+    """Int8 pools on the matrix cores (G = 4) with three head groups (ten kv
+    heads) and empty sequences first, last and between: head groups
+    interleaved in the grid both streamed and cached."""
+    w = empty_seq_workload("i8", 2500 + streaming)
+    say("attention int8 empty sequences", streaming, w.describe())
+    both_checks(hp, w, 4, 2510 + streaming, 1.0 / math.sqrt(w.head_dim),
+                what=f"int8 empty sequences stream={streaming}", streaming=streaming)
